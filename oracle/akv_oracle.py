@@ -1,0 +1,665 @@
+"""fp64 CPU oracle for AKV cache engineering over a paged KV pool.
+
+TEST INFRASTRUCTURE ONLY.  Only `tests/`, `__graft_entry__.smoke()` and the
+`cpu_baseline` leg of `bench.py` may import this module.  The product package
+(`kv_cache_drop_amd`) never imports it, and the two share no code: no kernels,
+headers, helpers, tables or constant generators.  The only module both sides
+use is `workloads`, which holds seeded input generators and no arithmetic of
+the method.
+
+Sources, cited by page title and section:
+
+  [AKV-blog]  "AKV: Cache Engineering for Autonomous Agents and State-Preserving
+              Prefix Invalidation Bypass" (A. Akhunji, technical breakdown)
+  [AKV-notes] "Cache Engineering for Agents" (reading notes on Fu et al.,
+              arXiv:2610.28577)
+  [Leyline]   "Leyline: KV Cache Directives for Agentic Inference" (paper digest)
+
+What is computed, and where the pages fix it:
+
+* append / drop / repos are the three cache operations of [AKV-notes] section 1
+  (Problem & Solution).  Drop marks a token span inactive without freeing or
+  rewriting it; attention then skips those entries ([AKV-blog] section 2,
+  "The Drop Primitive").
+* repos rotates retained keys by the RoPE closure R(a)R(b) = R(a+b)
+  ([AKV-blog] section 2, "The Repos Primitive and Rotary Position Embeddings";
+  [Leyline] Method).  Reading adopted: signed delta, new position = pos + delta,
+  new key = R(delta) key, with R(phi) = [[cos, -sin], [sin, cos]] acting on the
+  pair (k_2i, k_2i+1) at angle phi = delta * theta_i and
+  theta_i = base^(-2i/d_rot).  Deltas from several spans covering one token add
+  ([Leyline] Method, composition of directives of either sign).
+* MLA layouts rotate only K_pe; K_nope and V are left as they are ([Leyline]
+  Method).
+* splice is the [Leyline] AMORTIZE directive: a span is replaced by a stub and
+  every downstream token moves by delta = |R| - (s_end - s_start).
+* compaction copies the visible tokens into fresh dense pages when the
+  fraction of wasted slots in a sequence's referenced pages exceeds 40%
+  ([AKV-blog] section 7, Dilemma 2).
+* segment-batch attention: the queries are split into segments; each segment
+  gathers its own list of visible KV entries and runs ordinary causal attention
+  over it, with no dense mask ([AKV-notes] section 3, Segment-Batch Attention;
+  [AKV-blog] section 4).  The mask is bottom-right causal over list order.
+* dense_masked_attention is the masked-softmax definition of [AKV-blog]
+  section 2 taken literally (additive 0 / -inf mask over every token ever
+  appended), used only to pin the segment oracle.
+
+Page allocation (not described on the pages; a stated rule both sides follow):
+the pool holds a FIFO free queue initialised to a caller-given page order and
+a FIFO evictable queue.  Pages are taken from the free queue first, then from
+the evictable queue (dropped cache is evicted first, [AKV-notes] section 3,
+Cache Management).  A page enters the evictable queue when its last visible
+token is dropped or moved away, unless it is the sequence's open tail page.
+"""
+from __future__ import annotations
+
+from collections import deque
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+INT32_MAX = 2 ** 31 - 1
+DEFAULT_COMPACT_THRESHOLD = 0.40
+
+
+class OracleError(Exception):
+    code = 0
+
+
+class EInval(OracleError):
+    code = -1
+
+
+class ERange(OracleError):
+    code = -2
+
+
+class ENoMem(OracleError):
+    code = -3
+
+
+class EState(OracleError):
+    code = -4
+
+
+# ---------------------------------------------------------------------------
+# rotation
+# ---------------------------------------------------------------------------
+def rope_inv_freq(d_rot: int, base: float) -> np.ndarray:
+    """theta_i = base^(-2i/d_rot), i < d_rot/2 (reading of the RoPE angle
+    m*theta in [AKV-blog] section 2; no frequency scaling)."""
+    i = np.arange(d_rot // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * i / d_rot)
+
+
+def rotate(x: np.ndarray, delta: np.ndarray, inv_freq: np.ndarray, pairing: int) -> np.ndarray:
+    """R(delta) applied to every rotation pair on the last axis of x, in fp64.
+
+    x: [..., d_rot]; delta: shape x.shape[:-1] (or broadcastable to it).
+    Pair i is (2i, 2i+1) for interleaved pairing ([AKV-blog] section 2 writes
+    the update on (k_2i, k_2i+1)) or (i, i + d_rot/2) for half-split pairing.
+    Each pair (a, b) becomes (a cos phi - b sin phi, a sin phi + b cos phi)
+    with phi = delta * theta_i."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    phi = np.asarray(delta, dtype=np.float64)[..., None] * inv_freq
+    c, s = np.cos(phi), np.sin(phi)
+    out = np.empty_like(x)
+    if pairing == 0:
+        a, b = x[..., 0::2], x[..., 1::2]
+        out[..., 0::2] = a * c - b * s
+        out[..., 1::2] = a * s + b * c
+    else:
+        h = d // 2
+        a, b = x[..., :h], x[..., h:]
+        out[..., :h] = a * c - b * s
+        out[..., h:] = a * s + b * c
+    return out
+
+
+# ---------------------------------------------------------------------------
+# pool
+# ---------------------------------------------------------------------------
+class _Seq:
+    def __init__(self):
+        self.slot = np.zeros(0, np.int64)       # page * S + offset, -1 once its page is evicted
+        self.pos = np.zeros(0, np.int64)
+        self.dropped = np.zeros(0, bool)
+        self.pages: List[int] = []              # owned pages in allocation order
+        self.tail = -1                          # open (not yet full) page, or -1
+        self.alive = True
+        # token log for the dense brute force (only when keep_log)
+        self.log_k: List[np.ndarray] = []
+        self.log_kpe: List[np.ndarray] = []
+        self.log_v: List[np.ndarray] = []
+        self.log_pos: List[np.ndarray] = []
+
+    @property
+    def n(self) -> int:
+        return len(self.slot)
+
+
+class Pool:
+    """Paged KV pool with per-sequence token tables, in fp64.
+
+    Storage mirrors a paged layout: the rotated key part `kr[page, h, off, d_rope]`
+    (all of K for GQA; K_pe for MLA, with one head when K_pe is shared),
+    `kn[page, h, off, d_nope]` (MLA only) and `v[page, h, off, d_v]`."""
+
+    def __init__(self, layout, page_order: Optional[Sequence[int]] = None,
+                 keep_log: bool = False, compact_threshold: float = DEFAULT_COMPACT_THRESHOLD,
+                 inv_freq: Optional[np.ndarray] = None):
+        L = layout
+        self.L = L
+        S, P = L.page_size, L.num_pages
+        self.S = S
+        self.kr = np.zeros((P, L.n_rope_heads, S, L.d_rope))
+        self.kn = np.zeros((P, L.n_kv_heads, S, L.d_nope)) if L.mla else None
+        self.v = np.zeros((P, L.n_kv_heads, S, L.d_v))
+        order = list(range(P)) if page_order is None else [int(p) for p in page_order]
+        if sorted(order) != list(range(P)):
+            raise EInval("page_order must be a permutation of the pages")
+        self.free = deque(order)
+        self.evictable = deque()
+        self.owner = np.full(P, -1, np.int64)
+        self.nvis = np.zeros(P, np.int64)
+        self.filled = np.zeros(P, np.int64)
+        self.in_evict = np.zeros(P, bool)
+        self.seqs: List[_Seq] = []
+        self.keep_log = keep_log
+        self.compact_threshold = compact_threshold
+        self.inv_freq = rope_inv_freq(L.d_rope, L.rope_theta) if inv_freq is None else np.asarray(inv_freq, np.float64)
+
+    # -- sequences -----------------------------------------------------------
+    def seq_create(self) -> int:
+        self.seqs.append(_Seq())
+        return len(self.seqs) - 1
+
+    def _seq(self, s: int) -> _Seq:
+        if not (0 <= s < len(self.seqs)):
+            raise EInval(f"no sequence {s}")
+        q = self.seqs[s]
+        if not q.alive:
+            raise EState(f"sequence {s} was released")
+        return q
+
+    def seq_release(self, s: int) -> None:
+        """Return every page the sequence still owns to the back of the free
+        queue, in allocation order (pages waiting in the evictable queue are
+        taken out of it)."""
+        q = self._seq(s)
+        for p in q.pages:
+            if self.in_evict[p]:
+                self.evictable.remove(p)
+                self.in_evict[p] = False
+            self.owner[p] = -1
+            self.nvis[p] = 0
+            self.filled[p] = 0
+            self.free.append(p)
+        q.pages = []
+        q.tail = -1
+        q.alive = False
+
+    # -- allocation ------------------------------------------------------------
+    def _available(self) -> int:
+        return len(self.free) + len(self.evictable)
+
+    def _evict(self, p: int) -> None:
+        o = self.seqs[self.owner[p]]
+        S = self.S
+        hit = (o.slot >= 0) & (o.slot // S == p)
+        assert not np.any(hit & ~o.dropped), "evicting a page with visible tokens"
+        o.slot[hit] = -1
+        o.pages.remove(p)
+        self.in_evict[p] = False
+
+    def _take_page(self, s: int) -> int:
+        if self.free:
+            p = self.free.popleft()
+        else:
+            p = self.evictable.popleft()
+            self._evict(p)
+        self.owner[p] = s
+        self.nvis[p] = 0
+        self.filled[p] = 0
+        self.seqs[s].pages.append(p)
+        return p
+
+    def _pages_needed(self, q: _Seq, n: int) -> int:
+        room = self.S - self.filled[q.tail] if q.tail >= 0 else 0
+        extra = max(0, n - room)
+        return (extra + self.S - 1) // self.S
+
+    def _place(self, s: int, n: int) -> np.ndarray:
+        """Slots for n new tokens: fill the open tail page, then fresh pages."""
+        q = self.seqs[s]
+        S = self.S
+        slots = np.empty(n, np.int64)
+        for i in range(n):
+            if q.tail < 0:
+                q.tail = self._take_page(s)
+            p = q.tail
+            slots[i] = p * S + self.filled[p]
+            self.filled[p] += 1
+            self.nvis[p] += 1
+            if self.filled[p] == S:
+                q.tail = -1
+        return slots
+
+    # -- append (a cache operation of [AKV-notes] section 1) ---------------------
+    def _check_kv(self, n: int, k, kpe, v):
+        L = self.L
+        k = np.asarray(k, np.float64)
+        v = np.asarray(v, np.float64)
+        if L.mla:
+            if kpe is None or k.shape != (n, L.n_kv_heads, L.d_nope):
+                raise EInval("bad K_nope / K_pe")
+            kpe = np.asarray(kpe, np.float64)
+            if kpe.shape != (n, L.n_rope_heads, L.d_rope):
+                raise EInval("bad K_pe shape")
+        else:
+            if kpe is not None or k.shape != (n, L.n_kv_heads, L.d_rope):
+                raise EInval("bad K shape")
+        if v.shape != (n, L.n_kv_heads, L.d_v):
+            raise EInval("bad V shape")
+        return k, kpe, v
+
+    def append(self, s: int, pos, k, kpe, v) -> None:
+        q = self._seq(s)
+        L = self.L
+        pos = np.asarray(pos, np.int64)
+        n = len(pos)
+        if n == 0:
+            return
+        if np.any(pos < 0) or np.any(pos > INT32_MAX):
+            raise ERange("position out of range")
+        k, kpe, v = self._check_kv(n, k, kpe, v)
+        if self._pages_needed(q, n) > self._available():
+            raise ENoMem("pool exhausted")
+        slots = self._place(s, n)
+        pg, off = slots // self.S, slots % self.S
+        if L.mla:
+            self.kn[pg, :, off, :] = k
+            self.kr[pg, :, off, :] = kpe
+        else:
+            self.kr[pg, :, off, :] = k
+        self.v[pg, :, off, :] = v
+        q.slot = np.concatenate([q.slot, slots])
+        q.pos = np.concatenate([q.pos, pos])
+        q.dropped = np.concatenate([q.dropped, np.zeros(n, bool)])
+        if self.keep_log:
+            q.log_k.append(k.copy())
+            q.log_kpe.append(None if kpe is None else np.asarray(kpe, np.float64).copy())
+            q.log_v.append(v.copy())
+            q.log_pos.append(pos.copy())
+
+    # -- drop ([AKV-blog] section 2, The Drop Primitive) -----------------------------
+    @staticmethod
+    def _check_spans(spans, n) -> np.ndarray:
+        sp = np.asarray(spans, np.int64).reshape(-1, 2)
+        for b, e in sp:
+            if b > e:
+                raise EInval("span with end before begin")
+            if b < 0 or e > n:
+                raise ERange("span outside the sequence")
+        return sp
+
+    def _drop_tokens(self, q: _Seq, tokens) -> None:
+        S = self.S
+        for t in tokens:
+            if q.dropped[t]:
+                continue
+            q.dropped[t] = True
+            p = q.slot[t] // S
+            self.nvis[p] -= 1
+            if self.nvis[p] == 0 and p != q.tail and not self.in_evict[p]:
+                self.evictable.append(p)
+                self.in_evict[p] = True
+
+    def drop(self, s: int, spans, auto_compact: bool = True) -> None:
+        """Mark logical spans [b, e) inactive.  Nothing is freed or rewritten;
+        pages left without a visible token join the evictable queue (in the
+        order their last visible token is dropped)."""
+        q = self._seq(s)
+        sp = self._check_spans(spans, q.n)
+        for b, e in sp:
+            self._drop_tokens(q, range(int(b), int(e)))
+        if auto_compact:
+            self._auto_compact(s)
+
+    # -- fragmentation and compaction ([AKV-blog] section 7, Dilemma 2) -----------------
+    def fragmentation(self, s: int) -> float:
+        """1 - visible tokens / written slots of the pages holding a visible token."""
+        q = self._seq(s)
+        ref = [p for p in q.pages if self.nvis[p] > 0]
+        cap = int(sum(self.filled[p] for p in ref))
+        if cap == 0:
+            return 0.0
+        return 1.0 - int(np.count_nonzero(~q.dropped)) / cap
+
+    def _auto_compact(self, s: int) -> None:
+        if self.fragmentation(s) > self.compact_threshold:
+            self.compact(s, force=True)
+
+    def compact(self, s: int, force: bool = True) -> None:
+        """Copy every visible token, in visible-list order, into fresh pages
+        taken from the allocator; the old pages join the evictable queue in
+        allocation order.  Values are copied unchanged."""
+        q = self._seq(s)
+        if not force and self.fragmentation(s) <= self.compact_threshold:
+            return
+        order = self.visible(s)
+        nv = len(order)
+        need = (nv + self.S - 1) // self.S
+        if need > self._available():
+            raise ENoMem("pool exhausted")
+        old_pages = list(q.pages)
+        dest = [self._take_page(s) for _ in range(need)]
+        S = self.S
+        src = q.slot[order]
+        sp, so = src // S, src % S
+        new = np.array([dest[i // S] * S + i % S for i in range(nv)], np.int64)
+        dp, do = new // S, new % S
+        self.kr[dp, :, do, :] = self.kr[sp, :, so, :]
+        if self.kn is not None:
+            self.kn[dp, :, do, :] = self.kn[sp, :, so, :]
+        self.v[dp, :, do, :] = self.v[sp, :, so, :]
+        q.slot[order] = new
+        for i, p in enumerate(dest):
+            c = min(S, nv - i * S)
+            self.filled[p] = c
+            self.nvis[p] = c
+        q.tail = dest[-1] if (need and nv % S) else -1
+        for p in old_pages:
+            if p in dest or self.owner[p] != s:
+                continue
+            self.nvis[p] = 0
+            if not self.in_evict[p]:
+                self.evictable.append(p)
+                self.in_evict[p] = True
+
+    # -- repos ([AKV-blog] section 2, The Repos Primitive; [Leyline] Method) -----
+    def repos_deltas(self, s: int, spans, deltas) -> np.ndarray:
+        """Per-token total delta: deltas of every span covering a retained
+        token add up; dropped tokens get 0 (they are never rotated)."""
+        q = self._seq(s)
+        sp = self._check_spans(spans, q.n)
+        dl = np.asarray(deltas, np.int64).reshape(-1)
+        if len(dl) != len(sp):
+            raise EInval("one delta per span")
+        tot = np.zeros(q.n, np.int64)
+        for (b, e), d in zip(sp, dl):
+            tot[b:e] += d
+        tot[q.dropped] = 0
+        newpos = q.pos + tot
+        if np.any(newpos < 0) or np.any(newpos > INT32_MAX):
+            raise ERange("repositioned position out of range")
+        return tot
+
+    def _rotate_tokens(self, q: _Seq, tokens: np.ndarray, delta: np.ndarray) -> None:
+        S = self.S
+        pg, off = q.slot[tokens] // S, q.slot[tokens] % S
+        cur = self.kr[pg, :, off, :]                        # [m, Hr, d_rope]
+        self.kr[pg, :, off, :] = rotate(cur, np.broadcast_to(delta[:, None], cur.shape[:2]),
+                                        self.inv_freq, self.L.pairing)
+
+    def repos(self, s: int, spans, deltas) -> None:
+        q = self._seq(s)
+        tot = self.repos_deltas(s, spans, deltas)
+        t = np.nonzero(tot)[0]
+        if len(t):
+            self._rotate_tokens(q, t, tot[t])
+            q.pos[t] += tot[t]
+
+    # -- splice ([Leyline] Method, AMORTIZE mode) ---------------------------------------
+    def splice_plan(self, s: int, spans, stub_lens):
+        """Validate a batch of splices given in visible-list coordinates and
+        return (visible list, per-splice delta, stub positions, per-visible-
+        entry downstream delta)."""
+        q = self._seq(s)
+        vis = self.visible(s)
+        H = len(vis)
+        sp = np.asarray(spans, np.int64).reshape(-1, 2)
+        st = np.asarray(stub_lens, np.int64).reshape(-1)
+        if len(st) != len(sp):
+            raise EInval("one stub length per splice")
+        prev_e = 0
+        for j, (b, e) in enumerate(sp):
+            if b >= e or st[j] < 0:
+                raise EInval("empty splice span or negative stub")
+            if b < 0 or e > H:
+                raise ERange("splice span outside the visible list")
+            if j and b < prev_e:
+                raise EInval("splice spans must be sorted and disjoint")
+            prev_e = e
+        dj = st - (sp[:, 1] - sp[:, 0])                     # delta = |R| - (s_end - s_start)
+        down = np.zeros(H, np.int64)
+        for (b, e), d in zip(sp, dj):
+            down[e:] += d
+        stub_pos = []
+        for j, (b, e) in enumerate(sp):
+            p0 = q.pos[vis[b]] + int(dj[:j].sum())
+            stub_pos.append(np.arange(p0, p0 + st[j], dtype=np.int64))
+        stub_pos = np.concatenate(stub_pos) if stub_pos else np.zeros(0, np.int64)
+        newpos = q.pos[vis] + down
+        if np.any(newpos < 0) or np.any(newpos > INT32_MAX) or np.any(stub_pos < 0) or np.any(stub_pos > INT32_MAX):
+            raise ERange("splice moves a position out of range")
+        return vis, dj, stub_pos, down
+
+    def splice(self, s: int, spans, stub_lens, k, kpe, v) -> np.ndarray:
+        """Drop each span, append its stub at the span's start position, and
+        move every downstream visible token by the summed deltas of the
+        splices before it (one rotation per token).  Returns stub positions."""
+        q = self._seq(s)
+        vis, dj, stub_pos, down = self.splice_plan(s, spans, stub_lens)
+        sp = np.asarray(spans, np.int64).reshape(-1, 2)
+        n_stub = len(stub_pos)
+        self._check_kv(n_stub, k, kpe, v)
+        # stub pages must be available once the spans are dropped (dropped pages
+        # may be evicted for the stub): count before mutating anything
+        drop_tokens = np.concatenate([vis[b:e] for b, e in sp]) if len(sp) else np.zeros(0, np.int64)
+        freed = self._evictable_after_drop(q, drop_tokens)
+        if self._pages_needed(q, n_stub) > self._available() + freed:
+            raise ENoMem("pool exhausted")
+        self._drop_tokens(q, drop_tokens)
+        if n_stub:
+            self.append(s, stub_pos, k, kpe, v)
+        moved = np.nonzero(down)[0]
+        keep = np.ones(len(vis), bool)
+        keep[np.isin(vis, drop_tokens)] = False
+        moved = moved[keep[moved]]
+        if len(moved):
+            t = vis[moved]
+            self._rotate_tokens(q, t, down[moved])
+            q.pos[t] += down[moved]
+        self._auto_compact(s)
+        return stub_pos
+
+    def _evictable_after_drop(self, q: _Seq, tokens) -> int:
+        nv = self.nvis.copy()
+        cnt = 0
+        seen = set()
+        for t in tokens:
+            if q.dropped[t] or t in seen:
+                continue
+            seen.add(t)
+            p = q.slot[t] // self.S
+            nv[p] -= 1
+            if nv[p] == 0 and p != q.tail and not self.in_evict[p]:
+                cnt += 1
+        return cnt
+
+    # -- visibility ------------------------------------------------------------------
+    def visible(self, s: int, mask_spans=None) -> np.ndarray:
+        """Retained tokens (minus optional per-segment mask spans), ordered by
+        (position, logical index)."""
+        q = self._seq(s)
+        keep = ~q.dropped.copy()
+        if mask_spans is not None:
+            for b, e in self._check_spans(mask_spans, q.n):
+                keep[b:e] = False
+        t = np.nonzero(keep)[0]
+        order = np.lexsort((t, q.pos[t]))
+        return t[order]
+
+    def extents(self, s: int, mask_spans=None) -> np.ndarray:
+        """Page-table image of the visible list: maximal runs (page, lo, hi) of
+        consecutive offsets of one page, in list order."""
+        q = self.seqs[s]
+        vis = self.visible(s, mask_spans)
+        out = []
+        S = self.S
+        for t in vis:
+            p, o = int(q.slot[t] // S), int(q.slot[t] % S)
+            if out and out[-1][0] == p and out[-1][2] == o:
+                out[-1][2] = o + 1
+            else:
+                out.append([p, o, o + 1])
+        return np.asarray(out, np.int64).reshape(-1, 3)
+
+    # -- gathers -----------------------------------------------------------------------
+    def gather(self, extents):
+        """K (d_qk = d_nope + d_rope per head) and V rows of an extent list,
+        in list order: K [L, Hkv, d_qk], V [L, Hkv, d_v]."""
+        L = self.L
+        ex = np.asarray(extents, np.int64).reshape(-1, 3)
+        pg = np.concatenate([np.full(h - l, p) for p, l, h in ex]) if len(ex) else np.zeros(0, np.int64)
+        of = np.concatenate([np.arange(l, h) for p, l, h in ex]) if len(ex) else np.zeros(0, np.int64)
+        kr = self.kr[pg, :, of, :]
+        if L.mla:
+            kn = self.kn[pg, :, of, :]
+            kr = np.broadcast_to(kr, (len(pg), L.n_kv_heads, L.d_rope))
+            k = np.concatenate([kn, kr], axis=-1)
+        else:
+            k = kr
+        return k, self.v[pg, :, of, :]
+
+
+# ---------------------------------------------------------------------------
+# segment-batch attention ([AKV-notes] section 3; [AKV-blog] section 4)
+# ---------------------------------------------------------------------------
+def check_extents(pool: Pool, extents) -> np.ndarray:
+    ex = np.asarray(extents, np.int64).reshape(-1, 3)
+    for p, lo, hi in ex:
+        if not (0 <= p < pool.L.num_pages) or not (0 <= lo < hi <= pool.S):
+            raise ERange("extent outside the pool")
+    return ex
+
+
+def last_visible(lkv: int, lq: int, i: np.ndarray) -> np.ndarray:
+    """Last list index query i may attend to: the segment's own Lq entries are
+    the tail of its list, so causality is bottom-right over list order."""
+    return lkv - lq + i
+
+
+def segment_attention(pool: Pool, q: np.ndarray, segments, page_lists, scale: float = 0.0,
+                      rows: Optional[dict] = None) -> np.ndarray:
+    """Causal attention of each query segment over its own KV list.
+
+    q: [Nq, Hq, d_qk] fp64.  segments: iterable of (q_begin, q_len, ext_begin,
+    ext_len).  page_lists: [n_ext, 3] extents.  Query i of a segment with Lq
+    queries and Lkv list entries sees list entries 0 .. Lkv - Lq + i.  Query
+    head h reads kv head floor(h * Hkv / Hq).  Returns [Nq, Hq, d_v] with NaN
+    in rows no segment covers.  `rows` optionally maps a segment index to the
+    local query rows to evaluate (sampling)."""
+    L = pool.L
+    q = np.asarray(q, np.float64)
+    nq = q.shape[0]
+    if scale == 0.0:
+        scale = 1.0 / np.sqrt(L.d_qk)
+    ex_all = check_extents(pool, page_lists)
+    out = np.full((nq, L.n_q_heads, L.d_v), np.nan)
+    grp = L.n_q_heads // L.n_kv_heads
+    for si, (qb, ql, eb, el) in enumerate(segments):
+        if ql == 0:
+            continue
+        k, v = pool.gather(ex_all[eb:eb + el])
+        lkv = k.shape[0]
+        if lkv < ql:
+            raise EInval("segment has fewer KV entries than queries")
+        loc = np.arange(ql) if rows is None or si not in rows else np.asarray(rows[si])
+        lim = last_visible(lkv, ql, loc)
+        for h in range(L.n_q_heads):
+            g = h // grp
+            s = (q[qb + loc, h, :] @ k[:, g, :].T) * scale
+            s[np.arange(lkv)[None, :] > lim[:, None]] = -np.inf
+            s -= s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            out[qb + loc, h, :] = p @ v[:, g, :]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# dense brute force: the masked-softmax definition of [AKV-blog] section 2
+# ---------------------------------------------------------------------------
+def _rope_complex(x: np.ndarray, delta: np.ndarray, inv_freq: np.ndarray, pairing: int) -> np.ndarray:
+    """Rotation written as complex multiplication: pair (a, b) -> a + ib,
+    times exp(i * delta * theta_i).  A second formulation of the rotation, so
+    the brute force does not reuse `rotate`."""
+    d = x.shape[-1]
+    if pairing == 0:
+        z = x[..., 0::2] + 1j * x[..., 1::2]
+    else:
+        z = x[..., : d // 2] + 1j * x[..., d // 2:]
+    z = z * np.exp(1j * np.asarray(delta, np.float64)[..., None] * inv_freq)
+    out = np.empty_like(x)
+    if pairing == 0:
+        out[..., 0::2], out[..., 1::2] = z.real, z.imag
+    else:
+        out[..., : d // 2], out[..., d // 2:] = z.real, z.imag
+    return out
+
+
+def dense_masked_attention(pool: Pool, q: np.ndarray, seg_seq: int, q_rows, q_pos,
+                           mask_spans=None, scale: float = 0.0) -> np.ndarray:
+    """softmax(Q K^T * scale + M) V over every token ever appended to any
+    sequence of the pool, with M = 0 where the key belongs to the query's
+    sequence, is not dropped, is not hidden by the segment's mask spans and
+    has position <= the query's position, and M = -inf elsewhere.
+
+    Key values come from the append log and are moved to their current
+    position by complex rotation by (current position - appended position);
+    the pool's pages, extents and repos code are not used.  Needs keep_log."""
+    L = pool.L
+    assert pool.keep_log, "dense_masked_attention needs Pool(keep_log=True)"
+    if scale == 0.0:
+        scale = 1.0 / np.sqrt(L.d_qk)
+    ks, vs, allowed_parts = [], [], []
+    for si, sq in enumerate(pool.seqs):
+        if not sq.log_pos:
+            continue
+        pos0 = np.concatenate(sq.log_pos)
+        shift = sq.pos - pos0
+        if L.mla:
+            kn = np.concatenate(sq.log_k)
+            kpe = _rope_complex(np.concatenate(sq.log_kpe), shift[:, None], pool.inv_freq, L.pairing)
+            kpe = np.broadcast_to(kpe, (len(pos0), L.n_kv_heads, L.d_rope))
+            k = np.concatenate([kn, kpe], axis=-1)
+        else:
+            k = _rope_complex(np.concatenate(sq.log_k), shift[:, None], pool.inv_freq, L.pairing)
+        ks.append(k)
+        vs.append(np.concatenate(sq.log_v))
+        ok = np.zeros(len(pos0), bool)
+        if si == seg_seq and sq.alive:
+            ok = ~sq.dropped.copy()
+            if mask_spans is not None:
+                for b, e in np.asarray(mask_spans, np.int64).reshape(-1, 2):
+                    ok[b:e] = False
+        allowed_parts.append((ok, sq.pos.copy()))
+    K = np.concatenate(ks)
+    V = np.concatenate(vs)
+    ok = np.concatenate([a for a, _ in allowed_parts])
+    kpos = np.concatenate([p for _, p in allowed_parts])
+    q = np.asarray(q, np.float64)
+    q_rows = np.asarray(q_rows)
+    q_pos = np.asarray(q_pos, np.int64)
+    grp = L.n_q_heads // L.n_kv_heads
+    out = np.zeros((len(q_rows), L.n_q_heads, L.d_v))
+    M = np.where(ok[None, :] & (kpos[None, :] <= q_pos[:, None]), 0.0, -np.inf)
+    for h in range(L.n_q_heads):
+        g = h // grp
+        s = (q[q_rows, h, :] @ K[:, g, :].T) * scale + M
+        s -= s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        out[:, h, :] = (p / p.sum(axis=1, keepdims=True)) @ V[:, g, :]
+    return out

@@ -1,0 +1,78 @@
+"""Execute a `workloads` script on the fp64 oracle.
+
+TEST INFRASTRUCTURE ONLY (see akv_oracle's header).  Every operation is the
+oracle's own; this file only walks the script and records what the tests
+compare: the page-table image of every segment list, the per-token positions,
+and the attention outputs.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+
+import workloads as W
+from . import akv_oracle as AO
+from .akv_oracle import Pool
+
+
+@dataclass
+class OracleRun:
+    pool: Pool
+    attention: List[dict] = field(default_factory=list)   # one record per Attention op
+    splice_positions: List[np.ndarray] = field(default_factory=list)
+
+
+def _f64(u):
+    return None if u is None else W.bf16_to_f64(u)
+
+
+def apply_op(pool: Pool, op) -> Optional[np.ndarray]:
+    if isinstance(op, W.SeqCreate):
+        pool.seq_create()
+    elif isinstance(op, W.Append):
+        pool.append(op.seq, op.pos, _f64(op.k), _f64(op.kpe), _f64(op.v))
+    elif isinstance(op, W.Drop):
+        pool.drop(op.seq, op.spans)
+    elif isinstance(op, W.Repos):
+        pool.repos(op.seq, op.spans, op.deltas)
+    elif isinstance(op, W.Splice):
+        return pool.splice(op.seq, op.spans, op.stub_lens, _f64(op.k), _f64(op.kpe), _f64(op.v))
+    elif isinstance(op, W.Compact):
+        pool.compact(op.seq, bool(op.force))
+    else:
+        raise TypeError(op)
+    return None
+
+
+def segment_lists(pool: Pool, segments):
+    """Concatenated extents and (q_begin, q_len, ext_begin, ext_len) rows."""
+    exts, rows, eb = [], [], 0
+    for sg in segments:
+        ex = pool.extents(sg.seq, sg.mask_spans if len(sg.mask_spans) else None)
+        exts.append(ex)
+        rows.append((sg.q_begin, sg.q_len, eb, len(ex)))
+        eb += len(ex)
+    ex = np.concatenate(exts) if exts else np.zeros((0, 3), np.int64)
+    return ex, rows
+
+
+def run_workload(wl: W.Workload, keep_log: bool = False, attention: bool = True,
+        sample_rows: Optional[Dict[int, np.ndarray]] = None, stop_before_attention: bool = False) -> OracleRun:
+    pool = Pool(wl.layout, wl.page_order, keep_log=keep_log)
+    res = OracleRun(pool)
+    for op in wl.ops:
+        if isinstance(op, W.Attention):
+            if stop_before_attention:
+                break
+            ex, rows = segment_lists(pool, op.segments)
+            rec = dict(extents=ex, segments=rows)
+            if attention:
+                rec["out"] = AO.segment_attention(pool, W.bf16_to_f64(op.q), rows, ex, op.scale, rows=sample_rows)
+            res.attention.append(rec)
+        else:
+            sp = apply_op(pool, op)
+            if sp is not None:
+                res.splice_positions.append(sp)
+    return res

@@ -1,0 +1,540 @@
+"""Seeded synthetic workloads for AKV cache engineering (drop / repos / splice /
+segment-batch attention).
+
+This module is shared by both sides of every parity check: the fp64 oracle
+(`oracle/`) and the HIP path (`kv_cache_drop_amd`).  It therefore holds none of
+the method's arithmetic: no rotation, no attention, no visibility logic.  It
+only draws seeded random numbers, lays out token spans, and encodes float32
+values as bfloat16 bit patterns through torch's round-to-nearest-even cast.
+
+Every workload is a *script*: a layout, an initial free-page order, and a list
+of operations (create a sequence, append tokens, drop spans, reposition spans,
+splice, compact, run segment-batch attention).  Each side executes the same
+script with its own code.
+
+The shapes follow the agent traces described on the source pages:
+
+* "AKV: Cache Engineering for Autonomous Agents and State-Preserving Prefix
+  Invalidation Bypass" (A. Akhunji), section 1 (a 40-step agent trajectory
+  grows past 64K tokens) and section 2 (block-paged KV, 16-token blocks in the
+  drop/repos figure).
+* "Cache Engineering for Agents" (reading notes on Fu et al.), section 2
+  (keep all reasoning and recent tool responses, drop older tool responses).
+* "Leyline: KV Cache Directives for Agentic Inference" (paper digest), Method
+  and Results (span-replacement directives on ~17K-token MLA prompts).
+
+Raw keys are drawn N(0, 1) and stored without applying RoPE: a RoPE rotation
+of an isotropic Gaussian pair is again an isotropic Gaussian pair, so these
+values are distributed exactly like keys already rotated to their positions.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "Layout", "SeqCreate", "Append", "Drop", "Repos", "Splice", "Compact",
+    "Segment", "Attention", "Workload", "to_bf16", "bf16_to_f64",
+    "c1_tiny", "c2_64k", "c3_mla", "c4_batched", "c5_128k", "fuzz_small",
+    "CONFIGS", "make",
+]
+
+
+# --------------------------------------------------------------------------
+# bf16 encoding (torch's RNE cast; uint16 bit patterns in numpy)
+# --------------------------------------------------------------------------
+def to_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 array -> uint16 bf16 bit patterns (round to nearest even)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_to_f64(u: np.ndarray) -> np.ndarray:
+    """uint16 bf16 bit patterns -> float64 (exact)."""
+    u32 = np.asarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# script types
+# --------------------------------------------------------------------------
+@dataclass
+class Layout:
+    n_q_heads: int
+    n_kv_heads: int
+    d_nope: int          # 0 for GQA; per-head position-free key part for MLA
+    d_rope: int          # rotated key dims (all of K for GQA, K_pe for MLA)
+    d_v: int
+    page_size: int
+    num_pages: int
+    kpe_per_head: int = 0   # MLA: 0 = one K_pe row per token shared by all heads
+    pairing: int = 0        # 0 = interleaved pairs (2i, 2i+1); 1 = half-split (i, i+d/2)
+    rope_theta: float = 10000.0
+
+    @property
+    def d_qk(self) -> int:
+        return self.d_nope + self.d_rope
+
+    @property
+    def mla(self) -> bool:
+        return self.d_nope > 0
+
+    @property
+    def n_rope_heads(self) -> int:
+        """Heads stored in the rotated-key array."""
+        if self.mla and not self.kpe_per_head:
+            return 1
+        return self.n_kv_heads
+
+
+@dataclass
+class SeqCreate:
+    pass                 # sequence ids are 0, 1, 2, ... in creation order
+
+
+@dataclass
+class Append:
+    seq: int
+    pos: np.ndarray      # int32 [n]
+    k: np.ndarray        # uint16 bf16: GQA full K [n,Hkv,d_rope]; MLA K_nope [n,Hkv,d_nope]
+    kpe: Optional[np.ndarray]  # MLA only: [n, n_rope_heads, d_rope]
+    v: np.ndarray        # uint16 bf16 [n, Hkv, d_v]
+
+
+@dataclass
+class Drop:
+    seq: int
+    spans: np.ndarray    # int32 [m, 2], half-open logical-index spans
+
+
+@dataclass
+class Repos:
+    seq: int
+    spans: np.ndarray    # int32 [m, 2]
+    deltas: np.ndarray   # int32 [m]
+
+
+@dataclass
+class Splice:
+    seq: int
+    spans: np.ndarray    # int32 [m, 2] in visible-list coordinates, sorted, disjoint
+    stub_lens: np.ndarray  # int32 [m]
+    k: np.ndarray        # stub keys, concatenated over splices (same layout as Append.k)
+    kpe: Optional[np.ndarray]
+    v: np.ndarray
+
+
+@dataclass
+class Compact:
+    seq: int
+    force: int = 1
+
+
+@dataclass
+class Segment:
+    seq: int
+    q_begin: int
+    q_len: int
+    mask_spans: np.ndarray   # int32 [m, 2] logical spans hidden from this segment only
+
+
+@dataclass
+class Attention:
+    q: np.ndarray            # uint16 bf16 [Nq, Hq, d_qk]
+    segments: List[Segment]
+    scale: float = 0.0       # 0 => 1/sqrt(d_qk)
+
+
+@dataclass
+class Workload:
+    name: str
+    layout: Layout
+    page_order: np.ndarray   # int32 [num_pages], initial free-list order
+    ops: list = field(default_factory=list)
+    notes: dict = field(default_factory=dict)
+
+
+# --------------------------------------------------------------------------
+# helpers
+# --------------------------------------------------------------------------
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _normal_bf16(rng, shape, scale=1.0) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    return to_bf16(x)
+
+
+def _append_op(rng, lay: Layout, seq: int, pos: np.ndarray) -> Append:
+    n = int(len(pos))
+    if lay.mla:
+        k = _normal_bf16(rng, (n, lay.n_kv_heads, lay.d_nope))
+        kpe = _normal_bf16(rng, (n, lay.n_rope_heads, lay.d_rope))
+    else:
+        k = _normal_bf16(rng, (n, lay.n_kv_heads, lay.d_rope))
+        kpe = None
+    v = _normal_bf16(rng, (n, lay.n_kv_heads, lay.d_v))
+    return Append(seq, np.asarray(pos, dtype=np.int32), k, kpe, v)
+
+
+def _loguniform(rng, lo, hi, n) -> np.ndarray:
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), n))
+
+
+def _rescale_int(weights: np.ndarray, total: int) -> np.ndarray:
+    """Integer lengths proportional to `weights` that sum exactly to `total`
+    (largest-remainder rounding)."""
+    x = weights / weights.sum() * total
+    out = np.floor(x).astype(np.int64)
+    rem = int(total - out.sum())
+    order = np.argsort(-(x - out), kind="stable")
+    out[order[:rem]] += 1
+    return out
+
+
+def _spans(pairs) -> np.ndarray:
+    a = np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
+    return a
+
+
+def _survivor_runs(n: int, dropped: Sequence[Tuple[int, int]]):
+    """For sorted disjoint dropped spans, return (spans, deltas) of the kept
+    runs that follow each dropped span, with delta = -(tokens dropped before
+    the run).  Runs before the first dropped span keep delta 0 and are not
+    listed."""
+    spans, deltas = [], []
+    gone = 0
+    for j, (b, e) in enumerate(dropped):
+        gone += e - b
+        nxt = dropped[j + 1][0] if j + 1 < len(dropped) else n
+        if nxt > e:
+            spans.append((e, nxt))
+            deltas.append(-gone)
+    return _spans(spans), np.asarray(deltas, dtype=np.int32)
+
+
+def _query_segments(seq, hist_end_logical, q_row0, seg_lens, masks_per_seg):
+    """Segments over freshly appended query tokens.  Segment k sees the history
+    minus its own mask spans plus the new tokens of segments 0..k; the new
+    tokens of later segments are hidden with one more mask span."""
+    segs = []
+    total = int(sum(seg_lens))
+    off = 0
+    for k, L in enumerate(seg_lens):
+        m = list(masks_per_seg[k])
+        later_b = hist_end_logical + off + L
+        later_e = hist_end_logical + total
+        if later_e > later_b:
+            m.append((later_b, later_e))
+        segs.append(Segment(seq, q_row0 + off, int(L), _spans(m) if m else np.zeros((0, 2), np.int32)))
+        off += L
+    return segs
+
+
+# --------------------------------------------------------------------------
+# config 1: tiny single request (GQA 8/2, d 64)
+# --------------------------------------------------------------------------
+def c1_tiny(seed: int = 0, variant: str = "canonical") -> Workload:
+    """2048 cached tokens; drop 256 + 384 tokens, reposition the suffix by a
+    total of -640, append 256 query tokens as two 128-token segments.
+
+    variant "canonical":  drop [1024,1280) and [1280,1664); repos [1664,2048) by -640.
+    variant "cumulative": drop [512,768) and [1280,1664); repos [768,1280) by -256
+                          and [1664,2048) by -640.
+    variant "unaligned":  the canonical spans shifted by +5 tokens.
+    """
+    rng = _rng(seed)
+    lay = Layout(8, 2, 0, 64, 64, 16, 144, rope_theta=10000.0)
+    n = 2048
+    if variant == "canonical":
+        drop = [(1024, 1280), (1280, 1664)]
+        rep_s, rep_d = _spans([(1664, 2048)]), np.array([-640], np.int32)
+    elif variant == "cumulative":
+        drop = [(512, 768), (1280, 1664)]
+        rep_s, rep_d = _spans([(768, 1280), (1664, 2048)]), np.array([-256, -640], np.int32)
+    elif variant == "unaligned":
+        drop = [(1029, 1285), (1285, 1669)]
+        rep_s, rep_d = _spans([(1669, 2048)]), np.array([-640], np.int32)
+    else:
+        raise ValueError(variant)
+    h = n - sum(e - b for b, e in drop)           # 1408 visible
+    wl = Workload(f"c1_tiny_{variant}", lay, rng.permutation(lay.num_pages).astype(np.int32))
+    wl.ops.append(SeqCreate())
+    wl.ops.append(_append_op(rng, lay, 0, np.arange(n, dtype=np.int32)))
+    wl.ops.append(Drop(0, _spans(drop)))
+    wl.ops.append(Repos(0, rep_s, rep_d))
+    wl.ops.append(_append_op(rng, lay, 0, np.arange(h, h + 256, dtype=np.int32)))
+    q = _normal_bf16(rng, (256, lay.n_q_heads, lay.d_qk), scale=1.0 / 8.0)
+    segs = _query_segments(0, n, 0, [128, 128], [[], [(250, 390)]])
+    wl.ops.append(Attention(q, segs))
+    wl.notes.update(history=h, repositioned=int(sum(e - b for b, e in rep_s)))
+    return wl
+
+
+# --------------------------------------------------------------------------
+# config 2: Llama-3.1-8B-shaped layer, 64K tokens in 40 agent turns
+# --------------------------------------------------------------------------
+def _c2_like_history(rng, n_turns=40, n_recent=8, total=65536, drop_frac=0.40, reasoning=512):
+    """Turn lengths for a 40-turn trace of exactly `total` tokens: each turn is
+    `reasoning` tokens then a tool response.  Log-uniform[256, 8192] tool
+    lengths are rescaled per group so the older tools hold drop_frac of the
+    tokens (they are the ones dropped) and the recent tools hold the rest."""
+    old = n_turns - n_recent
+    old_total = int(round(drop_frac * total))
+    recent_total = total - n_turns * reasoning - old_total
+    t_old = _rescale_int(_loguniform(rng, 256, 8192, old), old_total)
+    t_new = _rescale_int(_loguniform(rng, 256, 8192, n_recent), recent_total)
+    tools = np.concatenate([t_old, t_new])
+    spans_tool, cur = [], 0
+    for t in tools:
+        cur += reasoning
+        spans_tool.append((cur, cur + int(t)))
+        cur += int(t)
+    assert cur == total
+    return spans_tool
+
+
+def c2_64k(seed: int = 0, num_pages: Optional[int] = None) -> Workload:
+    rng = _rng(seed)
+    n = 65536
+    nq = 2048
+    pages = num_pages if num_pages is not None else (n + nq) // 16
+    lay = Layout(32, 8, 0, 128, 128, 16, pages, rope_theta=500000.0)
+    tools = _c2_like_history(rng)
+    dropped = tools[:32]
+    rep_s, rep_d = _survivor_runs(n, dropped)
+    h = n - sum(e - b for b, e in dropped)
+    wl = Workload("c2_64k", lay, rng.permutation(lay.num_pages).astype(np.int32))
+    wl.ops.append(SeqCreate())
+    wl.ops.append(_append_op(rng, lay, 0, np.arange(n, dtype=np.int32)))
+    wl.ops.append(Drop(0, _spans(dropped)))
+    wl.ops.append(Repos(0, rep_s, rep_d))
+    wl.ops.append(_append_op(rng, lay, 0, np.arange(h, h + nq, dtype=np.int32)))
+    q = _normal_bf16(rng, (nq, lay.n_q_heads, lay.d_qk), scale=1.0 / 8.0)
+    masks = [[tools[32 + j] for j in range(k)] for k in range(4)]
+    wl.ops.append(Attention(q, _query_segments(0, n, 0, [512] * 4, masks)))
+    wl.notes.update(history=h, repositioned=int(sum(e - b for b, e in rep_s)),
+                    tool_spans=tools, dropped_spans=dropped)
+    return wl
+
+
+# --------------------------------------------------------------------------
+# config 3: MLA-shaped layer (DeepSeek-V2-Lite-like), Leyline splices
+# --------------------------------------------------------------------------
+def _place_disjoint(rng, n, lens, max_tries=10000):
+    """Uniform placement of spans with the given lengths inside [0, n) without
+    overlap (rejection sampling); returned sorted by start."""
+    for _ in range(max_tries):
+        starts = [int(rng.integers(0, n - L + 1)) for L in lens]
+        sp = sorted(zip(starts, [s + L for s, L in zip(starts, lens)]))
+        if all(sp[i][1] <= sp[i + 1][0] for i in range(len(sp) - 1)):
+            return sp
+    raise RuntimeError("could not place spans")
+
+
+def c3_mla(seed: int = 0) -> Workload:
+    rng = _rng(seed)
+    n = 17408
+    nq = 512
+    lay = Layout(16, 16, 128, 64, 128, 64, 288, kpe_per_head=0, rope_theta=10000.0)
+    m = int(rng.integers(1, 4))
+    lens = [int(rng.integers(500, 4001)) for _ in range(m)]
+    spans = _place_disjoint(rng, n, lens)
+    stub = np.array([int(rng.integers(8, 33)) for _ in range(m)], np.int32)
+    wl = Workload("c3_mla", lay, rng.permutation(lay.num_pages).astype(np.int32))
+    wl.ops.append(SeqCreate())
+    wl.ops.append(_append_op(rng, lay, 0, np.arange(n, dtype=np.int32)))
+    ns = int(stub.sum())
+    a = _append_op(rng, lay, 0, np.zeros(ns, np.int32))
+    wl.ops.append(Splice(0, _spans(spans), stub, a.k, a.kpe, a.v))
+    h = n - sum(e - b for b, e in spans) + ns
+    wl.ops.append(_append_op(rng, lay, 0, np.arange(h, h + nq, dtype=np.int32)))
+    q = _normal_bf16(rng, (nq, lay.n_q_heads, lay.d_qk), scale=1.0 / 8.0)
+    wl.ops.append(Attention(q, _query_segments(0, n + ns, 0, [nq], [[]])))
+    wl.notes.update(history=h, splices=spans, stub_lens=stub.tolist())
+    return wl
+
+
+# --------------------------------------------------------------------------
+# config 4: 16 concurrent requests on the config-2 layer shape
+# --------------------------------------------------------------------------
+def c4_batched(seed: int = 0, n_req: int = 16, ctx_lo: int = 8192, ctx_hi: int = 32768) -> Workload:
+    rng = _rng(seed)
+    reqs = []
+    for r in range(n_req):
+        ctx = int(rng.integers(ctx_lo, ctx_hi + 1))
+        tools, cur = [], 0
+        while cur < ctx:
+            cur = min(cur + 512, ctx)
+            if cur >= ctx:
+                break
+            t = int(_loguniform(rng, 256, 8192, 1)[0])
+            tools.append((cur, min(cur + t, ctx)))
+            cur = min(cur + t, ctx)
+        f = float(rng.uniform(0.10, 0.60))
+        cand = list(range(max(0, len(tools) - 2)))      # the last two tool spans are recent
+        rng.shuffle(cand)
+        gone, chosen = 0, []
+        for i in cand:
+            if gone >= f * ctx:
+                break
+            chosen.append(i)
+            gone += tools[i][1] - tools[i][0]
+        chosen.sort()
+        dropped = [tools[i] for i in chosen]
+        keep_tools = [tools[i] for i in range(len(tools)) if i not in set(chosen)]
+        n_seg = int(rng.integers(1, 5))
+        qtot = int(rng.integers(256, 1025))
+        cuts = np.sort(rng.choice(np.arange(1, qtot), size=n_seg - 1, replace=False)) if n_seg > 1 else np.array([], int)
+        bounds = [0] + [int(c) for c in cuts] + [qtot]
+        seg_lens = [bounds[i + 1] - bounds[i] for i in range(n_seg)]
+        reqs.append(dict(ctx=ctx, tools=tools, dropped=dropped, keep_tools=keep_tools,
+                         seg_lens=seg_lens, qtot=qtot))
+    pages = sum((q["ctx"] + q["qtot"] + 15) // 16 for q in reqs) + 16
+    lay = Layout(32, 8, 0, 128, 128, 16, pages, rope_theta=500000.0)
+    wl = Workload("c4_batched", lay, rng.permutation(pages).astype(np.int32))
+    for r in range(n_req):
+        wl.ops.append(SeqCreate())
+    for r, q in enumerate(reqs):            # histories, interleaved in the shared pool
+        wl.ops.append(_append_op(rng, lay, r, np.arange(q["ctx"], dtype=np.int32)))
+    for r, q in enumerate(reqs):
+        if q["dropped"]:
+            wl.ops.append(Drop(r, _spans(q["dropped"])))
+            rs, rd = _survivor_runs(q["ctx"], q["dropped"])
+            if len(rs):
+                wl.ops.append(Repos(r, rs, rd))
+    segs, row = [], 0
+    for r, q in enumerate(reqs):
+        h = q["ctx"] - sum(e - b for b, e in q["dropped"])
+        wl.ops.append(_append_op(rng, lay, r, np.arange(h, h + q["qtot"], dtype=np.int32)))
+        kt = q["keep_tools"]
+        masks = [[kt[j] for j in range(min(k, len(kt)))] for k in range(len(q["seg_lens"]))]
+        segs += _query_segments(r, q["ctx"], row, q["seg_lens"], masks)
+        row += q["qtot"]
+    qarr = _normal_bf16(rng, (row, lay.n_q_heads, lay.d_qk), scale=1.0 / 8.0)
+    wl.ops.append(Attention(qarr, segs))
+    wl.notes.update(requests=reqs)
+    return wl
+
+
+# --------------------------------------------------------------------------
+# config 5: Llama-3.1-70B-shaped layer on one GPU, 128K tokens
+# --------------------------------------------------------------------------
+def c5_128k(seed: int = 0) -> Workload:
+    rng = _rng(seed)
+    n = 131072
+    nq = 4096
+    lay = Layout(64, 8, 0, 128, 128, 16, (n + nq) // 16, rope_theta=500000.0)
+    keep = _rescale_int(_loguniform(rng, 256, 8192, 61), 39322)
+    drop = _rescale_int(_loguniform(rng, 256, 8192, 60), n - 39322)
+    runs_keep, dropped, cur = [], [], 0
+    for j in range(61):
+        runs_keep.append((cur, cur + int(keep[j])))
+        cur += int(keep[j])
+        if j < 60:
+            dropped.append((cur, cur + int(drop[j])))
+            cur += int(drop[j])
+    assert cur == n
+    rep_s, rep_d = _survivor_runs(n, dropped)
+    h = 39322
+    wl = Workload("c5_128k", lay, rng.permutation(lay.num_pages).astype(np.int32))
+    wl.ops.append(SeqCreate())
+    wl.ops.append(_append_op(rng, lay, 0, np.arange(n, dtype=np.int32)))
+    wl.ops.append(Drop(0, _spans(dropped)))
+    wl.ops.append(Repos(0, rep_s, rep_d))
+    wl.ops.append(_append_op(rng, lay, 0, np.arange(h, h + nq, dtype=np.int32)))
+    q = _normal_bf16(rng, (nq, lay.n_q_heads, lay.d_qk), scale=1.0 / 8.0)
+    masks = [[runs_keep[1 + j] for j in range(k)] for k in range(8)]
+    wl.ops.append(Attention(q, _query_segments(0, n, 0, [512] * 8, masks)))
+    wl.notes.update(history=h, repositioned=int(sum(e - b for b, e in rep_s)))
+    return wl
+
+
+# --------------------------------------------------------------------------
+# small random scripts (fuzz): overlapping spans, either sign of delta,
+# splices, forced compaction, several sequences, ragged pages
+# --------------------------------------------------------------------------
+def fuzz_small(seed: int, mla: bool = False, pairing: int = 0, n_seqs: int = 2,
+               max_tokens: int = 300, page_size: int = 16, n_rounds: int = 3,
+               compact: bool = True, kpe_per_head: int = 0) -> Workload:
+    rng = _rng(seed)
+    if mla:
+        lay = Layout(4, 4, 32, 16, 32, page_size, 0, kpe_per_head=kpe_per_head,
+                     pairing=pairing, rope_theta=10000.0)
+    else:
+        hkv = int(rng.choice([1, 2]))
+        g = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([16, 32, 64]))
+        lay = Layout(hkv * g, hkv, 0, d, d, page_size, 0, pairing=pairing, rope_theta=10000.0)
+    ops = []
+    ntok = [0] * n_seqs
+    npos = [200] * n_seqs          # room below: repos deltas here never push a position under 0
+    total_tokens = 0
+    for s in range(n_seqs):
+        ops.append(SeqCreate())
+    for rnd in range(n_rounds):
+        for s in range(n_seqs):
+            n = int(rng.integers(1, max_tokens // n_rounds + 2))
+            ops.append(_append_op(rng, lay, s, np.arange(npos[s], npos[s] + n, dtype=np.int32)))
+            ntok[s] += n
+            npos[s] += n
+            total_tokens += n
+            k = int(rng.integers(0, 3))
+            sp = []
+            for _ in range(k):
+                b = int(rng.integers(0, ntok[s]))
+                e = int(rng.integers(b, min(ntok[s], b + 40) + 1))
+                sp.append((b, e))
+            if sp:
+                ops.append(Drop(s, _spans(sp)))
+            k = int(rng.integers(0, 3))
+            sp, dl = [], []
+            for _ in range(k):
+                b = int(rng.integers(0, ntok[s]))
+                e = int(rng.integers(b, ntok[s] + 1))
+                sp.append((b, e))
+                dl.append(int(rng.integers(-30, 31)))
+            if sp:
+                ops.append(Repos(s, _spans(sp), np.asarray(dl, np.int32)))
+            if compact and rng.random() < 0.3:
+                ops.append(Compact(s, 1))
+    # a fresh sequence per segment tail: query tokens appended last
+    segs, row = [], 0
+    for s in range(n_seqs):
+        nq = int(rng.integers(1, 24))
+        p0 = npos[s] + 1000            # positions of the new tokens exceed every cached one
+        ops.append(_append_op(rng, lay, s, np.arange(p0, p0 + nq, dtype=np.int32)))
+        total_tokens += nq
+        hist = ntok[s]
+        ntok[s] += nq
+        nseg = int(rng.integers(1, 3)) if nq > 1 else 1
+        lens = [nq] if nseg == 1 else [nq // 2, nq - nq // 2]
+        masks = []
+        for k in range(nseg):
+            if k and hist > 4:
+                b = int(rng.integers(0, hist - 2))
+                masks.append([(b, b + int(rng.integers(1, 4)))])
+            else:
+                masks.append([])
+        segs += _query_segments(s, hist, row, lens, masks)
+        row += nq
+    lay.num_pages = 2 * ((total_tokens + page_size - 1) // page_size) + 4 * n_seqs + 8
+    q = _normal_bf16(rng, (row, lay.n_q_heads, lay.d_qk), scale=0.5)
+    ops.append(Attention(q, segs))
+    wl = Workload(f"fuzz_{seed}", lay, rng.permutation(lay.num_pages).astype(np.int32), ops)
+    return wl
+
+
+CONFIGS = {
+    "c1": c1_tiny, "c2": c2_64k, "c3": c3_mla, "c4": c4_batched, "c5": c5_128k,
+}
+
+
+def make(name: str, seed: int = 0, **kw) -> Workload:
+    return CONFIGS[name](seed, **kw)
