@@ -1,0 +1,236 @@
+/*
+ * akv.h -- C ABI of the AKV cache-engineering hot path for AMD MI355X (gfx950).
+ *
+ * Operations on a paged bf16 KV pool: append, drop, repos (RoPE delta
+ * rotation of retained keys), splice, compaction, and segment-batch
+ * attention.  Sources, cited by page title and section:
+ *
+ *   [AKV-blog]  "AKV: Cache Engineering for Autonomous Agents and
+ *               State-Preserving Prefix Invalidation Bypass" (A. Akhunji)
+ *   [AKV-notes] "Cache Engineering for Agents" (reading notes on Fu et al.,
+ *               arXiv:2610.28577)
+ *   [Leyline]   "Leyline: KV Cache Directives for Agentic Inference"
+ *               (paper digest)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Device memory (page arrays, Q, K, V, outputs, scratch) belongs to the
+ *   caller.  The library never allocates or frees device memory; it keeps raw
+ *   pointers.  It owns all host metadata and a pinned host staging ring.
+ * - Host arrays passed in (spans, positions, segments, extents) are copied
+ *   before the call returns.  Device inputs (K, V, Q) must stay valid until the
+ *   work is done (akv_sync or a sync of the pool's stream).
+ * - All device work is enqueued on the pool's HIP stream; calls return once it
+ *   is enqueued, with the host metadata already updated.
+ * - Calls on one pool are not re-entrant; separate pools are independent.
+ * - Every call validates all arguments before changing any state: a call that
+ *   fails leaves the pool as it was.  akv_last_error() gives the reason.
+ * - Spans are half-open [begin, end) over a sequence's logical token indices,
+ *   which never change: the n-th token appended to a sequence has index n.
+ * - Page slots are numbered page * page_size + offset.
+ *
+ * Pool memory layout (all bf16, caller-allocated, row-major):
+ *   GQA  (d_nope == 0): k_pages [num_pages][n_kv_heads][page_size][d_rope]
+ *                       v_pages [num_pages][n_kv_heads][page_size][d_v]
+ *                       kpe_pages must be NULL.
+ *   MLA  (d_nope  > 0): k_pages   = K_nope [num_pages][n_kv_heads][page_size][d_nope]
+ *                       kpe_pages = K_pe   [num_pages][H_pe][page_size][d_rope]
+ *                       with H_pe = 1 (shared by all heads) or n_kv_heads
+ *                       (kpe_per_head = 1);
+ *                       v_pages   [num_pages][n_kv_heads][page_size][d_v].
+ *
+ * Page allocation rule: a FIFO free queue initialised to page_order (or
+ * 0..num_pages-1), then a FIFO evictable queue of pages without any visible
+ * token (dropped cache is evicted first, [AKV-notes] section 3, Cache
+ * Management).  A sequence fills its open tail page before taking a new one.
+ * A page joins the evictable queue when its last visible token is dropped or
+ * moved away by compaction, unless it is the sequence's open tail page.
+ */
+#ifndef AKV_H
+#define AKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct akv_pool akv_pool;
+
+typedef enum {
+  AKV_OK = 0,
+  AKV_EINVAL = -1, /* malformed argument (NULL, bad shape, end < begin, ...) */
+  AKV_ERANGE = -2, /* index, span, page or position out of range            */
+  AKV_ENOMEM = -3, /* pool pages or scratch bytes exhausted                  */
+  AKV_ESTATE = -4, /* released sequence, or a device op on a page-table-only pool */
+  AKV_EHIP = -5    /* a HIP runtime call failed                              */
+} akv_status;
+
+typedef struct { int32_t begin, end; } akv_span;          /* [begin, end)             */
+typedef struct { int32_t page, lo, hi; } akv_extent;      /* slots lo..hi-1 of a page */
+typedef struct { int32_t q_begin, q_len, ext_begin, ext_len; } akv_segment;
+
+typedef struct {
+  int32_t n_q_heads;     /* multiple of n_kv_heads; q head h reads kv head h / (n_q_heads/n_kv_heads) */
+  int32_t n_kv_heads;
+  int32_t d_nope;        /* 0 for GQA; MLA position-free key dims per head          */
+  int32_t d_rope;        /* rotated key dims: all of K (GQA) or K_pe (MLA); even   */
+  int32_t d_v;
+  int32_t page_size;     /* power of two, 1..256                                    */
+  int32_t num_pages;
+  int32_t kpe_per_head;  /* MLA: 0 = one K_pe row per token shared by all heads     */
+  int32_t pairing;       /* 0 = interleaved pairs (2i, 2i+1); 1 = half-split (i, i + d_rope/2) */
+  double rope_theta;     /* theta_i = rope_theta^(-2i/d_rope) unless inv_freq is given */
+  const double* inv_freq;/* optional d_rope/2 angular frequencies (copied)          */
+  double compact_threshold; /* automatic compaction above this fragmentation;
+                               <= 0 selects 0.40, >= 1 disables it               */
+} akv_layout;
+
+/* ---- pool ---------------------------------------------------------------- */
+
+/* Create a pool over caller-owned device page arrays (layout above).
+ * page_order: optional permutation of 0..num_pages-1 (initial free queue).
+ * scratch / scratch_bytes: caller-owned device memory for work lists, slot maps
+ * and split-KV partials; attention needs about
+ *   64 KiB + 16 B * n_ext + 4 B * total list length + 16 B * work items
+ *   + split partials (4 B * n_split * rows * (d_v + 2)).
+ * hip_stream: the stream all device work goes to (NULL = the null stream).
+ * A pool with k_pages == v_pages == kpe_pages == NULL and scratch == NULL is
+ * page-table-only: it tracks slots, positions, visibility and allocation
+ * exactly like a device pool but holds no KV values, so attention on it
+ * returns AKV_ESTATE.
+ * Errors: AKV_EINVAL (bad layout, page_order not a permutation),
+ * AKV_EHIP (device query or pinned allocation failed). */
+akv_status akv_pool_create(const akv_layout* layout, const int32_t* page_order,
+                           void* k_pages, void* kpe_pages, void* v_pages,
+                           void* scratch, size_t scratch_bytes, void* hip_stream,
+                           akv_pool** out);
+akv_status akv_pool_destroy(akv_pool* pool);   /* waits for the pool's stream */
+
+/* Sequences get ids 0, 1, 2, ... in creation order; ids are not reused.
+ * Releasing returns every page the sequence still owns to the back of the
+ * free queue in allocation order.  Errors: AKV_EINVAL (unknown id),
+ * AKV_ESTATE (already released). */
+akv_status akv_seq_create(akv_pool* pool, int32_t* seq);
+akv_status akv_seq_release(akv_pool* pool, int32_t seq);
+
+/* ---- cache operations ([AKV-notes] section 1: append, drop, repos) ---------- */
+
+/* append: add n tokens with positions pos[0..n) (host array, each in
+ * [0, 2^31)).  K, K_pe, V are device arrays, token-major:
+ *   GQA: K [n][n_kv_heads][d_rope], K_pe NULL, V [n][n_kv_heads][d_v]
+ *   MLA: K = K_nope [n][n_kv_heads][d_nope], K_pe [n][H_pe][d_rope], V as above.
+ * Keys arrive already rotated to their positions.  Passing K == K_pe == V ==
+ * NULL reserves the slots only (a caller's own kernel writes them; see
+ * akv_seq_tokens).  Errors: AKV_EINVAL, AKV_ERANGE (position), AKV_ENOMEM
+ * (no page left in the free and evictable queues). */
+akv_status akv_append(akv_pool* pool, int32_t seq, const void* K, const void* K_pe,
+                      const void* V, const int32_t* pos, int32_t n);
+
+/* drop ([AKV-blog] section 2, The Drop Primitive): mark the tokens of every
+ * span inactive.  Nothing is freed or rewritten; later attention lists skip
+ * them.  Dropping a token twice is a no-op; an empty span is a no-op.  When
+ * the sequence's fragmentation (1 - visible tokens / written slots of the pages
+ * holding a visible token) then exceeds the threshold, compaction runs if the
+ * allocator can supply the fresh pages (it is skipped otherwise).
+ * Errors: AKV_EINVAL (end < begin), AKV_ERANGE (span outside 0..n). */
+akv_status akv_drop(akv_pool* pool, int32_t seq, const akv_span* spans, int32_t n_spans);
+
+/* compaction ([AKV-blog] section 7, Dilemma 2): copy every visible token, in
+ * visible-list order, into fresh pages (one device copy kernel), then move the
+ * old pages to the evictable queue.  Values are copied bit for bit.  Without
+ * force it runs only above the fragmentation threshold. */
+akv_status akv_compact(akv_pool* pool, int32_t seq, int32_t force);
+
+/* repos ([AKV-blog] section 2, The Repos Primitive; [Leyline] Method): every
+ * retained token covered by spans gets the sum of their deltas d (signed);
+ * its position becomes pos + d and its rotated key part becomes R(d) k, with
+ * R(phi) = [[cos, -sin], [sin, cos]] on each pair at angle d * theta_i.  The
+ * angle is formed in fp64 and reduced mod 2*pi, the rotation is done in fp32
+ * and rounded once to bf16 (round to nearest even).  GQA rotates all of K;
+ * MLA rotates K_pe only (K_nope and V are untouched).  Dropped tokens and
+ * tokens with total delta 0 are not touched.  One kernel launch covers all
+ * spans.  Errors: AKV_EINVAL, AKV_ERANGE (span, or a new position outside
+ * [0, 2^31)). */
+akv_status akv_repos(akv_pool* pool, int32_t seq, const akv_span* spans, const int32_t* delta,
+                     int32_t n_spans);
+
+/* splice ([Leyline] Method, AMORTIZE mode): spans are given in coordinates of
+ * the current visible list (entry i is the i-th visible token in position
+ * order), sorted and disjoint, each non-empty.  Splice j drops its span,
+ * appends stub_len[j] stub tokens at positions p_j + sum_{i<j} delta_i + 0..,
+ * where p_j is the position of the span's first entry, and moves every visible
+ * entry after the span by delta_j = stub_len[j] - (end_j - begin_j).  Per-token
+ * deltas of several splices are summed and applied in one rotation launch.
+ * Stub K/K_pe/V: device arrays as for akv_append, concatenated over splices,
+ * already rotated to their stub positions.  stub_pos_out (optional host array
+ * of sum(stub_len) entries) receives the stub positions. */
+akv_status akv_splice(akv_pool* pool, int32_t seq, const akv_span* spans, const int32_t* stub_len,
+                      int32_t n_splices, const void* stub_K, const void* stub_Kpe,
+                      const void* stub_V, int32_t* stub_pos_out);
+
+/* ---- visibility -------------------------------------------------------------- */
+
+/* Page-table image of the sequence's visible list: retained tokens minus the
+ * optional mask spans (hidden from this list only, not dropped), ordered by
+ * (position, logical index), encoded as maximal runs of consecutive slots of
+ * one page.  Writes up to cap extents; *n_out gets the full count (call again
+ * with a larger cap when *n_out > cap; AKV_ERANGE is returned then). */
+akv_status akv_seq_visible(akv_pool* pool, int32_t seq, const akv_span* mask, int32_t n_mask,
+                           akv_extent* out, int32_t cap, int32_t* n_out);
+
+/* ---- segment-batch attention ([AKV-notes] section 3; [AKV-blog] section 4) -------- */
+
+/* Q: device bf16 [n_q_tokens][n_q_heads][d_nope + d_rope] (MLA rows are
+ * [q_nope | q_pe]); out: device bf16 [n_q_tokens][n_q_heads][d_v].
+ * Segment s covers query rows q_begin .. q_begin+q_len-1 and reads the list
+ * page_lists[ext_begin .. ext_begin+ext_len) (host array of extents) of
+ * Lkv >= q_len entries.  Query i of the segment attends to list entries
+ * 0 .. Lkv - q_len + i (the segment's own tokens are the last q_len entries):
+ * out = softmax(scale * q K^T) V with fp32 accumulation; scale 0 selects
+ * 1/sqrt(d_nope + d_rope).  All segments run in one launch.  Segments must not
+ * overlap in Q rows; rows no segment covers are not written.  q_len == 0
+ * segments are skipped.  Errors: AKV_EINVAL (Lkv < q_len, overlapping rows),
+ * AKV_ERANGE (row or extent out of range), AKV_ENOMEM (scratch too small),
+ * AKV_ESTATE (page-table-only pool). */
+akv_status akv_segment_attention(akv_pool* pool, const void* Q, int32_t n_q_tokens,
+                                 const akv_segment* segs, int32_t n_segs,
+                                 const akv_extent* page_lists, int32_t n_ext, float scale,
+                                 void* out);
+
+/* ---- inspection, sync, errors ---------------------------------------------------- */
+
+/* Per-token metadata of tokens first .. first+n-1 (any output may be NULL);
+ * slot is -1 for a dropped token whose page was evicted. */
+akv_status akv_seq_tokens(akv_pool* pool, int32_t seq, int32_t first, int32_t n,
+                          int32_t* slot, int32_t* pos, uint8_t* dropped);
+/* Token count, visible count and fragmentation of a sequence. */
+akv_status akv_seq_info(akv_pool* pool, int32_t seq, int32_t* n_tokens, int32_t* n_visible,
+                        double* fragmentation);
+/* Current free and evictable queues, front first (outputs may be NULL). */
+akv_status akv_pool_queues(akv_pool* pool, int32_t* free_out, int32_t free_cap, int32_t* n_free,
+                           int32_t* evict_out, int32_t evict_cap, int32_t* n_evict);
+/* Dry run of akv_repos: the rotation work list it would launch, as (slot, delta)
+ * pairs of every token it would rotate, in launch order; *n_out gets the count.
+ * Changes nothing. */
+akv_status akv_repos_plan(akv_pool* pool, int32_t seq, const akv_span* spans, const int32_t* delta,
+                          int32_t n_spans, int32_t* slot_out, int32_t* delta_out, int32_t cap,
+                          int32_t* n_out);
+
+/* Kernel timing: when enabled, the library brackets each of its kernel
+ * launches with HIP events on the pool's stream.  akv_timing_read waits for the
+ * stream, returns the summed milliseconds and launch count of one kernel kind
+ * since the last read of that kind, and clears them. */
+enum { AKV_K_APPEND = 0, AKV_K_ROTATE = 1, AKV_K_COMPACT = 2, AKV_K_EXPAND = 3,
+       AKV_K_ATTN = 4, AKV_K_COMBINE = 5, AKV_K_KINDS = 6 };
+akv_status akv_timing_enable(akv_pool* pool, int32_t enable);
+akv_status akv_timing_read(akv_pool* pool, int32_t kind, double* total_ms, int32_t* count);
+
+akv_status akv_sync(akv_pool* pool);       /* wait for the pool's stream */
+const char* akv_last_error(void);          /* thread-local text of the last failure */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AKV_H */

@@ -1,0 +1,90 @@
+// Internal interface between the host runtime (akv_runtime.cpp) and the HIP
+// kernels (akv_kernels.hip).  Plain structs that both the host planner and the
+// device code read; every launcher enqueues on the given stream and returns the
+// hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace akv {
+
+// One repos work item: rows lo..hi-1 of one page, rotated by deltas[didx].
+struct RotItem {
+  int32_t page, lo, hi, didx;
+};
+
+// One row copy of the compaction kernel: token moves from src slot to dst slot.
+struct MovePair {
+  int32_t src, dst;
+};
+
+// A page-table extent (same layout as akv_extent).
+struct Extent {
+  int32_t page, lo, hi;
+};
+
+// Segment as the attention kernel sees it: query rows, list length, and the
+// offset of its slot list inside the expanded slot map.
+struct AttnSeg {
+  int32_t q_begin, q_len, lkv, list_off;
+};
+
+// One attention work item: a tile of ATTN_ROWS packed rows (token, q head in
+// group) of one segment and kv head, over list entries k_begin..k_end-1.
+// part >= 0: write an unnormalised fp32 partial (split-KV) at that index.
+// seg < 0: padding block, exits at once.
+struct AttnItem {
+  int32_t seg, kvh, row0, k_begin, k_end, part;
+};
+
+// Split-KV merge of nsplit consecutive partials part0.. for one row tile.
+struct CombItem {
+  int32_t seg, kvh, row0, part0, nsplit, pad;
+};
+
+constexpr int ATTN_ROWS = 256;   // packed rows per attention block (4 waves x 64)
+constexpr int ATTN_KTILE = 64;   // keys per pipeline stage
+
+// ---- launchers --------------------------------------------------------------
+hipError_t launch_rotate(hipStream_t st, uint16_t* kr, int n_heads, int page_size, int d_rope,
+                         int pairing, const RotItem* items, int n_items, const int32_t* deltas,
+                         const double* inv_freq);
+
+hipError_t launch_scatter_rows(hipStream_t st, const uint16_t* src, uint16_t* dst,
+                               const int32_t* slots, int n, int n_heads, int page_size,
+                               int log2_page, int row_elems);
+
+hipError_t launch_move_rows(hipStream_t st, uint16_t* base, const MovePair* pairs, int n,
+                            int n_heads, int page_size, int log2_page, int row_elems);
+
+hipError_t launch_expand(hipStream_t st, const Extent* ex, const int32_t* ex_off, int n_ext,
+                         int page_size, int32_t* slots);
+
+struct AttnArgs {
+  const uint16_t* q;
+  int n_q_heads, group;          // group = n_q_heads / n_kv_heads
+  const uint16_t* k_a;           // GQA: K pages; MLA: K_nope pages
+  const uint16_t* k_b;           // MLA: K_pe pages (else nullptr)
+  int kpe_heads;                 // MLA: heads stored in K_pe pages (1 = shared)
+  const uint16_t* v;
+  int n_kv_heads, page_size, log2_page;
+  const AttnSeg* segs;
+  const AttnItem* items;
+  int n_items;
+  const int32_t* slots;
+  float scale_log2e;             // softmax scale * log2(e)
+  uint16_t* out;
+  float* part_o;                 // [n_parts][ATTN_ROWS][d_v]
+  float* part_ml;                // [n_parts][ATTN_ROWS][2]
+};
+
+// Returns hipErrorInvalidValue when no kernel is instantiated for the dims.
+hipError_t launch_seg_attn(hipStream_t st, const AttnArgs& a, int d_nope, int d_rope, int d_v);
+
+hipError_t launch_combine(hipStream_t st, const AttnArgs& a, const CombItem* items, int n_items,
+                          int d_v);
+
+bool attn_dims_supported(int d_nope, int d_rope, int d_v);
+
+}  // namespace akv

@@ -1,0 +1,615 @@
+// HIP kernels of the AKV hot path for MI355X (gfx950, wave64, MFMA).
+//
+// Sources, cited by page title and section:
+//   [AKV-blog]  "AKV: Cache Engineering for Autonomous Agents and State-Preserving
+//               Prefix Invalidation Bypass" (A. Akhunji)
+//   [AKV-notes] "Cache Engineering for Agents" (reading notes on Fu et al.)
+//   [Leyline]   "Leyline: KV Cache Directives for Agentic Inference" (digest)
+//
+// Kernels:
+//   k_rotate       repos delta rotation, in place on the paged pool (HBM-bound)
+//   k_scatter_rows append: token-major rows -> page slots (HBM-bound)
+//   k_move_rows    compaction: slot -> slot row copies (HBM-bound)
+//   k_expand       extents -> per-entry slot list for the attention gather
+//   k_seg_attn     segment-batch attention, bf16 MFMA 32x32x16 (MFMA-bound)
+//   k_combine      split-KV merge of (m, l, O) partials
+#include <hip/hip_runtime.h>
+
+#include "akv_internal.h"
+
+namespace akv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 values -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack_bf2(float a, float b) {
+  bf16x2 v;
+  v.x = (__bf16)a;
+  v.y = (__bf16)b;
+  return __builtin_bit_cast(unsigned, v);
+}
+
+// ---------------------------------------------------------------------------
+// repos rotation ([AKV-blog] section 2, The Repos Primitive; [Leyline] Method)
+//
+// One block per work item (page, rows lo..hi-1, delta).  The block forms the
+// d_rope/2 angles delta * theta_i in fp64, reduces them mod 2*pi, takes sin
+// and cos once into LDS, and every head and row of the item reuses them.  A
+// "unit" is 8 rotation pairs held in two 16-byte loads; pair (x, y) becomes
+// (x cos - y sin, x sin + y cos) in fp32 and is rounded once to bf16.
+// The first pass issues its loads before the angle table is built so the
+// memory latency overlaps the fp64 work.
+// ---------------------------------------------------------------------------
+constexpr int ROT_THREADS = 256;
+constexpr int ROT_UPT = 4;
+
+__device__ __forceinline__ unsigned rot_pair_word(unsigned w, float c, float s) {
+  // word holds an interleaved pair (x = low half, y = high half)
+  float x = bf_lo(w), y = bf_hi(w);
+  return pack_bf2(fmaf(x, c, -y * s), fmaf(x, s, y * c));
+}
+
+__global__ __launch_bounds__(ROT_THREADS) void k_rotate(uint16_t* __restrict__ kr, int n_heads, int S,
+                                                         int d, int pairing,
+                                                         const RotItem* __restrict__ items,
+                                                         const int32_t* __restrict__ deltas,
+                                                         const double* __restrict__ inv_freq) {
+  __shared__ float s_c[128], s_s[128];
+  const RotItem it = items[blockIdx.x];
+  const int half = d >> 1;
+  const int upr = d >> 4;
+  const int rows = it.hi - it.lo;
+  const int per_head = rows * upr;
+  const int n_units = n_heads * per_head;
+  const int n_pass = (n_units + ROT_UPT * ROT_THREADS - 1) / (ROT_UPT * ROT_THREADS);
+
+  u32x4 ra[ROT_UPT], rb[ROT_UPT];
+  uint16_t* pa[ROT_UPT];
+  uint16_t* pb[ROT_UPT];
+  int cu[ROT_UPT];
+
+  auto locate = [&](int u, int i) {
+    const int h = u / per_head;
+    const int rem = u - h * per_head;
+    const int row = it.lo + rem / upr;
+    const int c = rem - (rem / upr) * upr;
+    uint16_t* base = kr + ((size_t)(it.page * n_heads + h) * S + row) * d;
+    cu[i] = c;
+    if (pairing == 0) {
+      pa[i] = base + 16 * c;
+      pb[i] = pa[i] + 8;
+    } else {
+      pa[i] = base + 8 * c;
+      pb[i] = base + half + 8 * c;
+    }
+  };
+
+#pragma unroll
+  for (int i = 0; i < ROT_UPT; ++i) {
+    const int u = threadIdx.x + i * ROT_THREADS;
+    if (u < n_units) {
+      locate(u, i);
+      ra[i] = *(const u32x4*)pa[i];
+      rb[i] = *(const u32x4*)pb[i];
+    }
+  }
+  if ((int)threadIdx.x < half) {
+    const double ang = (double)deltas[it.didx] * inv_freq[threadIdx.x];
+    const double red = ang - 6.283185307179586476925 * rint(ang * 0.15915494309189533577);
+    double sv, cv;
+    sincos(red, &sv, &cv);
+    s_c[threadIdx.x] = (float)cv;
+    s_s[threadIdx.x] = (float)sv;
+  }
+  __syncthreads();
+
+  for (int pass = 0; pass < n_pass; ++pass) {
+#pragma unroll
+    for (int i = 0; i < ROT_UPT; ++i) {
+      const int u = threadIdx.x + (pass * ROT_UPT + i) * ROT_THREADS;
+      if (u >= n_units) continue;
+      if (pass > 0) {
+        locate(u, i);
+        ra[i] = *(const u32x4*)pa[i];
+        rb[i] = *(const u32x4*)pb[i];
+      }
+      const int p0 = 8 * cu[i];  // first pair of the unit
+      u32x4 oa, ob;
+      if (pairing == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          oa[k] = rot_pair_word(ra[i][k], s_c[p0 + k], s_s[p0 + k]);
+          ob[k] = rot_pair_word(rb[i][k], s_c[p0 + 4 + k], s_s[p0 + 4 + k]);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float c0 = s_c[p0 + 2 * k], s0 = s_s[p0 + 2 * k];
+          const float c1 = s_c[p0 + 2 * k + 1], s1 = s_s[p0 + 2 * k + 1];
+          const float x0 = bf_lo(ra[i][k]), x1 = bf_hi(ra[i][k]);
+          const float y0 = bf_lo(rb[i][k]), y1 = bf_hi(rb[i][k]);
+          oa[k] = pack_bf2(fmaf(x0, c0, -y0 * s0), fmaf(x1, c1, -y1 * s1));
+          ob[k] = pack_bf2(fmaf(x0, s0, y0 * c0), fmaf(x1, s1, y1 * c1));
+        }
+      }
+      *(u32x4*)pa[i] = oa;
+      *(u32x4*)pb[i] = ob;
+    }
+  }
+}
+
+hipError_t launch_rotate(hipStream_t st, uint16_t* kr, int n_heads, int page_size, int d_rope,
+                         int pairing, const RotItem* items, int n_items, const int32_t* deltas,
+                         const double* inv_freq) {
+  if (n_items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rotate, dim3(n_items), dim3(ROT_THREADS), 0, st, kr, n_heads, page_size,
+                     d_rope, pairing, items, deltas, inv_freq);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// append: token-major rows [n][H][row] -> paged [page][H][S][row]
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_scatter_rows(const uint16_t* __restrict__ src,
+                                                      uint16_t* __restrict__ dst,
+                                                      const int32_t* __restrict__ slots, int n,
+                                                      int H, int S, int log2S, int row_elems) {
+  const int cpr = row_elems >> 3;
+  const long total = (long)n * H * cpr;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const int c = (int)(i % cpr);
+    const long r = i / cpr;
+    const int h = (int)(r % H);
+    const int t = (int)(r / H);
+    const int slot = slots[t];
+    const int page = slot >> log2S, off = slot & (S - 1);
+    *(u32x4*)(dst + (((size_t)page * H + h) * S + off) * row_elems + 8 * c) =
+        *(const u32x4*)(src + ((size_t)t * H + h) * row_elems + 8 * c);
+  }
+}
+
+static int grid_for(long chunks) {
+  long b = (chunks + 255) / 256;
+  if (b > 65536) b = 65536;
+  return (int)(b < 1 ? 1 : b);
+}
+
+hipError_t launch_scatter_rows(hipStream_t st, const uint16_t* src, uint16_t* dst,
+                               const int32_t* slots, int n, int n_heads, int page_size,
+                               int log2_page, int row_elems) {
+  if (n <= 0) return hipSuccess;
+  const long chunks = (long)n * n_heads * (row_elems >> 3);
+  hipLaunchKernelGGL(k_scatter_rows, dim3(grid_for(chunks)), dim3(256), 0, st, src, dst, slots, n,
+                     n_heads, page_size, log2_page, row_elems);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// compaction copy ([AKV-blog] section 7, Dilemma 2): rows move between slots of
+// one paged array; source and destination pages are disjoint.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_move_rows(uint16_t* __restrict__ base,
+                                                   const MovePair* __restrict__ pairs, int n, int H,
+                                                   int S, int log2S, int row_elems) {
+  const int cpr = row_elems >> 3;
+  const long total = (long)n * H * cpr;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const int c = (int)(i % cpr);
+    const long r = i / cpr;
+    const int h = (int)(r % H);
+    const int t = (int)(r / H);
+    const MovePair mp = pairs[t];
+    const int sp = mp.src >> log2S, so = mp.src & (S - 1);
+    const int dp = mp.dst >> log2S, dof = mp.dst & (S - 1);
+    *(u32x4*)(base + (((size_t)dp * H + h) * S + dof) * row_elems + 8 * c) =
+        *(const u32x4*)(base + (((size_t)sp * H + h) * S + so) * row_elems + 8 * c);
+  }
+}
+
+hipError_t launch_move_rows(hipStream_t st, uint16_t* base, const MovePair* pairs, int n,
+                            int n_heads, int page_size, int log2_page, int row_elems) {
+  if (n <= 0) return hipSuccess;
+  const long chunks = (long)n * n_heads * (row_elems >> 3);
+  hipLaunchKernelGGL(k_move_rows, dim3(grid_for(chunks)), dim3(256), 0, st, base, pairs, n,
+                     n_heads, page_size, log2_page, row_elems);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// extents -> slot list (one thread per extent)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_expand(const Extent* __restrict__ ex,
+                                                const int32_t* __restrict__ ex_off, int n_ext, int S,
+                                                int32_t* __restrict__ slots) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n_ext) return;
+  const Extent x = ex[e];
+  int32_t* o = slots + ex_off[e];
+  for (int i = x.lo; i < x.hi; ++i) o[i - x.lo] = x.page * S + i;
+}
+
+hipError_t launch_expand(hipStream_t st, const Extent* ex, const int32_t* ex_off, int n_ext,
+                         int page_size, int32_t* slots) {
+  if (n_ext <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_expand, dim3((n_ext + 255) / 256), dim3(256), 0, st, ex, ex_off, n_ext,
+                     page_size, slots);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// segment-batch attention ([AKV-notes] section 3, Segment-Batch Attention;
+// [AKV-blog] section 4)
+//
+// One block = 4 waves = ATTN_ROWS packed rows (token-major, the q heads of one
+// kv head side by side) of one segment, over list entries k_begin..k_end-1 in
+// tiles of 64 keys gathered from pages through the segment's slot list.
+//
+// Per wave: 64 query rows as two 32-row blocks.  S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16 (A = K tile from LDS, B = Q in registers), so every
+// lane owns one query row (lane % 32) and half of the 32 keys of each block;
+// row max / sum need one exchange with lane ^ 32.  O^T = V^T P^T reuses the
+// accumulator registers of S^T directly as the B operand (P in bf16), with V
+// stored transposed in LDS and its keys permuted inside every 16-key group to
+// match the accumulator's key order, so no register shuffles are needed.
+// Causality is bottom-right over list order: query i sees entries
+// 0 .. Lkv - Lq + i.  The K/V of tile j+1 are loaded into registers while tile
+// j is computed, then written to the other LDS buffer (one barrier per tile).
+// ---------------------------------------------------------------------------
+template <int DQK, int DV, int DNOPE>
+__global__ __launch_bounds__(256, 1) void k_seg_attn(AttnArgs a) {
+  constexpr int KT = ATTN_KTILE;
+  constexpr int KPAD = DQK + 8;        // LDS K row stride (elements)
+  constexpr int VPAD = KT + 8;         // LDS V^T row stride (elements)
+  constexpr int NKS = DQK / 16;        // k-steps of S^T
+  constexpr int NCB = DV / 32;         // 32-wide column blocks of O^T
+  constexpr int KCH = DQK / 8;         // 16-byte chunks per K row
+  constexpr int NKL = KT * KCH / 256;  // K chunks per thread per tile
+  constexpr int VCH = DV / 8;          // 16-byte chunks per V row
+  constexpr int VTHREADS = VCH * 16;   // V loaders: 4 keys x 8 columns each
+  static_assert(DQK % 32 == 0 && DV % 32 == 0 && NKL >= 1 && VTHREADS <= 256, "dims");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][KT * KPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][DV * VPAD];
+
+  const AttnItem it = a.items[blockIdx.x];
+  if (it.seg < 0) return;
+  const AttnSeg sg = a.segs[it.seg];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int G = a.group;
+  const int lq = sg.q_len, lkv = sg.lkv;
+  const int rows_total = lq * G;
+  const int brow_last = min(it.row0 + ATTN_ROWS, rows_total) - 1;
+  const int lim_first = lkv - lq + it.row0 / G;
+  const int lim_last = lkv - lq + brow_last / G;
+  const int k_end = it.k_end;
+  const int k_stop = min(k_end, lim_last + 1);
+  const int n_tiles = k_stop > it.k_begin ? (k_stop - it.k_begin + KT - 1) / KT : 0;
+  const int Hkv = a.n_kv_heads, S = a.page_size, lg = a.log2_page;
+  const int kvh = it.kvh;
+  const int32_t* __restrict__ slots = a.slots + sg.list_off;
+
+  // the lane's two query rows
+  int lim_q[2], tok_q[2], hq_q[2];
+  bool valid_q[2];
+  bf16x8 qf[2][NKS];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = it.row0 + 64 * w + 32 * qb + l32;
+    valid_q[qb] = r < rows_total;
+    const int rr = valid_q[qb] ? r : 0;
+    tok_q[qb] = rr / G;
+    hq_q[qb] = kvh * G + (rr - tok_q[qb] * G);
+    lim_q[qb] = valid_q[qb] ? lkv - lq + tok_q[qb] : k_stop;
+    const uint16_t* qp =
+        a.q + ((size_t)(sg.q_begin + tok_q[qb]) * a.n_q_heads + hq_q[qb]) * DQK + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (valid_q[qb]) {
+        qf[qb][ks] = *(const bf16x8*)(qp + 16 * ks);
+      } else {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qf[qb][ks] = __builtin_bit_cast(bf16x8, z);
+      }
+    }
+  }
+
+  u32x4 kreg[NKL];
+  u32x4 vreg[4];
+  const int vp = tid >> 4, vquad = tid & 15;
+
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < NKL; ++j) {
+      const int i = tid + 256 * j;
+      const int key = i / KCH, c = i - (i / KCH) * KCH;
+      const int kk = min(k0 + key, lkv - 1);
+      const int slot = slots[kk];
+      const int page = slot >> lg, off = slot & (S - 1);
+      const uint16_t* src;
+      if (DNOPE == 0) {
+        src = a.k_a + (((size_t)page * Hkv + kvh) * S + off) * DQK + 8 * c;
+      } else if (c < DNOPE / 8) {
+        src = a.k_a + (((size_t)page * Hkv + kvh) * S + off) * DNOPE + 8 * c;
+      } else {
+        const int hp = a.kpe_heads == 1 ? 0 : kvh;
+        src = a.k_b + (((size_t)page * a.kpe_heads + hp) * S + off) * (DQK - DNOPE) +
+              8 * (c - DNOPE / 8);
+      }
+      kreg[j] = *(const u32x4*)src;
+    }
+    if (tid < VTHREADS) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kk = min(k0 + 4 * vquad + e, lkv - 1);
+        const int slot = slots[kk];
+        const int page = slot >> lg, off = slot & (S - 1);
+        vreg[e] = *(const u32x4*)(a.v + (((size_t)page * Hkv + kvh) * S + off) * DV + 8 * vp);
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < NKL; ++j) {
+      const int i = tid + 256 * j;
+      const int key = i / KCH, c = i - (i / KCH) * KCH;
+      *(u32x4*)&sK[buf][key * KPAD + 8 * c] = kreg[j];
+    }
+    if (tid < VTHREADS) {
+      // keys 4*vquad..+3 go to LDS positions with quads 1 and 2 of every
+      // 16-key group swapped (the accumulator's key order)
+      const int qg = vquad & 3;
+      const int posq = (vquad & ~3) * 4 + (qg == 1 ? 2 : (qg == 2 ? 1 : qg)) * 4;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int dw = e >> 1;
+        unsigned lo, hi;
+        if ((e & 1) == 0) {
+          lo = (vreg[0][dw] & 0xffffu) | (vreg[1][dw] << 16);
+          hi = (vreg[2][dw] & 0xffffu) | (vreg[3][dw] << 16);
+        } else {
+          lo = (vreg[0][dw] >> 16) | (vreg[1][dw] & 0xffff0000u);
+          hi = (vreg[2][dw] >> 16) | (vreg[3][dw] & 0xffff0000u);
+        }
+        u32x2 v2 = {lo, hi};
+        *(u32x2*)&sV[buf][(8 * vp + e) * VPAD + posq] = v2;
+      }
+    }
+  };
+
+  f32x16 oacc[NCB][2];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[cb][qb][r] = 0.f;
+  float m_i[2] = {-INFINITY, -INFINITY};
+  float l_i[2] = {0.f, 0.f};
+  const float c2 = a.scale_log2e;
+
+  if (n_tiles > 0) {
+    load_tile(it.k_begin);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int buf = j & 1;
+    const int k0 = it.k_begin + j * KT;
+    const bool more = j + 1 < n_tiles;
+    if (more) load_tile(k0 + KT);
+
+    // S^T = K Q^T: two 32-key blocks x two 32-query blocks
+    f32x16 sacc[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][qb][r] = 0.f;
+    const uint16_t* kbase = &sK[buf][0];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 af = *(const bf16x8*)(kbase + (32 * kb + l32) * KPAD + 16 * ks + 8 * g);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[qb][ks], sacc[kb][qb], 0, 0, 0);
+      }
+    }
+
+    const bool need_mask = (k0 + KT > k_end) || (k0 + KT - 1 > lim_first);
+    bf16x8 pf[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (need_mask) {
+        const int lim = min(lim_q[qb], k_end - 1);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key > lim) sacc[kb][qb][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_i[qb], mx * c2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_i[qb] - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][r], c2, -m_use));
+          sacc[kb][qb][r] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 32);
+      l_i[qb] = l_i[qb] * alpha + rs;
+      m_i[qb] = m_new;
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[cb][qb][r] *= alpha;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int kb = t >> 1, r0 = 8 * (t & 1);
+        u32x4 pk;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pk[k] = pack_bf2(sacc[kb][qb][r0 + 2 * k], sacc[kb][qb][r0 + 2 * k + 1]);
+        pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
+      }
+    }
+
+    // O^T += V^T P^T
+    const uint16_t* vbase = &sV[buf][0];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const bf16x8 vf = *(const bf16x8*)(vbase + (32 * cb + l32) * VPAD + 16 * t + 8 * g);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          oacc[cb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], oacc[cb][qb], 0, 0, 0);
+      }
+    }
+
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds O^T columns c = 32cb + 8m + 4g + 0..3 of its row
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    if (!valid_q[qb]) continue;
+    if (it.part < 0) {
+      const float inv = l_i[qb] > 0.f ? 1.f / l_i[qb] : 0.f;
+      uint16_t* op = a.out + ((size_t)(sg.q_begin + tok_q[qb]) * a.n_q_heads + hq_q[qb]) * DV;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          u32x2 v2 = {pack_bf2(oacc[cb][qb][4 * m] * inv, oacc[cb][qb][4 * m + 1] * inv),
+                      pack_bf2(oacc[cb][qb][4 * m + 2] * inv, oacc[cb][qb][4 * m + 3] * inv)};
+          *(u32x2*)(op + 32 * cb + 8 * m + 4 * g) = v2;
+        }
+    } else {
+      const int prow = it.part * ATTN_ROWS + 64 * w + 32 * qb + l32;
+      float* po = a.part_o + (size_t)prow * DV;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          f32x4 v4 = {oacc[cb][qb][4 * m], oacc[cb][qb][4 * m + 1], oacc[cb][qb][4 * m + 2],
+                      oacc[cb][qb][4 * m + 3]};
+          *(f32x4*)(po + 32 * cb + 8 * m + 4 * g) = v4;
+        }
+      if (g == 0) {
+        a.part_ml[2 * (size_t)prow] = m_i[qb];
+        a.part_ml[2 * (size_t)prow + 1] = l_i[qb];
+      }
+    }
+  }
+}
+
+// Split-KV merge: O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j (m in log2
+// units).  One wave per row; lanes split the d_v columns.
+template <int DV>
+__global__ __launch_bounds__(256) void k_combine(AttnArgs a, const CombItem* __restrict__ items) {
+  constexpr int PER = DV / 64 > 0 ? DV / 64 : 1;
+  const CombItem it = items[blockIdx.x];
+  const AttnSeg sg = a.segs[it.seg];
+  const int G = a.group;
+  const int rows_total = sg.q_len * G;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int rl = w; rl < ATTN_ROWS; rl += 4) {
+    const int r = it.row0 + rl;
+    if (r >= rows_total) break;
+    float M = -INFINITY;
+    for (int j = 0; j < it.nsplit; ++j)
+      M = fmaxf(M, a.part_ml[2 * ((size_t)(it.part0 + j) * ATTN_ROWS + rl)]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    for (int j = 0; j < it.nsplit; ++j) {
+      const size_t prow = (size_t)(it.part0 + j) * ATTN_ROWS + rl;
+      const float wj = __builtin_amdgcn_exp2f(a.part_ml[2 * prow] - Mu);
+      L += wj * a.part_ml[2 * prow + 1];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int c = lane + 64 * e;
+        if (c < DV) acc[e] += wj * a.part_o[prow * DV + c];
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const int tok = r / G, hq = it.kvh * G + (r - tok * G);
+    uint16_t* op = a.out + ((size_t)(sg.q_begin + tok) * a.n_q_heads + hq) * DV;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int c = lane + 64 * e;
+      if (c < DV) {
+        const __bf16 b = (__bf16)(acc[e] * inv);
+        op[c] = __builtin_bit_cast(uint16_t, b);
+      }
+    }
+  }
+}
+
+bool attn_dims_supported(int d_nope, int d_rope, int d_v) {
+  if (d_nope == 0) return (d_rope == 32 || d_rope == 64 || d_rope == 128) && d_v == d_rope;
+  return (d_nope == 128 && d_rope == 64 && d_v == 128) || (d_nope == 32 && d_rope == 32 && d_v == 32);
+}
+
+template <int DQK, int DV, int DNOPE>
+static hipError_t launch_attn_t(hipStream_t st, const AttnArgs& a) {
+  hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE>), dim3(a.n_items), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_attn(hipStream_t st, const AttnArgs& a, int d_nope, int d_rope, int d_v) {
+  if (a.n_items <= 0) return hipSuccess;
+  if (d_nope == 0) {
+    if (d_rope == 128 && d_v == 128) return launch_attn_t<128, 128, 0>(st, a);
+    if (d_rope == 64 && d_v == 64) return launch_attn_t<64, 64, 0>(st, a);
+    if (d_rope == 32 && d_v == 32) return launch_attn_t<32, 32, 0>(st, a);
+  } else {
+    if (d_nope == 128 && d_rope == 64 && d_v == 128) return launch_attn_t<192, 128, 128>(st, a);
+    if (d_nope == 32 && d_rope == 32 && d_v == 32) return launch_attn_t<64, 32, 32>(st, a);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine(hipStream_t st, const AttnArgs& a, const CombItem* items, int n_items,
+                          int d_v) {
+  if (n_items <= 0) return hipSuccess;
+  switch (d_v) {
+    case 128: hipLaunchKernelGGL((k_combine<128>), dim3(n_items), dim3(256), 0, st, a, items); break;
+    case 64: hipLaunchKernelGGL((k_combine<64>), dim3(n_items), dim3(256), 0, st, a, items); break;
+    case 32: hipLaunchKernelGGL((k_combine<32>), dim3(n_items), dim3(256), 0, st, a, items); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace akv

@@ -1,0 +1,1349 @@
+// Host runtime and C ABI of the AKV hot path (include/akv.h).
+//
+// Holds the page allocator, per-sequence token tables (slot, position, drop
+// flag), the visible-list / page-table builder, the repos and attention
+// planners, a pinned staging ring for host->device metadata, and the launches
+// of the HIP kernels in akv_kernels.hip.
+//
+// Sources, cited by page title and section:
+//   [AKV-blog]  "AKV: Cache Engineering for Autonomous Agents and State-Preserving
+//               Prefix Invalidation Bypass" (A. Akhunji)
+//   [AKV-notes] "Cache Engineering for Agents" (reading notes on Fu et al.)
+//   [Leyline]   "Leyline: KV Cache Directives for Agentic Inference" (digest)
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <utility>
+#include <vector>
+
+#include "../../include/akv.h"
+#include "akv_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+akv_status fail(akv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+akv_status hip_fail(hipError_t e, const char* what) {
+  return fail(AKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr double kDefaultCompactThreshold = 0.40;
+constexpr int64_t kInt32Max = 2147483647LL;
+
+struct PageRec {
+  int32_t owner = -1;   // sequence id, -1 when free
+  int32_t nvis = 0;     // visible tokens held
+  int32_t filled = 0;   // slots written
+  bool in_evict = false;
+  uint32_t evict_gen = 0;
+  std::vector<int32_t> toks;   // tokens of the owner whose slot is in this page
+};
+
+struct SeqRec {
+  std::vector<int32_t> slot, pos;
+  std::vector<uint8_t> dropped;
+  std::vector<int32_t> pages;  // owned pages in allocation order
+  int32_t tail = -1;           // open page, or -1
+  bool alive = true;
+  int64_t n_vis = 0;
+  std::vector<int32_t> vis;    // cached visible order
+  bool vis_ok = false;
+};
+
+// Pinned host ring for metadata uploads.  A region may be rewritten once the
+// copy that read it has finished (its event has completed).
+struct Staging {
+  char* base = nullptr;
+  size_t cap = 0, head = 0;
+  struct Region {
+    size_t b, e;
+    hipEvent_t ev;
+  };
+  std::deque<Region> pending;
+  std::vector<hipEvent_t> spare;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+struct akv_pool {
+  akv_layout L{};
+  std::vector<double> inv_freq;
+  int log2S = 0;
+  bool device = false;
+  uint16_t* k = nullptr;    // GQA K / MLA K_nope
+  uint16_t* kpe = nullptr;  // MLA K_pe
+  uint16_t* v = nullptr;
+  char* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  size_t scratch_base = 0;  // first byte available to a call
+  hipStream_t stream = nullptr;
+  int n_cu = 256;
+  double thr = kDefaultCompactThreshold;
+
+  std::deque<int32_t> free_q;
+  std::deque<std::pair<int32_t, uint32_t>> evict_q;
+  int64_t n_evict = 0;
+  std::vector<PageRec> pages;
+  std::vector<SeqRec> seqs;
+
+  Staging stg;
+
+  bool timing = false;
+  struct TEv {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::vector<TEv> tev;
+  std::vector<hipEvent_t> ev_spare;
+  double t_ms[AKV_K_KINDS] = {};
+  int t_cnt[AKV_K_KINDS] = {};
+
+  int rope_heads() const { return (L.d_nope > 0 && !L.kpe_per_head) ? 1 : L.n_kv_heads; }
+  uint16_t* rope_array() const { return L.d_nope > 0 ? kpe : k; }
+};
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// staging + upload
+// ---------------------------------------------------------------------------
+hipError_t stg_event(akv_pool* p, hipEvent_t* ev) {
+  if (!p->stg.spare.empty()) {
+    *ev = p->stg.spare.back();
+    p->stg.spare.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreateWithFlags(ev, hipEventDisableTiming);
+}
+
+// Reserve n bytes of pinned staging (16-byte aligned).
+akv_status stg_reserve(akv_pool* p, size_t n, char** out) {
+  Staging& s = p->stg;
+  n = align_up(std::max<size_t>(n, 16), 256);
+  if (n > s.cap) {
+    hipError_t e = hipStreamSynchronize(p->stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    for (auto& r : s.pending) s.spare.push_back(r.ev);
+    s.pending.clear();
+    if (s.base) (void)hipHostFree(s.base);
+    s.base = nullptr;
+    size_t cap = std::max<size_t>(n, 2 * s.cap);
+    e = hipHostMalloc((void**)&s.base, cap, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      s.cap = 0;
+      return hip_fail(e, "hipHostMalloc(staging)");
+    }
+    s.cap = cap;
+    s.head = 0;
+  }
+  if (s.head + n > s.cap) s.head = 0;
+  const size_t b = s.head, e_ = s.head + n;
+  // wait for the newest pending region overlapping [b, e_); older ones are done too
+  int last = -1;
+  for (int i = 0; i < (int)s.pending.size(); ++i)
+    if (s.pending[i].b < e_ && b < s.pending[i].e) last = i;
+  if (last >= 0) {
+    hipError_t e = hipEventSynchronize(s.pending[last].ev);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging)");
+    for (int i = 0; i <= last; ++i) {
+      s.spare.push_back(s.pending.front().ev);
+      s.pending.pop_front();
+    }
+  }
+  s.head = e_;
+  *out = s.base + b;
+  return AKV_OK;
+}
+
+// Copy a filled staging region to device memory on the pool stream.
+akv_status stg_upload(akv_pool* p, const char* host, void* dev, size_t n) {
+  if (n == 0) return AKV_OK;
+  hipError_t e = hipMemcpyAsync(dev, host, n, hipMemcpyHostToDevice, p->stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(H2D)");
+  hipEvent_t ev;
+  e = stg_event(p, &ev);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  e = hipEventRecord(ev, p->stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  const size_t off = (size_t)(host - p->stg.base);
+  p->stg.pending.push_back({off, off + align_up(std::max<size_t>(n, 16), 256), ev});
+  return AKV_OK;
+}
+
+// Bump allocator over the per-call part of the scratch buffer.
+struct ScratchCursor {
+  akv_pool* p;
+  size_t off;
+  explicit ScratchCursor(akv_pool* pp) : p(pp), off(pp->scratch_base) {}
+  char* take(size_t n) {
+    off = align_up(off, 256);
+    char* r = p->scratch + off;
+    off += n;
+    return r;
+  }
+  bool ok() const { return off <= p->scratch_bytes; }
+};
+
+// ---------------------------------------------------------------------------
+// timing
+// ---------------------------------------------------------------------------
+hipError_t tev_get(akv_pool* p, hipEvent_t* ev) {
+  if (!p->ev_spare.empty()) {
+    *ev = p->ev_spare.back();
+    p->ev_spare.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreate(ev);
+}
+
+struct KTimer {
+  akv_pool* p;
+  int kind;
+  hipEvent_t a = nullptr, b = nullptr;
+  KTimer(akv_pool* pp, int k) : p(pp), kind(k) {
+    if (p->timing && tev_get(p, &a) == hipSuccess && tev_get(p, &b) == hipSuccess)
+      (void)hipEventRecord(a, p->stream);
+    else
+      a = b = nullptr;
+  }
+  void done() {
+    if (a && b) {
+      (void)hipEventRecord(b, p->stream);
+      p->tev.push_back({kind, a, b});
+      a = b = nullptr;
+    }
+  }
+};
+
+akv_status timing_collect(akv_pool* p) {
+  if (p->tev.empty()) return AKV_OK;
+  hipError_t e = hipEventSynchronize(p->tev.back().b);
+  if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(timing)");
+  for (auto& t : p->tev) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, t.a, t.b) == hipSuccess) {
+      p->t_ms[t.kind] += ms;
+      p->t_cnt[t.kind] += 1;
+    }
+    p->ev_spare.push_back(t.a);
+    p->ev_spare.push_back(t.b);
+  }
+  p->tev.clear();
+  return AKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// allocator
+// ---------------------------------------------------------------------------
+int64_t available(const akv_pool* p) { return (int64_t)p->free_q.size() + p->n_evict; }
+
+void evict_push(akv_pool* p, int32_t pg) {
+  PageRec& r = p->pages[pg];
+  r.in_evict = true;
+  r.evict_gen += 1;
+  p->evict_q.emplace_back(pg, r.evict_gen);
+  p->n_evict += 1;
+}
+
+void evict_unlink(akv_pool* p, int32_t pg) {  // entry becomes stale in the queue
+  p->pages[pg].in_evict = false;
+  p->n_evict -= 1;
+}
+
+int32_t evict_pop(akv_pool* p) {
+  while (!p->evict_q.empty()) {
+    auto [pg, gen] = p->evict_q.front();
+    p->evict_q.pop_front();
+    const PageRec& r = p->pages[pg];
+    if (r.in_evict && r.evict_gen == gen) {
+      evict_unlink(p, pg);
+      return pg;
+    }
+  }
+  return -1;
+}
+
+void remove_page_from_seq(SeqRec& q, int32_t pg) {
+  auto it = std::find(q.pages.begin(), q.pages.end(), pg);
+  if (it != q.pages.end()) q.pages.erase(it);
+}
+
+// Reclaim an evictable page: its tokens (all dropped) lose their slot.
+void evict_page(akv_pool* p, int32_t pg) {
+  PageRec& r = p->pages[pg];
+  SeqRec& o = p->seqs[r.owner];
+  for (int32_t t : r.toks) o.slot[t] = -1;
+  r.toks.clear();
+  remove_page_from_seq(o, pg);
+}
+
+int32_t take_page(akv_pool* p, int32_t s) {
+  int32_t pg;
+  if (!p->free_q.empty()) {
+    pg = p->free_q.front();
+    p->free_q.pop_front();
+  } else {
+    pg = evict_pop(p);
+    evict_page(p, pg);
+  }
+  PageRec& r = p->pages[pg];
+  r.owner = s;
+  r.nvis = 0;
+  r.filled = 0;
+  r.toks.clear();
+  p->seqs[s].pages.push_back(pg);
+  return pg;
+}
+
+int64_t pages_needed(const akv_pool* p, const SeqRec& q, int64_t n) {
+  const int64_t S = p->L.page_size;
+  const int64_t room = q.tail >= 0 ? S - p->pages[q.tail].filled : 0;
+  const int64_t extra = std::max<int64_t>(0, n - room);
+  return (extra + S - 1) / S;
+}
+
+// Slots for n new tokens of sequence s (tail page first, then fresh pages).
+void place_tokens(akv_pool* p, int32_t s, int32_t n, const int32_t* pos, int32_t* slots_out) {
+  SeqRec& q = p->seqs[s];
+  const int32_t S = p->L.page_size;
+  const int32_t t0 = (int32_t)q.slot.size();
+  for (int32_t i = 0; i < n; ++i) {
+    if (q.tail < 0) q.tail = take_page(p, s);
+    const int32_t pg = q.tail;
+    PageRec& r = p->pages[pg];
+    const int32_t slot = pg * S + r.filled;
+    r.filled += 1;
+    r.nvis += 1;
+    r.toks.push_back(t0 + i);
+    if (r.filled == S) q.tail = -1;
+    slots_out[i] = slot;
+    q.slot.push_back(slot);
+    q.pos.push_back(pos[i]);
+    q.dropped.push_back(0);
+  }
+  q.n_vis += n;
+  q.vis_ok = false;
+}
+
+akv_status get_seq(akv_pool* p, int32_t s, SeqRec** out) {
+  if (s < 0 || s >= (int32_t)p->seqs.size()) return fail(AKV_EINVAL, "no sequence %d", s);
+  if (!p->seqs[s].alive) return fail(AKV_ESTATE, "sequence %d was released", s);
+  *out = &p->seqs[s];
+  return AKV_OK;
+}
+
+akv_status check_spans(const akv_span* sp, int32_t n, int32_t len) {
+  if (n < 0) return fail(AKV_EINVAL, "negative span count");
+  if (n > 0 && !sp) return fail(AKV_EINVAL, "spans is NULL");
+  for (int32_t i = 0; i < n; ++i) {
+    if (sp[i].begin > sp[i].end) return fail(AKV_EINVAL, "span %d has end < begin", i);
+    if (sp[i].begin < 0 || sp[i].end > len)
+      return fail(AKV_ERANGE, "span %d [%d,%d) outside 0..%d", i, sp[i].begin, sp[i].end, len);
+  }
+  return AKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// visibility
+// ---------------------------------------------------------------------------
+const std::vector<int32_t>& visible(SeqRec& q) {
+  if (q.vis_ok) return q.vis;
+  q.vis.clear();
+  q.vis.reserve(q.n_vis);
+  bool sorted = true;
+  int64_t last = -1;
+  for (int32_t t = 0; t < (int32_t)q.slot.size(); ++t) {
+    if (q.dropped[t]) continue;
+    if (q.pos[t] < last) sorted = false;
+    last = q.pos[t];
+    q.vis.push_back(t);
+  }
+  if (!sorted)
+    std::stable_sort(q.vis.begin(), q.vis.end(),
+                     [&](int32_t a, int32_t b) { return q.pos[a] < q.pos[b]; });
+  q.vis_ok = true;
+  return q.vis;
+}
+
+void build_extents(const akv_pool* p, const SeqRec& q, const std::vector<int32_t>& order,
+                   const std::vector<uint8_t>* hide, std::vector<akv_extent>& out) {
+  const int32_t S = p->L.page_size;
+  out.clear();
+  for (int32_t t : order) {
+    if (hide && (*hide)[t]) continue;
+    const int32_t slot = q.slot[t];
+    const int32_t pg = slot / S, off = slot - pg * S;
+    if (!out.empty() && out.back().page == pg && out.back().hi == off)
+      out.back().hi = off + 1;
+    else
+      out.push_back({pg, off, off + 1});
+  }
+}
+
+double fragmentation(const akv_pool* p, const SeqRec& q) {
+  int64_t cap = 0;
+  for (int32_t pg : q.pages)
+    if (p->pages[pg].nvis > 0) cap += p->pages[pg].filled;
+  if (cap == 0) return 0.0;
+  return 1.0 - (double)q.n_vis / (double)cap;
+}
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+akv_status upload_array(akv_pool* p, ScratchCursor& sc, const void* src, size_t n, void** dev) {
+  char* h;
+  akv_status st = stg_reserve(p, n, &h);
+  if (st != AKV_OK) return st;
+  std::memcpy(h, src, n);
+  *dev = sc.take(n);
+  if (!sc.ok())
+    return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
+  return stg_upload(p, h, *dev, n);
+}
+
+// Per-call scratch bytes left after the persistent tables (a conservative
+// bound checked before any state changes, so a short buffer leaves no trace).
+akv_status scratch_fits(const akv_pool* p, size_t bytes) {
+  if (!p->device) return AKV_OK;
+  const size_t need = p->scratch_base + bytes + 4096;
+  if (need > p->scratch_bytes)
+    return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", need);
+  return AKV_OK;
+}
+
+akv_status check_launch(hipError_t e, const char* what) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  return AKV_OK;
+}
+
+// scatter appended rows of one token batch into the pool arrays
+akv_status device_append(akv_pool* p, const std::vector<int32_t>& slots, const void* K,
+                         const void* Kpe, const void* V) {
+  if (!p->device || !K) return AKV_OK;
+  ScratchCursor sc(p);
+  void* dslots;
+  akv_status st = upload_array(p, sc, slots.data(), slots.size() * 4, &dslots);
+  if (st != AKV_OK) return st;
+  const akv_layout& L = p->L;
+  const int n = (int)slots.size();
+  KTimer tm(p, AKV_K_APPEND);
+  hipError_t e;
+  if (L.d_nope > 0) {
+    e = akv::launch_scatter_rows(p->stream, (const uint16_t*)K, p->k, (const int32_t*)dslots, n,
+                                 L.n_kv_heads, L.page_size, p->log2S, L.d_nope);
+    if (e == hipSuccess)
+      e = akv::launch_scatter_rows(p->stream, (const uint16_t*)Kpe, p->kpe, (const int32_t*)dslots,
+                                   n, p->rope_heads(), L.page_size, p->log2S, L.d_rope);
+  } else {
+    e = akv::launch_scatter_rows(p->stream, (const uint16_t*)K, p->k, (const int32_t*)dslots, n,
+                                 L.n_kv_heads, L.page_size, p->log2S, L.d_rope);
+  }
+  if (e == hipSuccess)
+    e = akv::launch_scatter_rows(p->stream, (const uint16_t*)V, p->v, (const int32_t*)dslots, n,
+                                 L.n_kv_heads, L.page_size, p->log2S, L.d_v);
+  tm.done();
+  return check_launch(e, "append kernel launch");
+}
+
+// rotate the listed (slot, delta) runs; items are built here
+akv_status device_rotate(akv_pool* p, const std::vector<akv::RotItem>& items,
+                         const std::vector<int32_t>& deltas) {
+  if (!p->device || items.empty()) return AKV_OK;
+  ScratchCursor sc(p);
+  void *ditems, *ddeltas;
+  akv_status st = upload_array(p, sc, items.data(), items.size() * sizeof(akv::RotItem), &ditems);
+  if (st == AKV_OK) st = upload_array(p, sc, deltas.data(), deltas.size() * 4, &ddeltas);
+  if (st != AKV_OK) return st;
+  KTimer tm(p, AKV_K_ROTATE);
+  hipError_t e = akv::launch_rotate(p->stream, p->rope_array(), p->rope_heads(), p->L.page_size,
+                                    p->L.d_rope, p->L.pairing, (const akv::RotItem*)ditems,
+                                    (int)items.size(), (const int32_t*)ddeltas,
+                                    (const double*)p->scratch);
+  tm.done();
+  return check_launch(e, "rotate kernel launch");
+}
+
+akv_status device_move(akv_pool* p, const std::vector<akv::MovePair>& mv) {
+  if (!p->device || mv.empty()) return AKV_OK;
+  ScratchCursor sc(p);
+  void* dmv;
+  akv_status st = upload_array(p, sc, mv.data(), mv.size() * sizeof(akv::MovePair), &dmv);
+  if (st != AKV_OK) return st;
+  const akv_layout& L = p->L;
+  const int n = (int)mv.size();
+  KTimer tm(p, AKV_K_COMPACT);
+  hipError_t e;
+  if (L.d_nope > 0) {
+    e = akv::launch_move_rows(p->stream, p->k, (const akv::MovePair*)dmv, n, L.n_kv_heads,
+                              L.page_size, p->log2S, L.d_nope);
+    if (e == hipSuccess)
+      e = akv::launch_move_rows(p->stream, p->kpe, (const akv::MovePair*)dmv, n, p->rope_heads(),
+                                L.page_size, p->log2S, L.d_rope);
+  } else {
+    e = akv::launch_move_rows(p->stream, p->k, (const akv::MovePair*)dmv, n, L.n_kv_heads,
+                              L.page_size, p->log2S, L.d_rope);
+  }
+  if (e == hipSuccess)
+    e = akv::launch_move_rows(p->stream, p->v, (const akv::MovePair*)dmv, n, L.n_kv_heads,
+                              L.page_size, p->log2S, L.d_v);
+  tm.done();
+  return check_launch(e, "compaction kernel launch");
+}
+
+// ---------------------------------------------------------------------------
+// compaction ([AKV-blog] section 7, Dilemma 2)
+// ---------------------------------------------------------------------------
+akv_status compact_seq(akv_pool* p, int32_t s) {
+  SeqRec& q = p->seqs[s];
+  const std::vector<int32_t> order = visible(q);  // copy: q.vis is rebuilt below
+  const int32_t S = p->L.page_size;
+  const int64_t nv = (int64_t)order.size();
+  const int64_t need = (nv + S - 1) / S;
+  if (need > available(p)) return fail(AKV_ENOMEM, "compaction needs %lld free pages", (long long)need);
+  const std::vector<int32_t> old_pages = q.pages;
+  std::vector<int32_t> dest;
+  dest.reserve(need);
+  for (int64_t i = 0; i < need; ++i) dest.push_back(take_page(p, s));
+  std::vector<akv::MovePair> mv;
+  mv.reserve(nv);
+  std::vector<std::vector<int32_t>*> touched;
+  for (int64_t i = 0; i < nv; ++i) {
+    const int32_t t = order[i];
+    const int32_t dst = dest[i / S] * S + (int32_t)(i % S);
+    mv.push_back({q.slot[t], dst});
+    q.slot[t] = dst;
+    p->pages[dest[i / S]].toks.push_back(t);
+  }
+  for (int64_t i = 0; i < need; ++i) {
+    PageRec& r = p->pages[dest[i]];
+    const int32_t c = (int32_t)std::min<int64_t>(S, nv - i * S);
+    r.filled = c;
+    r.nvis = c;
+  }
+  q.tail = (need > 0 && nv % S) ? dest.back() : -1;
+  for (int32_t pg : old_pages) {
+    if (std::find(dest.begin(), dest.end(), pg) != dest.end()) continue;
+    PageRec& r = p->pages[pg];
+    if (r.owner != s) continue;
+    r.nvis = 0;
+    // keep only tokens that still point into this page (the dropped ones)
+    std::vector<int32_t> keep;
+    for (int32_t t : r.toks)
+      if (q.slot[t] >= 0 && q.slot[t] / S == pg) keep.push_back(t);
+    r.toks.swap(keep);
+    if (!r.in_evict) evict_push(p, pg);
+  }
+  q.vis_ok = false;
+  return device_move(p, mv);
+}
+
+void drop_tokens(akv_pool* p, SeqRec& q, int32_t b, int32_t e) {
+  const int32_t S = p->L.page_size;
+  for (int32_t t = b; t < e; ++t) {
+    if (q.dropped[t]) continue;
+    q.dropped[t] = 1;
+    q.n_vis -= 1;
+    const int32_t pg = q.slot[t] / S;
+    PageRec& r = p->pages[pg];
+    r.nvis -= 1;
+    if (r.nvis == 0 && pg != q.tail && !r.in_evict) evict_push(p, pg);
+  }
+  q.vis_ok = false;
+}
+
+akv_status auto_compact(akv_pool* p, int32_t s) {
+  SeqRec& q = p->seqs[s];
+  if (fragmentation(p, q) > p->thr) {
+    const int64_t need = (q.n_vis + p->L.page_size - 1) / p->L.page_size;
+    if (need <= available(p)) return compact_seq(p, s);
+  }
+  return AKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// repos planning ([AKV-blog] section 2; [Leyline] Method)
+// ---------------------------------------------------------------------------
+// Per-token total delta (difference array over the spans); dropped tokens get 0.
+akv_status repos_totals(akv_pool* p, SeqRec& q, const akv_span* sp, const int32_t* d, int32_t n,
+                        std::vector<int64_t>& tot) {
+  const int32_t len = (int32_t)q.slot.size();
+  akv_status st = check_spans(sp, n, len);
+  if (st != AKV_OK) return st;
+  if (n > 0 && !d) return fail(AKV_EINVAL, "delta is NULL");
+  std::vector<int64_t> diff(len + 1, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    diff[sp[i].begin] += d[i];
+    diff[sp[i].end] -= d[i];
+  }
+  tot.assign(len, 0);
+  int64_t run = 0;
+  for (int32_t t = 0; t < len; ++t) {
+    run += diff[t];
+    if (q.dropped[t] || run == 0) continue;
+    const int64_t np = (int64_t)q.pos[t] + run;
+    if (np < 0 || np > kInt32Max)
+      return fail(AKV_ERANGE, "token %d would move to position %lld", t, (long long)np);
+    tot[t] = run;
+  }
+  return AKV_OK;
+}
+
+// Work items: runs of consecutive slots of one page with one delta, in logical
+// token order.
+void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<int64_t>& tot,
+                 std::vector<akv::RotItem>& items, std::vector<int32_t>& deltas) {
+  const int32_t S = p->L.page_size;
+  std::unordered_map<int64_t, int32_t> didx;
+  items.clear();
+  deltas.clear();
+  for (int32_t t = 0; t < (int32_t)tot.size(); ++t) {
+    if (tot[t] == 0) continue;
+    const int32_t slot = q.slot[t];
+    const int32_t pg = slot / S, off = slot - pg * S;
+    auto f = didx.find(tot[t]);
+    int32_t di;
+    if (f == didx.end()) {
+      di = (int32_t)deltas.size();
+      deltas.push_back((int32_t)tot[t]);
+      didx.emplace(tot[t], di);
+    } else {
+      di = f->second;
+    }
+    if (!items.empty() && items.back().page == pg && items.back().hi == off &&
+        items.back().didx == di)
+      items.back().hi += 1;
+    else
+      items.push_back({pg, off, off + 1, di});
+  }
+}
+
+void repos_commit(SeqRec& q, const std::vector<int64_t>& tot) {
+  for (size_t t = 0; t < tot.size(); ++t)
+    if (tot[t]) q.pos[t] = (int32_t)(q.pos[t] + tot[t]);
+  q.vis_ok = false;
+}
+
+// ---------------------------------------------------------------------------
+// attention planning ([AKV-notes] section 3; [AKV-blog] section 4)
+// ---------------------------------------------------------------------------
+struct AttnPlan {
+  std::vector<akv::AttnSeg> segs;
+  std::vector<akv::AttnItem> items;  // grid order (XCD interleaved, padded)
+  std::vector<akv::CombItem> comb;
+  std::vector<int32_t> ext_off;
+  int64_t total_list = 0;
+  int32_t n_parts = 0;
+};
+
+constexpr int kXcds = 8;
+
+void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
+                    const std::vector<int64_t>& lkv, const std::vector<int64_t>& list_off,
+                    AttnPlan& plan) {
+  const akv_layout& L = p->L;
+  const int G = L.n_q_heads / L.n_kv_heads;
+  const int RB = akv::ATTN_ROWS;
+  const int KT = akv::ATTN_KTILE;
+  plan.segs.clear();
+  for (int32_t i = 0; i < n_segs; ++i)
+    plan.segs.push_back({segs[i].q_begin, segs[i].q_len, (int32_t)lkv[i], (int32_t)list_off[i]});
+  // base work: row tiles per (segment, kv head)
+  int64_t base = 0;
+  for (int32_t i = 0; i < n_segs; ++i)
+    if (segs[i].q_len > 0) base += (int64_t)L.n_kv_heads * ((segs[i].q_len * (int64_t)G + RB - 1) / RB);
+  int target = 1;
+  if (base > 0 && base < 2LL * p->n_cu) target = (int)std::min<int64_t>(16, (2LL * p->n_cu + base - 1) / base);
+
+  struct Group {
+    int64_t cost;
+    std::vector<akv::AttnItem> items;
+  };
+  std::vector<Group> groups;
+  plan.comb.clear();
+  int32_t part = 0;
+  for (int32_t i = 0; i < n_segs; ++i) {
+    const int32_t lq = segs[i].q_len;
+    if (lq <= 0) continue;
+    const int64_t rows = (int64_t)lq * G;
+    const int64_t ntile_rows = (rows + RB - 1) / RB;
+    const int64_t key_tiles = (lkv[i] + KT - 1) / KT;
+    int ns = target;
+    ns = (int)std::min<int64_t>(ns, std::max<int64_t>(1, lkv[i] / 512));
+    ns = (int)std::min<int64_t>(ns, key_tiles);
+    if (ns < 1) ns = 1;
+    for (int32_t h = 0; h < L.n_kv_heads; ++h) {
+      for (int sp = 0; sp < ns; ++sp) {
+        const int64_t tb = key_tiles * sp / ns, te = key_tiles * (sp + 1) / ns;
+        const int32_t kb = (int32_t)(tb * KT), ke = (int32_t)std::min<int64_t>(te * KT, lkv[i]);
+        Group gr;
+        gr.cost = 0;
+        for (int64_t m = 0; m < ntile_rows; ++m) {
+          const int32_t row0 = (int32_t)(m * RB);
+          const int64_t last_row = std::min<int64_t>(row0 + RB, rows) - 1;
+          const int64_t lim_last = lkv[i] - lq + last_row / G;
+          const int64_t keys = std::max<int64_t>(0, std::min<int64_t>(ke, lim_last + 1) - kb);
+          int32_t pidx = -1;
+          if (ns > 1) pidx = part + (int32_t)(m * ns + sp);
+          gr.items.push_back({i, h, row0, kb, ke, pidx});
+          gr.cost += keys + 64;  // + fixed cost of a block
+        }
+        groups.push_back(std::move(gr));
+      }
+      if (ns > 1) {
+        for (int64_t m = 0; m < ntile_rows; ++m)
+          plan.comb.push_back({i, h, (int32_t)(m * RB), part + (int32_t)(m * ns), ns, 0});
+        part += (int32_t)(ntile_rows * ns);
+      }
+    }
+  }
+  plan.n_parts = part;
+  // longest groups first, each to the least loaded XCD; inside a group, its
+  // row tiles stay together so they share K/V in that XCD's L2
+  std::stable_sort(groups.begin(), groups.end(),
+                   [](const Group& a, const Group& b) { return a.cost > b.cost; });
+  std::vector<std::vector<akv::AttnItem>> bins(kXcds);
+  std::vector<int64_t> load(kXcds, 0);
+  for (auto& gr : groups) {
+    int best = 0;
+    for (int x = 1; x < kXcds; ++x)
+      if (load[x] < load[best]) best = x;
+    load[best] += gr.cost;
+    for (auto& it : gr.items) bins[best].push_back(it);
+  }
+  size_t depth = 0;
+  for (auto& b : bins) depth = std::max(depth, b.size());
+  plan.items.assign(depth * kXcds, akv::AttnItem{-1, 0, 0, 0, 0, -1});
+  for (int x = 0; x < kXcds; ++x)
+    for (size_t i = 0; i < bins[x].size(); ++i) plan.items[i * kXcds + x] = bins[x][i];
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* akv_last_error(void) { return g_err.c_str(); }
+
+akv_status akv_pool_create(const akv_layout* layout, const int32_t* page_order, void* k_pages,
+                           void* kpe_pages, void* v_pages, void* scratch, size_t scratch_bytes,
+                           void* hip_stream, akv_pool** out) {
+  try {
+    if (!layout || !out) return fail(AKV_EINVAL, "layout and out must be non-NULL");
+    const akv_layout& L = *layout;
+    if (L.n_kv_heads <= 0 || L.n_q_heads <= 0 || L.n_q_heads % L.n_kv_heads)
+      return fail(AKV_EINVAL, "n_q_heads must be a positive multiple of n_kv_heads");
+    if (L.d_rope <= 0 || L.d_rope % 16 || L.d_rope > 256)
+      return fail(AKV_EINVAL, "d_rope must be a multiple of 16 in 16..256");
+    if (L.d_nope < 0 || L.d_nope % 8 || L.d_v <= 0 || L.d_v % 8)
+      return fail(AKV_EINVAL, "d_nope and d_v must be multiples of 8");
+    if (L.page_size < 1 || L.page_size > 256 || (L.page_size & (L.page_size - 1)))
+      return fail(AKV_EINVAL, "page_size must be a power of two in 1..256");
+    if (L.num_pages <= 0 || (int64_t)L.num_pages * L.page_size > kInt32Max)
+      return fail(AKV_EINVAL, "num_pages out of range");
+    if (L.pairing != 0 && L.pairing != 1) return fail(AKV_EINVAL, "pairing must be 0 or 1");
+    if (L.d_nope == 0 && L.kpe_per_head) return fail(AKV_EINVAL, "kpe_per_head needs an MLA layout");
+    const bool any_dev = k_pages || kpe_pages || v_pages || scratch;
+    if (any_dev) {
+      if (!k_pages || !v_pages) return fail(AKV_EINVAL, "k_pages and v_pages are required");
+      if ((L.d_nope > 0) != (kpe_pages != nullptr))
+        return fail(AKV_EINVAL, "kpe_pages is required exactly for MLA layouts (d_nope > 0)");
+      if (!scratch) return fail(AKV_EINVAL, "scratch is required for a device pool");
+    }
+    if (!L.inv_freq && !(L.rope_theta > 0)) return fail(AKV_EINVAL, "rope_theta must be > 0");
+    std::vector<int32_t> order(L.num_pages);
+    if (page_order) {
+      std::vector<uint8_t> seen(L.num_pages, 0);
+      for (int32_t i = 0; i < L.num_pages; ++i) {
+        const int32_t pg = page_order[i];
+        if (pg < 0 || pg >= L.num_pages || seen[pg])
+          return fail(AKV_EINVAL, "page_order is not a permutation of 0..num_pages-1");
+        seen[pg] = 1;
+        order[i] = pg;
+      }
+    } else {
+      for (int32_t i = 0; i < L.num_pages; ++i) order[i] = i;
+    }
+    akv_pool* p = new akv_pool();
+    p->L = L;
+    p->L.inv_freq = nullptr;
+    p->inv_freq.resize(L.d_rope / 2);
+    for (int i = 0; i < L.d_rope / 2; ++i)
+      p->inv_freq[i] = L.inv_freq ? L.inv_freq[i] : std::pow(L.rope_theta, -2.0 * i / L.d_rope);
+    p->log2S = 0;
+    while ((1 << p->log2S) < L.page_size) ++p->log2S;
+    p->thr = L.compact_threshold > 0 ? L.compact_threshold : kDefaultCompactThreshold;
+    p->free_q.assign(order.begin(), order.end());
+    p->pages.resize(L.num_pages);
+    p->device = any_dev;
+    if (p->device) {
+      p->k = (uint16_t*)k_pages;
+      p->kpe = (uint16_t*)kpe_pages;
+      p->v = (uint16_t*)v_pages;
+      p->scratch = (char*)scratch;
+      p->scratch_bytes = scratch_bytes;
+      p->stream = (hipStream_t)hip_stream;
+      const size_t tab = align_up(sizeof(double) * p->inv_freq.size(), 256);
+      if (scratch_bytes < tab + 65536) {
+        delete p;
+        return fail(AKV_ENOMEM, "scratch must hold at least %zu bytes", tab + 65536);
+      }
+      int dev = 0;
+      hipDeviceProp_t prop;
+      if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+        p->n_cu = prop.multiProcessorCount;
+      p->scratch_base = tab;
+      char* h;
+      akv_status st = stg_reserve(p, tab, &h);
+      if (st == AKV_OK) {
+        std::memcpy(h, p->inv_freq.data(), sizeof(double) * p->inv_freq.size());
+        st = stg_upload(p, h, p->scratch, sizeof(double) * p->inv_freq.size());
+      }
+      if (st == AKV_OK) {
+        hipError_t e = hipStreamSynchronize(p->stream);
+        if (e != hipSuccess) st = hip_fail(e, "hipStreamSynchronize");
+      }
+      if (st != AKV_OK) {
+        akv_pool_destroy(p);
+        return st;
+      }
+    }
+    *out = p;
+    return AKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_pool_destroy(akv_pool* p) {
+  if (!p) return AKV_OK;
+  if (p->device) (void)hipStreamSynchronize(p->stream);
+  for (auto& r : p->stg.pending) (void)hipEventDestroy(r.ev);
+  for (auto e : p->stg.spare) (void)hipEventDestroy(e);
+  if (p->stg.base) (void)hipHostFree(p->stg.base);
+  for (auto& t : p->tev) {
+    (void)hipEventDestroy(t.a);
+    (void)hipEventDestroy(t.b);
+  }
+  for (auto e : p->ev_spare) (void)hipEventDestroy(e);
+  delete p;
+  return AKV_OK;
+}
+
+akv_status akv_seq_create(akv_pool* p, int32_t* seq) {
+  if (!p || !seq) return fail(AKV_EINVAL, "NULL argument");
+  try {
+    p->seqs.emplace_back();
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+  *seq = (int32_t)p->seqs.size() - 1;
+  return AKV_OK;
+}
+
+akv_status akv_seq_release(akv_pool* p, int32_t s) {
+  if (!p) return fail(AKV_EINVAL, "NULL pool");
+  SeqRec* q;
+  akv_status st = get_seq(p, s, &q);
+  if (st != AKV_OK) return st;
+  for (int32_t pg : q->pages) {
+    PageRec& r = p->pages[pg];
+    if (r.in_evict) evict_unlink(p, pg);
+    r.owner = -1;
+    r.nvis = 0;
+    r.filled = 0;
+    r.toks.clear();
+    p->free_q.push_back(pg);
+  }
+  q->pages.clear();
+  q->tail = -1;
+  q->alive = false;
+  q->vis.clear();
+  q->vis_ok = false;
+  return AKV_OK;
+}
+
+akv_status akv_append(akv_pool* p, int32_t s, const void* K, const void* K_pe, const void* V,
+                      const int32_t* pos, int32_t n) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    SeqRec* q;
+    akv_status st = get_seq(p, s, &q);
+    if (st != AKV_OK) return st;
+    if (n < 0) return fail(AKV_EINVAL, "negative token count");
+    if (n == 0) return AKV_OK;
+    if (!pos) return fail(AKV_EINVAL, "pos is NULL");
+    const bool mla = p->L.d_nope > 0;
+    const bool none = !K && !K_pe && !V;
+    if (!none) {
+      if (!p->device) return fail(AKV_EINVAL, "a page-table-only pool takes no K/V data");
+      if (!K || !V || (mla != (K_pe != nullptr)))
+        return fail(AKV_EINVAL, "K and V (and K_pe exactly for MLA) must be given together");
+    }
+    for (int32_t i = 0; i < n; ++i)
+      if (pos[i] < 0) return fail(AKV_ERANGE, "position %d of token %d is negative", pos[i], i);
+    if ((int64_t)q->slot.size() + n > kInt32Max) return fail(AKV_ERANGE, "sequence too long");
+    if (pages_needed(p, *q, n) > available(p))
+      return fail(AKV_ENOMEM, "pool exhausted: %lld pages needed, %lld available",
+                  (long long)pages_needed(p, *q, n), (long long)available(p));
+    if (!none) {
+      st = scratch_fits(p, (size_t)n * 4 + 256);
+      if (st != AKV_OK) return st;
+    }
+    std::vector<int32_t> slots(n);
+    place_tokens(p, s, n, pos, slots.data());
+    return device_append(p, slots, K, K_pe, V);
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_drop(akv_pool* p, int32_t s, const akv_span* spans, int32_t n) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    SeqRec* q;
+    akv_status st = get_seq(p, s, &q);
+    if (st != AKV_OK) return st;
+    st = check_spans(spans, n, (int32_t)q->slot.size());
+    if (st != AKV_OK) return st;
+    st = scratch_fits(p, (size_t)q->n_vis * sizeof(akv::MovePair) + 256);
+    if (st != AKV_OK) return st;
+    for (int32_t i = 0; i < n; ++i) drop_tokens(p, *q, spans[i].begin, spans[i].end);
+    return auto_compact(p, s);
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_compact(akv_pool* p, int32_t s, int32_t force) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    SeqRec* q;
+    akv_status st = get_seq(p, s, &q);
+    if (st != AKV_OK) return st;
+    if (!force && fragmentation(p, *q) <= p->thr) return AKV_OK;
+    st = scratch_fits(p, (size_t)q->n_vis * sizeof(akv::MovePair) + 256);
+    if (st != AKV_OK) return st;
+    return compact_seq(p, s);
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_repos(akv_pool* p, int32_t s, const akv_span* spans, const int32_t* delta,
+                     int32_t n) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    SeqRec* q;
+    akv_status st = get_seq(p, s, &q);
+    if (st != AKV_OK) return st;
+    std::vector<int64_t> tot;
+    st = repos_totals(p, *q, spans, delta, n, tot);
+    if (st != AKV_OK) return st;
+    std::vector<akv::RotItem> items;
+    std::vector<int32_t> deltas;
+    repos_items(p, *q, tot, items, deltas);
+    st = scratch_fits(p, items.size() * sizeof(akv::RotItem) + deltas.size() * 4 + 512);
+    if (st != AKV_OK) return st;
+    st = device_rotate(p, items, deltas);
+    if (st != AKV_OK) return st;
+    repos_commit(*q, tot);
+    return AKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_repos_plan(akv_pool* p, int32_t s, const akv_span* spans, const int32_t* delta,
+                          int32_t n, int32_t* slot_out, int32_t* delta_out, int32_t cap,
+                          int32_t* n_out) {
+  try {
+    if (!p || !n_out) return fail(AKV_EINVAL, "NULL argument");
+    SeqRec* q;
+    akv_status st = get_seq(p, s, &q);
+    if (st != AKV_OK) return st;
+    std::vector<int64_t> tot;
+    st = repos_totals(p, *q, spans, delta, n, tot);
+    if (st != AKV_OK) return st;
+    std::vector<akv::RotItem> items;
+    std::vector<int32_t> deltas;
+    repos_items(p, *q, tot, items, deltas);
+    int32_t k = 0;
+    const int32_t S = p->L.page_size;
+    for (auto& it : items)
+      for (int32_t o = it.lo; o < it.hi; ++o) {
+        if (k < cap) {
+          if (slot_out) slot_out[k] = it.page * S + o;
+          if (delta_out) delta_out[k] = deltas[it.didx];
+        }
+        ++k;
+      }
+    *n_out = k;
+    if (k > cap) return fail(AKV_ERANGE, "plan has %d entries, cap %d", k, cap);
+    return AKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_splice(akv_pool* p, int32_t s, const akv_span* spans, const int32_t* stub_len,
+                      int32_t n, const void* sK, const void* sKpe, const void* sV,
+                      int32_t* stub_pos_out) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    SeqRec* q;
+    akv_status st = get_seq(p, s, &q);
+    if (st != AKV_OK) return st;
+    if (n < 0) return fail(AKV_EINVAL, "negative splice count");
+    if (n == 0) return AKV_OK;
+    if (!spans || !stub_len) return fail(AKV_EINVAL, "spans and stub_len are required");
+    const std::vector<int32_t> vis = visible(*q);
+    const int32_t H = (int32_t)vis.size();
+    int64_t n_stub = 0;
+    for (int32_t j = 0; j < n; ++j) {
+      if (spans[j].begin >= spans[j].end || stub_len[j] < 0)
+        return fail(AKV_EINVAL, "splice %d: empty span or negative stub", j);
+      if (spans[j].begin < 0 || spans[j].end > H)
+        return fail(AKV_ERANGE, "splice %d outside the visible list of %d entries", j, H);
+      if (j && spans[j].begin < spans[j - 1].end)
+        return fail(AKV_EINVAL, "splice spans must be sorted and disjoint");
+      n_stub += stub_len[j];
+    }
+    const bool mla = p->L.d_nope > 0;
+    const bool none = !sK && !sKpe && !sV;
+    if (n_stub > 0 && !none) {
+      if (!p->device) return fail(AKV_EINVAL, "a page-table-only pool takes no K/V data");
+      if (!sK || !sV || (mla != (sKpe != nullptr)))
+        return fail(AKV_EINVAL, "stub K and V (and K_pe exactly for MLA) must be given together");
+    }
+    // per-splice delta |R| - (end - begin), downstream sums, stub positions
+    std::vector<int64_t> dj(n);
+    for (int32_t j = 0; j < n; ++j) dj[j] = (int64_t)stub_len[j] - (spans[j].end - spans[j].begin);
+    std::vector<int64_t> down(H, 0);
+    {
+      int64_t run = 0;
+      int32_t j = 0;
+      for (int32_t i = 0; i < H; ++i) {
+        while (j < n && spans[j].end <= i) run += dj[j++];
+        down[i] = run;
+      }
+    }
+    std::vector<int32_t> stub_pos;
+    stub_pos.reserve(n_stub);
+    {
+      int64_t before = 0;
+      for (int32_t j = 0; j < n; ++j) {
+        const int64_t p0 = (int64_t)q->pos[vis[spans[j].begin]] + before;
+        for (int32_t k = 0; k < stub_len[j]; ++k) {
+          const int64_t ps = p0 + k;
+          if (ps < 0 || ps > kInt32Max) return fail(AKV_ERANGE, "stub position out of range");
+          stub_pos.push_back((int32_t)ps);
+        }
+        before += dj[j];
+      }
+    }
+    std::vector<uint8_t> in_span(H, 0);
+    for (int32_t j = 0; j < n; ++j)
+      for (int32_t i = spans[j].begin; i < spans[j].end; ++i) in_span[i] = 1;
+    std::vector<int64_t> tot(q->slot.size(), 0);
+    for (int32_t i = 0; i < H; ++i) {
+      if (in_span[i] || down[i] == 0) continue;
+      const int64_t np = (int64_t)q->pos[vis[i]] + down[i];
+      if (np < 0 || np > kInt32Max) return fail(AKV_ERANGE, "splice moves a position out of range");
+      tot[vis[i]] = down[i];
+    }
+    // pages for the stubs, counting those the drop will make evictable
+    {
+      std::vector<int32_t> nv_left;
+      int64_t freed = 0;
+      std::unordered_map<int32_t, int32_t> dec;
+      for (int32_t i = 0; i < H; ++i)
+        if (in_span[i]) dec[q->slot[vis[i]] / p->L.page_size] += 1;
+      for (auto& kv : dec) {
+        const PageRec& r = p->pages[kv.first];
+        if (r.nvis - kv.second == 0 && kv.first != q->tail && !r.in_evict) ++freed;
+      }
+      if (pages_needed(p, *q, n_stub) > available(p) + freed)
+        return fail(AKV_ENOMEM, "pool exhausted for the splice stubs");
+    }
+    // worst-case scratch of the stub copy, the rotation list and a compaction
+    st = scratch_fits(p, std::max<size_t>((size_t)n_stub * 4 + (size_t)H * (sizeof(akv::RotItem) + 4) + 1024,
+                                          (size_t)(q->n_vis + n_stub) * sizeof(akv::MovePair) + 256));
+    if (st != AKV_OK) return st;
+    // apply: drop, append stubs, rotate downstream (one launch), positions
+    for (int32_t i = 0; i < H; ++i)
+      if (in_span[i]) drop_tokens(p, *q, vis[i], vis[i] + 1);
+    if (n_stub > 0) {
+      std::vector<int32_t> slots(n_stub);
+      place_tokens(p, s, (int32_t)n_stub, stub_pos.data(), slots.data());
+      st = device_append(p, slots, sK, sKpe, sV);
+      if (st != AKV_OK) return st;
+    }
+    tot.resize(q->slot.size(), 0);
+    std::vector<akv::RotItem> items;
+    std::vector<int32_t> deltas;
+    repos_items(p, *q, tot, items, deltas);
+    st = device_rotate(p, items, deltas);
+    if (st != AKV_OK) return st;
+    repos_commit(*q, tot);
+    if (stub_pos_out) std::copy(stub_pos.begin(), stub_pos.end(), stub_pos_out);
+    return auto_compact(p, s);
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_seq_visible(akv_pool* p, int32_t s, const akv_span* mask, int32_t n_mask,
+                           akv_extent* out, int32_t cap, int32_t* n_out) {
+  try {
+    if (!p || !n_out) return fail(AKV_EINVAL, "NULL argument");
+    SeqRec* q;
+    akv_status st = get_seq(p, s, &q);
+    if (st != AKV_OK) return st;
+    st = check_spans(mask, n_mask, (int32_t)q->slot.size());
+    if (st != AKV_OK) return st;
+    const std::vector<int32_t>& vis = visible(*q);
+    std::vector<uint8_t> hide;
+    if (n_mask > 0) {
+      hide.assign(q->slot.size(), 0);
+      for (int32_t i = 0; i < n_mask; ++i)
+        std::fill(hide.begin() + mask[i].begin, hide.begin() + mask[i].end, 1);
+    }
+    std::vector<akv_extent> ex;
+    build_extents(p, *q, vis, n_mask > 0 ? &hide : nullptr, ex);
+    *n_out = (int32_t)ex.size();
+    if ((int32_t)ex.size() > cap) return fail(AKV_ERANGE, "%zu extents, cap %d", ex.size(), cap);
+    if (!ex.empty()) {
+      if (!out) return fail(AKV_EINVAL, "out is NULL");
+      std::memcpy(out, ex.data(), ex.size() * sizeof(akv_extent));
+    }
+    return AKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
+                                 const akv_segment* segs, int32_t n_segs,
+                                 const akv_extent* page_lists, int32_t n_ext, float scale,
+                                 void* out) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    if (!p->device) return fail(AKV_ESTATE, "attention needs a device pool");
+    const akv_layout& L = p->L;
+    if (!akv::attn_dims_supported(L.d_nope, L.d_rope, L.d_v))
+      return fail(AKV_EINVAL, "no attention kernel for d_nope=%d d_rope=%d d_v=%d", L.d_nope,
+                  L.d_rope, L.d_v);
+    if (n_segs < 0 || n_ext < 0 || n_q_tokens < 0) return fail(AKV_EINVAL, "negative count");
+    if ((n_segs > 0 && !segs) || (n_ext > 0 && !page_lists))
+      return fail(AKV_EINVAL, "segments / page lists are NULL");
+    if (!(scale >= 0.f) || !std::isfinite(scale)) return fail(AKV_EINVAL, "bad scale");
+    std::vector<int64_t> lkv(n_segs, 0), list_off(n_segs, 0);
+    int64_t total = 0;
+    std::vector<std::pair<int32_t, int32_t>> rows;
+    for (int32_t i = 0; i < n_segs; ++i) {
+      const akv_segment& sg = segs[i];
+      if (sg.q_len < 0 || sg.ext_len < 0) return fail(AKV_EINVAL, "segment %d: negative length", i);
+      if (sg.q_begin < 0 || (int64_t)sg.q_begin + sg.q_len > n_q_tokens)
+        return fail(AKV_ERANGE, "segment %d: query rows outside 0..%d", i, n_q_tokens);
+      if (sg.ext_begin < 0 || (int64_t)sg.ext_begin + sg.ext_len > n_ext)
+        return fail(AKV_ERANGE, "segment %d: extents outside 0..%d", i, n_ext);
+      int64_t n_keys = 0;
+      for (int32_t e = sg.ext_begin; e < sg.ext_begin + sg.ext_len; ++e) {
+        const akv_extent& x = page_lists[e];
+        if (x.page < 0 || x.page >= L.num_pages || x.lo < 0 || x.lo >= x.hi || x.hi > L.page_size)
+          return fail(AKV_ERANGE, "extent %d (%d, %d, %d) outside the pool", e, x.page, x.lo, x.hi);
+        n_keys += x.hi - x.lo;
+      }
+      if (sg.q_len > 0 && n_keys < sg.q_len)
+        return fail(AKV_EINVAL, "segment %d has %lld list entries for %d queries", i,
+                    (long long)n_keys, sg.q_len);
+      if (n_keys > kInt32Max) return fail(AKV_ERANGE, "segment %d list too long", i);
+      lkv[i] = n_keys;
+      list_off[i] = total;
+      total += n_keys;
+      if (sg.q_len > 0) rows.emplace_back(sg.q_begin, sg.q_begin + sg.q_len);
+    }
+    std::sort(rows.begin(), rows.end());
+    for (size_t i = 1; i < rows.size(); ++i)
+      if (rows[i].first < rows[i - 1].second) return fail(AKV_EINVAL, "segments overlap in Q rows");
+    if (rows.empty()) return AKV_OK;
+    if (!Q || !out) return fail(AKV_EINVAL, "Q and out are required");
+    if (total > kInt32Max) return fail(AKV_ERANGE, "page lists too long");
+
+    AttnPlan plan;
+    plan_attention(p, segs, n_segs, lkv, list_off, plan);
+    // extent offsets for the slot expansion (over all segments' ranges, in order)
+    std::vector<akv::Extent> ex_used;
+    std::vector<int32_t> ex_off;
+    for (int32_t i = 0; i < n_segs; ++i) {
+      int64_t o = list_off[i];
+      for (int32_t e = segs[i].ext_begin; e < segs[i].ext_begin + segs[i].ext_len; ++e) {
+        const akv_extent& x = page_lists[e];
+        ex_used.push_back({x.page, x.lo, x.hi});
+        ex_off.push_back((int32_t)o);
+        o += x.hi - x.lo;
+      }
+    }
+    ScratchCursor sc(p);
+    void *dsegs, *ditems, *dcomb = nullptr, *dex, *doff;
+    akv_status st = upload_array(p, sc, plan.segs.data(), plan.segs.size() * sizeof(akv::AttnSeg), &dsegs);
+    if (st == AKV_OK)
+      st = upload_array(p, sc, plan.items.data(), plan.items.size() * sizeof(akv::AttnItem), &ditems);
+    if (st == AKV_OK && !plan.comb.empty())
+      st = upload_array(p, sc, plan.comb.data(), plan.comb.size() * sizeof(akv::CombItem), &dcomb);
+    if (st == AKV_OK) st = upload_array(p, sc, ex_used.data(), ex_used.size() * sizeof(akv::Extent), &dex);
+    if (st == AKV_OK) st = upload_array(p, sc, ex_off.data(), ex_off.size() * 4, &doff);
+    if (st != AKV_OK) return st;
+    int32_t* dslots = (int32_t*)sc.take((size_t)std::max<int64_t>(total, 1) * 4);
+    float* part_o = nullptr;
+    float* part_ml = nullptr;
+    if (plan.n_parts > 0) {
+      part_o = (float*)sc.take((size_t)plan.n_parts * akv::ATTN_ROWS * L.d_v * 4);
+      part_ml = (float*)sc.take((size_t)plan.n_parts * akv::ATTN_ROWS * 2 * 4);
+    }
+    if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
+
+    hipError_t e;
+    {
+      KTimer tm(p, AKV_K_EXPAND);
+      e = akv::launch_expand(p->stream, (const akv::Extent*)dex, (const int32_t*)doff,
+                             (int)ex_used.size(), L.page_size, dslots);
+      tm.done();
+    }
+    if (e != hipSuccess) return hip_fail(e, "expand kernel launch");
+    akv::AttnArgs a{};
+    a.q = (const uint16_t*)Q;
+    a.n_q_heads = L.n_q_heads;
+    a.group = L.n_q_heads / L.n_kv_heads;
+    a.k_a = p->k;
+    a.k_b = p->kpe;
+    a.kpe_heads = p->rope_heads();
+    a.v = p->v;
+    a.n_kv_heads = L.n_kv_heads;
+    a.page_size = L.page_size;
+    a.log2_page = p->log2S;
+    a.segs = (const akv::AttnSeg*)dsegs;
+    a.items = (const akv::AttnItem*)ditems;
+    a.n_items = (int)plan.items.size();
+    a.slots = dslots;
+    const float sc_ = scale > 0.f ? scale : 1.f / std::sqrt((float)(L.d_nope + L.d_rope));
+    a.scale_log2e = sc_ * 1.4426950408889634f;
+    a.out = (uint16_t*)out;
+    a.part_o = part_o;
+    a.part_ml = part_ml;
+    {
+      KTimer tm(p, AKV_K_ATTN);
+      e = akv::launch_seg_attn(p->stream, a, L.d_nope, L.d_rope, L.d_v);
+      tm.done();
+    }
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    if (!plan.comb.empty()) {
+      KTimer tm(p, AKV_K_COMBINE);
+      e = akv::launch_combine(p->stream, a, (const akv::CombItem*)dcomb, (int)plan.comb.size(), L.d_v);
+      tm.done();
+      if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+    }
+    return AKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_seq_tokens(akv_pool* p, int32_t s, int32_t first, int32_t n, int32_t* slot,
+                          int32_t* pos, uint8_t* dropped) {
+  if (!p) return fail(AKV_EINVAL, "NULL pool");
+  SeqRec* q;
+  akv_status st = get_seq(p, s, &q);
+  if (st != AKV_OK) return st;
+  if (first < 0 || n < 0 || (int64_t)first + n > (int64_t)q->slot.size())
+    return fail(AKV_ERANGE, "tokens %d..%d outside 0..%zu", first, first + n, q->slot.size());
+  for (int32_t i = 0; i < n; ++i) {
+    if (slot) slot[i] = q->slot[first + i];
+    if (pos) pos[i] = q->pos[first + i];
+    if (dropped) dropped[i] = q->dropped[first + i];
+  }
+  return AKV_OK;
+}
+
+akv_status akv_seq_info(akv_pool* p, int32_t s, int32_t* n_tokens, int32_t* n_visible,
+                        double* frag) {
+  if (!p) return fail(AKV_EINVAL, "NULL pool");
+  SeqRec* q;
+  akv_status st = get_seq(p, s, &q);
+  if (st != AKV_OK) return st;
+  if (n_tokens) *n_tokens = (int32_t)q->slot.size();
+  if (n_visible) *n_visible = (int32_t)q->n_vis;
+  if (frag) *frag = fragmentation(p, *q);
+  return AKV_OK;
+}
+
+akv_status akv_pool_queues(akv_pool* p, int32_t* free_out, int32_t free_cap, int32_t* n_free,
+                           int32_t* evict_out, int32_t evict_cap, int32_t* n_evict) {
+  if (!p) return fail(AKV_EINVAL, "NULL pool");
+  int32_t k = 0;
+  for (int32_t pg : p->free_q) {
+    if (free_out && k < free_cap) free_out[k] = pg;
+    ++k;
+  }
+  if (n_free) *n_free = k;
+  k = 0;
+  for (auto& e : p->evict_q) {
+    const PageRec& r = p->pages[e.first];
+    if (!(r.in_evict && r.evict_gen == e.second)) continue;
+    if (evict_out && k < evict_cap) evict_out[k] = e.first;
+    ++k;
+  }
+  if (n_evict) *n_evict = k;
+  return AKV_OK;
+}
+
+akv_status akv_timing_enable(akv_pool* p, int32_t enable) {
+  if (!p) return fail(AKV_EINVAL, "NULL pool");
+  p->timing = enable != 0;
+  return AKV_OK;
+}
+
+akv_status akv_timing_read(akv_pool* p, int32_t kind, double* total_ms, int32_t* count) {
+  if (!p) return fail(AKV_EINVAL, "NULL pool");
+  if (kind < 0 || kind >= AKV_K_KINDS) return fail(AKV_EINVAL, "bad kernel kind %d", kind);
+  akv_status st = timing_collect(p);
+  if (st != AKV_OK) return st;
+  if (total_ms) *total_ms = p->t_ms[kind];
+  if (count) *count = p->t_cnt[kind];
+  p->t_ms[kind] = 0;
+  p->t_cnt[kind] = 0;
+  return AKV_OK;
+}
+
+akv_status akv_sync(akv_pool* p) {
+  if (!p) return fail(AKV_EINVAL, "NULL pool");
+  if (!p->device) return AKV_OK;
+  hipError_t e = hipStreamSynchronize(p->stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  return AKV_OK;
+}
+
+}  // extern "C"

@@ -337,8 +337,12 @@ class Pool:
         return 1.0 - int(np.count_nonzero(~q.dropped)) / cap
 
     def _auto_compact(self, s: int) -> None:
+        """Automatic compaction is opportunistic: above the threshold it runs
+        when the allocator can supply the fresh pages, else it is skipped."""
         if self.fragmentation(s) > self.compact_threshold:
-            self.compact(s, force=True)
+            nv = int(np.count_nonzero(~self.seqs[s].dropped))
+            if (nv + self.S - 1) // self.S <= self._available():
+                self.compact(s, force=True)
 
     def compact(self, s: int, force: bool = True) -> None:
         """Copy every visible token, in visible-list order, into fresh pages

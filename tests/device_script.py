@@ -1,0 +1,81 @@
+"""Run a `workloads` script on the HIP path through the C ABI binding.
+
+Only marshalling: every operation is a call of kv_cache_drop_amd.Pool (the
+library's kernels and host runtime).  Used by the GPU parity tests, smoke()
+and bench.py."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import kv_cache_drop_amd as akv
+import workloads as W
+
+
+def dev_bf16(u16: np.ndarray, device="cuda:0") -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(u16).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def make_pool(wl: W.Workload, scratch_bytes: int = 256 << 20, **kw) -> akv.Pool:
+    L = wl.layout
+    return akv.Pool(L.n_q_heads, L.n_kv_heads, L.d_nope, L.d_rope, L.d_v, L.page_size, L.num_pages,
+                    kpe_per_head=L.kpe_per_head, pairing=L.pairing, rope_theta=L.rope_theta,
+                    page_order=wl.page_order, device=True, scratch_bytes=scratch_bytes, **kw)
+
+
+def segment_inputs(pool: akv.Pool, att: W.Attention):
+    exts, rows, eb = [], [], 0
+    for sg in att.segments:
+        ex = pool.visible(sg.seq, sg.mask_spans if len(sg.mask_spans) else None)
+        exts.append(ex)
+        rows.append((sg.q_begin, sg.q_len, eb, len(ex)))
+        eb += len(ex)
+    ex = np.concatenate(exts) if exts else np.zeros((0, 3), np.int32)
+    return np.asarray(rows, np.int32).reshape(-1, 4), ex
+
+
+def apply_op(pool: akv.Pool, op, keep=None):
+    """Apply one script op; device inputs are kept alive in `keep`."""
+    keep = keep if keep is not None else []
+    if isinstance(op, W.SeqCreate):
+        pool.seq_create()
+    elif isinstance(op, W.Append):
+        k, v = dev_bf16(op.k), dev_bf16(op.v)
+        kpe = dev_bf16(op.kpe) if op.kpe is not None else None
+        keep += [k, v, kpe]
+        pool.append(op.seq, op.pos, k, kpe, v)
+    elif isinstance(op, W.Drop):
+        pool.drop(op.seq, op.spans)
+    elif isinstance(op, W.Repos):
+        pool.repos(op.seq, op.spans, op.deltas)
+    elif isinstance(op, W.Splice):
+        k, v = dev_bf16(op.k), dev_bf16(op.v)
+        kpe = dev_bf16(op.kpe) if op.kpe is not None else None
+        keep += [k, v, kpe]
+        return pool.splice(op.seq, op.spans, op.stub_lens, k, kpe, v)
+    elif isinstance(op, W.Compact):
+        pool.compact(op.seq, bool(op.force))
+    else:
+        raise TypeError(op)
+    return None
+
+
+def run(wl: W.Workload, pool: akv.Pool | None = None, **kw):
+    pool = pool if pool is not None else make_pool(wl, **kw)
+    keep, outs = [], []
+    for op in wl.ops:
+        if isinstance(op, W.Attention):
+            rows, ex = segment_inputs(pool, op)
+            q = dev_bf16(op.q)
+            keep.append(q)
+            out = pool.segment_attention(q, rows, ex, op.scale)
+            outs.append(dict(segments=rows, extents=ex, out=out))
+        else:
+            apply_op(pool, op, keep)
+    torch.cuda.synchronize()
+    return pool, outs

@@ -1,0 +1,308 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars (written in each test):
+  page tables, slots, positions, queues ........ bit-exact
+  appended / compacted / untouched KV .......... bit-exact
+  rotated bf16 keys ............................ per (token, head) relative L2 error <= 1e-2;
+                                                 single rotation: >= 99% of elements equal
+                                                 RNE(fp64), the rest within 1 bf16 ulp
+  attention outputs (bf16) ..................... max abs error <= 2e-2 against fp64
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle import akv_oracle as AO
+
+pytestmark = pytest.mark.gpu
+
+akv = pytest.importorskip("kv_cache_drop_amd")
+import device_script as D  # noqa: E402  (tests/ is on sys.path via conftest)
+
+ATOL_ATTN = 2e-2
+RTOL_KEY = 1e-2
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    akv.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _rne_bf16(x: np.ndarray) -> np.ndarray:
+    return W.bf16_to_f64(W.to_bf16(x.astype(np.float32)))
+
+
+def _dev_kv(pool, L):
+    """Device page arrays as fp64 numpy: (kr, kn, v) shaped like the oracle's."""
+    if L.mla:
+        return D.to_f64(pool.kpe_pages), D.to_f64(pool.k_pages), D.to_f64(pool.v_pages)
+    return D.to_f64(pool.k_pages), None, D.to_f64(pool.v_pages)
+
+
+def _check_tables(pool, op_pool):
+    fr, ev = pool.queues()
+    assert fr.tolist() == list(op_pool.free)
+    assert ev.tolist() == list(op_pool.evictable)
+    for s, q in enumerate(op_pool.seqs):
+        if not q.alive:
+            continue
+        slot, pos, dropped = pool.tokens(s)
+        np.testing.assert_array_equal(slot, q.slot)
+        np.testing.assert_array_equal(pos, q.pos)
+        np.testing.assert_array_equal(dropped, q.dropped)
+
+
+def _check_visible_kv(pool, op_pool, L):
+    """Every visible token's stored K/V against the oracle, at the same slot."""
+    kr, kn, v = _dev_kv(pool, L)
+    S = L.page_size
+    worst = 0.0
+    for s, q in enumerate(op_pool.seqs):
+        if not q.alive:
+            continue
+        t = op_pool.visible(s)
+        if len(t) == 0:
+            continue
+        pg, off = q.slot[t] // S, q.slot[t] % S
+        got, want = kr[pg, :, off, :], op_pool.kr[pg, :, off, :]
+        err = np.linalg.norm(got - want, axis=-1) / np.maximum(np.linalg.norm(want, axis=-1), 1e-30)
+        worst = max(worst, float(err.max()))
+        assert err.max() <= RTOL_KEY, f"rotated key rel err {err.max()}"
+        np.testing.assert_array_equal(v[pg, :, off, :], op_pool.v[pg, :, off, :])
+        if kn is not None:
+            np.testing.assert_array_equal(kn[pg, :, off, :], op_pool.kn[pg, :, off, :])
+    return worst
+
+
+def _check_attention(outs, res, wl, rows_per_seg=None):
+    worst = 0.0
+    for o, rec in zip(outs, res.attention):
+        np.testing.assert_array_equal(o["extents"], rec["extents"])
+        got = D.to_f64(o["out"])
+        want = rec["out"]
+        cover = ~np.isnan(want[:, 0, 0])
+        err = np.abs(got[cover] - want[cover])
+        worst = max(worst, float(err.max()) if err.size else 0.0)
+        assert err.size == 0 or err.max() <= ATOL_ATTN, f"attention max abs err {err.max()}"
+    return worst
+
+
+def _full_parity(wl, keep_log=False):
+    _say(f"[gpu] {wl.name}: layout {wl.layout}")
+    pool, outs = D.run(wl)
+    res = oracle.run_workload(wl, keep_log=keep_log)
+    _check_tables(pool, res.pool)
+    wk = _check_visible_kv(pool, res.pool, wl.layout)
+    wa = _check_attention(outs, res, wl)
+    _say(f"[gpu] {wl.name}: worst key rel err {wk:.2e}, worst attention abs err {wa:.2e}")
+    pool.close()
+
+
+# ---------------------------------------------------------------------------
+# rotation (repos) kernel
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("pairing", [0, 1])
+@pytest.mark.parametrize("d,heads,page,theta", [(128, 8, 16, 5e5), (64, 2, 16, 1e4), (64, 1, 64, 1e4),
+                                                 (32, 3, 8, 1e4), (16, 1, 4, 1e4)])
+def test_rotate_single_call_elementwise(pairing, d, heads, page, theta):
+    """One repos call from bf16 keys: every element equals RNE of the fp64
+    rotation of the same bf16 input, or is one bf16 ulp away (fp32 rounding
+    before the final RNE); at least 99% are equal.  Delta 0 is bit-exact."""
+    _say(f"[gpu] rotate d={d} heads={heads} page={page} pairing={pairing}")
+    rng = np.random.default_rng(d + heads + page + pairing)
+    n = 700
+    npages = (n + page - 1) // page + 2
+    order = rng.permutation(npages).astype(np.int32)
+    pool = akv.Pool(heads, heads, 0, d, d, page, npages, pairing=pairing, rope_theta=theta,
+                    page_order=order, scratch_bytes=16 << 20)
+    op = AO.Pool(W.Layout(heads, heads, 0, d, d, page, npages, pairing=pairing, rope_theta=theta), order)
+    s = pool.seq_create(); op.seq_create()
+    k = W.to_bf16(rng.standard_normal((n, heads, d), dtype=np.float32))
+    v = W.to_bf16(rng.standard_normal((n, heads, d), dtype=np.float32))
+    pos = np.arange(n, dtype=np.int32) + 131000
+    kd, vd = D.dev_bf16(k), D.dev_bf16(v)
+    pool.append(s, pos, kd, None, vd)
+    op.append(s, pos, W.bf16_to_f64(k), None, W.bf16_to_f64(v))
+    spans = np.array([[0, 300], [250, 650], [680, 700]], np.int32)
+    deltas = np.array([-131000, 77777, 0], np.int32)
+    pool.repos(s, spans, deltas)
+    op.repos(s, spans, deltas)
+    torch.cuda.synchronize()
+    got = D.to_f64(pool.k_pages)
+    q = op.seqs[s]
+    pg, off = q.slot // page, q.slot % page
+    g = got[pg, :, off, :]
+    want = _rne_bf16(op.kr[pg, :, off, :])
+    mag = np.maximum(np.abs(want), np.abs(g))
+    ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7), 2.0 ** -133)
+    diff = np.abs(g - want)
+    assert np.all(diff <= ulp), f"max diff in ulps {np.max(diff / ulp)}"
+    assert np.mean(diff == 0) >= 0.99, np.mean(diff == 0)
+    # tokens 650..679 have delta 0 and 680.. an explicit 0: untouched bit for bit
+    np.testing.assert_array_equal(g[650:], W.bf16_to_f64(k[650:]))
+    np.testing.assert_array_equal(pool.tokens(s)[1], q.pos)
+    pool.close()
+
+
+def test_repos_roundtrip_and_many_spans():
+    """R(d) then R(-d): back within 2 bf16 roundings; 60 spans in one launch."""
+    _say("[gpu] repos roundtrip, 60 spans")
+    rng = np.random.default_rng(5)
+    n, H, d, S = 6000, 8, 128, 16
+    npages = n // S + 4
+    pool = akv.Pool(32, H, 0, d, d, S, npages, rope_theta=5e5, page_order=rng.permutation(npages))
+    s = pool.seq_create()
+    k = W.to_bf16(rng.standard_normal((n, H, d), dtype=np.float32))
+    pool.append(s, np.arange(n) + 50000, D.dev_bf16(k), None, D.dev_bf16(k))
+    cuts = np.sort(rng.choice(np.arange(1, n), 119, replace=False))
+    b = np.concatenate([[0], cuts])
+    spans = np.stack([b[0::2][:60], b[1::2][:60]], 1).astype(np.int32)
+    deltas = rng.integers(-40000, 40000, 60).astype(np.int32)
+    pool.repos(s, spans, deltas)
+    pool.repos(s, spans, -deltas)
+    torch.cuda.synchronize()
+    slot, pos, _ = pool.tokens(s)
+    np.testing.assert_array_equal(pos, np.arange(n) + 50000)
+    got = D.to_f64(pool.k_pages)[slot // S, :, slot % S, :]
+    ref = W.bf16_to_f64(k)
+    err = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    assert err.max() <= RTOL_KEY
+    pool.close()
+
+
+# ---------------------------------------------------------------------------
+# append / compaction copies
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mla", [False, True])
+def test_append_and_compaction_bit_exact(mla):
+    _say(f"[gpu] append + compaction, mla={mla}")
+    wl = W.fuzz_small(7, mla=mla, n_seqs=3, page_size=8, compact=True,
+                      head_dims=(32, 64, 128), mla_dims=(32, 32, 32))
+    wl.ops = [o for o in wl.ops if not isinstance(o, (W.Attention, W.Repos))]
+    wl.ops += [W.Compact(0, 1), W.Compact(1, 1)]
+    pool, _ = D.run(wl)
+    res = oracle.run_workload(wl)
+    _check_tables(pool, res.pool)
+    _check_visible_kv(pool, res.pool, wl.layout)
+    pool.close()
+
+
+# ---------------------------------------------------------------------------
+# segment-batch attention, small scripts (whole outputs)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", ["canonical", "cumulative", "unaligned"])
+def test_c1_tiny_full(variant):
+    _full_parity(W.c1_tiny(0, variant))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fuzz_gqa_full(seed):
+    _full_parity(W.fuzz_small(200 + seed, n_seqs=3, page_size=[16, 8, 4, 32][seed % 4],
+                              head_dims=(32, 64, 128), groups=(1, 2, 4, 8)))
+
+
+@pytest.mark.parametrize("seed,kph,pairing", [(300, 0, 0), (301, 1, 0), (302, 0, 1)])
+def test_fuzz_mla_full(seed, kph, pairing):
+    _full_parity(W.fuzz_small(seed, mla=True, kpe_per_head=kph, pairing=pairing, n_seqs=2,
+                              mla_dims=(32, 32, 32)))
+
+
+def test_c3_mla_full():
+    _full_parity(W.c3_mla(0))
+
+
+def test_attention_edge_cases():
+    """Empty segments, one query, Lkv == Lq, one-entry extents, many segments
+    of one sequence, and rows no segment covers (left untouched)."""
+    _say("[gpu] attention edge cases")
+    rng = np.random.default_rng(11)
+    lay = W.Layout(8, 2, 0, 64, 64, 16, 40)
+    order = rng.permutation(40).astype(np.int32)
+    pool = akv.Pool(8, 2, 0, 64, 64, 16, 40, page_order=order)
+    op = AO.Pool(lay, order)
+    s = pool.seq_create(); op.seq_create()
+    n = 300
+    k = W.to_bf16(rng.standard_normal((n, 2, 64), dtype=np.float32))
+    v = W.to_bf16(rng.standard_normal((n, 2, 64), dtype=np.float32))
+    pool.append(s, np.arange(n), D.dev_bf16(k), None, D.dev_bf16(v))
+    op.append(s, np.arange(n), W.bf16_to_f64(k), None, W.bf16_to_f64(v))
+    ex = op.extents(0)
+    single = np.array([[ex[3, 0], 5, 6]])                           # a one-entry list
+    lists = [ex, single, ex[:2], ex]
+    lens = [int((e[:, 2] - e[:, 1]).sum()) for e in lists]
+    segs = [(0, 1, 0, len(ex)),                                       # one query
+            (1, 1, len(ex), 1),                                       # Lkv == Lq == 1
+            (2, 0, len(ex) + 1, 2),                                   # empty segment
+            (10, lens[3], len(ex) + 3, len(ex))]                      # Lkv == Lq == 300
+    allx = np.concatenate(lists)
+    nq = 10 + lens[3] + 5                                             # 5 trailing rows uncovered
+    qn = W.to_bf16(rng.standard_normal((nq, 8, 64), dtype=np.float32))
+    out = torch.full((nq, 8, 64), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    pool.segment_attention(D.dev_bf16(qn), segs, allx, 0.0, out=out)
+    want = AO.segment_attention(op, W.bf16_to_f64(qn), segs, allx)
+    got = D.to_f64(out)
+    cov = ~np.isnan(want[:, 0, 0])
+    assert np.abs(got[cov] - want[cov]).max() <= ATOL_ATTN
+    assert np.all(got[~cov] == 7.0)
+    pool.close()
+
+
+def test_attention_rejects_bad_inputs():
+    _say("[gpu] attention argument errors")
+    pool = akv.Pool(4, 2, 0, 64, 64, 16, 8)
+    s = pool.seq_create()
+    z = torch.zeros((20, 2, 64), dtype=torch.bfloat16, device="cuda:0")
+    pool.append(s, np.arange(20), z, None, z)
+    q = torch.zeros((30, 4, 64), dtype=torch.bfloat16, device="cuda:0")
+    ex = pool.visible(s)
+    for segs, lists, code in [([(0, 30, 0, len(ex))], ex, akv.AKV_EINVAL),      # Lkv < Lq
+                              ([(0, 5, 0, 1)], [[99, 0, 3]], akv.AKV_ERANGE),    # page out of range
+                              ([(0, 5, 0, 1)], [[0, 3, 17]], akv.AKV_ERANGE),    # offset out of range
+                              ([(28, 5, 0, len(ex))], ex, akv.AKV_ERANGE),       # rows beyond Q
+                              ([(0, 5, 0, len(ex)), (3, 5, 0, len(ex))], ex, akv.AKV_EINVAL)]:  # overlap
+        with pytest.raises(akv.AkvError) as ei:
+            pool.segment_attention(q, segs, lists)
+        assert ei.value.status == code
+    pool.close()
+
+
+# ---------------------------------------------------------------------------
+# full-size configurations: tables and keys in full, attention on sampled rows
+# ---------------------------------------------------------------------------
+def _sampled_parity(wl, n_rows=24, seed=0):
+    _say(f"[gpu] {wl.name} (full size, sampled rows)")
+    pool, outs = D.run(wl)
+    att = [o for o in wl.ops if isinstance(o, W.Attention)][0]
+    rng = np.random.default_rng(seed)
+    sample = {}
+    for i, sg in enumerate(att.segments):
+        if sg.q_len:
+            pick = rng.choice(sg.q_len, size=min(n_rows, sg.q_len), replace=False)
+            sample[i] = np.unique(np.concatenate([pick, [0, sg.q_len - 1]]))
+    res = oracle.run_workload(wl, sample_rows=sample)
+    _check_tables(pool, res.pool)
+    wk = _check_visible_kv(pool, res.pool, wl.layout)
+    wa = _check_attention(outs, res, wl)
+    _say(f"[gpu] {wl.name}: worst key rel err {wk:.2e}, worst attention abs err {wa:.2e}")
+    pool.close()
+
+
+def test_c2_64k_sampled():
+    _sampled_parity(W.c2_64k(0))
+
+
+def test_c4_batched_sampled():
+    _sampled_parity(W.c4_batched(0), n_rows=6)

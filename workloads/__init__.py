@@ -462,15 +462,19 @@ def c5_128k(seed: int = 0) -> Workload:
 # --------------------------------------------------------------------------
 def fuzz_small(seed: int, mla: bool = False, pairing: int = 0, n_seqs: int = 2,
                max_tokens: int = 300, page_size: int = 16, n_rounds: int = 3,
-               compact: bool = True, kpe_per_head: int = 0) -> Workload:
+               compact: bool = True, kpe_per_head: int = 0,
+               head_dims: Sequence[int] = (16, 32, 64), mla_dims: Tuple[int, int, int] = (32, 16, 32),
+               groups: Sequence[int] = (1, 2, 4)) -> Workload:
+    """head_dims: GQA head sizes to draw from; mla_dims: (d_nope, d_rope, d_v)."""
     rng = _rng(seed)
     if mla:
-        lay = Layout(4, 4, 32, 16, 32, page_size, 0, kpe_per_head=kpe_per_head,
+        dn, dr, dv = mla_dims
+        lay = Layout(4, 4, dn, dr, dv, page_size, 0, kpe_per_head=kpe_per_head,
                      pairing=pairing, rope_theta=10000.0)
     else:
         hkv = int(rng.choice([1, 2]))
-        g = int(rng.choice([1, 2, 4]))
-        d = int(rng.choice([16, 32, 64]))
+        g = int(rng.choice(list(groups)))
+        d = int(rng.choice(list(head_dims)))
         lay = Layout(hkv * g, hkv, 0, d, d, page_size, 0, pairing=pairing, rope_theta=10000.0)
     ops = []
     ntok = [0] * n_seqs
