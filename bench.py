@@ -1,0 +1,215 @@
+"""Benchmark of the AKV hot path on one MI355X: the 64K-token agent trace
+(Llama-3.1-8B-shaped layer: 32 q heads / 8 kv heads, head_dim 128, page 16).
+
+One step = one pass of the whole path over a cached 64K-token history:
+drop the 32 older tool responses (page-table compaction, compaction check),
+repos the 32 surviving runs by their cumulative deltas (one rotation launch),
+append the 2,048 new tokens, build the four segments' page lists, and run
+segment-batch attention for the 2,048 queries in one launch.  Every step works
+on its own copy of the history (appended before timing), so nothing is
+reused or undone between steps and each step starts from cold HBM data.
+
+Prints one JSON line.  Kernel durations come from HIP events the library
+records on the pool's stream around each of its launches.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+for _p in (ROOT, os.path.join(ROOT, "tests")):
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attention_flops(layout, segments, page_lists) -> tuple:
+    """2 * Hq * (d_qk + d_v) per visible (query, key) pair of the bottom-right
+    causal mask, and the number of such pairs."""
+    ex = np.asarray(page_lists).reshape(-1, 3)
+    pairs = 0
+    for qb, lq, eb, el in np.asarray(segments).reshape(-1, 4):
+        if lq == 0:
+            continue
+        lkv = int((ex[eb:eb + el, 2] - ex[eb:eb + el, 1]).sum())
+        pairs += lq * (lkv - lq) + lq * (lq + 1) // 2
+    d_qk = layout.d_nope + layout.d_rope
+    return 2.0 * layout.n_q_heads * (d_qk + layout.d_v) * pairs, pairs
+
+
+def cpu_baseline(wl, rows_per_seg: int):
+    """The fp64 oracle as it is, on the host cores: the same step at full size
+    for drop / repos / append / page lists, attention on sampled query rows
+    (scaled to the full step)."""
+    import oracle
+    from oracle import akv_oracle as AO
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    pool = AO.Pool(wl.layout, wl.page_order)
+    ops = list(wl.ops)
+    i_drop = next(i for i, o in enumerate(ops) if isinstance(o, W.Drop))
+    for op in ops[:i_drop]:
+        oracle.apply_op(pool, op)
+    att = ops[-1]
+    t0 = time.perf_counter()
+    for op in ops[i_drop:-1]:
+        oracle.apply_op(pool, op)
+    ex, rows = oracle.segment_lists(pool, att.segments)
+    t_ops = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    sample = {i: np.sort(rng.choice(sg.q_len, rows_per_seg, replace=False)) for i, sg in enumerate(att.segments)}
+    q = W.bf16_to_f64(att.q)
+    t0 = time.perf_counter()
+    AO.segment_attention(pool, q, rows, ex, 0.0, rows=sample)
+    t_att = time.perf_counter() - t0
+    full_rows = sum(sg.q_len for sg in att.segments)
+    frac = rows_per_seg * len(att.segments) / full_rows
+    flops, _ = attention_flops(wl.layout, rows, ex)
+    t_step = t_ops + t_att / frac
+    return dict(value=round(flops / t_step / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=(f"64K step: drop/repos/append/page lists at full size ({t_ops:.1f} s); attention on "
+                        f"{rows_per_seg} query rows per segment x all heads ({t_att:.1f} s), scaled by "
+                        f"{1 / frac:.0f}x to the {full_rows} query rows"),
+                est_step_s=round(t_step, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-rows", type=int, default=16, help="oracle query rows per segment")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path is measured on one "
+              "MI355X and has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import device_script as D
+    import kv_cache_drop_amd as akv
+    import workloads as W
+
+    wl = W.c2_64k(args.seed)
+    L = wl.layout
+    ops = wl.ops
+    hist, drop, repos, new, att = ops[1], ops[2], ops[3], ops[4], ops[5]
+    assert isinstance(drop, W.Drop) and isinstance(repos, W.Repos) and isinstance(att, W.Attention)
+    n_copies = args.warmup + args.steps
+    per_copy = L.num_pages                      # 4,224 pages: history + new tokens
+    rng = np.random.default_rng(args.seed + 1)
+    order = rng.permutation(per_copy * n_copies).astype(np.int32)
+    log(f"[bench] building {n_copies} copies of the 64K history ({per_copy * n_copies} pages)")
+    pool = akv.Pool(L.n_q_heads, L.n_kv_heads, 0, L.d_rope, L.d_v, L.page_size, per_copy * n_copies,
+                    rope_theta=L.rope_theta, page_order=order, scratch_bytes=256 << 20)
+    hk, hv = D.dev_bf16(hist.k), D.dev_bf16(hist.v)
+    nk, nv = D.dev_bf16(new.k), D.dev_bf16(new.v)
+    q = D.dev_bf16(att.q)
+    out = torch.empty((q.shape[0], L.n_q_heads, L.d_v), dtype=torch.bfloat16, device="cuda:0")
+    seqs = []
+    for c in range(n_copies):
+        s = pool.seq_create()
+        pool.append(s, hist.pos, hk, None, hv)
+        seqs.append(s)
+    torch.cuda.synchronize()
+
+    def step(s):
+        pool.drop(s, drop.spans)
+        pool.repos(s, repos.spans, repos.deltas)
+        pool.append(s, new.pos, nk, None, nv)
+        exts, segs, eb = [], [], 0
+        for sg in att.segments:
+            ex = pool.visible(s, sg.mask_spans if len(sg.mask_spans) else None)
+            exts.append(ex)
+            segs.append((sg.q_begin, sg.q_len, eb, len(ex)))
+            eb += len(ex)
+        page_lists = np.concatenate(exts)
+        pool.segment_attention(q, segs, page_lists, 0.0, out=out)
+        return segs, page_lists
+
+    for c in range(args.warmup):
+        segs, page_lists = step(seqs[c])
+    torch.cuda.synchronize()
+    pool.timing_enable(True)
+    for k in akv.KERNEL_KINDS:
+        pool.timing_read(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for c in range(args.warmup, n_copies):
+        segs, page_lists = step(seqs[c])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kt = {k: pool.timing_read(k) for k in akv.KERNEL_KINDS}
+    pool.timing_enable(False)
+
+    flops, pairs = attention_flops(L, segs, page_lists)
+    n_rep = int(sum(e - b for b, e in repos.spans))
+    rep_bytes = 2.0 * L.n_kv_heads * L.d_rope * 2 * n_rep      # read + write of the rotated keys
+    ms_step = wall / args.steps * 1e3
+    attn_ms = kt["attention"][0] / max(kt["attention"][1], 1)
+    rot_ms = kt["rotate"][0] / max(kt["rotate"][1], 1)
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    rot_gbps = rep_bytes / (rot_ms * 1e-3) / 1e9
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host (bounded sample)")
+        cpu = cpu_baseline(wl, args.cpu_rows)
+
+    rec = {
+        "metric": "segment-batch attn TFLOP/s + repos GB/s at 64K ctx, % of MI355X roofline",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "64K-token agent trace, Llama-3.1-8B-shaped layer (32 q / 8 kv heads, "
+                               "head_dim 128, page 16): drop 32 older tool spans, repos 32 runs, "
+                               "segment-batch attention for 2048 queries in 4 segments",
+                   "history_tokens": 65536, "visible_after_drop": int(wl.notes["history"]),
+                   "repositioned_tokens": n_rep, "query_tokens": int(att.q.shape[0]), "segments": 4,
+                   "seed": args.seed},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_seg_attn<128,128,0>", "flop_per_launch": flops,
+                     "avg_launch_ms": round(attn_ms, 5)},
+        "roofline_repos": {"bound": "hbm", "achieved": round(rot_gbps, 1), "peak": PEAK_HBM_GBPS,
+                           "unit": "GB/s", "frac": round(rot_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                           "kernel": "k_rotate", "bytes_per_launch": rep_bytes,
+                           "avg_launch_ms": round(rot_ms, 5)},
+        "kernels_ms_per_step": {k: round(v[0] / max(args.steps, 1), 5) for k, v in kt.items()},
+        "attention_pairs": int(pairs),
+        "query_tokens_per_s": round(att.q.shape[0] / (ms_step * 1e-3), 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    pool.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -147,7 +147,8 @@ akv_status stg_reserve(akv_pool* p, size_t n, char** out) {
     s.pending.clear();
     if (s.base) (void)hipHostFree(s.base);
     s.base = nullptr;
-    size_t cap = std::max<size_t>(n, 2 * s.cap);
+    // room for several calls in flight, so refills rarely wait on the GPU
+    size_t cap = std::max<size_t>({4 * n, 2 * s.cap, (size_t)8 << 20});
     e = hipHostMalloc((void**)&s.base, cap, hipHostMallocDefault);
     if (e != hipSuccess) {
       s.cap = 0;
