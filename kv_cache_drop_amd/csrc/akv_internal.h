@@ -43,7 +43,7 @@ struct CombItem {
   int32_t seg, kvh, row0, part0, nsplit, pad;
 };
 
-constexpr int ATTN_ROWS = 256;   // packed rows per attention block (4 waves x 64)
+constexpr int ATTN_ROWS = 256;   // packed rows per attention block (8 waves x 32)
 constexpr int ATTN_KTILE = 64;   // keys per pipeline stage
 
 // ---- launchers --------------------------------------------------------------

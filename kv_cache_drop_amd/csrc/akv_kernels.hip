@@ -248,30 +248,42 @@ hipError_t launch_expand(hipStream_t st, const Extent* ex, const int32_t* ex_off
 // segment-batch attention ([AKV-notes] section 3, Segment-Batch Attention;
 // [AKV-blog] section 4)
 //
-// One block = 4 waves = ATTN_ROWS packed rows (token-major, the q heads of one
-// kv head side by side) of one segment, over list entries k_begin..k_end-1 in
-// tiles of 64 keys gathered from pages through the segment's slot list.
+// One block = 8 waves = ATTN_ROWS (256) packed rows (token-major, the q heads
+// of one kv head side by side) of one segment, over list entries
+// k_begin..k_end-1, in tiles of 64 keys gathered from pages through the
+// segment's slot list.  Two waves share each SIMD, so one wave's softmax
+// overlaps the other's matrix work.
 //
-// Per wave: 64 query rows as two 32-row blocks.  S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16 (A = K tile from LDS, B = Q in registers), so every
-// lane owns one query row (lane % 32) and half of the 32 keys of each block;
-// row max / sum need one exchange with lane ^ 32.  O^T = V^T P^T reuses the
-// accumulator registers of S^T directly as the B operand (P in bf16), with V
-// stored transposed in LDS and its keys permuted inside every 16-key group to
-// match the accumulator's key order, so no register shuffles are needed.
-// Causality is bottom-right over list order: query i sees entries
-// 0 .. Lkv - Lq + i.  The K/V of tile j+1 are loaded into registers while tile
-// j is computed, then written to the other LDS buffer (one barrier per tile).
+// Per wave: 32 query rows.  S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K
+// tile from LDS, B = Q in registers), so every lane owns one query row
+// (lane % 32) and half of the keys of each 32-key block; the row max and sum
+// need one exchange with lane ^ 32.  O^T = V^T P^T takes the S^T accumulators
+// (as bf16 P) directly as the B operand: V is stored transposed in LDS with
+// the keys of every 16-key group permuted into the accumulator's key order, so
+// no register shuffles are needed.  Causality is bottom-right over list order:
+// query i sees entries 0 .. Lkv - Lq + i.
+//
+// Softmax runs in base 2 with a lazily updated running max: O and l are
+// rescaled only when a row's max grows by more than 2^RESCALE_LOG2 over the
+// reference (so P <= 2^8 in between), which takes the accumulator rescale off
+// almost every tile.
+//
+// Loads: threads 0..255 stage the K tile, threads 256..511 the V tile (4 keys
+// x 8 columns each, transposed on the way into LDS); the tile j+1 loads are
+// in flight while tile j is computed, then written to the other LDS buffer
+// (one barrier per tile).
 // ---------------------------------------------------------------------------
+constexpr float RESCALE_LOG2 = 8.f;
+
 template <int DQK, int DV, int DNOPE>
-__global__ __launch_bounds__(256, 1) void k_seg_attn(AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void k_seg_attn(AttnArgs a) {
   constexpr int KT = ATTN_KTILE;
   constexpr int KPAD = DQK + 8;        // LDS K row stride (elements)
   constexpr int VPAD = KT + 8;         // LDS V^T row stride (elements)
   constexpr int NKS = DQK / 16;        // k-steps of S^T
   constexpr int NCB = DV / 32;         // 32-wide column blocks of O^T
   constexpr int KCH = DQK / 8;         // 16-byte chunks per K row
-  constexpr int NKL = KT * KCH / 256;  // K chunks per thread per tile
+  constexpr int NKL = KT * KCH / 256;  // K chunks per loader thread per tile
   constexpr int VCH = DV / 8;          // 16-byte chunks per V row
   constexpr int VTHREADS = VCH * 16;   // V loaders: 4 keys x 8 columns each
   static_assert(DQK % 32 == 0 && DV % 32 == 0 && NKL >= 1 && VTHREADS <= 256, "dims");
@@ -297,74 +309,74 @@ __global__ __launch_bounds__(256, 1) void k_seg_attn(AttnArgs a) {
   const int kvh = it.kvh;
   const int32_t* __restrict__ slots = a.slots + sg.list_off;
 
-  // the lane's two query rows
-  int lim_q[2], tok_q[2], hq_q[2];
-  bool valid_q[2];
-  bf16x8 qf[2][NKS];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int r = it.row0 + 64 * w + 32 * qb + l32;
-    valid_q[qb] = r < rows_total;
-    const int rr = valid_q[qb] ? r : 0;
-    tok_q[qb] = rr / G;
-    hq_q[qb] = kvh * G + (rr - tok_q[qb] * G);
-    lim_q[qb] = valid_q[qb] ? lkv - lq + tok_q[qb] : k_stop;
-    const uint16_t* qp =
-        a.q + ((size_t)(sg.q_begin + tok_q[qb]) * a.n_q_heads + hq_q[qb]) * DQK + 8 * g;
+  // the lane's query row
+  const int r = it.row0 + 32 * w + l32;
+  const bool valid = r < rows_total;
+  const int tok = valid ? r / G : 0;
+  const int hq = kvh * G + (valid ? r - tok * G : 0);
+  const int lim = valid ? min(lkv - lq + tok, k_end - 1) : k_stop - 1;
+  bf16x8 qf[NKS];
+  {
+    const uint16_t* qp = a.q + ((size_t)(sg.q_begin + tok) * a.n_q_heads + hq) * DQK + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      if (valid_q[qb]) {
-        qf[qb][ks] = *(const bf16x8*)(qp + 16 * ks);
+      if (valid) {
+        qf[ks] = *(const bf16x8*)(qp + 16 * ks);
       } else {
         u32x4 z = {0u, 0u, 0u, 0u};
-        qf[qb][ks] = __builtin_bit_cast(bf16x8, z);
+        qf[ks] = __builtin_bit_cast(bf16x8, z);
       }
     }
   }
 
-  u32x4 kreg[NKL];
-  u32x4 vreg[4];
-  const int vp = tid >> 4, vquad = tid & 15;
+  // loader roles
+  const bool kload = tid < 256;
+  const int ltid = kload ? tid : tid - 256;
+  const bool vload = !kload && ltid < VTHREADS;
+  const int vp = ltid >> 4, vquad = ltid & 15;
+  u32x4 stage[NKL > 4 ? NKL : 4];
 
   auto load_tile = [&](int k0) {
+    if (kload) {
 #pragma unroll
-    for (int j = 0; j < NKL; ++j) {
-      const int i = tid + 256 * j;
-      const int key = i / KCH, c = i - (i / KCH) * KCH;
-      const int kk = min(k0 + key, lkv - 1);
-      const int slot = slots[kk];
-      const int page = slot >> lg, off = slot & (S - 1);
-      const uint16_t* src;
-      if (DNOPE == 0) {
-        src = a.k_a + (((size_t)page * Hkv + kvh) * S + off) * DQK + 8 * c;
-      } else if (c < DNOPE / 8) {
-        src = a.k_a + (((size_t)page * Hkv + kvh) * S + off) * DNOPE + 8 * c;
-      } else {
-        const int hp = a.kpe_heads == 1 ? 0 : kvh;
-        src = a.k_b + (((size_t)page * a.kpe_heads + hp) * S + off) * (DQK - DNOPE) +
-              8 * (c - DNOPE / 8);
+      for (int j = 0; j < NKL; ++j) {
+        const int i = ltid + 256 * j;
+        const int key = i / KCH, c = i - (i / KCH) * KCH;
+        const int kk = min(k0 + key, lkv - 1);
+        const int slot = slots[kk];
+        const int page = slot >> lg, off = slot & (S - 1);
+        const uint16_t* src;
+        if (DNOPE == 0) {
+          src = a.k_a + (((size_t)page * Hkv + kvh) * S + off) * DQK + 8 * c;
+        } else if (c < DNOPE / 8) {
+          src = a.k_a + (((size_t)page * Hkv + kvh) * S + off) * DNOPE + 8 * c;
+        } else {
+          const int hp = a.kpe_heads == 1 ? 0 : kvh;
+          src = a.k_b + (((size_t)page * a.kpe_heads + hp) * S + off) * (DQK - DNOPE) +
+                8 * (c - DNOPE / 8);
+        }
+        stage[j] = *(const u32x4*)src;
       }
-      kreg[j] = *(const u32x4*)src;
-    }
-    if (tid < VTHREADS) {
+    } else if (vload) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int kk = min(k0 + 4 * vquad + e, lkv - 1);
         const int slot = slots[kk];
         const int page = slot >> lg, off = slot & (S - 1);
-        vreg[e] = *(const u32x4*)(a.v + (((size_t)page * Hkv + kvh) * S + off) * DV + 8 * vp);
+        stage[e] = *(const u32x4*)(a.v + (((size_t)page * Hkv + kvh) * S + off) * DV + 8 * vp);
       }
     }
   };
 
   auto store_tile = [&](int buf) {
+    if (kload) {
 #pragma unroll
-    for (int j = 0; j < NKL; ++j) {
-      const int i = tid + 256 * j;
-      const int key = i / KCH, c = i - (i / KCH) * KCH;
-      *(u32x4*)&sK[buf][key * KPAD + 8 * c] = kreg[j];
-    }
-    if (tid < VTHREADS) {
+      for (int j = 0; j < NKL; ++j) {
+        const int i = ltid + 256 * j;
+        const int key = i / KCH, c = i - (i / KCH) * KCH;
+        *(u32x4*)&sK[buf][key * KPAD + 8 * c] = stage[j];
+      }
+    } else if (vload) {
       // keys 4*vquad..+3 go to LDS positions with quads 1 and 2 of every
       // 16-key group swapped (the accumulator's key order)
       const int qg = vquad & 3;
@@ -374,11 +386,11 @@ __global__ __launch_bounds__(256, 1) void k_seg_attn(AttnArgs a) {
         const int dw = e >> 1;
         unsigned lo, hi;
         if ((e & 1) == 0) {
-          lo = (vreg[0][dw] & 0xffffu) | (vreg[1][dw] << 16);
-          hi = (vreg[2][dw] & 0xffffu) | (vreg[3][dw] << 16);
+          lo = (stage[0][dw] & 0xffffu) | (stage[1][dw] << 16);
+          hi = (stage[2][dw] & 0xffffu) | (stage[3][dw] << 16);
         } else {
-          lo = (vreg[0][dw] >> 16) | (vreg[1][dw] & 0xffff0000u);
-          hi = (vreg[2][dw] >> 16) | (vreg[3][dw] & 0xffff0000u);
+          lo = (stage[0][dw] >> 16) | (stage[1][dw] & 0xffff0000u);
+          hi = (stage[2][dw] >> 16) | (stage[3][dw] & 0xffff0000u);
         }
         u32x2 v2 = {lo, hi};
         *(u32x2*)&sV[buf][(8 * vp + e) * VPAD + posq] = v2;
@@ -386,15 +398,13 @@ __global__ __launch_bounds__(256, 1) void k_seg_attn(AttnArgs a) {
     }
   };
 
-  f32x16 oacc[NCB][2];
+  f32x16 oacc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[cb][qb][r] = 0.f;
-  float m_i[2] = {-INFINITY, -INFINITY};
-  float l_i[2] = {0.f, 0.f};
+    for (int i = 0; i < 16; ++i) oacc[cb][i] = 0.f;
+  float m_run = -INFINITY;  // reference max (base-2 units) of O and l
+  float l_run = 0.f;
   const float c2 = a.scale_log2e;
 
   if (n_tiles > 0) {
@@ -409,76 +419,66 @@ __global__ __launch_bounds__(256, 1) void k_seg_attn(AttnArgs a) {
     const bool more = j + 1 < n_tiles;
     if (more) load_tile(k0 + KT);
 
-    // S^T = K Q^T: two 32-key blocks x two 32-query blocks
-    f32x16 sacc[2][2];
+    // S^T = K Q^T: two 32-key blocks
+    f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][qb][r] = 0.f;
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
     const uint16_t* kbase = &sK[buf][0];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 af = *(const bf16x8*)(kbase + (32 * kb + l32) * KPAD + 16 * ks + 8 * g);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[qb][ks], sacc[kb][qb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
 
-    const bool need_mask = (k0 + KT > k_end) || (k0 + KT - 1 > lim_first);
-    bf16x8 pf[2][4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      if (need_mask) {
-        const int lim = min(lim_q[qb], k_end - 1);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key > lim) sacc[kb][qb][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
+    if ((k0 + KT > k_end) || (k0 + KT - 1 > lim_first)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_i[qb], mx * c2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_i[qb] - m_use);
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][r], c2, -m_use));
-          sacc[kb][qb][r] = p;
-          rs += p;
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key > lim) sacc[kb][i] = -INFINITY;
         }
-      rs += __shfl_xor(rs, 32);
-      l_i[qb] = l_i[qb] * alpha + rs;
-      m_i[qb] = m_new;
-      if (__ballot(alpha != 1.f)) {
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_cand = fmaxf(m_run, mx * c2);
+    if (__ballot(m_cand > m_run + RESCALE_LOG2)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
+      l_run *= alpha;
+      if (j > 0) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[cb][qb][r] *= alpha;
+          for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
       }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int kb = t >> 1, r0 = 8 * (t & 1);
-        u32x4 pk;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) pk[k] = pack_bf2(sacc[kb][qb][r0 + 2 * k], sacc[kb][qb][r0 + 2 * k + 1]);
-        pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
-      }
+      m_run = m_cand;
     }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float rs = 0.f;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kb = t >> 1, r0 = 8 * (t & 1);
+      u32x4 pk;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r0 + 2 * k], c2, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r0 + 2 * k + 1], c2, -m_use));
+        rs += p0 + p1;
+        pk[k] = pack_bf2(p0, p1);
+      }
+      pf[t] = __builtin_bit_cast(bf16x8, pk);
+    }
+    l_run += rs;   // per-lane partial; the two halves of a row are added at the end
 
     // O^T += V^T P^T
     const uint16_t* vbase = &sV[buf][0];
@@ -487,9 +487,7 @@ __global__ __launch_bounds__(256, 1) void k_seg_attn(AttnArgs a) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const bf16x8 vf = *(const bf16x8*)(vbase + (32 * cb + l32) * VPAD + 16 * t + 8 * g);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          oacc[cb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], oacc[cb][qb], 0, 0, 0);
+        oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[cb], 0, 0, 0);
       }
     }
 
@@ -497,36 +495,34 @@ __global__ __launch_bounds__(256, 1) void k_seg_attn(AttnArgs a) {
     __syncthreads();
   }
 
+  // the two lanes of a row hold disjoint key halves of l
+  l_run += __shfl_xor(l_run, 32);
   // epilogue: lane holds O^T columns c = 32cb + 8m + 4g + 0..3 of its row
+  if (!valid) return;
+  if (it.part < 0) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* op = a.out + ((size_t)(sg.q_begin + tok) * a.n_q_heads + hq) * DV;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    if (!valid_q[qb]) continue;
-    if (it.part < 0) {
-      const float inv = l_i[qb] > 0.f ? 1.f / l_i[qb] : 0.f;
-      uint16_t* op = a.out + ((size_t)(sg.q_begin + tok_q[qb]) * a.n_q_heads + hq_q[qb]) * DV;
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          u32x2 v2 = {pack_bf2(oacc[cb][qb][4 * m] * inv, oacc[cb][qb][4 * m + 1] * inv),
-                      pack_bf2(oacc[cb][qb][4 * m + 2] * inv, oacc[cb][qb][4 * m + 3] * inv)};
-          *(u32x2*)(op + 32 * cb + 8 * m + 4 * g) = v2;
-        }
-    } else {
-      const int prow = it.part * ATTN_ROWS + 64 * w + 32 * qb + l32;
-      float* po = a.part_o + (size_t)prow * DV;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          f32x4 v4 = {oacc[cb][qb][4 * m], oacc[cb][qb][4 * m + 1], oacc[cb][qb][4 * m + 2],
-                      oacc[cb][qb][4 * m + 3]};
-          *(f32x4*)(po + 32 * cb + 8 * m + 4 * g) = v4;
-        }
-      if (g == 0) {
-        a.part_ml[2 * (size_t)prow] = m_i[qb];
-        a.part_ml[2 * (size_t)prow + 1] = l_i[qb];
+      for (int m = 0; m < 4; ++m) {
+        u32x2 v2 = {pack_bf2(oacc[cb][4 * m] * inv, oacc[cb][4 * m + 1] * inv),
+                    pack_bf2(oacc[cb][4 * m + 2] * inv, oacc[cb][4 * m + 3] * inv)};
+        *(u32x2*)(op + 32 * cb + 8 * m + 4 * g) = v2;
       }
+  } else {
+    const int prow = it.part * ATTN_ROWS + 32 * w + l32;
+    float* po = a.part_o + (size_t)prow * DV;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f32x4 v4 = {oacc[cb][4 * m], oacc[cb][4 * m + 1], oacc[cb][4 * m + 2], oacc[cb][4 * m + 3]};
+        *(f32x4*)(po + 32 * cb + 8 * m + 4 * g) = v4;
+      }
+    if (g == 0) {
+      a.part_ml[2 * (size_t)prow] = m_run;
+      a.part_ml[2 * (size_t)prow + 1] = l_run;
     }
   }
 }
@@ -583,7 +579,7 @@ bool attn_dims_supported(int d_nope, int d_rope, int d_v) {
 
 template <int DQK, int DV, int DNOPE>
 static hipError_t launch_attn_t(hipStream_t st, const AttnArgs& a) {
-  hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE>), dim3(a.n_items), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE>), dim3(a.n_items), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
