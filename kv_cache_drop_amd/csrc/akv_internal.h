@@ -30,7 +30,7 @@ struct AttnSeg {
   int32_t q_begin, q_len, lkv, list_off;
 };
 
-// One attention work item: a tile of ATTN_ROWS packed rows (token, q head in
+// One attention work item: a tile of attn_rows_per_block(d_nope) packed rows (token, q head in
 // group) of one segment and kv head, over list entries k_begin..k_end-1.
 // part >= 0: write an unnormalised fp32 partial (split-KV) at that index.
 // seg < 0: padding block, exits at once.
@@ -43,8 +43,12 @@ struct CombItem {
   int32_t seg, kvh, row0, part0, nsplit, pad;
 };
 
-constexpr int ATTN_ROWS = 256;   // packed rows per attention block (8 waves x 32)
-constexpr int ATTN_KTILE = 64;   // keys per pipeline stage
+constexpr int ATTN_PART_ROWS = 256;  // row stride of one split-KV partial (>= rows per block)
+constexpr int ATTN_KTILE = 64;       // keys per pipeline stage
+
+// Packed rows per attention block of the kernel variant launched for a layout
+// with this d_nope (128 or 256).
+int attn_rows_per_block(int d_nope);
 
 // ---- launchers --------------------------------------------------------------
 hipError_t launch_rotate(hipStream_t st, uint16_t* kr, int n_heads, int page_size, int d_rope,
@@ -75,8 +79,9 @@ struct AttnArgs {
   const int32_t* slots;
   float scale_log2e;             // softmax scale * log2(e)
   uint16_t* out;
-  float* part_o;                 // [n_parts][ATTN_ROWS][d_v]
-  float* part_ml;                // [n_parts][ATTN_ROWS][2]
+  float* part_o;                 // [n_parts][ATTN_PART_ROWS][d_v]
+  float* part_ml;                // [n_parts][ATTN_PART_ROWS][2]
+  int rows_per_block;
 };
 
 // Returns hipErrorInvalidValue when no kernel is instantiated for the dims.

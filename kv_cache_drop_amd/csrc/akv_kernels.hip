@@ -15,6 +15,8 @@
 //   k_combine      split-KV merge of (m, l, O) partials
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+
 #include "akv_internal.h"
 
 namespace akv {
@@ -248,11 +250,12 @@ hipError_t launch_expand(hipStream_t st, const Extent* ex, const int32_t* ex_off
 // segment-batch attention ([AKV-notes] section 3, Segment-Batch Attention;
 // [AKV-blog] section 4)
 //
-// One block = 8 waves = ATTN_ROWS (256) packed rows (token-major, the q heads
-// of one kv head side by side) of one segment, over list entries
-// k_begin..k_end-1, in tiles of 64 keys gathered from pages through the
-// segment's slot list.  Two waves share each SIMD, so one wave's softmax
-// overlaps the other's matrix work.
+// One block = NW waves = 32*NW packed rows (token-major, the q heads of one
+// kv head side by side) of one segment, over list entries k_begin..k_end-1,
+// in tiles of 64 keys gathered from pages through the segment's slot list.
+// Two waves share each SIMD (NW = 8: one block per CU; NW = 4: two blocks per
+// CU that run out of step), so one wave's softmax overlaps another's matrix
+// work.
 //
 // Per wave: 32 query rows.  S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K
 // tile from LDS, B = Q in registers), so every lane owns one query row
@@ -268,25 +271,26 @@ hipError_t launch_expand(hipStream_t st, const Extent* ex, const int32_t* ex_off
 // reference (so P <= 2^8 in between), which takes the accumulator rescale off
 // almost every tile.
 //
-// Loads: threads 0..255 stage the K tile, threads 256..511 the V tile (4 keys
-// x 8 columns each, transposed on the way into LDS); the tile j+1 loads are
-// in flight while tile j is computed, then written to the other LDS buffer
-// (one barrier per tile).
+// Loads: the tile j+1 loads are in flight in registers while tile j is
+// computed, then written to the other LDS buffer (one barrier per tile); V is
+// transposed on the way into LDS.
 // ---------------------------------------------------------------------------
 constexpr float RESCALE_LOG2 = 8.f;
 
-template <int DQK, int DV, int DNOPE>
-__global__ __launch_bounds__(512, 1) void k_seg_attn(AttnArgs a) {
+template <int DQK, int DV, int DNOPE, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_seg_attn(AttnArgs a) {
+  constexpr int NT = 64 * NW;          // threads per block
+  constexpr int RB = 32 * NW;          // packed rows per block
   constexpr int KT = ATTN_KTILE;
   constexpr int KPAD = DQK + 8;        // LDS K row stride (elements)
   constexpr int VPAD = KT + 8;         // LDS V^T row stride (elements)
   constexpr int NKS = DQK / 16;        // k-steps of S^T
   constexpr int NCB = DV / 32;         // 32-wide column blocks of O^T
   constexpr int KCH = DQK / 8;         // 16-byte chunks per K row
-  constexpr int NKL = KT * KCH / 256;  // K chunks per loader thread per tile
   constexpr int VCH = DV / 8;          // 16-byte chunks per V row
-  constexpr int VTHREADS = VCH * 16;   // V loaders: 4 keys x 8 columns each
-  static_assert(DQK % 32 == 0 && DV % 32 == 0 && NKL >= 1 && VTHREADS <= 256, "dims");
+  constexpr int VTASKS = VCH * 16;     // V tasks: 4 keys x 8 columns each
+  constexpr int NVL = (VTASKS + NT - 1) / NT;
+  static_assert(DQK % 32 == 0 && DV % 32 == 0, "dims");
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][KT * KPAD];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][DV * VPAD];
@@ -299,7 +303,7 @@ __global__ __launch_bounds__(512, 1) void k_seg_attn(AttnArgs a) {
   const int G = a.group;
   const int lq = sg.q_len, lkv = sg.lkv;
   const int rows_total = lq * G;
-  const int brow_last = min(it.row0 + ATTN_ROWS, rows_total) - 1;
+  const int brow_last = min(it.row0 + RB, rows_total) - 1;
   const int lim_first = lkv - lq + it.row0 / G;
   const int lim_last = lkv - lq + brow_last / G;
   const int k_end = it.k_end;
@@ -329,71 +333,94 @@ __global__ __launch_bounds__(512, 1) void k_seg_attn(AttnArgs a) {
     }
   }
 
-  // loader roles
-  const bool kload = tid < 256;
-  const int ltid = kload ? tid : tid - 256;
-  const bool vload = !kload && ltid < VTHREADS;
-  const int vp = ltid >> 4, vquad = ltid & 15;
-  u32x4 stage[NKL > 4 ? NKL : 4];
+  // Loaders.  K: TPK threads per key row, each staging CPT consecutive 16-byte
+  // chunks, so a thread resolves one slot per pass.  V: VTASKS tasks of 4
+  // keys x 8 columns, transposed on the way into LDS.  Page offsets use 24-bit
+  // multiplies (pools hold fewer than 2^24 pages).
+  constexpr int TPK = KCH < 8 ? KCH : 8;
+  constexpr int CPT = KCH / TPK;
+  constexpr int KPP = NT / TPK;                 // key rows per pass
+  constexpr int NKP = (KT + KPP - 1) / KPP;     // passes
+  u32x4 kst[NKP][CPT];
+  u32x4 vst[NVL][4];
+  const int HS = Hkv * S;
+  const int hoff = kvh * S;
+  const int kpe_hoff = (a.kpe_heads == 1 ? 0 : kvh) * S;
+  const int kpe_hs = a.kpe_heads * S;
 
   auto load_tile = [&](int k0) {
-    if (kload) {
 #pragma unroll
-      for (int j = 0; j < NKL; ++j) {
-        const int i = ltid + 256 * j;
-        const int key = i / KCH, c = i - (i / KCH) * KCH;
-        const int kk = min(k0 + key, lkv - 1);
-        const int slot = slots[kk];
-        const int page = slot >> lg, off = slot & (S - 1);
+    for (int ps = 0; ps < NKP; ++ps) {
+      const int key = tid / TPK + KPP * ps;
+      if (KT % KPP != 0 && key >= KT) break;
+      const int kk = min(k0 + key, lkv - 1);
+      const int slot = slots[kk];
+      const int page = slot >> lg, off = slot & (S - 1);
+      const int c0 = (tid % TPK) * CPT;
+      const uint32_t row = __umul24(page, HS) + hoff + off;
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int c = c0 + q;
         const uint16_t* src;
         if (DNOPE == 0) {
-          src = a.k_a + (((size_t)page * Hkv + kvh) * S + off) * DQK + 8 * c;
+          src = a.k_a + (size_t)row * DQK + 8 * c;
         } else if (c < DNOPE / 8) {
-          src = a.k_a + (((size_t)page * Hkv + kvh) * S + off) * DNOPE + 8 * c;
+          src = a.k_a + (size_t)row * DNOPE + 8 * c;
         } else {
-          const int hp = a.kpe_heads == 1 ? 0 : kvh;
-          src = a.k_b + (((size_t)page * a.kpe_heads + hp) * S + off) * (DQK - DNOPE) +
-                8 * (c - DNOPE / 8);
+          const uint32_t prow = __umul24(page, kpe_hs) + kpe_hoff + off;
+          src = a.k_b + (size_t)prow * (DQK - DNOPE) + 8 * (c - DNOPE / 8);
         }
-        stage[j] = *(const u32x4*)src;
+        kst[ps][q] = *(const u32x4*)src;
       }
-    } else if (vload) {
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kk = min(k0 + 4 * vquad + e, lkv - 1);
-        const int slot = slots[kk];
-        const int page = slot >> lg, off = slot & (S - 1);
-        stage[e] = *(const u32x4*)(a.v + (((size_t)page * Hkv + kvh) * S + off) * DV + 8 * vp);
+    for (int j = 0; j < NVL; ++j) {
+      const int vt = tid + NT * j;
+      if (VTASKS % NT == 0 || vt < VTASKS) {
+        const int vp = vt >> 4, vquad = vt & 15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kk = min(k0 + 4 * vquad + e, lkv - 1);
+          const int slot = slots[kk];
+          const uint32_t row = __umul24(slot >> lg, HS) + hoff + (slot & (S - 1));
+          vst[j][e] = *(const u32x4*)(a.v + (size_t)row * DV + 8 * vp);
+        }
       }
     }
   };
 
-  auto store_tile = [&](int buf) {
-    if (kload) {
+  auto store_tile = [&](int kbuf, int vbuf) {
 #pragma unroll
-      for (int j = 0; j < NKL; ++j) {
-        const int i = ltid + 256 * j;
-        const int key = i / KCH, c = i - (i / KCH) * KCH;
-        *(u32x4*)&sK[buf][key * KPAD + 8 * c] = stage[j];
-      }
-    } else if (vload) {
-      // keys 4*vquad..+3 go to LDS positions with quads 1 and 2 of every
-      // 16-key group swapped (the accumulator's key order)
-      const int qg = vquad & 3;
-      const int posq = (vquad & ~3) * 4 + (qg == 1 ? 2 : (qg == 2 ? 1 : qg)) * 4;
+    for (int ps = 0; ps < NKP; ++ps) {
+      const int key = tid / TPK + KPP * ps;
+      if (KT % KPP != 0 && key >= KT) break;
+      const int c0 = (tid % TPK) * CPT;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dw = e >> 1;
-        unsigned lo, hi;
-        if ((e & 1) == 0) {
-          lo = (stage[0][dw] & 0xffffu) | (stage[1][dw] << 16);
-          hi = (stage[2][dw] & 0xffffu) | (stage[3][dw] << 16);
-        } else {
-          lo = (stage[0][dw] >> 16) | (stage[1][dw] & 0xffff0000u);
-          hi = (stage[2][dw] >> 16) | (stage[3][dw] & 0xffff0000u);
+      for (int q = 0; q < CPT; ++q) *(u32x4*)&sK[kbuf][key * KPAD + 8 * (c0 + q)] = kst[ps][q];
+    }
+#pragma unroll
+    for (int j = 0; j < NVL; ++j) {
+      const int vt = tid + NT * j;
+      if (VTASKS % NT == 0 || vt < VTASKS) {
+        // keys 4*vquad..+3 go to LDS positions with quads 1 and 2 of every
+        // 16-key group swapped (the accumulator's key order)
+        const int vp = vt >> 4, vquad = vt & 15;
+        const int qg = vquad & 3;
+        const int posq = (vquad & ~3) * 4 + (qg == 1 ? 2 : (qg == 2 ? 1 : qg)) * 4;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int dw = e >> 1;
+          unsigned lo, hi;
+          if ((e & 1) == 0) {
+            lo = (vst[j][0][dw] & 0xffffu) | (vst[j][1][dw] << 16);
+            hi = (vst[j][2][dw] & 0xffffu) | (vst[j][3][dw] << 16);
+          } else {
+            lo = (vst[j][0][dw] >> 16) | (vst[j][1][dw] & 0xffff0000u);
+            hi = (vst[j][2][dw] >> 16) | (vst[j][3][dw] & 0xffff0000u);
+          }
+          u32x2 v2 = {lo, hi};
+          *(u32x2*)&sV[vbuf][(8 * vp + e) * VPAD + posq] = v2;
         }
-        u32x2 v2 = {lo, hi};
-        *(u32x2*)&sV[buf][(8 * vp + e) * VPAD + posq] = v2;
       }
     }
   };
@@ -409,7 +436,7 @@ __global__ __launch_bounds__(512, 1) void k_seg_attn(AttnArgs a) {
 
   if (n_tiles > 0) {
     load_tile(it.k_begin);
-    store_tile(0);
+    store_tile(0, 0);
   }
   __syncthreads();
 
@@ -473,8 +500,8 @@ __global__ __launch_bounds__(512, 1) void k_seg_attn(AttnArgs a) {
       for (int k = 0; k < 4; ++k) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r0 + 2 * k], c2, -m_use));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r0 + 2 * k + 1], c2, -m_use));
-        rs += p0 + p1;
         pk[k] = pack_bf2(p0, p1);
+        rs += p0 + p1;
       }
       pf[t] = __builtin_bit_cast(bf16x8, pk);
     }
@@ -491,7 +518,7 @@ __global__ __launch_bounds__(512, 1) void k_seg_attn(AttnArgs a) {
       }
     }
 
-    if (more) store_tile(buf ^ 1);
+    if (more) store_tile(buf ^ 1, buf ^ 1);
     __syncthreads();
   }
 
@@ -511,7 +538,7 @@ __global__ __launch_bounds__(512, 1) void k_seg_attn(AttnArgs a) {
         *(u32x2*)(op + 32 * cb + 8 * m + 4 * g) = v2;
       }
   } else {
-    const int prow = it.part * ATTN_ROWS + 32 * w + l32;
+    const int prow = it.part * ATTN_PART_ROWS + 32 * w + l32;
     float* po = a.part_o + (size_t)prow * DV;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
@@ -537,19 +564,19 @@ __global__ __launch_bounds__(256) void k_combine(AttnArgs a, const CombItem* __r
   const int G = a.group;
   const int rows_total = sg.q_len * G;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int rl = w; rl < ATTN_ROWS; rl += 4) {
+  for (int rl = w; rl < a.rows_per_block; rl += 4) {
     const int r = it.row0 + rl;
     if (r >= rows_total) break;
     float M = -INFINITY;
     for (int j = 0; j < it.nsplit; ++j)
-      M = fmaxf(M, a.part_ml[2 * ((size_t)(it.part0 + j) * ATTN_ROWS + rl)]);
+      M = fmaxf(M, a.part_ml[2 * ((size_t)(it.part0 + j) * ATTN_PART_ROWS + rl)]);
     const float Mu = M == -INFINITY ? 0.f : M;
     float L = 0.f;
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
     for (int j = 0; j < it.nsplit; ++j) {
-      const size_t prow = (size_t)(it.part0 + j) * ATTN_ROWS + rl;
+      const size_t prow = (size_t)(it.part0 + j) * ATTN_PART_ROWS + rl;
       const float wj = __builtin_amdgcn_exp2f(a.part_ml[2 * prow] - Mu);
       L += wj * a.part_ml[2 * prow + 1];
 #pragma unroll
@@ -577,9 +604,30 @@ bool attn_dims_supported(int d_nope, int d_rope, int d_v) {
   return (d_nope == 128 && d_rope == 64 && d_v == 128) || (d_nope == 32 && d_rope == 32 && d_v == 32);
 }
 
+// Waves per attention block: 8 (one 256-row block per CU, two waves per SIMD)
+// or 4 (128-row blocks, two independent blocks per CU).  The MLA 192-dim
+// kernel needs the registers of one block per CU.
+static int attn_waves(int d_nope) {
+  if (d_nope == 128) return 8;
+  static int w = [] {
+    const char* e = getenv("AKV_ATTN_WAVES");
+    return (e && atoi(e) == 4) ? 4 : 8;
+  }();
+  return w;
+}
+
+int attn_rows_per_block(int d_nope) { return 32 * attn_waves(d_nope); }
+
 template <int DQK, int DV, int DNOPE>
 static hipError_t launch_attn_t(hipStream_t st, const AttnArgs& a) {
-  hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE>), dim3(a.n_items), dim3(512), 0, st, a);
+  if constexpr (DNOPE == 128) {
+    hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE, 8>), dim3(a.n_items), dim3(512), 0, st, a);
+  } else {
+    if (attn_waves(DNOPE) == 8)
+      hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE, 8>), dim3(a.n_items), dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE, 4>), dim3(a.n_items), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

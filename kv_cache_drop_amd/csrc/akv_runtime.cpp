@@ -664,7 +664,7 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
                     AttnPlan& plan) {
   const akv_layout& L = p->L;
   const int G = L.n_q_heads / L.n_kv_heads;
-  const int RB = akv::ATTN_ROWS;
+  const int RB = akv::attn_rows_per_block(L.d_nope);
   const int KT = akv::ATTN_KTILE;
   plan.segs.clear();
   for (int32_t i = 0; i < n_segs; ++i)
@@ -1223,8 +1223,8 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
     float* part_o = nullptr;
     float* part_ml = nullptr;
     if (plan.n_parts > 0) {
-      part_o = (float*)sc.take((size_t)plan.n_parts * akv::ATTN_ROWS * L.d_v * 4);
-      part_ml = (float*)sc.take((size_t)plan.n_parts * akv::ATTN_ROWS * 2 * 4);
+      part_o = (float*)sc.take((size_t)plan.n_parts * akv::ATTN_PART_ROWS * L.d_v * 4);
+      part_ml = (float*)sc.take((size_t)plan.n_parts * akv::ATTN_PART_ROWS * 2 * 4);
     }
     if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
 
@@ -1256,6 +1256,7 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
     a.out = (uint16_t*)out;
     a.part_o = part_o;
     a.part_ml = part_ml;
+    a.rows_per_block = akv::attn_rows_per_block(L.d_nope);
     {
       KTimer tm(p, AKV_K_ATTN);
       e = akv::launch_seg_attn(p->stream, a, L.d_nope, L.d_rope, L.d_v);
