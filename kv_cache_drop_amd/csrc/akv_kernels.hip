@@ -288,7 +288,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_seg_attn(AttnArgs a) {
   constexpr int NCB = DV / 32;         // 32-wide column blocks of O^T
   constexpr int KCH = DQK / 8;         // 16-byte chunks per K row
   constexpr int VCH = DV / 8;          // 16-byte chunks per V row
-  constexpr int VTASKS = VCH * 16;     // V tasks: 4 keys x 8 columns each
+  constexpr int VTASKS = VCH * (KT / 2);  // V tasks: 2 keys x 8 columns each
   constexpr int NVL = (VTASKS + NT - 1) / NT;
   static_assert(DQK % 32 == 0 && DV % 32 == 0, "dims");
 
@@ -334,27 +334,51 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_seg_attn(AttnArgs a) {
   }
 
   // Loaders.  K: TPK threads per key row, each staging CPT consecutive 16-byte
-  // chunks, so a thread resolves one slot per pass.  V: VTASKS tasks of 4
-  // keys x 8 columns, transposed on the way into LDS.  Page offsets use 24-bit
-  // multiplies (pools hold fewer than 2^24 pages).
+  // chunks, so a thread resolves one slot per pass.  V: tasks of 2 keys x 8
+  // columns, transposed on the way into LDS.  Every thread issues the same
+  // loads (surplus threads repeat a task and write identical values), so the
+  // compiler can count outstanding loads exactly instead of draining them.
+  // Page offsets use 24-bit multiplies (pools hold fewer than 2^24 pages).
+  //
+  // The gather is a chain of two dependent global loads (slot index, then the
+  // row), each mostly an L2 miss, so it runs ahead of the compute: slot indices
+  // are fetched three tiles ahead and K/V rows two tiles ahead, into one of two
+  // register staging sets.  Indices past the list end are clamped to its last
+  // entry, so tail loads stay in bounds.
   constexpr int TPK = KCH < 8 ? KCH : 8;
   constexpr int CPT = KCH / TPK;
   constexpr int KPP = NT / TPK;                 // key rows per pass
   constexpr int NKP = (KT + KPP - 1) / KPP;     // passes
-  u32x4 kst[NKP][CPT];
-  u32x4 vst[NVL][4];
+  struct Slots {
+    int k[NKP];
+    int v[NVL][2];
+  };
+  struct Stage {
+    u32x4 k[NKP][CPT];
+    u32x4 v[NVL][2];
+  };
   const int HS = Hkv * S;
   const int hoff = kvh * S;
   const int kpe_hoff = (a.kpe_heads == 1 ? 0 : kvh) * S;
   const int kpe_hs = a.kpe_heads * S;
+  auto k_key = [&](int ps) { return (tid / TPK + KPP * ps) % KT; };
+  auto v_task = [&](int j) { return (tid + NT * j) % VTASKS; };
 
-  auto load_tile = [&](int k0) {
+  auto fetch_slots = [&](int k0, Slots& sl) {
+#pragma unroll
+    for (int ps = 0; ps < NKP; ++ps) sl.k[ps] = slots[min(k0 + k_key(ps), lkv - 1)];
+#pragma unroll
+    for (int j = 0; j < NVL; ++j) {
+      const int pair = v_task(j) % (KT / 2);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) sl.v[j][e] = slots[min(k0 + 2 * pair + e, lkv - 1)];
+    }
+  };
+
+  auto fetch_rows = [&](const Slots& sl, Stage& st) {
 #pragma unroll
     for (int ps = 0; ps < NKP; ++ps) {
-      const int key = tid / TPK + KPP * ps;
-      if (KT % KPP != 0 && key >= KT) break;
-      const int kk = min(k0 + key, lkv - 1);
-      const int slot = slots[kk];
+      const int slot = sl.k[ps];
       const int page = slot >> lg, off = slot & (S - 1);
       const int c0 = (tid % TPK) * CPT;
       const uint32_t row = __umul24(page, HS) + hoff + off;
@@ -364,63 +388,49 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_seg_attn(AttnArgs a) {
         const uint16_t* src;
         if (DNOPE == 0) {
           src = a.k_a + (size_t)row * DQK + 8 * c;
-        } else if (c < DNOPE / 8) {
-          src = a.k_a + (size_t)row * DNOPE + 8 * c;
         } else {
           const uint32_t prow = __umul24(page, kpe_hs) + kpe_hoff + off;
-          src = a.k_b + (size_t)prow * (DQK - DNOPE) + 8 * (c - DNOPE / 8);
+          const uint16_t* pn = a.k_a + (size_t)row * DNOPE + 8 * c;
+          const uint16_t* pp = a.k_b + (size_t)prow * (DQK - DNOPE) + 8 * (c - DNOPE / 8);
+          src = c < DNOPE / 8 ? pn : pp;
         }
-        kst[ps][q] = *(const u32x4*)src;
+        st.k[ps][q] = *(const u32x4*)src;
       }
     }
 #pragma unroll
     for (int j = 0; j < NVL; ++j) {
-      const int vt = tid + NT * j;
-      if (VTASKS % NT == 0 || vt < VTASKS) {
-        const int vp = vt >> 4, vquad = vt & 15;
+      const int vp = v_task(j) / (KT / 2);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kk = min(k0 + 4 * vquad + e, lkv - 1);
-          const int slot = slots[kk];
-          const uint32_t row = __umul24(slot >> lg, HS) + hoff + (slot & (S - 1));
-          vst[j][e] = *(const u32x4*)(a.v + (size_t)row * DV + 8 * vp);
-        }
+      for (int e = 0; e < 2; ++e) {
+        const int slot = sl.v[j][e];
+        const uint32_t row = __umul24(slot >> lg, HS) + hoff + (slot & (S - 1));
+        st.v[j][e] = *(const u32x4*)(a.v + (size_t)row * DV + 8 * vp);
       }
     }
   };
 
-  auto store_tile = [&](int kbuf, int vbuf) {
+  auto store_tile = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int ps = 0; ps < NKP; ++ps) {
-      const int key = tid / TPK + KPP * ps;
-      if (KT % KPP != 0 && key >= KT) break;
       const int c0 = (tid % TPK) * CPT;
 #pragma unroll
-      for (int q = 0; q < CPT; ++q) *(u32x4*)&sK[kbuf][key * KPAD + 8 * (c0 + q)] = kst[ps][q];
+      for (int q = 0; q < CPT; ++q)
+        *(u32x4*)&sK[buf][k_key(ps) * KPAD + 8 * (c0 + q)] = st.k[ps][q];
     }
 #pragma unroll
     for (int j = 0; j < NVL; ++j) {
-      const int vt = tid + NT * j;
-      if (VTASKS % NT == 0 || vt < VTASKS) {
-        // keys 4*vquad..+3 go to LDS positions with quads 1 and 2 of every
-        // 16-key group swapped (the accumulator's key order)
-        const int vp = vt >> 4, vquad = vt & 15;
-        const int qg = vquad & 3;
-        const int posq = (vquad & ~3) * 4 + (qg == 1 ? 2 : (qg == 2 ? 1 : qg)) * 4;
+      // keys 2*pair, 2*pair+1 go to LDS positions with quads 1 and 2 of every
+      // 16-key group swapped (the accumulator's key order)
+      const int vt = v_task(j);
+      const int pair = vt % (KT / 2), vp = vt / (KT / 2);
+      const int key = 2 * pair, quad = key >> 2, qg = quad & 3;
+      const int pos = (quad & ~3) * 4 + (qg == 1 ? 2 : (qg == 2 ? 1 : qg)) * 4 + (key & 3);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int dw = e >> 1;
-          unsigned lo, hi;
-          if ((e & 1) == 0) {
-            lo = (vst[j][0][dw] & 0xffffu) | (vst[j][1][dw] << 16);
-            hi = (vst[j][2][dw] & 0xffffu) | (vst[j][3][dw] << 16);
-          } else {
-            lo = (vst[j][0][dw] >> 16) | (vst[j][1][dw] & 0xffff0000u);
-            hi = (vst[j][2][dw] >> 16) | (vst[j][3][dw] & 0xffff0000u);
-          }
-          u32x2 v2 = {lo, hi};
-          *(u32x2*)&sV[vbuf][(8 * vp + e) * VPAD + posq] = v2;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int dw = e >> 1;
+        const unsigned w2 = (e & 1) == 0 ? (st.v[j][0][dw] & 0xffffu) | (st.v[j][1][dw] << 16)
+                                          : (st.v[j][0][dw] >> 16) | (st.v[j][1][dw] & 0xffff0000u);
+        *(unsigned*)&sV[buf][(8 * vp + e) * VPAD + pos] = w2;
       }
     }
   };
@@ -434,17 +444,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_seg_attn(AttnArgs a) {
   float l_run = 0.f;
   const float c2 = a.scale_log2e;
 
-  if (n_tiles > 0) {
-    load_tile(it.k_begin);
-    store_tile(0, 0);
-  }
+  Slots slA, slB;
+  Stage stA, stB;
+  const int k_begin = it.k_begin;
+  fetch_slots(k_begin, slA);
+  fetch_rows(slA, stA);
+  fetch_slots(k_begin + KT, slB);
+  fetch_rows(slB, stB);
+  fetch_slots(k_begin + 2 * KT, slA);
+  store_tile(stA, 0);
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
+  // Tile j: rows of tile j+2 are requested into the staging set tile j used,
+  // slots of tile j+3 into the slot set tile j+1 used, the tile is computed,
+  // and tile j+1 (requested one iteration earlier) is written to LDS.  The
+  // loop runs an even number of tiles: a tile past the range is fully masked
+  // and adds nothing.
+  auto step = [&](int j, Slots& sl_cur, Stage& st_cur, Slots& sl_nxt, Stage& st_nxt) {
     const int buf = j & 1;
-    const int k0 = it.k_begin + j * KT;
-    const bool more = j + 1 < n_tiles;
-    if (more) load_tile(k0 + KT);
+    const int k0 = k_begin + j * KT;
+    fetch_rows(sl_cur, st_cur);      // sl_cur holds tile j+2's slots
+    fetch_slots(k0 + 3 * KT, sl_nxt);
 
     // S^T = K Q^T: two 32-key blocks
     f32x16 sacc[2];
@@ -518,8 +538,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_seg_attn(AttnArgs a) {
       }
     }
 
-    if (more) store_tile(buf ^ 1, buf ^ 1);
+    store_tile(st_nxt, buf ^ 1);
     __syncthreads();
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, slA, stA, slB, stB);
+    step(j + 1, slB, stB, slA, stA);
   }
 
   // the two lanes of a row hold disjoint key halves of l
