@@ -30,6 +30,28 @@ for _p in (ROOT, os.path.join(ROOT, "tests")):
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
+# HBM byte counters per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE,
+# KiB) of the kernels as built from the source with this SHA-1, on this
+# workload.  A plain 1 GiB device copy reads FETCH_SIZE = 524,300 KiB and
+# WRITE_SIZE = 1,048,576 KiB, so fetched KiB are scaled by 2.0 and written KiB
+# by 1.0.  When the kernel source differs, traffic is reported as null.
+COUNTERS = {
+    "kernel_source_sha1": "7d09bde2caaaa84758f2301cc3f4bd74e464d218",
+    "fetch_scale": 1048576 / 524300, "write_scale": 1.0,
+    "attention": {"fetch_kib": 110381, "write_kib": 16384},
+    "rotate": {"fetch_kib": 39035, "write_kib": 77626},
+}
+
+
+def counted_traffic(kind: str):
+    import hashlib
+    src = os.path.join(ROOT, "kv_cache_drop_amd", "csrc", "akv_kernels.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha1(f.read()).hexdigest() != COUNTERS["kernel_source_sha1"]:
+            return None
+    c = COUNTERS[kind]
+    return round((c["fetch_kib"] * COUNTERS["fetch_scale"] + c["write_kib"] * COUNTERS["write_scale"]) * 1024)
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -97,7 +119,20 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=16, help="oracle query rows per segment")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 1 << 30, "copies": 3}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path is measured on one "
               "MI355X and has no multi-GPU mode", file=sys.stderr)
@@ -161,6 +196,8 @@ def main():
     pool.timing_enable(False)
 
     flops, pairs = attention_flops(L, segs, page_lists)
+    ex_all = np.asarray(page_lists).reshape(-1, 3)
+    kv_bytes = int((ex_all[:, 2] - ex_all[:, 1]).sum()) * L.n_kv_heads * (L.d_rope + L.d_v) * 2
     n_rep = int(sum(e - b for b, e in repos.spans))
     rep_bytes = 2.0 * L.n_kv_heads * L.d_rope * 2 * n_rep      # read + write of the rotated keys
     ms_step = wall / args.steps * 1e3
@@ -195,11 +232,14 @@ def main():
                    "repositioned_tokens": n_rep, "query_tokens": int(att.q.shape[0]), "segments": 4,
                    "seed": args.seed},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "k_seg_attn<128,128,0>", "flop_per_launch": flops,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": counted_traffic("attention"),
+                     "kernel": "k_seg_attn<128,128,0,8>", "flop_per_launch": flops,
+                     "kv_bytes_per_launch": kv_bytes,
                      "avg_launch_ms": round(attn_ms, 5)},
         "roofline_repos": {"bound": "hbm", "achieved": round(rot_gbps, 1), "peak": PEAK_HBM_GBPS,
-                           "unit": "GB/s", "frac": round(rot_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                           "unit": "GB/s", "frac": round(rot_gbps / PEAK_HBM_GBPS, 4),
+                           "traffic": counted_traffic("rotate"),
                            "kernel": "k_rotate", "bytes_per_launch": rep_bytes,
                            "avg_launch_ms": round(rot_ms, 5)},
         "kernels_ms_per_step": {k: round(v[0] / max(args.steps, 1), 5) for k, v in kt.items()},
