@@ -611,10 +611,13 @@ akv_status repos_totals(akv_pool* p, SeqRec& q, const akv_span* sp, const int32_
 }
 
 // Work items: runs of consecutive slots of one page with one delta, in logical
-// token order.
+// token order, cut to about 16 KiB of rotated keys each (half a 16-token page
+// of 8 heads x 128 dims) so the blocks spread evenly over the CUs.
 void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<int64_t>& tot,
                  std::vector<akv::RotItem>& items, std::vector<int32_t>& deltas) {
   const int32_t S = p->L.page_size;
+  const int32_t row_bytes = p->rope_heads() * p->L.d_rope * 2;
+  const int32_t max_rows = std::max<int32_t>(1, 16384 / row_bytes);
   std::unordered_map<int64_t, int32_t> didx;
   items.clear();
   deltas.clear();
@@ -632,7 +635,7 @@ void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<int64_t>&
       di = f->second;
     }
     if (!items.empty() && items.back().page == pg && items.back().hi == off &&
-        items.back().didx == di)
+        items.back().didx == di && items.back().hi - items.back().lo < max_rows)
       items.back().hi += 1;
     else
       items.push_back({pg, off, off + 1, di});
