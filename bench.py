@@ -32,14 +32,14 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 # HBM byte counters per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE,
 # KiB) of the kernels as built from the source with this SHA-1, on this
-# workload.  A plain 1 GiB device copy reads FETCH_SIZE = 524,300 KiB and
+# workload.  A plain 1 GiB device copy reads FETCH_SIZE = 524,302 KiB and
 # WRITE_SIZE = 1,048,576 KiB, so fetched KiB are scaled by 2.0 and written KiB
 # by 1.0.  When the kernel source differs, traffic is reported as null.
 COUNTERS = {
-    "kernel_source_sha1": "7d09bde2caaaa84758f2301cc3f4bd74e464d218",
-    "fetch_scale": 1048576 / 524300, "write_scale": 1.0,
-    "attention": {"fetch_kib": 110381, "write_kib": 16384},
-    "rotate": {"fetch_kib": 39035, "write_kib": 77626},
+    "kernel_source_sha1": "1da3e80b7fc9ee068418dfbeefde00fcbfadda42",
+    "fetch_scale": 1048576 / 524302, "write_scale": 1.0,
+    "attention": {"fetch_kib": 111093, "write_kib": 16384},
+    "rotate": {"fetch_kib": 39189, "write_kib": 77622},
 }
 
 
@@ -51,6 +51,14 @@ def counted_traffic(kind: str):
             return None
     c = COUNTERS[kind]
     return round((c["fetch_kib"] * COUNTERS["fetch_scale"] + c["write_kib"] * COUNTERS["write_scale"]) * 1024)
+
+
+def attention_kernel_name(layout) -> str:
+    """The attention kernel the library launches for this layout."""
+    if layout.d_nope == 0 and layout.d_rope == 128 and layout.d_v == 128 and \
+            os.environ.get("AKV_ATTN_KERNEL") != "staged" and os.environ.get("AKV_ATTN_WAVES") != "4":
+        return "k_seg_attn_dl<128,128,0,8,1,4>"
+    return "k_seg_attn"
 
 
 def log(*a):
@@ -234,7 +242,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": counted_traffic("attention"),
-                     "kernel": "k_seg_attn<128,128,0,8>", "flop_per_launch": flops,
+                     "kernel": attention_kernel_name(L), "flop_per_launch": flops,
                      "kv_bytes_per_launch": kv_bytes,
                      "avg_launch_ms": round(attn_ms, 5)},
         "roofline_repos": {"bound": "hbm", "achieved": round(rot_gbps, 1), "peak": PEAK_HBM_GBPS,

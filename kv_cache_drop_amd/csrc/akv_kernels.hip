@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "akv_internal.h"
@@ -603,11 +604,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_seg_attn(AttnArgs a) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define AKV_LDS __attribute__((address_space(3)))
 
-// Instruction interleave of one attention iteration's main block (groups are
-// filled in order: mask 0x8 MFMA, 0x2 VALU, 0x100 LDS read).
-#ifndef AKV_SCHED_ITER
-#define AKV_SCHED_ITER() ((void)0)
-#endif
 
 template <int CH, int PAD>
 struct LdsPart {
@@ -650,7 +646,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
   if (it.seg < 0) return;
   const AttnSeg sg = a.segs[it.seg];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 5, l32 = lane & 31;
   const int G = a.group;
   const int lq = sg.q_len, lkv = sg.lkv;
   const int rows_total = lq * G;
@@ -761,14 +757,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
     }
   };
 
-  // Mask, running max and lazy rescale for tile j (the branchy part of the
-  // online softmax); returns the exponent offset of each row block.
-  auto sm_prep = [&](f32x16 (&sacc)[QB][2], int j, float (&m_use)[QB]) __attribute__((always_inline)) {
+  // Causal / range mask of tile j (taken only on tiles that reach past a
+  // row's limit or the item's key range).
+  auto sm_mask = [&](f32x16 (&sacc)[QB][2], int j) __attribute__((always_inline)) {
     const int k0 = it.k_begin + j * KT;
-    const bool need_mask = (k0 + KT > k_end) || (k0 + KT - 1 > lim_first);
+    if ((k0 + KT > k_end) || (k0 + KT - 1 > lim_first)) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      if (need_mask) {
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -776,14 +771,26 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
             const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
             if (key > lim[qb]) sacc[qb][kb][i] = -INFINITY;
           }
-      }
-      float mx = -INFINITY;
+    }
+  };
+  // Row max of tile j's scores (both lane halves of a row agree).
+  auto sm_max = [&](const f32x16 (&sacc)[QB][2], float (&mx)[QB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float m = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[qb][kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_cand = fmaxf(m_run[qb], mx * c2);
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, sacc[qb][kb][i]);
+      mx[qb] = fmaxf(m, __shfl_xor(m, 32));
+    }
+  };
+  // Lazy rescale: move the running offset only when the max grew by more
+  // than 2^RESCALE_LOG2; returns the exponent offset of each row block.
+  auto sm_rescale = [&](const float (&mx)[QB], int j, float (&m_use)[QB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_cand = fmaxf(m_run[qb], mx[qb] * c2);
       if (__ballot(m_cand > m_run[qb] + RESCALE_LOG2)) {
         const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_cand);
         l_run[qb] *= alpha;
@@ -875,31 +882,65 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
   // tile j - 1's stage complete before any wave reloads it.
   constexpr int WAITV = NIW + 1;
   static_assert(WAITV <= 15, "vmcnt");
-  auto iteration = [&](int j, auto c, f32x16 (&s_cur)[QB][2], f32x16 (&s_nxt)[QB][2])
-      __attribute__((always_inline)) {
-    constexpr int C = decltype(c)::value;   // j % 4
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(WAITV) : "memory");
-    issue_tile(stage_ptr((C + 3) & 3), (C + 3) & 3);
-    slot_load((C + 1) & 3, j + 5);
-    // The scores of tile j + 1 run on the matrix cores while the vector units
-    // take tile j's max and exponentials; tile j's PV follows its exponentials.
-    qk(stage_ptr((C + 1) & 3), s_nxt);
-    float m_use[QB];
-    sm_prep(s_cur, j, m_use);
-    bf16x8 pf[QB][4];
-    sm_exp(s_cur, m_use, pf);
-    pv(stage_ptr(C), pf);
-    AKV_SCHED_ITER();
-  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  for (int j = 0; j < n_tiles; j += 4) {
-    iteration(j, I0{}, sa, sb);
-    iteration(j + 1, I1{}, sb, sa);
-    iteration(j + 2, I2{}, sa, sb);
-    iteration(j + 3, I3{}, sb, sa);
+  auto sync = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(WAITV) : "memory");
+  };
+  // Tiles j < jm need no mask (they end before every row's limit and before
+  // the item's key range end).  The main loop runs while tiles j .. j + 4 are
+  // all such tiles: its iteration is one basic block apart from the rare
+  // rescale branch at the top (the row max of tile j + 1 is taken at the end
+  // of iteration j).  The remaining tiles run in the masked loop.
+  const int lmask = min(k_end, lim_first + 1) - it.k_begin;
+  const int jm = lmask > 0 ? lmask / KT : 0;
+  float mx[QB];
+  auto main_iter = [&](int j, auto c, f32x16 (&s_cur)[QB][2], f32x16 (&s_nxt)[QB][2])
+      __attribute__((always_inline)) {
+    constexpr int C = decltype(c)::value;   // j % 4
+    sync();
+    float m_use[QB];
+    sm_rescale(mx, j, m_use);
+    issue_tile(stage_ptr((C + 3) & 3), (C + 3) & 3);
+    slot_load((C + 1) & 3, j + 5);
+    qk(stage_ptr((C + 1) & 3), s_nxt);
+    bf16x8 pf[QB][4];
+    sm_exp(s_cur, m_use, pf);
+    pv(stage_ptr(C), pf);
+    sm_max(s_nxt, mx);
+  };
+  auto tail_iter = [&](int j, auto c, f32x16 (&s_cur)[QB][2], f32x16 (&s_nxt)[QB][2])
+      __attribute__((always_inline)) {
+    constexpr int C = decltype(c)::value;
+    sync();
+    issue_tile(stage_ptr((C + 3) & 3), (C + 3) & 3);
+    slot_load((C + 1) & 3, j + 5);
+    float m_use[QB];
+    bf16x8 pf[QB][4];
+    sm_mask(s_cur, j);
+    qk(stage_ptr((C + 1) & 3), s_nxt);
+    sm_max(s_cur, mx);
+    sm_rescale(mx, j, m_use);
+    sm_exp(s_cur, m_use, pf);
+    pv(stage_ptr(C), pf);
+  };
+  int j = 0;
+  if (jm > 4) {
+    sm_max(sa, mx);
+    for (; j + 4 < jm; j += 4) {
+      main_iter(j, I0{}, sa, sb);
+      main_iter(j + 1, I1{}, sb, sa);
+      main_iter(j + 2, I2{}, sa, sb);
+      main_iter(j + 3, I3{}, sb, sa);
+    }
+  }
+  for (; j < n_tiles; j += 4) {
+    tail_iter(j, I0{}, sa, sb);
+    tail_iter(j + 1, I1{}, sb, sa);
+    tail_iter(j + 2, I2{}, sa, sb);
+    tail_iter(j + 3, I3{}, sb, sa);
   }
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -1002,25 +1043,21 @@ static int attn_waves(int d_nope) {
 int attn_rows_per_block(int d_nope) { return 32 * attn_waves(d_nope); }
 
 
-// Direct-to-LDS attention variant for the 128-dim GQA layout: 0 = off,
-// 1 = 8 waves x 32 rows, 2 = 4 waves x 64 rows.
-static int attn_dl_mode() {
-  static int m = [] {
-    const char* e = getenv("AKV_ATTN_DL");
-    return e ? atoi(e) : 0;
+// The 128-dim GQA layout runs the direct-to-LDS kernel; AKV_ATTN_KERNEL=staged
+// selects the register-staged kernel instead (kept for comparison).
+static bool attn_use_dl() {
+  static bool dl = [] {
+    const char* e = getenv("AKV_ATTN_KERNEL");
+    return !(e && strcmp(e, "staged") == 0);
   }();
-  return m;
+  return dl;
 }
 
 template <int DQK, int DV, int DNOPE>
 static hipError_t launch_attn_t(hipStream_t st, const AttnArgs& a) {
   if constexpr (DQK == 128 && DV == 128 && DNOPE == 0) {
-    if (attn_waves(DNOPE) == 8 && attn_dl_mode() == 1) {
+    if (attn_waves(DNOPE) == 8 && attn_use_dl()) {
       hipLaunchKernelGGL((k_seg_attn_dl<128, 128, 0, 8, 1, 4>), dim3(a.n_items), dim3(512), 0, st, a);
-      return hipGetLastError();
-    }
-    if (attn_waves(DNOPE) == 8 && attn_dl_mode() == 2) {
-      hipLaunchKernelGGL((k_seg_attn_dl<128, 128, 0, 4, 2, 4>), dim3(a.n_items), dim3(256), 0, st, a);
       return hipGetLastError();
     }
   }
