@@ -51,9 +51,14 @@ constexpr int ATTN_KTILE = 64;       // keys per pipeline stage
 int attn_rows_per_block(int d_nope);
 
 // ---- launchers --------------------------------------------------------------
+// fp32 cos/sin table of n_deltas deltas: table[di][0..d/2) = cos,
+// table[di][d/2..d) = sin (n_deltas x d_rope floats).
+hipError_t launch_rot_table(hipStream_t st, int d_rope, const int32_t* deltas, int n_deltas,
+                            const double* inv_freq, float* table);
+
+// Rotates the items in place with the table's rows (RotItem::didx).
 hipError_t launch_rotate(hipStream_t st, uint16_t* kr, int n_heads, int page_size, int d_rope,
-                         int pairing, const RotItem* items, int n_items, const int32_t* deltas,
-                         const double* inv_freq);
+                         int pairing, const RotItem* items, int n_items, const float* table);
 
 hipError_t launch_scatter_rows(hipStream_t st, const uint16_t* src, uint16_t* dst,
                                const int32_t* slots, int n, int n_heads, int page_size,

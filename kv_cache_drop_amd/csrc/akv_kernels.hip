@@ -44,16 +44,17 @@ __device__ __forceinline__ unsigned pack_bf2(float a, float b) {
 // ---------------------------------------------------------------------------
 // repos rotation ([AKV-blog] section 2, The Repos Primitive; [Leyline] Method)
 //
-// One block per work item (page, rows lo..hi-1, delta).  The block forms the
-// d_rope/2 angles delta * theta_i in fp64, reduces them mod 2*pi, takes sin
-// and cos once into LDS, and every head and row of the item reuses them.  A
-// "unit" is 8 rotation pairs held in two 16-byte loads; pair (x, y) becomes
-// (x cos - y sin, x sin + y cos) in fp32 and is rounded once to bf16.
-// The first pass issues its loads before the angle table is built so the
-// memory latency overlaps the fp64 work.
+// k_rot_table: one block per distinct delta forms the d_rope/2 angles
+// delta * theta_i in fp64, reduces them mod 2*pi and stores cos and sin as
+// fp32 (table[di][0..half) = cos, table[di][half..d) = sin).
+// k_rotate: one block per work item (page, rows lo..hi-1, delta); the block
+// stages its delta's row of the table in LDS and every head and row of the
+// item reuses it.  A "unit" is 8 rotation pairs held in two 16-byte loads;
+// pair (x, y) becomes (x cos - y sin, x sin + y cos) in fp32 and is rounded
+// once to bf16.  The first pass issues its loads before the table is staged.
 // ---------------------------------------------------------------------------
 constexpr int ROT_THREADS = 256;
-constexpr int ROT_UPT = 4;
+constexpr int ROT_UPT = 2;   // 512 units (one 16 KiB item) per pass
 
 __device__ __forceinline__ unsigned rot_pair_word(unsigned w, float c, float s) {
   // word holds an interleaved pair (x = low half, y = high half)
@@ -61,11 +62,23 @@ __device__ __forceinline__ unsigned rot_pair_word(unsigned w, float c, float s) 
   return pack_bf2(fmaf(x, c, -y * s), fmaf(x, s, y * c));
 }
 
-__global__ __launch_bounds__(ROT_THREADS) void k_rotate(uint16_t* __restrict__ kr, int n_heads, int S,
+__global__ __launch_bounds__(64) void k_rot_table(int d, const int32_t* __restrict__ deltas,
+                                                  const double* __restrict__ inv_freq,
+                                                  float* __restrict__ table) {
+  const int half = d >> 1, i = threadIdx.x;
+  if (i >= half) return;
+  const double ang = (double)deltas[blockIdx.x] * inv_freq[i];
+  const double red = ang - 6.283185307179586476925 * rint(ang * 0.15915494309189533577);
+  double sv, cv;
+  sincos(red, &sv, &cv);
+  table[(size_t)blockIdx.x * d + i] = (float)cv;
+  table[(size_t)blockIdx.x * d + half + i] = (float)sv;
+}
+
+__global__ __launch_bounds__(ROT_THREADS, 8) void k_rotate(uint16_t* __restrict__ kr, int n_heads, int S,
                                                          int d, int pairing,
                                                          const RotItem* __restrict__ items,
-                                                         const int32_t* __restrict__ deltas,
-                                                         const double* __restrict__ inv_freq) {
+                                                         const float* __restrict__ table) {
   __shared__ float s_c[128], s_s[128];
   const RotItem it = items[blockIdx.x];
   const int half = d >> 1;
@@ -106,12 +119,8 @@ __global__ __launch_bounds__(ROT_THREADS) void k_rotate(uint16_t* __restrict__ k
     }
   }
   if ((int)threadIdx.x < half) {
-    const double ang = (double)deltas[it.didx] * inv_freq[threadIdx.x];
-    const double red = ang - 6.283185307179586476925 * rint(ang * 0.15915494309189533577);
-    double sv, cv;
-    sincos(red, &sv, &cv);
-    s_c[threadIdx.x] = (float)cv;
-    s_s[threadIdx.x] = (float)sv;
+    s_c[threadIdx.x] = table[(size_t)it.didx * d + threadIdx.x];
+    s_s[threadIdx.x] = table[(size_t)it.didx * d + half + threadIdx.x];
   }
   __syncthreads();
 
@@ -150,12 +159,18 @@ __global__ __launch_bounds__(ROT_THREADS) void k_rotate(uint16_t* __restrict__ k
   }
 }
 
+hipError_t launch_rot_table(hipStream_t st, int d_rope, const int32_t* deltas, int n_deltas,
+                            const double* inv_freq, float* table) {
+  if (n_deltas <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rot_table, dim3(n_deltas), dim3(64), 0, st, d_rope, deltas, inv_freq, table);
+  return hipGetLastError();
+}
+
 hipError_t launch_rotate(hipStream_t st, uint16_t* kr, int n_heads, int page_size, int d_rope,
-                         int pairing, const RotItem* items, int n_items, const int32_t* deltas,
-                         const double* inv_freq) {
+                         int pairing, const RotItem* items, int n_items, const float* table) {
   if (n_items <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_rotate, dim3(n_items), dim3(ROT_THREADS), 0, st, kr, n_heads, page_size,
-                     d_rope, pairing, items, deltas, inv_freq);
+                     d_rope, pairing, items, table);
   return hipGetLastError();
 }
 

@@ -476,11 +476,14 @@ akv_status device_rotate(akv_pool* p, const std::vector<akv::RotItem>& items,
   akv_status st = upload_array(p, sc, items.data(), items.size() * sizeof(akv::RotItem), &ditems);
   if (st == AKV_OK) st = upload_array(p, sc, deltas.data(), deltas.size() * 4, &ddeltas);
   if (st != AKV_OK) return st;
+  float* dtab = (float*)sc.take(deltas.size() * (size_t)p->L.d_rope * 4);
+  if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
+  hipError_t e = akv::launch_rot_table(p->stream, p->L.d_rope, (const int32_t*)ddeltas,
+                                       (int)deltas.size(), (const double*)p->scratch, dtab);
+  if (e != hipSuccess) return check_launch(e, "rotation table kernel launch");
   KTimer tm(p, AKV_K_ROTATE);
-  hipError_t e = akv::launch_rotate(p->stream, p->rope_array(), p->rope_heads(), p->L.page_size,
-                                    p->L.d_rope, p->L.pairing, (const akv::RotItem*)ditems,
-                                    (int)items.size(), (const int32_t*)ddeltas,
-                                    (const double*)p->scratch);
+  e = akv::launch_rotate(p->stream, p->rope_array(), p->rope_heads(), p->L.page_size, p->L.d_rope,
+                         p->L.pairing, (const akv::RotItem*)ditems, (int)items.size(), dtab);
   tm.done();
   return check_launch(e, "rotate kernel launch");
 }
@@ -640,6 +643,10 @@ void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<int64_t>&
     else
       items.push_back({pg, off, off + 1, di});
   }
+  // Physical page order: neighbouring blocks then touch neighbouring memory.
+  std::sort(items.begin(), items.end(), [](const akv::RotItem& a, const akv::RotItem& b) {
+    return a.page != b.page ? a.page < b.page : a.lo < b.lo;
+  });
 }
 
 void repos_commit(SeqRec& q, const std::vector<int64_t>& tot) {
