@@ -119,8 +119,128 @@ def cpu_baseline(wl, rows_per_seg: int):
                 est_step_s=round(t_step, 2))
 
 
+def run_config(args) -> dict:
+    """One JSON record for a workload other than the headline: replay its op
+    script on a fresh device pool per rep (set-up appends untimed), flush L2 and
+    the Infinity Cache with a 1 GiB write, then time the remaining ops (drop /
+    repos / splice, the new tokens' append, attention) as one step."""
+    import torch
+    import device_script as D
+    import workloads as W
+
+    gens = {"c1": lambda s: W.c1_tiny(s, "canonical"), "c3": W.c3_mla, "c4": W.c4_batched, "c5": W.c5_128k}
+    wl = gens[args.config](args.seed)
+    L = wl.layout
+    ops = list(wl.ops)
+    i0 = next(i for i, o in enumerate(ops) if not isinstance(o, (W.SeqCreate, W.Append)))
+    n_seq = sum(isinstance(o, W.SeqCreate) for o in ops)
+    # device inputs of the timed ops, uploaded once (outside the timed region)
+    dev = {}
+    for i, op in enumerate(ops[i0:], start=i0):
+        if isinstance(op, (W.Append, W.Splice)):
+            dev[i] = (D.dev_bf16(op.k), D.dev_bf16(op.kpe) if op.kpe is not None else None, D.dev_bf16(op.v))
+        elif isinstance(op, W.Attention):
+            q = D.dev_bf16(op.q)
+            dev[i] = (q, torch.empty((q.shape[0], L.n_q_heads, L.d_v), dtype=torch.bfloat16, device="cuda:0"))
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    rope_heads = L.n_kv_heads if (not L.mla or L.kpe_per_head) else 1
+    tot = {k: [0.0, 0] for k in ("attention", "rotate", "append", "compact", "expand", "combine")}
+    walls, flops, pairs, kv_bytes, n_rot, n_q = [], 0.0, 0, 0, 0, 0
+    kern = None
+    for rep in range(args.warmup + args.steps):
+        pool = D.make_pool(wl)
+        keep = []
+        for op in ops[:i0]:
+            D.apply_op(pool, op, keep)
+        pre = [pool.tokens(s) for s in range(n_seq)] if rep == 0 else None
+        flush.fill_(rep & 255)
+        torch.cuda.synchronize()
+        timed = rep >= args.warmup
+        pool.timing_enable(timed)
+        lists = []
+        t0 = time.perf_counter()
+        for i, op in enumerate(ops[i0:], start=i0):
+            if isinstance(op, W.Append):
+                pool.append(op.seq, op.pos, dev[i][0], dev[i][1], dev[i][2])
+            elif isinstance(op, W.Splice):
+                pool.splice(op.seq, op.spans, op.stub_lens, dev[i][0], dev[i][1], dev[i][2])
+            elif isinstance(op, W.Attention):
+                rows, ex = D.segment_inputs(pool, op)
+                pool.segment_attention(dev[i][0], rows, ex, op.scale, out=dev[i][1])
+                lists.append((rows, ex, op))
+            else:
+                D.apply_op(pool, op, keep)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        if timed:
+            walls.append(wall)
+            for k in tot:
+                ms, n = pool.timing_read(k)
+                tot[k][0] += ms
+                tot[k][1] += n
+        if rep == 0:
+            for s in range(n_seq):
+                _, pos0, drop0 = pre[s]
+                _, pos1, drop1 = pool.tokens(s)
+                m = len(pos0)
+                n_rot += int(((pos1[:m] != pos0) & ~drop1[:m].astype(bool)).sum())
+            for rows, ex, op in lists:
+                f, p = attention_flops(L, rows, ex)
+                flops += float(f)
+                pairs += int(p)
+                exa = np.asarray(ex).reshape(-1, 3)
+                kv_bytes += int((exa[:, 2] - exa[:, 1]).sum()) * L.n_kv_heads * (L.d_nope + L.d_rope + L.d_v) * 2
+                n_q += int(op.q.shape[0])
+            kern = attention_kernel_name(L)
+        pool.close()
+        del pool, keep
+    ms_step = float(np.median(walls)) * 1e3
+    attn_ms = tot["attention"][0] / max(tot["attention"][1], 1)
+    rot_ms = tot["rotate"][0] / max(tot["rotate"][1], 1) if tot["rotate"][1] else None
+    rep_bytes = 2.0 * rope_heads * L.d_rope * 2 * n_rot
+    # per step: one attention launch; rotate launches per step = tot count / steps
+    rot_per_step = tot["rotate"][1] / max(args.steps, 1)
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "segment-batch attn TFLOP/s + repos GB/s, % of MI355X roofline",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": CONFIG_NAMES[args.config], "seed": args.seed, "query_tokens": n_q,
+                   "repositioned_tokens": n_rot, "attention_pairs": pairs},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": kern, "flop_per_launch": flops, "kv_bytes_per_launch": kv_bytes,
+                     "avg_launch_ms": round(attn_ms, 5)},
+        "kernels_ms_per_step": {k: round(v[0] / max(args.steps, 1), 5) for k, v in tot.items()},
+    }
+    if rot_ms is not None:
+        rot_gbps = rep_bytes / (rot_ms * rot_per_step * 1e-3) / 1e9
+        rec["roofline_repos"] = {"bound": "hbm", "achieved": round(rot_gbps, 1), "peak": PEAK_HBM_GBPS,
+                                 "unit": "GB/s", "frac": round(rot_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                                 "kernel": "k_rotate", "bytes_per_step": rep_bytes,
+                                 "launches_per_step": rot_per_step,
+                                 "avg_launch_ms": round(rot_ms, 5)}
+    return rec
+
+
+CONFIG_NAMES = {
+    "c1": "tiny 2K-token check (8 q / 2 kv heads, head_dim 64, page 16): drop 2 spans, repos the suffix by -640, "
+          "2 segments",
+    "c3": "MLA 17K context (16 heads, K_nope 128 + shared K_pe 64, V 128, page 64): 1-3 splices, one 512-query "
+          "segment",
+    "c4": "16 batched requests of 8K-32K tokens on the 64K layer shape (32 q / 8 kv heads, head_dim 128, "
+          "page 16), about 40 segments in one launch",
+    "c5": "128K-token agent trace, 64 q / 8 kv heads, head_dim 128, page 16: drop 60 spans, repos 60 runs, "
+          "4096 queries in 8 segments",
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"],
+                    help="c2 (default) is the headline 64K step; the others print one record each")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
@@ -145,6 +265,9 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path is measured on one "
               "MI355X and has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
+    if args.config != "c2":
+        print(json.dumps(run_config(args)), flush=True)
+        return
 
     import torch
     import device_script as D

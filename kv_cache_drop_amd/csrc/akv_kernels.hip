@@ -994,46 +994,65 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
 }
 
 // Split-KV merge: O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j (m in log2
-// units).  One wave per row; lanes split the d_v columns.
+// units).  One wave per row, four rows per block, so every row of every item
+// is its own wave: lane j holds split j's (m, l) (the planner splits at most
+// 64 ways), the row max and the weighted l come from wave reductions, and the
+// lanes split the d_v columns with all splits' loads in flight together.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 template <int DV>
-__global__ __launch_bounds__(256) void k_combine(AttnArgs a, const CombItem* __restrict__ items) {
+__global__ __launch_bounds__(256) void k_combine(AttnArgs a, const CombItem* __restrict__ items,
+                                                  int blocks_per_item) {
   constexpr int PER = DV / 64 > 0 ? DV / 64 : 1;
-  const CombItem it = items[blockIdx.x];
+  const CombItem it = items[blockIdx.x / blocks_per_item];
+  const int lane = threadIdx.x & 63;
+  const int rl = (blockIdx.x % blocks_per_item) * 4 + (threadIdx.x >> 6);
   const AttnSeg sg = a.segs[it.seg];
   const int G = a.group;
-  const int rows_total = sg.q_len * G;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int rl = w; rl < a.rows_per_block; rl += 4) {
-    const int r = it.row0 + rl;
-    if (r >= rows_total) break;
-    float M = -INFINITY;
-    for (int j = 0; j < it.nsplit; ++j)
-      M = fmaxf(M, a.part_ml[2 * ((size_t)(it.part0 + j) * ATTN_PART_ROWS + rl)]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float L = 0.f;
-    float acc[PER];
+  const int r = it.row0 + rl;
+  if (rl >= a.rows_per_block || r >= sg.q_len * G) return;
+  const int ns = it.nsplit;
+  float mj = -INFINITY, lj = 0.f;
+  if (lane < ns) {
+    const size_t prow = (size_t)(it.part0 + lane) * ATTN_PART_ROWS + rl;
+    mj = a.part_ml[2 * prow];
+    lj = a.part_ml[2 * prow + 1];
+  }
+  const float M = wave_max(mj);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  const float wj = lane < ns ? __builtin_amdgcn_exp2f(mj - Mu) : 0.f;
+  const float L = wave_sum(wj * lj);
+  float acc[PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    for (int j = 0; j < it.nsplit; ++j) {
-      const size_t prow = (size_t)(it.part0 + j) * ATTN_PART_ROWS + rl;
-      const float wj = __builtin_amdgcn_exp2f(a.part_ml[2 * prow] - Mu);
-      L += wj * a.part_ml[2 * prow + 1];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const int c = lane + 64 * e;
-        if (c < DV) acc[e] += wj * a.part_o[prow * DV + c];
-      }
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const int tok = r / G, hq = it.kvh * G + (r - tok * G);
-    uint16_t* op = a.out + ((size_t)(sg.q_begin + tok) * a.n_q_heads + hq) * DV;
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+#pragma unroll 4
+  for (int j = 0; j < ns; ++j) {
+    const float wb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j));
+    const float* po = a.part_o + ((size_t)(it.part0 + j) * ATTN_PART_ROWS + rl) * DV;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int c = lane + 64 * e;
-      if (c < DV) {
-        const __bf16 b = (__bf16)(acc[e] * inv);
-        op[c] = __builtin_bit_cast(uint16_t, b);
-      }
+      if (c < DV) acc[e] += wb * po[c];
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int tok = r / G, hq = it.kvh * G + (r - tok * G);
+  uint16_t* op = a.out + ((size_t)(sg.q_begin + tok) * a.n_q_heads + hq) * DV;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int c = lane + 64 * e;
+    if (c < DV) {
+      const __bf16 bv = (__bf16)(acc[e] * inv);
+      op[c] = __builtin_bit_cast(uint16_t, bv);
     }
   }
 }
@@ -1103,10 +1122,12 @@ hipError_t launch_seg_attn(hipStream_t st, const AttnArgs& a, int d_nope, int d_
 hipError_t launch_combine(hipStream_t st, const AttnArgs& a, const CombItem* items, int n_items,
                           int d_v) {
   if (n_items <= 0) return hipSuccess;
+  const int bpi = (a.rows_per_block + 3) / 4;
+  const dim3 grid((unsigned)(n_items * bpi));
   switch (d_v) {
-    case 128: hipLaunchKernelGGL((k_combine<128>), dim3(n_items), dim3(256), 0, st, a, items); break;
-    case 64: hipLaunchKernelGGL((k_combine<64>), dim3(n_items), dim3(256), 0, st, a, items); break;
-    case 32: hipLaunchKernelGGL((k_combine<32>), dim3(n_items), dim3(256), 0, st, a, items); break;
+    case 128: hipLaunchKernelGGL((k_combine<128>), grid, dim3(256), 0, st, a, items, bpi); break;
+    case 64: hipLaunchKernelGGL((k_combine<64>), grid, dim3(256), 0, st, a, items, bpi); break;
+    case 32: hipLaunchKernelGGL((k_combine<32>), grid, dim3(256), 0, st, a, items, bpi); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

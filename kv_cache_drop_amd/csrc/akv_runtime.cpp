@@ -685,6 +685,7 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
     if (segs[i].q_len > 0) base += (int64_t)L.n_kv_heads * ((segs[i].q_len * (int64_t)G + RB - 1) / RB);
   int target = 1;
   // split the key range only when the row tiles alone cannot fill the CUs
+  // (at most 16 splits: the combine kernel holds one split per lane of a wave)
   if (base > 0 && base < p->n_cu) target = (int)std::min<int64_t>(16, (2LL * p->n_cu + base - 1) / base);
 
   struct Group {
