@@ -624,18 +624,22 @@ void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<int64_t>&
   std::unordered_map<int64_t, int32_t> didx;
   items.clear();
   deltas.clear();
+  int64_t last_delta = 0;   // deltas are constant along runs: skip the lookup there
+  int32_t di = -1;
   for (int32_t t = 0; t < (int32_t)tot.size(); ++t) {
     if (tot[t] == 0) continue;
     const int32_t slot = q.slot[t];
     const int32_t pg = slot / S, off = slot - pg * S;
-    auto f = didx.find(tot[t]);
-    int32_t di;
-    if (f == didx.end()) {
-      di = (int32_t)deltas.size();
-      deltas.push_back((int32_t)tot[t]);
-      didx.emplace(tot[t], di);
-    } else {
-      di = f->second;
+    if (di < 0 || tot[t] != last_delta) {
+      auto f = didx.find(tot[t]);
+      if (f == didx.end()) {
+        di = (int32_t)deltas.size();
+        deltas.push_back((int32_t)tot[t]);
+        didx.emplace(tot[t], di);
+      } else {
+        di = f->second;
+      }
+      last_delta = tot[t];
     }
     if (!items.empty() && items.back().page == pg && items.back().hi == off &&
         items.back().didx == di && items.back().hi - items.back().lo < max_rows)
