@@ -36,10 +36,10 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # WRITE_SIZE = 1,048,576 KiB, so fetched KiB are scaled by 2.0 and written KiB
 # by 1.0.  When the kernel source differs, traffic is reported as null.
 COUNTERS = {
-    "kernel_source_sha1": "1da3e80b7fc9ee068418dfbeefde00fcbfadda42",
+    "kernel_source_sha1": "c6ba1cd9f3ac68913f75cd64e5373038c905a93c",
     "fetch_scale": 1048576 / 524302, "write_scale": 1.0,
-    "attention": {"fetch_kib": 111093, "write_kib": 16384},
-    "rotate": {"fetch_kib": 39189, "write_kib": 77622},
+    "attention": {"fetch_kib": 110863, "write_kib": 16384},
+    "rotate": {"fetch_kib": 39263, "write_kib": 77629},
 }
 
 
