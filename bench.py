@@ -119,6 +119,51 @@ def cpu_baseline(wl, rows_per_seg: int):
                 est_step_s=round(t_step, 2))
 
 
+def repos_layers_extra(args, L, hist, drop, repos, hk, hv, rep_bytes) -> dict:
+    """Extra line (not the headline config): the C2 repos over a model's
+    layers in one launch (akv_repos_layers), one pool per layer with the same
+    history and drop; alternating +delta / -delta keeps every rep on the same
+    data, and 32 layers of rotated keys (5 GB) do not fit any cache."""
+    import torch
+    import kv_cache_drop_amd as akv
+    nl = args.repos_layers
+    rng = np.random.default_rng(args.seed + 2)
+    order = rng.permutation(L.num_pages).astype(np.int32)
+    log(f"[bench] building {nl} layer pools for the batched repos line")
+    pools = []
+    for _ in range(nl):
+        p = akv.Pool(L.n_q_heads, L.n_kv_heads, 0, L.d_rope, L.d_v, L.page_size, L.num_pages,
+                     rope_theta=L.rope_theta, page_order=order, scratch_bytes=16 << 20)
+        s = p.seq_create()
+        p.append(s, hist.pos, hk, None, hv)
+        p.drop(s, drop.spans)
+        pools.append(p)
+    torch.cuda.synchronize()
+    neg = -np.asarray(repos.deltas, np.int32)
+    for r in range(2):
+        akv.repos_layers(pools, 0, repos.spans, repos.deltas if r % 2 == 0 else neg)
+    torch.cuda.synchronize()
+    pools[0].timing_enable(True)
+    pools[0].timing_read("rotate")
+    reps = 10
+    for r in range(reps):
+        akv.repos_layers(pools, 0, repos.spans, repos.deltas if r % 2 == 0 else neg)
+    torch.cuda.synchronize()
+    ms, n = pools[0].timing_read("rotate")
+    pools[0].timing_enable(False)
+    for p in pools:
+        p.close()
+    del pools
+    torch.cuda.empty_cache()
+    avg = ms / max(n, 1)
+    nbytes = rep_bytes * nl
+    gbps = nbytes / (avg * 1e-3) / 1e9
+    return {"extra": True, "what": f"C2 repos over {nl} layers in one launch (akv_repos_layers)",
+            "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4), "kernel": "k_rotate", "layers": nl,
+            "bytes_per_launch": nbytes, "avg_launch_ms": round(avg, 5), "launches": n}
+
+
 def run_config(args) -> dict:
     """One JSON record for a workload other than the headline: replay its op
     script on a fresh device pool per rep (set-up appends untimed), flush L2 and
@@ -247,6 +292,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=16, help="oracle query rows per segment")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--repos-layers", type=int, default=32,
+                    help="layers of the extra batched-repos line (0: skip it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -338,6 +385,10 @@ def main():
     rot_gbps = rep_bytes / (rot_ms * 1e-3) / 1e9
     value = flops / (ms_step * 1e-3) / 1e12
 
+    layers_rec = None
+    if args.repos_layers > 0:
+        layers_rec = repos_layers_extra(args, L, hist, drop, repos, hk, hv, rep_bytes)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host (bounded sample)")
@@ -373,6 +424,7 @@ def main():
                            "traffic": counted_traffic("rotate"),
                            "kernel": "k_rotate", "bytes_per_launch": rep_bytes,
                            "avg_launch_ms": round(rot_ms, 5)},
+        "roofline_repos_layers": layers_rec,
         "kernels_ms_per_step": {k: round(v[0] / max(args.steps, 1), 5) for k, v in kt.items()},
         "attention_pairs": int(pairs),
         "query_tokens_per_s": round(att.q.shape[0] / (ms_step * 1e-3), 1),

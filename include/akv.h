@@ -156,6 +156,20 @@ akv_status akv_compact(akv_pool* pool, int32_t seq, int32_t force);
 akv_status akv_repos(akv_pool* pool, int32_t seq, const akv_span* spans, const int32_t* delta,
                      int32_t n_spans);
 
+/* repos over the layers of a model in one launch (the same operation as
+ * akv_repos, applied to every pool in pools[0..n_pools)).  A model keeps one
+ * pool per layer with the same op history, so the layers' page tables and
+ * positions agree and one plan serves them all; the rotation of every
+ * layer's keys is a single kernel launch (grid rows = layers).  Requirements,
+ * checked before anything changes: the pools are distinct, share pool 0's
+ * layout, frequency table and HIP stream, and sequence seq has the same
+ * slots, positions and dropped flags in each.  Metadata is committed in every
+ * pool on success.  Device work goes on the shared stream; the pointer table
+ * lives in pool 0's scratch.  Errors: AKV_EINVAL (mismatch, NULL), AKV_ERANGE
+ * (as akv_repos), AKV_ENOMEM (pool 0's scratch). */
+akv_status akv_repos_layers(akv_pool* const* pools, int32_t n_pools, int32_t seq, const akv_span* spans,
+                            const int32_t* delta, int32_t n_spans);
+
 /* splice ([Leyline] Method, AMORTIZE mode): spans are given in coordinates of
  * the current visible list (entry i is the i-th visible token in position
  * order), sorted and disjoint, each non-empty.  Splice j drops its span,

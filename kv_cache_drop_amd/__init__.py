@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-__all__ = ["AkvError", "Pool", "lib", "LIB_PATH", "SYMBOLS", "KERNEL_KINDS", "attention_supported"]
+__all__ = ["AkvError", "Pool", "lib", "LIB_PATH", "SYMBOLS", "KERNEL_KINDS", "attention_supported",
+           "repos_layers"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libakv.so")
 
@@ -55,6 +56,7 @@ SYMBOLS = {
     "akv_drop": [_P, _I, _IP, _I],
     "akv_compact": [_P, _I, _I],
     "akv_repos": [_P, _I, _IP, _IP, _I],
+    "akv_repos_layers": [ctypes.POINTER(_P), _I, _I, _IP, _IP, _I],
     "akv_splice": [_P, _I, _IP, _IP, _I, _P, _P, _P, _IP],
     "akv_seq_visible": [_P, _I, _IP, _I, _IP, _I, _IP],
     "akv_segment_attention": [_P, _P, _I, _IP, _I, _IP, _I, ctypes.c_float, _P],
@@ -309,3 +311,13 @@ class Pool:
 
     def sync(self) -> None:
         _check(lib().akv_sync(self._h))
+
+
+def repos_layers(pools, seq: int, spans, deltas) -> None:
+    """akv_repos_layers: the same repos on every pool (one pool per model
+    layer, same op history and stream), rotated in one kernel launch."""
+    pools = list(pools)
+    hs = (_P * len(pools))(*[p._h.value for p in pools])
+    sp = _i32(spans).reshape(-1, 2)
+    dl = _i32(deltas).reshape(-1)
+    _check(lib().akv_repos_layers(hs, len(pools), seq, _ptr(sp), _ptr(dl), len(sp)))

@@ -56,9 +56,10 @@ int attn_rows_per_block(int d_nope);
 hipError_t launch_rot_table(hipStream_t st, int d_rope, const int32_t* deltas, int n_deltas,
                             const double* inv_freq, float* table);
 
-// Rotates the items in place with the table's rows (RotItem::didx).
-hipError_t launch_rotate(hipStream_t st, uint16_t* kr, int n_heads, int page_size, int d_rope,
-                         int pairing, const RotItem* items, int n_items, const float* table);
+// Rotates the items in place with the table's rows (RotItem::didx), in each
+// of the n_layers page arrays listed in krs (a device array of pointers).
+hipError_t launch_rotate(hipStream_t st, uint16_t* const* krs, int n_layers, int n_heads, int page_size,
+                         int d_rope, int pairing, const RotItem* items, int n_items, const float* table);
 
 hipError_t launch_scatter_rows(hipStream_t st, const uint16_t* src, uint16_t* dst,
                                const int32_t* slots, int n, int n_heads, int page_size,

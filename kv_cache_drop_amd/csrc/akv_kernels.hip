@@ -47,7 +47,9 @@ __device__ __forceinline__ unsigned pack_bf2(float a, float b) {
 // k_rot_table: one block per distinct delta forms the d_rope/2 angles
 // delta * theta_i in fp64, reduces them mod 2*pi and stores cos and sin as
 // fp32 (table[di][0..half) = cos, table[di][half..d) = sin).
-// k_rotate: one block per work item (page, rows lo..hi-1, delta); the block
+// k_rotate: one block per (work item, layer) — items are (page, rows lo..hi-1,
+// delta), the grid's second dimension picks one of n_layers page arrays that
+// share the page table; the block
 // stages its delta's row of the table in LDS and every head and row of the
 // item reuses it.  A "unit" is 8 rotation pairs held in two 16-byte loads;
 // pair (x, y) becomes (x cos - y sin, x sin + y cos) in fp32 and is rounded
@@ -75,12 +77,13 @@ __global__ __launch_bounds__(64) void k_rot_table(int d, const int32_t* __restri
   table[(size_t)blockIdx.x * d + half + i] = (float)sv;
 }
 
-__global__ __launch_bounds__(ROT_THREADS, 8) void k_rotate(uint16_t* __restrict__ kr, int n_heads, int S,
-                                                         int d, int pairing,
-                                                         const RotItem* __restrict__ items,
-                                                         const float* __restrict__ table) {
+__global__ __launch_bounds__(ROT_THREADS, 8) void k_rotate(uint16_t* const* __restrict__ krs, int n_heads,
+                                                            int S, int d, int pairing,
+                                                            const RotItem* __restrict__ items,
+                                                            const float* __restrict__ table) {
   __shared__ float s_c[128], s_s[128];
   const RotItem it = items[blockIdx.x];
+  uint16_t* __restrict__ kr = krs[blockIdx.y];   // one layer's rotated-key pages per grid row
   const int half = d >> 1;
   const int upr = d >> 4;
   const int rows = it.hi - it.lo;
@@ -166,10 +169,10 @@ hipError_t launch_rot_table(hipStream_t st, int d_rope, const int32_t* deltas, i
   return hipGetLastError();
 }
 
-hipError_t launch_rotate(hipStream_t st, uint16_t* kr, int n_heads, int page_size, int d_rope,
-                         int pairing, const RotItem* items, int n_items, const float* table) {
-  if (n_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rotate, dim3(n_items), dim3(ROT_THREADS), 0, st, kr, n_heads, page_size,
+hipError_t launch_rotate(hipStream_t st, uint16_t* const* krs, int n_layers, int n_heads, int page_size,
+                         int d_rope, int pairing, const RotItem* items, int n_items, const float* table) {
+  if (n_items <= 0 || n_layers <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rotate, dim3(n_items, n_layers), dim3(ROT_THREADS), 0, st, krs, n_heads, page_size,
                      d_rope, pairing, items, table);
   return hipGetLastError();
 }

@@ -425,6 +425,13 @@ akv_status upload_array(akv_pool* p, ScratchCursor& sc, const void* src, size_t 
 
 // Per-call scratch bytes left after the persistent tables (a conservative
 // bound checked before any state changes, so a short buffer leaves no trace).
+// Scratch bytes of one rotation: items, deltas, the cos/sin table, the layer
+// pointer table, and the alignment of each upload.
+size_t rotate_scratch_bytes(const akv_pool* p, size_t n_items, size_t n_deltas, size_t n_layers) {
+  return n_items * sizeof(akv::RotItem) + n_deltas * 4 + n_deltas * (size_t)p->L.d_rope * 4 +
+         n_layers * sizeof(void*) + 4 * 256;
+}
+
 akv_status scratch_fits(const akv_pool* p, size_t bytes) {
   if (!p->device) return AKV_OK;
   const size_t need = p->scratch_base + bytes + 4096;
@@ -467,14 +474,20 @@ akv_status device_append(akv_pool* p, const std::vector<int32_t>& slots, const v
   return check_launch(e, "append kernel launch");
 }
 
-// rotate the listed (slot, delta) runs; items are built here
+// rotate the listed (slot, delta) runs in the rotated-key arrays of `layers`
+// (pools sharing p's page table; p itself when empty) with one launch
 akv_status device_rotate(akv_pool* p, const std::vector<akv::RotItem>& items,
-                         const std::vector<int32_t>& deltas) {
+                         const std::vector<int32_t>& deltas,
+                         const std::vector<akv_pool*>& layers = {}) {
   if (!p->device || items.empty()) return AKV_OK;
+  std::vector<uint16_t*> krs;
+  if (layers.empty()) krs.push_back(p->rope_array());
+  for (akv_pool* l : layers) krs.push_back(l->rope_array());
   ScratchCursor sc(p);
-  void *ditems, *ddeltas;
+  void *ditems, *ddeltas, *dkrs;
   akv_status st = upload_array(p, sc, items.data(), items.size() * sizeof(akv::RotItem), &ditems);
   if (st == AKV_OK) st = upload_array(p, sc, deltas.data(), deltas.size() * 4, &ddeltas);
+  if (st == AKV_OK) st = upload_array(p, sc, krs.data(), krs.size() * sizeof(uint16_t*), &dkrs);
   if (st != AKV_OK) return st;
   float* dtab = (float*)sc.take(deltas.size() * (size_t)p->L.d_rope * 4);
   if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
@@ -482,8 +495,8 @@ akv_status device_rotate(akv_pool* p, const std::vector<akv::RotItem>& items,
                                        (int)deltas.size(), (const double*)p->scratch, dtab);
   if (e != hipSuccess) return check_launch(e, "rotation table kernel launch");
   KTimer tm(p, AKV_K_ROTATE);
-  e = akv::launch_rotate(p->stream, p->rope_array(), p->rope_heads(), p->L.page_size, p->L.d_rope,
-                         p->L.pairing, (const akv::RotItem*)ditems, (int)items.size(), dtab);
+  e = akv::launch_rotate(p->stream, (uint16_t* const*)dkrs, (int)krs.size(), p->rope_heads(), p->L.page_size,
+                         p->L.d_rope, p->L.pairing, (const akv::RotItem*)ditems, (int)items.size(), dtab);
   tm.done();
   return check_launch(e, "rotate kernel launch");
 }
@@ -982,11 +995,59 @@ akv_status akv_repos(akv_pool* p, int32_t s, const akv_span* spans, const int32_
     std::vector<akv::RotItem> items;
     std::vector<int32_t> deltas;
     repos_items(p, *q, tot, items, deltas);
-    st = scratch_fits(p, items.size() * sizeof(akv::RotItem) + deltas.size() * 4 + 512);
+    st = scratch_fits(p, rotate_scratch_bytes(p, items.size(), deltas.size(), 1));
     if (st != AKV_OK) return st;
     st = device_rotate(p, items, deltas);
     if (st != AKV_OK) return st;
     repos_commit(*q, tot);
+    return AKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_repos_layers(akv_pool* const* pools, int32_t n_pools, int32_t s, const akv_span* spans,
+                            const int32_t* delta, int32_t n) {
+  try {
+    if (!pools || n_pools <= 0) return fail(AKV_EINVAL, "no pools");
+    akv_pool* p = pools[0];
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    SeqRec* q;
+    akv_status st = get_seq(p, s, &q);
+    if (st != AKV_OK) return st;
+    std::vector<SeqRec*> qs{q};
+    std::vector<akv_pool*> layers{p};
+    for (int32_t i = 1; i < n_pools; ++i) {
+      akv_pool* o = pools[i];
+      if (!o) return fail(AKV_EINVAL, "pool %d is NULL", i);
+      for (int32_t k = 0; k < i; ++k)
+        if (pools[k] == o) return fail(AKV_EINVAL, "pool %d is listed twice", i);
+      const akv_layout &A = p->L, &B = o->L;
+      if (A.n_kv_heads != B.n_kv_heads || A.d_nope != B.d_nope || A.d_rope != B.d_rope ||
+          A.page_size != B.page_size || A.num_pages != B.num_pages || A.kpe_per_head != B.kpe_per_head ||
+          A.pairing != B.pairing || p->inv_freq != o->inv_freq)
+        return fail(AKV_EINVAL, "pool %d has another layout or frequency table", i);
+      if (o->device != p->device || o->stream != p->stream)
+        return fail(AKV_EINVAL, "pool %d runs on another stream", i);
+      SeqRec* oq;
+      st = get_seq(o, s, &oq);
+      if (st != AKV_OK) return st;
+      if (oq->slot != q->slot || oq->pos != q->pos || oq->dropped != q->dropped)
+        return fail(AKV_EINVAL, "pool %d: sequence %d differs from pool 0's", i, s);
+      qs.push_back(oq);
+      layers.push_back(o);
+    }
+    std::vector<int64_t> tot;
+    st = repos_totals(p, *q, spans, delta, n, tot);
+    if (st != AKV_OK) return st;
+    std::vector<akv::RotItem> items;
+    std::vector<int32_t> deltas;
+    repos_items(p, *q, tot, items, deltas);
+    st = scratch_fits(p, rotate_scratch_bytes(p, items.size(), deltas.size(), n_pools));
+    if (st != AKV_OK) return st;
+    st = device_rotate(p, items, deltas, layers);
+    if (st != AKV_OK) return st;
+    for (SeqRec* r : qs) repos_commit(*r, tot);
     return AKV_OK;
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");

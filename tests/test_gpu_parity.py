@@ -306,3 +306,50 @@ def test_c2_64k_sampled():
 
 def test_c4_batched_sampled():
     _sampled_parity(W.c4_batched(0), n_rows=6)
+
+
+def test_repos_layers_one_launch():
+    """akv_repos_layers on three layers holding different keys: every layer's
+    pages equal a per-layer akv_repos bit for bit, and the oracle's rotation
+    within the key tolerance; one rotate launch for all layers."""
+    _say("[gpu] repos over 3 layers in one launch")
+    rng = np.random.default_rng(23)
+    n, H, d, S = 3000, 4, 128, 16
+    npages = n // S + 4
+    order = rng.permutation(npages).astype(np.int32)
+    lay = W.Layout(16, H, 0, d, d, S, npages, rope_theta=5e5)
+    spans = np.array([[0, 700], [500, 2100], [2500, 2990]], np.int32)
+    deltas = np.array([-300, 1250, 77], np.int32)
+    layers, singles, keys = [], [], []
+    for li in range(3):
+        k = W.to_bf16(rng.standard_normal((n, H, d), dtype=np.float32))
+        keys.append(k)
+        for group in (layers, singles):
+            p = akv.Pool(16, H, 0, d, d, S, npages, rope_theta=5e5, page_order=order)
+            s = p.seq_create()
+            p.append(s, np.arange(n) + 4000, D.dev_bf16(k), None, D.dev_bf16(k))
+            p.drop(s, [[1000, 1200]])
+            group.append(p)
+    layers[0].timing_enable(True)
+    layers[0].timing_read("rotate")
+    akv.repos_layers(layers, 0, spans, deltas)
+    _, launches = layers[0].timing_read("rotate")
+    assert launches == 1
+    for p in singles:
+        p.repos(0, spans, deltas)
+    torch.cuda.synchronize()
+    for li, (pl, ps) in enumerate(zip(layers, singles)):
+        for a, b in zip(pl.tokens(0), ps.tokens(0)):
+            np.testing.assert_array_equal(a, b)
+        slot = torch.from_numpy(pl.tokens(0)[0].astype(np.int64)).to("cuda:0")
+        got = pl.k_pages[slot // S, :, slot % S, :]      # every appended token's row
+        want = ps.k_pages[slot // S, :, slot % S, :]
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"layer {li}"
+        op = AO.Pool(lay, order)
+        op.seq_create()
+        op.append(0, np.arange(n) + 4000, W.bf16_to_f64(keys[li]), None, W.bf16_to_f64(keys[li]))
+        op.drop(0, [[1000, 1200]])
+        op.repos(0, spans, deltas)
+        _check_visible_kv(pl, op, lay)
+    for p in layers + singles:
+        p.close()

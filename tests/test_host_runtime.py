@@ -260,3 +260,47 @@ def test_error_codes_match_oracle_fuzz():
                 code_h = ex.status
             assert code_o == code_h, (trial, kind, b, e, d)
             _compare(hp, op, f"trial {trial}")
+
+
+def test_repos_layers_host():
+    """akv_repos_layers on page-table-only pools: positions as one repos per
+    pool (and as the oracle's), and a refused call leaves every pool as it was."""
+    rng = np.random.default_rng(21)
+    lay = W.Layout(8, 2, 0, 64, 64, 16, 96, rope_theta=1e4)
+    order = rng.permutation(96).astype(np.int32)
+    layers = [_host_pool(lay, order) for _ in range(3)]
+    ref = _host_pool(lay, order)
+    op = AO.Pool(lay, order)
+    n = 1200
+    spans = np.array([[100, 300], [250, 900], [1000, 1100]], np.int32)
+    deltas = np.array([-50, 700, -3], np.int32)
+    for p in layers + [ref]:
+        s = p.seq_create()
+        p.append(s, np.arange(n) + 10)
+        p.drop(s, [[300, 400]])
+    op.seq_create()
+    op.append(0, np.arange(n) + 10, np.zeros((n, 2, 64)), None, np.zeros((n, 2, 64)))
+    op.drop(0, [[300, 400]])
+    akv.repos_layers(layers, 0, spans, deltas)
+    ref.repos(0, spans, deltas)
+    op.repos(0, spans, deltas)
+    for p in layers:
+        _compare(p, op, "repos_layers")
+        for a, b in zip(p.tokens(0), ref.tokens(0)):
+            np.testing.assert_array_equal(a, b)
+    # refused: a pool whose history differs, the same pool twice, another layout
+    before = [p.tokens(0) for p in layers]
+    odd = _host_pool(lay, order)
+    s = odd.seq_create()
+    odd.append(s, np.arange(n) + 10)
+    for bad in ([layers[0], odd], [layers[0], layers[0]],
+                [layers[0], _host_pool(W.Layout(8, 2, 0, 32, 32, 16, 96), order)]):
+        with pytest.raises(akv.AkvError) as e:
+            akv.repos_layers(bad, 0, spans, deltas)
+        assert e.value.status == -1
+    with pytest.raises(akv.AkvError) as e:
+        akv.repos_layers(layers, 0, [[0, n + 1]], [1])
+    assert e.value.status == -2
+    for p, b in zip(layers, before):
+        for x, y in zip(p.tokens(0), b):
+            np.testing.assert_array_equal(x, y)
