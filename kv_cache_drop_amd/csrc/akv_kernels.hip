@@ -890,8 +890,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
   slot_load(0, 4);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // A wave whose rows all lie past the segment's last row (a short segment's
+  // padding) computes nothing: it keeps its share of the tile loads and every
+  // barrier, and leaves its SIMD's matrix core to the other wave there.
+  const bool idle = it.row0 + 32 * QB * w >= rows_total;
   f32x16 sa[QB][2], sb[QB][2];
-  qk(stage_ptr(0), sa);
+  if (!idle) qk(stage_ptr(0), sa);
 
   // All of iteration j - 2's loads have landed once at most one iteration's
   // worth (NIW rows + 1 slot load) is outstanding.  The barrier carries no
@@ -944,21 +948,37 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
     sm_exp(s_cur, m_use, pf);
     pv(stage_ptr(C), pf);
   };
+  auto idle_iter = [&](int j, auto c) __attribute__((always_inline)) {
+    constexpr int C = decltype(c)::value;
+    sync();
+    issue_tile(stage_ptr((C + 3) & 3), (C + 3) & 3);
+    slot_load((C + 1) & 3, j + 5);
+  };
   int j = 0;
-  if (jm > 4) {
-    sm_max(sa, mx);
-    for (; j + 4 < jm; j += 4) {
-      main_iter(j, I0{}, sa, sb);
-      main_iter(j + 1, I1{}, sb, sa);
-      main_iter(j + 2, I2{}, sa, sb);
-      main_iter(j + 3, I3{}, sb, sa);
+  if (idle) {
+    // same number of iterations (and barriers) as the two loops below
+    for (; j < n_tiles; j += 4) {
+      idle_iter(j, I0{});
+      idle_iter(j + 1, I1{});
+      idle_iter(j + 2, I2{});
+      idle_iter(j + 3, I3{});
     }
-  }
-  for (; j < n_tiles; j += 4) {
-    tail_iter(j, I0{}, sa, sb);
-    tail_iter(j + 1, I1{}, sb, sa);
-    tail_iter(j + 2, I2{}, sa, sb);
-    tail_iter(j + 3, I3{}, sb, sa);
+  } else {
+    if (jm > 4) {
+      sm_max(sa, mx);
+      for (; j + 4 < jm; j += 4) {
+        main_iter(j, I0{}, sa, sb);
+        main_iter(j + 1, I1{}, sb, sa);
+        main_iter(j + 2, I2{}, sa, sb);
+        main_iter(j + 3, I3{}, sb, sa);
+      }
+    }
+    for (; j < n_tiles; j += 4) {
+      tail_iter(j, I0{}, sa, sb);
+      tail_iter(j + 1, I1{}, sb, sa);
+      tail_iter(j + 2, I2{}, sa, sb);
+      tail_iter(j + 3, I3{}, sb, sa);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
 
