@@ -708,6 +708,7 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
   struct Group {
     int64_t cost;
     std::vector<akv::AttnItem> items;
+    std::vector<int64_t> item_cost;
   };
   std::vector<Group> groups;
   plan.comb.clear();
@@ -736,7 +737,8 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
           int32_t pidx = -1;
           if (ns > 1) pidx = part + (int32_t)(m * ns + sp);
           gr.items.push_back({i, h, row0, kb, ke, pidx});
-          gr.cost += keys + 64;  // + fixed cost of a block
+          gr.item_cost.push_back(keys + 64);  // + fixed cost of a block
+          gr.cost += keys + 64;
         }
         groups.push_back(std::move(gr));
       }
@@ -748,18 +750,25 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
     }
   }
   plan.n_parts = part;
-  // longest groups first, each to the least loaded XCD; inside a group, its
-  // row tiles stay together so they share K/V in that XCD's L2
+  // Longest groups first, each to the least loaded XCD, so row tiles reading
+  // the same K/V share that XCD's L2; then each XCD's items are dispatched
+  // longest first, so the CUs of an XCD finish together.
   std::stable_sort(groups.begin(), groups.end(),
                    [](const Group& a, const Group& b) { return a.cost > b.cost; });
-  std::vector<std::vector<akv::AttnItem>> bins(kXcds);
+  std::vector<std::vector<std::pair<int64_t, akv::AttnItem>>> xbins(kXcds);
   std::vector<int64_t> load(kXcds, 0);
   for (auto& gr : groups) {
     int best = 0;
     for (int x = 1; x < kXcds; ++x)
       if (load[x] < load[best]) best = x;
     load[best] += gr.cost;
-    for (auto& it : gr.items) bins[best].push_back(it);
+    for (size_t k = 0; k < gr.items.size(); ++k) xbins[best].push_back({gr.item_cost[k], gr.items[k]});
+  }
+  std::vector<std::vector<akv::AttnItem>> bins(kXcds);
+  for (int x = 0; x < kXcds; ++x) {
+    std::stable_sort(xbins[x].begin(), xbins[x].end(),
+                     [](const auto& a, const auto& b) { return a.first > b.first; });
+    for (auto& ci : xbins[x]) bins[x].push_back(ci.second);
   }
   size_t depth = 0;
   for (auto& b : bins) depth = std::max(depth, b.size());
