@@ -36,10 +36,11 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # WRITE_SIZE = 1,048,576 KiB, so fetched KiB are scaled by 2.0 and written KiB
 # by 1.0.  When the kernel source differs, traffic is reported as null.
 COUNTERS = {
-    "kernel_source_sha1": "c6ba1cd9f3ac68913f75cd64e5373038c905a93c",
+    "kernel_source_sha1": "2a77ebb759dd3fb46334419f953c51ab2989453f",
     "fetch_scale": 1048576 / 524302, "write_scale": 1.0,
-    "attention": {"fetch_kib": 110863, "write_kib": 16384},
-    "rotate": {"fetch_kib": 39263, "write_kib": 77629},
+    "attention": {"fetch_kib": 111086, "write_kib": 16384},
+    "rotate": {"fetch_kib": 39271, "write_kib": 77629},
+    "rotate_32_layers": {"fetch_kib": 1248270, "write_kib": 2484290},
 }
 
 
@@ -160,7 +161,8 @@ def repos_layers_extra(args, L, hist, drop, repos, hk, hv, rep_bytes) -> dict:
     gbps = nbytes / (avg * 1e-3) / 1e9
     return {"extra": True, "what": f"C2 repos over {nl} layers in one launch (akv_repos_layers)",
             "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(gbps / PEAK_HBM_GBPS, 4), "kernel": "k_rotate", "layers": nl,
+            "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "traffic": counted_traffic("rotate_32_layers") if nl == 32 else None, "kernel": "k_rotate", "layers": nl,
             "bytes_per_launch": nbytes, "avg_launch_ms": round(avg, 5), "launches": n}
 
 
@@ -173,7 +175,8 @@ def run_config(args) -> dict:
     import device_script as D
     import workloads as W
 
-    gens = {"c1": lambda s: W.c1_tiny(s, "canonical"), "c3": W.c3_mla, "c4": W.c4_batched, "c5": W.c5_128k}
+    gens = {"c1": lambda s: W.c1_tiny(s, "canonical"), "c3": W.c3_mla, "c4": W.c4_batched, "c5": W.c5_128k,
+            "decode": W.decode_batch}
     wl = gens[args.config](args.seed)
     L = wl.layout
     ops = list(wl.ops)
@@ -260,6 +263,13 @@ def run_config(args) -> dict:
                      "avg_launch_ms": round(attn_ms, 5)},
         "kernels_ms_per_step": {k: round(v[0] / max(args.steps, 1), 5) for k, v in tot.items()},
     }
+    if args.config == "decode":
+        # one query row per kv-head group: the launch streams the visible K/V once
+        hbm_gbps = kv_bytes / (attn_ms * 1e-3) / 1e9
+        rec["roofline"] = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                           "frac": round(hbm_gbps / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": kern,
+                           "kv_bytes_per_launch": kv_bytes, "flop_per_launch": flops,
+                           "avg_launch_ms": round(attn_ms, 5)}
     if rot_ms is not None:
         rot_gbps = rep_bytes / (rot_ms * rot_per_step * 1e-3) / 1e9
         rec["roofline_repos"] = {"bound": "hbm", "achieved": round(rot_gbps, 1), "peak": PEAK_HBM_GBPS,
@@ -279,12 +289,14 @@ CONFIG_NAMES = {
           "page 16), about 40 segments in one launch",
     "c5": "128K-token agent trace, 64 q / 8 kv heads, head_dim 128, page 16: drop 60 spans, repos 60 runs, "
           "4096 queries in 8 segments",
+    "decode": "48 requests of 2K-16K tokens on the 64K layer shape (32 q / 8 kv heads, head_dim 128, page 16): "
+              "drop and repos per request, then one new token each, 48 one-query segments in one launch",
 }
 
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"],
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "decode"],
                     help="c2 (default) is the headline 64K step; the others print one record each")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)

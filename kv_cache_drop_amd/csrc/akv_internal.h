@@ -32,18 +32,19 @@ struct AttnSeg {
 
 // One attention work item: a tile of attn_rows_per_block(d_nope) packed rows (token, q head in
 // group) of one segment and kv head, over list entries k_begin..k_end-1.
-// part >= 0: write an unnormalised fp32 partial (split-KV) at that index.
+// part >= 0: write an unnormalised fp32 partial (split-KV): the tile's row r
+// goes to partial row part + r.
 // seg < 0: padding block, exits at once.
 struct AttnItem {
   int32_t seg, kvh, row0, k_begin, k_end, part;
 };
 
-// Split-KV merge of nsplit consecutive partials part0.. for one row tile.
+// Split-KV merge for one row tile of `rows` rows: split j's partial of tile
+// row r sits at partial row part0 + j * rows + r.
 struct CombItem {
-  int32_t seg, kvh, row0, part0, nsplit, pad;
+  int32_t seg, kvh, row0, part0, nsplit, rows;
 };
 
-constexpr int ATTN_PART_ROWS = 256;  // row stride of one split-KV partial (>= rows per block)
 constexpr int ATTN_KTILE = 64;       // keys per pipeline stage
 
 // Packed rows per attention block of the kernel variant launched for a layout
@@ -85,8 +86,8 @@ struct AttnArgs {
   const int32_t* slots;
   float scale_log2e;             // softmax scale * log2(e)
   uint16_t* out;
-  float* part_o;                 // [n_parts][ATTN_PART_ROWS][d_v]
-  float* part_ml;                // [n_parts][ATTN_PART_ROWS][2]
+  float* part_o;                 // [partial rows][d_v]
+  float* part_ml;                // [partial rows][2]: (running max, sum)
   int rows_per_block;
 };
 

@@ -582,7 +582,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_seg_attn(AttnArgs a) {
         *(u32x2*)(op + 32 * cb + 8 * m + 4 * g) = v2;
       }
   } else {
-    const int prow = it.part * ATTN_PART_ROWS + 32 * w + l32;
+    const int prow = it.part + 32 * w + l32;
     float* po = a.part_o + (size_t)prow * DV;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
@@ -998,7 +998,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
           *(u32x2*)(op + 32 * cb + 8 * m + 4 * g) = v2;
         }
     } else {
-      const int prow = it.part * ATTN_PART_ROWS + 32 * (QB * w + qb) + l32;
+      const int prow = it.part + 32 * (QB * w + qb) + l32;
       float* po = a.part_o + (size_t)prow * DV;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
@@ -1046,7 +1046,7 @@ __global__ __launch_bounds__(256) void k_combine(AttnArgs a, const CombItem* __r
   const int ns = it.nsplit;
   float mj = -INFINITY, lj = 0.f;
   if (lane < ns) {
-    const size_t prow = (size_t)(it.part0 + lane) * ATTN_PART_ROWS + rl;
+    const size_t prow = (size_t)it.part0 + (size_t)lane * it.rows + rl;
     mj = a.part_ml[2 * prow];
     lj = a.part_ml[2 * prow + 1];
   }
@@ -1057,14 +1057,25 @@ __global__ __launch_bounds__(256) void k_combine(AttnArgs a, const CombItem* __r
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-#pragma unroll 4
-  for (int j = 0; j < ns; ++j) {
-    const float wb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j));
-    const float* po = a.part_o + ((size_t)(it.part0 + j) * ATTN_PART_ROWS + rl) * DV;
+  // eight splits per round, their loads issued together (splits past ns
+  // re-read the last one with weight 0)
+  for (int j0 = 0; j0 < ns; j0 += 8) {
+    float x[8][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int c = lane + 64 * e;
-      if (c < DV) acc[e] += wb * po[c];
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + u, ns - 1);
+      const float* po = a.part_o + ((size_t)it.part0 + (size_t)j * it.rows + rl) * DV;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int c = lane + 64 * e;
+        x[u][e] = c < DV ? po[c] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wb = j0 + u < ns ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j0 + u)) : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += wb * x[u][e];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;

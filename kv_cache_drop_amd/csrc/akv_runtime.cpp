@@ -681,7 +681,7 @@ struct AttnPlan {
   std::vector<akv::CombItem> comb;
   std::vector<int32_t> ext_off;
   int64_t total_list = 0;
-  int32_t n_parts = 0;
+  int64_t part_rows = 0;  // rows of split-KV partials
 };
 
 constexpr int kXcds = 8;
@@ -704,6 +704,21 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
   // split the key range only when the row tiles alone cannot fill the CUs
   // (at most 16 splits: the combine kernel holds one split per lane of a wave)
   if (base > 0 && base < p->n_cu) target = (int)std::min<int64_t>(16, (2LL * p->n_cu + base - 1) / base);
+  // ... or when one row tile alone would hold a CU well past the even share
+  // of the launch (few query rows over long lists: decode): such a segment's
+  // key range is cut into blocks of at most half a CU's share.
+  int64_t total_cost = 0;
+  for (int32_t i = 0; i < n_segs; ++i) {
+    const int32_t lq = segs[i].q_len;
+    if (lq <= 0) continue;
+    const int64_t rows = (int64_t)lq * G;
+    for (int64_t row0 = 0; row0 < rows; row0 += RB) {
+      const int64_t last_row = std::min<int64_t>(row0 + RB, rows) - 1;
+      total_cost += (int64_t)L.n_kv_heads * (std::min<int64_t>(lkv[i], lkv[i] - lq + last_row / G + 1) + 64);
+    }
+  }
+  const int64_t cu_share = total_cost / p->n_cu;
+  const int64_t block_cap = std::max<int64_t>(2048, cu_share / 2);
 
   struct Group {
     int64_t cost;
@@ -712,7 +727,7 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
   };
   std::vector<Group> groups;
   plan.comb.clear();
-  int32_t part = 0;
+  int64_t part = 0;
   for (int32_t i = 0; i < n_segs; ++i) {
     const int32_t lq = segs[i].q_len;
     if (lq <= 0) continue;
@@ -720,9 +735,19 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
     const int64_t ntile_rows = (rows + RB - 1) / RB;
     const int64_t key_tiles = (lkv[i] + KT - 1) / KT;
     int ns = target;
+    if (4 * (lkv[i] + 64) > 5 * cu_share)
+      ns = (int)std::max<int64_t>(ns, std::min<int64_t>(16, (lkv[i] + 64 + block_cap - 1) / block_cap));
     ns = (int)std::min<int64_t>(ns, std::max<int64_t>(1, lkv[i] / 512));
     ns = (int)std::min<int64_t>(ns, key_tiles);
     if (ns < 1) ns = 1;
+    // partials of one kv head: row tile m's ns splits, each of the tile's rows
+    std::vector<int64_t> tile_base(ntile_rows, 0);
+    int64_t head_part_rows = 0;
+    if (ns > 1)
+      for (int64_t m = 0; m < ntile_rows; ++m) {
+        tile_base[m] = head_part_rows;
+        head_part_rows += ns * std::min<int64_t>(RB, rows - m * RB);
+      }
     for (int32_t h = 0; h < L.n_kv_heads; ++h) {
       for (int sp = 0; sp < ns; ++sp) {
         const int64_t tb = key_tiles * sp / ns, te = key_tiles * (sp + 1) / ns;
@@ -735,7 +760,7 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
           const int64_t lim_last = lkv[i] - lq + last_row / G;
           const int64_t keys = std::max<int64_t>(0, std::min<int64_t>(ke, lim_last + 1) - kb);
           int32_t pidx = -1;
-          if (ns > 1) pidx = part + (int32_t)(m * ns + sp);
+          if (ns > 1) pidx = (int32_t)(part + tile_base[m] + sp * std::min<int64_t>(RB, rows - row0));
           gr.items.push_back({i, h, row0, kb, ke, pidx});
           gr.item_cost.push_back(keys + 64);  // + fixed cost of a block
           gr.cost += keys + 64;
@@ -744,12 +769,13 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
       }
       if (ns > 1) {
         for (int64_t m = 0; m < ntile_rows; ++m)
-          plan.comb.push_back({i, h, (int32_t)(m * RB), part + (int32_t)(m * ns), ns, 0});
-        part += (int32_t)(ntile_rows * ns);
+          plan.comb.push_back({i, h, (int32_t)(m * RB), (int32_t)(part + tile_base[m]), ns,
+                               (int32_t)std::min<int64_t>(RB, rows - m * RB)});
+        part += head_part_rows;
       }
     }
   }
-  plan.n_parts = part;
+  plan.part_rows = part;
   // Longest groups first, each to the least loaded XCD, so row tiles reading
   // the same K/V share that XCD's L2; then each XCD's items are dispatched
   // longest first, so the CUs of an XCD finish together.
@@ -1282,6 +1308,7 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
 
     AttnPlan plan;
     plan_attention(p, segs, n_segs, lkv, list_off, plan);
+    if (plan.part_rows > kInt32Max) return fail(AKV_ERANGE, "too many split-KV partial rows");
     // extent offsets for the slot expansion (over all segments' ranges, in order)
     std::vector<akv::Extent> ex_used;
     std::vector<int32_t> ex_off;
@@ -1307,9 +1334,9 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
     int32_t* dslots = (int32_t*)sc.take((size_t)std::max<int64_t>(total, 1) * 4);
     float* part_o = nullptr;
     float* part_ml = nullptr;
-    if (plan.n_parts > 0) {
-      part_o = (float*)sc.take((size_t)plan.n_parts * akv::ATTN_PART_ROWS * L.d_v * 4);
-      part_ml = (float*)sc.take((size_t)plan.n_parts * akv::ATTN_PART_ROWS * 2 * 4);
+    if (plan.part_rows > 0) {
+      part_o = (float*)sc.take((size_t)plan.part_rows * L.d_v * 4);
+      part_ml = (float*)sc.take((size_t)plan.part_rows * 2 * 4);
     }
     if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
 

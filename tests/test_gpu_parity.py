@@ -308,6 +308,13 @@ def test_c4_batched_sampled():
     _sampled_parity(W.c4_batched(0), n_rows=6)
 
 
+@pytest.mark.parametrize("seed,n_req,lo,hi", [(0, 16, 1024, 4096), (1, 48, 256, 3072)])
+def test_decode_batch_full(seed, n_req, lo, hi):
+    """One new token per request after drop and repos, all requests in one
+    launch: every output row and every visible key against the oracle."""
+    _full_parity(W.decode_batch(seed, n_req=n_req, ctx_lo=lo, ctx_hi=hi))
+
+
 def test_repos_layers_one_launch():
     """akv_repos_layers on three layers holding different keys: every layer's
     pages equal a per-layer akv_repos bit for bit, and the oracle's rotation

@@ -37,7 +37,7 @@ import numpy as np
 __all__ = [
     "Layout", "SeqCreate", "Append", "Drop", "Repos", "Splice", "Compact",
     "Segment", "Attention", "Workload", "to_bf16", "bf16_to_f64",
-    "c1_tiny", "c2_64k", "c3_mla", "c4_batched", "c5_128k", "fuzz_small",
+    "c1_tiny", "c2_64k", "c3_mla", "c4_batched", "c5_128k", "decode_batch", "fuzz_small",
     "CONFIGS", "make",
 ]
 
@@ -424,6 +424,62 @@ def c4_batched(seed: int = 0, n_req: int = 16, ctx_lo: int = 8192, ctx_hi: int =
 
 
 # --------------------------------------------------------------------------
+# decode: one new token per request at high batch (the inter-token side)
+# --------------------------------------------------------------------------
+def decode_batch(seed: int = 0, n_req: int = 48, ctx_lo: int = 2048, ctx_hi: int = 16384) -> Workload:
+    """n_req agent histories in one pool, each built with the batched recipe
+    (512-token reasoning turns, log-uniform tool spans, 10-60% of the older
+    tools dropped, survivors repositioned); then every request appends one
+    token at the next position and runs one single-query segment over its
+    whole visible list, all in one attention launch."""
+    rng = _rng(seed)
+    reqs = []
+    for r in range(n_req):
+        ctx = int(rng.integers(ctx_lo, ctx_hi + 1))
+        tools, cur = [], 0
+        while cur < ctx:
+            cur = min(cur + 512, ctx)
+            if cur >= ctx:
+                break
+            t = int(_loguniform(rng, 256, 8192, 1)[0])
+            tools.append((cur, min(cur + t, ctx)))
+            cur = min(cur + t, ctx)
+        f = float(rng.uniform(0.10, 0.60))
+        cand = list(range(max(0, len(tools) - 2)))
+        rng.shuffle(cand)
+        gone, chosen = 0, []
+        for i in cand:
+            if gone >= f * ctx:
+                break
+            chosen.append(i)
+            gone += tools[i][1] - tools[i][0]
+        dropped = [tools[i] for i in sorted(chosen)]
+        reqs.append(dict(ctx=ctx, dropped=dropped))
+    pages = sum((q["ctx"] + 1 + 15) // 16 for q in reqs) + 16
+    lay = Layout(32, 8, 0, 128, 128, 16, pages, rope_theta=500000.0)
+    wl = Workload("decode_batch", lay, rng.permutation(pages).astype(np.int32))
+    for r in range(n_req):
+        wl.ops.append(SeqCreate())
+    for r, q in enumerate(reqs):
+        wl.ops.append(_append_op(rng, lay, r, np.arange(q["ctx"], dtype=np.int32)))
+    for r, q in enumerate(reqs):
+        if q["dropped"]:
+            wl.ops.append(Drop(r, _spans(q["dropped"])))
+            rs, rd = _survivor_runs(q["ctx"], q["dropped"])
+            if len(rs):
+                wl.ops.append(Repos(r, rs, rd))
+    segs = []
+    for r, q in enumerate(reqs):
+        h = q["ctx"] - sum(e - b for b, e in q["dropped"])
+        wl.ops.append(_append_op(rng, lay, r, np.array([h], dtype=np.int32)))
+        segs.append(Segment(r, r, 1, np.zeros((0, 2), np.int32)))
+    qarr = _normal_bf16(rng, (n_req, lay.n_q_heads, lay.d_qk), scale=1.0 / 8.0)
+    wl.ops.append(Attention(qarr, segs))
+    wl.notes.update(requests=reqs)
+    return wl
+
+
+# --------------------------------------------------------------------------
 # config 5: Llama-3.1-70B-shaped layer on one GPU, 128K tokens
 # --------------------------------------------------------------------------
 def c5_128k(seed: int = 0) -> Workload:
@@ -536,7 +592,7 @@ def fuzz_small(seed: int, mla: bool = False, pairing: int = 0, n_seqs: int = 2,
 
 
 CONFIGS = {
-    "c1": c1_tiny, "c2": c2_64k, "c3": c3_mla, "c4": c4_batched, "c5": c5_128k,
+    "c1": c1_tiny, "c2": c2_64k, "c3": c3_mla, "c4": c4_batched, "c5": c5_128k, "decode": decode_batch,
 }
 
 
