@@ -176,7 +176,7 @@ def run_config(args) -> dict:
     import workloads as W
 
     gens = {"c1": lambda s: W.c1_tiny(s, "canonical"), "c3": W.c3_mla, "c4": W.c4_batched, "c5": W.c5_128k,
-            "decode": W.decode_batch}
+            "decode": W.decode_batch, "retrigger": W.retrigger}
     wl = gens[args.config](args.seed)
     L = wl.layout
     ops = list(wl.ops)
@@ -192,8 +192,8 @@ def run_config(args) -> dict:
             dev[i] = (q, torch.empty((q.shape[0], L.n_q_heads, L.d_v), dtype=torch.bfloat16, device="cuda:0"))
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     rope_heads = L.n_kv_heads if (not L.mla or L.kpe_per_head) else 1
-    tot = {k: [0.0, 0] for k in ("attention", "rotate", "append", "compact", "expand", "combine")}
-    walls, flops, pairs, kv_bytes, n_rot, n_q = [], 0.0, 0, 0, 0, 0
+    tot = {k: [0.0, 0] for k in ("attention", "rotate", "append", "compact", "expand", "combine", "clone")}
+    walls, flops, pairs, kv_bytes, n_rot, n_q, clone_bytes = [], 0.0, 0, 0, 0, 0, 0
     kern = None
     for rep in range(args.warmup + args.steps):
         pool = D.make_pool(wl)
@@ -239,6 +239,12 @@ def run_config(args) -> dict:
                 exa = np.asarray(ex).reshape(-1, 3)
                 kv_bytes += int((exa[:, 2] - exa[:, 1]).sum()) * L.n_kv_heads * (L.d_nope + L.d_rope + L.d_v) * 2
                 n_q += int(op.q.shape[0])
+            # a clone reads and writes every row of each retained source token
+            row_bytes = 2 * (rope_heads * L.d_rope + L.n_kv_heads * (L.d_nope + L.d_v))
+            for op in ops[i0:]:
+                if isinstance(op, W.Clone):
+                    dr = pool.tokens(op.src)[2][op.first:op.first + op.n]
+                    clone_bytes += 2 * row_bytes * int((dr == 0).sum())
             kern = attention_kernel_name(L)
         pool.close()
         del pool, keep
@@ -270,6 +276,14 @@ def run_config(args) -> dict:
                            "frac": round(hbm_gbps / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": kern,
                            "kv_bytes_per_launch": kv_bytes, "flop_per_launch": flops,
                            "avg_launch_ms": round(attn_ms, 5)}
+    if tot["clone"][1]:
+        cl_ms = tot["clone"][0] / tot["clone"][1]
+        cl_per_step = tot["clone"][1] / max(args.steps, 1)
+        cl_gbps = clone_bytes / (cl_ms * cl_per_step * 1e-3) / 1e9
+        rec["roofline_clone"] = {"bound": "hbm", "achieved": round(cl_gbps, 1), "peak": PEAK_HBM_GBPS,
+                                 "unit": "GB/s", "frac": round(cl_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                                 "kernel": "k_clone_rows", "bytes_per_step": clone_bytes,
+                                 "launches_per_step": cl_per_step, "avg_launch_ms": round(cl_ms, 5)}
     if rot_ms is not None:
         rot_gbps = rep_bytes / (rot_ms * rot_per_step * 1e-3) / 1e9
         rec["roofline_repos"] = {"bound": "hbm", "achieved": round(rot_gbps, 1), "peak": PEAK_HBM_GBPS,
@@ -289,6 +303,10 @@ CONFIG_NAMES = {
           "page 16), about 40 segments in one launch",
     "c5": "128K-token agent trace, 64 q / 8 kv heads, head_dim 128, page 16: drop 60 spans, repos 60 runs, "
           "4096 queries in 8 segments",
+    "retrigger": "64K agent trace re-used at another offset (32 q / 8 kv heads, head_dim 128, page 16): request A "
+                 "(512-token preamble, the 64K trace, older tools dropped, survivors repositioned) and request B "
+                 "(the same trace after a preamble of another length) cloned from A's state with keys turned by "
+                 "the offset change; 512 queries each in one launch",
     "decode": "48 requests of 2K-16K tokens on the 64K layer shape (32 q / 8 kv heads, head_dim 128, page 16): "
               "drop and repos per request, then one new token each, 48 one-query segments in one launch",
 }
@@ -296,7 +314,7 @@ CONFIG_NAMES = {
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "decode"],
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "decode", "retrigger"],
                     help="c2 (default) is the headline 64K step; the others print one record each")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)

@@ -184,6 +184,24 @@ akv_status akv_splice(akv_pool* pool, int32_t seq, const akv_span* spans, const 
                       int32_t n_splices, const void* stub_K, const void* stub_Kpe,
                       const void* stub_V, int32_t* stub_pos_out);
 
+/* positional version ([AKV-notes] section 3, Cache Management: re-use by key
+ * rotation, and the retrigger match of the cache reuse matching rules): the
+ * retained tokens of src with logical index in [first, first+n), in logical
+ * order, are appended to dst at positions pos + delta.  Their keys are copied
+ * with the rotated part turned by R(delta) (GQA: all of K; MLA: K_pe, with
+ * K_nope copied as is) and their V rows are copied; the source rows are not
+ * touched, so src keeps its own version.  The new tokens take dst's next
+ * logical indices and slots exactly as akv_append would place them (src ==
+ * dst is allowed: the copies are read from the state before the call).
+ * Rotation arithmetic as akv_repos; delta 0 is a bit-exact copy.  Dropped
+ * tokens are skipped; when no token qualifies nothing changes.  All rows move
+ * in one kernel launch (after the cos/sin table launch).  Errors, checked before
+ * anything changes: AKV_EINVAL (bad sequence, n < 0), AKV_ERANGE ([first,
+ * first+n) outside src, a new position outside [0, 2^31), dst too long),
+ * AKV_ENOMEM (pages or scratch), AKV_ESTATE (released sequence). */
+akv_status akv_seq_clone(akv_pool* pool, int32_t src, int32_t first, int32_t n, int32_t dst,
+                         int32_t delta);
+
 /* ---- visibility -------------------------------------------------------------- */
 
 /* Page-table image of the sequence's visible list: retained tokens minus the
@@ -237,7 +255,7 @@ akv_status akv_repos_plan(akv_pool* pool, int32_t seq, const akv_span* spans, co
  * stream, returns the summed milliseconds and launch count of one kernel kind
  * since the last read of that kind, and clears them. */
 enum { AKV_K_APPEND = 0, AKV_K_ROTATE = 1, AKV_K_COMPACT = 2, AKV_K_EXPAND = 3,
-       AKV_K_ATTN = 4, AKV_K_COMBINE = 5, AKV_K_KINDS = 6 };
+       AKV_K_ATTN = 4, AKV_K_COMBINE = 5, AKV_K_CLONE = 6, AKV_K_KINDS = 7 };
 akv_status akv_timing_enable(akv_pool* pool, int32_t enable);
 akv_status akv_timing_read(akv_pool* pool, int32_t kind, double* total_ms, int32_t* count);
 

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libakv.so")
 AKV_OK, AKV_EINVAL, AKV_ERANGE, AKV_ENOMEM, AKV_ESTATE, AKV_EHIP = 0, -1, -2, -3, -4, -5
 STATUS_NAMES = {0: "AKV_OK", -1: "AKV_EINVAL", -2: "AKV_ERANGE", -3: "AKV_ENOMEM",
                 -4: "AKV_ESTATE", -5: "AKV_EHIP"}
-KERNEL_KINDS = {"append": 0, "rotate": 1, "compact": 2, "expand": 3, "attention": 4, "combine": 5}
+KERNEL_KINDS = {"append": 0, "rotate": 1, "compact": 2, "expand": 3, "attention": 4, "combine": 5,
+                "clone": 6}
 
 
 class AkvError(RuntimeError):
@@ -58,6 +59,7 @@ SYMBOLS = {
     "akv_repos": [_P, _I, _IP, _IP, _I],
     "akv_repos_layers": [ctypes.POINTER(_P), _I, _I, _IP, _IP, _I],
     "akv_splice": [_P, _I, _IP, _IP, _I, _P, _P, _P, _IP],
+    "akv_seq_clone": [_P, _I, _I, _I, _I, _I],
     "akv_seq_visible": [_P, _I, _IP, _I, _IP, _I, _IP],
     "akv_segment_attention": [_P, _P, _I, _IP, _I, _IP, _I, ctypes.c_float, _P],
     "akv_seq_tokens": [_P, _I, _I, _I, _IP, _IP, ctypes.POINTER(ctypes.c_uint8)],
@@ -218,6 +220,11 @@ class Pool:
         sp = _i32(spans).reshape(-1, 2)
         dl = _i32(deltas).reshape(-1)
         _check(lib().akv_repos(self._h, seq, _ptr(sp), _ptr(dl), len(sp)))
+
+    def clone(self, src: int, first: int, n: int, dst: int, delta: int) -> None:
+        """Positional version: append src's retained tokens [first, first+n)
+        to dst at pos + delta, keys turned by R(delta) (akv_seq_clone)."""
+        _check(lib().akv_seq_clone(self._h, src, first, n, dst, delta))
 
     def repos_plan(self, seq: int, spans, deltas):
         sp = _i32(spans).reshape(-1, 2)

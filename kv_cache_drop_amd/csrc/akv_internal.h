@@ -69,6 +69,16 @@ hipError_t launch_scatter_rows(hipStream_t st, const uint16_t* src, uint16_t* ds
 hipError_t launch_move_rows(hipStream_t st, uint16_t* base, const MovePair* pairs, int n,
                             int n_heads, int page_size, int log2_page, int row_elems);
 
+// Out-of-place repos (akv_version.hip): every row of each pair's token moves
+// from src slot to dst slot; the rotated-key rows (kr, rope_heads heads) are
+// turned by the single delta whose cos / sin row is `table` (d_rope floats:
+// cos of the d_rope/2 pairs, then sin; nullptr = plain copy), the V rows and
+// the MLA K_nope rows (kn, nullptr when d_nope == 0) are copied.  Source and
+// destination slots are disjoint.
+hipError_t launch_clone_rows(hipStream_t st, uint16_t* kr, uint16_t* v, uint16_t* kn, const MovePair* pairs,
+                             int n, int rope_heads, int n_heads, int page_size, int log2_page, int d_rope,
+                             int d_v, int d_nope, int pairing, const float* table);
+
 hipError_t launch_expand(hipStream_t st, const Extent* ex, const int32_t* ex_off, int n_ext,
                          int page_size, int32_t* slots);
 

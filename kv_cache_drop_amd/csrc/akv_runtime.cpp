@@ -985,6 +985,66 @@ akv_status akv_append(akv_pool* p, int32_t s, const void* K, const void* K_pe, c
   }
 }
 
+akv_status akv_seq_clone(akv_pool* p, int32_t src, int32_t first, int32_t n, int32_t dst,
+                         int32_t delta) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    SeqRec* qs;
+    SeqRec* qd;
+    akv_status st = get_seq(p, src, &qs);
+    if (st == AKV_OK) st = get_seq(p, dst, &qd);
+    if (st != AKV_OK) return st;
+    if (n < 0) return fail(AKV_EINVAL, "negative token count");
+    if (first < 0 || (int64_t)first + n > (int64_t)qs->slot.size())
+      return fail(AKV_ERANGE, "tokens [%d,%lld) outside sequence %d of %zu tokens", first,
+                  (long long)first + n, src, qs->slot.size());
+    std::vector<int32_t> pos;
+    std::vector<akv::MovePair> mv;
+    for (int32_t t = first; t < first + n; ++t) {
+      if (qs->dropped[t]) continue;
+      const int64_t np = (int64_t)qs->pos[t] + delta;
+      if (np < 0 || np > kInt32Max)
+        return fail(AKV_ERANGE, "token %d would move to position %lld", t, (long long)np);
+      pos.push_back((int32_t)np);
+      mv.push_back({qs->slot[t], -1});
+    }
+    const int32_t m = (int32_t)pos.size();
+    if (m == 0) return AKV_OK;
+    if ((int64_t)qd->slot.size() + m > kInt32Max) return fail(AKV_ERANGE, "sequence too long");
+    if (pages_needed(p, *qd, m) > available(p))
+      return fail(AKV_ENOMEM, "pool exhausted: %lld pages needed, %lld available",
+                  (long long)pages_needed(p, *qd, m), (long long)available(p));
+    st = scratch_fits(p, (size_t)m * sizeof(akv::MovePair) + 4 + (size_t)p->L.d_rope * 4 + 3 * 256);
+    if (st != AKV_OK) return st;
+    std::vector<int32_t> slots(m);
+    place_tokens(p, dst, m, pos.data(), slots.data());
+    for (int32_t i = 0; i < m; ++i) mv[i].dst = slots[i];
+    if (!p->device) return AKV_OK;
+    ScratchCursor sc(p);
+    void *dmv, *ddelta;
+    st = upload_array(p, sc, mv.data(), mv.size() * sizeof(akv::MovePair), &dmv);
+    if (st == AKV_OK) st = upload_array(p, sc, &delta, 4, &ddelta);
+    if (st != AKV_OK) return st;
+    float* dtab = (float*)sc.take((size_t)p->L.d_rope * 4);
+    if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
+    const akv_layout& L = p->L;
+    hipError_t e = hipSuccess;
+    if (delta != 0) {
+      e = akv::launch_rot_table(p->stream, L.d_rope, (const int32_t*)ddelta, 1, (const double*)p->scratch,
+                                dtab);
+      if (e != hipSuccess) return check_launch(e, "rotation table kernel launch");
+    }
+    KTimer tm(p, AKV_K_CLONE);
+    e = akv::launch_clone_rows(p->stream, p->rope_array(), p->v, L.d_nope > 0 ? p->k : nullptr,
+                               (const akv::MovePair*)dmv, m, p->rope_heads(), L.n_kv_heads, L.page_size,
+                               p->log2S, L.d_rope, L.d_v, L.d_nope, L.pairing, delta != 0 ? dtab : nullptr);
+    tm.done();
+    return check_launch(e, "clone kernel launch");
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
 akv_status akv_drop(akv_pool* p, int32_t s, const akv_span* spans, int32_t n) {
   try {
     if (!p) return fail(AKV_EINVAL, "NULL pool");

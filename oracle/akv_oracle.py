@@ -414,6 +414,36 @@ class Pool:
             self._rotate_tokens(q, t, tot[t])
             q.pos[t] += tot[t]
 
+    # -- positional version ([AKV-notes] section 3, Cache Management) ------------------
+    def clone(self, src: int, first: int, n: int, dst: int, delta: int) -> None:
+        """Re-use a cached state at other positions (re-use by key rotation; the
+        retrigger match of the cache reuse matching rules): the retained tokens
+        of src with logical index in [first, first+n) are appended to dst, in
+        logical order, at positions pos + delta, with their rotated key part
+        turned by R(delta) and every other row copied.  src is left as it is."""
+        qs = self._seq(src)
+        self._seq(dst)
+        if n < 0:
+            raise EInval("negative token count")
+        if first < 0 or first + n > qs.n:
+            raise ERange("clone range outside the source sequence")
+        t = np.arange(first, first + n, dtype=np.int64)
+        t = t[~qs.dropped[t]]
+        if len(t) == 0:
+            return
+        newpos = qs.pos[t] + int(delta)
+        if np.any(newpos < 0) or np.any(newpos > INT32_MAX):
+            raise ERange("cloned position out of range")
+        S = self.S
+        pg, off = qs.slot[t] // S, qs.slot[t] % S
+        kr = self.kr[pg, :, off, :]
+        kr = rotate(kr, np.full(kr.shape[:2], float(delta)), self.inv_freq, self.L.pairing)
+        v = self.v[pg, :, off, :].copy()
+        if self.L.mla:
+            self.append(dst, newpos, self.kn[pg, :, off, :].copy(), kr, v)
+        else:
+            self.append(dst, newpos, kr, None, v)
+
     # -- splice ([Leyline] Method, AMORTIZE mode) ---------------------------------------
     def splice_plan(self, s: int, spans, stub_lens):
         """Validate a batch of splices given in visible-list coordinates and

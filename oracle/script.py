@@ -41,6 +41,8 @@ def apply_op(pool: Pool, op) -> Optional[np.ndarray]:
         return pool.splice(op.seq, op.spans, op.stub_lens, _f64(op.k), _f64(op.kpe), _f64(op.v))
     elif isinstance(op, W.Compact):
         pool.compact(op.seq, bool(op.force))
+    elif isinstance(op, W.Clone):
+        pool.clone(op.src, op.first, op.n, op.dst, op.delta)
     else:
         raise TypeError(op)
     return None

@@ -60,6 +60,8 @@ def apply_op(pool: akv.Pool, op, keep=None):
         return pool.splice(op.seq, op.spans, op.stub_lens, k, kpe, v)
     elif isinstance(op, W.Compact):
         pool.compact(op.seq, bool(op.force))
+    elif isinstance(op, W.Clone):
+        pool.clone(op.src, op.first, op.n, op.dst, op.delta)
     else:
         raise TypeError(op)
     return None

@@ -184,6 +184,67 @@ def test_repos_roundtrip_and_many_spans():
 
 
 # ---------------------------------------------------------------------------
+# positional versions (clone with key rotation)
+# ---------------------------------------------------------------------------
+def _rows_i16(t, slots, S):
+    a = t.view(torch.int16).cpu().numpy()
+    return a[slots // S, :, slots % S, :]
+
+
+@pytest.mark.parametrize("pairing", [0, 1])
+@pytest.mark.parametrize("mla", [False, True])
+def test_clone_matches_in_place_rotate_bit_exact(pairing, mla):
+    """A clone by delta writes the same bf16 keys as an in-place repos by the
+    same delta of the same rows (same cos / sin table, same fp32 formula);
+    V and K_nope are copied bit for bit, the source rows stay untouched, and
+    delta 0 is a bit-exact copy."""
+    _say(f"[gpu] clone vs in-place rotate, mla={mla} pairing={pairing}")
+    rng = np.random.default_rng(40 + 2 * pairing + mla)
+    n, S = 777, 16
+    if mla:
+        Hq, H, dn, dr, dv = 8, 8, 32, 64, 32
+    else:
+        Hq, H, dn, dr, dv = 8, 4, 0, 64, 64
+    npages = 4 * ((n + S - 1) // S) + 4
+    pool = akv.Pool(Hq, H, dn, dr, dv, S, npages, pairing=pairing, rope_theta=1e4,
+                    page_order=rng.permutation(npages), scratch_bytes=16 << 20)
+    x, y, z, w = (pool.seq_create() for _ in range(4))
+    k = W.to_bf16(rng.standard_normal((n, H, dn if mla else dr), dtype=np.float32))
+    kpe = W.to_bf16(rng.standard_normal((n, 1, dr), dtype=np.float32)) if mla else None
+    v = W.to_bf16(rng.standard_normal((n, H, dv), dtype=np.float32))
+    pos = np.arange(n, dtype=np.int32) * 3 + 90000
+    kd, vd = D.dev_bf16(k), D.dev_bf16(v)
+    kped = D.dev_bf16(kpe) if mla else None
+    pool.append(x, pos, kd, kped, vd)
+    pool.append(z, pos, kd, kped, vd)
+    delta = -54321
+    pool.clone(x, 0, n, y, delta)
+    pool.repos(z, [[0, n]], [delta])
+    pool.clone(x, 0, n, w, 0)
+    torch.cuda.synchronize()
+    sl = {s: pool.tokens(s)[0] for s in (x, y, z, w)}
+    np.testing.assert_array_equal(pool.tokens(y)[1], pos + delta)
+    rope = pool.kpe_pages if mla else pool.k_pages
+    np.testing.assert_array_equal(_rows_i16(rope, sl[y], S), _rows_i16(rope, sl[z], S))
+    np.testing.assert_array_equal(_rows_i16(rope, sl[w], S), _rows_i16(rope, sl[x], S))
+    src_rope = (kpe if mla else k).view(np.int16)
+    np.testing.assert_array_equal(_rows_i16(rope, sl[x], S), src_rope)
+    assert not np.array_equal(_rows_i16(rope, sl[y], S), src_rope)
+    for s in (x, y, w):
+        np.testing.assert_array_equal(_rows_i16(pool.v_pages, sl[s], S), v.view(np.int16))
+        if mla:
+            np.testing.assert_array_equal(_rows_i16(pool.k_pages, sl[s], S), k.view(np.int16))
+    pool.close()
+
+
+@pytest.mark.parametrize("seed,mla,pre_b", [(0, False, None), (1, False, 0), (2, True, None)])
+def test_retrigger_full(seed, mla, pre_b):
+    """A cached state re-used at other positions: tables, every visible key of
+    both versions, and both segments' attention against the oracle."""
+    _full_parity(W.retrigger(seed, ctx=4096, pre_a=256, nq=128, n_turns=8, n_recent=2, pre_b=pre_b, mla=mla))
+
+
+# ---------------------------------------------------------------------------
 # append / compaction copies
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("mla", [False, True])
@@ -306,6 +367,10 @@ def test_c2_64k_sampled():
 
 def test_c4_batched_sampled():
     _sampled_parity(W.c4_batched(0), n_rows=6)
+
+
+def test_retrigger_64k_sampled():
+    _sampled_parity(W.retrigger(0), n_rows=12)
 
 
 @pytest.mark.parametrize("seed,n_req,lo,hi", [(0, 16, 1024, 4096), (1, 48, 256, 3072)])

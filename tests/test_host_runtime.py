@@ -97,6 +97,9 @@ def _replay(wl: W.Workload, check_every_op=True):
         elif isinstance(op, W.Compact):
             hp.compact(op.seq, bool(op.force))
             oracle.apply_op(op_pool, op)
+        elif isinstance(op, W.Clone):
+            hp.clone(op.src, op.first, op.n, op.dst, op.delta)
+            oracle.apply_op(op_pool, op)
         elif isinstance(op, W.Attention):
             ex, rows = oracle.segment_lists(op_pool, op.segments)
             got = [hp.visible(sg.seq, sg.mask_spans if len(sg.mask_spans) else None) for sg in op.segments]
@@ -202,6 +205,12 @@ def test_error_codes_and_atomicity():
         (lambda: hp.splice(s, [[2, 1]], [1]), akv.AKV_EINVAL),
         (lambda: hp.splice(s, [[2, 20]], [1]), akv.AKV_ERANGE),
         (lambda: hp.splice(s, [[4, 8], [6, 9]], [1, 1]), akv.AKV_EINVAL),
+        (lambda: hp.clone(s, 0, -1, s, 0), akv.AKV_EINVAL),
+        (lambda: hp.clone(s, 10, 5, s, 0), akv.AKV_ERANGE),
+        (lambda: hp.clone(s, 0, 14, s, -101), akv.AKV_ERANGE),
+        (lambda: hp.clone(s, 0, 14, s, 2 ** 31 - 110), akv.AKV_ERANGE),
+        (lambda: hp.clone(s, 0, 14, s, 5), akv.AKV_ENOMEM),
+        (lambda: hp.clone(s, 0, 1, 3, 0), akv.AKV_EINVAL),
         (lambda: hp.segment_attention(torch.zeros((1, 4, 16), dtype=torch.bfloat16), [[0, 1, 0, 1]],
                                       [[0, 0, 1]], out=torch.zeros((1, 4, 16), dtype=torch.bfloat16)),
          akv.AKV_ESTATE),
@@ -240,15 +249,18 @@ def test_error_codes_match_oracle_fuzz():
                 code_h = e.status
             assert code_o == code_h
         for _ in range(6):
-            kind = rng.integers(0, 3)
+            kind = rng.integers(0, 4)
             b = int(rng.integers(-2, 33)); e = int(rng.integers(-2, 33))
             d = int(rng.integers(-40, 40))
             if kind == 0:
                 fo, fh = (lambda: op.drop(0, [[b, e]])), (lambda: hp.drop(0, [[b, e]]))
             elif kind == 1:
                 fo, fh = (lambda: op.repos(0, [[b, e]], [d])), (lambda: hp.repos(0, [[b, e]], [d]))
-            else:
+            elif kind == 2:
                 fo, fh = (lambda: op.compact(0, True)), (lambda: hp.compact(0, True))
+            else:
+                fo = lambda: op.clone(0, b, e - b, 0, d)
+                fh = lambda: hp.clone(0, b, e - b, 0, d)
             code_o = code_h = 0
             try:
                 fo()
@@ -260,6 +272,48 @@ def test_error_codes_match_oracle_fuzz():
                 code_h = ex.status
             assert code_o == code_h, (trial, kind, b, e, d)
             _compare(hp, op, f"trial {trial}")
+
+
+@pytest.mark.parametrize("seed,mla,pre_b", [(0, False, None), (1, False, 0), (2, True, None), (3, True, 700)])
+def test_retrigger_clone_page_tables_bit_exact(seed, mla, pre_b):
+    """Positional versions: the clone's slots, positions and flags, and both
+    sequences' page-table images, equal the oracle's after every op."""
+    _replay(W.retrigger(seed, ctx=4096, pre_a=256, nq=64, n_turns=8, n_recent=2, pre_b=pre_b, mla=mla))
+
+
+def test_clone_skips_dropped_and_refusals_leave_no_trace():
+    lay = W.Layout(2, 1, 0, 16, 16, 4, 40)
+    order = np.random.default_rng(5).permutation(40)
+    op, hp = AO.Pool(lay, order), _host_pool(lay, order)
+    for p in (op, hp):
+        p.seq_create()
+        p.seq_create()
+    z = np.zeros((30, 1, 16))
+    op.append(0, np.arange(30) + 50, z, None, z)
+    hp.append(0, np.arange(30) + 50)
+    for p in (op, hp):
+        p.drop(0, [[3, 9], [20, 22]])
+    op.clone(0, 2, 25, 1, -40)
+    hp.clone(0, 2, 25, 1, -40)
+    _compare(hp, op, "clone")
+    assert hp.info(1)[0] == 25 - 6 - 2
+    # a clone of dropped tokens only changes nothing
+    before = _state(hp, 1)
+    hp.clone(0, 3, 6, 1, 7)
+    _same(_state(hp, 1), before)
+    # refused: no trace in either sequence or the queues
+    b0, b1 = _state(hp, 0), _state(hp, 1)
+    for args, code in [((0, 0, 30, 1, -61), akv.AKV_ERANGE), ((0, 0, 31, 1, 0), akv.AKV_ERANGE),
+                       ((0, -1, 3, 1, 0), akv.AKV_ERANGE)]:
+        with pytest.raises(akv.AkvError) as ei:
+            hp.clone(*args)
+        assert ei.value.status == code
+        _same(_state(hp, 0), b0)
+        _same(_state(hp, 1), b1)
+    hp.seq_release(1)
+    with pytest.raises(akv.AkvError) as ei:
+        hp.clone(0, 0, 1, 1, 0)
+    assert ei.value.status == akv.AKV_ESTATE
 
 
 def test_repos_layers_host():

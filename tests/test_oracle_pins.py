@@ -132,6 +132,102 @@ def test_repos_sequential_equals_summed_and_skips_dropped():
     assert np.all(p2.seqs[0].pos[10:30] == 100000 + np.arange(10, 30))
 
 
+# ---------------------------------------------------------------------------
+# positional versions ("Cache Engineering for Agents", section 3, Cache
+# Management: re-use by key rotation; the retrigger match rule)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("pairing", [0, 1])
+@pytest.mark.parametrize("base", [10000.0, 500000.0])
+def test_clone_equals_fresh_rope_at_shifted_position(pairing, base):
+    """Keys RoPE'd at m, cloned with delta, equal the raw keys RoPE'd at
+    m + delta (explicit 2x2 matrices); V is copied, dropped tokens are
+    skipped, and the source keeps its own version unchanged."""
+    rng = np.random.default_rng(11)
+    d, n = 32, 150
+    lay = _lay(d_rope=d, d_v=8, n_q_heads=4, n_kv_heads=2, pairing=pairing, rope_theta=base, num_pages=40)
+    raw = rng.standard_normal((n, 2, d))
+    m = np.arange(n, dtype=np.float64) * 11.0 + 900.0
+    v = rng.standard_normal((n, 2, 8))
+    pool = AO.Pool(lay)
+    a, b = pool.seq_create(), pool.seq_create()
+    pool.append(a, m.astype(np.int64), _rope_by_matrix(raw, m[:, None, None], base, pairing), None, v)
+    pool.drop(a, [[20, 35], [90, 91]], auto_compact=False)
+    kr0, v0 = pool.kr.copy(), pool.v.copy()
+    delta = -777
+    pool.clone(a, 10, 120, b, delta)
+    keep = np.array([t for t in range(10, 130) if not (20 <= t < 35 or t == 90)])
+    qb = pool.seqs[b]
+    np.testing.assert_array_equal(qb.pos, (m[keep] + delta).astype(np.int64))
+    S = lay.page_size
+    pg, off = qb.slot // S, qb.slot % S
+    want = _rope_by_matrix(raw[keep], (m[keep] + delta)[:, None, None], base, pairing)
+    np.testing.assert_allclose(pool.kr[pg, :, off, :], want, rtol=0, atol=1e-9)
+    np.testing.assert_array_equal(pool.v[pg, :, off, :], v[keep])
+    qa = pool.seqs[a]
+    pa, oa = qa.slot // S, qa.slot % S
+    np.testing.assert_array_equal(pool.kr[pa, :, oa, :], kr0[pa, :, oa, :])
+    np.testing.assert_array_equal(pool.v[pa, :, oa, :], v0[pa, :, oa, :])
+
+
+def test_clone_round_trip_zero_delta_and_mla_parts():
+    rng = np.random.default_rng(12)
+    lay = _lay(d_nope=16, d_rope=16, d_v=16, n_q_heads=4, n_kv_heads=4, page_size=8, num_pages=80)
+    pool = AO.Pool(lay)
+    a, b, c, z = (pool.seq_create() for _ in range(4))
+    k, kpe, v = _fill(pool, a, 100, rng, pos0=5000)
+    pool.clone(a, 0, 100, b, 4321)
+    pool.clone(b, 0, 100, c, -4321)                  # R(-d) R(d) = I
+    pool.clone(a, 0, 100, z, 0)                      # delta 0: a copy
+    S = lay.page_size
+    def rows(s):
+        q = pool.seqs[s]
+        return pool.kr[q.slot // S, :, q.slot % S, :], pool.kn[q.slot // S, :, q.slot % S, :], \
+            pool.v[q.slot // S, :, q.slot % S, :]
+    ra, rc, rz = rows(a), rows(c), rows(z)
+    np.testing.assert_allclose(rc[0], ra[0], rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(rz[0], ra[0])
+    for r in (rc, rz, rows(b)):
+        np.testing.assert_array_equal(r[1], kn := ra[1])       # K_nope carries no position
+        np.testing.assert_array_equal(r[2], ra[2])
+    assert kn.shape == (100, 4, 16)
+    # the shared K_pe head of b is turned: pair norms are kept, values are not
+    rb = rows(b)
+    assert rb[0].shape == (100, 1, 16)
+    nb = rb[0][..., 0::2] ** 2 + rb[0][..., 1::2] ** 2
+    na = ra[0][..., 0::2] ** 2 + ra[0][..., 1::2] ** 2
+    np.testing.assert_allclose(nb, na, rtol=1e-12)
+    assert np.abs(rb[0] - ra[0]).max() > 0.1
+    np.testing.assert_array_equal(pool.seqs[c].pos, pool.seqs[a].pos)
+
+
+def test_clone_places_like_append_and_refusals_are_atomic():
+    rng = np.random.default_rng(13)
+    lay = _lay(num_pages=21, page_size=4)
+    order = rng.permutation(21)
+    p1, p2 = AO.Pool(lay, order), AO.Pool(lay, order)
+    for p in (p1, p2):
+        p.seq_create(), p.seq_create()
+    r1, r2 = np.random.default_rng(3), np.random.default_rng(3)
+    _fill(p1, 0, 40, r1)
+    _fill(p2, 0, 40, r2)
+    _fill(p1, 1, 3, r1, pos0=7)
+    _fill(p2, 1, 3, r2, pos0=7)
+    for p in (p1, p2):
+        p.drop(0, [[0, 12]], auto_compact=False)      # pages 0..2 of seq 0 become evictable
+    p1.clone(0, 0, 40, 1, 100)
+    z = np.zeros((28, 2, 16))
+    p2.append(1, np.arange(12, 40) + 100, z, None, z)
+    np.testing.assert_array_equal(p1.seqs[1].slot, p2.seqs[1].slot)
+    assert list(p1.free) == list(p2.free) and list(p1.evictable) == list(p2.evictable)
+    snap = (p1.seqs[1].slot.copy(), list(p1.free), list(p1.evictable), p1.kr.copy())
+    for args, exc in [((0, 0, 41, 1, 0), AO.ERange), ((0, 0, 40, 1, -113), AO.ERange),
+                      ((0, 5, -1, 1, 0), AO.EInval), ((0, 0, 40, 1, 0), AO.ENoMem)]:
+        with pytest.raises(exc):
+            p1.clone(*args)
+        assert np.array_equal(p1.seqs[1].slot, snap[0]) and list(p1.free) == snap[1]
+        assert list(p1.evictable) == snap[2] and np.array_equal(p1.kr, snap[3])
+
+
 def test_repos_position_range_is_atomic():
     rng = np.random.default_rng(4)
     pool = AO.Pool(_lay())

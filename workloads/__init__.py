@@ -35,9 +35,9 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "Layout", "SeqCreate", "Append", "Drop", "Repos", "Splice", "Compact",
+    "Layout", "SeqCreate", "Append", "Drop", "Repos", "Splice", "Compact", "Clone",
     "Segment", "Attention", "Workload", "to_bf16", "bf16_to_f64",
-    "c1_tiny", "c2_64k", "c3_mla", "c4_batched", "c5_128k", "decode_batch", "fuzz_small",
+    "c1_tiny", "c2_64k", "c3_mla", "c4_batched", "c5_128k", "decode_batch", "retrigger", "fuzz_small",
     "CONFIGS", "make",
 ]
 
@@ -131,6 +131,15 @@ class Splice:
 class Compact:
     seq: int
     force: int = 1
+
+
+@dataclass
+class Clone:
+    src: int             # retained tokens [first, first+n) of src ...
+    first: int
+    n: int
+    dst: int             # ... appended to dst at pos + delta (positional version)
+    delta: int
 
 
 @dataclass
@@ -424,6 +433,54 @@ def c4_batched(seed: int = 0, n_req: int = 16, ctx_lo: int = 8192, ctx_hi: int =
 
 
 # --------------------------------------------------------------------------
+# retrigger: a cached state re-used at other positions (positional version)
+# --------------------------------------------------------------------------
+def retrigger(seed: int = 0, ctx: int = 65536, pre_a: int = 512, nq: int = 512, n_turns: int = 40,
+              n_recent: int = 8, pre_b: Optional[int] = None, mla: bool = False) -> Workload:
+    """Request A: a pre_a-token preamble, then a ctx-token agent trace (the
+    64K recipe: reasoning turns and log-uniform tool outputs, the older tools
+    holding 40% of the tokens, all dropped, the survivors repositioned).
+    Request B holds the same trace after a preamble of pre_b tokens (random in
+    [0, 2 pre_a] unless given): its cached state is A's, re-used at positions
+    shifted by pre_b - pre_a through one clone.  Both then append nq new
+    tokens and attend in one launch (one segment each)."""
+    rng = _rng(seed)
+    if pre_b is None:
+        pre_b = int(rng.integers(0, 2 * pre_a + 1))
+    if mla:
+        S = 64
+        lay = Layout(16, 16, 128, 64, 128, S, 1, kpe_per_head=0, rope_theta=10000.0)
+    else:
+        S = 16
+        lay = Layout(32, 8, 0, 128, 128, S, 1, rope_theta=500000.0)
+    reasoning = max(32, min(512, ctx // (2 * n_turns)))
+    tools = _c2_like_history(rng, n_turns, n_recent, ctx, 0.40, reasoning)
+    dropped = [(pre_a + b, pre_a + e) for b, e in tools[:n_turns - n_recent]]
+    n_a = pre_a + ctx
+    rep_s, rep_d = _survivor_runs(n_a, dropped)
+    kept = ctx - sum(e - b for b, e in dropped)
+    pages = (n_a + nq) // S + (pre_b + kept + nq) // S + 8
+    lay.num_pages = pages
+    wl = Workload("retrigger", lay, rng.permutation(pages).astype(np.int32))
+    wl.ops.append(SeqCreate())
+    wl.ops.append(SeqCreate())
+    wl.ops.append(_append_op(rng, lay, 0, np.arange(n_a, dtype=np.int32)))
+    wl.ops.append(_append_op(rng, lay, 1, np.arange(pre_b, dtype=np.int32)))
+    wl.ops.append(Drop(0, _spans(dropped)))
+    if len(rep_s):
+        wl.ops.append(Repos(0, rep_s, rep_d))
+    wl.ops.append(Clone(0, pre_a, ctx, 1, pre_b - pre_a))
+    h_a, h_b = pre_a + kept, pre_b + kept
+    wl.ops.append(_append_op(rng, lay, 0, np.arange(h_a, h_a + nq, dtype=np.int32)))
+    wl.ops.append(_append_op(rng, lay, 1, np.arange(h_b, h_b + nq, dtype=np.int32)))
+    q = _normal_bf16(rng, (2 * nq, lay.n_q_heads, lay.d_qk), scale=1.0 / 8.0)
+    none = np.zeros((0, 2), np.int32)
+    wl.ops.append(Attention(q, [Segment(0, 0, nq, none), Segment(1, nq, nq, none)]))
+    wl.notes.update(pre_a=pre_a, pre_b=pre_b, delta=pre_b - pre_a, kept=kept, dropped_spans=dropped)
+    return wl
+
+
+# --------------------------------------------------------------------------
 # decode: one new token per request at high batch (the inter-token side)
 # --------------------------------------------------------------------------
 def decode_batch(seed: int = 0, n_req: int = 48, ctx_lo: int = 2048, ctx_hi: int = 16384) -> Workload:
@@ -593,6 +650,7 @@ def fuzz_small(seed: int, mla: bool = False, pairing: int = 0, n_seqs: int = 2,
 
 CONFIGS = {
     "c1": c1_tiny, "c2": c2_64k, "c3": c3_mla, "c4": c4_batched, "c5": c5_128k, "decode": decode_batch,
+    "retrigger": retrigger,
 }
 
 
