@@ -120,6 +120,30 @@ def cpu_baseline(wl, rows_per_seg: int):
                 est_step_s=round(t_step, 2))
 
 
+def compact_extra(pool, seqs, L) -> dict:
+    """Extra line: forced compaction (k_move_rows) of C2 sequences after their
+    step, each the only work on its copy since that step (the earliest timed
+    copies first, so their pages are long out of every cache)."""
+    import torch
+    pool.timing_read("compact")
+    moved = 0
+    for s in seqs:
+        moved += pool.info(s)[1]
+        pool.compact(s, True)
+    torch.cuda.synchronize()
+    ms, n = pool.timing_read("compact")
+    avg = ms / max(n, 1)
+    per_tok = 2 * L.n_kv_heads * (L.d_nope + L.d_rope + L.d_v) * 2     # read + write of K and V
+    nbytes = per_tok * moved / max(len(seqs), 1)
+    gbps = nbytes / (avg * 1e-3) / 1e9
+    return {"extra": True, "what": "forced compaction of the 64K sequence after its step (visible history "
+                                   "+ new tokens into fresh pages)",
+            "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": "k_move_tokens",
+            "tokens_per_launch": moved / max(len(seqs), 1), "bytes_per_launch": nbytes,
+            "avg_launch_ms": round(avg, 5), "launches": n}
+
+
 def repos_layers_extra(args, L, hist, drop, repos, hk, hv, rep_bytes) -> dict:
     """Extra line (not the headline config): the C2 repos over a model's
     layers in one launch (akv_repos_layers), one pool per layer with the same
@@ -282,7 +306,7 @@ def run_config(args) -> dict:
         cl_gbps = clone_bytes / (cl_ms * cl_per_step * 1e-3) / 1e9
         rec["roofline_clone"] = {"bound": "hbm", "achieved": round(cl_gbps, 1), "peak": PEAK_HBM_GBPS,
                                  "unit": "GB/s", "frac": round(cl_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
-                                 "kernel": "k_clone_rows", "bytes_per_step": clone_bytes,
+                                 "kernel": "k_move_tokens", "bytes_per_step": clone_bytes,
                                  "launches_per_step": cl_per_step, "avg_launch_ms": round(cl_ms, 5)}
     if rot_ms is not None:
         rot_gbps = rep_bytes / (rot_ms * rot_per_step * 1e-3) / 1e9
@@ -401,7 +425,6 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kt = {k: pool.timing_read(k) for k in akv.KERNEL_KINDS}
-    pool.timing_enable(False)
 
     flops, pairs = attention_flops(L, segs, page_lists)
     ex_all = np.asarray(page_lists).reshape(-1, 3)
@@ -415,6 +438,8 @@ def main():
     rot_gbps = rep_bytes / (rot_ms * 1e-3) / 1e9
     value = flops / (ms_step * 1e-3) / 1e12
 
+    comp_rec = compact_extra(pool, seqs[args.warmup:args.warmup + min(10, args.steps)], L)
+    pool.timing_enable(False)
     layers_rec = None
     if args.repos_layers > 0:
         layers_rec = repos_layers_extra(args, L, hist, drop, repos, hk, hv, rep_bytes)
@@ -455,9 +480,11 @@ def main():
                            "kernel": "k_rotate", "bytes_per_launch": rep_bytes,
                            "avg_launch_ms": round(rot_ms, 5)},
         "roofline_repos_layers": layers_rec,
+        "roofline_compact": comp_rec,
         "kernels_ms_per_step": {k: round(v[0] / max(args.steps, 1), 5) for k, v in kt.items()},
         "attention_pairs": int(pairs),
         "query_tokens_per_s": round(att.q.shape[0] / (ms_step * 1e-3), 1),
+        "repositioned_tokens_per_s": round(n_rep / (rot_ms * 1e-3), 1),
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -62,22 +62,27 @@ hipError_t launch_rot_table(hipStream_t st, int d_rope, const int32_t* deltas, i
 hipError_t launch_rotate(hipStream_t st, uint16_t* const* krs, int n_layers, int n_heads, int page_size,
                          int d_rope, int pairing, const RotItem* items, int n_items, const float* table);
 
-hipError_t launch_scatter_rows(hipStream_t st, const uint16_t* src, uint16_t* dst,
-                               const int32_t* slots, int n, int n_heads, int page_size,
-                               int log2_page, int row_elems);
+// Rows of one paged array in a copy launch (akv_copy.hip): src is token-major
+// [n][heads][d] for an append, the paged array itself for a move; dst is the
+// paged array [pages][heads][page_size][d].
+struct TokenRows {
+  const uint16_t* src;
+  uint16_t* dst;
+  int heads, d;
+};
 
-hipError_t launch_move_rows(hipStream_t st, uint16_t* base, const MovePair* pairs, int n,
-                            int n_heads, int page_size, int log2_page, int row_elems);
+// append: token t's rows of every listed array (at most 3) go to slots[t].
+hipError_t launch_scatter_tokens(hipStream_t st, const TokenRows* rows, int n_rows, const int32_t* slots,
+                                 int n, int page_size, int log2_page);
 
-// Out-of-place repos (akv_version.hip): every row of each pair's token moves
-// from src slot to dst slot; the rotated-key rows (kr, rope_heads heads) are
-// turned by the single delta whose cos / sin row is `table` (d_rope floats:
-// cos of the d_rope/2 pairs, then sin; nullptr = plain copy), the V rows and
-// the MLA K_nope rows (kn, nullptr when d_nope == 0) are copied.  Source and
-// destination slots are disjoint.
-hipError_t launch_clone_rows(hipStream_t st, uint16_t* kr, uint16_t* v, uint16_t* kn, const MovePair* pairs,
-                             int n, int rope_heads, int n_heads, int page_size, int log2_page, int d_rope,
-                             int d_v, int d_nope, int pairing, const float* table);
+// slot -> slot moves of n tokens (compaction, positional versions): the
+// rotated-key array kr (rope_heads x d_rope) moves with each pair turned by
+// the delta whose cos / sin row is `table` (d_rope floats: cos of the d_rope/2
+// pairs, then sin; nullptr = plain copy); the plain arrays (V, MLA K_nope; at
+// most 2) are copied.  Source and destination slots are disjoint.
+hipError_t launch_move_tokens(hipStream_t st, uint16_t* kr, int rope_heads, int d_rope, int pairing,
+                              const TokenRows* plain, int n_plain, const MovePair* pairs, int n,
+                              int page_size, int log2_page, const float* table);
 
 hipError_t launch_expand(hipStream_t st, const Extent* ex, const int32_t* ex_off, int n_ext,
                          int page_size, int32_t* slots);

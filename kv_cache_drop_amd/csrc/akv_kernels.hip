@@ -8,8 +8,6 @@
 //
 // Kernels:
 //   k_rotate       repos delta rotation, in place on the paged pool (HBM-bound)
-//   k_scatter_rows append: token-major rows -> page slots (HBM-bound)
-//   k_move_rows    compaction: slot -> slot row copies (HBM-bound)
 //   k_expand       extents -> per-entry slot list for the attention gather
 //   k_seg_attn     segment-batch attention, bf16 MFMA 32x32x16 (MFMA-bound)
 //   k_combine      split-KV merge of (m, l, O) partials
@@ -177,73 +175,6 @@ hipError_t launch_rotate(hipStream_t st, uint16_t* const* krs, int n_layers, int
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// append: token-major rows [n][H][row] -> paged [page][H][S][row]
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_scatter_rows(const uint16_t* __restrict__ src,
-                                                      uint16_t* __restrict__ dst,
-                                                      const int32_t* __restrict__ slots, int n,
-                                                      int H, int S, int log2S, int row_elems) {
-  const int cpr = row_elems >> 3;
-  const long total = (long)n * H * cpr;
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
-    const int c = (int)(i % cpr);
-    const long r = i / cpr;
-    const int h = (int)(r % H);
-    const int t = (int)(r / H);
-    const int slot = slots[t];
-    const int page = slot >> log2S, off = slot & (S - 1);
-    *(u32x4*)(dst + (((size_t)page * H + h) * S + off) * row_elems + 8 * c) =
-        *(const u32x4*)(src + ((size_t)t * H + h) * row_elems + 8 * c);
-  }
-}
-
-static int grid_for(long chunks) {
-  long b = (chunks + 255) / 256;
-  if (b > 65536) b = 65536;
-  return (int)(b < 1 ? 1 : b);
-}
-
-hipError_t launch_scatter_rows(hipStream_t st, const uint16_t* src, uint16_t* dst,
-                               const int32_t* slots, int n, int n_heads, int page_size,
-                               int log2_page, int row_elems) {
-  if (n <= 0) return hipSuccess;
-  const long chunks = (long)n * n_heads * (row_elems >> 3);
-  hipLaunchKernelGGL(k_scatter_rows, dim3(grid_for(chunks)), dim3(256), 0, st, src, dst, slots, n,
-                     n_heads, page_size, log2_page, row_elems);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// compaction copy ([AKV-blog] section 7, Dilemma 2): rows move between slots of
-// one paged array; source and destination pages are disjoint.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_move_rows(uint16_t* __restrict__ base,
-                                                   const MovePair* __restrict__ pairs, int n, int H,
-                                                   int S, int log2S, int row_elems) {
-  const int cpr = row_elems >> 3;
-  const long total = (long)n * H * cpr;
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
-    const int c = (int)(i % cpr);
-    const long r = i / cpr;
-    const int h = (int)(r % H);
-    const int t = (int)(r / H);
-    const MovePair mp = pairs[t];
-    const int sp = mp.src >> log2S, so = mp.src & (S - 1);
-    const int dp = mp.dst >> log2S, dof = mp.dst & (S - 1);
-    *(u32x4*)(base + (((size_t)dp * H + h) * S + dof) * row_elems + 8 * c) =
-        *(const u32x4*)(base + (((size_t)sp * H + h) * S + so) * row_elems + 8 * c);
-  }
-}
-
-hipError_t launch_move_rows(hipStream_t st, uint16_t* base, const MovePair* pairs, int n,
-                            int n_heads, int page_size, int log2_page, int row_elems) {
-  if (n <= 0) return hipSuccess;
-  const long chunks = (long)n * n_heads * (row_elems >> 3);
-  hipLaunchKernelGGL(k_move_rows, dim3(grid_for(chunks)), dim3(256), 0, st, base, pairs, n,
-                     n_heads, page_size, log2_page, row_elems);
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------
 // extents -> slot list (one thread per extent)

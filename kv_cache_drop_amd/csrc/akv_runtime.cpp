@@ -3,7 +3,7 @@
 // Holds the page allocator, per-sequence token tables (slot, position, drop
 // flag), the visible-list / page-table builder, the repos and attention
 // planners, a pinned staging ring for host->device metadata, and the launches
-// of the HIP kernels in akv_kernels.hip.
+// of the HIP kernels in akv_kernels.hip and akv_copy.hip.
 //
 // Sources, cited by page title and section:
 //   [AKV-blog]  "AKV: Cache Engineering for Autonomous Agents and State-Preserving
@@ -455,21 +455,17 @@ akv_status device_append(akv_pool* p, const std::vector<int32_t>& slots, const v
   if (st != AKV_OK) return st;
   const akv_layout& L = p->L;
   const int n = (int)slots.size();
-  KTimer tm(p, AKV_K_APPEND);
-  hipError_t e;
+  akv::TokenRows rows[3];
+  int nr = 0;
   if (L.d_nope > 0) {
-    e = akv::launch_scatter_rows(p->stream, (const uint16_t*)K, p->k, (const int32_t*)dslots, n,
-                                 L.n_kv_heads, L.page_size, p->log2S, L.d_nope);
-    if (e == hipSuccess)
-      e = akv::launch_scatter_rows(p->stream, (const uint16_t*)Kpe, p->kpe, (const int32_t*)dslots,
-                                   n, p->rope_heads(), L.page_size, p->log2S, L.d_rope);
+    rows[nr++] = {(const uint16_t*)K, p->k, L.n_kv_heads, L.d_nope};
+    rows[nr++] = {(const uint16_t*)Kpe, p->kpe, p->rope_heads(), L.d_rope};
   } else {
-    e = akv::launch_scatter_rows(p->stream, (const uint16_t*)K, p->k, (const int32_t*)dslots, n,
-                                 L.n_kv_heads, L.page_size, p->log2S, L.d_rope);
+    rows[nr++] = {(const uint16_t*)K, p->k, L.n_kv_heads, L.d_rope};
   }
-  if (e == hipSuccess)
-    e = akv::launch_scatter_rows(p->stream, (const uint16_t*)V, p->v, (const int32_t*)dslots, n,
-                                 L.n_kv_heads, L.page_size, p->log2S, L.d_v);
+  rows[nr++] = {(const uint16_t*)V, p->v, L.n_kv_heads, L.d_v};
+  KTimer tm(p, AKV_K_APPEND);
+  hipError_t e = akv::launch_scatter_tokens(p->stream, rows, nr, (const int32_t*)dslots, n, L.page_size, p->log2S);
   tm.done();
   return check_launch(e, "append kernel launch");
 }
@@ -501,29 +497,27 @@ akv_status device_rotate(akv_pool* p, const std::vector<akv::RotItem>& items,
   return check_launch(e, "rotate kernel launch");
 }
 
+// One launch moving every paged array of n tokens (pairs on the device); the
+// rotated-key rows are turned by `table` when it is given.
+hipError_t move_tokens(akv_pool* p, const akv::MovePair* pairs, int n, const float* table) {
+  const akv_layout& L = p->L;
+  akv::TokenRows plain[2];
+  int np = 0;
+  plain[np++] = {p->v, p->v, L.n_kv_heads, L.d_v};
+  if (L.d_nope > 0) plain[np++] = {p->k, p->k, L.n_kv_heads, L.d_nope};
+  return akv::launch_move_tokens(p->stream, p->rope_array(), p->rope_heads(), L.d_rope, L.pairing, plain, np,
+                                 pairs, n, L.page_size, p->log2S, table);
+}
+
 akv_status device_move(akv_pool* p, const std::vector<akv::MovePair>& mv) {
   if (!p->device || mv.empty()) return AKV_OK;
   ScratchCursor sc(p);
   void* dmv;
   akv_status st = upload_array(p, sc, mv.data(), mv.size() * sizeof(akv::MovePair), &dmv);
   if (st != AKV_OK) return st;
-  const akv_layout& L = p->L;
   const int n = (int)mv.size();
   KTimer tm(p, AKV_K_COMPACT);
-  hipError_t e;
-  if (L.d_nope > 0) {
-    e = akv::launch_move_rows(p->stream, p->k, (const akv::MovePair*)dmv, n, L.n_kv_heads,
-                              L.page_size, p->log2S, L.d_nope);
-    if (e == hipSuccess)
-      e = akv::launch_move_rows(p->stream, p->kpe, (const akv::MovePair*)dmv, n, p->rope_heads(),
-                                L.page_size, p->log2S, L.d_rope);
-  } else {
-    e = akv::launch_move_rows(p->stream, p->k, (const akv::MovePair*)dmv, n, L.n_kv_heads,
-                              L.page_size, p->log2S, L.d_rope);
-  }
-  if (e == hipSuccess)
-    e = akv::launch_move_rows(p->stream, p->v, (const akv::MovePair*)dmv, n, L.n_kv_heads,
-                              L.page_size, p->log2S, L.d_v);
+  hipError_t e = move_tokens(p, (const akv::MovePair*)dmv, n, nullptr);
   tm.done();
   return check_launch(e, "compaction kernel launch");
 }
@@ -1035,9 +1029,7 @@ akv_status akv_seq_clone(akv_pool* p, int32_t src, int32_t first, int32_t n, int
       if (e != hipSuccess) return check_launch(e, "rotation table kernel launch");
     }
     KTimer tm(p, AKV_K_CLONE);
-    e = akv::launch_clone_rows(p->stream, p->rope_array(), p->v, L.d_nope > 0 ? p->k : nullptr,
-                               (const akv::MovePair*)dmv, m, p->rope_heads(), L.n_kv_heads, L.page_size,
-                               p->log2S, L.d_rope, L.d_v, L.d_nope, L.pairing, delta != 0 ? dtab : nullptr);
+    e = move_tokens(p, (const akv::MovePair*)dmv, m, delta != 0 ? dtab : nullptr);
     tm.done();
     return check_launch(e, "clone kernel launch");
   } catch (const std::bad_alloc&) {
