@@ -31,26 +31,29 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 # HBM byte counters per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE,
-# KiB) of the kernels as built from the source with this SHA-1, on this
-# workload.  A plain 1 GiB device copy reads FETCH_SIZE = 524,302 KiB and
+# KiB) of each kernel as built from the source file with the given SHA-1, on
+# the 64K step.  A plain 1 GiB device copy reads FETCH_SIZE = 524,302 KiB and
 # WRITE_SIZE = 1,048,576 KiB, so fetched KiB are scaled by 2.0 and written KiB
-# by 1.0.  When the kernel source differs, traffic is reported as null.
+# by 1.0.  When the kernel's source differs, its traffic is reported as null.
+_KERNELS_SHA1 = "23f137b6eeab98bf293555e82e812e78b0174f86"    # akv_kernels.hip
+_COPY_SHA1 = "2a16fbd3bdf4c924c007ee7a8f5e9337713b3565"       # akv_copy.hip
 COUNTERS = {
-    "kernel_source_sha1": "2a77ebb759dd3fb46334419f953c51ab2989453f",
     "fetch_scale": 1048576 / 524302, "write_scale": 1.0,
-    "attention": {"fetch_kib": 111086, "write_kib": 16384},
-    "rotate": {"fetch_kib": 39271, "write_kib": 77629},
-    "rotate_32_layers": {"fetch_kib": 1248270, "write_kib": 2484290},
+    "attention": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 110925, "write_kib": 16384},
+    "rotate": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 39271, "write_kib": 77633},
+    "rotate_32_layers": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 1248286,
+                         "write_kib": 2484294},
+    "compact": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 85345, "write_kib": 165578},
 }
 
 
 def counted_traffic(kind: str):
     import hashlib
-    src = os.path.join(ROOT, "kv_cache_drop_amd", "csrc", "akv_kernels.hip")
-    with open(src, "rb") as f:
-        if hashlib.sha1(f.read()).hexdigest() != COUNTERS["kernel_source_sha1"]:
-            return None
     c = COUNTERS[kind]
+    src = os.path.join(ROOT, "kv_cache_drop_amd", "csrc", c["source"])
+    with open(src, "rb") as f:
+        if hashlib.sha1(f.read()).hexdigest() != c["sha1"]:
+            return None
     return round((c["fetch_kib"] * COUNTERS["fetch_scale"] + c["write_kib"] * COUNTERS["write_scale"]) * 1024)
 
 
@@ -139,7 +142,7 @@ def compact_extra(pool, seqs, L) -> dict:
     return {"extra": True, "what": "forced compaction of the 64K sequence after its step (visible history "
                                    "+ new tokens into fresh pages)",
             "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": "k_move_tokens",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": counted_traffic("compact"), "kernel": "k_move_tokens",
             "tokens_per_launch": moved / max(len(seqs), 1), "bytes_per_launch": nbytes,
             "avg_launch_ms": round(avg, 5), "launches": n}
 
