@@ -124,7 +124,7 @@ def cpu_baseline(wl, rows_per_seg: int):
 
 
 def compact_extra(pool, seqs, L) -> dict:
-    """Extra line: forced compaction (k_move_rows) of C2 sequences after their
+    """Extra line: forced compaction (k_move_tokens) of C2 sequences after their
     step, each the only work on its copy since that step (the earliest timed
     copies first, so their pages are long out of every cache)."""
     import torch
