@@ -57,8 +57,12 @@ def counted_traffic(kind: str):
     return round((c["fetch_kib"] * COUNTERS["fetch_scale"] + c["write_kib"] * COUNTERS["write_scale"]) * 1024)
 
 
-def attention_kernel_name(layout) -> str:
-    """The attention kernel the library launches for this layout."""
+def attention_kernel_name(layout, max_rows=None) -> str:
+    """The attention kernel the library launches for this layout (max_rows:
+    the largest q_len x q heads per kv head over the launch's segments)."""
+    if layout.d_nope == 0 and layout.d_rope == 128 and layout.d_v == 128 and max_rows is not None and \
+            max_rows <= 16 and os.environ.get("AKV_DECODE_KERNEL") != "off":
+        return "k_decode_attn"
     if layout.d_nope == 0 and layout.d_rope == 128 and layout.d_v == 128 and \
             os.environ.get("AKV_ATTN_KERNEL") != "staged" and os.environ.get("AKV_ATTN_WAVES") != "4":
         return "k_seg_attn_dl<128,128,0,8,1,4>"
@@ -195,9 +199,10 @@ def repos_layers_extra(args, L, hist, drop, repos, hk, hv, rep_bytes) -> dict:
 
 def run_config(args) -> dict:
     """One JSON record for a workload other than the headline: replay its op
-    script on a fresh device pool per rep (set-up appends untimed), flush L2 and
-    the Infinity Cache with a 1 GiB write, then time the remaining ops (drop /
-    repos / splice, the new tokens' append, attention) as one step."""
+    script on a fresh device pool per rep (set-up untimed), flush L2 and the
+    Infinity Cache by reading 1 GiB (so no dirty lines are left to write back
+    inside the timed step), then time the remaining ops (drop / repos /
+    splice / clone, the new tokens' append, attention) as one step."""
     import torch
     import device_script as D
     import workloads as W
@@ -207,7 +212,11 @@ def run_config(args) -> dict:
     wl = gens[args.config](args.seed)
     L = wl.layout
     ops = list(wl.ops)
-    i0 = next(i for i, o in enumerate(ops) if not isinstance(o, (W.SeqCreate, W.Append)))
+    # timed ops: from the first cache operation on (drop / repos / splice /
+    # clone, the new tokens, attention), or from where the workload says its
+    # step starts (decode: the new tokens and attention after the histories)
+    i0 = wl.notes.get("step_from",
+                      next(i for i, o in enumerate(ops) if not isinstance(o, (W.SeqCreate, W.Append))))
     n_seq = sum(isinstance(o, W.SeqCreate) for o in ops)
     # device inputs of the timed ops, uploaded once (outside the timed region)
     dev = {}
@@ -217,7 +226,7 @@ def run_config(args) -> dict:
         elif isinstance(op, W.Attention):
             q = D.dev_bf16(op.q)
             dev[i] = (q, torch.empty((q.shape[0], L.n_q_heads, L.d_v), dtype=torch.bfloat16, device="cuda:0"))
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
     rope_heads = L.n_kv_heads if (not L.mla or L.kpe_per_head) else 1
     tot = {k: [0.0, 0] for k in ("attention", "rotate", "append", "compact", "expand", "combine", "clone")}
     walls, flops, pairs, kv_bytes, n_rot, n_q, clone_bytes = [], 0.0, 0, 0, 0, 0, 0
@@ -228,7 +237,7 @@ def run_config(args) -> dict:
         for op in ops[:i0]:
             D.apply_op(pool, op, keep)
         pre = [pool.tokens(s) for s in range(n_seq)] if rep == 0 else None
-        flush.fill_(rep & 255)
+        flush_sum = flush.sum(dtype=torch.int64)   # reads 1 GiB: evicts L2 / MALL, dirties nothing
         torch.cuda.synchronize()
         timed = rep >= args.warmup
         pool.timing_enable(timed)
@@ -272,7 +281,8 @@ def run_config(args) -> dict:
                 if isinstance(op, W.Clone):
                     dr = pool.tokens(op.src)[2][op.first:op.first + op.n]
                     clone_bytes += 2 * row_bytes * int((dr == 0).sum())
-            kern = attention_kernel_name(L)
+            grp = L.n_q_heads // L.n_kv_heads
+            kern = attention_kernel_name(L, max(sg.q_len * grp for _, _, op in lists for sg in op.segments))
         pool.close()
         del pool, keep
     ms_step = float(np.median(walls)) * 1e3
@@ -334,8 +344,9 @@ CONFIG_NAMES = {
                  "(512-token preamble, the 64K trace, older tools dropped, survivors repositioned) and request B "
                  "(the same trace after a preamble of another length) cloned from A's state with keys turned by "
                  "the offset change; 512 queries each in one launch",
-    "decode": "48 requests of 2K-16K tokens on the 64K layer shape (32 q / 8 kv heads, head_dim 128, page 16): "
-              "drop and repos per request, then one new token each, 48 one-query segments in one launch",
+    "decode": "48 requests of 2K-16K tokens on the 64K layer shape (32 q / 8 kv heads, head_dim 128, page 16), "
+              "dropped and repositioned at set-up; the step appends one token per request and runs 48 one-query "
+              "segments in one launch",
 }
 
 

@@ -112,6 +112,14 @@ hipError_t launch_seg_attn(hipStream_t st, const AttnArgs& a, int d_nope, int d_
 hipError_t launch_combine(hipStream_t st, const AttnArgs& a, const CombItem* items, int n_items,
                           int d_v);
 
+// Decode attention (akv_decode.hip): 128-dim GQA work items of at most
+// DECODE_ROWS packed rows, the block's waves splitting the key range.
+constexpr int DECODE_ROWS = 16;
+hipError_t launch_decode_attn(hipStream_t st, const AttnArgs& a);
+// False when the environment sets AKV_DECODE_KERNEL=off (the prefill kernel
+// then runs decode launches too, for comparison).
+bool decode_attn_enabled();
+
 bool attn_dims_supported(int d_nope, int d_rope, int d_v);
 
 }  // namespace akv

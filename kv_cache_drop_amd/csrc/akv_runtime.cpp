@@ -679,13 +679,13 @@ struct AttnPlan {
 };
 
 constexpr int kXcds = 8;
+constexpr int64_t kDecodeChunk = 1024;
 
 void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
-                    const std::vector<int64_t>& lkv, const std::vector<int64_t>& list_off,
+                    const std::vector<int64_t>& lkv, const std::vector<int64_t>& list_off, int RB,
                     AttnPlan& plan) {
   const akv_layout& L = p->L;
   const int G = L.n_q_heads / L.n_kv_heads;
-  const int RB = akv::attn_rows_per_block(L.d_nope);
   const int KT = akv::ATTN_KTILE;
   plan.segs.clear();
   for (int32_t i = 0; i < n_segs; ++i)
@@ -696,7 +696,8 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
     if (segs[i].q_len > 0) base += (int64_t)L.n_kv_heads * ((segs[i].q_len * (int64_t)G + RB - 1) / RB);
   int target = 1;
   // split the key range only when the row tiles alone cannot fill the CUs
-  // (at most 16 splits: the combine kernel holds one split per lane of a wave)
+  // (at most 16 here, 64 for decode items: the combine kernel holds one split
+  // per lane of a wave)
   if (base > 0 && base < p->n_cu) target = (int)std::min<int64_t>(16, (2LL * p->n_cu + base - 1) / base);
   // ... or when one row tile alone would hold a CU well past the even share
   // of the launch (few query rows over long lists: decode): such a segment's
@@ -731,6 +732,10 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
     int ns = target;
     if (4 * (lkv[i] + 64) > 5 * cu_share)
       ns = (int)std::max<int64_t>(ns, std::min<int64_t>(16, (lkv[i] + 64 + block_cap - 1) / block_cap));
+    // decode items stream their keys at the HBM rate: cut every list into
+    // chunks of about kDecodeChunk keys so that many blocks share the CUs
+    if (RB == akv::DECODE_ROWS)
+      ns = (int)std::max<int64_t>(ns, std::min<int64_t>(64, (lkv[i] + kDecodeChunk - 1) / kDecodeChunk));
     ns = (int)std::min<int64_t>(ns, std::max<int64_t>(1, lkv[i] / 512));
     ns = (int)std::min<int64_t>(ns, key_tiles);
     if (ns < 1) ns = 1;
@@ -1358,8 +1363,16 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
     if (!Q || !out) return fail(AKV_EINVAL, "Q and out are required");
     if (total > kInt32Max) return fail(AKV_ERANGE, "page lists too long");
 
+    // Launches whose every segment packs at most 16 rows per kv head (decode)
+    // run the decode kernel on 16-row items; the others the prefill kernels.
+    const int G = L.n_q_heads / L.n_kv_heads;
+    int64_t max_rows = 0;
+    for (int32_t i = 0; i < n_segs; ++i) max_rows = std::max<int64_t>(max_rows, (int64_t)segs[i].q_len * G);
+    const bool decode = akv::decode_attn_enabled() && L.d_nope == 0 && L.d_rope == 128 && L.d_v == 128 &&
+                        max_rows <= akv::DECODE_ROWS;
+    const int rb = decode ? akv::DECODE_ROWS : akv::attn_rows_per_block(L.d_nope);
     AttnPlan plan;
-    plan_attention(p, segs, n_segs, lkv, list_off, plan);
+    plan_attention(p, segs, n_segs, lkv, list_off, rb, plan);
     if (plan.part_rows > kInt32Max) return fail(AKV_ERANGE, "too many split-KV partial rows");
     // extent offsets for the slot expansion (over all segments' ranges, in order)
     std::vector<akv::Extent> ex_used;
@@ -1420,10 +1433,10 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
     a.out = (uint16_t*)out;
     a.part_o = part_o;
     a.part_ml = part_ml;
-    a.rows_per_block = akv::attn_rows_per_block(L.d_nope);
+    a.rows_per_block = rb;
     {
       KTimer tm(p, AKV_K_ATTN);
-      e = akv::launch_seg_attn(p->stream, a, L.d_nope, L.d_rope, L.d_v);
+      e = decode ? akv::launch_decode_attn(p->stream, a) : akv::launch_seg_attn(p->stream, a, L.d_nope, L.d_rope, L.d_v);
       tm.done();
     }
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");

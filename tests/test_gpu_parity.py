@@ -373,11 +373,14 @@ def test_retrigger_64k_sampled():
     _sampled_parity(W.retrigger(0), n_rows=12)
 
 
-@pytest.mark.parametrize("seed,n_req,lo,hi", [(0, 16, 1024, 4096), (1, 48, 256, 3072)])
-def test_decode_batch_full(seed, n_req, lo, hi):
-    """One new token per request after drop and repos, all requests in one
-    launch: every output row and every visible key against the oracle."""
-    _full_parity(W.decode_batch(seed, n_req=n_req, ctx_lo=lo, ctx_hi=hi))
+@pytest.mark.parametrize("seed,n_req,lo,hi,hq,lq", [(0, 16, 1024, 4096, 32, 1), (1, 48, 256, 3072, 32, 1),
+                                                   (2, 24, 1, 700, 64, 2), (3, 20, 1, 2500, 32, 4),
+                                                   (4, 12, 1, 40, 32, 1)])
+def test_decode_batch_full(seed, n_req, lo, hi, hq, lq):
+    """q_len new tokens per request after drop and repos, all requests in one
+    launch (4 to 16 rows per kv head, lists of 1 to several thousand keys):
+    every output row and every visible key against the oracle."""
+    _full_parity(W.decode_batch(seed, n_req=n_req, ctx_lo=lo, ctx_hi=hi, n_q_heads=hq, q_len=lq))
 
 
 def test_repos_layers_one_launch():

@@ -483,12 +483,14 @@ def retrigger(seed: int = 0, ctx: int = 65536, pre_a: int = 512, nq: int = 512, 
 # --------------------------------------------------------------------------
 # decode: one new token per request at high batch (the inter-token side)
 # --------------------------------------------------------------------------
-def decode_batch(seed: int = 0, n_req: int = 48, ctx_lo: int = 2048, ctx_hi: int = 16384) -> Workload:
+def decode_batch(seed: int = 0, n_req: int = 48, ctx_lo: int = 2048, ctx_hi: int = 16384,
+                 n_q_heads: int = 32, q_len: int = 1) -> Workload:
     """n_req agent histories in one pool, each built with the batched recipe
     (512-token reasoning turns, log-uniform tool spans, 10-60% of the older
-    tools dropped, survivors repositioned); then every request appends one
-    token at the next position and runs one single-query segment over its
-    whole visible list, all in one attention launch."""
+    tools dropped, survivors repositioned); then every request appends q_len
+    tokens (1: plain decode; a few: speculative or multi-token steps) at its
+    next positions and runs one segment over its whole visible list, all in
+    one attention launch."""
     rng = _rng(seed)
     reqs = []
     for r in range(n_req):
@@ -512,8 +514,8 @@ def decode_batch(seed: int = 0, n_req: int = 48, ctx_lo: int = 2048, ctx_hi: int
             gone += tools[i][1] - tools[i][0]
         dropped = [tools[i] for i in sorted(chosen)]
         reqs.append(dict(ctx=ctx, dropped=dropped))
-    pages = sum((q["ctx"] + 1 + 15) // 16 for q in reqs) + 16
-    lay = Layout(32, 8, 0, 128, 128, 16, pages, rope_theta=500000.0)
+    pages = sum((q["ctx"] + q_len + 15) // 16 for q in reqs) + 16
+    lay = Layout(n_q_heads, 8, 0, 128, 128, 16, pages, rope_theta=500000.0)
     wl = Workload("decode_batch", lay, rng.permutation(pages).astype(np.int32))
     for r in range(n_req):
         wl.ops.append(SeqCreate())
@@ -526,11 +528,12 @@ def decode_batch(seed: int = 0, n_req: int = 48, ctx_lo: int = 2048, ctx_hi: int
             if len(rs):
                 wl.ops.append(Repos(r, rs, rd))
     segs = []
+    wl.notes["step_from"] = len(wl.ops)     # one decode step: the new tokens and attention
     for r, q in enumerate(reqs):
         h = q["ctx"] - sum(e - b for b, e in q["dropped"])
-        wl.ops.append(_append_op(rng, lay, r, np.array([h], dtype=np.int32)))
-        segs.append(Segment(r, r, 1, np.zeros((0, 2), np.int32)))
-    qarr = _normal_bf16(rng, (n_req, lay.n_q_heads, lay.d_qk), scale=1.0 / 8.0)
+        wl.ops.append(_append_op(rng, lay, r, np.arange(h, h + q_len, dtype=np.int32)))
+        segs.append(Segment(r, r * q_len, q_len, np.zeros((0, 2), np.int32)))
+    qarr = _normal_bf16(rng, (n_req * q_len, lay.n_q_heads, lay.d_qk), scale=1.0 / 8.0)
     wl.ops.append(Attention(qarr, segs))
     wl.notes.update(requests=reqs)
     return wl
