@@ -221,7 +221,7 @@ def run_config(args) -> dict:
     # device inputs of the timed ops, uploaded once (outside the timed region)
     dev = {}
     for i, op in enumerate(ops[i0:], start=i0):
-        if isinstance(op, (W.Append, W.Splice)):
+        if isinstance(op, (W.Append, W.AppendBatch, W.Splice)):
             dev[i] = (D.dev_bf16(op.k), D.dev_bf16(op.kpe) if op.kpe is not None else None, D.dev_bf16(op.v))
         elif isinstance(op, W.Attention):
             q = D.dev_bf16(op.q)
@@ -246,12 +246,16 @@ def run_config(args) -> dict:
         for i, op in enumerate(ops[i0:], start=i0):
             if isinstance(op, W.Append):
                 pool.append(op.seq, op.pos, dev[i][0], dev[i][1], dev[i][2])
+            elif isinstance(op, W.AppendBatch):
+                pool.append_batch(op.seqs, op.counts, op.pos, dev[i][0], dev[i][1], dev[i][2])
             elif isinstance(op, W.Splice):
                 pool.splice(op.seq, op.spans, op.stub_lens, dev[i][0], dev[i][1], dev[i][2])
             elif isinstance(op, W.Attention):
-                rows, ex = D.segment_inputs(pool, op)
-                pool.segment_attention(dev[i][0], rows, ex, op.scale, out=dev[i][1])
-                lists.append((rows, ex, op))
+                # lists built inside the library from the sequences' page tables
+                pool.seq_attention(dev[i][0], [(sg.seq, sg.q_begin, sg.q_len,
+                                                sg.mask_spans if len(sg.mask_spans) else None)
+                                               for sg in op.segments], op.scale, out=dev[i][1])
+                lists.append(op)
             else:
                 D.apply_op(pool, op, keep)
         torch.cuda.synchronize()
@@ -268,7 +272,8 @@ def run_config(args) -> dict:
                 _, pos1, drop1 = pool.tokens(s)
                 m = len(pos0)
                 n_rot += int(((pos1[:m] != pos0) & ~drop1[:m].astype(bool)).sum())
-            for rows, ex, op in lists:
+            for op in lists:
+                rows, ex = D.segment_inputs(pool, op)     # the same lists, for the counts
                 f, p = attention_flops(L, rows, ex)
                 flops += float(f)
                 pairs += int(p)
@@ -282,7 +287,7 @@ def run_config(args) -> dict:
                     dr = pool.tokens(op.src)[2][op.first:op.first + op.n]
                     clone_bytes += 2 * row_bytes * int((dr == 0).sum())
             grp = L.n_q_heads // L.n_kv_heads
-            kern = attention_kernel_name(L, max(sg.q_len * grp for _, _, op in lists for sg in op.segments))
+            kern = attention_kernel_name(L, max(sg.q_len * grp for op in lists for sg in op.segments))
         pool.close()
         del pool, keep
     ms_step = float(np.median(walls)) * 1e3

@@ -70,6 +70,7 @@ typedef enum {
 typedef struct { int32_t begin, end; } akv_span;          /* [begin, end)             */
 typedef struct { int32_t page, lo, hi; } akv_extent;      /* slots lo..hi-1 of a page */
 typedef struct { int32_t q_begin, q_len, ext_begin, ext_len; } akv_segment;
+typedef struct { int32_t seq, q_begin, q_len, mask_begin, mask_len; } akv_seq_segment;
 
 typedef struct {
   int32_t n_q_heads;     /* multiple of n_kv_heads; q head h reads kv head h / (n_q_heads/n_kv_heads) */
@@ -127,6 +128,18 @@ akv_status akv_seq_release(akv_pool* pool, int32_t seq);
  * (no page left in the free and evictable queues). */
 akv_status akv_append(akv_pool* pool, int32_t seq, const void* K, const void* K_pe,
                       const void* V, const int32_t* pos, int32_t n);
+
+/* append to several sequences in one call (a decode step: a few new tokens
+ * for each of many requests).  Entry i appends counts[i] tokens to seqs[i];
+ * K, K_pe, V and pos hold all entries' tokens concatenated in entry order,
+ * laid out as for akv_append.  The result, slots and page order included,
+ * is that of calling akv_append for each entry in order (a sequence may
+ * appear more than once); every entry is validated and the pages for all of
+ * them are counted before anything changes, and all rows are written by one
+ * kernel launch.  Errors: as akv_append (AKV_EINVAL also for n_seqs < 0 or
+ * a negative count). */
+akv_status akv_append_batch(akv_pool* pool, int32_t n_seqs, const int32_t* seqs, const int32_t* counts,
+                            const void* K, const void* K_pe, const void* V, const int32_t* pos);
 
 /* drop ([AKV-blog] section 2, The Drop Primitive): mark the tokens of every
  * span inactive.  Nothing is freed or rewritten; later attention lists skip
@@ -230,6 +243,19 @@ akv_status akv_segment_attention(akv_pool* pool, const void* Q, int32_t n_q_toke
                                  const akv_segment* segs, int32_t n_segs,
                                  const akv_extent* page_lists, int32_t n_ext, float scale,
                                  void* out);
+
+/* segment-batch attention over sequences' own lists: segment i reads the
+ * visible list of sequence segs[i].seq minus the spans masks[mask_begin ..
+ * mask_begin+mask_len) (logical-index spans, hidden from this segment only),
+ * i.e. the list akv_seq_visible returns for that mask, and runs exactly as
+ * akv_segment_attention with those lists (same kernels, same results).  The
+ * lists are built inside the library from each sequence's cached page-table
+ * image, so a decode step hands over no extents.  Errors: AKV_EINVAL (bad
+ * sequence, negative count, mask range outside masks[]), AKV_ESTATE (released
+ * sequence), AKV_ERANGE (mask span outside its sequence), and those of
+ * akv_segment_attention. */
+akv_status akv_seq_attention(akv_pool* pool, const void* Q, int32_t n_q_tokens, const akv_seq_segment* segs,
+                             int32_t n_segs, const akv_span* masks, int32_t n_masks, float scale, void* out);
 
 /* ---- inspection, sync, errors ---------------------------------------------------- */
 

@@ -60,6 +60,8 @@ SYMBOLS = {
     "akv_repos_layers": [ctypes.POINTER(_P), _I, _I, _IP, _IP, _I],
     "akv_splice": [_P, _I, _IP, _IP, _I, _P, _P, _P, _IP],
     "akv_seq_clone": [_P, _I, _I, _I, _I, _I],
+    "akv_append_batch": [_P, _I, _IP, _IP, _P, _P, _P, _IP],
+    "akv_seq_attention": [_P, _P, _I, _IP, _I, _IP, _I, ctypes.c_float, _P],
     "akv_seq_visible": [_P, _I, _IP, _I, _IP, _I, _IP],
     "akv_segment_attention": [_P, _P, _I, _IP, _I, _IP, _I, ctypes.c_float, _P],
     "akv_seq_tokens": [_P, _I, _I, _I, _IP, _IP, ctypes.POINTER(ctypes.c_uint8)],
@@ -209,6 +211,16 @@ class Pool:
         self._check_kv(len(pos), k, kpe, v)
         _check(lib().akv_append(self._h, seq, _dptr(k), _dptr(kpe), _dptr(v), _ptr(pos), len(pos)))
 
+    def append_batch(self, seqs, counts, pos, k=None, kpe=None, v=None) -> None:
+        """counts[i] tokens to seqs[i] for every entry, rows concatenated in
+        entry order (akv_append_batch: one kernel launch)."""
+        sq, cn, pos = _i32(seqs).reshape(-1), _i32(counts).reshape(-1), _i32(pos).reshape(-1)
+        if len(sq) != len(cn) or int(cn.astype(np.int64).sum()) != len(pos):
+            raise ValueError("one count per sequence entry, and one position per token")
+        self._check_kv(len(pos), k, kpe, v)
+        _check(lib().akv_append_batch(self._h, len(sq), _ptr(sq), _ptr(cn), _dptr(k), _dptr(kpe), _dptr(v),
+                                      _ptr(pos)))
+
     def drop(self, seq: int, spans) -> None:
         sp = _i32(spans).reshape(-1, 2)
         _check(lib().akv_drop(self._h, seq, _ptr(sp), len(sp)))
@@ -257,13 +269,13 @@ class Pool:
         n = ctypes.c_int32()
         cap = 4096
         while True:
-            out = np.zeros((cap, 3), np.int32)
+            out = np.empty((cap, 3), np.int32)
             st = lib().akv_seq_visible(self._h, seq, _ptr(m), len(m), _ptr(out), cap, ctypes.byref(n))
             if st == AKV_ERANGE and n.value > cap:
                 cap = n.value
                 continue
             _check(st)
-            return out[: n.value].copy()
+            return out[: n.value]
 
     def tokens(self, seq: int):
         n, _, _ = self.info(seq)
@@ -305,6 +317,30 @@ class Pool:
             raise ValueError("out must be bf16 [Nq, n_q_heads, d_v]")
         _check(lib().akv_segment_attention(self._h, _dptr(q), q.shape[0], _ptr(sg), len(sg), _ptr(ex),
                                            len(ex), float(scale), _dptr(out)))
+        return out
+
+    def seq_attention(self, q, segments, scale: float = 0.0, out=None):
+        """Attention over sequences' own visible lists (akv_seq_attention):
+        segments are (seq, q_begin, q_len, mask_spans) with mask_spans an
+        [m, 2] array of logical spans hidden from that segment (or None)."""
+        import torch
+        rows, spans = [], []
+        for seq, qb, ql, m in segments:
+            m = _i32(m if m is not None else np.zeros((0, 2))).reshape(-1, 2)
+            rows.append((seq, qb, ql, len(spans), len(m)))
+            spans.extend(m.tolist())
+        sg = _i32(rows).reshape(-1, 5)
+        ms = _i32(spans).reshape(-1, 2)
+        L = self.layout
+        if q.dim() != 3 or q.shape[1] != L["n_q_heads"] or q.shape[2] != L["d_nope"] + L["d_rope"] \
+                or q.dtype != torch.bfloat16:
+            raise ValueError("q must be bf16 [Nq, n_q_heads, d_nope + d_rope]")
+        if out is None:
+            out = torch.zeros((q.shape[0], q.shape[1], L["d_v"]), dtype=torch.bfloat16, device=q.device)
+        if tuple(out.shape) != (q.shape[0], L["n_q_heads"], L["d_v"]) or out.dtype != torch.bfloat16:
+            raise ValueError("out must be bf16 [Nq, n_q_heads, d_v]")
+        _check(lib().akv_seq_attention(self._h, _dptr(q), q.shape[0], _ptr(sg), len(sg), _ptr(ms), len(ms),
+                                       float(scale), _dptr(out)))
         return out
 
     # -- timing / sync -------------------------------------------------------------

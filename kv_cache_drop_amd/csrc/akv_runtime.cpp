@@ -21,6 +21,7 @@
 #include <new>
 #include <string>
 #include <unordered_map>
+#include <initializer_list>
 #include <utility>
 #include <vector>
 
@@ -66,6 +67,9 @@ struct SeqRec {
   int64_t n_vis = 0;
   std::vector<int32_t> vis;    // cached visible order
   bool vis_ok = false;
+  std::vector<akv_extent> ext; // cached page-table image of vis (valid with ext_ok)
+  bool ext_ok = false;
+  void stale() { vis_ok = ext_ok = false; }
 };
 
 // Pinned host ring for metadata uploads.  A region may be rewritten once the
@@ -341,9 +345,24 @@ void place_tokens(akv_pool* p, int32_t s, int32_t n, const int32_t* pos, int32_t
     q.slot.push_back(slot);
     q.pos.push_back(pos[i]);
     q.dropped.push_back(0);
+    // a token placed at or after the last visible position extends the
+    // cached visible order (and its extents) at the end
+    if (q.vis_ok) {
+      if (q.vis.empty() || pos[i] >= q.pos[q.vis.back()]) {
+        q.vis.push_back(t0 + i);
+        if (q.ext_ok) {
+          const int32_t off = slot - pg * S;
+          if (!q.ext.empty() && q.ext.back().page == pg && q.ext.back().hi == off)
+            q.ext.back().hi = off + 1;
+          else
+            q.ext.push_back({pg, off, off + 1});
+        }
+      } else {
+        q.stale();
+      }
+    }
   }
   q.n_vis += n;
-  q.vis_ok = false;
 }
 
 akv_status get_seq(akv_pool* p, int32_t s, SeqRec** out) {
@@ -388,12 +407,12 @@ const std::vector<int32_t>& visible(SeqRec& q) {
 
 void build_extents(const akv_pool* p, const SeqRec& q, const std::vector<int32_t>& order,
                    const std::vector<uint8_t>* hide, std::vector<akv_extent>& out) {
-  const int32_t S = p->L.page_size;
+  const int32_t lg = p->log2S, mask = p->L.page_size - 1;
   out.clear();
   for (int32_t t : order) {
     if (hide && (*hide)[t]) continue;
     const int32_t slot = q.slot[t];
-    const int32_t pg = slot / S, off = slot - pg * S;
+    const int32_t pg = slot >> lg, off = slot & mask;
     if (!out.empty() && out.back().page == pg && out.back().hi == off)
       out.back().hi = off + 1;
     else
@@ -421,6 +440,27 @@ akv_status upload_array(akv_pool* p, ScratchCursor& sc, const void* src, size_t 
   if (!sc.ok())
     return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
   return stg_upload(p, h, *dev, n);
+}
+
+// Several host arrays through one staging region and one copy; dev[i]
+// receives array i's device address (each 256-byte aligned).
+akv_status upload_arrays(akv_pool* p, ScratchCursor& sc, std::initializer_list<std::pair<const void*, size_t>> parts,
+                         void** dev) {
+  size_t total = 0;
+  for (const auto& pr : parts) total += align_up(std::max<size_t>(pr.second, 1), 256);
+  char* h;
+  akv_status st = stg_reserve(p, total, &h);
+  if (st != AKV_OK) return st;
+  char* d = sc.take(total);
+  if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
+  size_t off = 0;
+  int i = 0;
+  for (const auto& pr : parts) {
+    if (pr.second) std::memcpy(h + off, pr.first, pr.second);
+    dev[i++] = d + off;
+    off += align_up(std::max<size_t>(pr.second, 1), 256);
+  }
+  return stg_upload(p, h, d, total);
 }
 
 // Per-call scratch bytes left after the persistent tables (a conservative
@@ -480,11 +520,14 @@ akv_status device_rotate(akv_pool* p, const std::vector<akv::RotItem>& items,
   if (layers.empty()) krs.push_back(p->rope_array());
   for (akv_pool* l : layers) krs.push_back(l->rope_array());
   ScratchCursor sc(p);
-  void *ditems, *ddeltas, *dkrs;
-  akv_status st = upload_array(p, sc, items.data(), items.size() * sizeof(akv::RotItem), &ditems);
-  if (st == AKV_OK) st = upload_array(p, sc, deltas.data(), deltas.size() * 4, &ddeltas);
-  if (st == AKV_OK) st = upload_array(p, sc, krs.data(), krs.size() * sizeof(uint16_t*), &dkrs);
+  void* dv[3];
+  akv_status st = upload_arrays(p, sc,
+                                {{items.data(), items.size() * sizeof(akv::RotItem)},
+                                 {deltas.data(), deltas.size() * 4},
+                                 {krs.data(), krs.size() * sizeof(uint16_t*)}},
+                                dv);
   if (st != AKV_OK) return st;
+  void *ditems = dv[0], *ddeltas = dv[1], *dkrs = dv[2];
   float* dtab = (float*)sc.take(deltas.size() * (size_t)p->L.d_rope * 4);
   if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
   hipError_t e = akv::launch_rot_table(p->stream, p->L.d_rope, (const int32_t*)ddeltas,
@@ -565,7 +608,7 @@ akv_status compact_seq(akv_pool* p, int32_t s) {
     r.toks.swap(keep);
     if (!r.in_evict) evict_push(p, pg);
   }
-  q.vis_ok = false;
+  q.stale();
   return device_move(p, mv);
 }
 
@@ -580,7 +623,7 @@ void drop_tokens(akv_pool* p, SeqRec& q, int32_t b, int32_t e) {
     r.nvis -= 1;
     if (r.nvis == 0 && pg != q.tail && !r.in_evict) evict_push(p, pg);
   }
-  q.vis_ok = false;
+  q.stale();
 }
 
 akv_status auto_compact(akv_pool* p, int32_t s) {
@@ -663,7 +706,7 @@ void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<int64_t>&
 void repos_commit(SeqRec& q, const std::vector<int64_t>& tot) {
   for (size_t t = 0; t < tot.size(); ++t)
     if (tot[t]) q.pos[t] = (int32_t)(q.pos[t] + tot[t]);
-  q.vis_ok = false;
+  q.stale();
 }
 
 // ---------------------------------------------------------------------------
@@ -715,14 +758,18 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
   const int64_t cu_share = total_cost / p->n_cu;
   const int64_t block_cap = std::max<int64_t>(2048, cu_share / 2);
 
+  // Items of one group (same segment, kv head and key split: the row tiles
+  // that read the same K/V) are contiguous in `all`; a group is its range.
   struct Group {
     int64_t cost;
-    std::vector<akv::AttnItem> items;
-    std::vector<int64_t> item_cost;
+    int32_t begin, end;
   };
+  std::vector<akv::AttnItem> all;
+  std::vector<int64_t> cost;
   std::vector<Group> groups;
   plan.comb.clear();
   int64_t part = 0;
+  std::vector<int64_t> tile_base;
   for (int32_t i = 0; i < n_segs; ++i) {
     const int32_t lq = segs[i].q_len;
     if (lq <= 0) continue;
@@ -740,7 +787,7 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
     ns = (int)std::min<int64_t>(ns, key_tiles);
     if (ns < 1) ns = 1;
     // partials of one kv head: row tile m's ns splits, each of the tile's rows
-    std::vector<int64_t> tile_base(ntile_rows, 0);
+    tile_base.assign(ntile_rows, 0);
     int64_t head_part_rows = 0;
     if (ns > 1)
       for (int64_t m = 0; m < ntile_rows; ++m) {
@@ -751,8 +798,7 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
       for (int sp = 0; sp < ns; ++sp) {
         const int64_t tb = key_tiles * sp / ns, te = key_tiles * (sp + 1) / ns;
         const int32_t kb = (int32_t)(tb * KT), ke = (int32_t)std::min<int64_t>(te * KT, lkv[i]);
-        Group gr;
-        gr.cost = 0;
+        Group gr{0, (int32_t)all.size(), 0};
         for (int64_t m = 0; m < ntile_rows; ++m) {
           const int32_t row0 = (int32_t)(m * RB);
           const int64_t last_row = std::min<int64_t>(row0 + RB, rows) - 1;
@@ -760,11 +806,12 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
           const int64_t keys = std::max<int64_t>(0, std::min<int64_t>(ke, lim_last + 1) - kb);
           int32_t pidx = -1;
           if (ns > 1) pidx = (int32_t)(part + tile_base[m] + sp * std::min<int64_t>(RB, rows - row0));
-          gr.items.push_back({i, h, row0, kb, ke, pidx});
-          gr.item_cost.push_back(keys + 64);  // + fixed cost of a block
+          all.push_back({i, h, row0, kb, ke, pidx});
+          cost.push_back(keys + 64);  // + fixed cost of a block
           gr.cost += keys + 64;
         }
-        groups.push_back(std::move(gr));
+        gr.end = (int32_t)all.size();
+        groups.push_back(gr);
       }
       if (ns > 1) {
         for (int64_t m = 0; m < ntile_rows; ++m)
@@ -780,26 +827,24 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
   // longest first, so the CUs of an XCD finish together.
   std::stable_sort(groups.begin(), groups.end(),
                    [](const Group& a, const Group& b) { return a.cost > b.cost; });
-  std::vector<std::vector<std::pair<int64_t, akv::AttnItem>>> xbins(kXcds);
+  std::vector<std::vector<int32_t>> xbins(kXcds);
   std::vector<int64_t> load(kXcds, 0);
-  for (auto& gr : groups) {
+  for (const Group& gr : groups) {
     int best = 0;
     for (int x = 1; x < kXcds; ++x)
       if (load[x] < load[best]) best = x;
     load[best] += gr.cost;
-    for (size_t k = 0; k < gr.items.size(); ++k) xbins[best].push_back({gr.item_cost[k], gr.items[k]});
-  }
-  std::vector<std::vector<akv::AttnItem>> bins(kXcds);
-  for (int x = 0; x < kXcds; ++x) {
-    std::stable_sort(xbins[x].begin(), xbins[x].end(),
-                     [](const auto& a, const auto& b) { return a.first > b.first; });
-    for (auto& ci : xbins[x]) bins[x].push_back(ci.second);
+    for (int32_t k = gr.begin; k < gr.end; ++k) xbins[best].push_back(k);
   }
   size_t depth = 0;
-  for (auto& b : bins) depth = std::max(depth, b.size());
+  for (int x = 0; x < kXcds; ++x) {
+    std::stable_sort(xbins[x].begin(), xbins[x].end(),
+                     [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
+    depth = std::max(depth, xbins[x].size());
+  }
   plan.items.assign(depth * kXcds, akv::AttnItem{-1, 0, 0, 0, 0, -1});
   for (int x = 0; x < kXcds; ++x)
-    for (size_t i = 0; i < bins[x].size(); ++i) plan.items[i * kXcds + x] = bins[x][i];
+    for (size_t i = 0; i < xbins[x].size(); ++i) plan.items[i * kXcds + x] = all[xbins[x][i]];
 }
 
 }  // namespace
@@ -945,7 +990,7 @@ akv_status akv_seq_release(akv_pool* p, int32_t s) {
   q->tail = -1;
   q->alive = false;
   q->vis.clear();
-  q->vis_ok = false;
+  q->stale();
   return AKV_OK;
 }
 
@@ -1037,6 +1082,68 @@ akv_status akv_seq_clone(akv_pool* p, int32_t src, int32_t first, int32_t n, int
     e = move_tokens(p, (const akv::MovePair*)dmv, m, delta != 0 ? dtab : nullptr);
     tm.done();
     return check_launch(e, "clone kernel launch");
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_append_batch(akv_pool* p, int32_t n_seqs, const int32_t* seqs, const int32_t* counts,
+                            const void* K, const void* K_pe, const void* V, const int32_t* pos) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    if (n_seqs < 0) return fail(AKV_EINVAL, "negative sequence count");
+    if (n_seqs == 0) return AKV_OK;
+    if (!seqs || !counts) return fail(AKV_EINVAL, "seqs and counts must be non-NULL");
+    const bool mla = p->L.d_nope > 0;
+    const bool none = !K && !K_pe && !V;
+    if (!none) {
+      if (!p->device) return fail(AKV_EINVAL, "a page-table-only pool takes no K/V data");
+      if (!K || !V || (mla != (K_pe != nullptr)))
+        return fail(AKV_EINVAL, "K and V (and K_pe exactly for MLA) must be given together");
+    }
+    // validate every entry; count pages with each sequence's tail room as the
+    // entries before it leave it
+    const int64_t S = p->L.page_size;
+    std::unordered_map<int32_t, std::pair<int64_t, int64_t>> st_of;   // seq -> (room, tokens)
+    int64_t total = 0, pages = 0;
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      SeqRec* q;
+      akv_status st = get_seq(p, seqs[i], &q);
+      if (st != AKV_OK) return st;
+      if (counts[i] < 0) return fail(AKV_EINVAL, "entry %d: negative token count", i);
+      auto it = st_of.find(seqs[i]);
+      if (it == st_of.end())
+        it = st_of.emplace(seqs[i], std::make_pair(q->tail >= 0 ? S - p->pages[q->tail].filled : 0,
+                                                   (int64_t)q->slot.size())).first;
+      int64_t& room = it->second.first;
+      int64_t& len = it->second.second;
+      const int64_t n = counts[i];
+      const int64_t extra = std::max<int64_t>(0, n - room);
+      pages += (extra + S - 1) / S;
+      room = n <= room ? room - n : (S - extra % S) % S;
+      len += n;
+      if (len > kInt32Max) return fail(AKV_ERANGE, "sequence %d too long", seqs[i]);
+      total += n;
+      if (total > kInt32Max) return fail(AKV_ERANGE, "too many tokens in one call");
+    }
+    if (total == 0) return AKV_OK;
+    if (!pos) return fail(AKV_EINVAL, "pos is NULL");
+    for (int64_t t = 0; t < total; ++t)
+      if (pos[t] < 0) return fail(AKV_ERANGE, "position %d of token %lld is negative", pos[t], (long long)t);
+    if (pages > available(p))
+      return fail(AKV_ENOMEM, "pool exhausted: %lld pages needed, %lld available", (long long)pages,
+                  (long long)available(p));
+    if (!none) {
+      akv_status st = scratch_fits(p, (size_t)total * 4 + 256);
+      if (st != AKV_OK) return st;
+    }
+    std::vector<int32_t> slots((size_t)total);
+    int64_t off = 0;
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      place_tokens(p, seqs[i], counts[i], pos + off, slots.data() + off);
+      off += counts[i];
+    }
+    return device_append(p, slots, K, K_pe, V);
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
   }
@@ -1295,14 +1402,17 @@ akv_status akv_seq_visible(akv_pool* p, int32_t s, const akv_span* mask, int32_t
     st = check_spans(mask, n_mask, (int32_t)q->slot.size());
     if (st != AKV_OK) return st;
     const std::vector<int32_t>& vis = visible(*q);
-    std::vector<uint8_t> hide;
+    std::vector<akv_extent> masked;
     if (n_mask > 0) {
-      hide.assign(q->slot.size(), 0);
+      std::vector<uint8_t> hide(q->slot.size(), 0);
       for (int32_t i = 0; i < n_mask; ++i)
         std::fill(hide.begin() + mask[i].begin, hide.begin() + mask[i].end, 1);
+      build_extents(p, *q, vis, &hide, masked);
+    } else if (!q->ext_ok) {
+      build_extents(p, *q, vis, nullptr, q->ext);
+      q->ext_ok = true;
     }
-    std::vector<akv_extent> ex;
-    build_extents(p, *q, vis, n_mask > 0 ? &hide : nullptr, ex);
+    const std::vector<akv_extent>& ex = n_mask > 0 ? masked : q->ext;
     *n_out = (int32_t)ex.size();
     if ((int32_t)ex.size() > cap) return fail(AKV_ERANGE, "%zu extents, cap %d", ex.size(), cap);
     if (!ex.empty()) {
@@ -1310,6 +1420,50 @@ akv_status akv_seq_visible(akv_pool* p, int32_t s, const akv_span* mask, int32_t
       std::memcpy(out, ex.data(), ex.size() * sizeof(akv_extent));
     }
     return AKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_seq_attention(akv_pool* p, const void* Q, int32_t n_q_tokens, const akv_seq_segment* segs,
+                             int32_t n_segs, const akv_span* masks, int32_t n_masks, float scale, void* out) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    if (n_segs < 0 || n_masks < 0) return fail(AKV_EINVAL, "negative count");
+    if ((n_segs > 0 && !segs) || (n_masks > 0 && !masks)) return fail(AKV_EINVAL, "segments / masks are NULL");
+    std::vector<akv_segment> rows((size_t)n_segs);
+    std::vector<akv_extent> lists;
+    std::vector<akv_extent> masked;
+    for (int32_t i = 0; i < n_segs; ++i) {
+      const akv_seq_segment& sg = segs[i];
+      SeqRec* q;
+      akv_status st = get_seq(p, sg.seq, &q);
+      if (st != AKV_OK) return st;
+      if (sg.mask_len < 0 || sg.mask_begin < 0 || (int64_t)sg.mask_begin + sg.mask_len > n_masks)
+        return fail(AKV_EINVAL, "segment %d: mask spans outside 0..%d", i, n_masks);
+      const akv_span* m = masks ? masks + sg.mask_begin : nullptr;
+      st = check_spans(m, sg.mask_len, (int32_t)q->slot.size());
+      if (st != AKV_OK) return st;
+      const std::vector<int32_t>& vis = visible(*q);
+      const std::vector<akv_extent>* ex;
+      if (sg.mask_len > 0) {
+        std::vector<uint8_t> hide(q->slot.size(), 0);
+        for (int32_t k = 0; k < sg.mask_len; ++k) std::fill(hide.begin() + m[k].begin, hide.begin() + m[k].end, 1);
+        build_extents(p, *q, vis, &hide, masked);
+        ex = &masked;
+      } else {
+        if (!q->ext_ok) {
+          build_extents(p, *q, vis, nullptr, q->ext);
+          q->ext_ok = true;
+        }
+        ex = &q->ext;
+      }
+      if (lists.size() + ex->size() > (size_t)kInt32Max) return fail(AKV_ERANGE, "page lists too long");
+      rows[i] = {sg.q_begin, sg.q_len, (int32_t)lists.size(), (int32_t)ex->size()};
+      lists.insert(lists.end(), ex->begin(), ex->end());
+    }
+    return akv_segment_attention(p, Q, n_q_tokens, rows.data(), n_segs, lists.data(), (int32_t)lists.size(), scale,
+                                 out);
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
   }
@@ -1387,15 +1541,17 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
       }
     }
     ScratchCursor sc(p);
-    void *dsegs, *ditems, *dcomb = nullptr, *dex, *doff;
-    akv_status st = upload_array(p, sc, plan.segs.data(), plan.segs.size() * sizeof(akv::AttnSeg), &dsegs);
-    if (st == AKV_OK)
-      st = upload_array(p, sc, plan.items.data(), plan.items.size() * sizeof(akv::AttnItem), &ditems);
-    if (st == AKV_OK && !plan.comb.empty())
-      st = upload_array(p, sc, plan.comb.data(), plan.comb.size() * sizeof(akv::CombItem), &dcomb);
-    if (st == AKV_OK) st = upload_array(p, sc, ex_used.data(), ex_used.size() * sizeof(akv::Extent), &dex);
-    if (st == AKV_OK) st = upload_array(p, sc, ex_off.data(), ex_off.size() * 4, &doff);
+    void* dv[5];
+    akv_status st = upload_arrays(p, sc,
+                                  {{plan.segs.data(), plan.segs.size() * sizeof(akv::AttnSeg)},
+                                   {plan.items.data(), plan.items.size() * sizeof(akv::AttnItem)},
+                                   {plan.comb.data(), plan.comb.size() * sizeof(akv::CombItem)},
+                                   {ex_used.data(), ex_used.size() * sizeof(akv::Extent)},
+                                   {ex_off.data(), ex_off.size() * 4}},
+                                  dv);
     if (st != AKV_OK) return st;
+    void *dsegs = dv[0], *ditems = dv[1], *dcomb = plan.comb.empty() ? nullptr : dv[2], *dex = dv[3],
+         *doff = dv[4];
     int32_t* dslots = (int32_t*)sc.take((size_t)std::max<int64_t>(total, 1) * 4);
     float* part_o = nullptr;
     float* part_ml = nullptr;

@@ -33,6 +33,14 @@ def apply_op(pool: Pool, op) -> Optional[np.ndarray]:
         pool.seq_create()
     elif isinstance(op, W.Append):
         pool.append(op.seq, op.pos, _f64(op.k), _f64(op.kpe), _f64(op.v))
+    elif isinstance(op, W.AppendBatch):
+        # the same as one append per entry, in entry order
+        off = 0
+        for s, n in zip(op.seqs, op.counts):
+            sl = slice(off, off + int(n))
+            pool.append(int(s), op.pos[sl], _f64(op.k[sl]), _f64(op.kpe[sl]) if op.kpe is not None else None,
+                        _f64(op.v[sl]))
+            off += int(n)
     elif isinstance(op, W.Drop):
         pool.drop(op.seq, op.spans)
     elif isinstance(op, W.Repos):

@@ -49,6 +49,11 @@ def apply_op(pool: akv.Pool, op, keep=None):
         kpe = dev_bf16(op.kpe) if op.kpe is not None else None
         keep += [k, v, kpe]
         pool.append(op.seq, op.pos, k, kpe, v)
+    elif isinstance(op, W.AppendBatch):
+        k, v = dev_bf16(op.k), dev_bf16(op.v)
+        kpe = dev_bf16(op.kpe) if op.kpe is not None else None
+        keep += [k, v, kpe]
+        pool.append_batch(op.seqs, op.counts, op.pos, k, kpe, v)
     elif isinstance(op, W.Drop):
         pool.drop(op.seq, op.spans)
     elif isinstance(op, W.Repos):

@@ -369,6 +369,24 @@ def test_c4_batched_sampled():
     _sampled_parity(W.c4_batched(0), n_rows=6)
 
 
+@pytest.mark.parametrize("make", [lambda: W.c1_tiny(0, "canonical"), lambda: W.fuzz_small(3, head_dims=(64, 128)),
+                                  lambda: W.decode_batch(5, n_req=12, ctx_lo=1, ctx_hi=3000, q_len=2)])
+def test_seq_attention_equals_segment_attention(make):
+    """Attention over sequence ids (lists built inside the library) gives the
+    same bits as the same call with caller-built page lists."""
+    wl = make()
+    _say(f"[gpu] seq attention vs segment attention: {wl.name}")
+    pool, outs = D.run(wl)
+    atts = [o for o in wl.ops if isinstance(o, W.Attention)]
+    for op, o in zip(atts, outs):
+        q = D.dev_bf16(op.q)
+        got = pool.seq_attention(q, [(sg.seq, sg.q_begin, sg.q_len, sg.mask_spans if len(sg.mask_spans) else None)
+                                     for sg in op.segments], op.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), o["out"].view(torch.int16))
+    pool.close()
+
+
 def test_retrigger_64k_sampled():
     _sampled_parity(W.retrigger(0), n_rows=12)
 

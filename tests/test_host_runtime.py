@@ -81,6 +81,9 @@ def _replay(wl: W.Workload, check_every_op=True):
         elif isinstance(op, W.Append):
             hp.append(op.seq, op.pos)
             oracle.apply_op(op_pool, op)
+        elif isinstance(op, W.AppendBatch):
+            hp.append_batch(op.seqs, op.counts, op.pos)
+            oracle.apply_op(op_pool, op)
         elif isinstance(op, W.Drop):
             hp.drop(op.seq, op.spans)
             oracle.apply_op(op_pool, op)
@@ -279,6 +282,69 @@ def test_retrigger_clone_page_tables_bit_exact(seed, mla, pre_b):
     """Positional versions: the clone's slots, positions and flags, and both
     sequences' page-table images, equal the oracle's after every op."""
     _replay(W.retrigger(seed, ctx=4096, pre_a=256, nq=64, n_turns=8, n_recent=2, pre_b=pre_b, mla=mla))
+
+
+@pytest.mark.parametrize("seed,lq", [(0, 1), (1, 3)])
+def test_decode_batch_page_tables_bit_exact(seed, lq):
+    """Histories with drops and repos, then one batched append of q_len tokens
+    per request: tables bit-exact against the oracle's per-entry appends."""
+    _replay(W.decode_batch(seed, n_req=10, ctx_lo=1, ctx_hi=1500, q_len=lq))
+
+
+def test_append_batch_equals_sequential_appends_and_is_atomic():
+    rng = np.random.default_rng(21)
+    lay = W.Layout(4, 2, 0, 16, 16, 8, 60)
+    order = rng.permutation(60)
+    a, b = _host_pool(lay, order), _host_pool(lay, order)
+    for p in (a, b):
+        for _ in range(4):
+            p.seq_create()
+    for trial in range(6):
+        m = int(rng.integers(1, 7))
+        seqs = rng.integers(0, 4, m)                   # repeats allowed
+        counts = rng.integers(0, 9, m)
+        pos = rng.integers(0, 1000, int(counts.sum()))
+        a.append_batch(seqs, counts, pos)
+        off = 0
+        for s, n in zip(seqs, counts):
+            b.append(int(s), pos[off:off + n])
+            off += n
+        for s in range(4):
+            for x, y in zip(a.tokens(s), b.tokens(s)):
+                np.testing.assert_array_equal(x, y)
+        assert [q.tolist() for q in a.queues()] == [q.tolist() for q in b.queues()]
+    before = [_state(a, s) for s in range(4)]
+    free = len(a.queues()[0])
+    cases = [
+        (([0, 1], [2, -1], [1]), akv.AKV_EINVAL),
+        (([0, 9], [1, 1], [1, 2]), akv.AKV_EINVAL),
+        (([0, 1], [1, 1], [1, -2]), akv.AKV_ERANGE),
+        (([2, 2, 3], [8 * free, 8, 1], list(range(8 * free + 9))), akv.AKV_ENOMEM),
+    ]
+    for (sq, cn, ps), code in cases:
+        with pytest.raises(akv.AkvError) as ei:
+            a.append_batch(sq, cn, ps)
+        assert ei.value.status == code, (sq, cn, ei.value)
+        for s in range(4):
+            _same(_state(a, s), before[s])
+    a.seq_release(3)
+    with pytest.raises(akv.AkvError) as ei:
+        a.append_batch([0, 3], [1, 1], [5, 6])
+    assert ei.value.status == akv.AKV_ESTATE
+    _same(list(a.tokens(0)), before[0][:3])     # seq 0 untouched (the release freed seq 3's pages)
+
+
+def test_seq_attention_validates_before_the_pool_state_check():
+    hp = akv.Pool(4, 2, 0, 16, 16, 4, 20, device=False)
+    s = hp.seq_create()
+    hp.append(s, np.arange(30))
+    q = torch.zeros((4, 4, 16), dtype=torch.bfloat16)
+    out = torch.zeros((4, 4, 16), dtype=torch.bfloat16)
+    for segs, code in [([(5, 0, 1, None)], akv.AKV_EINVAL), ([(s, 0, 1, [[3, 40]])], akv.AKV_ERANGE),
+                       ([(s, 0, 1, [[5, 2]])], akv.AKV_EINVAL), ([(s, 0, 1, None)], akv.AKV_ESTATE)]:
+        with pytest.raises(akv.AkvError) as ei:
+            hp.seq_attention(q, segs, out=out)
+        assert ei.value.status == code, (segs, ei.value)
 
 
 def test_clone_skips_dropped_and_refusals_leave_no_trace():

@@ -35,7 +35,7 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "Layout", "SeqCreate", "Append", "Drop", "Repos", "Splice", "Compact", "Clone",
+    "Layout", "SeqCreate", "Append", "AppendBatch", "Drop", "Repos", "Splice", "Compact", "Clone",
     "Segment", "Attention", "Workload", "to_bf16", "bf16_to_f64",
     "c1_tiny", "c2_64k", "c3_mla", "c4_batched", "c5_128k", "decode_batch", "retrigger", "fuzz_small",
     "CONFIGS", "make",
@@ -102,6 +102,16 @@ class Append:
     k: np.ndarray        # uint16 bf16: GQA full K [n,Hkv,d_rope]; MLA K_nope [n,Hkv,d_nope]
     kpe: Optional[np.ndarray]  # MLA only: [n, n_rope_heads, d_rope]
     v: np.ndarray        # uint16 bf16 [n, Hkv, d_v]
+
+
+@dataclass
+class AppendBatch:
+    seqs: np.ndarray     # int32 [m]: entry i appends counts[i] tokens to seqs[i]
+    counts: np.ndarray   # int32 [m]
+    pos: np.ndarray      # int32 [sum(counts)], entries concatenated in order
+    k: np.ndarray        # as Append, rows of all entries concatenated
+    kpe: Optional[np.ndarray]
+    v: np.ndarray
 
 
 @dataclass
@@ -527,12 +537,15 @@ def decode_batch(seed: int = 0, n_req: int = 48, ctx_lo: int = 2048, ctx_hi: int
             rs, rd = _survivor_runs(q["ctx"], q["dropped"])
             if len(rs):
                 wl.ops.append(Repos(r, rs, rd))
-    segs = []
+    segs, news = [], []
     wl.notes["step_from"] = len(wl.ops)     # one decode step: the new tokens and attention
     for r, q in enumerate(reqs):
         h = q["ctx"] - sum(e - b for b, e in q["dropped"])
-        wl.ops.append(_append_op(rng, lay, r, np.arange(h, h + q_len, dtype=np.int32)))
+        news.append(_append_op(rng, lay, r, np.arange(h, h + q_len, dtype=np.int32)))
         segs.append(Segment(r, r * q_len, q_len, np.zeros((0, 2), np.int32)))
+    wl.ops.append(AppendBatch(np.arange(n_req, dtype=np.int32), np.full(n_req, q_len, np.int32),
+                              np.concatenate([a.pos for a in news]), np.concatenate([a.k for a in news]),
+                              None, np.concatenate([a.v for a in news])))
     qarr = _normal_bf16(rng, (n_req * q_len, lay.n_q_heads, lay.d_qk), scale=1.0 / 8.0)
     wl.ops.append(Attention(qarr, segs))
     wl.notes.update(requests=reqs)
