@@ -360,7 +360,7 @@ def main():
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "decode", "retrigger"],
                     help="c2 (default) is the headline 64K step; the others print one record each")
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=16, help="oracle query rows per segment")
@@ -443,6 +443,8 @@ def main():
         segs, page_lists = step(seqs[c])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    pct = {k: [round(float(x), 5) for x in np.percentile(pool.timing_samples(k), [10, 50, 90])]
+           for k in ("attention", "rotate")}
     kt = {k: pool.timing_read(k) for k in akv.KERNEL_KINDS}
 
     flops, pairs = attention_flops(L, segs, page_lists)
@@ -492,12 +494,12 @@ def main():
                      "traffic": counted_traffic("attention"),
                      "kernel": attention_kernel_name(L), "flop_per_launch": flops,
                      "kv_bytes_per_launch": kv_bytes,
-                     "avg_launch_ms": round(attn_ms, 5)},
+                     "avg_launch_ms": round(attn_ms, 5), "launch_ms_p10_p50_p90": pct["attention"]},
         "roofline_repos": {"bound": "hbm", "achieved": round(rot_gbps, 1), "peak": PEAK_HBM_GBPS,
                            "unit": "GB/s", "frac": round(rot_gbps / PEAK_HBM_GBPS, 4),
                            "traffic": counted_traffic("rotate"),
                            "kernel": "k_rotate", "bytes_per_launch": rep_bytes,
-                           "avg_launch_ms": round(rot_ms, 5)},
+                           "avg_launch_ms": round(rot_ms, 5), "launch_ms_p10_p50_p90": pct["rotate"]},
         "roofline_repos_layers": layers_rec,
         "roofline_compact": comp_rec,
         "kernels_ms_per_step": {k: round(v[0] / max(args.steps, 1), 5) for k, v in kt.items()},

@@ -284,6 +284,10 @@ enum { AKV_K_APPEND = 0, AKV_K_ROTATE = 1, AKV_K_COMPACT = 2, AKV_K_EXPAND = 3,
        AKV_K_ATTN = 4, AKV_K_COMBINE = 5, AKV_K_CLONE = 6, AKV_K_KINDS = 7 };
 akv_status akv_timing_enable(akv_pool* pool, int32_t enable);
 akv_status akv_timing_read(akv_pool* pool, int32_t kind, double* total_ms, int32_t* count);
+/* The individual launch durations (ms) behind the next akv_timing_read of
+ * the same kind, in launch order; *n_out gets their count (AKV_ERANGE when it
+ * exceeds cap).  Does not clear them. */
+akv_status akv_timing_samples(akv_pool* pool, int32_t kind, float* ms, int32_t cap, int32_t* n_out);
 
 akv_status akv_sync(akv_pool* pool);       /* wait for the pool's stream */
 const char* akv_last_error(void);          /* thread-local text of the last failure */

@@ -70,6 +70,7 @@ SYMBOLS = {
     "akv_repos_plan": [_P, _I, _IP, _IP, _I, _IP, _IP, _I, _IP],
     "akv_timing_enable": [_P, _I],
     "akv_timing_read": [_P, _I, ctypes.POINTER(ctypes.c_double), _IP],
+    "akv_timing_samples": [_P, _I, ctypes.POINTER(ctypes.c_float), _I, _IP],
     "akv_sync": [_P],
     "akv_last_error": [],
 }
@@ -346,6 +347,18 @@ class Pool:
     # -- timing / sync -------------------------------------------------------------
     def timing_enable(self, on: bool = True) -> None:
         _check(lib().akv_timing_enable(self._h, int(on)))
+
+    def timing_samples(self, kind: str) -> np.ndarray:
+        """Each launch's milliseconds since the last timing_read of this kind."""
+        n = ctypes.c_int32()
+        st = lib().akv_timing_samples(self._h, KERNEL_KINDS[kind], None, 0, ctypes.byref(n))
+        if st not in (AKV_OK, AKV_ERANGE):
+            _check(st)
+        out = np.zeros(max(n.value, 1), np.float32)
+        _check(lib().akv_timing_samples(self._h, KERNEL_KINDS[kind],
+                                        out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), len(out),
+                                        ctypes.byref(n)))
+        return out[: n.value]
 
     def timing_read(self, kind: str):
         ms, cnt = ctypes.c_double(), ctypes.c_int32()

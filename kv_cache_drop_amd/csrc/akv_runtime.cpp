@@ -121,6 +121,7 @@ struct akv_pool {
   std::vector<hipEvent_t> ev_spare;
   double t_ms[AKV_K_KINDS] = {};
   int t_cnt[AKV_K_KINDS] = {};
+  std::vector<float> t_each[AKV_K_KINDS];   // each launch's milliseconds since the last read
 
   int rope_heads() const { return (L.d_nope > 0 && !L.kpe_per_head) ? 1 : L.n_kv_heads; }
   uint16_t* rope_array() const { return L.d_nope > 0 ? kpe : k; }
@@ -249,6 +250,7 @@ akv_status timing_collect(akv_pool* p) {
     if (hipEventElapsedTime(&ms, t.a, t.b) == hipSuccess) {
       p->t_ms[t.kind] += ms;
       p->t_cnt[t.kind] += 1;
+      p->t_each[t.kind].push_back(ms);
     }
     p->ev_spare.push_back(t.a);
     p->ev_spare.push_back(t.b);
@@ -1671,6 +1673,22 @@ akv_status akv_timing_read(akv_pool* p, int32_t kind, double* total_ms, int32_t*
   if (count) *count = p->t_cnt[kind];
   p->t_ms[kind] = 0;
   p->t_cnt[kind] = 0;
+  p->t_each[kind].clear();
+  return AKV_OK;
+}
+
+akv_status akv_timing_samples(akv_pool* p, int32_t kind, float* ms, int32_t cap, int32_t* n_out) {
+  if (!p || !n_out) return fail(AKV_EINVAL, "NULL argument");
+  if (kind < 0 || kind >= AKV_K_KINDS) return fail(AKV_EINVAL, "bad kernel kind %d", kind);
+  akv_status st = timing_collect(p);
+  if (st != AKV_OK) return st;
+  const std::vector<float>& v = p->t_each[kind];
+  *n_out = (int32_t)v.size();
+  if ((int32_t)v.size() > cap) return fail(AKV_ERANGE, "%zu samples, cap %d", v.size(), cap);
+  if (!v.empty()) {
+    if (!ms) return fail(AKV_EINVAL, "ms is NULL");
+    std::memcpy(ms, v.data(), v.size() * sizeof(float));
+  }
   return AKV_OK;
 }
 
