@@ -208,7 +208,8 @@ def run_config(args) -> dict:
     import workloads as W
 
     gens = {"c1": lambda s: W.c1_tiny(s, "canonical"), "c3": W.c3_mla, "c4": W.c4_batched, "c5": W.c5_128k,
-            "decode": W.decode_batch, "retrigger": W.retrigger}
+            "decode": W.decode_batch, "decode_fused": lambda s: W.decode_batch(s, deferred=True),
+            "retrigger": W.retrigger}
     wl = gens[args.config](args.seed)
     L = wl.layout
     ops = list(wl.ops)
@@ -288,6 +289,8 @@ def run_config(args) -> dict:
                     clone_bytes += 2 * row_bytes * int((dr == 0).sum())
             grp = L.n_q_heads // L.n_kv_heads
             kern = attention_kernel_name(L, max(sg.q_len * grp for op in lists for sg in op.segments))
+            if any(isinstance(o, W.Repos) and o.deferred for o in ops) and kern == "k_decode_attn":
+                kern = "k_decode_attn<rotating>"
         pool.close()
         del pool, keep
     ms_step = float(np.median(walls)) * 1e3
@@ -311,7 +314,7 @@ def run_config(args) -> dict:
                      "avg_launch_ms": round(attn_ms, 5)},
         "kernels_ms_per_step": {k: round(v[0] / max(args.steps, 1), 5) for k, v in tot.items()},
     }
-    if args.config == "decode":
+    if args.config in ("decode", "decode_fused"):
         # one query row per kv-head group: the launch streams the visible K/V once
         hbm_gbps = kv_bytes / (attn_ms * 1e-3) / 1e9
         rec["roofline"] = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -349,6 +352,8 @@ CONFIG_NAMES = {
                  "(512-token preamble, the 64K trace, older tools dropped, survivors repositioned) and request B "
                  "(the same trace after a preamble of another length) cloned from A's state with keys turned by "
                  "the offset change; 512 queries each in one launch",
+    "decode_fused": "the decode step of 48 requests of 2K-16K tokens whose survivors' repos was deferred: the "
+                    "keys stay at their old positions and the decode kernel turns them as it reads them",
     "decode": "48 requests of 2K-16K tokens on the 64K layer shape (32 q / 8 kv heads, head_dim 128, page 16), "
               "dropped and repositioned at set-up; the step appends one token per request and runs 48 one-query "
               "segments in one launch",
@@ -357,7 +362,7 @@ CONFIG_NAMES = {
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "decode", "retrigger"],
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "decode", "decode_fused", "retrigger"],
                     help="c2 (default) is the headline 64K step; the others print one record each")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)

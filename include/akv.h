@@ -169,6 +169,25 @@ akv_status akv_compact(akv_pool* pool, int32_t seq, int32_t force);
 akv_status akv_repos(akv_pool* pool, int32_t seq, const akv_span* spans, const int32_t* delta,
                      int32_t n_spans);
 
+/* deferred repos (the fused rotation of [AKV-blog] section 4 and rule of
+ * thumb 2: keys stay where they are and are turned where they are read):
+ * the same validation, positions and errors as akv_repos, but no key is
+ * rewritten; each token records the rotation its stored key still owes.
+ * akv_seq_attention applies owed rotations inside the decode kernel (with
+ * the rotation table and fp32 formula of akv_repos, so the results equal
+ * repos-then-attention bit for bit) and rotates the keys in place first for
+ * other launches; akv_segment_attention reads keys as stored.  Later repos
+ * calls, compaction, splices and clones keep each token's debt. */
+akv_status akv_repos_deferred(akv_pool* pool, int32_t seq, const akv_span* spans, const int32_t* delta,
+                              int32_t n_spans);
+/* Rotate the sequence's visible keys by what they owe, in place (one
+ * launch), as akv_repos would have; the debt is then 0.  Errors: AKV_EINVAL,
+ * AKV_ESTATE, AKV_ENOMEM (scratch). */
+akv_status akv_materialize(akv_pool* pool, int32_t seq);
+/* Owed rotation of tokens first .. first+n-1 (position minus the position
+ * their stored key encodes). */
+akv_status akv_seq_lag(akv_pool* pool, int32_t seq, int32_t first, int32_t n, int32_t* lag);
+
 /* repos over the layers of a model in one launch (the same operation as
  * akv_repos, applied to every pool in pools[0..n_pools)).  A model keeps one
  * pool per layer with the same op history, so the layers' page tables and

@@ -58,6 +58,9 @@ SYMBOLS = {
     "akv_compact": [_P, _I, _I],
     "akv_repos": [_P, _I, _IP, _IP, _I],
     "akv_repos_layers": [ctypes.POINTER(_P), _I, _I, _IP, _IP, _I],
+    "akv_repos_deferred": [_P, _I, _IP, _IP, _I],
+    "akv_materialize": [_P, _I],
+    "akv_seq_lag": [_P, _I, _I, _I, _IP],
     "akv_splice": [_P, _I, _IP, _IP, _I, _P, _P, _P, _IP],
     "akv_seq_clone": [_P, _I, _I, _I, _I, _I],
     "akv_append_batch": [_P, _I, _IP, _IP, _P, _P, _P, _IP],
@@ -233,6 +236,22 @@ class Pool:
         sp = _i32(spans).reshape(-1, 2)
         dl = _i32(deltas).reshape(-1)
         _check(lib().akv_repos(self._h, seq, _ptr(sp), _ptr(dl), len(sp)))
+
+    def repos_deferred(self, seq: int, spans, deltas) -> None:
+        """repos without rewriting keys: positions move, keys owe the rotation
+        (akv_repos_deferred)."""
+        sp = _i32(spans).reshape(-1, 2)
+        dl = _i32(deltas).reshape(-1)
+        _check(lib().akv_repos_deferred(self._h, seq, _ptr(sp), _ptr(dl), len(sp)))
+
+    def materialize(self, seq: int) -> None:
+        _check(lib().akv_materialize(self._h, seq))
+
+    def lag(self, seq: int) -> np.ndarray:
+        n, _, _ = self.info(seq)
+        out = np.zeros(max(n, 1), np.int32)
+        _check(lib().akv_seq_lag(self._h, seq, 0, n, _ptr(out)))
+        return out[:n]
 
     def clone(self, src: int, first: int, n: int, dst: int, delta: int) -> None:
         """Positional version: append src's retained tokens [first, first+n)

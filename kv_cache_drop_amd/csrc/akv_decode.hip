@@ -25,6 +25,7 @@
 // prefill kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -60,6 +61,34 @@ __device__ __forceinline__ unsigned pk_bf2(float a, float b) {
   return __builtin_bit_cast(unsigned, v);
 }
 
+// Key rotation in registers, with the fp32 formula of the in-place repos:
+// pair (x, y) -> (x cos - y sin, x sin + y cos), rounded once to bf16.
+// Interleaved pairing: word e of w holds pair (x, y) with cos / sin cs[e],
+// sn[e].
+__device__ __forceinline__ void turn_interleaved(u32x4_t& w, const f32x4_t& cs, const f32x4_t& sn) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x = __uint_as_float(w[e] << 16), y = __uint_as_float(w[e] & 0xffff0000u);
+    w[e] = pk_bf2(fmaf(x, cs[e], -y * sn[e]), fmaf(x, sn[e], y * cs[e]));
+  }
+}
+
+// Half-split pairing: xw holds the first elements of 8 pairs, yw their
+// second elements; cos / sin of the 8 pairs in (c0, c1), (s0, s1).
+__device__ __forceinline__ void turn_half(u32x4_t& xw, u32x4_t& yw, const f32x4_t& c0, const f32x4_t& c1,
+                                          const f32x4_t& s0, const f32x4_t& s1) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float cA = e < 2 ? c0[2 * e] : c1[2 * e - 4], cB = e < 2 ? c0[2 * e + 1] : c1[2 * e - 3];
+    const float sA = e < 2 ? s0[2 * e] : s1[2 * e - 4], sB = e < 2 ? s0[2 * e + 1] : s1[2 * e - 3];
+    const float x0 = __uint_as_float(xw[e] << 16), x1 = __uint_as_float(xw[e] & 0xffff0000u);
+    const float y0 = __uint_as_float(yw[e] << 16), y1 = __uint_as_float(yw[e] & 0xffff0000u);
+    xw[e] = pk_bf2(fmaf(x0, cA, -y0 * sA), fmaf(x1, cB, -y1 * sB));
+    yw[e] = pk_bf2(fmaf(x0, sA, y0 * cA), fmaf(x1, sB, y1 * cB));
+  }
+}
+
+template <bool ROT>
 __global__ __launch_bounds__(64 * DEC_WAVES, 2) void k_decode_attn(AttnArgs a) {
   // per wave: its staged V tile; after the key loop the same space holds the
   // waves' (m, l, O) for the merge
@@ -113,6 +142,16 @@ __global__ __launch_bounds__(64 * DEC_WAVES, 2) void k_decode_attn(AttnArgs a) {
     const int k = it.k_begin + (w + DEC_WAVES * j) * DEC_KT + (lane & 31);
     return slots[min(k, k_clamp)];
   };
+  // owed rotation (table row, or -1) of key `lane` of local tile j
+  const int32_t* __restrict__ kdidx = ROT ? a.key_didx + sg.list_off : nullptr;
+  auto didx_of = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (ROT) {
+      const int k = it.k_begin + (w + DEC_WAVES * j) * DEC_KT + (lane & 31);
+      return kdidx[min(k, k_clamp)];
+    } else {
+      return -1;
+    }
+  };
   // K and V rows of the tile whose slots `sv` holds: load b covers keys
   // 4b .. 4b+3, lane l taking chunk l % 16 of key 4b + l / 16, so each load
   // instruction reads whole 256-byte rows
@@ -135,7 +174,30 @@ __global__ __launch_bounds__(64 * DEC_WAVES, 2) void k_decode_attn(AttnArgs a) {
   // first half of a tile: K and V rows into this wave's LDS tile (the
   // tile's registers are free afterwards), then S^T of the two 16-key blocks
   // from K fragments (lane: key 16kb + l%16, chunk 4c + g)
-  auto tile_front = [&](const u32x4_t (&kr)[8], const u32x4_t (&vr)[8], f32x4_t (&s)[2])
+  // A key stored at an earlier position (deferred repos) is turned to its
+  // own position in the lane's fragments, with the table row and the fp32
+  // formula of the in-place repos, so the scores equal those of keys that
+  // repos had rotated.  Fragment c of key 16kb + l%16 holds d = 32c + 8g ..
+  // +7: interleaved pairs 16c + 4g .. +3; half-split pairs 32c + 8g .. +7 for
+  // c < 2, whose second elements are fragment c + 2 of the same lane.
+  auto turn_frags = [&](u32x4_t (&kf)[4], int dk) __attribute__((always_inline)) {
+    if (dk < 0) return;
+    const float* row = a.rot_table + (size_t)dk * DEC_D;
+    if (a.rot_pairing == 0) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        turn_interleaved(kf[c], *(const f32x4_t*)(row + 16 * c + 4 * g),
+                         *(const f32x4_t*)(row + DEC_D / 2 + 16 * c + 4 * g));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float* hr = row + 32 * c + 8 * g;
+        turn_half(kf[c], kf[c + 2], *(const f32x4_t*)hr, *(const f32x4_t*)(hr + 4),
+                  *(const f32x4_t*)(hr + DEC_D / 2), *(const f32x4_t*)(hr + DEC_D / 2 + 4));
+      }
+    }
+  };
+  auto tile_front = [&](const u32x4_t (&kr)[8], const u32x4_t (&vr)[8], f32x4_t (&s)[2], int dv)
       __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -147,12 +209,15 @@ __global__ __launch_bounds__(64 * DEC_WAVES, 2) void k_decode_attn(AttnArgs a) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      u32x4_t kf[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        kf[c] = *(const u32x4_t DEC_LDS*)(kl + (16 * kb + i16) * DEC_KROW + 16 * (4 * c + g));
+      if constexpr (ROT) turn_frags(kf, __shfl(dv, 16 * kb + i16));
       s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8_t kf = *(const bf16x8_t DEC_LDS*)(kl + (16 * kb + i16) * DEC_KROW + 16 * (4 * c + g));
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], s[kb], 0, 0, 0);
-      }
+      for (int c = 0; c < 4; ++c)
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[c]), qf[c], s[kb], 0, 0, 0);
     }
   };
   // second half: mask, softmax, O^T += V^T P^T
@@ -211,6 +276,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES, 2) void k_decode_attn(AttnArgs a) {
   // waits are exact counts.
   u32x4_t kA[8], vA[8], kB[8], vB[8];
   int sA = slot_of(0), sB = slot_of(1);
+  int dA = didx_of(0), dB = didx_of(1);
   load_tile(sA, kA, vA);
   sA = slot_of(2);
   load_tile(sB, kB, vB);
@@ -219,12 +285,14 @@ __global__ __launch_bounds__(64 * DEC_WAVES, 2) void k_decode_attn(AttnArgs a) {
   const int n_pairs = (n_loc + 1) / 2;
   for (int pj = 0; pj < n_pairs; ++pj) {
     const int j = 2 * pj;
-    tile_front(kA, vA, s);
+    tile_front(kA, vA, s, dA);
     load_tile(sA, kA, vA);
+    dA = didx_of(j + 2);
     sA = slot_of(j + 4);
     tile_back(j, s);
-    tile_front(kB, vB, s);
+    tile_front(kB, vB, s, dB);
     load_tile(sB, kB, vB);
+    dB = didx_of(j + 3);
     sB = slot_of(j + 5);
     tile_back(j + 1, s);
   }
@@ -291,9 +359,29 @@ bool decode_attn_enabled() {
   return on;
 }
 
+__global__ __launch_bounds__(256) void k_expand_didx(const Extent* __restrict__ ex, const int32_t* __restrict__ ex_off,
+                                                     const int32_t* __restrict__ ex_didx, int n_ext,
+                                                     int32_t* __restrict__ out) {
+  for (int e = blockIdx.x * 256 + threadIdx.x; e < n_ext; e += gridDim.x * 256) {
+    const int n = ex[e].hi - ex[e].lo, o = ex_off[e], d = ex_didx[e];
+    for (int i = 0; i < n; ++i) out[o + i] = d;
+  }
+}
+
+hipError_t launch_expand_didx(hipStream_t st, const Extent* ex, const int32_t* ex_off, const int32_t* ex_didx,
+                              int n_ext, int32_t* out) {
+  if (n_ext <= 0) return hipSuccess;
+  const int blocks = std::min(4096, (n_ext + 255) / 256);
+  hipLaunchKernelGGL(k_expand_didx, dim3(blocks), dim3(256), 0, st, ex, ex_off, ex_didx, n_ext, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_attn(hipStream_t st, const AttnArgs& a) {
   if (a.n_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_decode_attn, dim3(a.n_items), dim3(64 * DEC_WAVES), 0, st, a);
+  if (a.key_didx)
+    hipLaunchKernelGGL(k_decode_attn<true>, dim3(a.n_items), dim3(64 * DEC_WAVES), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_decode_attn<false>, dim3(a.n_items), dim3(64 * DEC_WAVES), 0, st, a);
   return hipGetLastError();
 }
 

@@ -104,6 +104,12 @@ struct AttnArgs {
   float* part_o;                 // [partial rows][d_v]
   float* part_ml;                // [partial rows][2]: (running max, sum)
   int rows_per_block;
+  // decode kernel only: per list entry the row of rot_table (cos of the
+  // d_rope/2 pairs, then sin) that turns its stored key to its position, or
+  // -1 (key already there); nullptr when no key owes a rotation
+  const int32_t* key_didx;
+  const float* rot_table;
+  int rot_pairing;
 };
 
 // Returns hipErrorInvalidValue when no kernel is instantiated for the dims.
@@ -116,6 +122,9 @@ hipError_t launch_combine(hipStream_t st, const AttnArgs& a, const CombItem* ite
 // DECODE_ROWS packed rows, the block's waves splitting the key range.
 constexpr int DECODE_ROWS = 16;
 hipError_t launch_decode_attn(hipStream_t st, const AttnArgs& a);
+// Per list entry of each extent e (entries ex_off[e] .. + hi - lo): ex_didx[e].
+hipError_t launch_expand_didx(hipStream_t st, const Extent* ex, const int32_t* ex_off, const int32_t* ex_didx,
+                              int n_ext, int32_t* out);
 // False when the environment sets AKV_DECODE_KERNEL=off (the prefill kernel
 // then runs decode launches too, for comparison).
 bool decode_attn_enabled();

@@ -61,6 +61,10 @@ struct PageRec {
 struct SeqRec {
   std::vector<int32_t> slot, pos;
   std::vector<uint8_t> dropped;
+  // rotation each stored key still owes (position minus the position its key
+  // encodes): nonzero only after a deferred repos, until it is materialized
+  std::vector<int32_t> lag;
+  bool lagging = false;        // some token may have lag != 0
   std::vector<int32_t> pages;  // owned pages in allocation order
   int32_t tail = -1;           // open page, or -1
   bool alive = true;
@@ -347,6 +351,7 @@ void place_tokens(akv_pool* p, int32_t s, int32_t n, const int32_t* pos, int32_t
     q.slot.push_back(slot);
     q.pos.push_back(pos[i]);
     q.dropped.push_back(0);
+    q.lag.push_back(0);
     // a token placed at or after the last visible position extends the
     // cached visible order (and its extents) at the end
     if (q.vis_ok) {
@@ -419,6 +424,27 @@ void build_extents(const akv_pool* p, const SeqRec& q, const std::vector<int32_t
       out.back().hi = off + 1;
     else
       out.push_back({pg, off, off + 1});
+  }
+}
+
+// The same image with runs also cut where the owed rotation changes; lag_out
+// gets each extent's owed rotation.
+void build_extents_lag(const akv_pool* p, const SeqRec& q, const std::vector<int32_t>& order,
+                       const std::vector<uint8_t>* hide, std::vector<akv_extent>& out,
+                       std::vector<int32_t>& lag_out) {
+  const int32_t lg = p->log2S, mask = p->L.page_size - 1;
+  out.clear();
+  lag_out.clear();
+  for (int32_t t : order) {
+    if (hide && (*hide)[t]) continue;
+    const int32_t slot = q.slot[t];
+    const int32_t pg = slot >> lg, off = slot & mask;
+    if (!out.empty() && out.back().page == pg && out.back().hi == off && lag_out.back() == q.lag[t]) {
+      out.back().hi = off + 1;
+    } else {
+      out.push_back({pg, off, off + 1});
+      lag_out.push_back(q.lag[t]);
+    }
   }
 }
 
@@ -709,6 +735,26 @@ void repos_commit(SeqRec& q, const std::vector<int64_t>& tot) {
   for (size_t t = 0; t < tot.size(); ++t)
     if (tot[t]) q.pos[t] = (int32_t)(q.pos[t] + tot[t]);
   q.stale();
+}
+
+// Rotate every visible key by the rotation it still owes (one launch) and
+// clear the debt.
+akv_status materialize_seq(akv_pool* p, SeqRec& q) {
+  if (!q.lagging) return AKV_OK;
+  std::vector<int64_t> tot(q.slot.size(), 0);
+  for (size_t t = 0; t < tot.size(); ++t)
+    if (!q.dropped[t]) tot[t] = q.lag[t];
+  std::vector<akv::RotItem> items;
+  std::vector<int32_t> deltas;
+  repos_items(p, q, tot, items, deltas);
+  akv_status st = scratch_fits(p, rotate_scratch_bytes(p, items.size(), deltas.size(), 1));
+  if (st != AKV_OK) return st;
+  st = device_rotate(p, items, deltas);
+  if (st != AKV_OK) return st;
+  for (size_t t = 0; t < tot.size(); ++t)
+    if (tot[t]) q.lag[t] = 0;
+  q.lagging = false;
+  return AKV_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -1062,9 +1108,19 @@ akv_status akv_seq_clone(akv_pool* p, int32_t src, int32_t first, int32_t n, int
                   (long long)pages_needed(p, *qd, m), (long long)available(p));
     st = scratch_fits(p, (size_t)m * sizeof(akv::MovePair) + 4 + (size_t)p->L.d_rope * 4 + 3 * 256);
     if (st != AKV_OK) return st;
+    std::vector<int32_t> lags;
+    lags.reserve(m);
+    for (int32_t t = first; t < first + n; ++t)
+      if (!qs->dropped[t]) lags.push_back(qs->lag[t]);
     std::vector<int32_t> slots(m);
     place_tokens(p, dst, m, pos.data(), slots.data());
-    for (int32_t i = 0; i < m; ++i) mv[i].dst = slots[i];
+    SeqRec& qd2 = p->seqs[dst];   // the copies owe what their sources owe
+    for (int32_t i = 0; i < m; ++i) {
+      mv[i].dst = slots[i];
+      const size_t t = qd2.slot.size() - m + i;
+      qd2.lag[t] = lags[i];
+      if (lags[i]) qd2.lagging = true;
+    }
     if (!p->device) return AKV_OK;
     ScratchCursor sc(p);
     void *dmv, *ddelta;
@@ -1181,6 +1237,52 @@ akv_status akv_compact(akv_pool* p, int32_t s, int32_t force) {
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
   }
+}
+
+akv_status akv_repos_deferred(akv_pool* p, int32_t s, const akv_span* spans, const int32_t* delta,
+                              int32_t n) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    SeqRec* q;
+    akv_status st = get_seq(p, s, &q);
+    if (st != AKV_OK) return st;
+    std::vector<int64_t> tot;
+    st = repos_totals(p, *q, spans, delta, n, tot);
+    if (st != AKV_OK) return st;
+    for (size_t t = 0; t < tot.size(); ++t)
+      if (tot[t]) {
+        q->lag[t] = (int32_t)(q->lag[t] + tot[t]);
+        q->lagging = true;
+      }
+    repos_commit(*q, tot);
+    return AKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_materialize(akv_pool* p, int32_t s) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    SeqRec* q;
+    akv_status st = get_seq(p, s, &q);
+    if (st != AKV_OK) return st;
+    return materialize_seq(p, *q);
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_seq_lag(akv_pool* p, int32_t s, int32_t first, int32_t n, int32_t* lag) {
+  if (!p) return fail(AKV_EINVAL, "NULL pool");
+  SeqRec* q;
+  akv_status st = get_seq(p, s, &q);
+  if (st != AKV_OK) return st;
+  if (first < 0 || n < 0 || (int64_t)first + n > (int64_t)q->slot.size())
+    return fail(AKV_ERANGE, "tokens %d..%d outside 0..%zu", first, first + n, q->slot.size());
+  if (n > 0 && !lag) return fail(AKV_EINVAL, "lag is NULL");
+  for (int32_t i = 0; i < n; ++i) lag[i] = q->lag[first + i];
+  return AKV_OK;
 }
 
 akv_status akv_repos(akv_pool* p, int32_t s, const akv_span* spans, const int32_t* delta,
@@ -1427,15 +1529,19 @@ akv_status akv_seq_visible(akv_pool* p, int32_t s, const akv_span* mask, int32_t
   }
 }
 
+static bool decode_launch(const akv_pool* p, const int64_t* q_len, int32_t n, int32_t stride);
+static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens, const akv_segment* segs,
+                                 int32_t n_segs, const akv_extent* page_lists, int32_t n_ext,
+                                 const int32_t* ext_lag, float scale, void* out);
+
 akv_status akv_seq_attention(akv_pool* p, const void* Q, int32_t n_q_tokens, const akv_seq_segment* segs,
                              int32_t n_segs, const akv_span* masks, int32_t n_masks, float scale, void* out) {
   try {
     if (!p) return fail(AKV_EINVAL, "NULL pool");
     if (n_segs < 0 || n_masks < 0) return fail(AKV_EINVAL, "negative count");
     if ((n_segs > 0 && !segs) || (n_masks > 0 && !masks)) return fail(AKV_EINVAL, "segments / masks are NULL");
-    std::vector<akv_segment> rows((size_t)n_segs);
-    std::vector<akv_extent> lists;
-    std::vector<akv_extent> masked;
+    bool lagging = false;
+    std::vector<int64_t> qlens(n_segs);
     for (int32_t i = 0; i < n_segs; ++i) {
       const akv_seq_segment& sg = segs[i];
       SeqRec* q;
@@ -1443,14 +1549,38 @@ akv_status akv_seq_attention(akv_pool* p, const void* Q, int32_t n_q_tokens, con
       if (st != AKV_OK) return st;
       if (sg.mask_len < 0 || sg.mask_begin < 0 || (int64_t)sg.mask_begin + sg.mask_len > n_masks)
         return fail(AKV_EINVAL, "segment %d: mask spans outside 0..%d", i, n_masks);
-      const akv_span* m = masks ? masks + sg.mask_begin : nullptr;
-      st = check_spans(m, sg.mask_len, (int32_t)q->slot.size());
+      st = check_spans(masks ? masks + sg.mask_begin : nullptr, sg.mask_len, (int32_t)q->slot.size());
       if (st != AKV_OK) return st;
+      lagging = lagging || q->lagging;
+      qlens[i] = sg.q_len;
+    }
+    // Owed rotations (deferred repos) are applied inside the decode kernel;
+    // a prefill launch first rotates the keys in place.
+    const bool fused = lagging && p->device && decode_launch(p, qlens.data(), n_segs, 1);
+    if (lagging && !fused && p->device)
+      for (int32_t i = 0; i < n_segs; ++i) {
+        akv_status st = materialize_seq(p, p->seqs[segs[i].seq]);
+        if (st != AKV_OK) return st;
+      }
+    std::vector<akv_segment> rows((size_t)n_segs);
+    std::vector<akv_extent> lists, masked;
+    std::vector<int32_t> lags, mlag;
+    for (int32_t i = 0; i < n_segs; ++i) {
+      const akv_seq_segment& sg = segs[i];
+      SeqRec* q = &p->seqs[sg.seq];
+      const akv_span* m = masks ? masks + sg.mask_begin : nullptr;
       const std::vector<int32_t>& vis = visible(*q);
-      const std::vector<akv_extent>* ex;
+      std::vector<uint8_t> hide;
       if (sg.mask_len > 0) {
-        std::vector<uint8_t> hide(q->slot.size(), 0);
+        hide.assign(q->slot.size(), 0);
         for (int32_t k = 0; k < sg.mask_len; ++k) std::fill(hide.begin() + m[k].begin, hide.begin() + m[k].end, 1);
+      }
+      const std::vector<akv_extent>* ex;
+      if (fused) {
+        build_extents_lag(p, *q, vis, sg.mask_len > 0 ? &hide : nullptr, masked, mlag);
+        lags.insert(lags.end(), mlag.begin(), mlag.end());
+        ex = &masked;
+      } else if (sg.mask_len > 0) {
         build_extents(p, *q, vis, &hide, masked);
         ex = &masked;
       } else {
@@ -1464,17 +1594,30 @@ akv_status akv_seq_attention(akv_pool* p, const void* Q, int32_t n_q_tokens, con
       rows[i] = {sg.q_begin, sg.q_len, (int32_t)lists.size(), (int32_t)ex->size()};
       lists.insert(lists.end(), ex->begin(), ex->end());
     }
-    return akv_segment_attention(p, Q, n_q_tokens, rows.data(), n_segs, lists.data(), (int32_t)lists.size(), scale,
-                                 out);
+    return attention_impl(p, Q, n_q_tokens, rows.data(), n_segs, lists.data(), (int32_t)lists.size(),
+                          fused ? lags.data() : nullptr, scale, out);
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
   }
 }
 
-akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
-                                 const akv_segment* segs, int32_t n_segs,
-                                 const akv_extent* page_lists, int32_t n_ext, float scale,
-                                 void* out) {
+// Launches whose every segment packs at most 16 rows per kv head (decode)
+// run the decode kernel on 16-row items; the others the prefill kernels.
+static bool decode_launch(const akv_pool* p, const int64_t* q_len, int32_t n, int32_t stride) {
+  const akv_layout& L = p->L;
+  const int G = L.n_q_heads / L.n_kv_heads;
+  int64_t max_rows = 0;
+  for (int32_t i = 0; i < n; ++i) max_rows = std::max<int64_t>(max_rows, q_len[(size_t)i * stride] * G);
+  return akv::decode_attn_enabled() && L.d_nope == 0 && L.d_rope == 128 && L.d_v == 128 &&
+         max_rows <= akv::DECODE_ROWS;
+}
+
+// Segment-batch attention over caller lists; ext_lag (optional, one per
+// extent) is the rotation each extent's keys still owe, applied inside the
+// decode kernel (only decode launches take it).
+static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens, const akv_segment* segs,
+                                 int32_t n_segs, const akv_extent* page_lists, int32_t n_ext,
+                                 const int32_t* ext_lag, float scale, void* out) {
   try {
     if (!p) return fail(AKV_EINVAL, "NULL pool");
     if (!p->device) return fail(AKV_ESTATE, "attention needs a device pool");
@@ -1519,18 +1662,28 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
     if (!Q || !out) return fail(AKV_EINVAL, "Q and out are required");
     if (total > kInt32Max) return fail(AKV_ERANGE, "page lists too long");
 
-    // Launches whose every segment packs at most 16 rows per kv head (decode)
-    // run the decode kernel on 16-row items; the others the prefill kernels.
-    const int G = L.n_q_heads / L.n_kv_heads;
-    int64_t max_rows = 0;
-    for (int32_t i = 0; i < n_segs; ++i) max_rows = std::max<int64_t>(max_rows, (int64_t)segs[i].q_len * G);
-    const bool decode = akv::decode_attn_enabled() && L.d_nope == 0 && L.d_rope == 128 && L.d_v == 128 &&
-                        max_rows <= akv::DECODE_ROWS;
+    std::vector<int64_t> qlens(n_segs);
+    for (int32_t i = 0; i < n_segs; ++i) qlens[i] = segs[i].q_len;
+    const bool decode = decode_launch(p, qlens.data(), n_segs, 1);
+    // distinct owed rotations of the lists (fused into the decode kernel)
+    std::vector<int32_t> rot_deltas, ex_didx;
+    if (ext_lag) {
+      std::unordered_map<int32_t, int32_t> di;
+      for (int32_t i = 0; i < n_segs; ++i)
+        for (int32_t e = segs[i].ext_begin; e < segs[i].ext_begin + segs[i].ext_len; ++e)
+          if (ext_lag[e] && !di.count(ext_lag[e])) {
+            di.emplace(ext_lag[e], (int32_t)rot_deltas.size());
+            rot_deltas.push_back(ext_lag[e]);
+          }
+      if (!rot_deltas.empty() && !decode)
+        return fail(AKV_EINVAL, "owed rotations are applied only in decode launches");
+    }
     const int rb = decode ? akv::DECODE_ROWS : akv::attn_rows_per_block(L.d_nope);
     AttnPlan plan;
     plan_attention(p, segs, n_segs, lkv, list_off, rb, plan);
     if (plan.part_rows > kInt32Max) return fail(AKV_ERANGE, "too many split-KV partial rows");
     // extent offsets for the slot expansion (over all segments' ranges, in order)
+    const bool fused = !rot_deltas.empty();
     std::vector<akv::Extent> ex_used;
     std::vector<int32_t> ex_off;
     for (int32_t i = 0; i < n_segs; ++i) {
@@ -1539,22 +1692,32 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
         const akv_extent& x = page_lists[e];
         ex_used.push_back({x.page, x.lo, x.hi});
         ex_off.push_back((int32_t)o);
+        if (fused) {
+          int32_t d = -1;
+          if (ext_lag[e])
+            d = (int32_t)(std::find(rot_deltas.begin(), rot_deltas.end(), ext_lag[e]) - rot_deltas.begin());
+          ex_didx.push_back(d);
+        }
         o += x.hi - x.lo;
       }
     }
     ScratchCursor sc(p);
-    void* dv[5];
+    void* dv[7];
     akv_status st = upload_arrays(p, sc,
                                   {{plan.segs.data(), plan.segs.size() * sizeof(akv::AttnSeg)},
                                    {plan.items.data(), plan.items.size() * sizeof(akv::AttnItem)},
                                    {plan.comb.data(), plan.comb.size() * sizeof(akv::CombItem)},
                                    {ex_used.data(), ex_used.size() * sizeof(akv::Extent)},
-                                   {ex_off.data(), ex_off.size() * 4}},
+                                   {ex_off.data(), ex_off.size() * 4},
+                                   {ex_didx.data(), ex_didx.size() * 4},
+                                   {rot_deltas.data(), rot_deltas.size() * 4}},
                                   dv);
     if (st != AKV_OK) return st;
     void *dsegs = dv[0], *ditems = dv[1], *dcomb = plan.comb.empty() ? nullptr : dv[2], *dex = dv[3],
          *doff = dv[4];
     int32_t* dslots = (int32_t*)sc.take((size_t)std::max<int64_t>(total, 1) * 4);
+    int32_t* dkey_didx = fused ? (int32_t*)sc.take((size_t)std::max<int64_t>(total, 1) * 4) : nullptr;
+    float* drot = fused ? (float*)sc.take(rot_deltas.size() * (size_t)L.d_rope * 4) : nullptr;
     float* part_o = nullptr;
     float* part_ml = nullptr;
     if (plan.part_rows > 0) {
@@ -1571,6 +1734,16 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
       tm.done();
     }
     if (e != hipSuccess) return hip_fail(e, "expand kernel launch");
+    if (fused) {
+      KTimer tm(p, AKV_K_EXPAND);
+      e = akv::launch_rot_table(p->stream, L.d_rope, (const int32_t*)dv[6], (int)rot_deltas.size(),
+                                (const double*)p->scratch, drot);
+      if (e == hipSuccess)
+        e = akv::launch_expand_didx(p->stream, (const akv::Extent*)dex, (const int32_t*)doff,
+                                    (const int32_t*)dv[5], (int)ex_used.size(), dkey_didx);
+      tm.done();
+      if (e != hipSuccess) return hip_fail(e, "owed-rotation table launch");
+    }
     akv::AttnArgs a{};
     a.q = (const uint16_t*)Q;
     a.n_q_heads = L.n_q_heads;
@@ -1592,6 +1765,9 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
     a.part_o = part_o;
     a.part_ml = part_ml;
     a.rows_per_block = rb;
+    a.key_didx = dkey_didx;
+    a.rot_table = drot;
+    a.rot_pairing = L.pairing;
     {
       KTimer tm(p, AKV_K_ATTN);
       e = decode ? akv::launch_decode_attn(p->stream, a) : akv::launch_seg_attn(p->stream, a, L.d_nope, L.d_rope, L.d_v);
@@ -1608,6 +1784,12 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
   }
+}
+
+akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens, const akv_segment* segs,
+                                 int32_t n_segs, const akv_extent* page_lists, int32_t n_ext, float scale,
+                                 void* out) {
+  return attention_impl(p, Q, n_q_tokens, segs, n_segs, page_lists, n_ext, nullptr, scale, out);
 }
 
 akv_status akv_seq_tokens(akv_pool* p, int32_t s, int32_t first, int32_t n, int32_t* slot,

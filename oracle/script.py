@@ -44,6 +44,8 @@ def apply_op(pool: Pool, op) -> Optional[np.ndarray]:
     elif isinstance(op, W.Drop):
         pool.drop(op.seq, op.spans)
     elif isinstance(op, W.Repos):
+        # a deferred repos means the same positions and the same attention;
+        # only where the device rotates the keys differs
         pool.repos(op.seq, op.spans, op.deltas)
     elif isinstance(op, W.Splice):
         return pool.splice(op.seq, op.spans, op.stub_lens, _f64(op.k), _f64(op.kpe), _f64(op.v))

@@ -57,7 +57,10 @@ def apply_op(pool: akv.Pool, op, keep=None):
     elif isinstance(op, W.Drop):
         pool.drop(op.seq, op.spans)
     elif isinstance(op, W.Repos):
-        pool.repos(op.seq, op.spans, op.deltas)
+        if op.deferred:
+            pool.repos_deferred(op.seq, op.spans, op.deltas)
+        else:
+            pool.repos(op.seq, op.spans, op.deltas)
     elif isinstance(op, W.Splice):
         k, v = dev_bf16(op.k), dev_bf16(op.v)
         kpe = dev_bf16(op.kpe) if op.kpe is not None else None
@@ -75,12 +78,18 @@ def apply_op(pool: akv.Pool, op, keep=None):
 def run(wl: W.Workload, pool: akv.Pool | None = None, **kw):
     pool = pool if pool is not None else make_pool(wl, **kw)
     keep, outs = [], []
+    deferred = any(isinstance(o, W.Repos) and o.deferred for o in wl.ops)
     for op in wl.ops:
         if isinstance(op, W.Attention):
             rows, ex = segment_inputs(pool, op)
             q = dev_bf16(op.q)
             keep.append(q)
-            out = pool.segment_attention(q, rows, ex, op.scale)
+            if deferred:   # keys owe rotations: the library applies them
+                out = pool.seq_attention(q, [(sg.seq, sg.q_begin, sg.q_len,
+                                              sg.mask_spans if len(sg.mask_spans) else None)
+                                             for sg in op.segments], op.scale)
+            else:
+                out = pool.segment_attention(q, rows, ex, op.scale)
             outs.append(dict(segments=rows, extents=ex, out=out))
         else:
             apply_op(pool, op, keep)

@@ -387,6 +387,63 @@ def test_seq_attention_equals_segment_attention(make):
     pool.close()
 
 
+# ---------------------------------------------------------------------------
+# deferred repos: keys owe their rotation, the decode kernel turns them
+# ---------------------------------------------------------------------------
+def _deferred_parity(wl):
+    """Attention against the oracle (its keys rotated eagerly), then every
+    sequence materialized and its stored keys against the oracle's."""
+    pool, outs = D.run(wl)
+    res = oracle.run_workload(wl)
+    _check_tables(pool, res.pool)
+    wa = _check_attention(outs, res, wl)
+    for s, q in enumerate(res.pool.seqs):
+        if q.alive:
+            pool.materialize(s)
+            assert not pool.lag(s)[~pool.tokens(s)[2]].any()
+    torch.cuda.synchronize()
+    wk = _check_visible_kv(pool, res.pool, wl.layout)
+    _say(f"[gpu] {wl.name} deferred: worst attention abs err {wa:.2e}, keys after materialize {wk:.2e}")
+    return pool
+
+
+@pytest.mark.parametrize("seed,pairing,lq", [(0, 0, 1), (1, 1, 1), (2, 0, 3)])
+def test_decode_deferred_repos_full(seed, pairing, lq):
+    """Deferred repos, then a decode launch that turns the owed keys as it
+    reads them: every output row against the oracle."""
+    _deferred_parity(W.decode_batch(seed, n_req=8, ctx_lo=4000, ctx_hi=9000, q_len=lq, deferred=True,
+                                    pairing=pairing)).close()
+
+
+@pytest.mark.parametrize("pairing", [0, 1])
+def test_fused_rotation_equals_materialized_bit_exact(pairing):
+    """The decode kernel's in-register rotation writes the same scores as
+    keys that repos rotated in place: outputs equal bit for bit."""
+    wl = W.decode_batch(7, n_req=12, ctx_lo=4000, ctx_hi=12000, deferred=True, pairing=pairing)
+    pool, outs = D.run(wl)
+    att = [o for o in wl.ops if isinstance(o, W.Attention)][0]
+    segs = [(sg.seq, sg.q_begin, sg.q_len, None) for sg in att.segments]
+    q = D.dev_bf16(att.q)
+    fused = pool.seq_attention(q, segs, att.scale)
+    assert any(pool.lag(s).any() for s in range(len(segs)))
+    for s in range(len(segs)):
+        pool.materialize(s)
+    plain = pool.seq_attention(q, segs, att.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), plain.view(torch.int16))
+    pool.close()
+
+
+def test_prefill_on_owed_keys_rotates_in_place_first():
+    """A launch for the prefill kernels (rows above 16 per kv head) rotates
+    the owed keys in place before it runs: C1 with every repos deferred."""
+    wl = W.c1_tiny(0, "cumulative")
+    for op in wl.ops:
+        if isinstance(op, W.Repos):
+            op.deferred = True
+    _deferred_parity(wl).close()
+
+
 def test_retrigger_64k_sampled():
     _sampled_parity(W.retrigger(0), n_rows=12)
 

@@ -91,7 +91,15 @@ def _replay(wl: W.Workload, check_every_op=True):
             slot, delta = hp.repos_plan(op.seq, op.spans, op.deltas)
             assert sorted(zip(slot.tolist(), delta.tolist())) == _oracle_repos_pairs(op_pool, op.seq, op.spans, op.deltas), tag
             assert len(set(slot.tolist())) == len(slot), "a slot rotated twice"
-            hp.repos(op.seq, op.spans, op.deltas)
+            if op.deferred:
+                owed = op_pool.repos_deltas(op.seq, op.spans, op.deltas)
+                before = hp.lag(op.seq)
+                hp.repos_deferred(op.seq, op.spans, op.deltas)
+                np.testing.assert_array_equal(hp.lag(op.seq), before + owed[:len(before)], err_msg=tag)
+            else:
+                before = hp.lag(op.seq)
+                hp.repos(op.seq, op.spans, op.deltas)
+                np.testing.assert_array_equal(hp.lag(op.seq), before, err_msg=tag)
             oracle.apply_op(op_pool, op)
         elif isinstance(op, W.Splice):
             sp = hp.splice(op.seq, op.spans, op.stub_lens)
@@ -284,11 +292,12 @@ def test_retrigger_clone_page_tables_bit_exact(seed, mla, pre_b):
     _replay(W.retrigger(seed, ctx=4096, pre_a=256, nq=64, n_turns=8, n_recent=2, pre_b=pre_b, mla=mla))
 
 
-@pytest.mark.parametrize("seed,lq", [(0, 1), (1, 3)])
-def test_decode_batch_page_tables_bit_exact(seed, lq):
-    """Histories with drops and repos, then one batched append of q_len tokens
-    per request: tables bit-exact against the oracle's per-entry appends."""
-    _replay(W.decode_batch(seed, n_req=10, ctx_lo=1, ctx_hi=1500, q_len=lq))
+@pytest.mark.parametrize("seed,lq,deferred", [(0, 1, False), (1, 3, False), (2, 1, True)])
+def test_decode_batch_page_tables_bit_exact(seed, lq, deferred):
+    """Histories with drops and repos (deferred: positions move, keys owe the
+    rotation), then one batched append of q_len tokens per request: tables
+    bit-exact against the oracle, owed rotations as the repos deltas say."""
+    _replay(W.decode_batch(seed, n_req=10, ctx_lo=1, ctx_hi=1500, q_len=lq, deferred=deferred))
 
 
 def test_append_batch_equals_sequential_appends_and_is_atomic():
@@ -345,6 +354,32 @@ def test_seq_attention_validates_before_the_pool_state_check():
         with pytest.raises(akv.AkvError) as ei:
             hp.seq_attention(q, segs, out=out)
         assert ei.value.status == code, (segs, ei.value)
+
+
+def test_owed_rotation_follows_tokens():
+    """Deferred repos records the debt; eager repos, compaction and clones
+    keep it with each token; materialize clears it."""
+    lay = W.Layout(4, 2, 0, 16, 16, 4, 80)
+    hp = _host_pool(lay, np.arange(80))
+    a, b = hp.seq_create(), hp.seq_create()
+    hp.append(a, np.arange(100, 160))
+    hp.drop(a, [[0, 10]])
+    hp.repos_deferred(a, [[10, 60]], [-10])
+    hp.repos_deferred(a, [[30, 60]], [5])
+    want = np.zeros(60, np.int32)
+    want[10:60] -= 10
+    want[30:60] += 5
+    np.testing.assert_array_equal(hp.lag(a), want)
+    hp.repos(a, [[10, 60]], [3])                 # rotates keys: the debt stays
+    np.testing.assert_array_equal(hp.lag(a), want)
+    hp.compact(a, True)
+    np.testing.assert_array_equal(hp.lag(a), want)
+    hp.clone(a, 20, 20, b, 7)
+    np.testing.assert_array_equal(hp.lag(b), want[20:40])
+    hp.materialize(a)
+    lag_a = hp.lag(a)
+    assert not lag_a[10:].any()
+    np.testing.assert_array_equal(hp.lag(b), want[20:40])
 
 
 def test_clone_skips_dropped_and_refusals_leave_no_trace():

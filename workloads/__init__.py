@@ -125,6 +125,7 @@ class Repos:
     seq: int
     spans: np.ndarray    # int32 [m, 2]
     deltas: np.ndarray   # int32 [m]
+    deferred: bool = False   # keys keep their rotation until read (same positions, same attention)
 
 
 @dataclass
@@ -494,13 +495,14 @@ def retrigger(seed: int = 0, ctx: int = 65536, pre_a: int = 512, nq: int = 512, 
 # decode: one new token per request at high batch (the inter-token side)
 # --------------------------------------------------------------------------
 def decode_batch(seed: int = 0, n_req: int = 48, ctx_lo: int = 2048, ctx_hi: int = 16384,
-                 n_q_heads: int = 32, q_len: int = 1) -> Workload:
+                 n_q_heads: int = 32, q_len: int = 1, deferred: bool = False, pairing: int = 0) -> Workload:
     """n_req agent histories in one pool, each built with the batched recipe
     (512-token reasoning turns, log-uniform tool spans, 10-60% of the older
     tools dropped, survivors repositioned); then every request appends q_len
     tokens (1: plain decode; a few: speculative or multi-token steps) at its
     next positions and runs one segment over its whole visible list, all in
-    one attention launch."""
+    one attention launch.  deferred: the survivors' repos leaves the keys
+    where they are (the decode kernel turns them as it reads them)."""
     rng = _rng(seed)
     reqs = []
     for r in range(n_req):
@@ -525,7 +527,7 @@ def decode_batch(seed: int = 0, n_req: int = 48, ctx_lo: int = 2048, ctx_hi: int
         dropped = [tools[i] for i in sorted(chosen)]
         reqs.append(dict(ctx=ctx, dropped=dropped))
     pages = sum((q["ctx"] + q_len + 15) // 16 for q in reqs) + 16
-    lay = Layout(n_q_heads, 8, 0, 128, 128, 16, pages, rope_theta=500000.0)
+    lay = Layout(n_q_heads, 8, 0, 128, 128, 16, pages, pairing=pairing, rope_theta=500000.0)
     wl = Workload("decode_batch", lay, rng.permutation(pages).astype(np.int32))
     for r in range(n_req):
         wl.ops.append(SeqCreate())
@@ -536,7 +538,7 @@ def decode_batch(seed: int = 0, n_req: int = 48, ctx_lo: int = 2048, ctx_hi: int
             wl.ops.append(Drop(r, _spans(q["dropped"])))
             rs, rd = _survivor_runs(q["ctx"], q["dropped"])
             if len(rs):
-                wl.ops.append(Repos(r, rs, rd))
+                wl.ops.append(Repos(r, rs, rd, deferred))
     segs, news = [], []
     wl.notes["step_from"] = len(wl.ops)     # one decode step: the new tokens and attention
     for r, q in enumerate(reqs):
