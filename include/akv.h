@@ -276,6 +276,49 @@ akv_status akv_segment_attention(akv_pool* pool, const void* Q, int32_t n_q_toke
 akv_status akv_seq_attention(akv_pool* pool, const void* Q, int32_t n_q_tokens, const akv_seq_segment* segs,
                              int32_t n_segs, const akv_span* masks, int32_t n_masks, float scale, void* out);
 
+/* ---- extended radix tree of cached states ([AKV-blog] section 3; [AKV-notes]
+ * section 3, Cache Management and Cache Reuse Matching Rules) -------------------- */
+
+/* A history is a sequence of events: a token (a = id, b = position), or one
+ * span of a cache operation (drop: [a, b); repos: [a, b) by c), in the order
+ * they were applied.  A checkpoint registers a pool sequence whose current
+ * state is the state of a history.  A node of the tree is served by a
+ * checkpoint below it when only token events lie between them (operations
+ * would have changed the node's tokens; appended tokens do not): the first
+ * n_tokens logical tokens of the checkpoint's sequence are then that node's
+ * state.  The tree is host metadata only; it holds sequence ids, not pages. */
+enum { AKV_EV_TOKEN = 0, AKV_EV_DROP = 1, AKV_EV_REPOS = 2 };
+typedef struct { int32_t kind, a, b, c; } akv_event;
+typedef struct akv_tree akv_tree;
+/* Result of a match: seq = -1 when nothing matched.  n_events of the request
+ * history matched; reuse the first n_tokens logical tokens of seq; exact = 1
+ * (tokens, positions and operations equal: reuse as is) or 0 (retrigger:
+ * tokens and operations equal, positions all shifted by delta: reuse through
+ * akv_seq_clone with that delta). */
+typedef struct { int32_t seq, n_events, n_tokens, exact, delta; } akv_tree_hit;
+
+akv_status akv_tree_create(akv_tree** out);
+akv_status akv_tree_destroy(akv_tree* tree);
+/* Register seq as the state of history ev[0..n) (n >= 1; a sequence is
+ * registered once).  Errors: AKV_EINVAL (bad event, empty history, seq
+ * registered), AKV_ENOMEM. */
+akv_status akv_tree_insert(akv_tree* tree, const akv_event* ev, int32_t n, int32_t seq);
+/* Longest reusable prefix of a request history: the walk stops at the
+ * first event that does not match; the longest exact prefix is taken first
+ * and a retrigger prefix replaces it only when strictly longer; among the
+ * checkpoints serving one node, the one registered last.  The hit's
+ * checkpoint counts as used now (eviction order). */
+akv_status akv_tree_match(akv_tree* tree, const akv_event* ev, int32_t n, akv_tree_hit* out);
+/* Pin (add > 0) or unpin (add < 0) a checkpoint in use by a running request;
+ * pinned checkpoints are not evicted. */
+akv_status akv_tree_pin(akv_tree* tree, int32_t seq, int32_t add);
+/* Remove up to max_n unpinned checkpoints, least recently used first (each
+ * positional version on its own); their sequence ids go to seqs_out for the
+ * caller to release.  Dropped tokens' pages are already the pool's first
+ * eviction candidates. */
+akv_status akv_tree_evict(akv_tree* tree, int32_t max_n, int32_t* seqs_out, int32_t* n_out);
+akv_status akv_tree_stats(akv_tree* tree, int32_t* n_nodes, int32_t* n_checkpoints);
+
 /* ---- inspection, sync, errors ---------------------------------------------------- */
 
 /* Per-token metadata of tokens first .. first+n-1 (any output may be NULL);

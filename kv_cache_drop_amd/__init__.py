@@ -15,14 +15,15 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-__all__ = ["AkvError", "Pool", "lib", "LIB_PATH", "SYMBOLS", "KERNEL_KINDS", "attention_supported",
-           "repos_layers"]
+__all__ = ["AkvError", "Pool", "Tree", "lib", "LIB_PATH", "SYMBOLS", "KERNEL_KINDS", "attention_supported",
+           "repos_layers", "EV_TOKEN", "EV_DROP", "EV_REPOS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libakv.so")
 
 AKV_OK, AKV_EINVAL, AKV_ERANGE, AKV_ENOMEM, AKV_ESTATE, AKV_EHIP = 0, -1, -2, -3, -4, -5
 STATUS_NAMES = {0: "AKV_OK", -1: "AKV_EINVAL", -2: "AKV_ERANGE", -3: "AKV_ENOMEM",
                 -4: "AKV_ESTATE", -5: "AKV_EHIP"}
+EV_TOKEN, EV_DROP, EV_REPOS = 0, 1, 2
 KERNEL_KINDS = {"append": 0, "rotate": 1, "compact": 2, "expand": 3, "attention": 4, "combine": 5,
                 "clone": 6}
 
@@ -71,6 +72,13 @@ SYMBOLS = {
     "akv_seq_info": [_P, _I, _IP, _IP, ctypes.POINTER(ctypes.c_double)],
     "akv_pool_queues": [_P, _IP, _I, _IP, _IP, _I, _IP],
     "akv_repos_plan": [_P, _I, _IP, _IP, _I, _IP, _IP, _I, _IP],
+    "akv_tree_create": [ctypes.POINTER(_P)],
+    "akv_tree_destroy": [_P],
+    "akv_tree_insert": [_P, _IP, _I, _I],
+    "akv_tree_match": [_P, _IP, _I, _IP],
+    "akv_tree_pin": [_P, _I, _I],
+    "akv_tree_evict": [_P, _I, _IP, _IP],
+    "akv_tree_stats": [_P, _IP, _IP],
     "akv_timing_enable": [_P, _I],
     "akv_timing_read": [_P, _I, ctypes.POINTER(ctypes.c_double), _IP],
     "akv_timing_samples": [_P, _I, ctypes.POINTER(ctypes.c_float), _I, _IP],
@@ -396,3 +404,54 @@ def repos_layers(pools, seq: int, spans, deltas) -> None:
     sp = _i32(spans).reshape(-1, 2)
     dl = _i32(deltas).reshape(-1)
     _check(lib().akv_repos_layers(hs, len(pools), seq, _ptr(sp), _ptr(dl), len(sp)))
+
+
+class Tree:
+    """Extended radix tree of cached states (akv_tree_*): histories are
+    [n, 4] int32 event rows (kind, a, b, c): EV_TOKEN (id, position),
+    EV_DROP [a, b), EV_REPOS [a, b) by c."""
+
+    def __init__(self):
+        h = _P()
+        _check(lib().akv_tree_create(ctypes.byref(h)))
+        self._h = h
+
+    def close(self) -> None:
+        if self._h:
+            lib().akv_tree_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _events(ev) -> np.ndarray:
+        return _i32(ev).reshape(-1, 4)
+
+    def insert(self, events, seq: int) -> None:
+        ev = self._events(events)
+        _check(lib().akv_tree_insert(self._h, _ptr(ev), len(ev), seq))
+
+    def match(self, events) -> dict:
+        ev = self._events(events)
+        out = np.zeros(5, np.int32)
+        _check(lib().akv_tree_match(self._h, _ptr(ev), len(ev), _ptr(out)))
+        return dict(seq=int(out[0]), n_events=int(out[1]), n_tokens=int(out[2]), exact=int(out[3]),
+                    delta=int(out[4]))
+
+    def pin(self, seq: int, add: int = 1) -> None:
+        _check(lib().akv_tree_pin(self._h, seq, add))
+
+    def evict(self, max_n: int) -> list:
+        out = np.zeros(max(max_n, 1), np.int32)
+        n = ctypes.c_int32()
+        _check(lib().akv_tree_evict(self._h, max_n, _ptr(out), ctypes.byref(n)))
+        return out[: n.value].tolist()
+
+    def stats(self):
+        a, b = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().akv_tree_stats(self._h, ctypes.byref(a), ctypes.byref(b)))
+        return a.value, b.value

@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libakv.so")
-SOURCES = ["akv_runtime.cpp", "akv_kernels.hip", "akv_copy.hip", "akv_decode.hip"]
+SOURCES = ["akv_runtime.cpp", "akv_kernels.hip", "akv_copy.hip", "akv_decode.hip", "akv_tree.cpp"]
 ARCH = os.environ.get("AKV_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU forms are kept out of the device code (hipcc flag; the host

@@ -131,4 +131,7 @@ bool decode_attn_enabled();
 
 bool attn_dims_supported(int d_nope, int d_rope, int d_v);
 
+// Text returned by akv_last_error (thread-local; host code of the library).
+void set_error(const char* msg);
+
 }  // namespace akv

@@ -42,6 +42,12 @@ akv_status fail(akv_status s, const char* fmt, ...) {
   return s;
 }
 
+}  // namespace
+
+void akv::set_error(const char* msg) { g_err = msg; }
+
+namespace {
+
 akv_status hip_fail(hipError_t e, const char* what) {
   return fail(AKV_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
