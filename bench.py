@@ -37,6 +37,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # by 1.0.  When the kernel's source differs, its traffic is reported as null.
 _KERNELS_SHA1 = "23f137b6eeab98bf293555e82e812e78b0174f86"    # akv_kernels.hip
 _COPY_SHA1 = "2a16fbd3bdf4c924c007ee7a8f5e9337713b3565"       # akv_copy.hip
+_DECODE_SHA1 = "76f26fe087c03d7e32a848e7a557f93254f5fc17"     # akv_decode.hip
 COUNTERS = {
     "fetch_scale": 1048576 / 524302, "write_scale": 1.0,
     "attention": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 110925, "write_kib": 16384},
@@ -44,6 +45,8 @@ COUNTERS = {
     "rotate_32_layers": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 1248286,
                          "write_kib": 2484294},
     "compact": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 85345, "write_kib": 165578},
+    # the decode step of 48 requests (seed 0), k_decode_attn<false>
+    "decode": {"source": "akv_decode.hip", "sha1": _DECODE_SHA1, "fetch_kib": 611213, "write_kib": 5168},
 }
 
 
@@ -318,7 +321,9 @@ def run_config(args) -> dict:
         # one query row per kv-head group: the launch streams the visible K/V once
         hbm_gbps = kv_bytes / (attn_ms * 1e-3) / 1e9
         rec["roofline"] = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                           "frac": round(hbm_gbps / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": kern,
+                           "frac": round(hbm_gbps / PEAK_HBM_GBPS, 4),
+                           "traffic": counted_traffic("decode") if args.config == "decode" and args.seed == 0
+                           and kern == "k_decode_attn" else None, "kernel": kern,
                            "kv_bytes_per_launch": kv_bytes, "flop_per_launch": flops,
                            "avg_launch_ms": round(attn_ms, 5)}
     if tot["clone"][1]:
@@ -422,22 +427,26 @@ def main():
         seqs.append(s)
     torch.cuda.synchronize()
 
+    masks = [sg.mask_spans if len(sg.mask_spans) else None for sg in att.segments]
+
     def step(s):
         pool.drop(s, drop.spans)
         pool.repos(s, repos.spans, repos.deltas)
         pool.append(s, new.pos, nk, None, nv)
+        # the attention call reads each segment's visible list from the pool
+        pool.seq_attention(q, [(s, sg.q_begin, sg.q_len, m) for sg, m in zip(att.segments, masks)], 0.0, out=out)
+
+    def page_lists_of(s):
         exts, segs, eb = [], [], 0
-        for sg in att.segments:
-            ex = pool.visible(s, sg.mask_spans if len(sg.mask_spans) else None)
+        for sg, m in zip(att.segments, masks):
+            ex = pool.visible(s, m)
             exts.append(ex)
             segs.append((sg.q_begin, sg.q_len, eb, len(ex)))
             eb += len(ex)
-        page_lists = np.concatenate(exts)
-        pool.segment_attention(q, segs, page_lists, 0.0, out=out)
-        return segs, page_lists
+        return segs, np.concatenate(exts)
 
     for c in range(args.warmup):
-        segs, page_lists = step(seqs[c])
+        step(seqs[c])
     torch.cuda.synchronize()
     pool.timing_enable(True)
     for k in akv.KERNEL_KINDS:
@@ -445,9 +454,10 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for c in range(args.warmup, n_copies):
-        segs, page_lists = step(seqs[c])
+        step(seqs[c])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    segs, page_lists = page_lists_of(seqs[-1])
     pct = {k: [round(float(x), 5) for x in np.percentile(pool.timing_samples(k), [10, 50, 90])]
            for k in ("attention", "rotate")}
     kt = {k: pool.timing_read(k) for k in akv.KERNEL_KINDS}

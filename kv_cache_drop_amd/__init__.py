@@ -295,12 +295,12 @@ class Pool:
         """Extents (page, lo, hi) of the visible list, optionally minus mask spans."""
         m = _i32(mask if mask is not None else np.zeros((0, 2))).reshape(-1, 2)
         n = ctypes.c_int32()
-        cap = 4096
+        cap = getattr(self, "_vis_cap", 4096)    # the largest list seen so far: one call as a rule
         while True:
             out = np.empty((cap, 3), np.int32)
             st = lib().akv_seq_visible(self._h, seq, _ptr(m), len(m), _ptr(out), cap, ctypes.byref(n))
             if st == AKV_ERANGE and n.value > cap:
-                cap = n.value
+                cap = self._vis_cap = n.value
                 continue
             _check(st)
             return out[: n.value]

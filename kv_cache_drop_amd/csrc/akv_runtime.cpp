@@ -647,12 +647,11 @@ akv_status compact_seq(akv_pool* p, int32_t s) {
 }
 
 void drop_tokens(akv_pool* p, SeqRec& q, int32_t b, int32_t e) {
-  const int32_t S = p->L.page_size;
   for (int32_t t = b; t < e; ++t) {
     if (q.dropped[t]) continue;
     q.dropped[t] = 1;
     q.n_vis -= 1;
-    const int32_t pg = q.slot[t] / S;
+    const int32_t pg = q.slot[t] >> p->log2S;
     PageRec& r = p->pages[pg];
     r.nvis -= 1;
     if (r.nvis == 0 && pg != q.tail && !r.in_evict) evict_push(p, pg);
@@ -672,74 +671,126 @@ akv_status auto_compact(akv_pool* p, int32_t s) {
 // ---------------------------------------------------------------------------
 // repos planning ([AKV-blog] section 2; [Leyline] Method)
 // ---------------------------------------------------------------------------
-// Per-token total delta (difference array over the spans); dropped tokens get 0.
-akv_status repos_totals(akv_pool* p, SeqRec& q, const akv_span* sp, const int32_t* d, int32_t n,
-                        std::vector<int64_t>& tot) {
+// Runs of logical tokens [b, e) that move by one total delta d != 0 (the sum
+// over the spans covering them); dropped tokens inside a run do not move.
+struct Run {
+  int32_t b, e;
+  int64_t d;
+};
+
+// Spans and deltas to runs in ascending token order (a sweep over the span
+// ends), then the range check of every moved position.
+akv_status repos_runs(const SeqRec& q, const akv_span* sp, const int32_t* d, int32_t n, std::vector<Run>& runs) {
   const int32_t len = (int32_t)q.slot.size();
   akv_status st = check_spans(sp, n, len);
   if (st != AKV_OK) return st;
   if (n > 0 && !d) return fail(AKV_EINVAL, "delta is NULL");
-  std::vector<int64_t> diff(len + 1, 0);
-  for (int32_t i = 0; i < n; ++i) {
-    diff[sp[i].begin] += d[i];
-    diff[sp[i].end] -= d[i];
+  std::vector<std::pair<int32_t, int64_t>> ev;
+  ev.reserve(2 * (size_t)n);
+  for (int32_t i = 0; i < n; ++i)
+    if (sp[i].begin < sp[i].end && d[i] != 0) {
+      ev.emplace_back(sp[i].begin, (int64_t)d[i]);
+      ev.emplace_back(sp[i].end, -(int64_t)d[i]);
+    }
+  std::sort(ev.begin(), ev.end(), [](const auto& a, const auto& b) { return a.first < b.first; });
+  runs.clear();
+  int64_t cur = 0;
+  int32_t x0 = 0;
+  for (size_t i = 0; i < ev.size();) {
+    const int32_t x = ev[i].first;
+    if (cur != 0 && x0 < x) runs.push_back({x0, x, cur});
+    for (; i < ev.size() && ev[i].first == x; ++i) cur += ev[i].second;
+    x0 = x;
   }
-  tot.assign(len, 0);
-  int64_t run = 0;
-  for (int32_t t = 0; t < len; ++t) {
-    run += diff[t];
-    if (q.dropped[t] || run == 0) continue;
-    const int64_t np = (int64_t)q.pos[t] + run;
-    if (np < 0 || np > kInt32Max)
-      return fail(AKV_ERANGE, "token %d would move to position %lld", t, (long long)np);
-    tot[t] = run;
-  }
+  for (const Run& r : runs)
+    for (int32_t t = r.b; t < r.e; ++t) {
+      if (q.dropped[t]) continue;
+      const int64_t np = (int64_t)q.pos[t] + r.d;
+      if (np < 0 || np > kInt32Max)
+        return fail(AKV_ERANGE, "token %d would move to position %lld", t, (long long)np);
+    }
   return AKV_OK;
 }
 
-// Work items: runs of consecutive slots of one page with one delta, in logical
-// token order, cut to about 16 KiB of rotated keys each (half a 16-token page
-// of 8 heads x 128 dims) so the blocks spread evenly over the CUs.
-void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<int64_t>& tot,
+// Sort rotation items by page * S + lo (LSD radix, 11-bit digits, as many
+// passes as the largest key needs).
+void sort_by_first_slot(std::vector<akv::RotItem>& items, int32_t S) {
+  const size_t n = items.size();
+  if (n < 2) return;
+  uint32_t kmax = 0;
+  std::vector<uint32_t> key(n), key2(n);
+  for (size_t i = 0; i < n; ++i) {
+    key[i] = (uint32_t)items[i].page * (uint32_t)S + (uint32_t)items[i].lo;
+    kmax = std::max(kmax, key[i]);
+  }
+  std::vector<akv::RotItem> tmp(n);
+  uint32_t cnt[2048];
+  for (int shift = 0; shift < 32 && (kmax >> shift) != 0; shift += 11) {
+    std::fill(cnt, cnt + 2048, 0u);
+    for (size_t i = 0; i < n; ++i) cnt[(key[i] >> shift) & 2047] += 1;
+    uint32_t sum = 0;
+    for (uint32_t& c : cnt) {
+      const uint32_t c0 = c;
+      c = sum;
+      sum += c0;
+    }
+    for (size_t i = 0; i < n; ++i) {
+      const uint32_t j = cnt[(key[i] >> shift) & 2047]++;
+      tmp[j] = items[i];
+      key2[j] = key[i];
+    }
+    items.swap(tmp);
+    key.swap(key2);
+  }
+}
+
+// Work items: runs of consecutive slots of one page with one delta, in the
+// runs' token order, cut to about 16 KiB of rotated keys each (half a 16-token
+// page of 8 heads x 128 dims) so the blocks spread evenly over the CUs.
+void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<Run>& runs,
                  std::vector<akv::RotItem>& items, std::vector<int32_t>& deltas) {
-  const int32_t S = p->L.page_size;
+  const int32_t S = p->L.page_size, lg = p->log2S;
   const int32_t row_bytes = p->rope_heads() * p->L.d_rope * 2;
   const int32_t max_rows = std::max<int32_t>(1, 16384 / row_bytes);
   std::unordered_map<int64_t, int32_t> didx;
   items.clear();
   deltas.clear();
-  int64_t last_delta = 0;   // deltas are constant along runs: skip the lookup there
-  int32_t di = -1;
-  for (int32_t t = 0; t < (int32_t)tot.size(); ++t) {
-    if (tot[t] == 0) continue;
-    const int32_t slot = q.slot[t];
-    const int32_t pg = slot / S, off = slot - pg * S;
-    if (di < 0 || tot[t] != last_delta) {
-      auto f = didx.find(tot[t]);
-      if (f == didx.end()) {
-        di = (int32_t)deltas.size();
-        deltas.push_back((int32_t)tot[t]);
-        didx.emplace(tot[t], di);
-      } else {
-        di = f->second;
+  size_t span_tokens = 0;
+  for (const Run& r : runs) span_tokens += (size_t)(r.e - r.b);
+  items.reserve(span_tokens / (size_t)std::min(max_rows, S) + 2 * runs.size() + 16);
+  for (const Run& r : runs) {
+    int32_t di = -1;   // looked up at the run's first moved token
+    for (int32_t t = r.b; t < r.e; ++t) {
+      if (q.dropped[t]) continue;
+      if (di < 0) {
+        auto f = didx.find(r.d);
+        if (f == didx.end()) {
+          di = (int32_t)deltas.size();
+          deltas.push_back((int32_t)r.d);
+          didx.emplace(r.d, di);
+        } else {
+          di = f->second;
+        }
       }
-      last_delta = tot[t];
+      const int32_t slot = q.slot[t];
+      const int32_t pg = slot >> lg, off = slot & (S - 1);
+      if (!items.empty() && items.back().page == pg && items.back().hi == off &&
+          items.back().didx == di && items.back().hi - items.back().lo < max_rows)
+        items.back().hi += 1;
+      else
+        items.push_back({pg, off, off + 1, di});
     }
-    if (!items.empty() && items.back().page == pg && items.back().hi == off &&
-        items.back().didx == di && items.back().hi - items.back().lo < max_rows)
-      items.back().hi += 1;
-    else
-      items.push_back({pg, off, off + 1, di});
   }
-  // Physical page order: neighbouring blocks then touch neighbouring memory.
-  std::sort(items.begin(), items.end(), [](const akv::RotItem& a, const akv::RotItem& b) {
-    return a.page != b.page ? a.page < b.page : a.lo < b.lo;
-  });
+  // Physical page order, then slot order in a page: neighbouring blocks then
+  // touch neighbouring memory.  Items never overlap, so an item's first slot
+  // is a unique key for that order: LSD radix sort on it.
+  sort_by_first_slot(items, S);
 }
 
-void repos_commit(SeqRec& q, const std::vector<int64_t>& tot) {
-  for (size_t t = 0; t < tot.size(); ++t)
-    if (tot[t]) q.pos[t] = (int32_t)(q.pos[t] + tot[t]);
+void repos_commit(SeqRec& q, const std::vector<Run>& runs) {
+  for (const Run& r : runs)
+    for (int32_t t = r.b; t < r.e; ++t)
+      if (!q.dropped[t]) q.pos[t] = (int32_t)(q.pos[t] + r.d);
   q.stale();
 }
 
@@ -747,18 +798,24 @@ void repos_commit(SeqRec& q, const std::vector<int64_t>& tot) {
 // clear the debt.
 akv_status materialize_seq(akv_pool* p, SeqRec& q) {
   if (!q.lagging) return AKV_OK;
-  std::vector<int64_t> tot(q.slot.size(), 0);
-  for (size_t t = 0; t < tot.size(); ++t)
-    if (!q.dropped[t]) tot[t] = q.lag[t];
+  std::vector<Run> runs;
+  const int32_t len = (int32_t)q.slot.size();
+  for (int32_t t = 0; t < len; ++t) {
+    if (q.dropped[t] || q.lag[t] == 0) continue;
+    if (!runs.empty() && runs.back().e == t && runs.back().d == q.lag[t])
+      runs.back().e = t + 1;
+    else
+      runs.push_back({t, t + 1, q.lag[t]});
+  }
   std::vector<akv::RotItem> items;
   std::vector<int32_t> deltas;
-  repos_items(p, q, tot, items, deltas);
+  repos_items(p, q, runs, items, deltas);
   akv_status st = scratch_fits(p, rotate_scratch_bytes(p, items.size(), deltas.size(), 1));
   if (st != AKV_OK) return st;
   st = device_rotate(p, items, deltas);
   if (st != AKV_OK) return st;
-  for (size_t t = 0; t < tot.size(); ++t)
-    if (tot[t]) q.lag[t] = 0;
+  for (const Run& r : runs)
+    for (int32_t t = r.b; t < r.e; ++t) q.lag[t] = 0;
   q.lagging = false;
   return AKV_OK;
 }
@@ -1252,15 +1309,16 @@ akv_status akv_repos_deferred(akv_pool* p, int32_t s, const akv_span* spans, con
     SeqRec* q;
     akv_status st = get_seq(p, s, &q);
     if (st != AKV_OK) return st;
-    std::vector<int64_t> tot;
-    st = repos_totals(p, *q, spans, delta, n, tot);
+    std::vector<Run> runs;
+    st = repos_runs(*q, spans, delta, n, runs);
     if (st != AKV_OK) return st;
-    for (size_t t = 0; t < tot.size(); ++t)
-      if (tot[t]) {
-        q->lag[t] = (int32_t)(q->lag[t] + tot[t]);
-        q->lagging = true;
-      }
-    repos_commit(*q, tot);
+    for (const Run& r : runs)
+      for (int32_t t = r.b; t < r.e; ++t)
+        if (!q->dropped[t]) {
+          q->lag[t] = (int32_t)(q->lag[t] + r.d);
+          q->lagging = true;
+        }
+    repos_commit(*q, runs);
     return AKV_OK;
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
@@ -1298,17 +1356,17 @@ akv_status akv_repos(akv_pool* p, int32_t s, const akv_span* spans, const int32_
     SeqRec* q;
     akv_status st = get_seq(p, s, &q);
     if (st != AKV_OK) return st;
-    std::vector<int64_t> tot;
-    st = repos_totals(p, *q, spans, delta, n, tot);
+    std::vector<Run> runs;
+    st = repos_runs(*q, spans, delta, n, runs);
     if (st != AKV_OK) return st;
     std::vector<akv::RotItem> items;
     std::vector<int32_t> deltas;
-    repos_items(p, *q, tot, items, deltas);
+    repos_items(p, *q, runs, items, deltas);
     st = scratch_fits(p, rotate_scratch_bytes(p, items.size(), deltas.size(), 1));
     if (st != AKV_OK) return st;
     st = device_rotate(p, items, deltas);
     if (st != AKV_OK) return st;
-    repos_commit(*q, tot);
+    repos_commit(*q, runs);
     return AKV_OK;
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
@@ -1346,17 +1404,17 @@ akv_status akv_repos_layers(akv_pool* const* pools, int32_t n_pools, int32_t s, 
       qs.push_back(oq);
       layers.push_back(o);
     }
-    std::vector<int64_t> tot;
-    st = repos_totals(p, *q, spans, delta, n, tot);
+    std::vector<Run> runs;
+    st = repos_runs(*q, spans, delta, n, runs);
     if (st != AKV_OK) return st;
     std::vector<akv::RotItem> items;
     std::vector<int32_t> deltas;
-    repos_items(p, *q, tot, items, deltas);
+    repos_items(p, *q, runs, items, deltas);
     st = scratch_fits(p, rotate_scratch_bytes(p, items.size(), deltas.size(), n_pools));
     if (st != AKV_OK) return st;
     st = device_rotate(p, items, deltas, layers);
     if (st != AKV_OK) return st;
-    for (SeqRec* r : qs) repos_commit(*r, tot);
+    for (SeqRec* r : qs) repos_commit(*r, runs);
     return AKV_OK;
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
@@ -1371,12 +1429,12 @@ akv_status akv_repos_plan(akv_pool* p, int32_t s, const akv_span* spans, const i
     SeqRec* q;
     akv_status st = get_seq(p, s, &q);
     if (st != AKV_OK) return st;
-    std::vector<int64_t> tot;
-    st = repos_totals(p, *q, spans, delta, n, tot);
+    std::vector<Run> runs;
+    st = repos_runs(*q, spans, delta, n, runs);
     if (st != AKV_OK) return st;
     std::vector<akv::RotItem> items;
     std::vector<int32_t> deltas;
-    repos_items(p, *q, tot, items, deltas);
+    repos_items(p, *q, runs, items, deltas);
     int32_t k = 0;
     const int32_t S = p->L.page_size;
     for (auto& it : items)
@@ -1454,12 +1512,15 @@ akv_status akv_splice(akv_pool* p, int32_t s, const akv_span* spans, const int32
     std::vector<uint8_t> in_span(H, 0);
     for (int32_t j = 0; j < n; ++j)
       for (int32_t i = spans[j].begin; i < spans[j].end; ++i) in_span[i] = 1;
-    std::vector<int64_t> tot(q->slot.size(), 0);
+    std::vector<Run> runs;
     for (int32_t i = 0; i < H; ++i) {
       if (in_span[i] || down[i] == 0) continue;
       const int64_t np = (int64_t)q->pos[vis[i]] + down[i];
       if (np < 0 || np > kInt32Max) return fail(AKV_ERANGE, "splice moves a position out of range");
-      tot[vis[i]] = down[i];
+      if (!runs.empty() && runs.back().e == vis[i] && runs.back().d == down[i])
+        runs.back().e = vis[i] + 1;
+      else
+        runs.push_back({vis[i], vis[i] + 1, down[i]});
     }
     // pages for the stubs, counting those the drop will make evictable
     {
@@ -1488,13 +1549,12 @@ akv_status akv_splice(akv_pool* p, int32_t s, const akv_span* spans, const int32
       st = device_append(p, slots, sK, sKpe, sV);
       if (st != AKV_OK) return st;
     }
-    tot.resize(q->slot.size(), 0);
     std::vector<akv::RotItem> items;
     std::vector<int32_t> deltas;
-    repos_items(p, *q, tot, items, deltas);
+    repos_items(p, *q, runs, items, deltas);
     st = device_rotate(p, items, deltas);
     if (st != AKV_OK) return st;
-    repos_commit(*q, tot);
+    repos_commit(*q, runs);
     if (stub_pos_out) std::copy(stub_pos.begin(), stub_pos.end(), stub_pos_out);
     return auto_compact(p, s);
   } catch (const std::bad_alloc&) {
