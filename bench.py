@@ -15,6 +15,7 @@ records on the pool's stream around each of its launches.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -246,6 +247,8 @@ def run_config(args) -> dict:
         timed = rep >= args.warmup
         pool.timing_enable(timed)
         lists = []
+        gc.collect()
+        gc.disable()        # no collector pause inside the timed step
         t0 = time.perf_counter()
         for i, op in enumerate(ops[i0:], start=i0):
             if isinstance(op, W.Append):
@@ -264,6 +267,7 @@ def run_config(args) -> dict:
                 D.apply_op(pool, op, keep)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        gc.enable()
         if timed:
             walls.append(wall)
             for k in tot:
@@ -452,11 +456,15 @@ def main():
     for k in akv.KERNEL_KINDS:
         pool.timing_read(k)
     torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()            # a collector pause (tens of ms) would land in the timed steps
     t0 = time.perf_counter()
     for c in range(args.warmup, n_copies):
         step(seqs[c])
+    t_host = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     segs, page_lists = page_lists_of(seqs[-1])
     pct = {k: [round(float(x), 5) for x in np.percentile(pool.timing_samples(k), [10, 50, 90])]
            for k in ("attention", "rotate")}
@@ -518,6 +526,7 @@ def main():
         "roofline_repos_layers": layers_rec,
         "roofline_compact": comp_rec,
         "kernels_ms_per_step": {k: round(v[0] / max(args.steps, 1), 5) for k, v in kt.items()},
+        "host_ms_per_step": round(t_host / args.steps * 1e3, 4),
         "attention_pairs": int(pairs),
         "query_tokens_per_s": round(att.q.shape[0] / (ms_step * 1e-3), 1),
         "repositioned_tokens_per_s": round(n_rep / (rot_ms * 1e-3), 1),

@@ -111,6 +111,18 @@ struct akv_pool {
   size_t scratch_bytes = 0;
   size_t scratch_base = 0;  // first byte available to a call
   hipStream_t stream = nullptr;
+  // Metadata uploads run on their own stream, so a call's tables can arrive
+  // while the kernels of earlier calls still run; the pool stream waits for
+  // each upload.  Per-call scratch is taken round-robin from [scratch_base,
+  // scratch_bytes), and an upload into a range waits (on the copy stream)
+  // for the last call that used that range.
+  hipStream_t cstream = nullptr;
+  size_t ring_head = 0;
+  struct RingUse {
+    size_t b0, e0, b1, e1;   // at most two ranges (a call may wrap once)
+    hipEvent_t ev;           // recorded on the pool stream after the call's kernels
+  };
+  std::deque<RingUse> ring_uses;
   int n_cu = 256;
   double thr = kDefaultCompactThreshold;
 
@@ -156,7 +168,8 @@ akv_status stg_reserve(akv_pool* p, size_t n, char** out) {
   Staging& s = p->stg;
   n = align_up(std::max<size_t>(n, 16), 256);
   if (n > s.cap) {
-    hipError_t e = hipStreamSynchronize(p->stream);
+    hipError_t e = hipStreamSynchronize(p->cstream);
+    if (e == hipSuccess) e = hipStreamSynchronize(p->stream);
     if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
     for (auto& r : s.pending) s.spare.push_back(r.ev);
     s.pending.clear();
@@ -192,32 +205,96 @@ akv_status stg_reserve(akv_pool* p, size_t n, char** out) {
 }
 
 // Copy a filled staging region to device memory on the pool stream.
+// The copy runs on the copy stream; the pool stream waits for it, so the
+// call's kernels (enqueued after this) see the data.
 akv_status stg_upload(akv_pool* p, const char* host, void* dev, size_t n) {
   if (n == 0) return AKV_OK;
-  hipError_t e = hipMemcpyAsync(dev, host, n, hipMemcpyHostToDevice, p->stream);
+  hipError_t e = hipMemcpyAsync(dev, host, n, hipMemcpyHostToDevice, p->cstream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(H2D)");
   hipEvent_t ev;
   e = stg_event(p, &ev);
   if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-  e = hipEventRecord(ev, p->stream);
+  e = hipEventRecord(ev, p->cstream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   const size_t off = (size_t)(host - p->stg.base);
   p->stg.pending.push_back({off, off + align_up(std::max<size_t>(n, 16), 256), ev});
+  e = hipStreamWaitEvent(p->stream, ev, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   return AKV_OK;
 }
 
-// Bump allocator over the per-call part of the scratch buffer.
+// The copy stream waits until every earlier call that used bytes of [b, e)
+// has finished on the pool stream (the newest such call is enough: the pool
+// stream is in order), and forgets those calls.
+void ring_wait(akv_pool* p, size_t b, size_t e) {
+  auto& u = p->ring_uses;
+  int last = -1;
+  for (int i = 0; i < (int)u.size(); ++i)
+    if ((u[i].b0 < e && b < u[i].e0) || (u[i].b1 < e && b < u[i].e1)) last = i;
+  // keep the list short: also retire the oldest calls once it grows long
+  if (last < 0 && u.size() > 256) last = 127;
+  if (last < 0) return;
+  (void)hipStreamWaitEvent(p->cstream, u[last].ev, 0);
+  for (int i = 0; i <= last; ++i) {
+    p->stg.spare.push_back(u.front().ev);
+    u.pop_front();
+  }
+}
+
+// Per-call scratch, taken round-robin from [scratch_base, scratch_bytes):
+// `need` (the call's bound, when known) starts the call at the ring's start
+// if it does not fit before the end.  On destruction the call's ranges are
+// recorded with an event on the pool stream, enqueued after its kernels.
 struct ScratchCursor {
   akv_pool* p;
-  size_t off;
-  explicit ScratchCursor(akv_pool* pp) : p(pp), off(pp->scratch_base) {}
+  size_t off;            // next byte
+  size_t first = 0;      // the call's first byte
+  bool bad = false, wrapped = false, any = false;
+  size_t r0b = 0, r0e = 0, r1b = 0, r1e = 0;
+  explicit ScratchCursor(akv_pool* pp, size_t need = 0) : p(pp), off(pp->ring_head) {
+    if (off < p->scratch_base || off + align_up(need, 256) > p->scratch_bytes) off = p->scratch_base;
+    first = off;
+  }
+  ScratchCursor(const ScratchCursor&) = delete;
+  ScratchCursor& operator=(const ScratchCursor&) = delete;
   char* take(size_t n) {
+    const size_t m = align_up(std::max<size_t>(n, 1), 256);
     off = align_up(off, 256);
+    if (off + m > p->scratch_bytes) {
+      // wrap once; the new range must stay clear of this call's own bytes
+      if (wrapped || p->scratch_base + m > first) {
+        bad = true;
+        return p->scratch + p->scratch_base;
+      }
+      wrapped = true;
+      off = p->scratch_base;
+    }
+    if (!bad && p->device) ring_wait(p, off, off + m);
+    if (!wrapped) {
+      if (!any) r0b = off;
+      r0e = off + m;
+    } else {
+      if (r1e == 0) r1b = off;
+      r1e = off + m;
+    }
+    any = true;
     char* r = p->scratch + off;
-    off += n;
+    off += m;
     return r;
   }
-  bool ok() const { return off <= p->scratch_bytes; }
+  bool ok() const { return !bad; }
+  size_t needed() const { return bad ? p->scratch_bytes + 1 : off; }
+  ~ScratchCursor() {
+    if (!any || bad || !p->device) return;
+    hipEvent_t ev;
+    if (stg_event(p, &ev) != hipSuccess) return;
+    if (hipEventRecord(ev, p->stream) != hipSuccess) {
+      p->stg.spare.push_back(ev);
+      return;
+    }
+    p->ring_uses.push_back({r0b, r0e, r1b, r1e, ev});
+    p->ring_head = off;
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -472,7 +549,8 @@ akv_status upload_array(akv_pool* p, ScratchCursor& sc, const void* src, size_t 
   std::memcpy(h, src, n);
   *dev = sc.take(n);
   if (!sc.ok())
-    return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
+    return fail(AKV_ENOMEM, "scratch too small for this call (%zu bytes per call)",
+                                 p->scratch_bytes - p->scratch_base);
   return stg_upload(p, h, *dev, n);
 }
 
@@ -486,7 +564,8 @@ akv_status upload_arrays(akv_pool* p, ScratchCursor& sc, std::initializer_list<s
   akv_status st = stg_reserve(p, total, &h);
   if (st != AKV_OK) return st;
   char* d = sc.take(total);
-  if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
+  if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small for this call (%zu bytes per call)",
+                                 p->scratch_bytes - p->scratch_base);
   size_t off = 0;
   int i = 0;
   for (const auto& pr : parts) {
@@ -523,7 +602,7 @@ akv_status check_launch(hipError_t e, const char* what) {
 akv_status device_append(akv_pool* p, const std::vector<int32_t>& slots, const void* K,
                          const void* Kpe, const void* V) {
   if (!p->device || !K) return AKV_OK;
-  ScratchCursor sc(p);
+  ScratchCursor sc(p, slots.size() * 4 + 256);
   void* dslots;
   akv_status st = upload_array(p, sc, slots.data(), slots.size() * 4, &dslots);
   if (st != AKV_OK) return st;
@@ -553,7 +632,7 @@ akv_status device_rotate(akv_pool* p, const std::vector<akv::RotItem>& items,
   std::vector<uint16_t*> krs;
   if (layers.empty()) krs.push_back(p->rope_array());
   for (akv_pool* l : layers) krs.push_back(l->rope_array());
-  ScratchCursor sc(p);
+  ScratchCursor sc(p, rotate_scratch_bytes(p, items.size(), deltas.size(), krs.size()));
   void* dv[3];
   akv_status st = upload_arrays(p, sc,
                                 {{items.data(), items.size() * sizeof(akv::RotItem)},
@@ -563,7 +642,8 @@ akv_status device_rotate(akv_pool* p, const std::vector<akv::RotItem>& items,
   if (st != AKV_OK) return st;
   void *ditems = dv[0], *ddeltas = dv[1], *dkrs = dv[2];
   float* dtab = (float*)sc.take(deltas.size() * (size_t)p->L.d_rope * 4);
-  if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
+  if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small for this call (%zu bytes per call)",
+                                 p->scratch_bytes - p->scratch_base);
   hipError_t e = akv::launch_rot_table(p->stream, p->L.d_rope, (const int32_t*)ddeltas,
                                        (int)deltas.size(), (const double*)p->scratch, dtab);
   if (e != hipSuccess) return check_launch(e, "rotation table kernel launch");
@@ -588,7 +668,7 @@ hipError_t move_tokens(akv_pool* p, const akv::MovePair* pairs, int n, const flo
 
 akv_status device_move(akv_pool* p, const std::vector<akv::MovePair>& mv) {
   if (!p->device || mv.empty()) return AKV_OK;
-  ScratchCursor sc(p);
+  ScratchCursor sc(p, mv.size() * sizeof(akv::MovePair) + 256);
   void* dmv;
   akv_status st = upload_array(p, sc, mv.data(), mv.size() * sizeof(akv::MovePair), &dmv);
   if (st != AKV_OK) return st;
@@ -1030,11 +1110,18 @@ akv_status akv_pool_create(const akv_layout* layout, const int32_t* page_order, 
         delete p;
         return fail(AKV_ENOMEM, "scratch must hold at least %zu bytes", tab + 65536);
       }
+      hipError_t ce = hipStreamCreateWithFlags(&p->cstream, hipStreamNonBlocking);
+      if (ce != hipSuccess) {
+        p->cstream = nullptr;
+        delete p;
+        return hip_fail(ce, "hipStreamCreateWithFlags(copy stream)");
+      }
       int dev = 0;
       hipDeviceProp_t prop;
       if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
         p->n_cu = prop.multiProcessorCount;
       p->scratch_base = tab;
+      p->ring_head = tab;
       char* h;
       akv_status st = stg_reserve(p, tab, &h);
       if (st == AKV_OK) {
@@ -1060,6 +1147,11 @@ akv_status akv_pool_create(const akv_layout* layout, const int32_t* page_order, 
 akv_status akv_pool_destroy(akv_pool* p) {
   if (!p) return AKV_OK;
   if (p->device) (void)hipStreamSynchronize(p->stream);
+  if (p->cstream) {
+    (void)hipStreamSynchronize(p->cstream);
+    (void)hipStreamDestroy(p->cstream);
+  }
+  for (auto& u : p->ring_uses) (void)hipEventDestroy(u.ev);
   for (auto& r : p->stg.pending) (void)hipEventDestroy(r.ev);
   for (auto e : p->stg.spare) (void)hipEventDestroy(e);
   if (p->stg.base) (void)hipHostFree(p->stg.base);
@@ -1185,13 +1277,14 @@ akv_status akv_seq_clone(akv_pool* p, int32_t src, int32_t first, int32_t n, int
       if (lags[i]) qd2.lagging = true;
     }
     if (!p->device) return AKV_OK;
-    ScratchCursor sc(p);
+    ScratchCursor sc(p, mv.size() * sizeof(akv::MovePair) + (size_t)p->L.d_rope * 4 + 4 * 256);
     void *dmv, *ddelta;
     st = upload_array(p, sc, mv.data(), mv.size() * sizeof(akv::MovePair), &dmv);
     if (st == AKV_OK) st = upload_array(p, sc, &delta, 4, &ddelta);
     if (st != AKV_OK) return st;
     float* dtab = (float*)sc.take((size_t)p->L.d_rope * 4);
-    if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
+    if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small for this call (%zu bytes per call)",
+                                 p->scratch_bytes - p->scratch_base);
     const akv_layout& L = p->L;
     hipError_t e = hipSuccess;
     if (delta != 0) {
@@ -1767,7 +1860,13 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
         o += x.hi - x.lo;
       }
     }
-    ScratchCursor sc(p);
+    const size_t keys4 = (size_t)std::max<int64_t>(total, 1) * 4;
+    const size_t need = plan.segs.size() * sizeof(akv::AttnSeg) + plan.items.size() * sizeof(akv::AttnItem) +
+                        plan.comb.size() * sizeof(akv::CombItem) + ex_used.size() * sizeof(akv::Extent) +
+                        (ex_off.size() + ex_didx.size() + rot_deltas.size()) * 4 + keys4 * (fused ? 2 : 1) +
+                        rot_deltas.size() * (size_t)L.d_rope * 4 + (size_t)plan.part_rows * (L.d_v + 2) * 4 +
+                        12 * 256;
+    ScratchCursor sc(p, need);
     void* dv[7];
     akv_status st = upload_arrays(p, sc,
                                   {{plan.segs.data(), plan.segs.size() * sizeof(akv::AttnSeg)},
@@ -1790,7 +1889,8 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
       part_o = (float*)sc.take((size_t)plan.part_rows * L.d_v * 4);
       part_ml = (float*)sc.take((size_t)plan.part_rows * 2 * 4);
     }
-    if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small: need at least %zu bytes", sc.off);
+    if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small for this call (%zu bytes per call)",
+                                 p->scratch_bytes - p->scratch_base);
 
     hipError_t e;
     {

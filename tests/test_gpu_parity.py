@@ -100,9 +100,9 @@ def _check_attention(outs, res, wl, rows_per_seg=None):
     return worst
 
 
-def _full_parity(wl, keep_log=False):
+def _full_parity(wl, keep_log=False, **pool_kw):
     _say(f"[gpu] {wl.name}: layout {wl.layout}")
-    pool, outs = D.run(wl)
+    pool, outs = D.run(wl, **pool_kw)
     res = oracle.run_workload(wl, keep_log=keep_log)
     _check_tables(pool, res.pool)
     wk = _check_visible_kv(pool, res.pool, wl.layout)
@@ -283,6 +283,34 @@ def test_fuzz_mla_full(seed, kph, pairing):
 
 def test_c3_mla_full():
     _full_parity(W.c3_mla(0))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_scratch_ring_small_buffer(seed):
+    """Per-call tables are taken round-robin from the scratch buffer and
+    uploaded on a copy stream that waits for the last call using the range.
+    With the smallest buffer (of 1, 2, 4, ... MiB) that holds the largest
+    call, the ring wraps many times over a script of back-to-back calls
+    without syncs; every table, key and output still matches the oracle.  A
+    buffer too small for a call fails that call with AKV_ENOMEM."""
+    wl = W.fuzz_small(400 + seed, n_seqs=3, n_rounds=6, page_size=8, head_dims=(64,), groups=(4,))
+    for mib in (1, 2, 4, 8, 16, 32, 64):
+        _say(f"[gpu] ring: {wl.name} with {mib} MiB of scratch")
+        try:
+            pool, outs = D.run(wl, scratch_bytes=mib << 20)
+        except akv.AkvError as e:
+            torch.cuda.synchronize()
+            assert "scratch too small" in str(e)
+            continue
+        break
+    else:
+        pytest.fail("no scratch size held the script's largest call")
+    res = oracle.run_workload(wl)
+    _check_tables(pool, res.pool)
+    _check_visible_kv(pool, res.pool, wl.layout)
+    wa = _check_attention(outs, res, wl)
+    _say(f"[gpu] ring: {mib} MiB, worst attention abs err {wa:.2e}")
+    pool.close()
 
 
 def test_attention_edge_cases():
