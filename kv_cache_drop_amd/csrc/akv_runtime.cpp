@@ -149,6 +149,13 @@ struct akv_pool {
   uint16_t* rope_array() const { return L.d_nope > 0 ? kpe : k; }
 };
 
+namespace akv {
+LaunchEvents& launch_events() {
+  thread_local LaunchEvents ev;
+  return ev;
+}
+}  // namespace akv
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -309,20 +316,30 @@ hipError_t tev_get(akv_pool* p, hipEvent_t* ev) {
   return hipEventCreate(ev);
 }
 
+// Times the kernels launched between construction and done(): the launches
+// stamp the two events themselves (akv::launch_events).  A region that
+// launched nothing records no sample.
 struct KTimer {
   akv_pool* p;
   int kind;
   hipEvent_t a = nullptr, b = nullptr;
   KTimer(akv_pool* pp, int k) : p(pp), kind(k) {
     if (p->timing && tev_get(p, &a) == hipSuccess && tev_get(p, &b) == hipSuccess)
-      (void)hipEventRecord(a, p->stream);
+      akv::launch_events() = {a, b};
     else
       a = b = nullptr;
   }
   void done() {
     if (a && b) {
-      (void)hipEventRecord(b, p->stream);
-      p->tev.push_back({kind, a, b});
+      akv::LaunchEvents& ev = akv::launch_events();
+      const bool launched = ev.start == nullptr;
+      ev = akv::LaunchEvents{};
+      if (launched) {
+        p->tev.push_back({kind, a, b});
+      } else {
+        p->ev_spare.push_back(a);
+        p->ev_spare.push_back(b);
+      }
       a = b = nullptr;
     }
   }
