@@ -156,6 +156,31 @@ akv_status akv_drop(akv_pool* pool, int32_t seq, const akv_span* spans, int32_t 
  * force it runs only above the fragmentation threshold. */
 akv_status akv_compact(akv_pool* pool, int32_t seq, int32_t force);
 
+/* Deferred compaction ([AKV-blog] section 7, Dilemma 2: the defragmentation
+ * pass runs asynchronously, in decode bubbles, without pausing inference).  AKV_COMPACT_IMMEDIATE (the default):
+ * akv_drop and akv_splice compact a sequence as soon as it exceeds the
+ * threshold.  AKV_COMPACT_DEFERRED: they only append it to a FIFO queue (once;
+ * releasing the sequence removes it), and the caller runs the copies when the
+ * GPU has room, with akv_compact_pending.  Errors: AKV_EINVAL (unknown mode). */
+enum { AKV_COMPACT_IMMEDIATE = 0, AKV_COMPACT_DEFERRED = 1 };
+akv_status akv_compaction_mode(akv_pool* pool, int32_t mode);
+
+/* Compact queued sequences in queue order: a sequence no longer above the
+ * threshold leaves the queue without a copy; the walk stops at the first one
+ * whose visible tokens would take the moved total past max_tokens, that the
+ * allocator cannot supply pages for, or whose copy list does not fit the
+ * scratch buffer, and after max_seqs compactions.  Each compaction is the same
+ * as akv_compact's; the copies of consecutive compactions share one kernel
+ * launch unless a sequence takes its fresh pages from the evictable queue (it
+ * then starts a new launch, ordered after the copies that read those pages).
+ * seqs_out (max_seqs entries, may be NULL) receives the compacted sequences,
+ * n_out their number.  Errors: AKV_EINVAL (negative budget, NULL n_out). */
+akv_status akv_compact_pending(akv_pool* pool, int64_t max_tokens, int32_t max_seqs, int32_t* seqs_out,
+                               int32_t* n_out);
+
+/* The queued sequences in queue order (the first cap of them; n_out = all). */
+akv_status akv_compact_queue(akv_pool* pool, int32_t* seqs_out, int32_t cap, int32_t* n_out);
+
 /* repos ([AKV-blog] section 2, The Repos Primitive; [Leyline] Method): every
  * retained token covered by spans gets the sum of their deltas d (signed);
  * its position becomes pos + d and its rotated key part becomes R(d) k, with

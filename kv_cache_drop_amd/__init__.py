@@ -57,6 +57,9 @@ SYMBOLS = {
     "akv_append": [_P, _I, _P, _P, _P, _IP, _I],
     "akv_drop": [_P, _I, _IP, _I],
     "akv_compact": [_P, _I, _I],
+    "akv_compaction_mode": [_P, _I],
+    "akv_compact_pending": [_P, ctypes.c_int64, _I, _IP, _IP],
+    "akv_compact_queue": [_P, _IP, _I, _IP],
     "akv_repos": [_P, _I, _IP, _IP, _I],
     "akv_repos_layers": [ctypes.POINTER(_P), _I, _I, _IP, _IP, _I],
     "akv_repos_deferred": [_P, _I, _IP, _IP, _I],
@@ -239,6 +242,26 @@ class Pool:
 
     def compact(self, seq: int, force: bool = True) -> None:
         _check(lib().akv_compact(self._h, seq, int(bool(force))))
+
+    def compaction_mode(self, deferred: bool) -> None:
+        """Deferred: drops and splices queue fragmented sequences instead of
+        compacting them (akv_compaction_mode)."""
+        _check(lib().akv_compaction_mode(self._h, int(bool(deferred))))
+
+    def compact_pending(self, max_tokens: int, max_seqs: int = 1 << 30) -> list:
+        """Compact queued sequences within the budget; returns their ids."""
+        n = ctypes.c_int32()
+        out = np.zeros(max(min(max_seqs, len(self.compact_queue())), 1), np.int32)
+        _check(lib().akv_compact_pending(self._h, int(max_tokens), min(max_seqs, len(out)), _ptr(out),
+                                         ctypes.byref(n)))
+        return out[: n.value].tolist()
+
+    def compact_queue(self) -> list:
+        n = ctypes.c_int32()
+        _check(lib().akv_compact_queue(self._h, None, 0, ctypes.byref(n)))
+        out = np.zeros(max(n.value, 1), np.int32)
+        _check(lib().akv_compact_queue(self._h, _ptr(out), n.value, ctypes.byref(n)))
+        return out[: n.value].tolist()
 
     def repos(self, seq: int, spans, deltas) -> None:
         sp = _i32(spans).reshape(-1, 2)

@@ -79,6 +79,7 @@ struct SeqRec {
   bool vis_ok = false;
   std::vector<akv_extent> ext; // cached page-table image of vis (valid with ext_ok)
   bool ext_ok = false;
+  bool queued = false;         // waiting in the deferred-compaction queue
   void stale() { vis_ok = ext_ok = false; }
 };
 
@@ -125,6 +126,8 @@ struct akv_pool {
   std::deque<RingUse> ring_uses;
   int n_cu = 256;
   double thr = kDefaultCompactThreshold;
+  int compact_mode = AKV_COMPACT_IMMEDIATE;
+  std::deque<int32_t> compact_q;   // deferred compactions, in the order queued
 
   std::deque<int32_t> free_q;
   std::deque<std::pair<int32_t, uint32_t>> evict_q;
@@ -699,7 +702,9 @@ akv_status device_move(akv_pool* p, const std::vector<akv::MovePair>& mv) {
 // ---------------------------------------------------------------------------
 // compaction ([AKV-blog] section 7, Dilemma 2)
 // ---------------------------------------------------------------------------
-akv_status compact_seq(akv_pool* p, int32_t s) {
+// Host side of compacting s: fresh pages, new slots, old pages to the
+// evictable queue; the copies are appended to mv for the caller to launch.
+akv_status compact_plan(akv_pool* p, int32_t s, std::vector<akv::MovePair>& mv) {
   SeqRec& q = p->seqs[s];
   const std::vector<int32_t> order = visible(q);  // copy: q.vis is rebuilt below
   const int32_t S = p->L.page_size;
@@ -710,9 +715,7 @@ akv_status compact_seq(akv_pool* p, int32_t s) {
   std::vector<int32_t> dest;
   dest.reserve(need);
   for (int64_t i = 0; i < need; ++i) dest.push_back(take_page(p, s));
-  std::vector<akv::MovePair> mv;
-  mv.reserve(nv);
-  std::vector<std::vector<int32_t>*> touched;
+  mv.reserve(mv.size() + nv);
   for (int64_t i = 0; i < nv; ++i) {
     const int32_t t = order[i];
     const int32_t dst = dest[i / S] * S + (int32_t)(i % S);
@@ -740,6 +743,13 @@ akv_status compact_seq(akv_pool* p, int32_t s) {
     if (!r.in_evict) evict_push(p, pg);
   }
   q.stale();
+  return AKV_OK;
+}
+
+akv_status compact_seq(akv_pool* p, int32_t s) {
+  std::vector<akv::MovePair> mv;
+  akv_status st = compact_plan(p, s, mv);
+  if (st != AKV_OK) return st;
   return device_move(p, mv);
 }
 
@@ -756,9 +766,19 @@ void drop_tokens(akv_pool* p, SeqRec& q, int32_t b, int32_t e) {
   q.stale();
 }
 
+// Above the threshold: compact now when the allocator can supply the pages
+// (skipped otherwise), or, in deferred mode, queue the sequence for
+// akv_compact_pending.
 akv_status auto_compact(akv_pool* p, int32_t s) {
   SeqRec& q = p->seqs[s];
   if (fragmentation(p, q) > p->thr) {
+    if (p->compact_mode == AKV_COMPACT_DEFERRED) {
+      if (!q.queued) {
+        q.queued = true;
+        p->compact_q.push_back(s);
+      }
+      return AKV_OK;
+    }
     const int64_t need = (q.n_vis + p->L.page_size - 1) / p->L.page_size;
     if (need <= available(p)) return compact_seq(p, s);
   }
@@ -1209,6 +1229,10 @@ akv_status akv_seq_release(akv_pool* p, int32_t s) {
   q->pages.clear();
   q->tail = -1;
   q->alive = false;
+  if (q->queued) {
+    p->compact_q.erase(std::find(p->compact_q.begin(), p->compact_q.end(), s));
+    q->queued = false;
+  }
   q->vis.clear();
   q->stale();
   return AKV_OK;
@@ -1407,6 +1431,76 @@ akv_status akv_compact(akv_pool* p, int32_t s, int32_t force) {
     st = scratch_fits(p, (size_t)q->n_vis * sizeof(akv::MovePair) + 256);
     if (st != AKV_OK) return st;
     return compact_seq(p, s);
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_compaction_mode(akv_pool* p, int32_t mode) {
+  if (!p) return fail(AKV_EINVAL, "NULL pool");
+  if (mode != AKV_COMPACT_IMMEDIATE && mode != AKV_COMPACT_DEFERRED)
+    return fail(AKV_EINVAL, "unknown compaction mode %d", mode);
+  p->compact_mode = mode;
+  return AKV_OK;
+}
+
+akv_status akv_compact_queue(akv_pool* p, int32_t* seqs_out, int32_t cap, int32_t* n_out) {
+  if (!p || !n_out) return fail(AKV_EINVAL, "NULL argument");
+  if (cap < 0 || (cap > 0 && !seqs_out)) return fail(AKV_EINVAL, "bad output");
+  *n_out = (int32_t)p->compact_q.size();
+  for (int32_t i = 0; i < cap && i < *n_out; ++i) seqs_out[i] = p->compact_q[i];
+  return AKV_OK;
+}
+
+akv_status akv_compact_pending(akv_pool* p, int64_t max_tokens, int32_t max_seqs, int32_t* seqs_out,
+                               int32_t* n_out) {
+  try {
+    if (!p || !n_out) return fail(AKV_EINVAL, "NULL argument");
+    if (max_tokens < 0 || max_seqs < 0) return fail(AKV_EINVAL, "negative budget");
+    *n_out = 0;
+    const int32_t S = p->L.page_size;
+    std::vector<akv::MovePair> mv;
+    // Copies of one batch run in one launch.  A sequence whose fresh pages
+    // would come from the evictable queue (possibly pages this batch still
+    // reads) starts a new batch, so its copies run after the earlier ones.
+    auto flush = [&]() -> akv_status {
+      if (mv.empty()) return AKV_OK;
+      akv_status st = device_move(p, mv);
+      mv.clear();
+      return st;
+    };
+    int64_t used = 0;
+    int32_t k = 0;
+    while (!p->compact_q.empty() && k < max_seqs) {
+      const int32_t s = p->compact_q.front();
+      SeqRec& q = p->seqs[s];
+      if (fragmentation(p, q) <= p->thr) {   // appends since queuing brought it under
+        q.queued = false;
+        p->compact_q.pop_front();
+        continue;
+      }
+      const int64_t need = (q.n_vis + S - 1) / S;
+      if (used + q.n_vis > max_tokens || need > available(p)) break;
+      if ((int64_t)p->free_q.size() < need) {
+        akv_status st = flush();
+        if (st != AKV_OK) return st;
+      }
+      auto fits = [&](size_t n) { return !p->device || p->scratch_base + n * sizeof(akv::MovePair) + 4352 <= p->scratch_bytes; };
+      if (!fits(mv.size() + q.n_vis)) {
+        akv_status st = flush();
+        if (st != AKV_OK) return st;
+        if (!fits(q.n_vis)) break;   // stays queued; akv_compact reports the shortage
+      }
+      akv_status st = compact_plan(p, s, mv);
+      if (st != AKV_OK) return st;
+      used += q.n_vis;
+      q.queued = false;
+      p->compact_q.pop_front();
+      if (seqs_out) seqs_out[k] = s;
+      ++k;
+      *n_out = k;
+    }
+    return flush();
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
   }

@@ -167,6 +167,8 @@ class Pool:
         self.seqs: List[_Seq] = []
         self.keep_log = keep_log
         self.compact_threshold = compact_threshold
+        self.deferred = False           # deferred compaction: fragmented sequences wait in `queue`
+        self.queue: deque = deque()
         self.inv_freq = rope_inv_freq(L.d_rope, L.rope_theta) if inv_freq is None else np.asarray(inv_freq, np.float64)
 
     # -- sequences -----------------------------------------------------------
@@ -198,6 +200,8 @@ class Pool:
         q.pages = []
         q.tail = -1
         q.alive = False
+        if s in self.queue:
+            self.queue.remove(s)
 
     # -- allocation ------------------------------------------------------------
     def _available(self) -> int:
@@ -338,7 +342,12 @@ class Pool:
 
     def _auto_compact(self, s: int) -> None:
         """Automatic compaction is opportunistic: above the threshold it runs
-        when the allocator can supply the fresh pages, else it is skipped."""
+        when the allocator can supply the fresh pages, else it is skipped.  In
+        deferred mode the sequence joins the queue instead (once)."""
+        if self.fragmentation(s) > self.compact_threshold and self.deferred:
+            if s not in self.queue:
+                self.queue.append(s)
+            return
         if self.fragmentation(s) > self.compact_threshold:
             nv = int(np.count_nonzero(~self.seqs[s].dropped))
             if (nv + self.S - 1) // self.S <= self._available():
@@ -380,6 +389,32 @@ class Pool:
             if not self.in_evict[p]:
                 self.evictable.append(p)
                 self.in_evict[p] = True
+
+    # -- deferred compaction ([AKV-blog] section 7, Dilemma 2: the pass runs
+    # asynchronously, in decode bubbles) ---------------------------------------
+    def compaction_mode(self, deferred: bool) -> None:
+        self.deferred = bool(deferred)
+
+    def compact_pending(self, max_tokens: int, max_seqs: int = 1 << 30) -> list:
+        """Walk the queue front to back: a sequence no longer above the
+        threshold leaves it without a copy; the walk stops at the first one
+        whose visible tokens would take the moved total past max_tokens or
+        that the allocator cannot supply pages for, and after max_seqs
+        compactions.  Returns the compacted sequences."""
+        done, used = [], 0
+        while self.queue and len(done) < max_seqs:
+            s = self.queue[0]
+            if self.fragmentation(s) <= self.compact_threshold:
+                self.queue.popleft()
+                continue
+            nv = int(np.count_nonzero(~self.seqs[s].dropped))
+            if used + nv > max_tokens or (nv + self.S - 1) // self.S > self._available():
+                break
+            self.compact(s, force=True)
+            used += nv
+            self.queue.popleft()
+            done.append(s)
+        return done
 
     # -- repos ([AKV-blog] section 2, The Repos Primitive; [Leyline] Method) -----
     def repos_deltas(self, s: int, spans, deltas) -> np.ndarray:

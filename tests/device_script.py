@@ -70,6 +70,12 @@ def apply_op(pool: akv.Pool, op, keep=None):
         pool.compact(op.seq, bool(op.force))
     elif isinstance(op, W.Clone):
         pool.clone(op.src, op.first, op.n, op.dst, op.delta)
+    elif isinstance(op, W.CompactMode):
+        pool.compaction_mode(op.deferred)
+    elif isinstance(op, W.CompactPending):
+        return pool.compact_pending(op.max_tokens, op.max_seqs)
+    elif isinstance(op, W.Release):
+        pool.seq_release(op.seq)
     else:
         raise TypeError(op)
     return None

@@ -285,6 +285,15 @@ def test_c3_mla_full():
     _full_parity(W.c3_mla(0))
 
 
+@pytest.mark.parametrize("seed,pages_factor", [(0, 3.0), (1, 3.0), (2, 0.7), (3, 0.7)])
+def test_deferred_compaction_full(seed, pages_factor):
+    """Queued compactions run in later passes, several sequences' copies in one
+    launch, a new launch when fresh pages come back from the evictable queue
+    (tight pool): tables and every visible K/V row bit-exact, attention
+    against the oracle."""
+    _full_parity(W.deferred_compaction(seed, pages_factor=pages_factor))
+
+
 @pytest.mark.parametrize("seed", [0, 1])
 def test_scratch_ring_small_buffer(seed):
     """Per-call tables are taken round-robin from the scratch buffer and

@@ -11,6 +11,8 @@ is exported, and failing calls leave no trace.
 import os
 import re
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -51,6 +53,7 @@ def _compare(hp, op_pool, tag=""):
     fr, ev = hp.queues()
     assert fr.tolist() == list(op_pool.free), tag
     assert ev.tolist() == list(op_pool.evictable), tag
+    assert hp.compact_queue() == list(op_pool.queue), tag
     for s, q in enumerate(op_pool.seqs):
         if not q.alive:
             continue
@@ -111,6 +114,15 @@ def _replay(wl: W.Workload, check_every_op=True):
         elif isinstance(op, W.Clone):
             hp.clone(op.src, op.first, op.n, op.dst, op.delta)
             oracle.apply_op(op_pool, op)
+        elif isinstance(op, (W.CompactMode, W.Release)):
+            if isinstance(op, W.CompactMode):
+                hp.compaction_mode(op.deferred)
+            else:
+                hp.seq_release(op.seq)
+            oracle.apply_op(op_pool, op)
+        elif isinstance(op, W.CompactPending):
+            got = hp.compact_pending(op.max_tokens, op.max_seqs)
+            assert got == oracle.apply_op(op_pool, op), tag
         elif isinstance(op, W.Attention):
             ex, rows = oracle.segment_lists(op_pool, op.segments)
             got = [hp.visible(sg.seq, sg.mask_spans if len(sg.mask_spans) else None) for sg in op.segments]
@@ -120,6 +132,65 @@ def _replay(wl: W.Workload, check_every_op=True):
             _compare(hp, op_pool, tag)
     _compare(hp, op_pool, wl.name + " end")
     return hp, op_pool
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("pages_factor", [3.0, 0.7])
+def test_deferred_compaction_scripts_bit_exact(seed, pages_factor):
+    """Deferred compaction: the queue after every op, every pass's compacted
+    sequences and the page tables equal the oracle's (with a tight pool the
+    compactions take pages back from the evictable queue)."""
+    wl = W.deferred_compaction(seed, pages_factor=pages_factor)
+    _replay(wl)
+    kinds = [type(o).__name__ for o in wl.ops]
+    assert "Release" in kinds and kinds.count("CompactPending") >= 3
+
+
+def test_deferred_compaction_queue_rules():
+    """Hand-built cases: drops queue a fragmented sequence once and compact
+    nothing; a budget below the head's visible count compacts nothing; one
+    sequence per pass with max_seqs 1; a sequence appended back under the
+    threshold leaves the queue without a copy; release removes it; immediate
+    mode compacts at the drop.  The same calls on the oracle agree."""
+    lay = W.Layout(4, 2, 0, 16, 16, 8, 64)
+    order = np.arange(64, dtype=np.int32)
+    for impl in ("library", "oracle"):
+        p = _host_pool(lay, order) if impl == "library" else AO.Pool(lay, order)
+        cm = (lambda d: p.compaction_mode(d))
+        queue = (lambda: p.compact_queue()) if impl == "library" else (lambda: list(p.queue))
+        app = (lambda s, pos: p.append(s, pos)) if impl == "library" else \
+            (lambda s, pos: p.append(s, pos, np.zeros((len(pos), 2, 16)), None, np.zeros((len(pos), 2, 16))))
+        cm(True)
+        a, b, c = p.seq_create(), p.seq_create(), p.seq_create()
+        for s in (a, b, c):
+            app(s, np.arange(64))
+        shred = np.asarray([(i, i + 4) for i in range(0, 64, 8)], np.int32)   # half of every page
+        before = p.queues() if impl == "library" else None
+        p.drop(a, shred)
+        p.drop(a, shred)                      # already queued: stays once
+        p.drop(b, shred)
+        assert queue() == [a, b], impl
+        if impl == "library":
+            assert [x.tolist() for x in p.queues()] == [x.tolist() for x in before]   # no copy yet
+        assert p.compact_pending(31) == [], impl        # a has 32 visible tokens
+        assert p.compact_pending(1000, 1) == [a], impl
+        assert queue() == [b], impl
+        p.drop(c, shred)
+        assert queue() == [b, c], impl
+        app(b, np.arange(64, 200))              # b back under the threshold
+        p.seq_release(c)
+        assert queue() == [b], impl
+        assert p.compact_pending(1000) == [], impl      # b leaves without a copy
+        assert queue() == [], impl
+        cm(False)
+        d = p.seq_create()
+        app(d, np.arange(64))
+        p.drop(d, shred)
+        assert queue() == [], impl
+        assert p.fragmentation(d) == 0.0 if impl == "oracle" else p.info(d)[2] == 0.0
+    hp = _host_pool(lay, order)
+    assert akv.lib().akv_compaction_mode(hp._h, 2) == akv.AKV_EINVAL
+    assert akv.lib().akv_compact_pending(hp._h, -1, 1, None, ctypes.byref(ctypes.c_int32())) == akv.AKV_EINVAL
 
 
 @pytest.mark.parametrize("seed", range(12))

@@ -145,6 +145,22 @@ class Compact:
 
 
 @dataclass
+class CompactMode:
+    deferred: bool           # True: drops and splices queue fragmented sequences
+
+
+@dataclass
+class CompactPending:
+    max_tokens: int          # budget of moved tokens for this pass
+    max_seqs: int = 1 << 30
+
+
+@dataclass
+class Release:
+    seq: int
+
+
+@dataclass
 class Clone:
     src: int             # retained tokens [first, first+n) of src ...
     first: int
@@ -664,6 +680,74 @@ def fuzz_small(seed: int, mla: bool = False, pairing: int = 0, n_seqs: int = 2,
     ops.append(Attention(q, segs))
     wl = Workload(f"fuzz_{seed}", lay, rng.permutation(lay.num_pages).astype(np.int32), ops)
     return wl
+
+
+def deferred_compaction(seed: int, n_seqs: int = 4, n_rounds: int = 5, page_size: int = 8,
+                        pages_factor: float = 3.0) -> Workload:
+    """Sequences whose drops leave them fragmented, in deferred-compaction
+    mode: the compactions wait in the queue and run in later passes under
+    token budgets (some too small for the queue's head, some limited to one
+    sequence), some queued sequences are brought back under the threshold by
+    appends before their turn, one queued sequence is released, and attention
+    runs between passes and at the end ([AKV-blog] section 7, Dilemma 2)."""
+    rng = _rng(seed)
+    lay = Layout(8, 2, 0, 64, 64, page_size, 0, rope_theta=10000.0)
+    ops = [CompactMode(True)]
+    n_all = n_seqs + 1                   # the last sequence is released while queued
+    ntok, npos = [0] * n_all, [64] * n_all
+    total = 0
+    for _ in range(n_all):
+        ops.append(SeqCreate())
+
+    def append(s, n):
+        nonlocal total
+        ops.append(_append_op(rng, lay, s, np.arange(npos[s], npos[s] + n, dtype=np.int32)))
+        ntok[s] += n
+        npos[s] += n
+        total += n
+
+    def shred(s):
+        # drop every other block of 4..12 tokens over a random range: most
+        # pages keep some visible token, so fragmentation passes 0.4
+        b = int(rng.integers(0, max(1, ntok[s] // 4)))
+        sp, t = [], b
+        while t < ntok[s]:
+            w = int(rng.integers(4, 13))
+            sp.append((t, min(t + w, ntok[s])))
+            t += 2 * w
+        ops.append(Drop(s, _spans(sp)))
+
+    for rnd in range(n_rounds):
+        for s in range(n_all):
+            if s == n_seqs and rnd > 1:
+                continue
+            append(s, int(rng.integers(24, 96)))
+            if rng.random() < 0.6:
+                shred(s)
+            if rng.random() < 0.3:
+                b = int(rng.integers(0, ntok[s]))
+                ops.append(Repos(s, _spans([(b, ntok[s])]), np.asarray([int(rng.integers(-20, 21))], np.int32)))
+        if rnd == 1:
+            shred(n_seqs)
+            ops.append(Release(n_seqs))
+        budget = [0, 40, 150, 1 << 20][int(rng.integers(0, 4))]
+        ops.append(CompactPending(budget, [1, 2, 1 << 30][int(rng.integers(0, 3))]))
+        if rnd == 2:                     # appends after queuing can bring one under the threshold
+            append(int(rng.integers(0, n_seqs)), 200)
+    segs, row = [], 0
+    for s in range(n_seqs):
+        nq = int(rng.integers(4, 20))
+        hist = ntok[s]
+        append(s, nq)
+        segs += _query_segments(s, hist, row, [nq], [[]])
+        row += nq
+    ops.append(CompactPending(1 << 20))
+    q = _normal_bf16(rng, (row, lay.n_q_heads, lay.d_qk), scale=0.5)
+    ops.append(Attention(q, segs))
+    # pages_factor near 1: compactions must take pages back from the evictable queue
+    lay.num_pages = int(pages_factor * ((total + page_size - 1) // page_size)) + 8 * n_all + 16
+    return Workload(f"deferred_compaction_{seed}", lay, rng.permutation(lay.num_pages).astype(np.int32), ops,
+                    notes={"deferred_compaction": True})
 
 
 CONFIGS = {
