@@ -41,13 +41,15 @@ _COPY_SHA1 = "2a16fbd3bdf4c924c007ee7a8f5e9337713b3565"       # akv_copy.hip
 _DECODE_SHA1 = "76f26fe087c03d7e32a848e7a557f93254f5fc17"     # akv_decode.hip
 COUNTERS = {
     "fetch_scale": 1048576 / 524302, "write_scale": 1.0,
-    "attention": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 110925, "write_kib": 16384},
-    "rotate": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 39271, "write_kib": 77633},
-    "rotate_32_layers": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 1248286,
-                         "write_kib": 2484294},
-    "compact": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 85345, "write_kib": 165578},
+    "attention": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 110730, "write_kib": 16390},
+    "rotate": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 39284, "write_kib": 77631},
+    "rotate_32_layers": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 1248998,
+                         "write_kib": 2484434},
+    "compact": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 85349, "write_kib": 165593},
     # the decode step of 48 requests (seed 0), k_decode_attn<false>
-    "decode": {"source": "akv_decode.hip", "sha1": _DECODE_SHA1, "fetch_kib": 611213, "write_kib": 5168},
+    "decode": {"source": "akv_decode.hip", "sha1": _DECODE_SHA1, "fetch_kib": 611195, "write_kib": 5168},
+    # the retrigger clone (seed 0), k_move_tokens with the rotation
+    "clone": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 80734, "write_kib": 157501},
 }
 
 
@@ -335,7 +337,9 @@ def run_config(args) -> dict:
         cl_per_step = tot["clone"][1] / max(args.steps, 1)
         cl_gbps = clone_bytes / (cl_ms * cl_per_step * 1e-3) / 1e9
         rec["roofline_clone"] = {"bound": "hbm", "achieved": round(cl_gbps, 1), "peak": PEAK_HBM_GBPS,
-                                 "unit": "GB/s", "frac": round(cl_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                                 "unit": "GB/s", "frac": round(cl_gbps / PEAK_HBM_GBPS, 4),
+                                 "traffic": counted_traffic("clone") if args.config == "retrigger" and args.seed == 0
+                                 else None,
                                  "kernel": "k_move_tokens", "bytes_per_step": clone_bytes,
                                  "launches_per_step": cl_per_step, "avg_launch_ms": round(cl_ms, 5)}
     if rot_ms is not None:

@@ -32,7 +32,6 @@
 #include <cstring>
 
 #include "akv_internal.h"
-#include "akv_launch.h"
 
 namespace akv {
 namespace {
@@ -373,16 +372,16 @@ hipError_t launch_expand_didx(hipStream_t st, const Extent* ex, const int32_t* e
                               int n_ext, int32_t* out) {
   if (n_ext <= 0) return hipSuccess;
   const int blocks = std::min(4096, (n_ext + 255) / 256);
-  launch(k_expand_didx, dim3(blocks), dim3(256), 0, st, ex, ex_off, ex_didx, n_ext, out);
+  hipLaunchKernelGGL(k_expand_didx, dim3(blocks), dim3(256), 0, st, ex, ex_off, ex_didx, n_ext, out);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_attn(hipStream_t st, const AttnArgs& a) {
   if (a.n_items <= 0) return hipSuccess;
   if (a.key_didx)
-    launch(k_decode_attn<true>, dim3(a.n_items), dim3(64 * DEC_WAVES), 0, st, a);
+    hipLaunchKernelGGL(k_decode_attn<true>, dim3(a.n_items), dim3(64 * DEC_WAVES), 0, st, a);
   else
-    launch(k_decode_attn<false>, dim3(a.n_items), dim3(64 * DEC_WAVES), 0, st, a);
+    hipLaunchKernelGGL(k_decode_attn<false>, dim3(a.n_items), dim3(64 * DEC_WAVES), 0, st, a);
   return hipGetLastError();
 }
 

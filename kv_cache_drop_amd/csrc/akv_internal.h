@@ -9,15 +9,6 @@
 
 namespace akv {
 
-// Events of the timed launch region in progress on this thread, set by the
-// runtime's kernel timer: the first kernel launched takes `start` and every
-// kernel launched records `stop`, so the region spans the first kernel's
-// start to the last one's end, stamped by the dispatches themselves.
-struct LaunchEvents {
-  hipEvent_t start = nullptr, stop = nullptr;
-};
-LaunchEvents& launch_events();
-
 // One repos work item: rows lo..hi-1 of one page, rotated by deltas[didx].
 struct RotItem {
   int32_t page, lo, hi, didx;

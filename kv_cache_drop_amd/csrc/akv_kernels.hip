@@ -18,7 +18,6 @@
 #include <type_traits>
 
 #include "akv_internal.h"
-#include "akv_launch.h"
 
 namespace akv {
 
@@ -164,14 +163,14 @@ __global__ __launch_bounds__(ROT_THREADS, 8) void k_rotate(uint16_t* const* __re
 hipError_t launch_rot_table(hipStream_t st, int d_rope, const int32_t* deltas, int n_deltas,
                             const double* inv_freq, float* table) {
   if (n_deltas <= 0) return hipSuccess;
-  launch(k_rot_table, dim3(n_deltas), dim3(64), 0, st, d_rope, deltas, inv_freq, table);
+  hipLaunchKernelGGL(k_rot_table, dim3(n_deltas), dim3(64), 0, st, d_rope, deltas, inv_freq, table);
   return hipGetLastError();
 }
 
 hipError_t launch_rotate(hipStream_t st, uint16_t* const* krs, int n_layers, int n_heads, int page_size,
                          int d_rope, int pairing, const RotItem* items, int n_items, const float* table) {
   if (n_items <= 0 || n_layers <= 0) return hipSuccess;
-  launch(k_rotate, dim3(n_items, n_layers), dim3(ROT_THREADS), 0, st, krs, n_heads, page_size,
+  hipLaunchKernelGGL(k_rotate, dim3(n_items, n_layers), dim3(ROT_THREADS), 0, st, krs, n_heads, page_size,
                      d_rope, pairing, items, table);
   return hipGetLastError();
 }
@@ -193,7 +192,7 @@ __global__ __launch_bounds__(256) void k_expand(const Extent* __restrict__ ex,
 hipError_t launch_expand(hipStream_t st, const Extent* ex, const int32_t* ex_off, int n_ext,
                          int page_size, int32_t* slots) {
   if (n_ext <= 0) return hipSuccess;
-  launch(k_expand, dim3((n_ext + 255) / 256), dim3(256), 0, st, ex, ex_off, n_ext,
+  hipLaunchKernelGGL(k_expand, dim3((n_ext + 255) / 256), dim3(256), 0, st, ex, ex_off, n_ext,
                      page_size, slots);
   return hipGetLastError();
 }
@@ -1057,17 +1056,17 @@ template <int DQK, int DV, int DNOPE>
 static hipError_t launch_attn_t(hipStream_t st, const AttnArgs& a) {
   if constexpr (DQK == 128 && DV == 128 && DNOPE == 0) {
     if (attn_waves(DNOPE) == 8 && attn_use_dl()) {
-      launch((k_seg_attn_dl<128, 128, 0, 8, 1, 4>), dim3(a.n_items), dim3(512), 0, st, a);
+      hipLaunchKernelGGL((k_seg_attn_dl<128, 128, 0, 8, 1, 4>), dim3(a.n_items), dim3(512), 0, st, a);
       return hipGetLastError();
     }
   }
   if constexpr (DNOPE == 128) {
-    launch((k_seg_attn<DQK, DV, DNOPE, 8>), dim3(a.n_items), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE, 8>), dim3(a.n_items), dim3(512), 0, st, a);
   } else {
     if (attn_waves(DNOPE) == 8)
-      launch((k_seg_attn<DQK, DV, DNOPE, 8>), dim3(a.n_items), dim3(512), 0, st, a);
+      hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE, 8>), dim3(a.n_items), dim3(512), 0, st, a);
     else
-      launch((k_seg_attn<DQK, DV, DNOPE, 4>), dim3(a.n_items), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE, 4>), dim3(a.n_items), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -1091,9 +1090,9 @@ hipError_t launch_combine(hipStream_t st, const AttnArgs& a, const CombItem* ite
   const int bpi = (a.rows_per_block + 3) / 4;
   const dim3 grid((unsigned)(n_items * bpi));
   switch (d_v) {
-    case 128: launch((k_combine<128>), grid, dim3(256), 0, st, a, items, bpi); break;
-    case 64: launch((k_combine<64>), grid, dim3(256), 0, st, a, items, bpi); break;
-    case 32: launch((k_combine<32>), grid, dim3(256), 0, st, a, items, bpi); break;
+    case 128: hipLaunchKernelGGL((k_combine<128>), grid, dim3(256), 0, st, a, items, bpi); break;
+    case 64: hipLaunchKernelGGL((k_combine<64>), grid, dim3(256), 0, st, a, items, bpi); break;
+    case 32: hipLaunchKernelGGL((k_combine<32>), grid, dim3(256), 0, st, a, items, bpi); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -112,16 +112,15 @@ struct akv_pool {
   size_t scratch_bytes = 0;
   size_t scratch_base = 0;  // first byte available to a call
   hipStream_t stream = nullptr;
-  // Metadata uploads run on their own stream, so a call's tables can arrive
-  // while the kernels of earlier calls still run; the pool stream waits for
-  // each upload.  Per-call scratch is taken round-robin from [scratch_base,
-  // scratch_bytes), and an upload into a range waits (on the copy stream)
-  // for the last call that used that range.
+  // While the pool stream is busy, metadata uploads run on their own stream,
+  // so a call's tables arrive while the kernels of earlier calls still run;
+  // the pool stream waits for each such upload.  Per-call scratch is taken
+  // round-robin from [scratch_base, scratch_bytes), and an upload into a
+  // range waits (on the copy stream) for the last call that used the range.
   hipStream_t cstream = nullptr;
   size_t ring_head = 0;
   struct RingUse {
     size_t b0, e0, b1, e1;   // at most two ranges (a call may wrap once)
-    hipEvent_t ev;           // recorded on the pool stream after the call's kernels
   };
   std::deque<RingUse> ring_uses;
   int n_cu = 256;
@@ -151,13 +150,6 @@ struct akv_pool {
   int rope_heads() const { return (L.d_nope > 0 && !L.kpe_per_head) ? 1 : L.n_kv_heads; }
   uint16_t* rope_array() const { return L.d_nope > 0 ? kpe : k; }
 };
-
-namespace akv {
-LaunchEvents& launch_events() {
-  thread_local LaunchEvents ev;
-  return ev;
-}
-}  // namespace akv
 
 namespace {
 
@@ -215,27 +207,36 @@ akv_status stg_reserve(akv_pool* p, size_t n, char** out) {
 }
 
 // Copy a filled staging region to device memory on the pool stream.
-// The copy runs on the copy stream; the pool stream waits for it, so the
-// call's kernels (enqueued after this) see the data.
+// While the pool stream still has work queued, the copy runs on the copy
+// stream and the pool stream waits for it: the copy then overlaps the
+// earlier kernels.  On an idle pool stream the copy is enqueued there
+// directly (fewer calls, no cross-queue wait).  Either way the call's
+// kernels, enqueued after this, see the data.
 akv_status stg_upload(akv_pool* p, const char* host, void* dev, size_t n) {
   if (n == 0) return AKV_OK;
-  hipError_t e = hipMemcpyAsync(dev, host, n, hipMemcpyHostToDevice, p->cstream);
+  const bool overlap = hipStreamQuery(p->stream) == hipErrorNotReady;
+  hipStream_t cs = overlap ? p->cstream : p->stream;
+  hipError_t e = hipMemcpyAsync(dev, host, n, hipMemcpyHostToDevice, cs);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(H2D)");
   hipEvent_t ev;
   e = stg_event(p, &ev);
   if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-  e = hipEventRecord(ev, p->cstream);
+  e = hipEventRecord(ev, cs);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   const size_t off = (size_t)(host - p->stg.base);
   p->stg.pending.push_back({off, off + align_up(std::max<size_t>(n, 16), 256), ev});
-  e = hipStreamWaitEvent(p->stream, ev, 0);
-  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  if (overlap) {
+    e = hipStreamWaitEvent(p->stream, ev, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
   return AKV_OK;
 }
 
-// The copy stream waits until every earlier call that used bytes of [b, e)
-// has finished on the pool stream (the newest such call is enough: the pool
-// stream is in order), and forgets those calls.
+// Before a range is written by an upload (which may run on the copy
+// stream), the copy stream waits until every earlier call that used bytes of
+// [b, e) has finished on the pool stream; those calls are then forgotten.
+// The calls' ranges carry no event: one recorded now on the pool stream
+// follows all of their kernels (the pool stream is in order).
 void ring_wait(akv_pool* p, size_t b, size_t e) {
   auto& u = p->ring_uses;
   int last = -1;
@@ -244,17 +245,18 @@ void ring_wait(akv_pool* p, size_t b, size_t e) {
   // keep the list short: also retire the oldest calls once it grows long
   if (last < 0 && u.size() > 256) last = 127;
   if (last < 0) return;
-  (void)hipStreamWaitEvent(p->cstream, u[last].ev, 0);
-  for (int i = 0; i <= last; ++i) {
-    p->stg.spare.push_back(u.front().ev);
-    u.pop_front();
+  hipEvent_t ev;
+  if (stg_event(p, &ev) == hipSuccess) {
+    if (hipEventRecord(ev, p->stream) == hipSuccess) (void)hipStreamWaitEvent(p->cstream, ev, 0);
+    p->stg.spare.push_back(ev);
   }
+  u.erase(u.begin(), u.begin() + last + 1);
 }
 
 // Per-call scratch, taken round-robin from [scratch_base, scratch_bytes):
 // `need` (the call's bound, when known) starts the call at the ring's start
 // if it does not fit before the end.  On destruction the call's ranges are
-// recorded with an event on the pool stream, enqueued after its kernels.
+// recorded (ring_wait orders later uploads into them after its kernels).
 struct ScratchCursor {
   akv_pool* p;
   size_t off;            // next byte
@@ -296,13 +298,7 @@ struct ScratchCursor {
   size_t needed() const { return bad ? p->scratch_bytes + 1 : off; }
   ~ScratchCursor() {
     if (!any || bad || !p->device) return;
-    hipEvent_t ev;
-    if (stg_event(p, &ev) != hipSuccess) return;
-    if (hipEventRecord(ev, p->stream) != hipSuccess) {
-      p->stg.spare.push_back(ev);
-      return;
-    }
-    p->ring_uses.push_back({r0b, r0e, r1b, r1e, ev});
+    p->ring_uses.push_back({r0b, r0e, r1b, r1e});
     p->ring_head = off;
   }
 };
@@ -319,30 +315,20 @@ hipError_t tev_get(akv_pool* p, hipEvent_t* ev) {
   return hipEventCreate(ev);
 }
 
-// Times the kernels launched between construction and done(): the launches
-// stamp the two events themselves (akv::launch_events).  A region that
-// launched nothing records no sample.
 struct KTimer {
   akv_pool* p;
   int kind;
   hipEvent_t a = nullptr, b = nullptr;
   KTimer(akv_pool* pp, int k) : p(pp), kind(k) {
     if (p->timing && tev_get(p, &a) == hipSuccess && tev_get(p, &b) == hipSuccess)
-      akv::launch_events() = {a, b};
+      (void)hipEventRecord(a, p->stream);
     else
       a = b = nullptr;
   }
   void done() {
     if (a && b) {
-      akv::LaunchEvents& ev = akv::launch_events();
-      const bool launched = ev.start == nullptr;
-      ev = akv::LaunchEvents{};
-      if (launched) {
-        p->tev.push_back({kind, a, b});
-      } else {
-        p->ev_spare.push_back(a);
-        p->ev_spare.push_back(b);
-      }
+      (void)hipEventRecord(b, p->stream);
+      p->tev.push_back({kind, a, b});
       a = b = nullptr;
     }
   }
@@ -1188,7 +1174,6 @@ akv_status akv_pool_destroy(akv_pool* p) {
     (void)hipStreamSynchronize(p->cstream);
     (void)hipStreamDestroy(p->cstream);
   }
-  for (auto& u : p->ring_uses) (void)hipEventDestroy(u.ev);
   for (auto& r : p->stg.pending) (void)hipEventDestroy(r.ev);
   for (auto e : p->stg.spare) (void)hipEventDestroy(e);
   if (p->stg.base) (void)hipHostFree(p->stg.base);
