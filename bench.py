@@ -84,7 +84,7 @@ def attention_flops(layout, segments, page_lists) -> tuple:
     causal mask, and the number of such pairs."""
     ex = np.asarray(page_lists).reshape(-1, 3)
     pairs = 0
-    for qb, lq, eb, el in np.asarray(segments).reshape(-1, 4):
+    for qb, lq, eb, el in np.asarray(segments).reshape(-1, 4).tolist():   # Python ints: no int32 wrap
         if lq == 0:
             continue
         lkv = int((ex[eb:eb + el, 2] - ex[eb:eb + el, 1]).sum())
@@ -238,6 +238,8 @@ def run_config(args) -> dict:
     tot = {k: [0.0, 0] for k in ("attention", "rotate", "append", "compact", "expand", "combine", "clone")}
     walls, flops, pairs, kv_bytes, n_rot, n_q, clone_bytes = [], 0.0, 0, 0, 0, 0, 0
     kern = None
+    n_dec = args.decode_steps if args.config in ("decode", "decode_fused") else 1
+    first_walls = []
     for rep in range(args.warmup + args.steps):
         pool = D.make_pool(wl)
         keep = []
@@ -249,29 +251,49 @@ def run_config(args) -> dict:
         timed = rep >= args.warmup
         pool.timing_enable(timed)
         lists = []
+
+        def run_ops(shift):
+            # shift > 0: the next decode step (each request's new tokens one
+            # step further on; the same query and K/V values)
+            for i, op in enumerate(ops[i0:], start=i0):
+                if isinstance(op, W.Append):
+                    pool.append(op.seq, op.pos, dev[i][0], dev[i][1], dev[i][2])
+                elif isinstance(op, W.AppendBatch):
+                    pos = op.pos + shift * np.repeat(op.counts, op.counts).astype(np.int32)
+                    pool.append_batch(op.seqs, op.counts, pos, dev[i][0], dev[i][1], dev[i][2])
+                elif isinstance(op, W.Splice):
+                    pool.splice(op.seq, op.spans, op.stub_lens, dev[i][0], dev[i][1], dev[i][2])
+                elif isinstance(op, W.Attention):
+                    # lists built inside the library from the sequences' page tables
+                    pool.seq_attention(dev[i][0], [(sg.seq, sg.q_begin, sg.q_len,
+                                                    sg.mask_spans if len(sg.mask_spans) else None)
+                                                   for sg in op.segments], op.scale, out=dev[i][1])
+                    if shift == 0:
+                        lists.append(op)
+                else:
+                    D.apply_op(pool, op, keep)
+
         gc.collect()
         gc.disable()        # no collector pause inside the timed step
         t0 = time.perf_counter()
-        for i, op in enumerate(ops[i0:], start=i0):
-            if isinstance(op, W.Append):
-                pool.append(op.seq, op.pos, dev[i][0], dev[i][1], dev[i][2])
-            elif isinstance(op, W.AppendBatch):
-                pool.append_batch(op.seqs, op.counts, op.pos, dev[i][0], dev[i][1], dev[i][2])
-            elif isinstance(op, W.Splice):
-                pool.splice(op.seq, op.spans, op.stub_lens, dev[i][0], dev[i][1], dev[i][2])
-            elif isinstance(op, W.Attention):
-                # lists built inside the library from the sequences' page tables
-                pool.seq_attention(dev[i][0], [(sg.seq, sg.q_begin, sg.q_len,
-                                                sg.mask_spans if len(sg.mask_spans) else None)
-                                               for sg in op.segments], op.scale, out=dev[i][1])
-                lists.append(op)
-            else:
-                D.apply_op(pool, op, keep)
+        run_ops(0)
+        if n_dec > 1:
+            # the first decode step rebuilds the lists after the histories'
+            # drops and repos; the steps after it are the steady state
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for t in range(1, n_dec):
+                run_ops(t)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        if n_dec > 1:
+            first = t1 - t0
+            wall = (time.perf_counter() - t1) / (n_dec - 1)
         gc.enable()
         if timed:
             walls.append(wall)
+            if n_dec > 1:
+                first_walls.append(first)
             for k in tot:
                 ms, n = pool.timing_read(k)
                 tot[k][0] += ms
@@ -285,10 +307,25 @@ def run_config(args) -> dict:
             for op in lists:
                 rows, ex = D.segment_inputs(pool, op)     # the same lists, for the counts
                 f, p = attention_flops(L, rows, ex)
+                exa = np.asarray(ex).reshape(-1, 3)
+                kv = int((exa[:, 2] - exa[:, 1]).sum()) * L.n_kv_heads * (L.d_nope + L.d_rope + L.d_v) * 2
+                if n_dec > 1:
+                    # these are the lists after the last decode step: step t
+                    # attended (n_dec - 1 - t) * q_len fewer keys per segment;
+                    # report the mean over the steps
+                    f, p, kv = 0.0, 0, 0
+                    d_qk = L.d_nope + L.d_rope
+                    for t in range(n_dec):
+                        for qb, lq, eb, el in np.asarray(rows).reshape(-1, 4).tolist():
+                            lkv = int((exa[eb:eb + el, 2] - exa[eb:eb + el, 1]).sum()) - (n_dec - 1 - t) * lq
+                            pr = lq * (lkv - lq) + lq * (lq + 1) // 2
+                            p += pr
+                            f += 2.0 * L.n_q_heads * (d_qk + L.d_v) * pr
+                            kv += lkv * L.n_kv_heads * (d_qk + L.d_v) * 2
+                    f, p, kv = f / n_dec, p // n_dec, kv // n_dec
                 flops += float(f)
                 pairs += int(p)
-                exa = np.asarray(ex).reshape(-1, 3)
-                kv_bytes += int((exa[:, 2] - exa[:, 1]).sum()) * L.n_kv_heads * (L.d_nope + L.d_rope + L.d_v) * 2
+                kv_bytes += int(kv)
                 n_q += int(op.q.shape[0])
             # a clone reads and writes every row of each retained source token
             row_bytes = 2 * (rope_heads * L.d_rope + L.n_kv_heads * (L.d_nope + L.d_v))
@@ -304,10 +341,11 @@ def run_config(args) -> dict:
         del pool, keep
     ms_step = float(np.median(walls)) * 1e3
     attn_ms = tot["attention"][0] / max(tot["attention"][1], 1)
+    n_launch_steps = max(args.steps, 1) * n_dec     # steps whose kernels the timers saw
     rot_ms = tot["rotate"][0] / max(tot["rotate"][1], 1) if tot["rotate"][1] else None
     rep_bytes = 2.0 * rope_heads * L.d_rope * 2 * n_rot
     # per step: one attention launch; rotate launches per step = tot count / steps
-    rot_per_step = tot["rotate"][1] / max(args.steps, 1)
+    rot_per_step = tot["rotate"][1] / n_launch_steps
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     rec = {
         "metric": "segment-batch attn TFLOP/s + repos GB/s, % of MI355X roofline",
@@ -321,8 +359,14 @@ def run_config(args) -> dict:
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": kern, "flop_per_launch": flops, "kv_bytes_per_launch": kv_bytes,
                      "avg_launch_ms": round(attn_ms, 5)},
-        "kernels_ms_per_step": {k: round(v[0] / max(args.steps, 1), 5) for k, v in tot.items()},
+        "kernels_ms_per_step": {k: round(v[0] / n_launch_steps, 5) for k, v in tot.items()},
     }
+    if n_dec > 1:
+        rec["config"]["decode_steps_per_rep"] = n_dec
+        rec["first_step_ms"] = round(float(np.median(first_walls)) * 1e3, 4)
+        rec["note"] = (f"ms_per_step: steady decode steps 2..{n_dec} on the same pool (each appends one token "
+                       "per request and attends over every list); first_step_ms: the first step after the "
+                       "histories' drops and repos, which rebuilds each visible list")
     if args.config in ("decode", "decode_fused"):
         # one query row per kv-head group: the launch streams the visible K/V once
         hbm_gbps = kv_bytes / (attn_ms * 1e-3) / 1e9
@@ -334,7 +378,7 @@ def run_config(args) -> dict:
                            "avg_launch_ms": round(attn_ms, 5)}
     if tot["clone"][1]:
         cl_ms = tot["clone"][0] / tot["clone"][1]
-        cl_per_step = tot["clone"][1] / max(args.steps, 1)
+        cl_per_step = tot["clone"][1] / n_launch_steps
         cl_gbps = clone_bytes / (cl_ms * cl_per_step * 1e-3) / 1e9
         rec["roofline_clone"] = {"bound": "hbm", "achieved": round(cl_gbps, 1), "peak": PEAK_HBM_GBPS,
                                  "unit": "GB/s", "frac": round(cl_gbps / PEAK_HBM_GBPS, 4),
@@ -381,6 +425,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--decode-steps", type=int, default=8, help="decode steps per rep (decode configs)")
     ap.add_argument("--cpu-rows", type=int, default=16, help="oracle query rows per segment")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--repos-layers", type=int, default=32,

@@ -79,8 +79,13 @@ struct SeqRec {
   bool vis_ok = false;
   std::vector<akv_extent> ext; // cached page-table image of vis (valid with ext_ok)
   bool ext_ok = false;
+  // the same image with runs also cut where the owed rotation changes, and
+  // each extent's owed rotation (valid with lg_ok)
+  std::vector<akv_extent> ext_lg;
+  std::vector<int32_t> ext_lg_lag;
+  bool lg_ok = false;
   bool queued = false;         // waiting in the deferred-compaction queue
-  void stale() { vis_ok = ext_ok = false; }
+  void stale() { vis_ok = ext_ok = lg_ok = false; }
 };
 
 // Pinned host ring for metadata uploads.  A region may be rewritten once the
@@ -446,12 +451,21 @@ void place_tokens(akv_pool* p, int32_t s, int32_t n, const int32_t* pos, int32_t
     if (q.vis_ok) {
       if (q.vis.empty() || pos[i] >= q.pos[q.vis.back()]) {
         q.vis.push_back(t0 + i);
+        const int32_t off = slot - pg * S;
         if (q.ext_ok) {
-          const int32_t off = slot - pg * S;
           if (!q.ext.empty() && q.ext.back().page == pg && q.ext.back().hi == off)
             q.ext.back().hi = off + 1;
           else
             q.ext.push_back({pg, off, off + 1});
+        }
+        if (q.lg_ok) {   // a new token owes nothing
+          if (!q.ext_lg.empty() && q.ext_lg.back().page == pg && q.ext_lg.back().hi == off &&
+              q.ext_lg_lag.back() == 0) {
+            q.ext_lg.back().hi = off + 1;
+          } else {
+            q.ext_lg.push_back({pg, off, off + 1});
+            q.ext_lg_lag.push_back(0);
+          }
         }
       } else {
         q.stale();
@@ -920,6 +934,7 @@ akv_status materialize_seq(akv_pool* p, SeqRec& q) {
   for (const Run& r : runs)
     for (int32_t t = r.b; t < r.e; ++t) q.lag[t] = 0;
   q.lagging = false;
+  q.lg_ok = false;
   return AKV_OK;
 }
 
@@ -1300,7 +1315,10 @@ akv_status akv_seq_clone(akv_pool* p, int32_t src, int32_t first, int32_t n, int
       mv[i].dst = slots[i];
       const size_t t = qd2.slot.size() - m + i;
       qd2.lag[t] = lags[i];
-      if (lags[i]) qd2.lagging = true;
+      if (lags[i]) {
+        qd2.lagging = true;
+        qd2.lg_ok = false;
+      }
     }
     if (!p->device) return AKV_OK;
     ScratchCursor sc(p, mv.size() * sizeof(akv::MovePair) + (size_t)p->L.d_rope * 4 + 4 * 256);
@@ -1831,10 +1849,17 @@ akv_status akv_seq_attention(akv_pool* p, const void* Q, int32_t n_q_tokens, con
         for (int32_t k = 0; k < sg.mask_len; ++k) std::fill(hide.begin() + m[k].begin, hide.begin() + m[k].end, 1);
       }
       const std::vector<akv_extent>* ex;
-      if (fused) {
-        build_extents_lag(p, *q, vis, sg.mask_len > 0 ? &hide : nullptr, masked, mlag);
+      if (fused && sg.mask_len > 0) {
+        build_extents_lag(p, *q, vis, &hide, masked, mlag);
         lags.insert(lags.end(), mlag.begin(), mlag.end());
         ex = &masked;
+      } else if (fused) {
+        if (!q->lg_ok) {
+          build_extents_lag(p, *q, vis, nullptr, q->ext_lg, q->ext_lg_lag);
+          q->lg_ok = true;
+        }
+        lags.insert(lags.end(), q->ext_lg_lag.begin(), q->ext_lg_lag.end());
+        ex = &q->ext_lg;
       } else if (sg.mask_len > 0) {
         build_extents(p, *q, vis, &hide, masked);
         ex = &masked;
@@ -1922,8 +1947,8 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
     const bool decode = decode_launch(p, qlens.data(), n_segs, 1);
     // distinct owed rotations of the lists (fused into the decode kernel)
     std::vector<int32_t> rot_deltas, ex_didx;
+    std::unordered_map<int32_t, int32_t> di;   // owed rotation -> its table row
     if (ext_lag) {
-      std::unordered_map<int32_t, int32_t> di;
       for (int32_t i = 0; i < n_segs; ++i)
         for (int32_t e = segs[i].ext_begin; e < segs[i].ext_begin + segs[i].ext_len; ++e)
           if (ext_lag[e] && !di.count(ext_lag[e])) {
@@ -1948,10 +1973,7 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
         ex_used.push_back({x.page, x.lo, x.hi});
         ex_off.push_back((int32_t)o);
         if (fused) {
-          int32_t d = -1;
-          if (ext_lag[e])
-            d = (int32_t)(std::find(rot_deltas.begin(), rot_deltas.end(), ext_lag[e]) - rot_deltas.begin());
-          ex_didx.push_back(d);
+          ex_didx.push_back(ext_lag[e] ? di.find(ext_lag[e])->second : -1);
         }
         o += x.hi - x.lo;
       }

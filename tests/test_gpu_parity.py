@@ -452,6 +452,25 @@ def test_decode_deferred_repos_full(seed, pairing, lq):
                                     pairing=pairing)).close()
 
 
+@pytest.mark.parametrize("deferred", [False, True])
+def test_decode_steady_steps_full(deferred):
+    """Three decode steps on one pool: after the first, each step's append
+    extends the cached page-table images (with owed rotations for deferred
+    repos) instead of rebuilding them; every step's output against the
+    oracle."""
+    wl = W.decode_batch(9, n_req=10, ctx_lo=3000, ctx_hi=9000, deferred=deferred)
+    i0 = wl.notes["step_from"]
+    ab, att = wl.ops[i0], wl.ops[i0 + 1]
+    for t in (1, 2):
+        shift = (t * np.repeat(ab.counts, ab.counts)).astype(np.int32)
+        wl.ops += [W.AppendBatch(ab.seqs, ab.counts, ab.pos + shift, ab.k, ab.kpe, ab.v),
+                   W.Attention(att.q, att.segments, att.scale)]
+    if deferred:
+        _deferred_parity(wl).close()
+    else:
+        _full_parity(wl)
+
+
 @pytest.mark.parametrize("pairing", [0, 1])
 def test_fused_rotation_equals_materialized_bit_exact(pairing):
     """The decode kernel's in-register rotation writes the same scores as
