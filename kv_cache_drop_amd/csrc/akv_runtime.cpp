@@ -105,6 +105,14 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
+// Host lists of an attention call, kept by the pool so their capacity
+// persists from call to call (calls on one pool are not re-entrant).
+struct AttnHostBufs {
+  std::vector<akv_extent> lists, masked;
+  std::vector<int32_t> lags, mlag, ex_off, ex_didx;
+  std::vector<akv::Extent> ex_used;
+};
+
 struct akv_pool {
   akv_layout L{};
   std::vector<double> inv_freq;
@@ -140,6 +148,7 @@ struct akv_pool {
   std::vector<SeqRec> seqs;
 
   Staging stg;
+  AttnHostBufs hb;
 
   bool timing = false;
   struct TEv {
@@ -996,6 +1005,9 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
   std::vector<akv::AttnItem> all;
   std::vector<int64_t> cost;
   std::vector<Group> groups;
+  all.reserve((size_t)base * target + 64);
+  cost.reserve((size_t)base * target + 64);
+  groups.reserve((size_t)base * target + 64);
   plan.comb.clear();
   int64_t part = 0;
   std::vector<int64_t> tile_base;
@@ -1054,9 +1066,12 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
   // Longest groups first, each to the least loaded XCD, so row tiles reading
   // the same K/V share that XCD's L2; then each XCD's items are dispatched
   // longest first, so the CUs of an XCD finish together.
-  std::stable_sort(groups.begin(), groups.end(),
-                   [](const Group& a, const Group& b) { return a.cost > b.cost; });
+  // (ties keep their build order: `begin` grows with it)
+  std::sort(groups.begin(), groups.end(), [](const Group& a, const Group& b) {
+    return a.cost != b.cost ? a.cost > b.cost : a.begin < b.begin;
+  });
   std::vector<std::vector<int32_t>> xbins(kXcds);
+  for (auto& b : xbins) b.reserve(all.size() / kXcds + 16);
   std::vector<int64_t> load(kXcds, 0);
   for (const Group& gr : groups) {
     int best = 0;
@@ -1066,9 +1081,11 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
     for (int32_t k = gr.begin; k < gr.end; ++k) xbins[best].push_back(k);
   }
   size_t depth = 0;
+  auto longer = [&](int32_t a, int32_t b) { return cost[a] > cost[b]; };
   for (int x = 0; x < kXcds; ++x) {
-    std::stable_sort(xbins[x].begin(), xbins[x].end(),
-                     [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
+    // one-item groups (decode) arrive already in this order
+    if (!std::is_sorted(xbins[x].begin(), xbins[x].end(), longer))
+      std::stable_sort(xbins[x].begin(), xbins[x].end(), longer);
     depth = std::max(depth, xbins[x].size());
   }
   plan.items.assign(depth * kXcds, akv::AttnItem{-1, 0, 0, 0, 0, -1});
@@ -1836,8 +1853,12 @@ akv_status akv_seq_attention(akv_pool* p, const void* Q, int32_t n_q_tokens, con
         if (st != AKV_OK) return st;
       }
     std::vector<akv_segment> rows((size_t)n_segs);
-    std::vector<akv_extent> lists, masked;
-    std::vector<int32_t> lags, mlag;
+    std::vector<akv_extent>& lists = p->hb.lists;
+    std::vector<akv_extent>& masked = p->hb.masked;
+    std::vector<int32_t>& lags = p->hb.lags;
+    std::vector<int32_t>& mlag = p->hb.mlag;
+    lists.clear();
+    lags.clear();
     for (int32_t i = 0; i < n_segs; ++i) {
       const akv_seq_segment& sg = segs[i];
       SeqRec* q = &p->seqs[sg.seq];
@@ -1946,7 +1967,9 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
     for (int32_t i = 0; i < n_segs; ++i) qlens[i] = segs[i].q_len;
     const bool decode = decode_launch(p, qlens.data(), n_segs, 1);
     // distinct owed rotations of the lists (fused into the decode kernel)
-    std::vector<int32_t> rot_deltas, ex_didx;
+    std::vector<int32_t> rot_deltas;
+    std::vector<int32_t>& ex_didx = p->hb.ex_didx;
+    ex_didx.clear();
     std::unordered_map<int32_t, int32_t> di;   // owed rotation -> its table row
     if (ext_lag) {
       for (int32_t i = 0; i < n_segs; ++i)
@@ -1964,13 +1987,26 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
     if (plan.part_rows > kInt32Max) return fail(AKV_ERANGE, "too many split-KV partial rows");
     // extent offsets for the slot expansion (over all segments' ranges, in order)
     const bool fused = !rot_deltas.empty();
-    std::vector<akv::Extent> ex_used;
-    std::vector<int32_t> ex_off;
+    // The segments' ranges usually tile the page lists in order: then the
+    // lists are uploaded as they are (akv_extent and akv::Extent share
+    // their layout); otherwise the ranges are gathered.
+    bool in_order = true;
+    int64_t covered = 0;
+    for (int32_t i = 0; i < n_segs && in_order; ++i) {
+      in_order = segs[i].ext_begin == covered;
+      covered += segs[i].ext_len;
+    }
+    in_order = in_order && covered == n_ext;
+    static_assert(sizeof(akv::Extent) == sizeof(akv_extent), "extent layouts");
+    std::vector<akv::Extent>& ex_used = p->hb.ex_used;
+    std::vector<int32_t>& ex_off = p->hb.ex_off;
+    ex_used.clear();
+    ex_off.clear();
     for (int32_t i = 0; i < n_segs; ++i) {
       int64_t o = list_off[i];
       for (int32_t e = segs[i].ext_begin; e < segs[i].ext_begin + segs[i].ext_len; ++e) {
         const akv_extent& x = page_lists[e];
-        ex_used.push_back({x.page, x.lo, x.hi});
+        if (!in_order) ex_used.push_back({x.page, x.lo, x.hi});
         ex_off.push_back((int32_t)o);
         if (fused) {
           ex_didx.push_back(ext_lag[e] ? di.find(ext_lag[e])->second : -1);
@@ -1980,7 +2016,7 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
     }
     const size_t keys4 = (size_t)std::max<int64_t>(total, 1) * 4;
     const size_t need = plan.segs.size() * sizeof(akv::AttnSeg) + plan.items.size() * sizeof(akv::AttnItem) +
-                        plan.comb.size() * sizeof(akv::CombItem) + ex_used.size() * sizeof(akv::Extent) +
+                        plan.comb.size() * sizeof(akv::CombItem) + ex_off.size() * sizeof(akv::Extent) +
                         (ex_off.size() + ex_didx.size() + rot_deltas.size()) * 4 + keys4 * (fused ? 2 : 1) +
                         rot_deltas.size() * (size_t)L.d_rope * 4 + (size_t)plan.part_rows * (L.d_v + 2) * 4 +
                         12 * 256;
@@ -1990,7 +2026,8 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
                                   {{plan.segs.data(), plan.segs.size() * sizeof(akv::AttnSeg)},
                                    {plan.items.data(), plan.items.size() * sizeof(akv::AttnItem)},
                                    {plan.comb.data(), plan.comb.size() * sizeof(akv::CombItem)},
-                                   {ex_used.data(), ex_used.size() * sizeof(akv::Extent)},
+                                   {in_order ? (const void*)page_lists : (const void*)ex_used.data(),
+                                    ex_off.size() * sizeof(akv::Extent)},
                                    {ex_off.data(), ex_off.size() * 4},
                                    {ex_didx.data(), ex_didx.size() * 4},
                                    {rot_deltas.data(), rot_deltas.size() * 4}},
@@ -2014,7 +2051,7 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
     {
       KTimer tm(p, AKV_K_EXPAND);
       e = akv::launch_expand(p->stream, (const akv::Extent*)dex, (const int32_t*)doff,
-                             (int)ex_used.size(), L.page_size, dslots);
+                             (int)ex_off.size(), L.page_size, dslots);
       tm.done();
     }
     if (e != hipSuccess) return hip_fail(e, "expand kernel launch");
@@ -2024,7 +2061,7 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
                                 (const double*)p->scratch, drot);
       if (e == hipSuccess)
         e = akv::launch_expand_didx(p->stream, (const akv::Extent*)dex, (const int32_t*)doff,
-                                    (const int32_t*)dv[5], (int)ex_used.size(), dkey_didx);
+                                    (const int32_t*)dv[5], (int)ex_off.size(), dkey_didx);
       tm.done();
       if (e != hipSuccess) return hip_fail(e, "owed-rotation table launch");
     }
