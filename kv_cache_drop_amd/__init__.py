@@ -377,11 +377,14 @@ class Pool:
         import torch
         rows, spans = [], []
         for seq, qb, ql, m in segments:
-            m = _i32(m if m is not None else np.zeros((0, 2))).reshape(-1, 2)
+            if m is None or len(m) == 0:
+                rows.append((seq, qb, ql, len(spans), 0))
+                continue
+            m = _i32(m).reshape(-1, 2)
             rows.append((seq, qb, ql, len(spans), len(m)))
             spans.extend(m.tolist())
-        sg = _i32(rows).reshape(-1, 5)
-        ms = _i32(spans).reshape(-1, 2)
+        sg = np.asarray(rows, np.int32).reshape(-1, 5)
+        ms = np.asarray(spans, np.int32).reshape(-1, 2)
         L = self.layout
         if q.dim() != 3 or q.shape[1] != L["n_q_heads"] or q.shape[2] != L["d_nope"] + L["d_rope"] \
                 or q.dtype != torch.bfloat16:
