@@ -229,6 +229,7 @@ akv_status stg_reserve(akv_pool* p, size_t n, char** out) {
 akv_status stg_upload(akv_pool* p, const char* host, void* dev, size_t n) {
   if (n == 0) return AKV_OK;
   const bool overlap = hipStreamQuery(p->stream) == hipErrorNotReady;
+  (void)hipGetLastError();   // "not ready" is a status, not an error for the launch checks that follow
   hipStream_t cs = overlap ? p->cstream : p->stream;
   hipError_t e = hipMemcpyAsync(dev, host, n, hipMemcpyHostToDevice, cs);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(H2D)");
