@@ -406,6 +406,13 @@ def test_c4_batched_sampled():
     _sampled_parity(W.c4_batched(0), n_rows=6)
 
 
+def test_c5_128k_sampled():
+    """128K tokens, 64 q heads over 8 kv heads, 60 dropped spans, 8 segments
+    of 512 queries: tables and every visible key in full, 6 random rows plus
+    the first and last of every segment against the oracle."""
+    _sampled_parity(W.c5_128k(0), n_rows=6)
+
+
 @pytest.mark.parametrize("make", [lambda: W.c1_tiny(0, "canonical"), lambda: W.fuzz_small(3, head_dims=(64, 128)),
                                   lambda: W.decode_batch(5, n_req=12, ctx_lo=1, ctx_hi=3000, q_len=2)])
 def test_seq_attention_equals_segment_attention(make):
