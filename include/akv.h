@@ -194,6 +194,16 @@ akv_status akv_compact_queue(akv_pool* pool, int32_t* seqs_out, int32_t cap, int
 akv_status akv_repos(akv_pool* pool, int32_t seq, const akv_span* spans, const int32_t* delta,
                      int32_t n_spans);
 
+/* repos of many sequences in one call: entry i applies span_counts[i] spans
+ * (and as many deltas) to seqs[i]; spans and deltas are concatenated in entry
+ * order.  The result equals akv_repos on each entry in turn; all entries are
+ * validated first (any error leaves every sequence as it was), and one
+ * rotation launch covers every entry.  The sequences must be distinct.
+ * Errors: AKV_EINVAL (a sequence named twice, negative counts), AKV_ERANGE
+ * (as akv_repos), AKV_ESTATE (released sequence). */
+akv_status akv_repos_batch(akv_pool* pool, int32_t n_seqs, const int32_t* seqs, const int32_t* span_counts,
+                           const akv_span* spans, const int32_t* delta);
+
 /* deferred repos (the fused rotation of [AKV-blog] section 4 and rule of
  * thumb 2: keys stay where they are and are turned where they are read):
  * the same validation, positions and errors as akv_repos, but no key is

@@ -61,6 +61,7 @@ SYMBOLS = {
     "akv_compact_pending": [_P, ctypes.c_int64, _I, _IP, _IP],
     "akv_compact_queue": [_P, _IP, _I, _IP],
     "akv_repos": [_P, _I, _IP, _IP, _I],
+    "akv_repos_batch": [_P, _I, _IP, _IP, _IP, _IP],
     "akv_repos_layers": [ctypes.POINTER(_P), _I, _I, _IP, _IP, _I],
     "akv_repos_deferred": [_P, _I, _IP, _IP, _I],
     "akv_materialize": [_P, _I],
@@ -267,6 +268,24 @@ class Pool:
         sp = _i32(spans).reshape(-1, 2)
         dl = _i32(deltas).reshape(-1)
         _check(lib().akv_repos(self._h, seq, _ptr(sp), _ptr(dl), len(sp)))
+
+    def repos_batch(self, entries) -> None:
+        """entries: (seq, spans [m, 2], deltas [m]) per distinct sequence; one
+        call and one rotation launch (akv_repos_batch)."""
+        sq, cnt, sps, dls = [], [], [], []
+        for seq, spans, deltas in entries:
+            sp = _i32(spans).reshape(-1, 2)
+            dl = _i32(deltas).reshape(-1)
+            if len(sp) != len(dl):
+                raise ValueError("one delta per span")
+            sq.append(seq)
+            cnt.append(len(sp))
+            sps.append(sp)
+            dls.append(dl)
+        sq, cnt = _i32(sq), _i32(cnt)
+        sp = np.concatenate(sps) if sps else np.zeros((0, 2), np.int32)
+        dl = np.concatenate(dls) if dls else np.zeros(0, np.int32)
+        _check(lib().akv_repos_batch(self._h, len(sq), _ptr(sq), _ptr(cnt), _ptr(sp), _ptr(dl)))
 
     def repos_deferred(self, seq: int, spans, deltas) -> None:
         """repos without rewriting keys: positions move, keys owe the rotation

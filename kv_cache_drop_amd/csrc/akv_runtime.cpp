@@ -874,17 +874,18 @@ void sort_by_first_slot(std::vector<akv::RotItem>& items, int32_t S) {
 // Work items: runs of consecutive slots of one page with one delta, in the
 // runs' token order, cut to about 16 KiB of rotated keys each (half a 16-token
 // page of 8 heads x 128 dims) so the blocks spread evenly over the CUs.
-void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<Run>& runs,
-                 std::vector<akv::RotItem>& items, std::vector<int32_t>& deltas) {
+// The items of one sequence's runs, appended to `items`; their deltas are
+// appended to `deltas` once each (didx maps a delta to its index).  The
+// caller sorts the items into page order.
+void repos_items_append(const akv_pool* p, const SeqRec& q, const std::vector<Run>& runs,
+                        std::vector<akv::RotItem>& items, std::vector<int32_t>& deltas,
+                        std::unordered_map<int64_t, int32_t>& didx) {
   const int32_t S = p->L.page_size, lg = p->log2S;
   const int32_t row_bytes = p->rope_heads() * p->L.d_rope * 2;
   const int32_t max_rows = std::max<int32_t>(1, 16384 / row_bytes);
-  std::unordered_map<int64_t, int32_t> didx;
-  items.clear();
-  deltas.clear();
   size_t span_tokens = 0;
   for (const Run& r : runs) span_tokens += (size_t)(r.e - r.b);
-  items.reserve(span_tokens / (size_t)std::min(max_rows, S) + 2 * runs.size() + 16);
+  items.reserve(items.size() + span_tokens / (size_t)std::min(max_rows, S) + 2 * runs.size() + 16);
   for (const Run& r : runs) {
     int32_t di = -1;   // looked up at the run's first moved token
     for (int32_t t = r.b; t < r.e; ++t) {
@@ -908,10 +909,18 @@ void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<Run>& run
         items.push_back({pg, off, off + 1, di});
     }
   }
+}
+
+void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<Run>& runs,
+                 std::vector<akv::RotItem>& items, std::vector<int32_t>& deltas) {
+  std::unordered_map<int64_t, int32_t> didx;
+  items.clear();
+  deltas.clear();
+  repos_items_append(p, q, runs, items, deltas, didx);
   // Physical page order, then slot order in a page: neighbouring blocks then
   // touch neighbouring memory.  Items never overlap, so an item's first slot
   // is a unique key for that order: LSD radix sort on it.
-  sort_by_first_slot(items, S);
+  sort_by_first_slot(items, p->L.page_size);
 }
 
 void repos_commit(SeqRec& q, const std::vector<Run>& runs) {
@@ -1592,6 +1601,45 @@ akv_status akv_repos(akv_pool* p, int32_t s, const akv_span* spans, const int32_
     st = device_rotate(p, items, deltas);
     if (st != AKV_OK) return st;
     repos_commit(*q, runs);
+    return AKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_repos_batch(akv_pool* p, int32_t n_seqs, const int32_t* seqs, const int32_t* span_counts,
+                           const akv_span* spans, const int32_t* delta) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    if (n_seqs < 0) return fail(AKV_EINVAL, "negative sequence count");
+    if (n_seqs == 0) return AKV_OK;
+    if (!seqs || !span_counts) return fail(AKV_EINVAL, "seqs and span_counts must be non-NULL");
+    // validate every entry before any change: sequences distinct (two
+    // entries on one sequence would put two items on one slot in a launch)
+    std::vector<std::vector<Run>> runs((size_t)n_seqs);
+    std::unordered_map<int32_t, int32_t> seen;
+    int64_t off = 0;
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      SeqRec* q;
+      akv_status st = get_seq(p, seqs[i], &q);
+      if (st != AKV_OK) return st;
+      if (!seen.emplace(seqs[i], i).second)
+        return fail(AKV_EINVAL, "entries %d and %d name the same sequence %d", seen[seqs[i]], i, seqs[i]);
+      if (span_counts[i] < 0) return fail(AKV_EINVAL, "entry %d: negative span count", i);
+      st = repos_runs(*q, spans ? spans + off : nullptr, delta ? delta + off : nullptr, span_counts[i], runs[i]);
+      if (st != AKV_OK) return st;
+      off += span_counts[i];
+    }
+    std::vector<akv::RotItem> items;
+    std::vector<int32_t> deltas;
+    std::unordered_map<int64_t, int32_t> didx;
+    for (int32_t i = 0; i < n_seqs; ++i) repos_items_append(p, p->seqs[seqs[i]], runs[i], items, deltas, didx);
+    sort_by_first_slot(items, p->L.page_size);
+    akv_status st = scratch_fits(p, rotate_scratch_bytes(p, items.size(), deltas.size(), 1));
+    if (st != AKV_OK) return st;
+    st = device_rotate(p, items, deltas);
+    if (st != AKV_OK) return st;
+    for (int32_t i = 0; i < n_seqs; ++i) repos_commit(p->seqs[seqs[i]], runs[i]);
     return AKV_OK;
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");

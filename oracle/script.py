@@ -53,6 +53,10 @@ def apply_op(pool: Pool, op) -> Optional[np.ndarray]:
         pool.compact(op.seq, bool(op.force))
     elif isinstance(op, W.Clone):
         pool.clone(op.src, op.first, op.n, op.dst, op.delta)
+    elif isinstance(op, W.ReposBatch):
+        # the same as one repos per entry, in entry order
+        for seq, spans, deltas in op.entries():
+            pool.repos(int(seq), spans, deltas)
     elif isinstance(op, W.CompactMode):
         pool.compaction_mode(op.deferred)
     elif isinstance(op, W.CompactPending):

@@ -70,6 +70,8 @@ def apply_op(pool: akv.Pool, op, keep=None):
         pool.compact(op.seq, bool(op.force))
     elif isinstance(op, W.Clone):
         pool.clone(op.src, op.first, op.n, op.dst, op.delta)
+    elif isinstance(op, W.ReposBatch):
+        pool.repos_batch(list(op.entries()))
     elif isinstance(op, W.CompactMode):
         pool.compaction_mode(op.deferred)
     elif isinstance(op, W.CompactPending):

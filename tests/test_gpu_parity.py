@@ -406,6 +406,31 @@ def test_c4_batched_sampled():
     _sampled_parity(W.c4_batched(0), n_rows=6)
 
 
+def test_repos_batch_bit_exact_with_per_request_repos():
+    """The 16 requests' repos in one akv_repos_batch launch write the same
+    bf16 keys as one akv_repos per request, bit for bit."""
+    _say("[gpu] repos batch vs per-request repos")
+    pools = []
+    for batched in (True, False):
+        wl = W.c4_batched(1, n_req=8, ctx_lo=3000, ctx_hi=9000, batched=batched)
+        # histories, drops and repos only (the new tokens and attention cut)
+        last = max(i for i, o in enumerate(wl.ops) if isinstance(o, (W.Drop, W.Repos, W.ReposBatch)))
+        wl.ops = wl.ops[:last + 1]
+        pool, _ = D.run(wl)
+        pools.append(pool)
+    torch.cuda.synchronize()
+    S = wl.layout.page_size
+    for s in range(8):
+        sl, _, dr = pools[0].tokens(s)
+        sl1, _, _ = pools[1].tokens(s)
+        np.testing.assert_array_equal(sl, sl1)
+        keep = sl[~dr]
+        np.testing.assert_array_equal(_rows_i16(pools[0].k_pages, keep, S), _rows_i16(pools[1].k_pages, keep, S))
+        np.testing.assert_array_equal(_rows_i16(pools[0].v_pages, keep, S), _rows_i16(pools[1].v_pages, keep, S))
+    for p in pools:
+        p.close()
+
+
 def test_c5_128k_sampled():
     """128K tokens, 64 q heads over 8 kv heads, 60 dropped spans, 8 segments
     of 512 queries: tables and every visible key in full, 6 random rows plus

@@ -104,6 +104,9 @@ def _replay(wl: W.Workload, check_every_op=True):
                 hp.repos(op.seq, op.spans, op.deltas)
                 np.testing.assert_array_equal(hp.lag(op.seq), before, err_msg=tag)
             oracle.apply_op(op_pool, op)
+        elif isinstance(op, W.ReposBatch):
+            hp.repos_batch(list(op.entries()))
+            oracle.apply_op(op_pool, op)
         elif isinstance(op, W.Splice):
             sp = hp.splice(op.seq, op.spans, op.stub_lens)
             want = oracle.apply_op(op_pool, op)
@@ -237,8 +240,40 @@ def test_c3_splices_bit_exact():
     _replay(W.c3_mla(1))
 
 
-def test_c4_shared_pool_bit_exact():
-    _replay(W.c4_batched(0, n_req=6, ctx_lo=2000, ctx_hi=6000), check_every_op=False)
+@pytest.mark.parametrize("batched", [True, False])
+def test_c4_shared_pool_bit_exact(batched):
+    _replay(W.c4_batched(0, n_req=6, ctx_lo=2000, ctx_hi=6000, batched=batched), check_every_op=False)
+
+
+def test_repos_batch_equals_sequential_and_is_atomic():
+    """akv_repos_batch leaves every sequence as akv_repos on each entry does;
+    a bad entry (span out of range, a sequence named twice, a position pushed
+    below 0) fails the whole call and changes nothing."""
+    lay = W.Layout(4, 2, 0, 16, 16, 8, 256)
+    order = np.random.default_rng(5).permutation(256).astype(np.int32)
+    a, b = _host_pool(lay, order), _host_pool(lay, order)
+    for p in (a, b):
+        for s in range(3):
+            p.seq_create()
+            p.append(s, np.arange(100 + 40 * s, 300 + 40 * s))
+        p.drop(1, [[10, 50]])
+    entries = [(0, [[20, 120], [60, 200]], [-7, 3]), (1, [[50, 200]], [-40]), (2, [[0, 5]], [9])]
+    for s, sp, dl in entries:
+        a.repos(s, sp, dl)
+    b.repos_batch(entries)
+    for s in range(3):
+        for x, y in zip(a.tokens(s), b.tokens(s)):
+            np.testing.assert_array_equal(x, y)
+    before = [b.tokens(s) for s in range(3)]
+    bad = [[(0, [[0, 10]], [1]), (1, [[0, 999]], [1])],          # span out of range
+           [(0, [[0, 10]], [1]), (0, [[20, 30]], [1])],          # sequence twice
+           [(2, [[0, 10]], [1]), (1, [[0, 200]], [-100000])]]    # position below 0
+    for e in bad:
+        with pytest.raises(akv.AkvError):
+            b.repos_batch(e)
+        for s in range(3):
+            for x, y in zip(before[s], b.tokens(s)):
+                np.testing.assert_array_equal(x, y)
 
 
 def test_golden_figure_through_the_abi():

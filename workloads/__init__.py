@@ -129,6 +129,20 @@ class Repos:
 
 
 @dataclass
+class ReposBatch:
+    seqs: np.ndarray         # int32 [m], distinct
+    span_counts: np.ndarray  # int32 [m]
+    spans: np.ndarray        # int32 [sum(span_counts), 2], entries concatenated in order
+    deltas: np.ndarray       # int32 [sum(span_counts)]
+
+    def entries(self):
+        off = 0
+        for s, c in zip(self.seqs.tolist(), self.span_counts.tolist()):
+            yield s, self.spans[off:off + c], self.deltas[off:off + c]
+            off += c
+
+
+@dataclass
 class Splice:
     seq: int
     spans: np.ndarray    # int32 [m, 2] in visible-list coordinates, sorted, disjoint
@@ -400,7 +414,12 @@ def c3_mla(seed: int = 0) -> Workload:
 # --------------------------------------------------------------------------
 # config 4: 16 concurrent requests on the config-2 layer shape
 # --------------------------------------------------------------------------
-def c4_batched(seed: int = 0, n_req: int = 16, ctx_lo: int = 8192, ctx_hi: int = 32768) -> Workload:
+def c4_batched(seed: int = 0, n_req: int = 16, ctx_lo: int = 8192, ctx_hi: int = 32768,
+               batched: bool = True) -> Workload:
+    """batched: the requests' repos go in one ReposBatch (one rotation launch)
+    and their new tokens in one AppendBatch; otherwise one call per request.
+    The two forms give the same state (ops on different sequences commute and
+    the appends keep their order)."""
     rng = _rng(seed)
     reqs = []
     for r in range(n_req):
@@ -439,20 +458,36 @@ def c4_batched(seed: int = 0, n_req: int = 16, ctx_lo: int = 8192, ctx_hi: int =
         wl.ops.append(SeqCreate())
     for r, q in enumerate(reqs):            # histories, interleaved in the shared pool
         wl.ops.append(_append_op(rng, lay, r, np.arange(q["ctx"], dtype=np.int32)))
+    rep = []
     for r, q in enumerate(reqs):
         if q["dropped"]:
             wl.ops.append(Drop(r, _spans(q["dropped"])))
             rs, rd = _survivor_runs(q["ctx"], q["dropped"])
             if len(rs):
-                wl.ops.append(Repos(r, rs, rd))
+                rep.append(Repos(r, rs, rd))
+    if batched and rep:
+        wl.ops.append(ReposBatch(np.asarray([o.seq for o in rep], np.int32),
+                                 np.asarray([len(o.spans) for o in rep], np.int32),
+                                 np.concatenate([o.spans for o in rep]).astype(np.int32),
+                                 np.concatenate([o.deltas for o in rep]).astype(np.int32)))
+    else:
+        wl.ops += rep
     segs, row = [], 0
+    new = []
     for r, q in enumerate(reqs):
         h = q["ctx"] - sum(e - b for b, e in q["dropped"])
-        wl.ops.append(_append_op(rng, lay, r, np.arange(h, h + q["qtot"], dtype=np.int32)))
+        new.append(_append_op(rng, lay, r, np.arange(h, h + q["qtot"], dtype=np.int32)))
         kt = q["keep_tools"]
         masks = [[kt[j] for j in range(min(k, len(kt)))] for k in range(len(q["seg_lens"]))]
         segs += _query_segments(r, q["ctx"], row, q["seg_lens"], masks)
         row += q["qtot"]
+    if batched:
+        wl.ops.append(AppendBatch(np.asarray([a.seq for a in new], np.int32),
+                                  np.asarray([len(a.pos) for a in new], np.int32),
+                                  np.concatenate([a.pos for a in new]), np.concatenate([a.k for a in new]),
+                                  None, np.concatenate([a.v for a in new])))
+    else:
+        wl.ops += new
     qarr = _normal_bf16(rng, (row, lay.n_q_heads, lay.d_qk), scale=1.0 / 8.0)
     wl.ops.append(Attention(qarr, segs))
     wl.notes.update(requests=reqs)
