@@ -77,6 +77,7 @@ struct SeqRec {
   int64_t n_vis = 0;
   std::vector<int32_t> vis;    // cached visible order
   bool vis_ok = false;
+  bool vis_logical = false;    // vis is in logical order (positions never decrease along it)
   std::vector<akv_extent> ext; // cached page-table image of vis (valid with ext_ok)
   bool ext_ok = false;
   // the same image with runs also cut where the owed rotation changes, and
@@ -522,7 +523,50 @@ const std::vector<int32_t>& visible(SeqRec& q) {
     std::stable_sort(q.vis.begin(), q.vis.end(),
                      [&](int32_t a, int32_t b) { return q.pos[a] < q.pos[b]; });
   q.vis_ok = true;
+  q.vis_logical = sorted;
   return q.vis;
+}
+
+// The page-table image of vis minus the tokens of the mask spans, cut from
+// the cached image: with vis in logical order a span is one range of it, so
+// only the extents it meets are trimmed, and pieces that become adjacent
+// merge as build_extents would merge them (the result is the same list).
+void masked_from_image(const SeqRec& q, const akv_span* m, int32_t nm, std::vector<akv_extent>& out) {
+  std::vector<std::pair<int64_t, int64_t>> cut;
+  for (int32_t k = 0; k < nm; ++k) {
+    const int64_t i0 = std::lower_bound(q.vis.begin(), q.vis.end(), m[k].begin) - q.vis.begin();
+    const int64_t i1 = std::lower_bound(q.vis.begin(), q.vis.end(), m[k].end) - q.vis.begin();
+    if (i0 < i1) cut.emplace_back(i0, i1);
+  }
+  std::sort(cut.begin(), cut.end());
+  size_t w = 0;   // coalesce overlapping ranges
+  for (size_t k = 0; k < cut.size(); ++k) {
+    if (w && cut[k].first <= cut[w - 1].second)
+      cut[w - 1].second = std::max(cut[w - 1].second, cut[k].second);
+    else
+      cut[w++] = cut[k];
+  }
+  cut.resize(w);
+  out.clear();
+  auto emit = [&](int32_t pg, int32_t lo, int32_t hi) {
+    if (!out.empty() && out.back().page == pg && out.back().hi == lo)
+      out.back().hi = hi;
+    else
+      out.push_back({pg, lo, hi});
+  };
+  int64_t off = 0;
+  size_t c = 0;
+  for (const akv_extent& x : q.ext) {
+    const int64_t a = off, b = off + (x.hi - x.lo);
+    while (c < cut.size() && cut[c].second <= a) ++c;
+    int64_t cur = a;
+    for (size_t k = c; k < cut.size() && cut[k].first < b; ++k) {
+      if (cut[k].first > cur) emit(x.page, x.lo + (int32_t)(cur - a), x.lo + (int32_t)(cut[k].first - a));
+      cur = std::max(cur, cut[k].second);
+    }
+    if (cur < b) emit(x.page, x.lo + (int32_t)(cur - a), x.hi);
+    off = b;
+  }
 }
 
 void build_extents(const akv_pool* p, const SeqRec& q, const std::vector<int32_t>& order,
@@ -1846,7 +1890,13 @@ akv_status akv_seq_visible(akv_pool* p, int32_t s, const akv_span* mask, int32_t
     if (st != AKV_OK) return st;
     const std::vector<int32_t>& vis = visible(*q);
     std::vector<akv_extent> masked;
-    if (n_mask > 0) {
+    if (n_mask > 0 && q->vis_logical) {
+      if (!q->ext_ok) {
+        build_extents(p, *q, vis, nullptr, q->ext);
+        q->ext_ok = true;
+      }
+      masked_from_image(*q, mask, n_mask, masked);
+    } else if (n_mask > 0) {
       std::vector<uint8_t> hide(q->slot.size(), 0);
       for (int32_t i = 0; i < n_mask; ++i)
         std::fill(hide.begin() + mask[i].begin, hide.begin() + mask[i].end, 1);
@@ -1914,7 +1964,8 @@ akv_status akv_seq_attention(akv_pool* p, const void* Q, int32_t n_q_tokens, con
       const akv_span* m = masks ? masks + sg.mask_begin : nullptr;
       const std::vector<int32_t>& vis = visible(*q);
       std::vector<uint8_t> hide;
-      if (sg.mask_len > 0) {
+      const bool from_image = sg.mask_len > 0 && !fused && q->vis_logical;
+      if (sg.mask_len > 0 && !from_image) {
         hide.assign(q->slot.size(), 0);
         for (int32_t k = 0; k < sg.mask_len; ++k) std::fill(hide.begin() + m[k].begin, hide.begin() + m[k].end, 1);
       }
@@ -1930,6 +1981,13 @@ akv_status akv_seq_attention(akv_pool* p, const void* Q, int32_t n_q_tokens, con
         }
         lags.insert(lags.end(), q->ext_lg_lag.begin(), q->ext_lg_lag.end());
         ex = &q->ext_lg;
+      } else if (from_image) {
+        if (!q->ext_ok) {
+          build_extents(p, *q, vis, nullptr, q->ext);
+          q->ext_ok = true;
+        }
+        masked_from_image(*q, m, sg.mask_len, masked);
+        ex = &masked;
       } else if (sg.mask_len > 0) {
         build_extents(p, *q, vis, &hide, masked);
         ex = &masked;

@@ -245,6 +245,36 @@ def test_c4_shared_pool_bit_exact(batched):
     _replay(W.c4_batched(0, n_req=6, ctx_lo=2000, ctx_hi=6000, batched=batched), check_every_op=False)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_masked_lists_equal_oracle(seed):
+    """A segment's list minus its mask spans (cut from the cached page-table
+    image when positions keep the logical order, built token by token when a
+    repos reordered them) equals the oracle's, for random overlapping,
+    unsorted and empty spans over dropped tokens and page edges."""
+    rng = np.random.default_rng(seed)
+    lay = W.Layout(4, 2, 0, 16, 16, 8, 400)
+    order = rng.permutation(400).astype(np.int32)
+    hp, op = _host_pool(lay, order), AO.Pool(lay, order)
+    z = lambda n: np.zeros((n, 2, 16))
+    s = hp.seq_create(); op.seq_create()
+    n = 900
+    hp.append(s, np.arange(n)); op.append(s, np.arange(n), z(n), None, z(n))
+    drops = [[int(b), int(b) + int(rng.integers(1, 40))] for b in rng.integers(0, n - 40, 12)]
+    hp.drop(s, drops)
+    op.drop(s, drops)
+    if seed % 2:   # reorder: a run moves below earlier tokens
+        hp.repos(s, [[700, 800]], [-650]); op.repos(s, [[700, 800]], [-650])
+    for _ in range(25):
+        k = int(rng.integers(0, 5))
+        m = []
+        for _ in range(k):
+            b = int(rng.integers(0, n))
+            m.append([b, min(n, b + int(rng.integers(0, 60)))])
+        got = hp.visible(s, np.asarray(m, np.int32).reshape(-1, 2) if m else None)
+        want = op.extents(s, np.asarray(m).reshape(-1, 2) if m else None).reshape(-1, 3)
+        np.testing.assert_array_equal(got, want)
+
+
 def test_repos_batch_equals_sequential_and_is_atomic():
     """akv_repos_batch leaves every sequence as akv_repos on each entry does;
     a bad entry (span out of range, a sequence named twice, a position pushed
