@@ -275,6 +275,19 @@ def test_fuzz_gqa_full(seed):
                               head_dims=(32, 64, 128), groups=(1, 2, 4, 8)))
 
 
+@pytest.mark.parametrize("page_size", [1, 2, 128, 256])
+def test_fuzz_page_size_extremes_full(page_size):
+    """Pages of 1, 2, 128 and 256 tokens through every kernel (append,
+    repos, compaction, both attention kernels): tables, keys and attention."""
+    for seed, d in ((500, 64), (501, 128)):      # d 128: the direct-to-LDS kernel
+        _full_parity(W.fuzz_small(seed, n_seqs=3, page_size=page_size, head_dims=(d,), groups=(1, 4, 8)))
+
+
+@pytest.mark.parametrize("page_size", [1, 256])
+def test_decode_page_size_extremes_full(page_size):
+    _full_parity(W.decode_batch(6, n_req=8, ctx_lo=200, ctx_hi=2500, page_size=page_size))
+
+
 @pytest.mark.parametrize("seed,kph,pairing", [(300, 0, 0), (301, 1, 0), (302, 0, 1)])
 def test_fuzz_mla_full(seed, kph, pairing):
     _full_parity(W.fuzz_small(seed, mla=True, kpe_per_head=kph, pairing=pairing, n_seqs=2,

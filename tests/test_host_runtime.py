@@ -196,6 +196,14 @@ def test_deferred_compaction_queue_rules():
     assert akv.lib().akv_compact_pending(hp._h, -1, 1, None, ctypes.byref(ctypes.c_int32())) == akv.AKV_EINVAL
 
 
+@pytest.mark.parametrize("page_size", [1, 2, 128, 256])
+def test_fuzz_scripts_page_size_extremes(page_size):
+    """Pages of 1 and 2 tokens (every token its own extent) and of 128 and
+    256 (the largest the pool takes): tables after every op as the oracle."""
+    for seed in range(3):
+        _replay(W.fuzz_small(500 + seed, n_seqs=3, page_size=page_size, head_dims=(64, 128), groups=(1, 4, 8)))
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_fuzz_scripts_bit_exact(seed):
     _replay(W.fuzz_small(seed, n_seqs=3, page_size=[16, 8, 4][seed % 3]))

@@ -546,7 +546,8 @@ def retrigger(seed: int = 0, ctx: int = 65536, pre_a: int = 512, nq: int = 512, 
 # decode: one new token per request at high batch (the inter-token side)
 # --------------------------------------------------------------------------
 def decode_batch(seed: int = 0, n_req: int = 48, ctx_lo: int = 2048, ctx_hi: int = 16384,
-                 n_q_heads: int = 32, q_len: int = 1, deferred: bool = False, pairing: int = 0) -> Workload:
+                 n_q_heads: int = 32, q_len: int = 1, deferred: bool = False, pairing: int = 0,
+                 page_size: int = 16) -> Workload:
     """n_req agent histories in one pool, each built with the batched recipe
     (512-token reasoning turns, log-uniform tool spans, 10-60% of the older
     tools dropped, survivors repositioned); then every request appends q_len
@@ -577,8 +578,8 @@ def decode_batch(seed: int = 0, n_req: int = 48, ctx_lo: int = 2048, ctx_hi: int
             gone += tools[i][1] - tools[i][0]
         dropped = [tools[i] for i in sorted(chosen)]
         reqs.append(dict(ctx=ctx, dropped=dropped))
-    pages = sum((q["ctx"] + q_len + 15) // 16 for q in reqs) + 16
-    lay = Layout(n_q_heads, 8, 0, 128, 128, 16, pages, pairing=pairing, rope_theta=500000.0)
+    pages = sum((q["ctx"] + q_len + page_size - 1) // page_size for q in reqs) + 16
+    lay = Layout(n_q_heads, 8, 0, 128, 128, page_size, pages, pairing=pairing, rope_theta=500000.0)
     wl = Workload("decode_batch", lay, rng.permutation(pages).astype(np.int32))
     for r in range(n_req):
         wl.ops.append(SeqCreate())
