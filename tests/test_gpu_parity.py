@@ -285,7 +285,7 @@ def test_fuzz_page_size_extremes_full(page_size):
 
 @pytest.mark.parametrize("page_size", [1, 256])
 def test_decode_page_size_extremes_full(page_size):
-    _full_parity(W.decode_batch(6, n_req=8, ctx_lo=200, ctx_hi=2500, page_size=page_size))
+    _full_parity(W.decode_batch(6, n_req=8, ctx_lo=3000, ctx_hi=7000, page_size=page_size))
 
 
 @pytest.mark.parametrize("seed,kph,pairing", [(300, 0, 0), (301, 1, 0), (302, 0, 1)])
