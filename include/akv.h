@@ -101,8 +101,10 @@ typedef struct {
  * page-table-only: it tracks slots, positions, visibility and allocation
  * exactly like a device pool but holds no KV values, so attention on it
  * returns AKV_ESTATE.
- * Errors: AKV_EINVAL (bad layout, page_order not a permutation),
- * AKV_EHIP (device query or pinned allocation failed). */
+ * Limits: num_pages < 2^24 and num_pages * n_kv_heads * page_size < 2^32
+ * (row indices in the kernels), num_pages * page_size < 2^31 (slots).
+ * Errors: AKV_EINVAL (bad layout or a limit exceeded, page_order not a
+ * permutation), AKV_EHIP (device query or pinned allocation failed). */
 akv_status akv_pool_create(const akv_layout* layout, const int32_t* page_order,
                            void* k_pages, void* kpe_pages, void* v_pages,
                            void* scratch, size_t scratch_bytes, void* hip_stream,

@@ -1172,6 +1172,12 @@ akv_status akv_pool_create(const akv_layout* layout, const int32_t* page_order, 
       return fail(AKV_EINVAL, "page_size must be a power of two in 1..256");
     if (L.num_pages <= 0 || (int64_t)L.num_pages * L.page_size > kInt32Max)
       return fail(AKV_EINVAL, "num_pages out of range");
+    // the kernels form row indices with 24-bit multiplies (page * heads *
+    // page_size) and keep them in 32 bits
+    if (L.num_pages >= (1 << 24)) return fail(AKV_EINVAL, "num_pages must be below 2^24");
+    if ((int64_t)L.num_pages * L.n_kv_heads * L.page_size >= (int64_t(1) << 32) ||
+        (int64_t)L.n_kv_heads * L.page_size >= (1 << 24))
+      return fail(AKV_EINVAL, "num_pages x n_kv_heads x page_size must be below 2^32");
     if (L.pairing != 0 && L.pairing != 1) return fail(AKV_EINVAL, "pairing must be 0 or 1");
     if (L.d_nope == 0 && L.kpe_per_head) return fail(AKV_EINVAL, "kpe_per_head needs an MLA layout");
     const bool any_dev = k_pages || kpe_pages || v_pages || scratch;

@@ -283,6 +283,20 @@ def test_masked_lists_equal_oracle(seed):
         np.testing.assert_array_equal(got, want)
 
 
+def test_pool_size_limits():
+    """Row indices in the kernels use 24-bit page multiplies and 32-bit rows:
+    a pool at the limits is refused before any allocation, one page below
+    is accepted (page-table-only, so nothing large is allocated on a GPU)."""
+    for n_pages, heads, page in [(1 << 24, 1, 1), ((1 << 24) - 1, 256, 256), ((1 << 31) // 128, 1, 128)]:
+        with pytest.raises(akv.AkvError):
+            akv.Pool(heads, heads, 0, 16, 16, page, n_pages, device=False)
+    p = akv.Pool(8, 8, 0, 16, 16, 16, (1 << 24) - 1, device=False)
+    s = p.seq_create()
+    p.append(s, np.arange(40))
+    assert p.info(s)[0] == 40
+    p.close()
+
+
 def test_repos_batch_equals_sequential_and_is_atomic():
     """akv_repos_batch leaves every sequence as akv_repos on each entry does;
     a bad entry (span out of range, a sequence named twice, a position pushed
