@@ -99,7 +99,7 @@ __global__ __launch_bounds__(ROT_THREADS, 8) void k_rotate(uint16_t* const* __re
     const int rem = u - h * per_head;
     const int row = it.lo + rem / upr;
     const int c = rem - (rem / upr) * upr;
-    uint16_t* base = kr + ((size_t)(it.page * n_heads + h) * S + row) * d;
+    uint16_t* base = kr + (((size_t)it.page * n_heads + h) * S + row) * d;
     cu[i] = c;
     if (pairing == 0) {
       pa[i] = base + 16 * c;
