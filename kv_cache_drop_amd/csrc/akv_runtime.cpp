@@ -204,17 +204,18 @@ akv_status stg_reserve(akv_pool* p, size_t n, char** out) {
   }
   if (s.head + n > s.cap) s.head = 0;
   const size_t b = s.head, e_ = s.head + n;
-  // wait for the newest pending region overlapping [b, e_); older ones are done too
+  // Wait for the newest pending region overlapping [b, e_) and every region
+  // before it.  Their events come from two streams, so a newer one having
+  // completed says nothing of an older one: each is synchronized (at no cost
+  // once it has completed).
   int last = -1;
   for (int i = 0; i < (int)s.pending.size(); ++i)
     if (s.pending[i].b < e_ && b < s.pending[i].e) last = i;
-  if (last >= 0) {
-    hipError_t e = hipEventSynchronize(s.pending[last].ev);
+  for (int i = 0; i <= last; ++i) {
+    hipError_t e = hipEventSynchronize(s.pending.front().ev);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging)");
-    for (int i = 0; i <= last; ++i) {
-      s.spare.push_back(s.pending.front().ev);
-      s.pending.pop_front();
-    }
+    s.spare.push_back(s.pending.front().ev);
+    s.pending.pop_front();
   }
   s.head = e_;
   *out = s.base + b;
