@@ -537,7 +537,9 @@ const std::vector<int32_t>& visible(SeqRec& q) {
 // the cached image: with vis in logical order a span is one range of it, so
 // only the extents it meets are trimmed, and pieces that become adjacent
 // merge as build_extents would merge them (the result is the same list).
-void masked_from_image(const SeqRec& q, const akv_span* m, int32_t nm, std::vector<akv_extent>& out) {
+// The ranges of vis (in logical order) that the logical spans cover, sorted
+// and merged.
+std::vector<std::pair<int64_t, int64_t>> vis_ranges(const SeqRec& q, const akv_span* m, int32_t nm) {
   std::vector<std::pair<int64_t, int64_t>> cut;
   for (int32_t k = 0; k < nm; ++k) {
     const int64_t i0 = std::lower_bound(q.vis.begin(), q.vis.end(), m[k].begin) - q.vis.begin();
@@ -553,6 +555,11 @@ void masked_from_image(const SeqRec& q, const akv_span* m, int32_t nm, std::vect
       cut[w++] = cut[k];
   }
   cut.resize(w);
+  return cut;
+}
+
+void masked_from_image(const SeqRec& q, const akv_span* m, int32_t nm, std::vector<akv_extent>& out) {
+  const std::vector<std::pair<int64_t, int64_t>> cut = vis_ranges(q, m, nm);
   out.clear();
   auto emit = [&](int32_t pg, int32_t lo, int32_t hi) {
     if (!out.empty() && out.back().page == pg && out.back().hi == lo)
@@ -573,6 +580,45 @@ void masked_from_image(const SeqRec& q, const akv_span* m, int32_t nm, std::vect
     if (cur < b) emit(x.page, x.lo + (int32_t)(cur - a), x.hi);
     off = b;
   }
+}
+
+// After a drop of logical spans: with vis in logical order the dropped
+// tokens are whole ranges of it, so the cached order loses those ranges and
+// the cached image is trimmed like a masked list (the same lists a rebuild
+// gives); otherwise the caches are rebuilt on next use.
+void cache_after_drop(SeqRec& q, const akv_span* sp, int32_t n) {
+  if (!q.vis_ok || !q.vis_logical) {
+    q.stale();
+    return;
+  }
+  if (q.ext_ok) {
+    std::vector<akv_extent> trimmed;
+    masked_from_image(q, sp, n, trimmed);
+    q.ext.swap(trimmed);
+  }
+  const std::vector<std::pair<int64_t, int64_t>> cut = vis_ranges(q, sp, n);
+  size_t w = 0, c = 0;
+  for (size_t i = 0; i < q.vis.size(); ++i) {
+    while (c < cut.size() && (int64_t)i >= cut[c].second) ++c;
+    if (c < cut.size() && (int64_t)i >= cut[c].first) continue;
+    q.vis[w++] = q.vis[i];
+  }
+  q.vis.resize(w);
+  q.lg_ok = false;
+}
+
+// After positions moved (repos) with slots unchanged: the cached order and
+// image stay valid while positions still never decrease along vis.
+void cache_after_move(SeqRec& q) {
+  if (!q.vis_ok || !q.vis_logical) {
+    q.stale();
+    return;
+  }
+  for (size_t i = 1; i < q.vis.size(); ++i)
+    if (q.pos[q.vis[i]] < q.pos[q.vis[i - 1]]) {
+      q.stale();
+      return;
+    }
 }
 
 void build_extents(const akv_pool* p, const SeqRec& q, const std::vector<int32_t>& order,
@@ -868,7 +914,7 @@ akv_status compact_seq(akv_pool* p, int32_t s) {
   return device_move(p, mv);
 }
 
-void drop_tokens(akv_pool* p, SeqRec& q, int32_t b, int32_t e) {
+void drop_tokens(akv_pool* p, SeqRec& q, int32_t b, int32_t e, bool keep_cache = false) {
   for (int32_t t = b; t < e; ++t) {
     if (q.dropped[t]) continue;
     q.dropped[t] = 1;
@@ -878,7 +924,7 @@ void drop_tokens(akv_pool* p, SeqRec& q, int32_t b, int32_t e) {
     r.nvis -= 1;
     if (r.nvis == 0 && pg != q.tail && !r.in_evict) evict_push(p, pg);
   }
-  q.stale();
+  if (!keep_cache) q.stale();
 }
 
 // Above the threshold: compact now when the allocator can supply the pages
@@ -1032,7 +1078,7 @@ void repos_commit(SeqRec& q, const std::vector<Run>& runs) {
   for (const Run& r : runs)
     for (int32_t t = r.b; t < r.e; ++t)
       if (!q.dropped[t]) q.pos[t] = (int32_t)(q.pos[t] + r.d);
-  q.stale();
+  if (!runs.empty()) cache_after_move(q);
 }
 
 // Rotate every visible key by the rotation it still owes (one launch) and
@@ -1555,7 +1601,8 @@ akv_status akv_drop(akv_pool* p, int32_t s, const akv_span* spans, int32_t n) {
     if (st != AKV_OK) return st;
     st = scratch_fits(p, (size_t)q->n_vis * sizeof(akv::MovePair) + 256);
     if (st != AKV_OK) return st;
-    for (int32_t i = 0; i < n; ++i) drop_tokens(p, *q, spans[i].begin, spans[i].end);
+    for (int32_t i = 0; i < n; ++i) drop_tokens(p, *q, spans[i].begin, spans[i].end, true);
+    cache_after_drop(*q, spans, n);
     return auto_compact(p, s);
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
@@ -1663,6 +1710,7 @@ akv_status akv_repos_deferred(akv_pool* p, int32_t s, const akv_span* spans, con
           q->lag[t] = (int32_t)(q->lag[t] + r.d);
           q->lagging = true;
         }
+    q->lg_ok = false;
     repos_commit(*q, runs);
     return AKV_OK;
   } catch (const std::bad_alloc&) {
