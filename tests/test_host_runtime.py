@@ -297,6 +297,42 @@ def test_pool_size_limits():
     p.close()
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_cached_lists_through_drops_and_repos(seed):
+    """A serving loop: the lists are read, then drops and repos follow (some
+    repos keep positions rising, some reorder them), each followed by reading
+    the lists with and without masks: every list equals the oracle's."""
+    rng = np.random.default_rng(40 + seed)
+    lay = W.Layout(4, 2, 0, 16, 16, 8, 600)
+    order = rng.permutation(600).astype(np.int32)
+    hp, op = _host_pool(lay, order), AO.Pool(lay, order)
+    z = lambda n: np.zeros((n, 2, 16))
+    s = hp.seq_create(); op.seq_create()
+    n, pos = 1500, 3000
+    hp.append(s, np.arange(pos, pos + n)); op.append(s, np.arange(pos, pos + n), z(n), None, z(n))
+    for it in range(30):
+        np.testing.assert_array_equal(hp.visible(s), op.extents(s).reshape(-1, 3))
+        k = int(rng.integers(0, 3))
+        if k == 0:
+            b = int(rng.integers(0, n - 50))
+            sp = [[b, b + int(rng.integers(1, 50))], [int(rng.integers(0, n)), n]] if rng.random() < 0.2 else \
+                [[b, b + int(rng.integers(1, 50))]]
+            hp.drop(s, sp); op.drop(s, sp)
+        elif k == 1:           # shift a suffix right (positions keep rising along the list)
+            b = int(rng.integers(0, n))
+            d = int(rng.integers(1, 20))
+            hp.repos(s, [[b, n]], [d])
+            op.repos(s, [[b, n]], [d])
+        else:                  # move a run below earlier tokens (reorders), sometimes
+            b = int(rng.integers(0, n - 30))
+            d = -int(rng.integers(1, 400))
+            if (op.seqs[s].pos[b:b + 30] + d >= 0).all():
+                hp.repos(s, [[b, b + 30]], [d]); op.repos(s, [[b, b + 30]], [d])
+        m = [[int(x), int(x) + int(rng.integers(0, 40))] for x in rng.integers(0, n - 40, int(rng.integers(1, 4)))]
+        np.testing.assert_array_equal(hp.visible(s, m), op.extents(s, np.asarray(m)).reshape(-1, 3))
+        np.testing.assert_array_equal(hp.tokens(s)[1], op.seqs[s].pos)
+
+
 def test_repos_batch_equals_sequential_and_is_atomic():
     """akv_repos_batch leaves every sequence as akv_repos on each entry does;
     a bad entry (span out of range, a sequence named twice, a position pushed
