@@ -20,8 +20,11 @@
  * - Host arrays passed in (spans, positions, segments, extents) are copied
  *   before the call returns.  Device inputs (K, V, Q) must stay valid until the
  *   work is done (akv_sync or a sync of the pool's stream).
- * - All device work is enqueued on the pool's HIP stream; calls return once it
- *   is enqueued, with the host metadata already updated.
+ * - All kernels are enqueued on the pool's HIP stream; calls return once they
+ *   are enqueued, with the host metadata already updated.  A device pool also
+ *   owns one stream of its own (default priority) for metadata copies into
+ *   scratch while the pool's stream is busy; the pool's stream waits for each
+ *   such copy, so syncing the pool's stream covers all of a pool's work.
  * - Calls on one pool are not re-entrant; separate pools are independent.
  * - Every call validates all arguments before changing any state: a call that
  *   fails leaves the pool as it was.  akv_last_error() gives the reason.
