@@ -1227,10 +1227,27 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
   // Longest groups first, each to the least loaded XCD, so row tiles reading
   // the same K/V share that XCD's L2; then each XCD's items are dispatched
   // longest first, so the CUs of an XCD finish together.
-  // (ties keep their build order: `begin` grows with it)
-  std::sort(groups.begin(), groups.end(), [](const Group& a, const Group& b) {
-    return a.cost != b.cost ? a.cost > b.cost : a.begin < b.begin;
-  });
+  // Longest first, ties in build order: a stable LSD radix sort on the cost
+  // counted down from the largest (the same order as a comparison sort with
+  // `begin` as tie-break; decode plans hold thousands of equal-cost groups).
+  {
+    int64_t cmax = 0;
+    for (const Group& g : groups) cmax = std::max(cmax, g.cost);
+    std::vector<Group> tmp(groups.size());
+    uint32_t cnt[2048];
+    for (int shift = 0; shift < 63 && (cmax >> shift) != 0; shift += 11) {
+      std::fill(cnt, cnt + 2048, 0u);
+      for (const Group& g : groups) cnt[((cmax - g.cost) >> shift) & 2047] += 1;
+      uint32_t sum = 0;
+      for (uint32_t& c : cnt) {
+        const uint32_t c0 = c;
+        c = sum;
+        sum += c0;
+      }
+      for (const Group& g : groups) tmp[cnt[((cmax - g.cost) >> shift) & 2047]++] = g;
+      groups.swap(tmp);
+    }
+  }
   std::vector<std::vector<int32_t>> xbins(kXcds);
   for (auto& b : xbins) b.reserve(all.size() / kXcds + 16);
   std::vector<int64_t> load(kXcds, 0);
