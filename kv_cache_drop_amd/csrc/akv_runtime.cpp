@@ -110,10 +110,34 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Host lists of an attention call, kept by the pool so their capacity
 // persists from call to call (calls on one pool are not re-entrant).
+// Launch plan of one attention call, and the planner's working space (kept
+// in the pool between calls, so a steady decode loop allocates nothing).
+struct AttnPlan {
+  std::vector<akv::AttnSeg> segs;
+  std::vector<akv::AttnItem> items;  // grid order (XCD interleaved, padded)
+  std::vector<akv::CombItem> comb;
+  int64_t part_rows = 0;  // rows of split-KV partials
+  // Items of one group (same segment, kv head and key split: the row tiles
+  // that read the same K/V) are contiguous in `all`; a group is its range.
+  struct Group {
+    int64_t cost;
+    int32_t begin, end;
+  };
+  std::vector<akv::AttnItem> all;
+  std::vector<int64_t> cost;
+  std::vector<Group> groups, gtmp;
+  std::vector<int32_t> nsplit;                          // key splits of each segment
+  std::vector<int32_t> split_kb, split_ke;              // one segment's key splits
+  std::vector<int64_t> tile_base, tile_rows, tile_lim;  // one segment's row tiles
+  std::vector<int32_t> gbin, order;
+  std::vector<uint32_t> cnt;
+};
+
 struct AttnHostBufs {
   std::vector<akv_extent> lists, masked;
   std::vector<int32_t> lags, mlag, ex_off, ex_didx;
   std::vector<akv::Extent> ex_used;
+  AttnPlan plan;
 };
 
 struct akv_pool {
@@ -1111,15 +1135,6 @@ akv_status materialize_seq(akv_pool* p, SeqRec& q) {
 // ---------------------------------------------------------------------------
 // attention planning ([AKV-notes] section 3; [AKV-blog] section 4)
 // ---------------------------------------------------------------------------
-struct AttnPlan {
-  std::vector<akv::AttnSeg> segs;
-  std::vector<akv::AttnItem> items;  // grid order (XCD interleaved, padded)
-  std::vector<akv::CombItem> comb;
-  std::vector<int32_t> ext_off;
-  int64_t total_list = 0;
-  int64_t part_rows = 0;  // rows of split-KV partials
-};
-
 constexpr int kXcds = 8;
 constexpr int64_t kDecodeChunk = 1024;
 
@@ -1157,26 +1172,13 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
   const int64_t cu_share = total_cost / p->n_cu;
   const int64_t block_cap = std::max<int64_t>(2048, cu_share / 2);
 
-  // Items of one group (same segment, kv head and key split: the row tiles
-  // that read the same K/V) are contiguous in `all`; a group is its range.
-  struct Group {
-    int64_t cost;
-    int32_t begin, end;
-  };
-  std::vector<akv::AttnItem> all;
-  std::vector<int64_t> cost;
-  std::vector<Group> groups;
-  all.reserve((size_t)base * target + 64);
-  cost.reserve((size_t)base * target + 64);
-  groups.reserve((size_t)base * target + 64);
-  plan.comb.clear();
-  int64_t part = 0;
-  std::vector<int64_t> tile_base;
+  // key splits of each segment
+  std::vector<int32_t>& nsplit = plan.nsplit;
+  nsplit.assign(n_segs, 0);
+  size_t n_items = 0, n_groups = 0;
   for (int32_t i = 0; i < n_segs; ++i) {
     const int32_t lq = segs[i].q_len;
     if (lq <= 0) continue;
-    const int64_t rows = (int64_t)lq * G;
-    const int64_t ntile_rows = (rows + RB - 1) / RB;
     const int64_t key_tiles = (lkv[i] + KT - 1) / KT;
     int ns = target;
     if (4 * (lkv[i] + 64) > 5 * cu_share)
@@ -1188,37 +1190,64 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
     ns = (int)std::min<int64_t>(ns, std::max<int64_t>(1, lkv[i] / 512));
     ns = (int)std::min<int64_t>(ns, key_tiles);
     if (ns < 1) ns = 1;
-    // partials of one kv head: row tile m's ns splits, each of the tile's rows
-    tile_base.assign(ntile_rows, 0);
+    nsplit[i] = ns;
+    n_groups += (size_t)L.n_kv_heads * ns;
+    n_items += (size_t)L.n_kv_heads * ns * ((lq * (int64_t)G + RB - 1) / RB);
+  }
+  std::vector<akv::AttnItem>& all = plan.all;
+  std::vector<int64_t>& cost = plan.cost;
+  std::vector<AttnPlan::Group>& groups = plan.groups;
+  all.resize(n_items);
+  cost.resize(n_items);
+  groups.resize(n_groups);
+  plan.comb.clear();
+  int64_t part = 0;
+  int32_t at = 0, gat = 0;
+  for (int32_t i = 0; i < n_segs; ++i) {
+    const int32_t lq = segs[i].q_len;
+    if (lq <= 0) continue;
+    const int64_t rows = (int64_t)lq * G;
+    const int64_t ntile_rows = (rows + RB - 1) / RB;
+    const int64_t key_tiles = (lkv[i] + KT - 1) / KT;
+    const int ns = nsplit[i];
+    // key range of each split: whole key tiles, as even as they divide
+    plan.split_kb.resize(ns);
+    plan.split_ke.resize(ns);
+    for (int sp = 0; sp < ns; ++sp) {
+      plan.split_kb[sp] = (int32_t)(key_tiles * sp / ns * KT);
+      plan.split_ke[sp] = (int32_t)std::min<int64_t>(key_tiles * (sp + 1) / ns * KT, lkv[i]);
+    }
+    // each row tile: its rows, one past the last key its last row sees, and
+    // (split) the first partial row of its splits within one kv head
+    plan.tile_rows.resize(ntile_rows);
+    plan.tile_lim.resize(ntile_rows);
+    plan.tile_base.resize(ntile_rows);
     int64_t head_part_rows = 0;
-    if (ns > 1)
-      for (int64_t m = 0; m < ntile_rows; ++m) {
-        tile_base[m] = head_part_rows;
-        head_part_rows += ns * std::min<int64_t>(RB, rows - m * RB);
-      }
+    for (int64_t m = 0; m < ntile_rows; ++m) {
+      const int64_t nr = std::min<int64_t>(RB, rows - m * RB);
+      plan.tile_rows[m] = nr;
+      plan.tile_lim[m] = lkv[i] - lq + (m * RB + nr - 1) / G + 1;
+      plan.tile_base[m] = head_part_rows;
+      if (ns > 1) head_part_rows += ns * nr;
+    }
     for (int32_t h = 0; h < L.n_kv_heads; ++h) {
       for (int sp = 0; sp < ns; ++sp) {
-        const int64_t tb = key_tiles * sp / ns, te = key_tiles * (sp + 1) / ns;
-        const int32_t kb = (int32_t)(tb * KT), ke = (int32_t)std::min<int64_t>(te * KT, lkv[i]);
-        Group gr{0, (int32_t)all.size(), 0};
-        for (int64_t m = 0; m < ntile_rows; ++m) {
-          const int32_t row0 = (int32_t)(m * RB);
-          const int64_t last_row = std::min<int64_t>(row0 + RB, rows) - 1;
-          const int64_t lim_last = lkv[i] - lq + last_row / G;
-          const int64_t keys = std::max<int64_t>(0, std::min<int64_t>(ke, lim_last + 1) - kb);
-          int32_t pidx = -1;
-          if (ns > 1) pidx = (int32_t)(part + tile_base[m] + sp * std::min<int64_t>(RB, rows - row0));
-          all.push_back({i, h, row0, kb, ke, pidx});
-          cost.push_back(keys + 64);  // + fixed cost of a block
+        const int32_t kb = plan.split_kb[sp], ke = plan.split_ke[sp];
+        AttnPlan::Group gr{0, at, 0};
+        for (int64_t m = 0; m < ntile_rows; ++m, ++at) {
+          const int64_t keys = std::max<int64_t>(0, std::min<int64_t>(ke, plan.tile_lim[m]) - kb);
+          const int32_t pidx = ns > 1 ? (int32_t)(part + plan.tile_base[m] + sp * plan.tile_rows[m]) : -1;
+          all[at] = {i, h, (int32_t)(m * RB), kb, ke, pidx};
+          cost[at] = keys + 64;  // + fixed cost of a block
           gr.cost += keys + 64;
         }
-        gr.end = (int32_t)all.size();
-        groups.push_back(gr);
+        gr.end = at;
+        groups[gat++] = gr;
       }
       if (ns > 1) {
         for (int64_t m = 0; m < ntile_rows; ++m)
-          plan.comb.push_back({i, h, (int32_t)(m * RB), (int32_t)(part + tile_base[m]), ns,
-                               (int32_t)std::min<int64_t>(RB, rows - m * RB)});
+          plan.comb.push_back({i, h, (int32_t)(m * RB), (int32_t)(part + plan.tile_base[m]), ns,
+                               (int32_t)plan.tile_rows[m]});
         part += head_part_rows;
       }
     }
@@ -1227,48 +1256,71 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
   // Longest groups first, each to the least loaded XCD, so row tiles reading
   // the same K/V share that XCD's L2; then each XCD's items are dispatched
   // longest first, so the CUs of an XCD finish together.
-  // Longest first, ties in build order: a stable LSD radix sort on the cost
-  // counted down from the largest (the same order as a comparison sort with
-  // `begin` as tie-break; decode plans hold thousands of equal-cost groups).
-  {
-    int64_t cmax = 0;
-    for (const Group& g : groups) cmax = std::max(cmax, g.cost);
-    std::vector<Group> tmp(groups.size());
-    uint32_t cnt[2048];
-    for (int shift = 0; shift < 63 && (cmax >> shift) != 0; shift += 11) {
-      std::fill(cnt, cnt + 2048, 0u);
-      for (const Group& g : groups) cnt[((cmax - g.cost) >> shift) & 2047] += 1;
+  // Longest first, ties in build order: a stable counting sort on the cost
+  // counted down from the largest, in one pass when the costs span at most
+  // 4096 values (decode plans: thousands of groups of nearly equal cost),
+  // else in 11-bit digits.  The order equals a comparison sort's with
+  // `begin` as tie-break.
+  if (!groups.empty()) {
+    int64_t cmin = groups[0].cost, cmax = 0;
+    for (const AttnPlan::Group& g : groups) {
+      cmax = std::max(cmax, g.cost);
+      cmin = std::min(cmin, g.cost);
+    }
+    std::vector<AttnPlan::Group>& tmp = plan.gtmp;
+    tmp.resize(groups.size());
+    std::vector<uint32_t>& cnt = plan.cnt;
+    auto pass = [&](int shift, int64_t mask) {
+      cnt.assign((size_t)mask + 1, 0u);
+      for (const AttnPlan::Group& g : groups) cnt[((cmax - g.cost) >> shift) & mask] += 1;
       uint32_t sum = 0;
       for (uint32_t& c : cnt) {
         const uint32_t c0 = c;
         c = sum;
         sum += c0;
       }
-      for (const Group& g : groups) tmp[cnt[((cmax - g.cost) >> shift) & 2047]++] = g;
+      for (const AttnPlan::Group& g : groups) tmp[cnt[((cmax - g.cost) >> shift) & mask]++] = g;
       groups.swap(tmp);
-    }
+    };
+    if (cmax - cmin < 4096)
+      pass(0, 4095);
+    else
+      for (int shift = 0; shift < 63 && (cmax >> shift) != 0; shift += 11) pass(shift, 2047);
   }
-  std::vector<std::vector<int32_t>> xbins(kXcds);
-  for (auto& b : xbins) b.reserve(all.size() / kXcds + 16);
-  std::vector<int64_t> load(kXcds, 0);
-  for (const Group& gr : groups) {
+  // XCD of each group, then every XCD's items in a range of `order`
+  std::vector<int32_t>& gbin = plan.gbin;
+  gbin.resize(groups.size());
+  int64_t load[kXcds] = {};
+  size_t bin_n[kXcds] = {};
+  for (size_t gi = 0; gi < groups.size(); ++gi) {
     int best = 0;
     for (int x = 1; x < kXcds; ++x)
       if (load[x] < load[best]) best = x;
-    load[best] += gr.cost;
-    for (int32_t k = gr.begin; k < gr.end; ++k) xbins[best].push_back(k);
+    load[best] += groups[gi].cost;
+    gbin[gi] = best;
+    bin_n[best] += groups[gi].end - groups[gi].begin;
+  }
+  size_t bin_at[kXcds + 1] = {};
+  for (int x = 0; x < kXcds; ++x) bin_at[x + 1] = bin_at[x] + bin_n[x];
+  std::vector<int32_t>& order = plan.order;
+  order.resize(all.size());
+  {
+    size_t fill[kXcds];
+    std::copy(bin_at, bin_at + kXcds, fill);
+    for (size_t gi = 0; gi < groups.size(); ++gi)
+      for (int32_t k = groups[gi].begin; k < groups[gi].end; ++k) order[fill[gbin[gi]]++] = k;
   }
   size_t depth = 0;
   auto longer = [&](int32_t a, int32_t b) { return cost[a] > cost[b]; };
   for (int x = 0; x < kXcds; ++x) {
+    auto b0 = order.begin() + bin_at[x], b1 = order.begin() + bin_at[x + 1];
     // one-item groups (decode) arrive already in this order
-    if (!std::is_sorted(xbins[x].begin(), xbins[x].end(), longer))
-      std::stable_sort(xbins[x].begin(), xbins[x].end(), longer);
-    depth = std::max(depth, xbins[x].size());
+    if (!std::is_sorted(b0, b1, longer)) std::stable_sort(b0, b1, longer);
+    depth = std::max(depth, bin_n[x]);
   }
   plan.items.assign(depth * kXcds, akv::AttnItem{-1, 0, 0, 0, 0, -1});
   for (int x = 0; x < kXcds; ++x)
-    for (size_t i = 0; i < xbins[x].size(); ++i) plan.items[i * kXcds + x] = all[xbins[x][i]];
+    for (size_t i = 0; i < bin_n[x]; ++i) plan.items[i * kXcds + x] = all[order[bin_at[x] + i]];
 }
 
 }  // namespace
@@ -2221,7 +2273,7 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
         return fail(AKV_EINVAL, "owed rotations are applied only in decode launches");
     }
     const int rb = decode ? akv::DECODE_ROWS : akv::attn_rows_per_block(L.d_nope);
-    AttnPlan plan;
+    AttnPlan& plan = p->hb.plan;
     plan_attention(p, segs, n_segs, lkv, list_off, rb, plan);
     if (plan.part_rows > kInt32Max) return fail(AKV_ERANGE, "too many split-KV partial rows");
     // extent offsets for the slot expansion (over all segments' ranges, in order)
