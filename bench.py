@@ -232,7 +232,15 @@ def run_config(args) -> dict:
             dev[i] = (D.dev_bf16(op.k), D.dev_bf16(op.kpe) if op.kpe is not None else None, D.dev_bf16(op.v))
         elif isinstance(op, W.Attention):
             q = D.dev_bf16(op.q)
-            dev[i] = (q, torch.empty((q.shape[0], L.n_q_heads, L.d_v), dtype=torch.bfloat16, device="cuda:0"))
+            # the segment descriptions, as a caller keeps them: one int array
+            # when no segment hides spans
+            if all(len(sg.mask_spans) == 0 for sg in op.segments):
+                segs = np.array([(sg.seq, sg.q_begin, sg.q_len) for sg in op.segments], np.int32).reshape(-1, 3)
+            else:
+                segs = [(sg.seq, sg.q_begin, sg.q_len, sg.mask_spans if len(sg.mask_spans) else None)
+                        for sg in op.segments]
+            dev[i] = (q, torch.empty((q.shape[0], L.n_q_heads, L.d_v), dtype=torch.bfloat16, device="cuda:0"),
+                      segs)
     flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
     rope_heads = L.n_kv_heads if (not L.mla or L.kpe_per_head) else 1
     tot = {k: [0.0, 0] for k in ("attention", "rotate", "append", "compact", "expand", "combine", "clone")}
@@ -265,9 +273,7 @@ def run_config(args) -> dict:
                     pool.splice(op.seq, op.spans, op.stub_lens, dev[i][0], dev[i][1], dev[i][2])
                 elif isinstance(op, W.Attention):
                     # lists built inside the library from the sequences' page tables
-                    pool.seq_attention(dev[i][0], [(sg.seq, sg.q_begin, sg.q_len,
-                                                    sg.mask_spans if len(sg.mask_spans) else None)
-                                                   for sg in op.segments], op.scale, out=dev[i][1])
+                    pool.seq_attention(dev[i][0], dev[i][2], op.scale, out=dev[i][1])
                     if shift == 0:
                         lists.append(op)
                 else:

@@ -118,6 +118,9 @@ def _i32(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
 
 
+_NO_SPANS = np.zeros((0, 2), np.int32)
+
+
 def _ptr(a: np.ndarray):
     return a.ctypes.data_as(_IP) if a.size else None
 
@@ -392,18 +395,26 @@ class Pool:
     def seq_attention(self, q, segments, scale: float = 0.0, out=None):
         """Attention over sequences' own visible lists (akv_seq_attention):
         segments are (seq, q_begin, q_len, mask_spans) with mask_spans an
-        [m, 2] array of logical spans hidden from that segment (or None)."""
+        [m, 2] array of logical spans hidden from that segment (or None), or,
+        when no segment hides spans, an int [n, 3] array of (seq, q_begin,
+        q_len) rows."""
         import torch
-        rows, spans = [], []
-        for seq, qb, ql, m in segments:
-            if m is None or len(m) == 0:
-                rows.append((seq, qb, ql, len(spans), 0))
-                continue
-            m = _i32(m).reshape(-1, 2)
-            rows.append((seq, qb, ql, len(spans), len(m)))
-            spans.extend(m.tolist())
-        sg = np.asarray(rows, np.int32).reshape(-1, 5)
-        ms = np.asarray(spans, np.int32).reshape(-1, 2)
+        if isinstance(segments, np.ndarray):
+            a = np.asarray(segments).reshape(-1, 3)
+            sg = np.zeros((len(a), 5), np.int32)
+            sg[:, :3] = a
+            ms = _NO_SPANS
+        else:
+            rows, spans = [], []
+            for seq, qb, ql, m in segments:
+                if m is None or len(m) == 0:
+                    rows.append((seq, qb, ql, len(spans), 0))
+                    continue
+                m = _i32(m).reshape(-1, 2)
+                rows.append((seq, qb, ql, len(spans), len(m)))
+                spans.extend(m.tolist())
+            sg = np.asarray(rows, np.int32).reshape(-1, 5)
+            ms = np.asarray(spans, np.int32).reshape(-1, 2)
         L = self.layout
         if q.dim() != 3 or q.shape[1] != L["n_q_heads"] or q.shape[2] != L["d_nope"] + L["d_rope"] \
                 or q.dtype != torch.bfloat16:

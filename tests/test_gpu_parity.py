@@ -466,6 +466,12 @@ def test_seq_attention_equals_segment_attention(make):
                                      for sg in op.segments], op.scale)
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), o["out"].view(torch.int16))
+        if all(len(sg.mask_spans) == 0 for sg in op.segments):
+            # the same segments given as one (seq, q_begin, q_len) array
+            arr = np.array([(sg.seq, sg.q_begin, sg.q_len) for sg in op.segments], np.int64)
+            got = pool.seq_attention(q, arr, op.scale)
+            torch.cuda.synchronize()
+            assert torch.equal(got.view(torch.int16), o["out"].view(torch.int16))
     pool.close()
 
 

@@ -548,6 +548,12 @@ def test_seq_attention_validates_before_the_pool_state_check():
         with pytest.raises(akv.AkvError) as ei:
             hp.seq_attention(q, segs, out=out)
         assert ei.value.status == code, (segs, ei.value)
+    # the array form of unmasked segments goes through the same checks
+    for arr, code in [(np.array([[5, 0, 1]]), akv.AKV_EINVAL), (np.array([[-1, 0, 1]]), akv.AKV_EINVAL),
+                      (np.array([[s, 0, 1]]), akv.AKV_ESTATE)]:
+        with pytest.raises(akv.AkvError) as ei:
+            hp.seq_attention(q, arr, out=out)
+        assert ei.value.status == code, (arr, ei.value)
 
 
 def test_owed_rotation_follows_tokens():
