@@ -682,9 +682,15 @@ void build_extents_lag(const akv_pool* p, const SeqRec& q, const std::vector<int
 }
 
 double fragmentation(const akv_pool* p, const SeqRec& q) {
+  // the sequence's page records are scattered: fetch a few ahead
+  constexpr size_t kAhead = 16;
+  const size_t np = q.pages.size();
   int64_t cap = 0;
-  for (int32_t pg : q.pages)
-    if (p->pages[pg].nvis > 0) cap += p->pages[pg].filled;
+  for (size_t i = 0; i < np; ++i) {
+    if (i + kAhead < np) __builtin_prefetch(&p->pages[q.pages[i + kAhead]]);
+    const PageRec& r = p->pages[q.pages[i]];
+    if (r.nvis > 0) cap += r.filled;
+  }
   if (cap == 0) return 0.0;
   return 1.0 - (double)q.n_vis / (double)cap;
 }
@@ -899,7 +905,10 @@ akv_status compact_plan(akv_pool* p, int32_t s, std::vector<akv::MovePair>& mv) 
   const std::vector<int32_t> old_pages = q.pages;
   std::vector<int32_t> dest;
   dest.reserve(need);
-  for (int64_t i = 0; i < need; ++i) dest.push_back(take_page(p, s));
+  for (int64_t i = 0; i < need; ++i) {
+    dest.push_back(take_page(p, s));
+    p->pages[dest.back()].toks.reserve(S);
+  }
   mv.reserve(mv.size() + nv);
   for (int64_t i = 0; i < nv; ++i) {
     const int32_t t = order[i];
@@ -915,16 +924,18 @@ akv_status compact_plan(akv_pool* p, int32_t s, std::vector<akv::MovePair>& mv) 
     r.nvis = c;
   }
   q.tail = (need > 0 && nv % S) ? dest.back() : -1;
+  // an old page may come back as a fresh one (from the evictable queue)
+  std::vector<int32_t> dest_sorted(dest);
+  std::sort(dest_sorted.begin(), dest_sorted.end());
   for (int32_t pg : old_pages) {
-    if (std::find(dest.begin(), dest.end(), pg) != dest.end()) continue;
+    if (std::binary_search(dest_sorted.begin(), dest_sorted.end(), pg)) continue;
     PageRec& r = p->pages[pg];
     if (r.owner != s) continue;
     r.nvis = 0;
     // keep only tokens that still point into this page (the dropped ones)
-    std::vector<int32_t> keep;
-    for (int32_t t : r.toks)
-      if (q.slot[t] >= 0 && q.slot[t] / S == pg) keep.push_back(t);
-    r.toks.swap(keep);
+    r.toks.erase(std::remove_if(r.toks.begin(), r.toks.end(),
+                                [&](int32_t t) { return !(q.slot[t] >= 0 && q.slot[t] / S == pg); }),
+                 r.toks.end());
     if (!r.in_evict) evict_push(p, pg);
   }
   q.stale();
@@ -939,7 +950,11 @@ akv_status compact_seq(akv_pool* p, int32_t s) {
 }
 
 void drop_tokens(akv_pool* p, SeqRec& q, int32_t b, int32_t e, bool keep_cache = false) {
+  // page records lie in allocation order, not in the sequence's: fetch the
+  // record a few pages ahead
+  constexpr int32_t kAhead = 64;
   for (int32_t t = b; t < e; ++t) {
+    if (t + kAhead < e) __builtin_prefetch(&p->pages[q.slot[t + kAhead] >> p->log2S]);
     if (q.dropped[t]) continue;
     q.dropped[t] = 1;
     q.n_vis -= 1;
