@@ -687,7 +687,7 @@ double fragmentation(const akv_pool* p, const SeqRec& q) {
   const size_t np = q.pages.size();
   int64_t cap = 0;
   for (size_t i = 0; i < np; ++i) {
-    if (i + kAhead < np) __builtin_prefetch(&p->pages[q.pages[i + kAhead]]);
+    if (i + kAhead < np) __builtin_prefetch(p->pages.data() + q.pages[i + kAhead]);
     const PageRec& r = p->pages[q.pages[i]];
     if (r.nvis > 0) cap += r.filled;
   }
@@ -951,10 +951,11 @@ akv_status compact_seq(akv_pool* p, int32_t s) {
 
 void drop_tokens(akv_pool* p, SeqRec& q, int32_t b, int32_t e, bool keep_cache = false) {
   // page records lie in allocation order, not in the sequence's: fetch the
-  // record a few pages ahead
+  // record a few pages ahead (tokens of evicted pages have no slot)
   constexpr int32_t kAhead = 64;
   for (int32_t t = b; t < e; ++t) {
-    if (t + kAhead < e) __builtin_prefetch(&p->pages[q.slot[t + kAhead] >> p->log2S]);
+    if (t + kAhead < e && q.slot[t + kAhead] >= 0)
+      __builtin_prefetch(p->pages.data() + (q.slot[t + kAhead] >> p->log2S));
     if (q.dropped[t]) continue;
     q.dropped[t] = 1;
     q.n_vis -= 1;
