@@ -1152,7 +1152,7 @@ akv_status materialize_seq(akv_pool* p, SeqRec& q) {
 // attention planning ([AKV-notes] section 3; [AKV-blog] section 4)
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;
-constexpr int64_t kDecodeChunk = 1024;
+constexpr int64_t kDecodeChunk = 1536;
 
 void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
                     const std::vector<int64_t>& lkv, const std::vector<int64_t>& list_off, int RB,
