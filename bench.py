@@ -67,10 +67,9 @@ def attention_kernel_name(layout, max_rows=None) -> str:
     """The attention kernel the library launches for this layout (max_rows:
     the largest q_len x q heads per kv head over the launch's segments)."""
     if layout.d_nope == 0 and layout.d_rope == 128 and layout.d_v == 128 and max_rows is not None and \
-            max_rows <= 16 and os.environ.get("AKV_DECODE_KERNEL") != "off":
+            max_rows <= 16:
         return "k_decode_attn"
-    if layout.d_nope == 0 and layout.d_rope == 128 and layout.d_v == 128 and \
-            os.environ.get("AKV_ATTN_KERNEL") != "staged" and os.environ.get("AKV_ATTN_WAVES") != "4":
+    if layout.d_nope == 0 and layout.d_rope == 128 and layout.d_v == 128:
         return "k_seg_attn_dl<128,128,0,8,1,4>"
     return "k_seg_attn"
 
@@ -93,18 +92,51 @@ def attention_flops(layout, segments, page_lists) -> tuple:
     return 2.0 * layout.n_q_heads * (d_qk + layout.d_v) * pairs, pairs
 
 
-def cpu_baseline(wl, rows_per_seg: int):
-    """The fp64 oracle as it is, on the host cores: the same step at full size
-    for drop / repos / append / page lists, attention on sampled query rows
-    (scaled to the full step)."""
+_CPU_JOB = {}
+
+
+def _cpu_item(task):
+    """One (segment, kv head) item of the oracle's attention, in a worker."""
+    from threadpoolctl import threadpool_limits
+    from oracle import akv_oracle as AO
+    j = _CPU_JOB
+    si, g = task
+    G = j["pool"].L.n_q_heads // j["pool"].L.n_kv_heads
+    qb, ql, _, _ = j["rows"][si]
+    only = {i: np.zeros(0, np.int64) for i in range(len(j["rows"])) if i != si}   # the other segments: no rows
+    with threadpool_limits(1):
+        out = AO.segment_attention(j["pool"], j["q"], j["rows"], j["ex"], 0.0, rows=only,
+                                   heads=range(g * G, (g + 1) * G))
+    return si, g, out[qb:qb + ql, g * G:(g + 1) * G]
+
+
+def host_cpu():
+    """CPU model and the cores this process may use (at most 16: the GPU machine's
+    share for one GPU)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return model, max(1, min(16, n))
+
+
+def cpu_baseline(wl):
+    """The fp64 oracle as it is, on the host cores, over the whole 64K step:
+    drop, repos, append and page lists in this process, then segment-batch
+    attention for all 2,048 queries split into (segment, kv head) items over
+    worker processes, each with one BLAS thread.  Must run before this
+    process touches the GPU (the workers are forked)."""
+    import multiprocessing as mp
     import oracle
     from oracle import akv_oracle as AO
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+    model, cores = host_cpu()
     pool = AO.Pool(wl.layout, wl.page_order)
     ops = list(wl.ops)
     i_drop = next(i for i, o in enumerate(ops) if isinstance(o, W.Drop))
@@ -116,21 +148,25 @@ def cpu_baseline(wl, rows_per_seg: int):
         oracle.apply_op(pool, op)
     ex, rows = oracle.segment_lists(pool, att.segments)
     t_ops = time.perf_counter() - t0
-    rng = np.random.default_rng(0)
-    sample = {i: np.sort(rng.choice(sg.q_len, rows_per_seg, replace=False)) for i, sg in enumerate(att.segments)}
     q = W.bf16_to_f64(att.q)
+    _CPU_JOB.update(pool=pool, q=q, rows=rows, ex=ex)
+    tasks = [(si, g) for si in range(len(rows)) for g in range(wl.layout.n_kv_heads)]
     t0 = time.perf_counter()
-    AO.segment_attention(pool, q, rows, ex, 0.0, rows=sample)
+    with mp.get_context("fork").Pool(cores) as workers:
+        done = workers.map(_cpu_item, tasks, chunksize=1)
     t_att = time.perf_counter() - t0
-    full_rows = sum(sg.q_len for sg in att.segments)
-    frac = rows_per_seg * len(att.segments) / full_rows
+    _CPU_JOB.clear()
+    assert len(done) == len(tasks) and all(np.isfinite(o).all() for _, _, o in done)
     flops, _ = attention_flops(wl.layout, rows, ex)
-    t_step = t_ops + t_att / frac
+    t_step = t_ops + t_att
+    n_q = int(att.q.shape[0])
     return dict(value=round(flops / t_step / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample=(f"64K step: drop/repos/append/page lists at full size ({t_ops:.1f} s); attention on "
-                        f"{rows_per_seg} query rows per segment x all heads ({t_att:.1f} s), scaled by "
-                        f"{1 / frac:.0f}x to the {full_rows} query rows"),
-                est_step_s=round(t_step, 2))
+                cpu=model, ms_per_step=round(t_step * 1e3, 1),
+                query_tokens_per_s=round(n_q / t_step, 1),
+                sample=(f"the whole 64K step once: drop / repos / append / page lists in one process "
+                        f"({t_ops:.1f} s), attention for all {n_q} query rows as {len(tasks)} "
+                        f"(segment, kv head) items over {cores} worker processes with one BLAS thread each "
+                        f"({t_att:.1f} s)"))
 
 
 def compact_extra(pool, seqs, L) -> dict:
@@ -432,7 +468,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--decode-steps", type=int, default=8, help="decode steps per rep (decode configs)")
-    ap.add_argument("--cpu-rows", type=int, default=16, help="oracle query rows per segment")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--repos-layers", type=int, default=32,
                     help="layers of the extra batched-repos line (0: skip it)")
@@ -458,12 +493,20 @@ def main():
         print(json.dumps(run_config(args)), flush=True)
         return
 
-    import torch
-    import device_script as D
-    import kv_cache_drop_amd as akv
     import workloads as W
 
     wl = W.c2_64k(args.seed)
+    cpu = None
+    if not args.no_cpu_baseline:
+        # before any GPU use: the oracle's workers are forked from this process
+        log("[bench] timing the fp64 oracle on the host cores (the whole 64K step)")
+        cpu = cpu_baseline(wl)
+        log(f"[bench] oracle: {cpu['sample']}")
+
+    import torch
+    import device_script as D
+    import kv_cache_drop_amd as akv
+
     L = wl.layout
     ops = wl.ops
     hist, drop, repos, new, att = ops[1], ops[2], ops[3], ops[4], ops[5]
@@ -542,11 +585,6 @@ def main():
     layers_rec = None
     if args.repos_layers > 0:
         layers_rec = repos_layers_extra(args, L, hist, drop, repos, hk, hv, rep_bytes)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the fp64 oracle on the host (bounded sample)")
-        cpu = cpu_baseline(wl, args.cpu_rows)
 
     rec = {
         "metric": "segment-batch attn TFLOP/s + repos GB/s at 64K ctx, % of MI355X roofline",

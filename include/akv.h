@@ -378,6 +378,25 @@ akv_status akv_repos_plan(akv_pool* pool, int32_t seq, const akv_span* spans, co
                           int32_t n_spans, int32_t* slot_out, int32_t* delta_out, int32_t cap,
                           int32_t* n_out);
 
+/* Dry run of the segment planner of akv_segment_attention ([AKV-notes]
+ * section 3: one launch over every segment; [AKV-blog] section 4): the same
+ * validation and errors (a page-table-only pool is accepted), then the work
+ * list the call would launch, in grid order.  Item i runs as block i: rows
+ * row0 .. row0 + rows_per_block - 1 (clipped to the segment's q_len x group
+ * packed rows, token-major) of kv head kv_head, over list entries k_begin ..
+ * k_end - 1 clipped to each row's causal limit; seg = -1 marks a padding
+ * block.  part >= 0: the item writes fp32 partials of its rows from partial
+ * row `part` on, and combine entry (seg, kv_head, row0, part0, n_split, rows)
+ * merges split j's partial rows part0 + j * rows + r.  n_cu: compute units to
+ * plan for (0 = the pool's device, or 256).  Outputs may be NULL (counts
+ * only); AKV_ERANGE when a capacity is too small.  Changes nothing. */
+typedef struct { int32_t seg, kv_head, row0, k_begin, k_end, part; } akv_attn_item;
+typedef struct { int32_t seg, kv_head, row0, part0, n_split, rows; } akv_attn_combine;
+akv_status akv_attention_plan(akv_pool* pool, int32_t n_q_tokens, const akv_segment* segs, int32_t n_segs,
+                              const akv_extent* page_lists, int32_t n_ext, int32_t n_cu, akv_attn_item* items,
+                              int32_t items_cap, int32_t* n_items, akv_attn_combine* comb, int32_t comb_cap,
+                              int32_t* n_comb, int32_t* rows_per_block, int64_t* part_rows);
+
 /* Kernel timing: when enabled, the library brackets each of its kernel
  * launches with HIP events on the pool's stream.  akv_timing_read waits for the
  * stream, returns the summed milliseconds and launch count of one kernel kind

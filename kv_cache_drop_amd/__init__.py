@@ -76,6 +76,8 @@ SYMBOLS = {
     "akv_seq_info": [_P, _I, _IP, _IP, ctypes.POINTER(ctypes.c_double)],
     "akv_pool_queues": [_P, _IP, _I, _IP, _IP, _I, _IP],
     "akv_repos_plan": [_P, _I, _IP, _IP, _I, _IP, _IP, _I, _IP],
+    "akv_attention_plan": [_P, _I, _IP, _I, _IP, _I, _I, _IP, _I, _IP, _IP, _I, _IP, _IP,
+                           ctypes.POINTER(ctypes.c_int64)],
     "akv_tree_create": [ctypes.POINTER(_P)],
     "akv_tree_destroy": [_P],
     "akv_tree_insert": [_P, _IP, _I, _I],
@@ -142,7 +144,8 @@ def attention_supported(d_nope: int, d_rope: int, d_v: int) -> bool:
 class Pool:
     """A paged KV pool.  With device=True the page arrays and the scratch
     buffer are torch tensors on `device` (attributes k_pages, kpe_pages,
-    v_pages, scratch); with device=False the pool is page-table-only."""
+    v_pages, scratch; the page arrays start zero-filled, so unused slots never
+    hold stale bits); with device=False the pool is page-table-only."""
 
     def __init__(self, n_q_heads: int, n_kv_heads: int, d_nope: int, d_rope: int, d_v: int,
                  page_size: int, num_pages: int, kpe_per_head: int = 0, pairing: int = 0,
@@ -169,11 +172,11 @@ class Pool:
             bf = torch.bfloat16
             if d_nope > 0:
                 hpe = n_kv_heads if kpe_per_head else 1
-                self.k_pages = torch.empty((num_pages, n_kv_heads, page_size, d_nope), dtype=bf, device=dev)
-                self.kpe_pages = torch.empty((num_pages, hpe, page_size, d_rope), dtype=bf, device=dev)
+                self.k_pages = torch.zeros((num_pages, n_kv_heads, page_size, d_nope), dtype=bf, device=dev)
+                self.kpe_pages = torch.zeros((num_pages, hpe, page_size, d_rope), dtype=bf, device=dev)
             else:
-                self.k_pages = torch.empty((num_pages, n_kv_heads, page_size, d_rope), dtype=bf, device=dev)
-            self.v_pages = torch.empty((num_pages, n_kv_heads, page_size, d_v), dtype=bf, device=dev)
+                self.k_pages = torch.zeros((num_pages, n_kv_heads, page_size, d_rope), dtype=bf, device=dev)
+            self.v_pages = torch.zeros((num_pages, n_kv_heads, page_size, d_v), dtype=bf, device=dev)
             self.scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device=dev)
             self.stream = stream if stream is not None else torch.cuda.current_stream(dev)
             st = L.akv_pool_create(ctypes.byref(lay), _ptr(order) if order is not None else None,
@@ -323,6 +326,24 @@ class Pool:
         _check(lib().akv_repos_plan(self._h, seq, _ptr(sp), _ptr(dl), len(sp), _ptr(slot), _ptr(delta),
                                     n.value, ctypes.byref(n)))
         return slot[: n.value], delta[: n.value]
+
+    def attention_plan(self, n_q_tokens: int, segments, page_lists, n_cu: int = 0):
+        """Dry run of the attention planner (akv_attention_plan): returns
+        (items [n, 6] = seg, kv_head, row0, k_begin, k_end, part in grid order;
+        combine [m, 6] = seg, kv_head, row0, part0, n_split, rows;
+        rows_per_block, partial rows)."""
+        sg = _i32(segments).reshape(-1, 4)
+        ex = _i32(page_lists).reshape(-1, 3)
+        ni, nc, rb = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        pr = ctypes.c_int64()
+        args = (self._h, int(n_q_tokens), _ptr(sg), len(sg), _ptr(ex), len(ex), int(n_cu))
+        _check(lib().akv_attention_plan(*args, None, 0, ctypes.byref(ni), None, 0, ctypes.byref(nc),
+                                        ctypes.byref(rb), ctypes.byref(pr)))
+        items = np.zeros((max(ni.value, 1), 6), np.int32)
+        comb = np.zeros((max(nc.value, 1), 6), np.int32)
+        _check(lib().akv_attention_plan(*args, _ptr(items), ni.value, ctypes.byref(ni), _ptr(comb), nc.value,
+                                        ctypes.byref(nc), ctypes.byref(rb), ctypes.byref(pr)))
+        return items[: ni.value], comb[: nc.value], rb.value, pr.value
 
     def splice(self, seq: int, spans, stub_lens, k=None, kpe=None, v=None) -> np.ndarray:
         sp = _i32(spans).reshape(-1, 2)

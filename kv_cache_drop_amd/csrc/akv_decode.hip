@@ -28,8 +28,6 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
-#include <cstring>
 
 #include "akv_internal.h"
 
@@ -350,14 +348,6 @@ __global__ __launch_bounds__(64 * DEC_WAVES, 2) void k_decode_attn(AttnArgs a) {
 }
 
 }  // namespace
-
-bool decode_attn_enabled() {
-  static const bool on = [] {
-    const char* e = getenv("AKV_DECODE_KERNEL");
-    return !(e && strcmp(e, "off") == 0);
-  }();
-  return on;
-}
 
 __global__ __launch_bounds__(256) void k_expand_didx(const Extent* __restrict__ ex, const int32_t* __restrict__ ex_off,
                                                      const int32_t* __restrict__ ex_didx, int n_ext,

@@ -47,17 +47,12 @@ struct CombItem {
 
 constexpr int ATTN_KTILE = 64;       // keys per pipeline stage
 
-// Packed rows per attention block of the kernel variant launched for a layout
-// with this d_nope (128 or 256).
+// Packed rows per block of the prefill attention kernels (256 for every layout).
 int attn_rows_per_block(int d_nope);
 
 // ---- launchers --------------------------------------------------------------
-// fp32 cos/sin table of n_deltas deltas: table[di][0..d/2) = cos,
-// table[di][d/2..d) = sin (n_deltas x d_rope floats).
-hipError_t launch_rot_table(hipStream_t st, int d_rope, const int32_t* deltas, int n_deltas,
-                            const double* inv_freq, float* table);
-
-// Rotates the items in place with the table's rows (RotItem::didx), in each
+// Rotates the items in place with the fp32 cos/sin table's rows (RotItem::didx;
+// row = cos of the d_rope/2 pairs, then sin), in each
 // of the n_layers page arrays listed in krs (a device array of pointers).
 hipError_t launch_rotate(hipStream_t st, uint16_t* const* krs, int n_layers, int n_heads, int page_size,
                          int d_rope, int pairing, const RotItem* items, int n_items, const float* table);
@@ -125,9 +120,6 @@ hipError_t launch_decode_attn(hipStream_t st, const AttnArgs& a);
 // Per list entry of each extent e (entries ex_off[e] .. + hi - lo): ex_didx[e].
 hipError_t launch_expand_didx(hipStream_t st, const Extent* ex, const int32_t* ex_off, const int32_t* ex_didx,
                               int n_ext, int32_t* out);
-// False when the environment sets AKV_DECODE_KERNEL=off (the prefill kernel
-// then runs decode launches too, for comparison).
-bool decode_attn_enabled();
 
 bool attn_dims_supported(int d_nope, int d_rope, int d_v);
 

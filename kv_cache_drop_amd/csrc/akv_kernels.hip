@@ -13,8 +13,6 @@
 //   k_combine      split-KV merge of (m, l, O) partials
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
-#include <cstring>
 #include <type_traits>
 
 #include "akv_internal.h"
@@ -42,9 +40,9 @@ __device__ __forceinline__ unsigned pack_bf2(float a, float b) {
 // ---------------------------------------------------------------------------
 // repos rotation ([AKV-blog] section 2, The Repos Primitive; [Leyline] Method)
 //
-// k_rot_table: one block per distinct delta forms the d_rope/2 angles
-// delta * theta_i in fp64, reduces them mod 2*pi and stores cos and sin as
-// fp32 (table[di][0..half) = cos, table[di][half..d) = sin).
+// The host forms each distinct delta's row of cos and sin (fp64 angle
+// delta * theta_i reduced mod 2*pi, stored as fp32: table[di][0..half) = cos,
+// table[di][half..d) = sin) and uploads it with the work list.
 // k_rotate: one block per (work item, layer) — items are (page, rows lo..hi-1,
 // delta), the grid's second dimension picks one of n_layers page arrays that
 // share the page table; the block
@@ -60,19 +58,6 @@ __device__ __forceinline__ unsigned rot_pair_word(unsigned w, float c, float s) 
   // word holds an interleaved pair (x = low half, y = high half)
   float x = bf_lo(w), y = bf_hi(w);
   return pack_bf2(fmaf(x, c, -y * s), fmaf(x, s, y * c));
-}
-
-__global__ __launch_bounds__(64) void k_rot_table(int d, const int32_t* __restrict__ deltas,
-                                                  const double* __restrict__ inv_freq,
-                                                  float* __restrict__ table) {
-  const int half = d >> 1, i = threadIdx.x;
-  if (i >= half) return;
-  const double ang = (double)deltas[blockIdx.x] * inv_freq[i];
-  const double red = ang - 6.283185307179586476925 * rint(ang * 0.15915494309189533577);
-  double sv, cv;
-  sincos(red, &sv, &cv);
-  table[(size_t)blockIdx.x * d + i] = (float)cv;
-  table[(size_t)blockIdx.x * d + half + i] = (float)sv;
 }
 
 __global__ __launch_bounds__(ROT_THREADS, 8) void k_rotate(uint16_t* const* __restrict__ krs, int n_heads,
@@ -158,13 +143,6 @@ __global__ __launch_bounds__(ROT_THREADS, 8) void k_rotate(uint16_t* const* __re
       *(u32x4*)pb[i] = ob;
     }
   }
-}
-
-hipError_t launch_rot_table(hipStream_t st, int d_rope, const int32_t* deltas, int n_deltas,
-                            const double* inv_freq, float* table) {
-  if (n_deltas <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rot_table, dim3(n_deltas), dim3(64), 0, st, d_rope, deltas, inv_freq, table);
-  return hipGetLastError();
 }
 
 hipError_t launch_rotate(hipStream_t st, uint16_t* const* krs, int n_layers, int n_heads, int page_size,
@@ -1027,46 +1005,17 @@ bool attn_dims_supported(int d_nope, int d_rope, int d_v) {
   return (d_nope == 128 && d_rope == 64 && d_v == 128) || (d_nope == 32 && d_rope == 32 && d_v == 32);
 }
 
-// Waves per attention block: 8 (one 256-row block per CU, two waves per SIMD)
-// or 4 (128-row blocks, two independent blocks per CU).  The MLA 192-dim
-// kernel needs the registers of one block per CU.
-static int attn_waves(int d_nope) {
-  if (d_nope == 128) return 8;
-  static int w = [] {
-    const char* e = getenv("AKV_ATTN_WAVES");
-    return (e && atoi(e) == 4) ? 4 : 8;
-  }();
-  return w;
-}
-
-int attn_rows_per_block(int d_nope) { return 32 * attn_waves(d_nope); }
-
-
-// The 128-dim GQA layout runs the direct-to-LDS kernel; AKV_ATTN_KERNEL=staged
-// selects the register-staged kernel instead (kept for comparison).
-static bool attn_use_dl() {
-  static bool dl = [] {
-    const char* e = getenv("AKV_ATTN_KERNEL");
-    return !(e && strcmp(e, "staged") == 0);
-  }();
-  return dl;
-}
+// Every attention block holds 8 waves (256 packed rows, one block per CU, two
+// waves per SIMD).
+int attn_rows_per_block(int) { return 256; }
 
 template <int DQK, int DV, int DNOPE>
 static hipError_t launch_attn_t(hipStream_t st, const AttnArgs& a) {
   if constexpr (DQK == 128 && DV == 128 && DNOPE == 0) {
-    if (attn_waves(DNOPE) == 8 && attn_use_dl()) {
-      hipLaunchKernelGGL((k_seg_attn_dl<128, 128, 0, 8, 1, 4>), dim3(a.n_items), dim3(512), 0, st, a);
-      return hipGetLastError();
-    }
-  }
-  if constexpr (DNOPE == 128) {
-    hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE, 8>), dim3(a.n_items), dim3(512), 0, st, a);
+    // the 128-dim GQA layout: direct-to-LDS pipeline
+    hipLaunchKernelGGL((k_seg_attn_dl<128, 128, 0, 8, 1, 4>), dim3(a.n_items), dim3(512), 0, st, a);
   } else {
-    if (attn_waves(DNOPE) == 8)
-      hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE, 8>), dim3(a.n_items), dim3(512), 0, st, a);
-    else
-      hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE, 4>), dim3(a.n_items), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE, 8>), dim3(a.n_items), dim3(512), 0, st, a);
   }
   return hipGetLastError();
 }

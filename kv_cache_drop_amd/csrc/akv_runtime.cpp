@@ -188,6 +188,11 @@ struct akv_pool {
   int t_cnt[AKV_K_KINDS] = {};
   std::vector<float> t_each[AKV_K_KINDS];   // each launch's milliseconds since the last read
 
+  // cos / sin rows of recently used deltas (rotation tables are formed on the
+  // host and uploaded with each call's work list)
+  std::unordered_map<int32_t, std::vector<float>> rot_cache;
+  std::vector<float> rot_tab;
+
   int rope_heads() const { return (L.d_nope > 0 && !L.kpe_per_head) ? 1 : L.n_kv_heads; }
   uint16_t* rope_array() const { return L.d_nope > 0 ? kpe : k; }
 };
@@ -778,13 +783,39 @@ void stg_release(akv_pool* p, const DirectRegion& r) {
   p->stg.pending.push_back({r.b, r.e, ev});
 }
 
+// Rotation table of the given deltas into p->rot_tab: row i holds cos of the
+// d_rope/2 pairs at angle deltas[i] * theta_j, then their sin, as fp32
+// ([AKV-blog] section 2, The Repos Primitive; [Leyline] Method and
+// Limitations, fp32 rotation).  The angle is formed in fp64 and reduced mod
+// 2 pi before sincos, so large deltas keep full accuracy.  Rows of recent
+// deltas are kept in the pool (the same deltas recur over layers and steps).
+const std::vector<float>& rot_table_rows(akv_pool* p, const int32_t* deltas, size_t n) {
+  const int d = p->L.d_rope, half = d / 2;
+  p->rot_tab.resize(n * (size_t)d);
+  if (p->rot_cache.size() > 8192) p->rot_cache.clear();
+  for (size_t i = 0; i < n; ++i) {
+    std::vector<float>& row = p->rot_cache[deltas[i]];
+    if (row.empty()) {
+      row.resize(d);
+      for (int j = 0; j < half; ++j) {
+        const double ang = (double)deltas[i] * p->inv_freq[j];
+        const double red = ang - 6.283185307179586476925 * std::rint(ang * 0.15915494309189533577);
+        row[j] = (float)std::cos(red);
+        row[half + j] = (float)std::sin(red);
+      }
+    }
+    std::copy(row.begin(), row.end(), p->rot_tab.begin() + i * (size_t)d);
+  }
+  return p->rot_tab;
+}
+
 // Per-call scratch bytes left after the persistent tables (a conservative
 // bound checked before any state changes, so a short buffer leaves no trace).
-// Scratch bytes of one rotation: items, deltas, the cos/sin table, the layer
-// pointer table, and the alignment of each upload.
+// Scratch bytes of one rotation: items, the cos/sin table, the layer pointer
+// table, and the alignment of each upload.
 size_t rotate_scratch_bytes(const akv_pool* p, size_t n_items, size_t n_deltas, size_t n_layers) {
-  return n_items * sizeof(akv::RotItem) + n_deltas * 4 + n_deltas * (size_t)p->L.d_rope * 4 +
-         n_layers * sizeof(void*) + 4 * 256;
+  return n_items * sizeof(akv::RotItem) + n_deltas * (size_t)p->L.d_rope * 4 + n_layers * sizeof(void*) +
+         3 * 256;
 }
 
 akv_status scratch_fits(const akv_pool* p, size_t bytes) {
@@ -844,20 +875,17 @@ akv_status device_rotate(akv_pool* p, const std::vector<akv::RotItem>& items,
   // item before it can address its keys, and reading it across PCIe would
   // add that latency to each block (measured: 30 -> 35 us at the 64K step).
   ScratchCursor sc(p, rotate_scratch_bytes(p, items.size(), deltas.size(), krs.size()));
+  const std::vector<float>& tab = rot_table_rows(p, deltas.data(), deltas.size());
   void* dv[3];
   akv_status st = upload_arrays(p, sc,
                                 {{items.data(), items.size() * sizeof(akv::RotItem)},
-                                 {deltas.data(), deltas.size() * 4},
+                                 {tab.data(), tab.size() * 4},
                                  {krs.data(), krs.size() * sizeof(uint16_t*)}},
                                 dv);
   if (st != AKV_OK) return st;
-  void *ditems = dv[0], *ddeltas = dv[1], *dkrs = dv[2];
-  float* dtab = (float*)sc.take(deltas.size() * (size_t)p->L.d_rope * 4);
-  if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small for this call (%zu bytes per call)",
-                                 p->scratch_bytes - p->scratch_base);
-  hipError_t e = akv::launch_rot_table(p->stream, p->L.d_rope, (const int32_t*)ddeltas,
-                                       (int)deltas.size(), (const double*)p->scratch, dtab);
-  if (e != hipSuccess) return check_launch(e, "rotation table kernel launch");
+  void *ditems = dv[0], *dkrs = dv[2];
+  const float* dtab = (const float*)dv[1];
+  hipError_t e;
   KTimer tm(p, AKV_K_ROTATE);
   e = akv::launch_rotate(p->stream, (uint16_t* const*)dkrs, (int)krs.size(), p->rope_heads(), p->L.page_size,
                          p->L.d_rope, p->L.pairing, (const akv::RotItem*)ditems, (int)items.size(), dtab);
@@ -1155,7 +1183,7 @@ constexpr int kXcds = 8;
 constexpr int64_t kDecodeChunk = 1536;
 
 void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
-                    const std::vector<int64_t>& lkv, const std::vector<int64_t>& list_off, int RB,
+                    const std::vector<int64_t>& lkv, const std::vector<int64_t>& list_off, int RB, int n_cu,
                     AttnPlan& plan) {
   const akv_layout& L = p->L;
   const int G = L.n_q_heads / L.n_kv_heads;
@@ -1171,7 +1199,7 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
   // split the key range only when the row tiles alone cannot fill the CUs
   // (at most 16 here, 64 for decode items: the combine kernel holds one split
   // per lane of a wave)
-  if (base > 0 && base < p->n_cu) target = (int)std::min<int64_t>(16, (2LL * p->n_cu + base - 1) / base);
+  if (base > 0 && base < n_cu) target = (int)std::min<int64_t>(16, (2LL * n_cu + base - 1) / base);
   // ... or when one row tile alone would hold a CU well past the even share
   // of the launch (few query rows over long lists: decode): such a segment's
   // key range is cut into blocks of at most half a CU's share.
@@ -1185,7 +1213,7 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
       total_cost += (int64_t)L.n_kv_heads * (std::min<int64_t>(lkv[i], lkv[i] - lq + last_row / G + 1) + 64);
     }
   }
-  const int64_t cu_share = total_cost / p->n_cu;
+  const int64_t cu_share = total_cost / n_cu;
   const int64_t block_cap = std::max<int64_t>(2048, cu_share / 2);
 
   // key splits of each segment
@@ -1412,10 +1440,9 @@ akv_status akv_pool_create(const akv_layout* layout, const int32_t* page_order, 
       p->scratch = (char*)scratch;
       p->scratch_bytes = scratch_bytes;
       p->stream = (hipStream_t)hip_stream;
-      const size_t tab = align_up(sizeof(double) * p->inv_freq.size(), 256);
-      if (scratch_bytes < tab + 65536) {
+      if (scratch_bytes < 65536) {
         delete p;
-        return fail(AKV_ENOMEM, "scratch must hold at least %zu bytes", tab + 65536);
+        return fail(AKV_ENOMEM, "scratch must hold at least 65536 bytes");
       }
       hipError_t ce = hipStreamCreateWithFlags(&p->cstream, hipStreamNonBlocking);
       if (ce != hipSuccess) {
@@ -1427,22 +1454,8 @@ akv_status akv_pool_create(const akv_layout* layout, const int32_t* page_order, 
       hipDeviceProp_t prop;
       if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
         p->n_cu = prop.multiProcessorCount;
-      p->scratch_base = tab;
-      p->ring_head = tab;
-      char* h;
-      akv_status st = stg_reserve(p, tab, &h);
-      if (st == AKV_OK) {
-        std::memcpy(h, p->inv_freq.data(), sizeof(double) * p->inv_freq.size());
-        st = stg_upload(p, h, p->scratch, sizeof(double) * p->inv_freq.size());
-      }
-      if (st == AKV_OK) {
-        hipError_t e = hipStreamSynchronize(p->stream);
-        if (e != hipSuccess) st = hip_fail(e, "hipStreamSynchronize");
-      }
-      if (st != AKV_OK) {
-        akv_pool_destroy(p);
-        return st;
-      }
+      p->scratch_base = 0;
+      p->ring_head = 0;
     }
     *out = p;
     return AKV_OK;
@@ -1590,21 +1603,15 @@ akv_status akv_seq_clone(akv_pool* p, int32_t src, int32_t first, int32_t n, int
       }
     }
     if (!p->device) return AKV_OK;
-    ScratchCursor sc(p, mv.size() * sizeof(akv::MovePair) + (size_t)p->L.d_rope * 4 + 4 * 256);
-    void *dmv, *ddelta;
-    st = upload_array(p, sc, mv.data(), mv.size() * sizeof(akv::MovePair), &dmv);
-    if (st == AKV_OK) st = upload_array(p, sc, &delta, 4, &ddelta);
+    ScratchCursor sc(p, mv.size() * sizeof(akv::MovePair) + (size_t)p->L.d_rope * 4 + 3 * 256);
+    const std::vector<float>& tab = rot_table_rows(p, &delta, 1);
+    void* dv[2];
+    st = upload_arrays(p, sc, {{mv.data(), mv.size() * sizeof(akv::MovePair)},
+                               {tab.data(), delta != 0 ? tab.size() * 4 : 0}}, dv);
     if (st != AKV_OK) return st;
-    float* dtab = (float*)sc.take((size_t)p->L.d_rope * 4);
-    if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small for this call (%zu bytes per call)",
-                                 p->scratch_bytes - p->scratch_base);
-    const akv_layout& L = p->L;
-    hipError_t e = hipSuccess;
-    if (delta != 0) {
-      e = akv::launch_rot_table(p->stream, L.d_rope, (const int32_t*)ddelta, 1, (const double*)p->scratch,
-                                dtab);
-      if (e != hipSuccess) return check_launch(e, "rotation table kernel launch");
-    }
+    const void* dmv = dv[0];
+    const float* dtab = (const float*)dv[1];
+    hipError_t e;
     KTimer tm(p, AKV_K_CLONE);
     e = move_tokens(p, (const akv::MovePair*)dmv, m, delta != 0 ? dtab : nullptr);
     tm.done();
@@ -2216,13 +2223,62 @@ static bool decode_launch(const akv_pool* p, const int64_t* q_len, int32_t n, in
   const int G = L.n_q_heads / L.n_kv_heads;
   int64_t max_rows = 0;
   for (int32_t i = 0; i < n; ++i) max_rows = std::max<int64_t>(max_rows, q_len[(size_t)i * stride] * G);
-  return akv::decode_attn_enabled() && L.d_nope == 0 && L.d_rope == 128 && L.d_v == 128 &&
+  return L.d_nope == 0 && L.d_rope == 128 && L.d_v == 128 &&
          max_rows <= akv::DECODE_ROWS;
 }
 
 // Segment-batch attention over caller lists; ext_lag (optional, one per
 // extent) is the rotation each extent's keys still owe, applied inside the
 // decode kernel (only decode launches take it).
+// Checks the segments and page lists of an attention launch; fills each
+// segment's list length and offset in the expanded slot list.  *any_rows is
+// false when no segment has a query row.
+static akv_status attn_validate(akv_pool* p, int32_t n_q_tokens, const akv_segment* segs, int32_t n_segs,
+                                const akv_extent* page_lists, int32_t n_ext, std::vector<int64_t>& lkv,
+                                std::vector<int64_t>& list_off, int64_t* total_out, bool* any_rows) {
+  const akv_layout& L = p->L;
+  if (!akv::attn_dims_supported(L.d_nope, L.d_rope, L.d_v))
+    return fail(AKV_EINVAL, "no attention kernel for d_nope=%d d_rope=%d d_v=%d", L.d_nope,
+                L.d_rope, L.d_v);
+  if (n_segs < 0 || n_ext < 0 || n_q_tokens < 0) return fail(AKV_EINVAL, "negative count");
+  if ((n_segs > 0 && !segs) || (n_ext > 0 && !page_lists))
+    return fail(AKV_EINVAL, "segments / page lists are NULL");
+  lkv.assign(n_segs, 0);
+  list_off.assign(n_segs, 0);
+  int64_t total = 0;
+  std::vector<std::pair<int32_t, int32_t>> rows;
+  for (int32_t i = 0; i < n_segs; ++i) {
+    const akv_segment& sg = segs[i];
+    if (sg.q_len < 0 || sg.ext_len < 0) return fail(AKV_EINVAL, "segment %d: negative length", i);
+    if (sg.q_begin < 0 || (int64_t)sg.q_begin + sg.q_len > n_q_tokens)
+      return fail(AKV_ERANGE, "segment %d: query rows outside 0..%d", i, n_q_tokens);
+    if (sg.ext_begin < 0 || (int64_t)sg.ext_begin + sg.ext_len > n_ext)
+      return fail(AKV_ERANGE, "segment %d: extents outside 0..%d", i, n_ext);
+    int64_t n_keys = 0;
+    for (int32_t e = sg.ext_begin; e < sg.ext_begin + sg.ext_len; ++e) {
+      const akv_extent& x = page_lists[e];
+      if (x.page < 0 || x.page >= L.num_pages || x.lo < 0 || x.lo >= x.hi || x.hi > L.page_size)
+        return fail(AKV_ERANGE, "extent %d (%d, %d, %d) outside the pool", e, x.page, x.lo, x.hi);
+      n_keys += x.hi - x.lo;
+    }
+    if (sg.q_len > 0 && n_keys < sg.q_len)
+      return fail(AKV_EINVAL, "segment %d has %lld list entries for %d queries", i,
+                  (long long)n_keys, sg.q_len);
+    if (n_keys > kInt32Max) return fail(AKV_ERANGE, "segment %d list too long", i);
+    lkv[i] = n_keys;
+    list_off[i] = total;
+    total += n_keys;
+    if (sg.q_len > 0) rows.emplace_back(sg.q_begin, sg.q_begin + sg.q_len);
+  }
+  std::sort(rows.begin(), rows.end());
+  for (size_t i = 1; i < rows.size(); ++i)
+    if (rows[i].first < rows[i - 1].second) return fail(AKV_EINVAL, "segments overlap in Q rows");
+  if (total > kInt32Max) return fail(AKV_ERANGE, "page lists too long");
+  *total_out = total;
+  *any_rows = !rows.empty();
+  return AKV_OK;
+}
+
 static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens, const akv_segment* segs,
                                  int32_t n_segs, const akv_extent* page_lists, int32_t n_ext,
                                  const int32_t* ext_lag, float scale, void* out) {
@@ -2230,45 +2286,15 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
     if (!p) return fail(AKV_EINVAL, "NULL pool");
     if (!p->device) return fail(AKV_ESTATE, "attention needs a device pool");
     const akv_layout& L = p->L;
-    if (!akv::attn_dims_supported(L.d_nope, L.d_rope, L.d_v))
-      return fail(AKV_EINVAL, "no attention kernel for d_nope=%d d_rope=%d d_v=%d", L.d_nope,
-                  L.d_rope, L.d_v);
-    if (n_segs < 0 || n_ext < 0 || n_q_tokens < 0) return fail(AKV_EINVAL, "negative count");
-    if ((n_segs > 0 && !segs) || (n_ext > 0 && !page_lists))
-      return fail(AKV_EINVAL, "segments / page lists are NULL");
     if (!(scale >= 0.f) || !std::isfinite(scale)) return fail(AKV_EINVAL, "bad scale");
-    std::vector<int64_t> lkv(n_segs, 0), list_off(n_segs, 0);
+    std::vector<int64_t> lkv, list_off;
     int64_t total = 0;
-    std::vector<std::pair<int32_t, int32_t>> rows;
-    for (int32_t i = 0; i < n_segs; ++i) {
-      const akv_segment& sg = segs[i];
-      if (sg.q_len < 0 || sg.ext_len < 0) return fail(AKV_EINVAL, "segment %d: negative length", i);
-      if (sg.q_begin < 0 || (int64_t)sg.q_begin + sg.q_len > n_q_tokens)
-        return fail(AKV_ERANGE, "segment %d: query rows outside 0..%d", i, n_q_tokens);
-      if (sg.ext_begin < 0 || (int64_t)sg.ext_begin + sg.ext_len > n_ext)
-        return fail(AKV_ERANGE, "segment %d: extents outside 0..%d", i, n_ext);
-      int64_t n_keys = 0;
-      for (int32_t e = sg.ext_begin; e < sg.ext_begin + sg.ext_len; ++e) {
-        const akv_extent& x = page_lists[e];
-        if (x.page < 0 || x.page >= L.num_pages || x.lo < 0 || x.lo >= x.hi || x.hi > L.page_size)
-          return fail(AKV_ERANGE, "extent %d (%d, %d, %d) outside the pool", e, x.page, x.lo, x.hi);
-        n_keys += x.hi - x.lo;
-      }
-      if (sg.q_len > 0 && n_keys < sg.q_len)
-        return fail(AKV_EINVAL, "segment %d has %lld list entries for %d queries", i,
-                    (long long)n_keys, sg.q_len);
-      if (n_keys > kInt32Max) return fail(AKV_ERANGE, "segment %d list too long", i);
-      lkv[i] = n_keys;
-      list_off[i] = total;
-      total += n_keys;
-      if (sg.q_len > 0) rows.emplace_back(sg.q_begin, sg.q_begin + sg.q_len);
-    }
-    std::sort(rows.begin(), rows.end());
-    for (size_t i = 1; i < rows.size(); ++i)
-      if (rows[i].first < rows[i - 1].second) return fail(AKV_EINVAL, "segments overlap in Q rows");
-    if (rows.empty()) return AKV_OK;
+    bool any_rows = false;
+    akv_status vst = attn_validate(p, n_q_tokens, segs, n_segs, page_lists, n_ext, lkv, list_off, &total,
+                                   &any_rows);
+    if (vst != AKV_OK) return vst;
+    if (!any_rows) return AKV_OK;
     if (!Q || !out) return fail(AKV_EINVAL, "Q and out are required");
-    if (total > kInt32Max) return fail(AKV_ERANGE, "page lists too long");
 
     std::vector<int64_t> qlens(n_segs);
     for (int32_t i = 0; i < n_segs; ++i) qlens[i] = segs[i].q_len;
@@ -2290,7 +2316,7 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
     }
     const int rb = decode ? akv::DECODE_ROWS : akv::attn_rows_per_block(L.d_nope);
     AttnPlan& plan = p->hb.plan;
-    plan_attention(p, segs, n_segs, lkv, list_off, rb, plan);
+    plan_attention(p, segs, n_segs, lkv, list_off, rb, p->n_cu, plan);
     if (plan.part_rows > kInt32Max) return fail(AKV_ERANGE, "too many split-KV partial rows");
     // extent offsets for the slot expansion (over all segments' ranges, in order)
     const bool fused = !rot_deltas.empty();
@@ -2324,10 +2350,12 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
     const size_t keys4 = (size_t)std::max<int64_t>(total, 1) * 4;
     const size_t need = plan.segs.size() * sizeof(akv::AttnSeg) + plan.items.size() * sizeof(akv::AttnItem) +
                         plan.comb.size() * sizeof(akv::CombItem) + ex_off.size() * sizeof(akv::Extent) +
-                        (ex_off.size() + ex_didx.size() + rot_deltas.size()) * 4 + keys4 * (fused ? 2 : 1) +
+                        (ex_off.size() + ex_didx.size()) * 4 + keys4 * (fused ? 2 : 1) +
                         rot_deltas.size() * (size_t)L.d_rope * 4 + (size_t)plan.part_rows * (L.d_v + 2) * 4 +
                         12 * 256;
     ScratchCursor sc(p, need);
+    static const std::vector<float> no_rows;
+    const std::vector<float>& rot_rows = fused ? rot_table_rows(p, rot_deltas.data(), rot_deltas.size()) : no_rows;
     void* dv[7];
     akv_status st = upload_arrays(p, sc,
                                   {{plan.segs.data(), plan.segs.size() * sizeof(akv::AttnSeg)},
@@ -2337,14 +2365,14 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
                                     ex_off.size() * sizeof(akv::Extent)},
                                    {ex_off.data(), ex_off.size() * 4},
                                    {ex_didx.data(), ex_didx.size() * 4},
-                                   {rot_deltas.data(), rot_deltas.size() * 4}},
+                                   {rot_rows.data(), rot_rows.size() * 4}},
                                   dv);
     if (st != AKV_OK) return st;
     void *dsegs = dv[0], *ditems = dv[1], *dcomb = plan.comb.empty() ? nullptr : dv[2], *dex = dv[3],
          *doff = dv[4];
     int32_t* dslots = (int32_t*)sc.take((size_t)std::max<int64_t>(total, 1) * 4);
     int32_t* dkey_didx = fused ? (int32_t*)sc.take((size_t)std::max<int64_t>(total, 1) * 4) : nullptr;
-    float* drot = fused ? (float*)sc.take(rot_deltas.size() * (size_t)L.d_rope * 4) : nullptr;
+    const float* drot = fused ? (const float*)dv[6] : nullptr;
     float* part_o = nullptr;
     float* part_ml = nullptr;
     if (plan.part_rows > 0) {
@@ -2364,10 +2392,7 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
     if (e != hipSuccess) return hip_fail(e, "expand kernel launch");
     if (fused) {
       KTimer tm(p, AKV_K_EXPAND);
-      e = akv::launch_rot_table(p->stream, L.d_rope, (const int32_t*)dv[6], (int)rot_deltas.size(),
-                                (const double*)p->scratch, drot);
-      if (e == hipSuccess)
-        e = akv::launch_expand_didx(p->stream, (const akv::Extent*)dex, (const int32_t*)doff,
+      e = akv::launch_expand_didx(p->stream, (const akv::Extent*)dex, (const int32_t*)doff,
                                     (const int32_t*)dv[5], (int)ex_off.size(), dkey_didx);
       tm.done();
       if (e != hipSuccess) return hip_fail(e, "owed-rotation table launch");
@@ -2418,6 +2443,46 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
                                  int32_t n_segs, const akv_extent* page_lists, int32_t n_ext, float scale,
                                  void* out) {
   return attention_impl(p, Q, n_q_tokens, segs, n_segs, page_lists, n_ext, nullptr, scale, out);
+}
+
+akv_status akv_attention_plan(akv_pool* p, int32_t n_q_tokens, const akv_segment* segs, int32_t n_segs,
+                              const akv_extent* page_lists, int32_t n_ext, int32_t n_cu, akv_attn_item* items,
+                              int32_t items_cap, int32_t* n_items, akv_attn_combine* comb, int32_t comb_cap,
+                              int32_t* n_comb, int32_t* rows_per_block, int64_t* part_rows) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    if (!n_items || !n_comb || !rows_per_block || !part_rows) return fail(AKV_EINVAL, "NULL output count");
+    if (n_cu < 0 || items_cap < 0 || comb_cap < 0) return fail(AKV_EINVAL, "negative count");
+    std::vector<int64_t> lkv, list_off;
+    int64_t total = 0;
+    bool any_rows = false;
+    akv_status st = attn_validate(p, n_q_tokens, segs, n_segs, page_lists, n_ext, lkv, list_off, &total,
+                                  &any_rows);
+    if (st != AKV_OK) return st;
+    *n_items = 0;
+    *n_comb = 0;
+    *part_rows = 0;
+    std::vector<int64_t> qlens(n_segs);
+    for (int32_t i = 0; i < n_segs; ++i) qlens[i] = segs[i].q_len;
+    const bool decode = decode_launch(p, qlens.data(), n_segs, 1);
+    const int rb = decode ? akv::DECODE_ROWS : akv::attn_rows_per_block(p->L.d_nope);
+    *rows_per_block = rb;
+    if (!any_rows) return AKV_OK;
+    AttnPlan plan;
+    plan_attention(p, segs, n_segs, lkv, list_off, rb, n_cu > 0 ? n_cu : p->n_cu, plan);
+    *n_items = (int32_t)plan.items.size();
+    *n_comb = (int32_t)plan.comb.size();
+    *part_rows = plan.part_rows;
+    static_assert(sizeof(akv_attn_item) == sizeof(akv::AttnItem), "item layouts");
+    static_assert(sizeof(akv_attn_combine) == sizeof(akv::CombItem), "combine layouts");
+    if ((items && items_cap < *n_items) || (comb && comb_cap < *n_comb))
+      return fail(AKV_ERANGE, "plan needs %d items and %d combine entries", *n_items, *n_comb);
+    if (items) std::memcpy(items, plan.items.data(), plan.items.size() * sizeof(akv::AttnItem));
+    if (comb) std::memcpy(comb, plan.comb.data(), plan.comb.size() * sizeof(akv::CombItem));
+    return AKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
 }
 
 akv_status akv_seq_tokens(akv_pool* p, int32_t s, int32_t first, int32_t n, int32_t* slot,

@@ -621,7 +621,7 @@ def last_visible(lkv: int, lq: int, i: np.ndarray) -> np.ndarray:
 
 
 def segment_attention(pool: Pool, q: np.ndarray, segments, page_lists, scale: float = 0.0,
-                      rows: Optional[dict] = None) -> np.ndarray:
+                      rows: Optional[dict] = None, heads=None) -> np.ndarray:
     """Causal attention of each query segment over its own KV list.
 
     q: [Nq, Hq, d_qk] fp64.  segments: iterable of (q_begin, q_len, ext_begin,
@@ -629,7 +629,8 @@ def segment_attention(pool: Pool, q: np.ndarray, segments, page_lists, scale: fl
     queries and Lkv list entries sees list entries 0 .. Lkv - Lq + i.  Query
     head h reads kv head floor(h * Hkv / Hq).  Returns [Nq, Hq, d_v] with NaN
     in rows no segment covers.  `rows` optionally maps a segment index to the
-    local query rows to evaluate (sampling)."""
+    local query rows to evaluate (sampling); `heads` optionally lists the q
+    heads to evaluate (the others stay NaN)."""
     L = pool.L
     q = np.asarray(q, np.float64)
     nq = q.shape[0]
@@ -647,7 +648,7 @@ def segment_attention(pool: Pool, q: np.ndarray, segments, page_lists, scale: fl
             raise EInval("segment has fewer KV entries than queries")
         loc = np.arange(ql) if rows is None or si not in rows else np.asarray(rows[si])
         lim = last_visible(lkv, ql, loc)
-        for h in range(L.n_q_heads):
+        for h in (range(L.n_q_heads) if heads is None else heads):
             g = h // grp
             s = (q[qb + loc, h, :] @ k[:, g, :].T) * scale
             s[np.arange(lkv)[None, :] > lim[:, None]] = -np.inf

@@ -6,7 +6,16 @@ Bars (written in each test):
   rotated bf16 keys ............................ per (token, head) relative L2 error <= 1e-2;
                                                  single rotation: >= 99% of elements equal
                                                  RNE(fp64), the rest within 1 bf16 ulp
-  attention outputs (bf16) ..................... max abs error <= 2e-2 against fp64
+  attention outputs (bf16) ..................... max abs error <= 2e-2 against fp64, and
+                                                 per (row, head) relative L2 error <= 1e-2
+                                                 (tests/parity_check.py; the CPU test
+                                                 test_parity_check.py shows both bars fail on
+                                                 a missing tile, a causal limit off by one and
+                                                 a missing decode split)
+
+Workloads run with their base queries (N(0,1)/8) and, at full size, with the
+stress queries (N(0,1)) and focused queries (rows aimed at their own key, at
+the next hidden key, or at needle keys) of workloads.query_variant.
 """
 import sys
 
@@ -22,8 +31,8 @@ pytestmark = pytest.mark.gpu
 
 akv = pytest.importorskip("kv_cache_drop_amd")
 import device_script as D  # noqa: E402  (tests/ is on sys.path via conftest)
+from parity_check import ATOL_ATTN, check_attention_rows  # noqa: E402
 
-ATOL_ATTN = 2e-2
 RTOL_KEY = 1e-2
 
 
@@ -88,16 +97,14 @@ def _check_visible_kv(pool, op_pool, L):
 
 
 def _check_attention(outs, res, wl, rows_per_seg=None):
-    worst = 0.0
+    """Page tables bit-exact, then both attention bars; returns the worst
+    (abs, relative L2) errors."""
+    wa = wr = 0.0
     for o, rec in zip(outs, res.attention):
         np.testing.assert_array_equal(o["extents"], rec["extents"])
-        got = D.to_f64(o["out"])
-        want = rec["out"]
-        cover = ~np.isnan(want[:, 0, 0])
-        err = np.abs(got[cover] - want[cover])
-        worst = max(worst, float(err.max()) if err.size else 0.0)
-        assert err.size == 0 or err.max() <= ATOL_ATTN, f"attention max abs err {err.max()}"
-    return worst
+        ea, er = check_attention_rows(D.to_f64(o["out"]), rec["out"], wl.name)
+        wa, wr = max(wa, ea), max(wr, er)
+    return wa, wr
 
 
 def _full_parity(wl, keep_log=False, **pool_kw):
@@ -106,8 +113,8 @@ def _full_parity(wl, keep_log=False, **pool_kw):
     res = oracle.run_workload(wl, keep_log=keep_log)
     _check_tables(pool, res.pool)
     wk = _check_visible_kv(pool, res.pool, wl.layout)
-    wa = _check_attention(outs, res, wl)
-    _say(f"[gpu] {wl.name}: worst key rel err {wk:.2e}, worst attention abs err {wa:.2e}")
+    wa, wr = _check_attention(outs, res, wl)
+    _say(f"[gpu] {wl.name}: worst key rel err {wk:.2e}, attention abs err {wa:.2e}, rel L2 {wr:.2e}")
     pool.close()
 
 
@@ -116,7 +123,8 @@ def _full_parity(wl, keep_log=False, **pool_kw):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("pairing", [0, 1])
 @pytest.mark.parametrize("d,heads,page,theta", [(128, 8, 16, 5e5), (64, 2, 16, 1e4), (64, 1, 64, 1e4),
-                                                 (32, 3, 8, 1e4), (16, 1, 4, 1e4)])
+                                                 (32, 3, 8, 1e4), (16, 1, 4, 1e4), (256, 2, 16, 1e4),
+                                                 (192, 1, 8, 5e5)])
 def test_rotate_single_call_elementwise(pairing, d, heads, page, theta):
     """One repos call from bf16 keys: every element equals RNE of the fp64
     rotation of the same bf16 input, or is one bf16 ulp away (fp32 rounding
@@ -265,8 +273,9 @@ def test_append_and_compaction_bit_exact(mla):
 # segment-batch attention, small scripts (whole outputs)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("variant", ["canonical", "cumulative", "unaligned"])
-def test_c1_tiny_full(variant):
-    _full_parity(W.c1_tiny(0, variant))
+@pytest.mark.parametrize("mode", ["base", "focus"])
+def test_c1_tiny_full(variant, mode):
+    _full_parity(_variant(W.c1_tiny(0, variant), mode))
 
 
 @pytest.mark.parametrize("seed", range(8))
@@ -294,8 +303,9 @@ def test_fuzz_mla_full(seed, kph, pairing):
                               mla_dims=(32, 32, 32)))
 
 
-def test_c3_mla_full():
-    _full_parity(W.c3_mla(0))
+@pytest.mark.parametrize("mode", ["base", "stress", "focus"])
+def test_c3_mla_full(mode):
+    _full_parity(_variant(W.c3_mla(0), mode))
 
 
 @pytest.mark.parametrize("seed,pages_factor", [(0, 3.0), (1, 3.0), (2, 0.7), (3, 0.7)])
@@ -330,8 +340,8 @@ def test_scratch_ring_small_buffer(seed):
     res = oracle.run_workload(wl)
     _check_tables(pool, res.pool)
     _check_visible_kv(pool, res.pool, wl.layout)
-    wa = _check_attention(outs, res, wl)
-    _say(f"[gpu] ring: {mib} MiB, worst attention abs err {wa:.2e}")
+    wa, wr = _check_attention(outs, res, wl)
+    _say(f"[gpu] ring: {mib} MiB, worst attention abs err {wa:.2e}, rel L2 {wr:.2e}")
     pool.close()
 
 
@@ -366,7 +376,7 @@ def test_attention_edge_cases():
     want = AO.segment_attention(op, W.bf16_to_f64(qn), segs, allx)
     got = D.to_f64(out)
     cov = ~np.isnan(want[:, 0, 0])
-    assert np.abs(got[cov] - want[cov]).max() <= ATOL_ATTN
+    check_attention_rows(got, want, "edge cases")
     assert np.all(got[~cov] == 7.0)
     pool.close()
 
@@ -406,17 +416,23 @@ def _sampled_parity(wl, n_rows=24, seed=0):
     res = oracle.run_workload(wl, sample_rows=sample)
     _check_tables(pool, res.pool)
     wk = _check_visible_kv(pool, res.pool, wl.layout)
-    wa = _check_attention(outs, res, wl)
-    _say(f"[gpu] {wl.name}: worst key rel err {wk:.2e}, worst attention abs err {wa:.2e}")
+    wa, wr = _check_attention(outs, res, wl)
+    _say(f"[gpu] {wl.name}: worst key rel err {wk:.2e}, attention abs err {wa:.2e}, rel L2 {wr:.2e}")
     pool.close()
 
 
-def test_c2_64k_sampled():
-    _sampled_parity(W.c2_64k(0))
+def _variant(wl, mode):
+    return wl if mode == "base" else W.query_variant(wl, mode)
 
 
-def test_c4_batched_sampled():
-    _sampled_parity(W.c4_batched(0), n_rows=6)
+@pytest.mark.parametrize("mode", ["base", "stress", "focus"])
+def test_c2_64k_sampled(mode):
+    _sampled_parity(_variant(W.c2_64k(0), mode))
+
+
+@pytest.mark.parametrize("mode", ["base", "focus"])
+def test_c4_batched_sampled(mode):
+    _sampled_parity(_variant(W.c4_batched(0), mode), n_rows=6)
 
 
 def test_repos_batch_bit_exact_with_per_request_repos():
@@ -444,11 +460,12 @@ def test_repos_batch_bit_exact_with_per_request_repos():
         p.close()
 
 
-def test_c5_128k_sampled():
+@pytest.mark.parametrize("mode", ["base", "stress", "focus"])
+def test_c5_128k_sampled(mode):
     """128K tokens, 64 q heads over 8 kv heads, 60 dropped spans, 8 segments
     of 512 queries: tables and every visible key in full, 6 random rows plus
     the first and last of every segment against the oracle."""
-    _sampled_parity(W.c5_128k(0), n_rows=6)
+    _sampled_parity(_variant(W.c5_128k(0), mode), n_rows=6)
 
 
 @pytest.mark.parametrize("make", [lambda: W.c1_tiny(0, "canonical"), lambda: W.fuzz_small(3, head_dims=(64, 128)),
@@ -484,23 +501,24 @@ def _deferred_parity(wl):
     pool, outs = D.run(wl)
     res = oracle.run_workload(wl)
     _check_tables(pool, res.pool)
-    wa = _check_attention(outs, res, wl)
+    wa, wr = _check_attention(outs, res, wl)
     for s, q in enumerate(res.pool.seqs):
         if q.alive:
             pool.materialize(s)
             assert not pool.lag(s)[~pool.tokens(s)[2]].any()
     torch.cuda.synchronize()
     wk = _check_visible_kv(pool, res.pool, wl.layout)
-    _say(f"[gpu] {wl.name} deferred: worst attention abs err {wa:.2e}, keys after materialize {wk:.2e}")
+    _say(f"[gpu] {wl.name} deferred: attention abs err {wa:.2e}, rel L2 {wr:.2e}, keys after materialize {wk:.2e}")
     return pool
 
 
 @pytest.mark.parametrize("seed,pairing,lq", [(0, 0, 1), (1, 1, 1), (2, 0, 3)])
-def test_decode_deferred_repos_full(seed, pairing, lq):
+@pytest.mark.parametrize("mode", ["base", "focus"])
+def test_decode_deferred_repos_full(seed, pairing, lq, mode):
     """Deferred repos, then a decode launch that turns the owed keys as it
     reads them: every output row against the oracle."""
-    _deferred_parity(W.decode_batch(seed, n_req=8, ctx_lo=4000, ctx_hi=9000, q_len=lq, deferred=True,
-                                    pairing=pairing)).close()
+    _deferred_parity(_variant(W.decode_batch(seed, n_req=8, ctx_lo=4000, ctx_hi=9000, q_len=lq, deferred=True,
+                                             pairing=pairing), mode)).close()
 
 
 @pytest.mark.parametrize("deferred", [False, True])
@@ -551,18 +569,20 @@ def test_prefill_on_owed_keys_rotates_in_place_first():
     _deferred_parity(wl).close()
 
 
-def test_retrigger_64k_sampled():
-    _sampled_parity(W.retrigger(0), n_rows=12)
+@pytest.mark.parametrize("mode", ["base", "stress"])
+def test_retrigger_64k_sampled(mode):
+    _sampled_parity(_variant(W.retrigger(0), mode), n_rows=12)
 
 
 @pytest.mark.parametrize("seed,n_req,lo,hi,hq,lq", [(0, 16, 1024, 4096, 32, 1), (1, 48, 256, 3072, 32, 1),
                                                    (2, 24, 1, 700, 64, 2), (3, 20, 1, 2500, 32, 4),
                                                    (4, 12, 1, 40, 32, 1)])
-def test_decode_batch_full(seed, n_req, lo, hi, hq, lq):
+@pytest.mark.parametrize("mode", ["base", "stress", "focus"])
+def test_decode_batch_full(seed, n_req, lo, hi, hq, lq, mode):
     """q_len new tokens per request after drop and repos, all requests in one
     launch (4 to 16 rows per kv head, lists of 1 to several thousand keys):
     every output row and every visible key against the oracle."""
-    _full_parity(W.decode_batch(seed, n_req=n_req, ctx_lo=lo, ctx_hi=hi, n_q_heads=hq, q_len=lq))
+    _full_parity(_variant(W.decode_batch(seed, n_req=n_req, ctx_lo=lo, ctx_hi=hi, n_q_heads=hq, q_len=lq), mode))
 
 
 def test_repos_layers_one_launch():

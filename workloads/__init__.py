@@ -38,7 +38,7 @@ __all__ = [
     "Layout", "SeqCreate", "Append", "AppendBatch", "Drop", "Repos", "Splice", "Compact", "Clone",
     "Segment", "Attention", "Workload", "to_bf16", "bf16_to_f64",
     "c1_tiny", "c2_64k", "c3_mla", "c4_batched", "c5_128k", "decode_batch", "retrigger", "fuzz_small",
-    "CONFIGS", "make",
+    "CONFIGS", "make", "query_variant",
 ]
 
 
@@ -784,6 +784,175 @@ def deferred_compaction(seed: int, n_seqs: int = 4, n_rounds: int = 5, page_size
     lay.num_pages = int(pages_factor * ((total + page_size - 1) // page_size)) + 8 * n_all + 16
     return Workload(f"deferred_compaction_{seed}", lay, rng.permutation(lay.num_pages).astype(np.int32), ops,
                     notes={"deferred_compaction": True})
+
+
+# --------------------------------------------------------------------------
+# query variants: stress (Q ~ N(0,1)) and focused attention
+# --------------------------------------------------------------------------
+FOCUS_GAIN = 20.0     # a focused query adds FOCUS_GAIN x a unit vector: score ~ 20 above the rest
+FOCUS_V_CLIP = 3.5    # focused workloads keep |V| <= 3.5 (exact in bf16), see query_variant
+
+
+def _low_freq_dims(lay: Layout, n: int = 8) -> np.ndarray:
+    """Key dims whose rotation angle per position is smallest: the last n/2
+    rotation pairs (MLA: the first n position-free K_nope dims, which are
+    never rotated).  A needle key put there stays aligned with its query
+    direction after a repos by tens of thousands of positions."""
+    if lay.mla:
+        return np.arange(n)
+    d = lay.d_rope
+    pairs = np.arange(d // 2 - n // 2, d // 2)
+    if lay.pairing == 0:
+        return np.sort(np.concatenate([2 * pairs, 2 * pairs + 1]))
+    return np.sort(np.concatenate([pairs, pairs + d // 2]))
+
+
+def _bf16_f32(u: np.ndarray) -> np.ndarray:
+    return bf16_to_f64(u).astype(np.float32)
+
+
+def query_variant(wl: Workload, mode: str, seed: int = 0, n_dirs: int = 4, needles_per_dir: int = 2) -> Workload:
+    """A copy of `wl` with other queries.
+
+    "stress": every query row is drawn N(0,1) in fp32 (the base workloads
+    draw N(0,1)/8, which leaves the softmax nearly uniform over long lists).
+
+    "focus": stress queries, then row i of each segment, q head h, gets one
+    target by (i + h) % 4:
+      0  its own key (the segment's i-th own token, the last entry it sees),
+      1  the key of the next token (hidden from it by causality or by the
+         segment's mask of later tokens),
+      2  a needle direction u: n_dirs directions per sequence, each added
+         (times sqrt(d_qk)) to the keys of needles_per_dir random history
+         tokens, some of which later drops or masks hide,
+      3  nothing;
+    the target's unit vector times FOCUS_GAIN is added to the row, so the
+    target's score stands about 20 above the others and a handful of keys
+    carry almost all of the softmax mass.  Values are clipped to
+    |v| <= FOCUS_V_CLIP so an output dominated by one key stays within the
+    range where bf16 output rounding leaves room under a 2e-2 error bar.
+
+    Own tokens of a segment are its sequence's last q_len appended tokens
+    outside its mask spans (the generators append the query tokens last);
+    workloads whose query tokens are rewritten later (repos, splice or clone
+    after their append) or that clone tokens are refused in focus mode.
+    Input construction only: no rotation, attention or visibility rule."""
+    if mode not in ("stress", "focus"):
+        raise ValueError(mode)
+    rng = _rng(1_000_003 + seed)
+    lay = wl.layout
+    ops = list(wl.ops)
+    out = Workload(f"{wl.name}_{mode}", lay, wl.page_order, ops, dict(wl.notes))
+    if mode == "stress":
+        for i, op in enumerate(ops):
+            if isinstance(op, Attention):
+                ops[i] = Attention(_normal_bf16(rng, op.q.shape), op.segments, op.scale)
+        return out
+
+    G = lay.n_q_heads // lay.n_kv_heads
+    # copies of every op array this variant changes
+    for i, op in enumerate(ops):
+        if isinstance(op, (Append, AppendBatch, Splice)):
+            vf = np.clip(_bf16_f32(op.v), -FOCUS_V_CLIP, FOCUS_V_CLIP)
+            kw = dict(op.__dict__)
+            kw["v"] = to_bf16(vf)
+            kw["k"] = op.k.copy()
+            ops[i] = type(op)(**kw)
+    # logical index -> (op index, row) per sequence, as the ops append tokens
+    src = {}          # seq -> list of (op index, row)
+    hist_ops = {}     # seq -> set of op indices that appended plain (non-stub) tokens
+    last_rewrite = {} # seq -> op index of its last repos / splice
+    n_seqs = 0
+    dims = _low_freq_dims(lay)
+    dirs = {}         # seq -> [n_dirs, len(dims)] unit vectors
+    beta = float(np.sqrt(lay.d_qk))
+
+    def key_row(seq, t):
+        oi, r = src[seq][t]
+        op = ops[oi]
+        if lay.mla:
+            kpe = op.kpe[r]
+            kn = _bf16_f32(op.k[r])                       # [Hkv, d_nope]
+            kp = _bf16_f32(kpe)                           # [H_pe, d_rope]
+            kp = np.broadcast_to(kp, (lay.n_kv_heads, lay.d_rope)) if kp.shape[0] == 1 else kp
+            return np.concatenate([kn, kp], axis=-1)
+        return _bf16_f32(op.k[r])                         # [Hkv, d]
+
+    for i, op in enumerate(ops):
+        if isinstance(op, SeqCreate):
+            src[n_seqs] = []
+            hist_ops[n_seqs] = set()
+            n_seqs += 1
+        elif isinstance(op, Append):
+            src[op.seq] += [(i, r) for r in range(len(op.pos))]
+            hist_ops[op.seq].add(i)
+        elif isinstance(op, AppendBatch):
+            off = 0
+            for s_, c in zip(op.seqs.tolist(), op.counts.tolist()):
+                src[s_] += [(i, off + r) for r in range(c)]
+                hist_ops[s_].add(i)
+                off += c
+        elif isinstance(op, Splice):
+            src[op.seq] += [(i, r) for r in range(int(np.sum(op.stub_lens)))]
+            last_rewrite[op.seq] = i
+        elif isinstance(op, (Repos,)):
+            last_rewrite[op.seq] = i
+        elif isinstance(op, ReposBatch):
+            for s_ in op.seqs.tolist():
+                last_rewrite[s_] = i
+        elif isinstance(op, Clone):
+            raise ValueError("focus queries: workloads with clones are not supported")
+        elif isinstance(op, Attention):
+            q = rng.standard_normal(op.q.shape, dtype=np.float32)
+            for sg in op.segments:
+                if sg.q_len == 0:
+                    continue
+                n = len(src[sg.seq])
+                hidden = np.zeros(n, bool)
+                for b, e in np.asarray(sg.mask_spans).reshape(-1, 2):
+                    hidden[b:e] = True
+                shown = np.flatnonzero(~hidden)
+                own = shown[-sg.q_len:]
+                if len(own) < sg.q_len:
+                    raise ValueError("focus queries: segment has fewer tokens than rows")
+                if any(src[sg.seq][t][0] <= last_rewrite.get(sg.seq, -1) for t in own):
+                    raise ValueError("focus queries: query tokens rewritten after their append")
+                if sg.seq not in dirs:
+                    # needle directions and tokens among the history before the query tokens
+                    u = np.zeros((n_dirs, lay.d_qk), np.float32)
+                    u[:, dims] = rng.standard_normal((n_dirs, len(dims)), dtype=np.float32)
+                    u /= np.linalg.norm(u, axis=1, keepdims=True)
+                    dirs[sg.seq] = u
+                    cand = [t for t in range(int(own[0])) if src[sg.seq][t][0] in hist_ops[sg.seq]]
+                    m = min(len(cand), n_dirs * needles_per_dir)
+                    pick = rng.choice(len(cand), size=m, replace=False) if m else []
+                    for j, c in enumerate(pick):
+                        oi, r = src[sg.seq][cand[c]]
+                        o = ops[oi]
+                        add = beta * u[j % n_dirs]
+                        if lay.mla:
+                            o.k[r] = to_bf16(_bf16_f32(o.k[r]) + add[None, :lay.d_nope])
+                        else:
+                            o.k[r] = to_bf16(_bf16_f32(o.k[r]) + add[None, :])
+                u = dirs[sg.seq]
+                for li, t in enumerate(own):
+                    row = sg.q_begin + li
+                    k_own = key_row(sg.seq, int(t))
+                    k_next = key_row(sg.seq, int(t) + 1) if int(t) + 1 < n else None
+                    for h in range(lay.n_q_heads):
+                        g = h // G
+                        sel = (li + h) % 4
+                        if sel == 0:
+                            tgt = k_own[g]
+                        elif sel == 1 and k_next is not None:
+                            tgt = k_next[g]
+                        elif sel == 2:
+                            tgt = u[(li // 4 + h) % n_dirs]
+                        else:
+                            continue
+                        q[row, h] += FOCUS_GAIN * tgt / max(float(np.linalg.norm(tgt)), 1e-6)
+            ops[i] = Attention(to_bf16(q), op.segments, op.scale)
+    return out
 
 
 CONFIGS = {
