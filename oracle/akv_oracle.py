@@ -116,6 +116,14 @@ def rotate(x: np.ndarray, delta: np.ndarray, inv_freq: np.ndarray, pairing: int)
     return out
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp64 values to bfloat16 precision (8 significant bits, the
+    exponent range of fp32), to nearest with ties to even: x = m 2^e with
+    0.5 <= |m| < 1, and m 2^8 is rounded to an integer, half to even."""
+    m, e = np.frexp(np.asarray(x, np.float64))
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
 # ---------------------------------------------------------------------------
 # pool
 # ---------------------------------------------------------------------------
@@ -143,13 +151,22 @@ class Pool:
 
     Storage mirrors a paged layout: the rotated key part `kr[page, h, off, d_rope]`
     (all of K for GQA; K_pe for MLA, with one head when K_pe is shared),
-    `kn[page, h, off, d_nope]` (MLA only) and `v[page, h, off, d_v]`."""
+    `kn[page, h, off, d_nope]` (MLA only) and `v[page, h, off, d_v]`.
+
+    key_store: "fp64" keeps a rotated key exactly (the method's own values);
+    "bf16" stores each key a repos, splice or clone rotates as its bfloat16
+    rounding, once per call, as a pool held in bf16 does (the benchmark spec: the
+    paged pool is bf16; [Leyline] Limitations: the rotation is done in
+    higher precision and stored)."""
 
     def __init__(self, layout, page_order: Optional[Sequence[int]] = None,
                  keep_log: bool = False, compact_threshold: float = DEFAULT_COMPACT_THRESHOLD,
-                 inv_freq: Optional[np.ndarray] = None):
+                 inv_freq: Optional[np.ndarray] = None, key_store: str = "fp64"):
         L = layout
         self.L = L
+        if key_store not in ("fp64", "bf16"):
+            raise EInval("key_store must be fp64 or bf16")
+        self.key_store = key_store
         S, P = L.page_size, L.num_pages
         self.S = S
         self.kr = np.zeros((P, L.n_rope_heads, S, L.d_rope))
@@ -438,8 +455,11 @@ class Pool:
         S = self.S
         pg, off = q.slot[tokens] // S, q.slot[tokens] % S
         cur = self.kr[pg, :, off, :]                        # [m, Hr, d_rope]
-        self.kr[pg, :, off, :] = rotate(cur, np.broadcast_to(delta[:, None], cur.shape[:2]),
-                                        self.inv_freq, self.L.pairing)
+        self.kr[pg, :, off, :] = self._store(rotate(cur, np.broadcast_to(delta[:, None], cur.shape[:2]),
+                                                    self.inv_freq, self.L.pairing))
+
+    def _store(self, k: np.ndarray) -> np.ndarray:
+        return round_bf16(k) if self.key_store == "bf16" else k
 
     def repos(self, s: int, spans, deltas) -> None:
         q = self._seq(s)
@@ -472,7 +492,7 @@ class Pool:
         S = self.S
         pg, off = qs.slot[t] // S, qs.slot[t] % S
         kr = self.kr[pg, :, off, :]
-        kr = rotate(kr, np.full(kr.shape[:2], float(delta)), self.inv_freq, self.L.pairing)
+        kr = self._store(rotate(kr, np.full(kr.shape[:2], float(delta)), self.inv_freq, self.L.pairing))
         v = self.v[pg, :, off, :].copy()
         if self.L.mla:
             self.append(dst, newpos, self.kn[pg, :, off, :].copy(), kr, v)

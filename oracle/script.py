@@ -81,8 +81,9 @@ def segment_lists(pool: Pool, segments):
 
 
 def run_workload(wl: W.Workload, keep_log: bool = False, attention: bool = True,
-        sample_rows: Optional[Dict[int, np.ndarray]] = None, stop_before_attention: bool = False) -> OracleRun:
-    pool = Pool(wl.layout, wl.page_order, keep_log=keep_log)
+        sample_rows: Optional[Dict[int, np.ndarray]] = None, stop_before_attention: bool = False,
+        key_store: str = "fp64") -> OracleRun:
+    pool = Pool(wl.layout, wl.page_order, keep_log=keep_log, key_store=key_store)
     res = OracleRun(pool)
     for op in wl.ops:
         if isinstance(op, W.Attention):

@@ -133,6 +133,83 @@ def test_repos_sequential_equals_summed_and_skips_dropped():
 
 
 # ---------------------------------------------------------------------------
+# bf16 storage of rotated keys (the pool is bf16): round to nearest, ties to even
+# ---------------------------------------------------------------------------
+def _bf16_by_bits(x):
+    """Nearest bfloat16 by enumeration: the bf16 numbers are the float32
+    numbers whose low 16 bits are zero; take the three such numbers around
+    float32(x) (its upper 16 bits, one step below, one above), keep the
+    nearest to x in fp64, and on a tie the one whose last kept bit is 0."""
+    x = np.asarray(x, np.float64)
+    hi = (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.int64)
+    best = np.full(x.shape, np.nan)
+    bd = np.full(x.shape, np.inf)
+    bodd = np.ones(x.shape, bool)
+    for k in (-1, 0, 1):
+        c = ((hi + k) & 0xFFFF).astype(np.uint32) << 16
+        v = c.view(np.float32).astype(np.float64)
+        d = np.abs(v - x)
+        odd = ((hi + k) & 1).astype(bool)
+        take = (d < bd) | ((d == bd) & bodd & ~odd)
+        best = np.where(take, v, best)
+        bd = np.where(take, d, bd)
+        bodd = np.where(take, odd, bodd)
+    return best
+
+
+def test_round_bf16_nearest_even():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))
+    np.testing.assert_array_equal(AO.round_bf16(x), _bf16_by_bits(x))
+    # exact ties go to the even neighbour
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), (1.5 + 2.0 ** -8) * 2.0 ** -9])
+    np.testing.assert_array_equal(AO.round_bf16(ties), [1.0, 1 + 2.0 ** -6, -1.0, 1.5 * 2.0 ** -9])
+    np.testing.assert_array_equal(AO.round_bf16(np.array([0.0, -0.0, 1.0, 2.0 ** -100])), [0.0, 0.0, 1.0, 2.0 ** -100])
+
+
+def test_bf16_key_store_rounds_each_call():
+    """A bf16 pool stores each rotated key as the bf16 rounding of its exact
+    rotation, once per repos or clone call, from the key as stored before the
+    call; values and unrotated keys are kept as appended."""
+    rng = np.random.default_rng(13)
+    d, n, base = 32, 120, 10000.0
+    lay = _lay(d_rope=d, d_v=8, n_q_heads=2, n_kv_heads=1, rope_theta=base, num_pages=40)
+    raw = AO.round_bf16(rng.standard_normal((n, 1, d)))
+    v = AO.round_bf16(rng.standard_normal((n, 1, 8)))
+    m = np.arange(n) + 500
+    pool = AO.Pool(lay, key_store="bf16")
+    s = pool.seq_create()
+    pool.append(s, m, raw, None, v)
+    pool.repos(s, [[20, 120]], [-333])
+    pool.repos(s, [[60, 120]], [71])
+    t = pool.seqs[s]
+    d1 = np.zeros(n); d1[20:] = -333
+    d2 = np.zeros(n); d2[60:] = 71
+    step1 = np.where((d1 != 0)[:, None, None], _bf16_by_bits(_rope_by_matrix(raw, d1[:, None], base, 0)), raw)
+    want = np.where((d2 != 0)[:, None, None], _bf16_by_bits(_rope_by_matrix(step1, d2[:, None], base, 0)), step1)
+    got = pool.kr[t.slot // 16, :, t.slot % 16, :]
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12 * np.abs(want).max())
+    np.testing.assert_array_equal(got[:20], raw[:20])
+    np.testing.assert_array_equal(pool.v[t.slot // 16, :, t.slot % 16, :], v)
+    # clone: one rounding of R(delta) applied to the stored source key
+    s2 = pool.seq_create()
+    pool.clone(s, 0, n, s2, 1000)
+    t2 = pool.seqs[s2]
+    np.testing.assert_allclose(pool.kr[t2.slot // 16, :, t2.slot % 16, :],
+                               _bf16_by_bits(_rope_by_matrix(want, np.full((n, 1), 1000.0), base, 0)),
+                               rtol=0, atol=1e-12 * np.abs(want).max())
+    # the exact store keeps the exact rotation
+    exact = AO.Pool(lay)
+    exact.seq_create()
+    exact.append(0, m, raw, None, v)
+    exact.repos(0, [[20, 120]], [-333])
+    te = exact.seqs[0]
+    np.testing.assert_allclose(exact.kr[te.slot // 16, :, te.slot % 16, :],
+                               np.where((d1 != 0)[:, None, None], _rope_by_matrix(raw, d1[:, None], base, 0), raw),
+                               rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # positional versions ("Cache Engineering for Agents", section 3, Cache
 # Management: re-use by key rotation; the retrigger match rule)
 # ---------------------------------------------------------------------------

@@ -824,13 +824,22 @@ def query_variant(wl: Workload, mode: str, seed: int = 0, n_dirs: int = 4, needl
          segment's mask of later tokens),
       2  a needle direction u: n_dirs directions per sequence, each added
          (times sqrt(d_qk)) to the keys of needles_per_dir random history
-         tokens, some of which later drops or masks hide,
+         tokens, some of which later drops or masks hide (GQA: only tokens
+         no repos moves, see below),
       3  nothing;
     the target's unit vector times FOCUS_GAIN is added to the row, so the
     target's score stands about 20 above the others and a handful of keys
     carry almost all of the softmax mass.  Values are clipped to
     |v| <= FOCUS_V_CLIP so an output dominated by one key stays within the
     range where bf16 output rounding leaves room under a 2e-2 error bar.
+
+    The targets are keys whose stored bits are exact inputs on every side:
+    own and next tokens are appended after the history's repos, and GQA
+    needles sit on tokens no repos span covers (MLA needles live in K_nope,
+    which no repos touches).  A repositioned key is stored rounded to bf16
+    (its 1e-2 relative bar), and a softmax this sharp would turn that
+    rounding into output differences of a few 1e-2 between two competing
+    keys; the stress queries cover repositioned keys with a soft softmax.
 
     Own tokens of a segment are its sequence's last q_len appended tokens
     outside its mask spans (the generators append the query tokens last);
@@ -842,7 +851,7 @@ def query_variant(wl: Workload, mode: str, seed: int = 0, n_dirs: int = 4, needl
     rng = _rng(1_000_003 + seed)
     lay = wl.layout
     ops = list(wl.ops)
-    out = Workload(f"{wl.name}_{mode}", lay, wl.page_order, ops, dict(wl.notes))
+    out = Workload(f"{wl.name}_{mode}", lay, wl.page_order, ops, dict(wl.notes, query_variant=mode))
     if mode == "stress":
         for i, op in enumerate(ops):
             if isinstance(op, Attention):
@@ -850,6 +859,21 @@ def query_variant(wl: Workload, mode: str, seed: int = 0, n_dirs: int = 4, needl
         return out
 
     G = lay.n_q_heads // lay.n_kv_heads
+    moved = {}   # seq -> logical spans any repos of the script covers
+    for op in ops:
+        if isinstance(op, Repos):
+            moved.setdefault(op.seq, []).extend(np.asarray(op.spans).reshape(-1, 2).tolist())
+        elif isinstance(op, ReposBatch):
+            for s_, sp, _ in op.entries():
+                moved.setdefault(s_, []).extend(np.asarray(sp).reshape(-1, 2).tolist())
+
+    def unmoved(seq, n):
+        keep = np.ones(n, bool)
+        if not lay.mla:
+            for b, e in moved.get(seq, []):
+                keep[b:e] = False
+        return keep
+
     # copies of every op array this variant changes
     for i, op in enumerate(ops):
         if isinstance(op, (Append, AppendBatch, Splice)):
@@ -923,7 +947,8 @@ def query_variant(wl: Workload, mode: str, seed: int = 0, n_dirs: int = 4, needl
                     u[:, dims] = rng.standard_normal((n_dirs, len(dims)), dtype=np.float32)
                     u /= np.linalg.norm(u, axis=1, keepdims=True)
                     dirs[sg.seq] = u
-                    cand = [t for t in range(int(own[0])) if src[sg.seq][t][0] in hist_ops[sg.seq]]
+                    keep = unmoved(sg.seq, n)
+                    cand = [t for t in range(int(own[0])) if keep[t] and src[sg.seq][t][0] in hist_ops[sg.seq]]
                     m = min(len(cand), n_dirs * needles_per_dir)
                     pick = rng.choice(len(cand), size=m, replace=False) if m else []
                     for j, c in enumerate(pick):
