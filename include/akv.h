@@ -303,6 +303,27 @@ akv_status akv_segment_attention(akv_pool* pool, const void* Q, int32_t n_q_toke
                                  const akv_extent* page_lists, int32_t n_ext, float scale,
                                  void* out);
 
+/* akv_segment_attention for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same validation, plan, kernels and results (bit for bit),
+ * but the call's work tables, expanded slot list and split-KV partials live
+ * in a static device workspace of the library (128 MiB per GPU, held from
+ * the library's first use on that GPU until the process ends) instead of
+ * the pool's scratch buffer.  The call allocates nothing: no hipMalloc,
+ * hipHostMalloc or hipFree (the tables are copied from host memory the pool
+ * already holds, on the pool's stream, after the kernels of earlier calls).
+ * Every call on one GPU shares that GPU's workspace, which keeps the last
+ * call's contents (nothing in it needs clearing): calls on one stream are
+ * ordered, but calls that overlap on one GPU (other streams, other pools,
+ * other threads) race.  Errors: those of akv_segment_attention, and
+ * AKV_ENOMEM when the call needs more than 128 MiB of workspace (about 4 B per
+ * list entry + 16 B per extent + 24 B per work item + split partials of
+ * 4 B * (d_v + 2) per row and split), before anything is enqueued. */
+akv_status akv_segment_attention_static(akv_pool* pool, const void* Q, int32_t n_q_tokens,
+                                        const akv_segment* segs, int32_t n_segs,
+                                        const akv_extent* page_lists, int32_t n_ext, float scale,
+                                        void* out);
+
 /* segment-batch attention over sequences' own lists: segment i reads the
  * visible list of sequence segs[i].seq minus the spans masks[mask_begin ..
  * mask_begin+mask_len) (logical-index spans, hidden from this segment only),

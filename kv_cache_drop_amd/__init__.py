@@ -72,6 +72,7 @@ SYMBOLS = {
     "akv_seq_attention": [_P, _P, _I, _IP, _I, _IP, _I, ctypes.c_float, _P],
     "akv_seq_visible": [_P, _I, _IP, _I, _IP, _I, _IP],
     "akv_segment_attention": [_P, _P, _I, _IP, _I, _IP, _I, ctypes.c_float, _P],
+    "akv_segment_attention_static": [_P, _P, _I, _IP, _I, _IP, _I, ctypes.c_float, _P],
     "akv_seq_tokens": [_P, _I, _I, _I, _IP, _IP, ctypes.POINTER(ctypes.c_uint8)],
     "akv_seq_info": [_P, _I, _IP, _IP, ctypes.POINTER(ctypes.c_double)],
     "akv_pool_queues": [_P, _IP, _I, _IP, _IP, _I, _IP],
@@ -411,6 +412,23 @@ class Pool:
             raise ValueError("out must be bf16 [Nq, n_q_heads, d_v]")
         _check(lib().akv_segment_attention(self._h, _dptr(q), q.shape[0], _ptr(sg), len(sg), _ptr(ex),
                                            len(ex), float(scale), _dptr(out)))
+        return out
+
+    def segment_attention_static(self, q, segments, page_lists, out, scale: float = 0.0):
+        """akv_segment_attention_static: segment_attention with the call's
+        tables in the library's static device workspace (no allocation); out
+        is the caller's bf16 tensor [Nq, Hq, d_v]."""
+        import torch
+        sg = _i32(segments).reshape(-1, 4)
+        ex = _i32(page_lists).reshape(-1, 3)
+        L = self.layout
+        if q.dim() != 3 or q.shape[1] != L["n_q_heads"] or q.shape[2] != L["d_nope"] + L["d_rope"] \
+                or q.dtype != torch.bfloat16:
+            raise ValueError("q must be bf16 [Nq, n_q_heads, d_nope + d_rope]")
+        if tuple(out.shape) != (q.shape[0], L["n_q_heads"], L["d_v"]) or out.dtype != torch.bfloat16:
+            raise ValueError("out must be bf16 [Nq, n_q_heads, d_v]")
+        _check(lib().akv_segment_attention_static(self._h, _dptr(q), q.shape[0], _ptr(sg), len(sg), _ptr(ex),
+                                                  len(ex), float(scale), _dptr(out)))
         return out
 
     def seq_attention(self, q, segments, scale: float = 0.0, out=None):

@@ -123,6 +123,12 @@ hipError_t launch_expand_didx(hipStream_t st, const Extent* ex, const int32_t* e
 
 bool attn_dims_supported(int d_nope, int d_rope, int d_v);
 
+// Static device workspace of the no-allocation attention entry point: its
+// size, and its device address on the current device (looked up once per
+// device with hipGetSymbolAddress).
+constexpr size_t STATIC_WORKSPACE_BYTES = (size_t)128 << 20;
+hipError_t static_workspace(void** ptr);
+
 // Text returned by akv_last_error (thread-local; host code of the library).
 void set_error(const char* msg);
 

@@ -13,6 +13,7 @@
 //   k_combine      split-KV merge of (m, l, O) partials
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "akv_internal.h"
@@ -998,6 +999,35 @@ __global__ __launch_bounds__(256) void k_combine(AttnArgs a, const CombItem* __r
       op[c] = __builtin_bit_cast(uint16_t, bv);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Static workspace for callers that cannot allocate (akv_segment_attention_static):
+// a file-scope device array of fixed size.  Each GPU holds its own copy from
+// the moment the library's code object is loaded on it until the process
+// ends.  On the host the array's name is only a stand-in for the symbol, so
+// its device address is looked up once per device (with that device
+// current) and every kernel argument, copy or fill uses that address.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[STATIC_WORKSPACE_BYTES];
+
+hipError_t static_workspace(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 bool attn_dims_supported(int d_nope, int d_rope, int d_v) {

@@ -134,6 +134,7 @@ struct AttnPlan {
 };
 
 struct AttnHostBufs {
+  std::vector<char> static_up;   // tables of a static-workspace call, before their copy
   std::vector<akv_extent> lists, masked;
   std::vector<int32_t> lags, mlag, ex_off, ex_didx;
   std::vector<akv::Extent> ex_used;
@@ -2128,7 +2129,7 @@ akv_status akv_seq_visible(akv_pool* p, int32_t s, const akv_span* mask, int32_t
 static bool decode_launch(const akv_pool* p, const int64_t* q_len, int32_t n, int32_t stride);
 static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens, const akv_segment* segs,
                                  int32_t n_segs, const akv_extent* page_lists, int32_t n_ext,
-                                 const int32_t* ext_lag, float scale, void* out);
+                                 const int32_t* ext_lag, float scale, void* out, bool ws_static = false);
 
 akv_status akv_seq_attention(akv_pool* p, const void* Q, int32_t n_q_tokens, const akv_seq_segment* segs,
                              int32_t n_segs, const akv_span* masks, int32_t n_masks, float scale, void* out) {
@@ -2281,7 +2282,7 @@ static akv_status attn_validate(akv_pool* p, int32_t n_q_tokens, const akv_segme
 
 static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens, const akv_segment* segs,
                                  int32_t n_segs, const akv_extent* page_lists, int32_t n_ext,
-                                 const int32_t* ext_lag, float scale, void* out) {
+                                 const int32_t* ext_lag, float scale, void* out, bool ws_static) {
   try {
     if (!p) return fail(AKV_EINVAL, "NULL pool");
     if (!p->device) return fail(AKV_ESTATE, "attention needs a device pool");
@@ -2353,34 +2354,73 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
                         (ex_off.size() + ex_didx.size()) * 4 + keys4 * (fused ? 2 : 1) +
                         rot_deltas.size() * (size_t)L.d_rope * 4 + (size_t)plan.part_rows * (L.d_v + 2) * 4 +
                         12 * 256;
-    ScratchCursor sc(p, need);
     static const std::vector<float> no_rows;
     const std::vector<float>& rot_rows = fused ? rot_table_rows(p, rot_deltas.data(), rot_deltas.size()) : no_rows;
+    const std::pair<const void*, size_t> up_parts[7] = {
+        {plan.segs.data(), plan.segs.size() * sizeof(akv::AttnSeg)},
+        {plan.items.data(), plan.items.size() * sizeof(akv::AttnItem)},
+        {plan.comb.data(), plan.comb.size() * sizeof(akv::CombItem)},
+        {in_order ? (const void*)page_lists : (const void*)ex_used.data(), ex_off.size() * sizeof(akv::Extent)},
+        {ex_off.data(), ex_off.size() * 4},
+        {ex_didx.data(), ex_didx.size() * 4},
+        {rot_rows.data(), rot_rows.size() * 4}};
     void* dv[7];
-    akv_status st = upload_arrays(p, sc,
-                                  {{plan.segs.data(), plan.segs.size() * sizeof(akv::AttnSeg)},
-                                   {plan.items.data(), plan.items.size() * sizeof(akv::AttnItem)},
-                                   {plan.comb.data(), plan.comb.size() * sizeof(akv::CombItem)},
-                                   {in_order ? (const void*)page_lists : (const void*)ex_used.data(),
-                                    ex_off.size() * sizeof(akv::Extent)},
-                                   {ex_off.data(), ex_off.size() * 4},
-                                   {ex_didx.data(), ex_didx.size() * 4},
-                                   {rot_rows.data(), rot_rows.size() * 4}},
-                                  dv);
-    if (st != AKV_OK) return st;
-    void *dsegs = dv[0], *ditems = dv[1], *dcomb = plan.comb.empty() ? nullptr : dv[2], *dex = dv[3],
-         *doff = dv[4];
-    int32_t* dslots = (int32_t*)sc.take((size_t)std::max<int64_t>(total, 1) * 4);
-    int32_t* dkey_didx = fused ? (int32_t*)sc.take((size_t)std::max<int64_t>(total, 1) * 4) : nullptr;
-    const float* drot = fused ? (const float*)dv[6] : nullptr;
+    int32_t* dslots = nullptr;
+    int32_t* dkey_didx = nullptr;
     float* part_o = nullptr;
     float* part_ml = nullptr;
-    if (plan.part_rows > 0) {
-      part_o = (float*)sc.take((size_t)plan.part_rows * L.d_v * 4);
-      part_ml = (float*)sc.take((size_t)plan.part_rows * 2 * 4);
+    if (ws_static) {
+      // The call's tables, slot list and partials in the library's static
+      // device workspace: one copy of the tables on the pool stream (after
+      // the kernels of earlier calls, which may still read the workspace),
+      // no allocation of any kind.
+      char* base = nullptr;
+      hipError_t we = akv::static_workspace((void**)&base);
+      if (we != hipSuccess) return hip_fail(we, "static workspace address (hipGetSymbolAddress)");
+      size_t up = 0;
+      for (const auto& pr : up_parts) up += align_up(std::max<size_t>(pr.second, 1), 256);
+      const size_t slots_at = up, didx_at = slots_at + align_up(keys4, 256);
+      const size_t po_at = didx_at + (fused ? align_up(keys4, 256) : 0);
+      const size_t pml_at = po_at + align_up((size_t)plan.part_rows * L.d_v * 4, 256);
+      const size_t end = pml_at + align_up((size_t)plan.part_rows * 2 * 4, 256);
+      if (end > akv::STATIC_WORKSPACE_BYTES)
+        return fail(AKV_ENOMEM, "this call needs %zu bytes of workspace; the static workspace holds %zu",
+                    end, akv::STATIC_WORKSPACE_BYTES);
+      std::vector<char>& hst = p->hb.static_up;
+      hst.assign(up, 0);
+      size_t off = 0;
+      int i = 0;
+      for (const auto& pr : up_parts) {
+        if (pr.second) std::memcpy(hst.data() + off, pr.first, pr.second);
+        dv[i++] = base + off;
+        off += align_up(std::max<size_t>(pr.second, 1), 256);
+      }
+      // pageable source: the runtime has read it when the call returns
+      we = hipMemcpyAsync(base, hst.data(), up, hipMemcpyHostToDevice, p->stream);
+      if (we != hipSuccess) return hip_fail(we, "hipMemcpyAsync(static workspace)");
+      dslots = (int32_t*)(base + slots_at);
+      if (fused) dkey_didx = (int32_t*)(base + didx_at);
+      if (plan.part_rows > 0) {
+        part_o = (float*)(base + po_at);
+        part_ml = (float*)(base + pml_at);
+      }
+    } else {
+      ScratchCursor sc(p, need);
+      akv_status st = upload_arrays(p, sc, {up_parts[0], up_parts[1], up_parts[2], up_parts[3], up_parts[4],
+                                            up_parts[5], up_parts[6]}, dv);
+      if (st != AKV_OK) return st;
+      dslots = (int32_t*)sc.take((size_t)std::max<int64_t>(total, 1) * 4);
+      dkey_didx = fused ? (int32_t*)sc.take((size_t)std::max<int64_t>(total, 1) * 4) : nullptr;
+      if (plan.part_rows > 0) {
+        part_o = (float*)sc.take((size_t)plan.part_rows * L.d_v * 4);
+        part_ml = (float*)sc.take((size_t)plan.part_rows * 2 * 4);
+      }
+      if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small for this call (%zu bytes per call)",
+                                   p->scratch_bytes - p->scratch_base);
     }
-    if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small for this call (%zu bytes per call)",
-                                 p->scratch_bytes - p->scratch_base);
+    void *dsegs = dv[0], *ditems = dv[1], *dcomb = plan.comb.empty() ? nullptr : dv[2], *dex = dv[3],
+         *doff = dv[4];
+    const float* drot = fused ? (const float*)dv[6] : nullptr;
 
     hipError_t e;
     {
@@ -2443,6 +2483,12 @@ akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens,
                                  int32_t n_segs, const akv_extent* page_lists, int32_t n_ext, float scale,
                                  void* out) {
   return attention_impl(p, Q, n_q_tokens, segs, n_segs, page_lists, n_ext, nullptr, scale, out);
+}
+
+akv_status akv_segment_attention_static(akv_pool* p, const void* Q, int32_t n_q_tokens, const akv_segment* segs,
+                                        int32_t n_segs, const akv_extent* page_lists, int32_t n_ext, float scale,
+                                        void* out) {
+  return attention_impl(p, Q, n_q_tokens, segs, n_segs, page_lists, n_ext, nullptr, scale, out, true);
 }
 
 akv_status akv_attention_plan(akv_pool* p, int32_t n_q_tokens, const akv_segment* segs, int32_t n_segs,
