@@ -70,7 +70,7 @@ def attention_kernel_name(layout, max_rows=None) -> str:
             max_rows <= 16:
         return "k_decode_attn"
     if layout.d_nope == 0 and layout.d_rope == 128 and layout.d_v == 128:
-        return "k_seg_attn_dl<128,128,0,8,1,4>"
+        return "k_seg_attn_dl<128,128,0,8,1,4,false>"
     return "k_seg_attn"
 
 
@@ -249,9 +249,15 @@ def run_config(args) -> dict:
     import device_script as D
     import workloads as W
 
+    def deferred(wl):
+        for op in wl.ops:
+            if isinstance(op, W.Repos):
+                op.deferred = True
+        return wl
+
     gens = {"c1": lambda s: W.c1_tiny(s, "canonical"), "c3": W.c3_mla, "c4": W.c4_batched, "c5": W.c5_128k,
             "decode": W.decode_batch, "decode_fused": lambda s: W.decode_batch(s, deferred=True),
-            "retrigger": W.retrigger}
+            "retrigger": W.retrigger, "c2_fused": lambda s: deferred(W.c2_64k(s))}
     wl = gens[args.config](args.seed)
     L = wl.layout
     ops = list(wl.ops)
@@ -286,6 +292,8 @@ def run_config(args) -> dict:
     first_walls = []
     for rep in range(args.warmup + args.steps):
         pool = D.make_pool(wl)
+        if args.config == "c2_fused":
+            pool.fused_rotation("always")     # keys turned in the attention kernel, not in place
         keep = []
         for op in ops[:i0]:
             D.apply_op(pool, op, keep)
@@ -377,8 +385,9 @@ def run_config(args) -> dict:
                     clone_bytes += 2 * row_bytes * int((dr == 0).sum())
             grp = L.n_q_heads // L.n_kv_heads
             kern = attention_kernel_name(L, max(sg.q_len * grp for op in lists for sg in op.segments))
-            if any(isinstance(o, W.Repos) and o.deferred for o in ops) and kern == "k_decode_attn":
-                kern = "k_decode_attn<rotating>"
+            if any(isinstance(o, W.Repos) and o.deferred for o in ops):
+                kern = "k_decode_attn<rotating>" if kern == "k_decode_attn" else (
+                    "k_seg_attn_dl<128,128,0,8,1,4,rotating>" if kern.startswith("k_seg_attn_dl") else kern)
         pool.close()
         del pool, keep
     ms_step = float(np.median(walls)) * 1e3
@@ -451,6 +460,8 @@ CONFIG_NAMES = {
                  "(512-token preamble, the 64K trace, older tools dropped, survivors repositioned) and request B "
                  "(the same trace after a preamble of another length) cloned from A's state with keys turned by "
                  "the offset change; 512 queries each in one launch",
+    "c2_fused": "the 64K step (Llama-3.1-8B-shaped layer, 32 q / 8 kv heads, head_dim 128, page 16) with its repos "
+                "deferred: no rotation pass; the attention kernel turns each landed key tile in LDS",
     "decode_fused": "the decode step of 48 requests of 2K-16K tokens whose survivors' repos was deferred: the "
                     "keys stay at their old positions and the decode kernel turns them as it reads them",
     "decode": "48 requests of 2K-16K tokens on the 64K layer shape (32 q / 8 kv heads, head_dim 128, page 16), "
@@ -461,7 +472,8 @@ CONFIG_NAMES = {
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "decode", "decode_fused", "retrigger"],
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2_fused", "c3", "c4", "c5", "decode", "decode_fused",
+                                                       "retrigger"],
                     help="c2 (default) is the headline 64K step; the others print one record each")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)

@@ -213,13 +213,26 @@ akv_status akv_repos_batch(akv_pool* pool, int32_t n_seqs, const int32_t* seqs, 
  * thumb 2: keys stay where they are and are turned where they are read):
  * the same validation, positions and errors as akv_repos, but no key is
  * rewritten; each token records the rotation its stored key still owes.
- * akv_seq_attention applies owed rotations inside the decode kernel (with
- * the rotation table and fp32 formula of akv_repos, so the results equal
- * repos-then-attention bit for bit) and rotates the keys in place first for
- * other launches; akv_segment_attention reads keys as stored.  Later repos
+ * akv_seq_attention applies owed rotations where the kernels read the keys:
+ * the decode kernel in registers, the 128-dim GQA prefill kernel in LDS
+ * (each landed key tile turned once per block), both with the rotation table
+ * and fp32 formula of akv_repos, so the results equal repos-then-attention
+ * bit for bit; other launches rotate the keys in place first (see
+ * akv_fused_rotation).  akv_segment_attention reads keys as stored.  Later repos
  * calls, compaction, splices and clones keep each token's debt. */
 akv_status akv_repos_deferred(akv_pool* pool, int32_t seq, const akv_span* spans, const int32_t* delta,
                               int32_t n_spans);
+/* Where akv_seq_attention applies owed rotations.  AKV_FUSE_AUTO (the
+ * default): decode launches turn keys in the kernel; a prefill launch on the
+ * 128-dim GQA layout does so when it turns each owed key at most once per kv
+ * head (every segment one row tile of 256 packed rows, every sequence in one
+ * segment), and otherwise rotates the keys in place first (a prefill block
+ * turns every tile it reads, so keys read by many row tiles are cheaper to
+ * rotate once in HBM).  AKV_FUSE_ALWAYS: every launch whose kernel can turn
+ * keys does.  AKV_FUSE_NEVER: keys are always rotated in place first.
+ * Results are the same bits in every mode.  Errors: AKV_EINVAL. */
+enum { AKV_FUSE_AUTO = 0, AKV_FUSE_ALWAYS = 1, AKV_FUSE_NEVER = 2 };
+akv_status akv_fused_rotation(akv_pool* pool, int32_t mode);
 /* Rotate the sequence's visible keys by what they owe, in place (one
  * launch), as akv_repos would have; the debt is then 0.  Errors: AKV_EINVAL,
  * AKV_ESTATE, AKV_ENOMEM (scratch). */

@@ -58,6 +58,7 @@ SYMBOLS = {
     "akv_drop": [_P, _I, _IP, _I],
     "akv_compact": [_P, _I, _I],
     "akv_compaction_mode": [_P, _I],
+    "akv_fused_rotation": [_P, _I],
     "akv_compact_pending": [_P, ctypes.c_int64, _I, _IP, _IP],
     "akv_compact_queue": [_P, _IP, _I, _IP],
     "akv_repos": [_P, _I, _IP, _IP, _I],
@@ -250,6 +251,10 @@ class Pool:
 
     def compact(self, seq: int, force: bool = True) -> None:
         _check(lib().akv_compact(self._h, seq, int(bool(force))))
+
+    def fused_rotation(self, mode: str) -> None:
+        """Where akv_seq_attention applies owed rotations: "auto", "always" or "never"."""
+        _check(lib().akv_fused_rotation(self._h, {"auto": 0, "always": 1, "never": 2}[mode]))
 
     def compaction_mode(self, deferred: bool) -> None:
         """Deferred: drops and splices queue fragmented sequences instead of

@@ -543,7 +543,24 @@ struct LdsPart {
   }
 };
 
-template <int DQK, int DV, int DNOPE, int NW, int QB, int NST>
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// Eight floats from a wave-uniform address through the scalar data cache
+// (a load: counted by lgkmcnt, so waiting for it never drains the tile DMAs
+// that vmcnt counts).
+__device__ __forceinline__ f32x8 scalar_load8(const float* p) {
+  return *(const __attribute__((address_space(4))) f32x8*)(size_t)p;
+}
+
+// ROT: keys may owe a rotation (deferred repos, [AKV-blog] section 4 and rule
+// of thumb 2: turn the key where it is read).  Every list entry carries the
+// row of the cos / sin table that turns its stored key to its position, or
+// -1.  Each landed K tile is turned once, in LDS, by the whole block before
+// any wave reads it: wave w takes rotation pairs 8w .. 8w + 7 of every key
+// (lane = key), with the table row read through the scalar cache, one
+// distinct row at a time, and the formula of the in-place repos, so the
+// scores equal those of keys rotated in place bit for bit.
+template <int DQK, int DV, int DNOPE, int NW, int QB, int NST, bool ROT>
 __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
   constexpr int RB = 32 * QB * NW;
   constexpr int KT = ATTN_KTILE;
@@ -559,16 +576,21 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
   static_assert(DNOPE == 0 && DQK == DV, "one K part with V's row size");
   static_assert(KT == 64 && 64 % CH == 0 && CH % NW == 0, "tile");
   static_assert(NST == 4, "the unrolled pipeline below is written for four stages");
+  static_assert(!ROT || (NW == 8 && DQK == 128), "the in-LDS rotation maps wave w to pairs 8w .. 8w + 7");
+  constexpr int WAIT_LDS = 0xF | (0x3 << 14) | (0x7 << 4);                        // lgkmcnt(0) only
 
   __shared__ __attribute__((aligned(16))) unsigned char st0[SSTAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st1[SSTAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st2[SSTAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st3[SSTAGE];
   // per-wave slot ring: entry e holds the 64 slots of tile t, t % 4 == e
-  __shared__ __attribute__((aligned(16))) int32_t sr0[NW * 64];
-  __shared__ __attribute__((aligned(16))) int32_t sr1[NW * 64];
-  __shared__ __attribute__((aligned(16))) int32_t sr2[NW * 64];
-  __shared__ __attribute__((aligned(16))) int32_t sr3[NW * 64];
+  // (ROT: then the tile's 64 rotation-table rows, in the same array, so the
+  // compiler's wait tracking still sees eight LDS targets of the DMA)
+  constexpr int RING = (ROT ? 2 : 1) * NW * 64;
+  __shared__ __attribute__((aligned(16))) int32_t sr0[RING];
+  __shared__ __attribute__((aligned(16))) int32_t sr1[RING];
+  __shared__ __attribute__((aligned(16))) int32_t sr2[RING];
+  __shared__ __attribute__((aligned(16))) int32_t sr3[RING];
 
   const AttnItem it = a.items[blockIdx.x];
   if (it.seg < 0) return;
@@ -618,9 +640,70 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
     int32_t* r = e == 0 ? sr0 : (e == 1 ? sr1 : (e == 2 ? sr2 : sr3));
     return (int32_t AKV_LDS*)r + 64 * w;
   };
+  auto dring_ptr = [&](int e) __attribute__((always_inline)) -> int32_t AKV_LDS* {
+    int32_t* r = e == 0 ? sr0 : (e == 1 ? sr1 : (e == 2 ? sr2 : sr3));
+    return (int32_t AKV_LDS*)r + NW * 64 + 64 * w;
+  };
   auto slot_load = [&](int e, int t) __attribute__((always_inline)) {
-    const int32_t* src = slots + min(it.k_begin + t * KT + lane, lkv - 1);
-    __builtin_amdgcn_global_load_lds(src, (void AKV_LDS*)ring_ptr(e), 4, 0, 0);
+    const int idx = min(it.k_begin + t * KT + lane, lkv - 1);
+    __builtin_amdgcn_global_load_lds(slots + idx, (void AKV_LDS*)ring_ptr(e), 4, 0, 0);
+    if constexpr (ROT)
+      __builtin_amdgcn_global_load_lds(a.key_didx + sg.list_off + idx, (void AKV_LDS*)dring_ptr(e), 4, 0, 0);
+  };
+  // Turn the owed keys of the K tile in stage stg (di: this lane's key's
+  // table row, read from the ring before the ring entry was reloaded), then
+  // a barrier so every wave reads turned keys.  Skipped, barrier included,
+  // when no key of the tile owes a rotation (the same decision in every
+  // wave: each holds the tile's 64 rows).
+  auto rotate_tile = [&](unsigned char AKV_LDS* stg, int di) __attribute__((always_inline)) {
+    if constexpr (ROT) {
+      uint64_t todo = __ballot(di >= 0);
+      if (todo == 0) return;
+      const int c0 = a.rot_pairing == 0 ? 2 * w : w;
+      const int c1 = a.rot_pairing == 0 ? 2 * w + 1 : w + 8;
+      u32x4 AKV_LDS* p0 = (u32x4 AKV_LDS*)(stg + PA::off(lane, c0));
+      u32x4 AKV_LDS* p1 = (u32x4 AKV_LDS*)(stg + PA::off(lane, c1));
+      const u32x4 x0 = *p0, x1 = *p1;
+      u32x4 o0 = x0, o1 = x1;
+      while (todo) {
+        const int d0 = __builtin_amdgcn_readlane(di, __builtin_ctzll(todo));
+        const float* row = a.rot_table + (size_t)d0 * DQK + 8 * w;
+        const f32x8 cs = scalar_load8(row);
+        const f32x8 sn = scalar_load8(row + DQK / 2);
+        const bool mine = di == d0;
+        if (mine) {
+          if (a.rot_pairing == 0) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              o0[k] = rot_pair_word(x0[k], cs[k], sn[k]);
+              o1[k] = rot_pair_word(x1[k], cs[4 + k], sn[4 + k]);
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float xa = bf_lo(x0[k]), xb = bf_hi(x0[k]);
+              const float ya = bf_lo(x1[k]), yb = bf_hi(x1[k]);
+              o0[k] = pack_bf2(fmaf(xa, cs[2 * k], -ya * sn[2 * k]), fmaf(xb, cs[2 * k + 1], -yb * sn[2 * k + 1]));
+              o1[k] = pack_bf2(fmaf(xa, sn[2 * k], ya * cs[2 * k]), fmaf(xb, sn[2 * k + 1], yb * cs[2 * k + 1]));
+            }
+          }
+        }
+        todo &= ~__ballot(mine);
+      }
+      *p0 = o0;
+      *p1 = o1;
+      __builtin_amdgcn_s_waitcnt(WAIT_LDS);
+      __builtin_amdgcn_s_barrier();
+    }
+  };
+  auto ring_didx = [&](int e) __attribute__((always_inline)) -> int {
+    if constexpr (ROT) {
+      const int d = dring_ptr(e)[lane];
+      // read before this wave's next slot load rewrites the entry
+      __builtin_amdgcn_s_waitcnt(WAIT_LDS);
+      return d;
+    }
+    return -1;
   };
   // Row loads of one tile: this wave's blocks b = w + NW m; lane holds key
   // b + CH (lane / CH), chunk lane % CH, of both K and V.
@@ -795,11 +878,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) slot_load(t, t);
   __builtin_amdgcn_s_waitcnt(0);
+  const int di0 = ring_didx(0);
 #pragma unroll
   for (int t = 0; t < 3; ++t) issue_tile(stage_ptr(t), t);
   slot_load(0, 4);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  rotate_tile(stage_ptr(0), di0);
   // A wave whose rows all lie past the segment's last row (a short segment's
   // padding) computes nothing: it keeps its share of the tile loads and every
   // barrier, and leaves its SIMD's matrix core to the other wave there.
@@ -812,14 +897,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
   // memory fence: a workgroup fence would wait for every LDS load in flight,
   // tiles j + 2 and j + 3 included.  lgkmcnt(0) makes this wave's reads of
   // tile j - 1's stage complete before any wave reloads it.
-  constexpr int WAITV = NIW + 1;
+  constexpr int WAITV = NIW + (ROT ? 2 : 1);
+  // s_waitcnt operands (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+  // 6:4, lgkmcnt 11:8), given through the builtin so the compiler's own wait
+  // tracking knows them and adds no stricter wait of its own
+  constexpr int WAIT_SYNC = (WAITV & 0xF) | ((WAITV >> 4) << 14) | (0x7 << 4);   // vmcnt(WAITV) lgkmcnt(0)
   static_assert(WAITV <= 15, "vmcnt");
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
   auto sync = [&]() __attribute__((always_inline)) {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(WAITV) : "memory");
+    __builtin_amdgcn_s_waitcnt(WAIT_SYNC);
+    __builtin_amdgcn_s_barrier();
   };
   // Tiles j < jm need no mask (they end before every row's limit and before
   // the item's key range end).  The main loop runs while tiles j .. j + 4 are
@@ -835,8 +925,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
     sync();
     float m_use[QB];
     sm_rescale(mx, j, m_use);
+    const int di = ring_didx((C + 1) & 3);
     issue_tile(stage_ptr((C + 3) & 3), (C + 3) & 3);
     slot_load((C + 1) & 3, j + 5);
+    rotate_tile(stage_ptr((C + 1) & 3), di);
     qk(stage_ptr((C + 1) & 3), s_nxt);
     bf16x8 pf[QB][4];
     sm_exp(s_cur, m_use, pf);
@@ -847,8 +939,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
       __attribute__((always_inline)) {
     constexpr int C = decltype(c)::value;
     sync();
+    const int di = ring_didx((C + 1) & 3);
     issue_tile(stage_ptr((C + 3) & 3), (C + 3) & 3);
     slot_load((C + 1) & 3, j + 5);
+    rotate_tile(stage_ptr((C + 1) & 3), di);
     float m_use[QB];
     bf16x8 pf[QB][4];
     sm_mask(s_cur, j);
@@ -861,8 +955,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
   auto idle_iter = [&](int j, auto c) __attribute__((always_inline)) {
     constexpr int C = decltype(c)::value;
     sync();
+    const int di = ring_didx((C + 1) & 3);
     issue_tile(stage_ptr((C + 3) & 3), (C + 3) & 3);
     slot_load((C + 1) & 3, j + 5);
+    rotate_tile(stage_ptr((C + 1) & 3), di);
   };
   int j = 0;
   if (idle) {
@@ -1042,8 +1138,12 @@ int attn_rows_per_block(int) { return 256; }
 template <int DQK, int DV, int DNOPE>
 static hipError_t launch_attn_t(hipStream_t st, const AttnArgs& a) {
   if constexpr (DQK == 128 && DV == 128 && DNOPE == 0) {
-    // the 128-dim GQA layout: direct-to-LDS pipeline
-    hipLaunchKernelGGL((k_seg_attn_dl<128, 128, 0, 8, 1, 4>), dim3(a.n_items), dim3(512), 0, st, a);
+    // the 128-dim GQA layout: direct-to-LDS pipeline (keys owing a rotation
+    // are turned in LDS when the launch carries a rotation table)
+    if (a.key_didx)
+      hipLaunchKernelGGL((k_seg_attn_dl<128, 128, 0, 8, 1, 4, true>), dim3(a.n_items), dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_seg_attn_dl<128, 128, 0, 8, 1, 4, false>), dim3(a.n_items), dim3(512), 0, st, a);
   } else {
     hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE, 8>), dim3(a.n_items), dim3(512), 0, st, a);
   }

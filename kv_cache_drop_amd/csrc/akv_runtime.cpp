@@ -167,6 +167,7 @@ struct akv_pool {
   int n_cu = 256;
   double thr = kDefaultCompactThreshold;
   int compact_mode = AKV_COMPACT_IMMEDIATE;
+  int fuse_mode = AKV_FUSE_AUTO;   // where owed rotations are applied (akv_fused_rotation)
   std::deque<int32_t> compact_q;   // deferred compactions, in the order queued
 
   std::deque<int32_t> free_q;
@@ -1725,6 +1726,14 @@ akv_status akv_compaction_mode(akv_pool* p, int32_t mode) {
   return AKV_OK;
 }
 
+akv_status akv_fused_rotation(akv_pool* p, int32_t mode) {
+  if (!p) return fail(AKV_EINVAL, "NULL pool");
+  if (mode != AKV_FUSE_AUTO && mode != AKV_FUSE_ALWAYS && mode != AKV_FUSE_NEVER)
+    return fail(AKV_EINVAL, "unknown fused-rotation mode %d", mode);
+  p->fuse_mode = mode;
+  return AKV_OK;
+}
+
 akv_status akv_compact_queue(akv_pool* p, int32_t* seqs_out, int32_t cap, int32_t* n_out) {
   if (!p || !n_out) return fail(AKV_EINVAL, "NULL argument");
   if (cap < 0 || (cap > 0 && !seqs_out)) return fail(AKV_EINVAL, "bad output");
@@ -2127,6 +2136,10 @@ akv_status akv_seq_visible(akv_pool* p, int32_t s, const akv_span* mask, int32_t
 }
 
 static bool decode_launch(const akv_pool* p, const int64_t* q_len, int32_t n, int32_t stride);
+// The prefill kernel that turns owed keys in LDS: the 128-dim GQA layout.
+static bool rotating_prefill(const akv_pool* p) {
+  return p->L.d_nope == 0 && p->L.d_rope == 128 && p->L.d_v == 128;
+}
 static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens, const akv_segment* segs,
                                  int32_t n_segs, const akv_extent* page_lists, int32_t n_ext,
                                  const int32_t* ext_lag, float scale, void* out, bool ws_static = false);
@@ -2151,9 +2164,31 @@ akv_status akv_seq_attention(akv_pool* p, const void* Q, int32_t n_q_tokens, con
       lagging = lagging || q->lagging;
       qlens[i] = sg.q_len;
     }
-    // Owed rotations (deferred repos) are applied inside the decode kernel;
-    // a prefill launch first rotates the keys in place.
-    const bool fused = lagging && p->device && decode_launch(p, qlens.data(), n_segs, 1);
+    // Owed rotations (deferred repos) are applied inside the attention
+    // kernels that turn keys where they read them (the decode kernel, and the
+    // direct-to-LDS prefill kernel of the 128-dim GQA layout), or the keys are
+    // first rotated in place (akv_fused_rotation picks; by default a prefill
+    // launch fuses only when it turns each owed key at most once per kv head:
+    // one row tile per segment and one segment per sequence; a prefill block
+    // turns every tile it reads, so keys read by many row tiles are cheaper
+    // to rotate once in place).
+    bool fused = false;
+    if (lagging && p->device && p->fuse_mode != AKV_FUSE_NEVER) {
+      if (decode_launch(p, qlens.data(), n_segs, 1)) {
+        fused = true;
+      } else if (rotating_prefill(p)) {
+        fused = p->fuse_mode == AKV_FUSE_ALWAYS;
+        if (!fused) {
+          const akv_layout& L = p->L;
+          const int64_t G = L.n_q_heads / L.n_kv_heads;
+          std::unordered_map<int32_t, int> uses;
+          bool once = true;
+          for (int32_t i = 0; i < n_segs && once; ++i)
+            once = segs[i].q_len * G <= akv::attn_rows_per_block(L.d_nope) && ++uses[segs[i].seq] == 1;
+          fused = once;
+        }
+      }
+    }
     if (lagging && !fused && p->device)
       for (int32_t i = 0; i < n_segs; ++i) {
         akv_status st = materialize_seq(p, p->seqs[segs[i].seq]);
@@ -2312,8 +2347,8 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
             di.emplace(ext_lag[e], (int32_t)rot_deltas.size());
             rot_deltas.push_back(ext_lag[e]);
           }
-      if (!rot_deltas.empty() && !decode)
-        return fail(AKV_EINVAL, "owed rotations are applied only in decode launches");
+      if (!rot_deltas.empty() && !decode && !rotating_prefill(p))
+        return fail(AKV_EINVAL, "owed rotations are applied only by the decode and 128-dim GQA prefill kernels");
     }
     const int rb = decode ? akv::DECODE_ROWS : akv::attn_rows_per_block(L.d_nope);
     AttnPlan& plan = p->hb.plan;

@@ -503,10 +503,10 @@ def test_seq_attention_equals_segment_attention(make):
 # ---------------------------------------------------------------------------
 # deferred repos: keys owe their rotation, the decode kernel turns them
 # ---------------------------------------------------------------------------
-def _deferred_parity(wl):
+def _deferred_parity(wl, pool=None):
     """Attention against the oracle (its keys rotated eagerly), then every
     sequence materialized and its stored keys against the oracle's."""
-    pool, outs = D.run(wl)
+    pool, outs = D.run(wl, pool=pool)
     res = oracle.run_workload(wl, key_store=_key_store(wl))
     _check_tables(pool, res.pool)
     wa, wr = _check_attention(outs, res, wl)
@@ -638,3 +638,108 @@ def test_repos_layers_one_launch():
         _check_visible_kv(pl, op, lay)
     for p in layers + singles:
         p.close()
+
+
+# ---------------------------------------------------------------------------
+# extended radix tree -> positional version -> attention, end to end
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["base", "stress"])
+def test_tree_retrigger_hit_reused_through_clone_attention(mode):
+    """Request A (an agent trace, older tools dropped, survivors
+    repositioned) is registered in the library's extended radix tree.
+    Request B replays A's history at positions shifted by 777: the tree
+    answers with a retrigger hit (the brute-force matcher of the reuse rules
+    gives the same hit), B's state is rebuilt from A's through akv_seq_clone
+    with the hit's delta, both append new tokens and attend in one launch.
+    Tables, every visible key of both versions and the attention outputs
+    against the oracle, which applies the clone with the matcher's hit."""
+    from oracle.akv_tree_oracle import DROP, REPOS, TOKEN, TreeOracle
+    rng = np.random.default_rng(31)
+    n, nq, shift = 12000, 256, 777
+    lay = W.Layout(32, 8, 0, 128, 128, 16, 1, rope_theta=500000.0)
+    spans = W._c2_like_history(rng, n_turns=12, n_recent=3, total=n, reasoning=256)
+    dropped = spans[:9]
+    rep_s, rep_d = W._survivor_runs(n, dropped)
+    ids = rng.integers(0, 32000, n)
+    hist_a = [(TOKEN, int(t), i, 0) for i, t in enumerate(ids)]
+    hist_a += [(DROP, b, e, 0) for b, e in dropped] + [(REPOS, int(b), int(e), int(d)) for (b, e), d in zip(rep_s, rep_d)]
+    req_b = [(k, a, b + shift, c) if k == TOKEN else (k, a, b, c) for k, a, b, c in hist_a]
+    tree, ref = akv.Tree(), TreeOracle()
+    tree.insert(hist_a, 0)
+    ref.insert(hist_a, 0)
+    hit, want_hit = tree.match(req_b), ref.match(req_b)
+    assert hit == want_hit == dict(seq=0, n_events=len(hist_a), n_tokens=n, exact=0, delta=shift)
+    tree.close()
+    kept = n - sum(e - b for b, e in dropped)
+    lay.num_pages = 2 * ((n + nq) // 16 + 8)
+    wl = W.Workload("tree_retrigger", lay, rng.permutation(lay.num_pages).astype(np.int32))
+    wl.ops += [W.SeqCreate(), W.SeqCreate(), W._append_op(rng, lay, 0, np.arange(n, dtype=np.int32)),
+               W.Drop(0, W._spans(dropped)), W.Repos(0, rep_s, rep_d),
+               W.Clone(want_hit["seq"], 0, want_hit["n_tokens"], 1, want_hit["delta"]),
+               W._append_op(rng, lay, 0, np.arange(kept, kept + nq, dtype=np.int32)),
+               W._append_op(rng, lay, 1, np.arange(kept + shift, kept + shift + nq, dtype=np.int32))]
+    q = W._normal_bf16(rng, (2 * nq, lay.n_q_heads, lay.d_qk), scale=1.0 / 8.0)
+    none = np.zeros((0, 2), np.int32)
+    wl.ops.append(W.Attention(q, [W.Segment(0, 0, nq, none), W.Segment(1, nq, nq, none)]))
+    _full_parity(_variant(wl, mode))
+
+
+# ---------------------------------------------------------------------------
+# deferred repos in prefill: the direct-to-LDS kernel turns owed keys in LDS
+# ---------------------------------------------------------------------------
+def _deferred(wl):
+    for op in wl.ops:
+        if isinstance(op, W.Repos):
+            op.deferred = True
+    return wl
+
+
+@pytest.mark.parametrize("seed,pairing", [(0, 0), (1, 1), (2, 0), (3, 1)])
+@pytest.mark.parametrize("mode", ["auto", "always", "never"])
+def test_prefill_fused_rotation_full(seed, pairing, mode):
+    """Random scripts on the 128-dim GQA layout with every repos deferred
+    (overlapping spans, either sign, splices, compaction, several
+    sequences): prefill launches turn the owed keys in LDS ("always"), or
+    when each key is turned once per kv head ("auto"), or rotate them in
+    place first ("never").  Every output row against the oracle, then each
+    sequence materialized and its stored keys against the oracle's."""
+    wl = _deferred(W.fuzz_small(900 + seed, n_seqs=3, pairing=pairing, page_size=[16, 8, 32, 1][seed],
+                                head_dims=(128,), groups=(1, 4, 8)))
+    assert any(isinstance(o, W.Repos) for o in wl.ops)
+    pool = D.make_pool(wl)
+    pool.fused_rotation(mode)
+    _deferred_parity(wl, pool).close()
+
+
+@pytest.mark.parametrize("pairing", [0, 1])
+def test_prefill_fused_rotation_64k(pairing):
+    """The 64K step with its repos deferred: the four 512-query segments run
+    on keys that still owe their rotation and the kernel turns each landed
+    tile in LDS.  The outputs equal, bit for bit, those of the same launch
+    after the keys were rotated in place (the table and fp32 formula of
+    repos); sampled rows against the oracle (both bars)."""
+    wl = _deferred(W.c2_64k(0))
+    wl.layout.pairing = pairing
+    _say(f"[gpu] 64K prefill with deferred repos, pairing {pairing}")
+    pool = D.make_pool(wl)
+    pool.fused_rotation("always")
+    pool, outs = D.run(wl, pool=pool)
+    att = [o for o in wl.ops if isinstance(o, W.Attention)][0]
+    assert pool.lag(0).any()
+    segs = [(sg.seq, sg.q_begin, sg.q_len, sg.mask_spans if len(sg.mask_spans) else None) for sg in att.segments]
+    q = D.dev_bf16(att.q)
+    fused = outs[0]["out"]
+    pool.materialize(0)
+    assert not pool.lag(0)[~pool.tokens(0)[2]].any()
+    plain = pool.seq_attention(q, segs, att.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), plain.view(torch.int16))
+    rng = np.random.default_rng(5)
+    sample = {i: np.unique(np.concatenate([rng.choice(sg.q_len, 12, replace=False), [0, sg.q_len - 1]]))
+              for i, sg in enumerate(att.segments)}
+    res = oracle.run_workload(wl, sample_rows=sample)
+    _check_tables(pool, res.pool)
+    wa, wr = _check_attention(outs, res, wl)
+    wk = _check_visible_kv(pool, res.pool, wl.layout)
+    _say(f"[gpu] 64K deferred prefill: attention abs {wa:.2e} rel L2 {wr:.2e}; keys after materialize {wk:.2e}")
+    pool.close()

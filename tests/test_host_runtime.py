@@ -659,3 +659,10 @@ def test_repos_layers_host():
     for p, b in zip(layers, before):
         for x, y in zip(p.tokens(0), b):
             np.testing.assert_array_equal(x, y)
+
+
+def test_fused_rotation_mode_is_validated():
+    hp = _host_pool(W.Layout(8, 2, 0, 128, 128, 16, 8), None)
+    for m in ("auto", "always", "never"):
+        hp.fused_rotation(m)
+    assert akv.lib().akv_fused_rotation(hp._h, 7) == akv.AKV_EINVAL
