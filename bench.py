@@ -257,7 +257,9 @@ def run_config(args) -> dict:
 
     gens = {"c1": lambda s: W.c1_tiny(s, "canonical"), "c3": W.c3_mla, "c4": W.c4_batched, "c5": W.c5_128k,
             "decode": W.decode_batch, "decode_fused": lambda s: W.decode_batch(s, deferred=True),
-            "retrigger": W.retrigger, "c2_fused": lambda s: deferred(W.c2_64k(s))}
+            "retrigger": W.retrigger, "c2_fused": lambda s: deferred(W.c2_64k(s)),
+            "decode_compact": W.decode_with_idle,
+            "c2_compact": lambda s: W.with_idle_compaction(W.c2_64k(s), s, n_idle=2, idle_ctx=16384)}
     wl = gens[args.config](args.seed)
     L = wl.layout
     ops = list(wl.ops)
@@ -287,8 +289,9 @@ def run_config(args) -> dict:
     rope_heads = L.n_kv_heads if (not L.mla or L.kpe_per_head) else 1
     tot = {k: [0.0, 0] for k in ("attention", "rotate", "append", "compact", "expand", "combine", "clone")}
     walls, flops, pairs, kv_bytes, n_rot, n_q, clone_bytes = [], 0.0, 0, 0, 0, 0, 0
+    idle_moved = 0
     kern = None
-    n_dec = args.decode_steps if args.config in ("decode", "decode_fused") else 1
+    n_dec = args.decode_steps if args.config in ("decode", "decode_fused", "decode_compact") else 1
     first_walls = []
     for rep in range(args.warmup + args.steps):
         pool = D.make_pool(wl)
@@ -349,6 +352,7 @@ def run_config(args) -> dict:
                 tot[k][0] += ms
                 tot[k][1] += n
         if rep == 0:
+            idle_moved = sum(pool.info(s)[1] for s in wl.notes.get("idle", []))
             for s in range(n_seq):
                 _, pos0, drop0 = pre[s]
                 _, pos1, drop1 = pool.tokens(s)
@@ -418,7 +422,21 @@ def run_config(args) -> dict:
         rec["note"] = (f"ms_per_step: steady decode steps 2..{n_dec} on the same pool (each appends one token "
                        "per request and attends over every list); first_step_ms: the first step after the "
                        "histories' drops and repos, which rebuilds each visible list")
-    if args.config in ("decode", "decode_fused"):
+    if args.config in ("decode_compact", "c2_compact") and tot["compact"][1]:
+        # the background pass: every visible token of the idle sequences moves
+        # (K and V rows read and written), beside the decode step
+        cm_ms = tot["compact"][0] / tot["compact"][1]
+        cm_per_step = tot["compact"][1] / max(args.steps, 1)    # launches per rep (one pass per rep)
+        per_tok = 2 * L.n_kv_heads * (L.d_nope + L.d_rope + L.d_v) * 2
+        cm_bytes = per_tok * idle_moved
+        cm_gbps = cm_bytes / (cm_ms * cm_per_step * 1e-3) / 1e9
+        rec["roofline_compact"] = {"bound": "hbm", "achieved": round(cm_gbps, 1), "peak": PEAK_HBM_GBPS,
+                                   "unit": "GB/s", "frac": round(cm_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                                   "kernel": "k_move_tokens (background stream)", "bytes_per_step": cm_bytes,
+                                   "launches_per_pass": cm_per_step, "avg_launch_ms": round(cm_ms, 5)}
+        rec["note"] = ("the workload's step on the pool stream, then the background compaction pass (its copies on "
+                       "the pool's second stream, beside the step's kernels)")
+    if args.config in ("decode", "decode_fused", "decode_compact"):
         # one query row per kv-head group: the launch streams the visible K/V once
         hbm_gbps = kv_bytes / (attn_ms * 1e-3) / 1e9
         rec["roofline"] = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -462,6 +480,12 @@ CONFIG_NAMES = {
                  "the offset change; 512 queries each in one launch",
     "c2_fused": "the 64K step (Llama-3.1-8B-shaped layer, 32 q / 8 kv heads, head_dim 128, page 16) with its repos "
                 "deferred: no rotation pass; the attention kernel turns each landed key tile in LDS",
+    "decode_compact": "the decode step of 48 requests of 2K-16K tokens (32 q / 8 kv heads, head_dim 128, page 16) "
+                      "while 8 idle 32K-token sequences, half their tokens dropped in 8-token blocks, are compacted "
+                      "by one background pass (second stream) in the same step",
+    "c2_compact": "the 64K step (Llama-3.1-8B-shaped layer, 32 q / 8 kv heads, head_dim 128, page 16), then a "
+                  "background compaction pass over 2 idle 16K-token sequences with half their tokens dropped in "
+                  "8-token blocks, its copies on the pool's second stream beside the step's attention",
     "decode_fused": "the decode step of 48 requests of 2K-16K tokens whose survivors' repos was deferred: the "
                     "keys stay at their old positions and the decode kernel turns them as it reads them",
     "decode": "48 requests of 2K-16K tokens on the 64K layer shape (32 q / 8 kv heads, head_dim 128, page 16), "
@@ -473,7 +497,7 @@ CONFIG_NAMES = {
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2_fused", "c3", "c4", "c5", "decode", "decode_fused",
-                                                       "retrigger"],
+                                                       "decode_compact", "c2_compact", "retrigger"],
                     help="c2 (default) is the headline 64K step; the others print one record each")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)

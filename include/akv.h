@@ -20,11 +20,16 @@
  * - Host arrays passed in (spans, positions, segments, extents) are copied
  *   before the call returns.  Device inputs (K, V, Q) must stay valid until the
  *   work is done (akv_sync or a sync of the pool's stream).
- * - All kernels are enqueued on the pool's HIP stream; calls return once they
+ * - Kernels are enqueued on the pool's HIP stream; calls return once they
  *   are enqueued, with the host metadata already updated.  A device pool also
- *   owns one stream of its own (default priority) for metadata copies into
- *   scratch while the pool's stream is busy; the pool's stream waits for each
- *   such copy, so syncing the pool's stream covers all of a pool's work.
+ *   owns two streams of its own (default priority): one for metadata copies
+ *   into scratch while the pool's stream is busy (the pool's stream waits for
+ *   each such copy), and one for the background compaction copies of
+ *   akv_compact_pending, which run beside later work on the pool's stream.
+ *   The pool's stream waits for those copies before any later library launch
+ *   that reads or writes a page they touch; akv_sync waits for every stream of
+ *   the pool (a caller's own kernels that read the page arrays order
+ *   themselves after akv_sync or after such a launch).
  * - Calls on one pool are not re-entrant; separate pools are independent.
  * - Every call validates all arguments before changing any state: a call that
  *   fails leaves the pool as it was.  akv_last_error() gives the reason.
@@ -170,7 +175,10 @@ akv_status akv_compact(akv_pool* pool, int32_t seq, int32_t force);
 enum { AKV_COMPACT_IMMEDIATE = 0, AKV_COMPACT_DEFERRED = 1 };
 akv_status akv_compaction_mode(akv_pool* pool, int32_t mode);
 
-/* Compact queued sequences in queue order: a sequence no longer above the
+/* Compact queued sequences in queue order, as a background pass: the copies
+ * run on the pool's background stream, after the pool stream's work so far
+ * and beside its later work (a later launch touching a page the copies read
+ * or write waits for them first).  A sequence no longer above the
  * threshold leaves the queue without a copy; the walk stops at the first one
  * whose visible tokens would take the moved total past max_tokens, that the
  * allocator cannot supply pages for, or whose copy list does not fit the
@@ -444,7 +452,7 @@ akv_status akv_timing_read(akv_pool* pool, int32_t kind, double* total_ms, int32
  * exceeds cap).  Does not clear them. */
 akv_status akv_timing_samples(akv_pool* pool, int32_t kind, float* ms, int32_t cap, int32_t* n_out);
 
-akv_status akv_sync(akv_pool* pool);       /* wait for the pool's stream */
+akv_status akv_sync(akv_pool* pool);       /* wait for the pool's streams */
 const char* akv_last_error(void);          /* thread-local text of the last failure */
 
 #ifdef __cplusplus

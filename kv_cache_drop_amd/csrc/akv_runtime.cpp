@@ -162,8 +162,28 @@ struct akv_pool {
   size_t ring_head = 0;
   struct RingUse {
     size_t b0, e0, b1, e1;   // at most two ranges (a call may wrap once)
+    bool bg;                 // read by a background-compaction launch (kstream)
   };
   std::deque<RingUse> ring_uses;
+  // Background compaction ([AKV-blog] section 7, Dilemma 2: defragmentation
+  // runs asynchronously, without pausing inference): akv_compact_pending
+  // launches its copies on kstream (default priority), ordered after the pool
+  // stream's earlier work; bg_done follows the last of them.  Until the pool
+  // stream waits for bg_done, the pages those copies read or write are
+  // flagged, and pool-stream work touching a flagged page waits first; other
+  // work runs beside the copies.
+  hipStream_t kstream = nullptr;
+  hipEvent_t bg_done = nullptr;
+  bool bg_pending = false;
+  // Points of the pool stream the background copies are ordered after: the
+  // end of the last launch that wrote pool rows, and the end of the work
+  // enqueued before the last call that gave pages back to the queues (work
+  // that may still read those pages).  Later pool-stream work is not waited
+  // for, so the copies run beside it.
+  hipEvent_t write_ev = nullptr, free_ev = nullptr;
+  bool write_set = false, free_set = false;
+  std::vector<uint8_t> page_bg;
+  std::vector<int32_t> bg_pages;
   int n_cu = 256;
   double thr = kDefaultCompactThreshold;
   int compact_mode = AKV_COMPACT_IMMEDIATE;
@@ -220,6 +240,7 @@ akv_status stg_reserve(akv_pool* p, size_t n, char** out) {
   if (n > s.cap) {
     hipError_t e = hipStreamSynchronize(p->cstream);
     if (e == hipSuccess) e = hipStreamSynchronize(p->stream);
+    if (e == hipSuccess && p->kstream) e = hipStreamSynchronize(p->kstream);
     if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
     for (auto& r : s.pending) s.spare.push_back(r.ev);
     s.pending.clear();
@@ -290,7 +311,7 @@ akv_status stg_upload(akv_pool* p, const char* host, void* dev, size_t n) {
 // [b, e) has finished on the pool stream; those calls are then forgotten.
 // The calls' ranges carry no event: one recorded now on the pool stream
 // follows all of their kernels (the pool stream is in order).
-void ring_wait(akv_pool* p, size_t b, size_t e) {
+void ring_wait(akv_pool* p, size_t b, size_t e, bool bg_upload = false) {
   auto& u = p->ring_uses;
   int last = -1;
   for (int i = 0; i < (int)u.size(); ++i)
@@ -300,9 +321,20 @@ void ring_wait(akv_pool* p, size_t b, size_t e) {
   if (last < 0) return;
   hipEvent_t ev;
   if (stg_event(p, &ev) == hipSuccess) {
-    if (hipEventRecord(ev, p->stream) == hipSuccess) (void)hipStreamWaitEvent(p->cstream, ev, 0);
+    if (hipEventRecord(ev, p->stream) == hipSuccess) {
+      (void)hipStreamWaitEvent(p->cstream, ev, 0);
+      if (bg_upload) (void)hipStreamWaitEvent(p->kstream, ev, 0);   // the upload runs on kstream
+    }
     p->stg.spare.push_back(ev);
   }
+  // a range a background copy reads: the upload (on either stream) waits for
+  // the background stream's last launch
+  for (int i = 0; i <= last; ++i)
+    if (u[i].bg) {
+      (void)hipStreamWaitEvent(p->cstream, p->bg_done, 0);
+      (void)hipStreamWaitEvent(p->stream, p->bg_done, 0);
+      break;
+    }
   u.erase(u.begin(), u.begin() + last + 1);
 }
 
@@ -314,7 +346,7 @@ struct ScratchCursor {
   akv_pool* p;
   size_t off;            // next byte
   size_t first = 0;      // the call's first byte
-  bool bad = false, wrapped = false, any = false;
+  bool bad = false, wrapped = false, any = false, bg = false;
   size_t r0b = 0, r0e = 0, r1b = 0, r1e = 0;
   explicit ScratchCursor(akv_pool* pp, size_t need = 0) : p(pp), off(pp->ring_head) {
     if (off < p->scratch_base || off + align_up(need, 256) > p->scratch_bytes) off = p->scratch_base;
@@ -334,7 +366,7 @@ struct ScratchCursor {
       wrapped = true;
       off = p->scratch_base;
     }
-    if (!bad && p->device) ring_wait(p, off, off + m);
+    if (!bad && p->device) ring_wait(p, off, off + m, bg);
     if (!wrapped) {
       if (!any) r0b = off;
       r0e = off + m;
@@ -351,7 +383,7 @@ struct ScratchCursor {
   size_t needed() const { return bad ? p->scratch_bytes + 1 : off; }
   ~ScratchCursor() {
     if (!any || bad || !p->device) return;
-    p->ring_uses.push_back({r0b, r0e, r1b, r1e});
+    p->ring_uses.push_back({r0b, r0e, r1b, r1e, bg});
     p->ring_head = off;
   }
 };
@@ -371,16 +403,17 @@ hipError_t tev_get(akv_pool* p, hipEvent_t* ev) {
 struct KTimer {
   akv_pool* p;
   int kind;
+  hipStream_t st;
   hipEvent_t a = nullptr, b = nullptr;
-  KTimer(akv_pool* pp, int k) : p(pp), kind(k) {
+  KTimer(akv_pool* pp, int k, hipStream_t s = nullptr) : p(pp), kind(k), st(s ? s : pp->stream) {
     if (p->timing && tev_get(p, &a) == hipSuccess && tev_get(p, &b) == hipSuccess)
-      (void)hipEventRecord(a, p->stream);
+      (void)hipEventRecord(a, st);
     else
       a = b = nullptr;
   }
   void done() {
     if (a && b) {
-      (void)hipEventRecord(b, p->stream);
+      (void)hipEventRecord(b, st);
       p->tev.push_back({kind, a, b});
       a = b = nullptr;
     }
@@ -389,8 +422,10 @@ struct KTimer {
 
 akv_status timing_collect(akv_pool* p) {
   if (p->tev.empty()) return AKV_OK;
-  hipError_t e = hipEventSynchronize(p->tev.back().b);
-  if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(timing)");
+  for (auto& t : p->tev) {   // launches of two streams: each end event on its own
+    hipError_t e = hipEventSynchronize(t.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(timing)");
+  }
   for (auto& t : p->tev) {
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, t.a, t.b) == hipSuccess) {
@@ -833,10 +868,42 @@ akv_status check_launch(hipError_t e, const char* what) {
   return AKV_OK;
 }
 
+// Marks the pool stream's current end as the last write of pool rows.
+void note_write(akv_pool* p) {
+  if (p->device && hipEventRecord(p->write_ev, p->stream) == hipSuccess) p->write_set = true;
+}
+// Marks the pool stream's current end: pages just given back to the queues
+// are read by no pool-stream work enqueued later.
+void note_free(akv_pool* p) {
+  if (p->device && hipEventRecord(p->free_ev, p->stream) == hipSuccess) p->free_set = true;
+}
+
+// The pool stream waits for the background compaction copies; their pages
+// are no longer flagged.
+akv_status bg_wait(akv_pool* p) {
+  if (!p->bg_pending) return AKV_OK;
+  hipError_t e = hipStreamWaitEvent(p->stream, p->bg_done, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(background compaction)");
+  p->bg_pending = false;
+  for (int32_t pg : p->bg_pages) p->page_bg[pg] = 0;
+  p->bg_pages.clear();
+  return AKV_OK;
+}
+
+// bg_wait when any of the slots lies in a page a background copy touches.
+akv_status bg_wait_slots(akv_pool* p, const int32_t* slots, size_t n) {
+  if (!p->bg_pending) return AKV_OK;
+  for (size_t i = 0; i < n; ++i)
+    if (slots[i] >= 0 && p->page_bg[slots[i] >> p->log2S]) return bg_wait(p);
+  return AKV_OK;
+}
+
 // scatter appended rows of one token batch into the pool arrays
 akv_status device_append(akv_pool* p, const std::vector<int32_t>& slots, const void* K,
                          const void* Kpe, const void* V) {
   if (!p->device || !K) return AKV_OK;
+  akv_status bst = bg_wait_slots(p, slots.data(), slots.size());
+  if (bst != AKV_OK) return bst;
   ScratchCursor sc(p, slots.size() * 4 + 256);
   void* dslots;
   DirectRegion dr;
@@ -861,6 +928,7 @@ akv_status device_append(akv_pool* p, const std::vector<int32_t>& slots, const v
   hipError_t e = akv::launch_scatter_tokens(p->stream, rows, nr, (const int32_t*)dslots, n, L.page_size, p->log2S);
   tm.done();
   stg_release(p, dr);
+  note_write(p);
   return check_launch(e, "append kernel launch");
 }
 
@@ -870,6 +938,10 @@ akv_status device_rotate(akv_pool* p, const std::vector<akv::RotItem>& items,
                          const std::vector<int32_t>& deltas,
                          const std::vector<akv_pool*>& layers = {}) {
   if (!p->device || items.empty()) return AKV_OK;
+  akv_status bst = bg_wait(p);
+  for (akv_pool* l : layers)
+    if (bst == AKV_OK && l != p) bst = bg_wait(l);
+  if (bst != AKV_OK) return bst;
   std::vector<uint16_t*> krs;
   if (layers.empty()) krs.push_back(p->rope_array());
   for (akv_pool* l : layers) krs.push_back(l->rope_array());
@@ -892,6 +964,9 @@ akv_status device_rotate(akv_pool* p, const std::vector<akv::RotItem>& items,
   e = akv::launch_rotate(p->stream, (uint16_t* const*)dkrs, (int)krs.size(), p->rope_heads(), p->L.page_size,
                          p->L.d_rope, p->L.pairing, (const akv::RotItem*)ditems, (int)items.size(), dtab);
   tm.done();
+  note_write(p);
+  for (akv_pool* l : layers)
+    if (l != p) note_write(l);
   return check_launch(e, "rotate kernel launch");
 }
 
@@ -909,6 +984,8 @@ hipError_t move_tokens(akv_pool* p, const akv::MovePair* pairs, int n, const flo
 
 akv_status device_move(akv_pool* p, const std::vector<akv::MovePair>& mv) {
   if (!p->device || mv.empty()) return AKV_OK;
+  akv_status bst = bg_wait(p);
+  if (bst != AKV_OK) return bst;
   ScratchCursor sc(p, mv.size() * sizeof(akv::MovePair) + 256);
   void* dmv;
   akv_status st = upload_array(p, sc, mv.data(), mv.size() * sizeof(akv::MovePair), &dmv);
@@ -917,7 +994,71 @@ akv_status device_move(akv_pool* p, const std::vector<akv::MovePair>& mv) {
   KTimer tm(p, AKV_K_COMPACT);
   hipError_t e = move_tokens(p, (const akv::MovePair*)dmv, n, nullptr);
   tm.done();
+  note_write(p);
+  note_free(p);   // compaction gave the old pages back
   return check_launch(e, "compaction kernel launch");
+}
+
+// The same copies as a background launch on kstream: after the pool
+// stream's work so far (which wrote the rows read and last read the pages
+// written), beside the pool stream's later work; every page the copies read
+// or write is flagged until the pool stream waits for them.
+akv_status device_move_bg(akv_pool* p, const std::vector<akv::MovePair>& mv, bool after_all) {
+  if (!p->device || mv.empty()) return AKV_OK;
+  // ordered after the last write of pool rows and after the work that may
+  // still read pages given back to the queues, not after later work; when
+  // fresh pages come from the evictable queue (pages an earlier background
+  // pass gave back may still be read by work enqueued before it), after all
+  // of the pool stream's work so far
+  hipError_t e = hipSuccess;
+  if (after_all) {
+    e = hipEventRecord(p->free_ev, p->stream);
+    if (e == hipSuccess) p->free_set = true;
+  }
+  if (e == hipSuccess && p->write_set) e = hipStreamWaitEvent(p->kstream, p->write_ev, 0);
+  if (e == hipSuccess && p->free_set) e = hipStreamWaitEvent(p->kstream, p->free_ev, 0);
+  if (e != hipSuccess) return hip_fail(e, "ordering the background copies");
+  // the copy list goes up on kstream itself
+  const size_t nb = mv.size() * sizeof(akv::MovePair);
+  ScratchCursor sc(p, nb + 256);
+  sc.bg = true;
+  char* h;
+  akv_status st = stg_reserve(p, nb, &h);
+  if (st != AKV_OK) return st;
+  std::memcpy(h, mv.data(), nb);
+  void* dmv = sc.take(nb);
+  if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small for this call (%zu bytes per call)",
+                            p->scratch_bytes - p->scratch_base);
+  e = hipMemcpyAsync(dmv, h, nb, hipMemcpyHostToDevice, p->kstream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(H2D, background)");
+  hipEvent_t uev;
+  e = stg_event(p, &uev);
+  if (e == hipSuccess) e = hipEventRecord(uev, p->kstream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(background upload)");
+  const size_t off = (size_t)(h - p->stg.base);
+  p->stg.pending.push_back({off, off + align_up(std::max<size_t>(nb, 16), 256), uev});
+  const akv_layout& L = p->L;
+  akv::TokenRows plain[2];
+  int np = 0;
+  plain[np++] = {p->v, p->v, L.n_kv_heads, L.d_v};
+  if (L.d_nope > 0) plain[np++] = {p->k, p->k, L.n_kv_heads, L.d_nope};
+  KTimer tm(p, AKV_K_COMPACT, p->kstream);
+  e = akv::launch_move_tokens(p->kstream, p->rope_array(), p->rope_heads(), L.d_rope, L.pairing, plain, np,
+                              (const akv::MovePair*)dmv, (int)mv.size(), L.page_size, p->log2S, nullptr);
+  tm.done();
+  if (e != hipSuccess) return check_launch(e, "background compaction kernel launch");
+  e = hipEventRecord(p->bg_done, p->kstream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(background compaction)");
+  p->bg_pending = true;
+  for (const akv::MovePair& m : mv)
+    for (int32_t slot : {m.src, m.dst}) {
+      const int32_t pg = slot >> p->log2S;
+      if (!p->page_bg[pg]) {
+        p->page_bg[pg] = 1;
+        p->bg_pages.push_back(pg);
+      }
+    }
+  return AKV_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -1452,6 +1593,15 @@ akv_status akv_pool_create(const akv_layout* layout, const int32_t* page_order, 
         delete p;
         return hip_fail(ce, "hipStreamCreateWithFlags(copy stream)");
       }
+      ce = hipStreamCreateWithFlags(&p->kstream, hipStreamNonBlocking);
+      if (ce == hipSuccess) ce = hipEventCreateWithFlags(&p->bg_done, hipEventDisableTiming);
+      if (ce == hipSuccess) ce = hipEventCreateWithFlags(&p->write_ev, hipEventDisableTiming);
+      if (ce == hipSuccess) ce = hipEventCreateWithFlags(&p->free_ev, hipEventDisableTiming);
+      if (ce != hipSuccess) {
+        akv_pool_destroy(p);
+        return hip_fail(ce, "background compaction stream");
+      }
+      p->page_bg.assign(L.num_pages, 0);
       int dev = 0;
       hipDeviceProp_t prop;
       if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
@@ -1473,6 +1623,13 @@ akv_status akv_pool_destroy(akv_pool* p) {
     (void)hipStreamSynchronize(p->cstream);
     (void)hipStreamDestroy(p->cstream);
   }
+  if (p->kstream) {
+    (void)hipStreamSynchronize(p->kstream);
+    (void)hipStreamDestroy(p->kstream);
+  }
+  if (p->bg_done) (void)hipEventDestroy(p->bg_done);
+  if (p->write_ev) (void)hipEventDestroy(p->write_ev);
+  if (p->free_ev) (void)hipEventDestroy(p->free_ev);
   for (auto& r : p->stg.pending) (void)hipEventDestroy(r.ev);
   for (auto e : p->stg.spare) (void)hipEventDestroy(e);
   if (p->stg.base) (void)hipHostFree(p->stg.base);
@@ -1519,6 +1676,7 @@ akv_status akv_seq_release(akv_pool* p, int32_t s) {
   }
   q->vis.clear();
   q->stale();
+  note_free(p);
   return AKV_OK;
 }
 
@@ -1614,9 +1772,12 @@ akv_status akv_seq_clone(akv_pool* p, int32_t src, int32_t first, int32_t n, int
     const void* dmv = dv[0];
     const float* dtab = (const float*)dv[1];
     hipError_t e;
+    st = bg_wait(p);
+    if (st != AKV_OK) return st;
     KTimer tm(p, AKV_K_CLONE);
     e = move_tokens(p, (const akv::MovePair*)dmv, m, delta != 0 ? dtab : nullptr);
     tm.done();
+    note_write(p);
     return check_launch(e, "clone kernel launch");
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
@@ -1697,6 +1858,7 @@ akv_status akv_drop(akv_pool* p, int32_t s, const akv_span* spans, int32_t n) {
     if (st != AKV_OK) return st;
     for (int32_t i = 0; i < n; ++i) drop_tokens(p, *q, spans[i].begin, spans[i].end, true);
     cache_after_drop(*q, spans, n);
+    note_free(p);
     return auto_compact(p, s);
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
@@ -1750,13 +1912,15 @@ akv_status akv_compact_pending(akv_pool* p, int64_t max_tokens, int32_t max_seqs
     *n_out = 0;
     const int32_t S = p->L.page_size;
     std::vector<akv::MovePair> mv;
+    bool from_evict = false;   // this batch takes fresh pages from the evictable queue
     // Copies of one batch run in one launch.  A sequence whose fresh pages
     // would come from the evictable queue (possibly pages this batch still
     // reads) starts a new batch, so its copies run after the earlier ones.
     auto flush = [&]() -> akv_status {
       if (mv.empty()) return AKV_OK;
-      akv_status st = device_move(p, mv);
+      akv_status st = device_move_bg(p, mv, from_evict);
       mv.clear();
+      from_evict = false;
       return st;
     };
     int64_t used = 0;
@@ -1774,6 +1938,7 @@ akv_status akv_compact_pending(akv_pool* p, int64_t max_tokens, int32_t max_seqs
       if ((int64_t)p->free_q.size() < need) {
         akv_status st = flush();
         if (st != AKV_OK) return st;
+        from_evict = true;
       }
       auto fits = [&](size_t n) { return !p->device || p->scratch_base + n * sizeof(akv::MovePair) + 4352 <= p->scratch_bytes; };
       if (!fits(mv.size() + q.n_vis)) {
@@ -2077,6 +2242,7 @@ akv_status akv_splice(akv_pool* p, int32_t s, const akv_span* spans, const int32
     // apply: drop, append stubs, rotate downstream (one launch), positions
     for (int32_t i = 0; i < H; ++i)
       if (in_span[i]) drop_tokens(p, *q, vis[i], vis[i] + 1);
+    note_free(p);
     if (n_stub > 0) {
       std::vector<int32_t> slots(n_stub);
       place_tokens(p, s, (int32_t)n_stub, stub_pos.data(), slots.data());
@@ -2331,6 +2497,14 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
     if (vst != AKV_OK) return vst;
     if (!any_rows) return AKV_OK;
     if (!Q || !out) return fail(AKV_EINVAL, "Q and out are required");
+    if (p->bg_pending) {   // lists reading pages a background copy touches wait for it
+      bool touch = false;
+      for (int32_t e = 0; e < n_ext && !touch; ++e) touch = p->page_bg[page_lists[e].page] != 0;
+      if (touch) {
+        akv_status bst = bg_wait(p);
+        if (bst != AKV_OK) return bst;
+      }
+    }
 
     std::vector<int64_t> qlens(n_segs);
     for (int32_t i = 0; i < n_segs; ++i) qlens[i] = segs[i].q_len;
@@ -2652,6 +2826,7 @@ akv_status akv_sync(akv_pool* p) {
   if (!p) return fail(AKV_EINVAL, "NULL pool");
   if (!p->device) return AKV_OK;
   hipError_t e = hipStreamSynchronize(p->stream);
+  if (e == hipSuccess && p->kstream) e = hipStreamSynchronize(p->kstream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   return AKV_OK;
 }

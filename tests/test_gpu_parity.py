@@ -743,3 +743,14 @@ def test_prefill_fused_rotation_64k(pairing):
     wk = _check_visible_kv(pool, res.pool, wl.layout)
     _say(f"[gpu] 64K deferred prefill: attention abs {wa:.2e} rel L2 {wr:.2e}; keys after materialize {wk:.2e}")
     pool.close()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_background_compaction_beside_decode_full(seed):
+    """A background compaction pass (copies on the pool's second stream) is
+    followed at once, with no sync, by a decode step over other requests
+    (which reads none of the compacted pages and runs beside the copies) and
+    by a launch over the compacted sequences (which waits for them).  Tables,
+    queues, every visible K/V row and every output row against the oracle."""
+    _full_parity(W.decode_with_idle(seed, n_req=12, n_idle=4, idle_ctx=6000, ctx_lo=2000, ctx_hi=6000,
+                                    attend_idle=True))

@@ -666,3 +666,15 @@ def test_fused_rotation_mode_is_validated():
     for m in ("auto", "always", "never"):
         hp.fused_rotation(m)
     assert akv.lib().akv_fused_rotation(hp._h, 7) == akv.AKV_EINVAL
+
+
+def test_decode_with_idle_compaction_bit_exact():
+    """Deferred compaction queued by idle sequences, one pass, then a decode
+    step and a launch over the compacted sequences: tables and queues after
+    every op equal the oracle's."""
+    wl = W.decode_with_idle(2, n_req=10, n_idle=3, idle_ctx=5000, ctx_lo=1000, ctx_hi=4000, attend_idle=True)
+    i0 = wl.notes["step_from"]
+    head = W.Workload(wl.name, wl.layout, wl.page_order, wl.ops[:i0], wl.notes)
+    hp, op = _replay(head)
+    assert op.queue and list(op.queue) == hp.compact_queue()      # the idle sequences wait for the pass
+    _replay(wl)

@@ -37,7 +37,9 @@ import numpy as np
 __all__ = [
     "Layout", "SeqCreate", "Append", "AppendBatch", "Drop", "Repos", "Splice", "Compact", "Clone",
     "Segment", "Attention", "Workload", "to_bf16", "bf16_to_f64",
-    "c1_tiny", "c2_64k", "c3_mla", "c4_batched", "c5_128k", "decode_batch", "retrigger", "fuzz_small",
+    "c1_tiny", "c2_64k", "c3_mla", "c4_batched", "c5_128k", "decode_batch", "decode_with_idle", "retrigger",
+    "with_idle_compaction",
+    "fuzz_small",
     "CONFIGS", "make", "query_variant",
 ]
 
@@ -604,6 +606,58 @@ def decode_batch(seed: int = 0, n_req: int = 48, ctx_lo: int = 2048, ctx_hi: int
     wl.ops.append(Attention(qarr, segs))
     wl.notes.update(requests=reqs)
     return wl
+
+
+def with_idle_compaction(wl: Workload, seed: int = 0, n_idle: int = 8, idle_ctx: int = 32768, block: int = 8,
+                         attend_idle: bool = False) -> Workload:
+    """`wl` while other agents wait on tools: n_idle idle sequences of
+    idle_ctx tokens (created after wl's own sequences) lose every other
+    block of `block` tokens (half a 16-token page: fragmentation 0.5, above
+    the 0.4 threshold) in deferred compaction mode, so they wait in the
+    compaction queue.  The step runs wl's own step (its operations from
+    notes["step_from"], else from its first operation other than a sequence
+    creation or an append), then the background compaction pass over the
+    queue (its copies read and write none of the pages wl's step reads, so
+    they run beside it).  attend_idle appends one more launch with a
+    one-query segment over each idle sequence (its last token)."""
+    rng = _rng(seed + 7919)
+    lay = wl.layout
+    S = lay.page_size
+    i0 = wl.notes.get("step_from",
+                      next(i for i, o in enumerate(wl.ops) if not isinstance(o, (SeqCreate, Append))))
+    head, step = wl.ops[:i0], wl.ops[i0:]
+    n_own = sum(isinstance(o, SeqCreate) for o in wl.ops)
+    idle = list(range(n_own, n_own + n_idle))
+    last_create = max(i for i, o in enumerate(head) if isinstance(o, SeqCreate))
+    ops = head[:last_create + 1] + [SeqCreate() for _ in idle] + head[last_create + 1:]
+    for s in idle:
+        ops.append(_append_op(rng, lay, s, np.arange(idle_ctx, dtype=np.int32)))
+    ops.append(CompactMode(True))
+    for s in idle:
+        ops.append(Drop(s, _spans([(b, min(b + block, idle_ctx)) for b in range(block, idle_ctx, 2 * block)])))
+    out = Workload(f"{wl.name}_idle", lay, wl.page_order, ops, dict(wl.notes))
+    out.notes["step_from"] = len(ops)
+    ops += step
+    ops.append(CompactPending(1 << 40))
+    if attend_idle:
+        q = _normal_bf16(rng, (n_idle, lay.n_q_heads, lay.d_qk), scale=1.0 / 8.0)
+        none = np.zeros((0, 2), np.int32)
+        ops.append(Attention(q, [Segment(s, i, 1, none) for i, s in enumerate(idle)]))
+    # pages: the idle sequences and their compacted copies
+    extra = n_idle * (2 * ((idle_ctx + S - 1) // S) + 2)
+    lay.num_pages += extra
+    order = np.concatenate([wl.page_order, np.arange(lay.num_pages - extra, lay.num_pages, dtype=np.int32)])
+    out.page_order = rng.permutation(order).astype(np.int32)
+    out.notes["idle"] = idle
+    return out
+
+
+def decode_with_idle(seed: int = 0, n_req: int = 48, n_idle: int = 8, idle_ctx: int = 32768,
+                     attend_idle: bool = False, **kw) -> Workload:
+    """The decode step of decode_batch, then a background compaction pass
+    over n_idle fragmented idle sequences (with_idle_compaction)."""
+    return with_idle_compaction(decode_batch(seed, n_req=n_req, **kw), seed, n_idle, idle_ctx,
+                                attend_idle=attend_idle)
 
 
 # --------------------------------------------------------------------------
