@@ -225,25 +225,32 @@ akv_status akv_repos_batch(akv_pool* pool, int32_t n_seqs, const int32_t* seqs, 
  * the decode kernel in registers, the 128-dim GQA prefill kernel in LDS
  * (each landed key tile turned once per block), both with the rotation table
  * and fp32 formula of akv_repos, so the results equal repos-then-attention
- * bit for bit; other launches rotate the keys in place first (see
- * akv_fused_rotation).  akv_segment_attention reads keys as stored.  Later repos
- * calls, compaction, splices and clones keep each token's debt. */
+ * bit for bit; other launches first materialize each sequence they read
+ * (as akv_materialize: own rows rotated in place, rows in shared pages copied
+ * into the sequence's own pages, which can fail with AKV_ENOMEM before the
+ * launch; see akv_fused_rotation).  akv_segment_attention reads keys as
+ * stored.  Later repos calls, compaction, splices and clones keep each
+ * token's debt. */
 akv_status akv_repos_deferred(akv_pool* pool, int32_t seq, const akv_span* spans, const int32_t* delta,
                               int32_t n_spans);
 /* Where akv_seq_attention applies owed rotations.  AKV_FUSE_AUTO (the
  * default): decode launches turn keys in the kernel; a prefill launch on the
  * 128-dim GQA layout does so when it turns each owed key at most once per kv
  * head (every segment one row tile of 256 packed rows, every sequence in one
- * segment), and otherwise rotates the keys in place first (a prefill block
+ * segment), and otherwise materializes the sequences first (a prefill block
  * turns every tile it reads, so keys read by many row tiles are cheaper to
  * rotate once in HBM).  AKV_FUSE_ALWAYS: every launch whose kernel can turn
- * keys does.  AKV_FUSE_NEVER: keys are always rotated in place first.
- * Results are the same bits in every mode.  Errors: AKV_EINVAL. */
+ * keys does.  AKV_FUSE_NEVER: the sequences are always materialized first.
+ * Outputs are the same bits in every mode (materializing copies rows of
+ * shared pages, so page tables can differ).  Errors: AKV_EINVAL. */
 enum { AKV_FUSE_AUTO = 0, AKV_FUSE_ALWAYS = 1, AKV_FUSE_NEVER = 2 };
 akv_status akv_fused_rotation(akv_pool* pool, int32_t mode);
-/* Rotate the sequence's visible keys by what they owe, in place (one
- * launch), as akv_repos would have; the debt is then 0.  Errors: AKV_EINVAL,
- * AKV_ESTATE, AKV_ENOMEM (scratch). */
+/* Rotate the sequence's visible keys by what they owe, as akv_repos would
+ * have; the debt is then 0.  Rows of its own pages are turned in place (one
+ * launch); rows in shared pages (akv_seq_share) are copied, turned, into new
+ * slots of its own pages, placed as an append places tokens (one copy launch
+ * per distinct owed rotation).  Errors: AKV_EINVAL, AKV_ESTATE, AKV_ENOMEM
+ * (scratch, or no pages for the copies: then nothing changed). */
 akv_status akv_materialize(akv_pool* pool, int32_t seq);
 /* Owed rotation of tokens first .. first+n-1 (position minus the position
  * their stored key encodes). */
@@ -294,6 +301,34 @@ akv_status akv_splice(akv_pool* pool, int32_t seq, const akv_span* spans, const 
  * AKV_ENOMEM (pages or scratch), AKV_ESTATE (released sequence). */
 akv_status akv_seq_clone(akv_pool* pool, int32_t src, int32_t first, int32_t n, int32_t dst,
                          int32_t delta);
+
+/* Shared pages for cached states ([AKV-blog] section 3, branching on
+ * divergence with copy-on-write page-table references; [AKV-notes] section 3,
+ * Cache Management: a positional version re-uses a cached state through a
+ * key rotation, and versions are evicted once nothing uses them).
+ *
+ * akv_seq_freeze makes a sequence a checkpoint: keys owing a rotation are
+ * turned in place first, then its rows never change; calls that would change
+ * it (append, drop, repos, splice, compaction, clone into it) return
+ * AKV_ESTATE.  Releasing it while other sequences still hold slots in its
+ * pages keeps those pages until the last of them lets go (release, drop of
+ * the shared tokens, compaction or copy on write).
+ *
+ * akv_seq_share appends the retained tokens of frozen sequence src with
+ * logical index in [first, first+n), in logical order, to dst at positions
+ * pos + delta without writing anything: each new token holds the source
+ * token's slot (a reference into src's page) and owes the rotation by delta
+ * (akv_seq_lag), which the attention kernels apply where they read the key
+ * (akv_fused_rotation).  On dst, tokens in shared pages are never written in
+ * place: a repos makes them owe the rotation, akv_materialize gives them
+ * private rows (copy on write: K turned by what it owes, V and K_nope
+ * copied), compaction copies them like any visible token, and a drop gives
+ * their slot up at once (akv_seq_tokens then reports -1).  dst's appends go to
+ * its own pages.  Errors: AKV_EINVAL (bad sequence, n < 0), AKV_ESTATE (src not
+ * frozen, dst frozen or released), AKV_ERANGE ([first, first+n) outside src, a
+ * new position outside [0, 2^31), dst too long). */
+akv_status akv_seq_freeze(akv_pool* pool, int32_t seq);
+akv_status akv_seq_share(akv_pool* pool, int32_t src, int32_t first, int32_t n, int32_t dst, int32_t delta);
 
 /* ---- visibility -------------------------------------------------------------- */
 

@@ -69,6 +69,8 @@ SYMBOLS = {
     "akv_seq_lag": [_P, _I, _I, _I, _IP],
     "akv_splice": [_P, _I, _IP, _IP, _I, _P, _P, _P, _IP],
     "akv_seq_clone": [_P, _I, _I, _I, _I, _I],
+    "akv_seq_freeze": [_P, _I],
+    "akv_seq_share": [_P, _I, _I, _I, _I, _I],
     "akv_append_batch": [_P, _I, _IP, _IP, _P, _P, _P, _IP],
     "akv_seq_attention": [_P, _P, _I, _IP, _I, _IP, _I, ctypes.c_float, _P],
     "akv_seq_visible": [_P, _I, _IP, _I, _IP, _I, _IP],
@@ -314,6 +316,12 @@ class Pool:
         out = np.zeros(max(n, 1), np.int32)
         _check(lib().akv_seq_lag(self._h, seq, 0, n, _ptr(out)))
         return out[:n]
+
+    def freeze(self, seq: int) -> None:
+        _check(lib().akv_seq_freeze(self._h, seq))
+
+    def share(self, src: int, first: int, n: int, dst: int, delta: int = 0) -> None:
+        _check(lib().akv_seq_share(self._h, src, first, n, dst, delta))
 
     def clone(self, src: int, first: int, n: int, dst: int, delta: int) -> None:
         """Positional version: append src's retained tokens [first, first+n)

@@ -86,6 +86,15 @@ struct SeqRec {
   std::vector<int32_t> ext_lg_lag;
   bool lg_ok = false;
   bool queued = false;         // waiting in the deferred-compaction queue
+  // Shared pages (akv_seq_share): a frozen sequence is a checkpoint whose
+  // rows never change; other sequences hold tokens whose slots lie in its
+  // pages (foreign slots: the page's owner is another sequence).
+  int32_t id = -1;
+  bool frozen = false;
+  int32_t refs = 0;             // sequences holding slots in this sequence's pages
+  bool zombie = false;          // released while referenced: pages kept until refs reach 0
+  std::unordered_map<int32_t, int32_t> owners;  // owner sequence -> this sequence's tokens in its pages
+  std::unordered_map<int32_t, int32_t> fvis;    // foreign page -> this sequence's visible tokens in it
   void stale() { vis_ok = ext_ok = lg_ok = false; }
 };
 
@@ -565,6 +574,58 @@ akv_status get_seq(akv_pool* p, int32_t s, SeqRec** out) {
   return AKV_OK;
 }
 
+// A sequence whose tokens or rows a call changes: alive and not frozen.
+akv_status get_live_seq(akv_pool* p, int32_t s, SeqRec** out) {
+  akv_status st = get_seq(p, s, out);
+  if (st != AKV_OK) return st;
+  if ((*out)->frozen) return fail(AKV_ESTATE, "sequence %d is frozen (a shared checkpoint)", s);
+  return AKV_OK;
+}
+
+// The slot lies in a page another sequence allocated (a shared page).
+inline bool foreign_slot(const akv_pool* p, int32_t s, int32_t slot) {
+  return slot >= 0 && p->pages[slot >> p->log2S].owner != s;
+}
+
+void note_free(akv_pool* p);
+
+// The pages of a released sequence go back to the free queue, in allocation
+// order (pages waiting in the evictable queue are taken out of it).
+void finish_release(akv_pool* p, int32_t s) {
+  SeqRec& q = p->seqs[s];
+  for (int32_t pg : q.pages) {
+    PageRec& r = p->pages[pg];
+    if (r.in_evict) evict_unlink(p, pg);
+    r.owner = -1;
+    r.nvis = 0;
+    r.filled = 0;
+    r.toks.clear();
+    p->free_q.push_back(pg);
+  }
+  q.pages.clear();
+  q.tail = -1;
+  q.zombie = false;
+  note_free(p);
+}
+
+// A token of q stops holding a slot in another sequence's page.
+void unref(akv_pool* p, SeqRec& q, int32_t slot) {
+  const int32_t o = p->pages[slot >> p->log2S].owner;
+  auto it = q.owners.find(o);
+  if (it == q.owners.end()) return;
+  if (--it->second == 0) {
+    q.owners.erase(it);
+    SeqRec& so = p->seqs[o];
+    if (--so.refs == 0 && so.zombie) finish_release(p, o);
+  }
+}
+
+// q's visible token in foreign page pg stops being visible there.
+void fvis_dec(SeqRec& q, int32_t pg) {
+  auto f = q.fvis.find(pg);
+  if (f != q.fvis.end() && --f->second == 0) q.fvis.erase(f);
+}
+
 akv_status check_spans(const akv_span* sp, int32_t n, int32_t len) {
   if (n < 0) return fail(AKV_EINVAL, "negative span count");
   if (n > 0 && !sp) return fail(AKV_EINVAL, "spans is NULL");
@@ -733,6 +794,7 @@ double fragmentation(const akv_pool* p, const SeqRec& q) {
     const PageRec& r = p->pages[q.pages[i]];
     if (r.nvis > 0) cap += r.filled;
   }
+  for (const auto& f : q.fvis) cap += p->pages[f.first].filled;   // shared pages holding a visible token
   if (cap == 0) return 0.0;
   return 1.0 - (double)q.n_vis / (double)cap;
 }
@@ -1081,13 +1143,17 @@ akv_status compact_plan(akv_pool* p, int32_t s, std::vector<akv::MovePair>& mv) 
     p->pages[dest.back()].toks.reserve(S);
   }
   mv.reserve(mv.size() + nv);
+  std::vector<int32_t> shared_src;   // slots given up in other sequences' pages
   for (int64_t i = 0; i < nv; ++i) {
     const int32_t t = order[i];
     const int32_t dst = dest[i / S] * S + (int32_t)(i % S);
     mv.push_back({q.slot[t], dst});
+    if (foreign_slot(p, s, q.slot[t])) shared_src.push_back(q.slot[t]);
     q.slot[t] = dst;
     p->pages[dest[i / S]].toks.push_back(t);
   }
+  q.fvis.clear();
+  for (int32_t sl : shared_src) unref(p, q, sl);
   for (int64_t i = 0; i < need; ++i) {
     PageRec& r = p->pages[dest[i]];
     const int32_t c = (int32_t)std::min<int64_t>(S, nv - i * S);
@@ -1131,6 +1197,12 @@ void drop_tokens(akv_pool* p, SeqRec& q, int32_t b, int32_t e, bool keep_cache =
     q.dropped[t] = 1;
     q.n_vis -= 1;
     const int32_t pg = q.slot[t] >> p->log2S;
+    if (foreign_slot(p, q.id, q.slot[t])) {   // a shared token gives its slot up at once
+      fvis_dec(q, pg);
+      unref(p, q, q.slot[t]);
+      q.slot[t] = -1;
+      continue;
+    }
     PageRec& r = p->pages[pg];
     r.nvis -= 1;
     if (r.nvis == 0 && pg != q.tail && !r.in_evict) evict_push(p, pg);
@@ -1252,6 +1324,7 @@ void repos_items_append(const akv_pool* p, const SeqRec& q, const std::vector<Ru
     int32_t di = -1;   // looked up at the run's first moved token
     for (int32_t t = r.b; t < r.e; ++t) {
       if (q.dropped[t]) continue;
+      if (foreign_slot(p, q.id, q.slot[t])) continue;   // a shared row is not written: the token owes it
       if (di < 0) {
         auto f = didx.find(r.d);
         if (f == didx.end()) {
@@ -1285,35 +1358,112 @@ void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<Run>& run
   sort_by_first_slot(items, p->L.page_size);
 }
 
-void repos_commit(SeqRec& q, const std::vector<Run>& runs) {
+// Positions after a repos; tokens whose rows are shared pages (not rotated in
+// place) owe the rotation instead, as after a deferred repos.
+void repos_commit(const akv_pool* p, SeqRec& q, const std::vector<Run>& runs, bool owe_shared = true) {
   for (const Run& r : runs)
     for (int32_t t = r.b; t < r.e; ++t)
-      if (!q.dropped[t]) q.pos[t] = (int32_t)(q.pos[t] + r.d);
+      if (!q.dropped[t]) {
+        q.pos[t] = (int32_t)(q.pos[t] + r.d);
+        if (owe_shared && foreign_slot(p, q.id, q.slot[t])) {
+          q.lag[t] = (int32_t)(q.lag[t] + r.d);
+          q.lagging = true;
+          q.lg_ok = false;
+        }
+      }
   if (!runs.empty()) cache_after_move(q);
 }
 
 // Rotate every visible key by the rotation it still owes (one launch) and
 // clear the debt.
+// Slots for existing tokens of s that leave shared pages (tail page first,
+// then fresh pages, as place_tokens).
+void place_existing(akv_pool* p, int32_t s, const std::vector<int32_t>& toks, std::vector<int32_t>& slots_out) {
+  SeqRec& q = p->seqs[s];
+  const int32_t S = p->L.page_size;
+  for (int32_t t : toks) {
+    if (q.tail < 0) q.tail = take_page(p, s);
+    const int32_t pg = q.tail;
+    PageRec& r = p->pages[pg];
+    const int32_t slot = pg * S + r.filled;
+    r.filled += 1;
+    r.nvis += 1;
+    r.toks.push_back(t);
+    if (r.filled == S) q.tail = -1;
+    slots_out.push_back(slot);
+    q.slot[t] = slot;
+  }
+}
+
+// One launch copying rows (all paged arrays) from src to dst slots, the
+// rotated-key part turned by R(delta) (the table row and fp32 formula of an
+// in-place repos; delta 0 copies).
+akv_status device_copy_rows(akv_pool* p, const std::vector<akv::MovePair>& mv, int32_t delta) {
+  if (!p->device || mv.empty()) return AKV_OK;
+  ScratchCursor sc(p, mv.size() * sizeof(akv::MovePair) + (size_t)p->L.d_rope * 4 + 3 * 256);
+  const std::vector<float>& tab = rot_table_rows(p, &delta, 1);
+  void* dv[2];
+  akv_status st = upload_arrays(p, sc, {{mv.data(), mv.size() * sizeof(akv::MovePair)},
+                                        {tab.data(), delta != 0 ? tab.size() * 4 : 0}}, dv);
+  if (st != AKV_OK) return st;
+  st = bg_wait(p);
+  if (st != AKV_OK) return st;
+  KTimer tm(p, AKV_K_CLONE);
+  hipError_t e = move_tokens(p, (const akv::MovePair*)dv[0], (int)mv.size(), delta != 0 ? (const float*)dv[1] : nullptr);
+  tm.done();
+  note_write(p);
+  return check_launch(e, "row copy kernel launch");
+}
+
+// Every visible key of q turned by what it owes: rows of q's own pages in
+// place; rows in shared pages (which other sequences read as they are) are
+// copied with the rotation into slots of q's own (copy on write).
 akv_status materialize_seq(akv_pool* p, SeqRec& q) {
   if (!q.lagging) return AKV_OK;
   std::vector<Run> runs;
+  std::vector<int32_t> cow;
   const int32_t len = (int32_t)q.slot.size();
   for (int32_t t = 0; t < len; ++t) {
     if (q.dropped[t] || q.lag[t] == 0) continue;
+    if (foreign_slot(p, q.id, q.slot[t])) {
+      cow.push_back(t);
+      continue;
+    }
     if (!runs.empty() && runs.back().e == t && runs.back().d == q.lag[t])
       runs.back().e = t + 1;
     else
       runs.push_back({t, t + 1, q.lag[t]});
   }
+  if (!cow.empty() && pages_needed(p, q, (int64_t)cow.size()) > available(p))
+    return fail(AKV_ENOMEM, "copy on write of %zu shared rows: pool exhausted", cow.size());
   std::vector<akv::RotItem> items;
   std::vector<int32_t> deltas;
   repos_items(p, q, runs, items, deltas);
-  akv_status st = scratch_fits(p, rotate_scratch_bytes(p, items.size(), deltas.size(), 1));
+  akv_status st = scratch_fits(p, std::max(rotate_scratch_bytes(p, items.size(), deltas.size(), 1),
+                                           cow.size() * sizeof(akv::MovePair) + (size_t)p->L.d_rope * 4 + 1024));
   if (st != AKV_OK) return st;
   st = device_rotate(p, items, deltas);
   if (st != AKV_OK) return st;
+  if (!cow.empty()) {
+    std::vector<int32_t> old_slots, new_slots;
+    for (int32_t t : cow) old_slots.push_back(q.slot[t]);
+    place_existing(p, q.id, cow, new_slots);
+    // one copy launch per distinct owed rotation
+    std::unordered_map<int32_t, std::vector<akv::MovePair>> by_lag;
+    for (size_t i = 0; i < cow.size(); ++i) by_lag[q.lag[cow[i]]].push_back({old_slots[i], new_slots[i]});
+    for (const auto& kv : by_lag) {
+      st = device_copy_rows(p, kv.second, kv.first);
+      if (st != AKV_OK) return st;
+    }
+    for (size_t i = 0; i < cow.size(); ++i) {
+      fvis_dec(q, old_slots[i] >> p->log2S);
+      unref(p, q, old_slots[i]);
+    }
+    q.stale();
+  }
   for (const Run& r : runs)
     for (int32_t t = r.b; t < r.e; ++t) q.lag[t] = 0;
+  for (int32_t t : cow) q.lag[t] = 0;
   q.lagging = false;
   q.lg_ok = false;
   return AKV_OK;
@@ -1650,6 +1800,7 @@ akv_status akv_seq_create(akv_pool* p, int32_t* seq) {
     return fail(AKV_ENOMEM, "host allocation failed");
   }
   *seq = (int32_t)p->seqs.size() - 1;
+  p->seqs.back().id = *seq;
   return AKV_OK;
 }
 
@@ -1658,17 +1809,13 @@ akv_status akv_seq_release(akv_pool* p, int32_t s) {
   SeqRec* q;
   akv_status st = get_seq(p, s, &q);
   if (st != AKV_OK) return st;
-  for (int32_t pg : q->pages) {
-    PageRec& r = p->pages[pg];
-    if (r.in_evict) evict_unlink(p, pg);
-    r.owner = -1;
-    r.nvis = 0;
-    r.filled = 0;
-    r.toks.clear();
-    p->free_q.push_back(pg);
-  }
-  q->pages.clear();
-  q->tail = -1;
+  // slots this sequence holds in other sequences' pages are given up
+  const int32_t len = (int32_t)q->slot.size();
+  for (int32_t t = 0; t < len; ++t)
+    if (foreign_slot(p, s, q->slot[t])) q->slot[t] = -1;
+  const std::vector<std::pair<int32_t, int32_t>> held(q->owners.begin(), q->owners.end());
+  q->owners.clear();
+  q->fvis.clear();
   q->alive = false;
   if (q->queued) {
     p->compact_q.erase(std::find(p->compact_q.begin(), p->compact_q.end(), s));
@@ -1676,7 +1823,15 @@ akv_status akv_seq_release(akv_pool* p, int32_t s) {
   }
   q->vis.clear();
   q->stale();
-  note_free(p);
+  for (const auto& h : held) {
+    SeqRec& so = p->seqs[h.first];
+    if (--so.refs == 0 && so.zombie) finish_release(p, h.first);
+  }
+  // pages other sequences still read stay until the last of them lets go
+  if (q->refs > 0)
+    q->zombie = true;
+  else
+    finish_release(p, s);
   return AKV_OK;
 }
 
@@ -1685,7 +1840,7 @@ akv_status akv_append(akv_pool* p, int32_t s, const void* K, const void* K_pe, c
   try {
     if (!p) return fail(AKV_EINVAL, "NULL pool");
     SeqRec* q;
-    akv_status st = get_seq(p, s, &q);
+    akv_status st = get_live_seq(p, s, &q);
     if (st != AKV_OK) return st;
     if (n < 0) return fail(AKV_EINVAL, "negative token count");
     if (n == 0) return AKV_OK;
@@ -1722,7 +1877,7 @@ akv_status akv_seq_clone(akv_pool* p, int32_t src, int32_t first, int32_t n, int
     SeqRec* qs;
     SeqRec* qd;
     akv_status st = get_seq(p, src, &qs);
-    if (st == AKV_OK) st = get_seq(p, dst, &qd);
+    if (st == AKV_OK) st = get_live_seq(p, dst, &qd);
     if (st != AKV_OK) return st;
     if (n < 0) return fail(AKV_EINVAL, "negative token count");
     if (first < 0 || (int64_t)first + n > (int64_t)qs->slot.size())
@@ -1784,6 +1939,75 @@ akv_status akv_seq_clone(akv_pool* p, int32_t src, int32_t first, int32_t n, int
   }
 }
 
+akv_status akv_seq_freeze(akv_pool* p, int32_t s) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    SeqRec* q;
+    akv_status st = get_seq(p, s, &q);
+    if (st != AKV_OK) return st;
+    if (q->frozen) return AKV_OK;
+    // sharers read the rows as stored: keys owing a rotation are turned first
+    st = materialize_seq(p, *q);
+    if (st != AKV_OK) return st;
+    q->frozen = true;
+    if (q->queued) {
+      p->compact_q.erase(std::find(p->compact_q.begin(), p->compact_q.end(), s));
+      q->queued = false;
+    }
+    return AKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+akv_status akv_seq_share(akv_pool* p, int32_t src, int32_t first, int32_t n, int32_t dst, int32_t delta) {
+  try {
+    if (!p) return fail(AKV_EINVAL, "NULL pool");
+    SeqRec* qs;
+    SeqRec* qd;
+    akv_status st = get_seq(p, src, &qs);
+    if (st == AKV_OK) st = get_live_seq(p, dst, &qd);
+    if (st != AKV_OK) return st;
+    if (!qs->frozen) return fail(AKV_ESTATE, "sequence %d is not frozen (akv_seq_freeze)", src);
+    if (n < 0) return fail(AKV_EINVAL, "negative token count");
+    if (first < 0 || (int64_t)first + n > (int64_t)qs->slot.size())
+      return fail(AKV_ERANGE, "tokens [%d,%lld) outside sequence %d of %zu tokens", first,
+                  (long long)first + n, src, qs->slot.size());
+    int64_t m = 0;
+    for (int32_t t = first; t < first + n; ++t) {
+      if (qs->dropped[t]) continue;
+      const int64_t np = (int64_t)qs->pos[t] + delta;
+      if (np < 0 || np > kInt32Max)
+        return fail(AKV_ERANGE, "token %d would move to position %lld", t, (long long)np);
+      ++m;
+    }
+    if (m == 0) return AKV_OK;
+    if ((int64_t)qd->slot.size() + m > kInt32Max) return fail(AKV_ERANGE, "sequence too long");
+    // the new tokens hold the source's slots: nothing is written
+    for (int32_t t = first; t < first + n; ++t) {
+      if (qs->dropped[t]) continue;
+      const int32_t slot = qs->slot[t];
+      const int32_t pg = slot >> p->log2S;
+      const int32_t o = p->pages[pg].owner;
+      if (qd->owners[o]++ == 0) p->seqs[o].refs += 1;
+      qd->fvis[pg] += 1;
+      qd->slot.push_back(slot);
+      qd->pos.push_back((int32_t)(qs->pos[t] + delta));
+      qd->dropped.push_back(0);
+      qd->lag.push_back((int32_t)(qs->lag[t] + delta));
+    }
+    qd->n_vis += m;
+    if (delta != 0) {
+      qd->lagging = true;
+      qd->lg_ok = false;
+    }
+    qd->stale();
+    return AKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
 akv_status akv_append_batch(akv_pool* p, int32_t n_seqs, const int32_t* seqs, const int32_t* counts,
                             const void* K, const void* K_pe, const void* V, const int32_t* pos) {
   try {
@@ -1805,7 +2029,7 @@ akv_status akv_append_batch(akv_pool* p, int32_t n_seqs, const int32_t* seqs, co
     int64_t total = 0, pages = 0;
     for (int32_t i = 0; i < n_seqs; ++i) {
       SeqRec* q;
-      akv_status st = get_seq(p, seqs[i], &q);
+      akv_status st = get_live_seq(p, seqs[i], &q);
       if (st != AKV_OK) return st;
       if (counts[i] < 0) return fail(AKV_EINVAL, "entry %d: negative token count", i);
       auto it = st_of.find(seqs[i]);
@@ -1850,7 +2074,7 @@ akv_status akv_drop(akv_pool* p, int32_t s, const akv_span* spans, int32_t n) {
   try {
     if (!p) return fail(AKV_EINVAL, "NULL pool");
     SeqRec* q;
-    akv_status st = get_seq(p, s, &q);
+    akv_status st = get_live_seq(p, s, &q);
     if (st != AKV_OK) return st;
     st = check_spans(spans, n, (int32_t)q->slot.size());
     if (st != AKV_OK) return st;
@@ -1869,7 +2093,7 @@ akv_status akv_compact(akv_pool* p, int32_t s, int32_t force) {
   try {
     if (!p) return fail(AKV_EINVAL, "NULL pool");
     SeqRec* q;
-    akv_status st = get_seq(p, s, &q);
+    akv_status st = get_live_seq(p, s, &q);
     if (st != AKV_OK) return st;
     if (!force && fragmentation(p, *q) <= p->thr) return AKV_OK;
     st = scratch_fits(p, (size_t)q->n_vis * sizeof(akv::MovePair) + 256);
@@ -1966,7 +2190,7 @@ akv_status akv_repos_deferred(akv_pool* p, int32_t s, const akv_span* spans, con
   try {
     if (!p) return fail(AKV_EINVAL, "NULL pool");
     SeqRec* q;
-    akv_status st = get_seq(p, s, &q);
+    akv_status st = get_live_seq(p, s, &q);
     if (st != AKV_OK) return st;
     std::vector<Run> runs;
     st = repos_runs(*q, spans, delta, n, runs);
@@ -1978,7 +2202,7 @@ akv_status akv_repos_deferred(akv_pool* p, int32_t s, const akv_span* spans, con
           q->lagging = true;
         }
     q->lg_ok = false;
-    repos_commit(*q, runs);
+    repos_commit(p, *q, runs, false);
     return AKV_OK;
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
@@ -2014,7 +2238,7 @@ akv_status akv_repos(akv_pool* p, int32_t s, const akv_span* spans, const int32_
   try {
     if (!p) return fail(AKV_EINVAL, "NULL pool");
     SeqRec* q;
-    akv_status st = get_seq(p, s, &q);
+    akv_status st = get_live_seq(p, s, &q);
     if (st != AKV_OK) return st;
     std::vector<Run> runs;
     st = repos_runs(*q, spans, delta, n, runs);
@@ -2026,7 +2250,7 @@ akv_status akv_repos(akv_pool* p, int32_t s, const akv_span* spans, const int32_
     if (st != AKV_OK) return st;
     st = device_rotate(p, items, deltas);
     if (st != AKV_OK) return st;
-    repos_commit(*q, runs);
+    repos_commit(p, *q, runs);
     return AKV_OK;
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
@@ -2047,7 +2271,7 @@ akv_status akv_repos_batch(akv_pool* p, int32_t n_seqs, const int32_t* seqs, con
     int64_t off = 0;
     for (int32_t i = 0; i < n_seqs; ++i) {
       SeqRec* q;
-      akv_status st = get_seq(p, seqs[i], &q);
+      akv_status st = get_live_seq(p, seqs[i], &q);
       if (st != AKV_OK) return st;
       if (!seen.emplace(seqs[i], i).second)
         return fail(AKV_EINVAL, "entries %d and %d name the same sequence %d", seen[seqs[i]], i, seqs[i]);
@@ -2065,7 +2289,7 @@ akv_status akv_repos_batch(akv_pool* p, int32_t n_seqs, const int32_t* seqs, con
     if (st != AKV_OK) return st;
     st = device_rotate(p, items, deltas);
     if (st != AKV_OK) return st;
-    for (int32_t i = 0; i < n_seqs; ++i) repos_commit(p->seqs[seqs[i]], runs[i]);
+    for (int32_t i = 0; i < n_seqs; ++i) repos_commit(p, p->seqs[seqs[i]], runs[i]);
     return AKV_OK;
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
@@ -2079,7 +2303,7 @@ akv_status akv_repos_layers(akv_pool* const* pools, int32_t n_pools, int32_t s, 
     akv_pool* p = pools[0];
     if (!p) return fail(AKV_EINVAL, "NULL pool");
     SeqRec* q;
-    akv_status st = get_seq(p, s, &q);
+    akv_status st = get_live_seq(p, s, &q);
     if (st != AKV_OK) return st;
     std::vector<SeqRec*> qs{q};
     std::vector<akv_pool*> layers{p};
@@ -2113,7 +2337,7 @@ akv_status akv_repos_layers(akv_pool* const* pools, int32_t n_pools, int32_t s, 
     if (st != AKV_OK) return st;
     st = device_rotate(p, items, deltas, layers);
     if (st != AKV_OK) return st;
-    for (SeqRec* r : qs) repos_commit(*r, runs);
+    for (size_t i = 0; i < qs.size(); ++i) repos_commit(layers[i], *qs[i], runs);
     return AKV_OK;
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
@@ -2158,7 +2382,7 @@ akv_status akv_splice(akv_pool* p, int32_t s, const akv_span* spans, const int32
   try {
     if (!p) return fail(AKV_EINVAL, "NULL pool");
     SeqRec* q;
-    akv_status st = get_seq(p, s, &q);
+    akv_status st = get_live_seq(p, s, &q);
     if (st != AKV_OK) return st;
     if (n < 0) return fail(AKV_EINVAL, "negative splice count");
     if (n == 0) return AKV_OK;
@@ -2254,7 +2478,7 @@ akv_status akv_splice(akv_pool* p, int32_t s, const akv_span* spans, const int32
     repos_items(p, *q, runs, items, deltas);
     st = device_rotate(p, items, deltas);
     if (st != AKV_OK) return st;
-    repos_commit(*q, runs);
+    repos_commit(p, *q, runs);
     if (stub_pos_out) std::copy(stub_pos.begin(), stub_pos.end(), stub_pos_out);
     return auto_compact(p, s);
   } catch (const std::bad_alloc&) {

@@ -135,6 +135,16 @@ class _Seq:
         self.pages: List[int] = []              # owned pages in allocation order
         self.tail = -1                          # open (not yet full) page, or -1
         self.alive = True
+        # shared pages: the rotation each token's stored key still owes (a
+        # token reading another sequence's row owes the share's delta), and the
+        # reference bookkeeping of checkpoints and their sharers
+        self.lag = np.zeros(0, np.int64)
+        self.id = -1
+        self.frozen = False
+        self.refs = 0                           # sequences holding slots in this sequence's pages
+        self.zombie = False                     # released while referenced
+        self.owners: dict = {}                  # owner sequence -> this sequence's tokens in its pages
+        self.fvis: dict = {}                    # foreign page -> this sequence's visible tokens in it
         # token log for the dense brute force (only when keep_log)
         self.log_k: List[np.ndarray] = []
         self.log_kpe: List[np.ndarray] = []
@@ -191,7 +201,34 @@ class Pool:
     # -- sequences -----------------------------------------------------------
     def seq_create(self) -> int:
         self.seqs.append(_Seq())
+        self.seqs[-1].id = len(self.seqs) - 1
         return len(self.seqs) - 1
+
+    def _live(self, s: int) -> _Seq:
+        """A sequence a call changes: alive and not frozen."""
+        q = self._seq(s)
+        if q.frozen:
+            raise EState(f"sequence {s} is frozen")
+        return q
+
+    def _foreign(self, q: _Seq, slot: int) -> bool:
+        """The slot lies in a page another sequence allocated (a shared page)."""
+        return slot >= 0 and self.owner[slot // self.S] != q.id
+
+    def _unref(self, q: _Seq, slot: int) -> None:
+        o = int(self.owner[slot // self.S])
+        q.owners[o] -= 1
+        if q.owners[o] == 0:
+            del q.owners[o]
+            so = self.seqs[o]
+            so.refs -= 1
+            if so.refs == 0 and so.zombie:
+                self._finish_release(o)
+
+    def _fvis_dec(self, q: _Seq, page: int) -> None:
+        q.fvis[page] -= 1
+        if q.fvis[page] == 0:
+            del q.fvis[page]
 
     def _seq(self, s: int) -> _Seq:
         if not (0 <= s < len(self.seqs)):
@@ -204,8 +241,30 @@ class Pool:
     def seq_release(self, s: int) -> None:
         """Return every page the sequence still owns to the back of the free
         queue, in allocation order (pages waiting in the evictable queue are
-        taken out of it)."""
+        taken out of it).  Slots it holds in other sequences' pages are given
+        up; while other sequences still hold slots in its pages, those pages
+        stay until the last of them lets go."""
         q = self._seq(s)
+        for t in range(q.n):
+            if self._foreign(q, int(q.slot[t])):
+                q.slot[t] = -1
+        held = list(q.owners.items())
+        q.owners, q.fvis = {}, {}
+        q.alive = False
+        if s in self.queue:
+            self.queue.remove(s)
+        for o, _ in held:
+            so = self.seqs[o]
+            so.refs -= 1
+            if so.refs == 0 and so.zombie:
+                self._finish_release(o)
+        if q.refs > 0:
+            q.zombie = True
+        else:
+            self._finish_release(s)
+
+    def _finish_release(self, s: int) -> None:
+        q = self.seqs[s]
         for p in q.pages:
             if self.in_evict[p]:
                 self.evictable.remove(p)
@@ -216,9 +275,100 @@ class Pool:
             self.free.append(p)
         q.pages = []
         q.tail = -1
-        q.alive = False
+        q.zombie = False
+
+    # -- shared pages ([AKV-blog] section 3: copy-on-write page-table references;
+    # [AKV-notes] section 3, Cache Management: re-use by key rotation) ---------------
+    def freeze(self, s: int) -> None:
+        """Make s a checkpoint whose rows never change (keys owing a rotation
+        are turned first)."""
+        q = self._seq(s)
+        if q.frozen:
+            return
+        self.materialize(s)
+        q.frozen = True
         if s in self.queue:
             self.queue.remove(s)
+
+    def share(self, src: int, first: int, n: int, dst: int, delta: int) -> None:
+        """Append the retained tokens of frozen src in [first, first+n) to dst
+        at pos + delta, each holding the source token's slot and owing the
+        rotation by delta; nothing is written."""
+        qs = self._seq(src)
+        qd = self._live(dst)
+        if not qs.frozen:
+            raise EState("the source of a share must be frozen")
+        if n < 0:
+            raise EInval("negative token count")
+        if first < 0 or first + n > qs.n:
+            raise ERange("share range outside the source sequence")
+        t = np.arange(first, first + n, dtype=np.int64)
+        t = t[~qs.dropped[t]]
+        if len(t) == 0:
+            return
+        newpos = qs.pos[t] + int(delta)
+        if np.any(newpos < 0) or np.any(newpos > INT32_MAX):
+            raise ERange("shared position out of range")
+        for k in t:
+            slot = int(qs.slot[k])
+            o = int(self.owner[slot // self.S])
+            if qd.owners.get(o, 0) == 0:
+                self.seqs[o].refs += 1
+            qd.owners[o] = qd.owners.get(o, 0) + 1
+            qd.fvis[slot // self.S] = qd.fvis.get(slot // self.S, 0) + 1
+        qd.slot = np.concatenate([qd.slot, qs.slot[t]])
+        qd.pos = np.concatenate([qd.pos, newpos])
+        qd.dropped = np.concatenate([qd.dropped, np.zeros(len(t), bool)])
+        qd.lag = np.concatenate([qd.lag, qs.lag[t] + int(delta)])
+
+    def materialize(self, s: int) -> None:
+        """Turn every visible key by what it owes: rows of s's own pages in
+        place; rows in shared pages are copied, turned, into slots of s's own
+        (copy on write)."""
+        q = self._seq(s)
+        vis = np.nonzero(~q.dropped & (q.lag != 0))[0]
+        own = [int(t) for t in vis if not self._foreign(q, int(q.slot[t]))]
+        cow = [int(t) for t in vis if self._foreign(q, int(q.slot[t]))]
+        if cow and self._pages_needed(q, len(cow)) > self._available():
+            raise ENoMem("pool exhausted")
+        if own:
+            self._rotate_tokens(q, np.asarray(own, np.int64), q.lag[own].astype(np.float64))
+        if cow:
+            S = self.S
+            old = q.slot[cow].copy()
+            new = self._place_existing(s, cow)
+            sp, so_ = old // S, old % S
+            dp, do = new // S, new % S
+            rot = self.kr[sp, :, so_, :]
+            self.kr[dp, :, do, :] = self._store(rotate(rot, np.broadcast_to(q.lag[cow].astype(np.float64)[:, None],
+                                                                            rot.shape[:2]),
+                                                       self.inv_freq, self.L.pairing))
+            if self.kn is not None:
+                self.kn[dp, :, do, :] = self.kn[sp, :, so_, :]
+            self.v[dp, :, do, :] = self.v[sp, :, so_, :]
+            for sl in old:
+                self._fvis_dec(q, int(sl) // S)
+                self._unref(q, int(sl))
+        q.lag[vis] = 0
+
+    def _place_existing(self, s: int, toks) -> np.ndarray:
+        """New slots of s's own for existing tokens (tail page first, then
+        fresh pages, as for an append)."""
+        q = self.seqs[s]
+        S = self.S
+        out = []
+        for t in toks:
+            if q.tail < 0:
+                q.tail = self._take_page(s)
+            p = q.tail
+            slot = p * S + int(self.filled[p])
+            self.filled[p] += 1
+            self.nvis[p] += 1
+            if self.filled[p] == S:
+                q.tail = -1
+            q.slot[t] = slot
+            out.append(slot)
+        return np.asarray(out, np.int64)
 
     # -- allocation ------------------------------------------------------------
     def _available(self) -> int:
@@ -285,7 +435,7 @@ class Pool:
         return k, kpe, v
 
     def append(self, s: int, pos, k, kpe, v) -> None:
-        q = self._seq(s)
+        q = self._live(s)
         L = self.L
         pos = np.asarray(pos, np.int64)
         n = len(pos)
@@ -307,6 +457,7 @@ class Pool:
         q.slot = np.concatenate([q.slot, slots])
         q.pos = np.concatenate([q.pos, pos])
         q.dropped = np.concatenate([q.dropped, np.zeros(n, bool)])
+        q.lag = np.concatenate([q.lag, np.zeros(n, np.int64)])
         if self.keep_log:
             q.log_k.append(k.copy())
             q.log_kpe.append(None if kpe is None else np.asarray(kpe, np.float64).copy())
@@ -331,6 +482,11 @@ class Pool:
                 continue
             q.dropped[t] = True
             p = q.slot[t] // S
+            if self._foreign(q, int(q.slot[t])):     # a shared token gives its slot up at once
+                self._fvis_dec(q, int(p))
+                self._unref(q, int(q.slot[t]))
+                q.slot[t] = -1
+                continue
             self.nvis[p] -= 1
             if self.nvis[p] == 0 and p != q.tail and not self.in_evict[p]:
                 self.evictable.append(p)
@@ -340,7 +496,7 @@ class Pool:
         """Mark logical spans [b, e) inactive.  Nothing is freed or rewritten;
         pages left without a visible token join the evictable queue (in the
         order their last visible token is dropped)."""
-        q = self._seq(s)
+        q = self._live(s)
         sp = self._check_spans(spans, q.n)
         for b, e in sp:
             self._drop_tokens(q, range(int(b), int(e)))
@@ -351,7 +507,7 @@ class Pool:
     def fragmentation(self, s: int) -> float:
         """1 - visible tokens / written slots of the pages holding a visible token."""
         q = self._seq(s)
-        ref = [p for p in q.pages if self.nvis[p] > 0]
+        ref = [p for p in q.pages if self.nvis[p] > 0] + list(q.fvis)
         cap = int(sum(self.filled[p] for p in ref))
         if cap == 0:
             return 0.0
@@ -374,7 +530,7 @@ class Pool:
         """Copy every visible token, in visible-list order, into fresh pages
         taken from the allocator; the old pages join the evictable queue in
         allocation order.  Values are copied unchanged."""
-        q = self._seq(s)
+        q = self._live(s)
         if not force and self.fragmentation(s) <= self.compact_threshold:
             return
         order = self.visible(s)
@@ -393,7 +549,11 @@ class Pool:
         if self.kn is not None:
             self.kn[dp, :, do, :] = self.kn[sp, :, so, :]
         self.v[dp, :, do, :] = self.v[sp, :, so, :]
+        shared = [int(x) for x in src if self._foreign(q, int(x))]
         q.slot[order] = new
+        q.fvis = {}
+        for x in shared:
+            self._unref(q, x)
         for i, p in enumerate(dest):
             c = min(S, nv - i * S)
             self.filled[p] = c
@@ -462,12 +622,20 @@ class Pool:
         return round_bf16(k) if self.key_store == "bf16" else k
 
     def repos(self, s: int, spans, deltas) -> None:
-        q = self._seq(s)
+        q = self._live(s)
         tot = self.repos_deltas(s, spans, deltas)
         t = np.nonzero(tot)[0]
         if len(t):
-            self._rotate_tokens(q, t, tot[t])
+            shared = np.array([self._foreign(q, int(q.slot[k])) for k in t], bool)
+            if np.any(~shared):
+                self._rotate_tokens(q, t[~shared], tot[t[~shared]])
+            q.lag[t[shared]] += tot[t[shared]]     # a shared row is not written: the token owes it
             q.pos[t] += tot[t]
+
+    def rotated_in_place(self, s: int, tokens) -> np.ndarray:
+        """Which of the tokens a repos rotates in place (not shared rows)."""
+        q = self.seqs[s]
+        return np.array([not self._foreign(q, int(q.slot[k])) for k in tokens], bool)
 
     # -- positional version ([AKV-notes] section 3, Cache Management) ------------------
     def clone(self, src: int, first: int, n: int, dst: int, delta: int) -> None:
@@ -477,7 +645,7 @@ class Pool:
         logical order, at positions pos + delta, with their rotated key part
         turned by R(delta) and every other row copied.  src is left as it is."""
         qs = self._seq(src)
-        self._seq(dst)
+        self._live(dst)
         if n < 0:
             raise EInval("negative token count")
         if first < 0 or first + n > qs.n:
@@ -494,10 +662,13 @@ class Pool:
         kr = self.kr[pg, :, off, :]
         kr = self._store(rotate(kr, np.full(kr.shape[:2], float(delta)), self.inv_freq, self.L.pairing))
         v = self.v[pg, :, off, :].copy()
+        lag = qs.lag[t].copy()
         if self.L.mla:
             self.append(dst, newpos, self.kn[pg, :, off, :].copy(), kr, v)
         else:
             self.append(dst, newpos, kr, None, v)
+        qd = self.seqs[dst]
+        qd.lag[qd.n - len(t):] = lag      # the copies owe what their sources owe
 
     # -- splice ([Leyline] Method, AMORTIZE mode) ---------------------------------------
     def splice_plan(self, s: int, spans, stub_lens):
@@ -538,7 +709,7 @@ class Pool:
         """Drop each span, append its stub at the span's start position, and
         move every downstream visible token by the summed deltas of the
         splices before it (one rotation per token).  Returns stub positions."""
-        q = self._seq(s)
+        q = self._live(s)
         vis, dj, stub_pos, down = self.splice_plan(s, spans, stub_lens)
         sp = np.asarray(spans, np.int64).reshape(-1, 2)
         n_stub = len(stub_pos)
@@ -558,8 +729,12 @@ class Pool:
         moved = moved[keep[moved]]
         if len(moved):
             t = vis[moved]
-            self._rotate_tokens(q, t, down[moved])
-            q.pos[t] += down[moved]
+            d = down[moved]
+            shared = np.array([self._foreign(q, int(q.slot[k])) for k in t], bool)
+            if np.any(~shared):
+                self._rotate_tokens(q, t[~shared], d[~shared])
+            q.lag[t[shared]] += d[shared]
+            q.pos[t] += d
         self._auto_compact(s)
         return stub_pos
 
@@ -606,14 +781,24 @@ class Pool:
         return np.asarray(out, np.int64).reshape(-1, 3)
 
     # -- gathers -----------------------------------------------------------------------
-    def gather(self, extents):
+    def visible_lag(self, s: int, mask_spans=None) -> np.ndarray:
+        """The rotation each entry of the visible list still owes, in list order."""
+        return self.seqs[s].lag[self.visible(s, mask_spans)]
+
+    def gather(self, extents, lag=None):
         """K (d_qk = d_nope + d_rope per head) and V rows of an extent list,
-        in list order: K [L, Hkv, d_qk], V [L, Hkv, d_v]."""
+        in list order: K [L, Hkv, d_qk], V [L, Hkv, d_v].  lag (optional, one
+        per entry): the rotation each stored key still owes, applied here (the
+        key as attention sees it; stored once in bf16 with key_store bf16)."""
         L = self.L
         ex = np.asarray(extents, np.int64).reshape(-1, 3)
         pg = np.concatenate([np.full(h - l, p) for p, l, h in ex]) if len(ex) else np.zeros(0, np.int64)
         of = np.concatenate([np.arange(l, h) for p, l, h in ex]) if len(ex) else np.zeros(0, np.int64)
         kr = self.kr[pg, :, of, :]
+        if lag is not None and np.any(np.asarray(lag) != 0):
+            lag = np.asarray(lag, np.float64)
+            turned = self._store(rotate(kr, np.broadcast_to(lag[:, None], kr.shape[:2]), self.inv_freq, L.pairing))
+            kr = np.where((lag != 0)[:, None, None], turned, kr)
         if L.mla:
             kn = self.kn[pg, :, of, :]
             kr = np.broadcast_to(kr, (len(pg), L.n_kv_heads, L.d_rope))
@@ -641,7 +826,7 @@ def last_visible(lkv: int, lq: int, i: np.ndarray) -> np.ndarray:
 
 
 def segment_attention(pool: Pool, q: np.ndarray, segments, page_lists, scale: float = 0.0,
-                      rows: Optional[dict] = None, heads=None) -> np.ndarray:
+                      rows: Optional[dict] = None, heads=None, lags=None) -> np.ndarray:
     """Causal attention of each query segment over its own KV list.
 
     q: [Nq, Hq, d_qk] fp64.  segments: iterable of (q_begin, q_len, ext_begin,
@@ -650,7 +835,8 @@ def segment_attention(pool: Pool, q: np.ndarray, segments, page_lists, scale: fl
     head h reads kv head floor(h * Hkv / Hq).  Returns [Nq, Hq, d_v] with NaN
     in rows no segment covers.  `rows` optionally maps a segment index to the
     local query rows to evaluate (sampling); `heads` optionally lists the q
-    heads to evaluate (the others stay NaN)."""
+    heads to evaluate (the others stay NaN); `lags` optionally gives every
+    list entry's owed rotation (concatenated over segments in list order)."""
     L = pool.L
     q = np.asarray(q, np.float64)
     nq = q.shape[0]
@@ -662,7 +848,12 @@ def segment_attention(pool: Pool, q: np.ndarray, segments, page_lists, scale: fl
     for si, (qb, ql, eb, el) in enumerate(segments):
         if ql == 0:
             continue
-        k, v = pool.gather(ex_all[eb:eb + el])
+        seg_lag = None
+        if lags is not None:
+            off = int(sum((ex_all[:eb, 2] - ex_all[:eb, 1]).tolist()))
+            n_e = int((ex_all[eb:eb + el, 2] - ex_all[eb:eb + el, 1]).sum())
+            seg_lag = np.asarray(lags)[off:off + n_e]
+        k, v = pool.gather(ex_all[eb:eb + el], seg_lag)
         lkv = k.shape[0]
         if lkv < ql:
             raise EInval("segment has fewer KV entries than queries")

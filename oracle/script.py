@@ -8,7 +8,7 @@ and the attention outputs.
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import Dict, List, Optional
+from typing import Callable, Dict, List, Optional
 
 import numpy as np
 
@@ -53,6 +53,12 @@ def apply_op(pool: Pool, op) -> Optional[np.ndarray]:
         pool.compact(op.seq, bool(op.force))
     elif isinstance(op, W.Clone):
         pool.clone(op.src, op.first, op.n, op.dst, op.delta)
+    elif isinstance(op, W.Freeze):
+        pool.freeze(op.seq)
+    elif isinstance(op, W.Share):
+        pool.share(op.src, op.first, op.n, op.dst, op.delta)
+    elif isinstance(op, W.Materialize):
+        pool.materialize(op.seq)
     elif isinstance(op, W.ReposBatch):
         # the same as one repos per entry, in entry order
         for seq, spans, deltas in op.entries():
@@ -68,31 +74,42 @@ def apply_op(pool: Pool, op) -> Optional[np.ndarray]:
     return None
 
 
-def segment_lists(pool: Pool, segments):
-    """Concatenated extents and (q_begin, q_len, ext_begin, ext_len) rows."""
-    exts, rows, eb = [], [], 0
+def segment_lists(pool: Pool, segments, with_lags: bool = False):
+    """Concatenated extents and (q_begin, q_len, ext_begin, ext_len) rows
+    (and, with_lags, every list entry's owed rotation)."""
+    exts, rows, lags, eb = [], [], [], 0
     for sg in segments:
-        ex = pool.extents(sg.seq, sg.mask_spans if len(sg.mask_spans) else None)
+        m = sg.mask_spans if len(sg.mask_spans) else None
+        ex = pool.extents(sg.seq, m)
         exts.append(ex)
+        lags.append(pool.visible_lag(sg.seq, m))
         rows.append((sg.q_begin, sg.q_len, eb, len(ex)))
         eb += len(ex)
     ex = np.concatenate(exts) if exts else np.zeros((0, 3), np.int64)
+    if with_lags:
+        return ex, rows, (np.concatenate(lags) if lags else np.zeros(0, np.int64))
     return ex, rows
 
 
 def run_workload(wl: W.Workload, keep_log: bool = False, attention: bool = True,
         sample_rows: Optional[Dict[int, np.ndarray]] = None, stop_before_attention: bool = False,
-        key_store: str = "fp64") -> OracleRun:
+        key_store: str = "fp64", materialize_at: Optional[Callable[[W.Attention], bool]] = None) -> OracleRun:
+    """materialize_at(op) True: every segment's sequence is materialized
+    before that attention (the launch that rotates owed keys in place first)."""
     pool = Pool(wl.layout, wl.page_order, keep_log=keep_log, key_store=key_store)
     res = OracleRun(pool)
     for op in wl.ops:
         if isinstance(op, W.Attention):
             if stop_before_attention:
                 break
-            ex, rows = segment_lists(pool, op.segments)
+            if materialize_at is not None and materialize_at(op):
+                for sg in op.segments:
+                    pool.materialize(sg.seq)
+            ex, rows, lags = segment_lists(pool, op.segments, with_lags=True)
             rec = dict(extents=ex, segments=rows)
             if attention:
-                rec["out"] = AO.segment_attention(pool, W.bf16_to_f64(op.q), rows, ex, op.scale, rows=sample_rows)
+                rec["out"] = AO.segment_attention(pool, W.bf16_to_f64(op.q), rows, ex, op.scale, rows=sample_rows,
+                                                  lags=lags)
             res.attention.append(rec)
         else:
             sp = apply_op(pool, op)

@@ -70,6 +70,12 @@ def apply_op(pool: akv.Pool, op, keep=None):
         pool.compact(op.seq, bool(op.force))
     elif isinstance(op, W.Clone):
         pool.clone(op.src, op.first, op.n, op.dst, op.delta)
+    elif isinstance(op, W.Freeze):
+        pool.freeze(op.seq)
+    elif isinstance(op, W.Share):
+        pool.share(op.src, op.first, op.n, op.dst, op.delta)
+    elif isinstance(op, W.Materialize):
+        pool.materialize(op.seq)
     elif isinstance(op, W.ReposBatch):
         pool.repos_batch(list(op.entries()))
     elif isinstance(op, W.CompactMode):
@@ -86,17 +92,22 @@ def apply_op(pool: akv.Pool, op, keep=None):
 def run(wl: W.Workload, pool: akv.Pool | None = None, **kw):
     pool = pool if pool is not None else make_pool(wl, **kw)
     keep, outs = [], []
-    deferred = any(isinstance(o, W.Repos) and o.deferred for o in wl.ops)
+    # keys that owe a rotation (deferred repos, shared rows): attention over
+    # sequence ids, which applies what each key owes
+    deferred = any((isinstance(o, W.Repos) and o.deferred) or isinstance(o, W.Share) for o in wl.ops)
     for op in wl.ops:
         if isinstance(op, W.Attention):
-            rows, ex = segment_inputs(pool, op)
             q = dev_bf16(op.q)
             keep.append(q)
             if deferred:   # keys owe rotations: the library applies them
                 out = pool.seq_attention(q, [(sg.seq, sg.q_begin, sg.q_len,
                                               sg.mask_spans if len(sg.mask_spans) else None)
                                              for sg in op.segments], op.scale)
+                # the lists the launch read (a launch that materializes first
+                # can move rows of shared pages)
+                rows, ex = segment_inputs(pool, op)
             else:
+                rows, ex = segment_inputs(pool, op)
                 out = pool.segment_attention(q, rows, ex, op.scale)
             outs.append(dict(segments=rows, extents=ex, out=out))
         else:

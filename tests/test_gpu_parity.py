@@ -503,18 +503,38 @@ def test_seq_attention_equals_segment_attention(make):
 # ---------------------------------------------------------------------------
 # deferred repos: keys owe their rotation, the decode kernel turns them
 # ---------------------------------------------------------------------------
-def _deferred_parity(wl, pool=None):
+def _fuses(wl, mode):
+    """Whether an attention launch turns owed keys as it reads them (the
+    rule akv_fused_rotation states): otherwise each sequence of the launch
+    is materialized first, rows in shared pages by copy on write."""
+    L = wl.layout
+    G = L.n_q_heads // L.n_kv_heads
+
+    def f(op):
+        if mode == "never" or not (L.d_nope == 0 and L.d_rope == 128 and L.d_v == 128):
+            return False
+        if max(sg.q_len for sg in op.segments) * G <= 16 or mode == "always":
+            return True
+        seqs = [sg.seq for sg in op.segments]
+        return all(sg.q_len * G <= 256 for sg in op.segments) and len(set(seqs)) == len(seqs)
+    return f
+
+
+def _deferred_parity(wl, pool=None, mode="auto"):
     """Attention against the oracle (its keys rotated eagerly), then every
     sequence materialized and its stored keys against the oracle's."""
     pool, outs = D.run(wl, pool=pool)
-    res = oracle.run_workload(wl, key_store=_key_store(wl))
+    fuses = _fuses(wl, mode)
+    res = oracle.run_workload(wl, key_store=_key_store(wl), materialize_at=lambda op: not fuses(op))
     _check_tables(pool, res.pool)
     wa, wr = _check_attention(outs, res, wl)
     for s, q in enumerate(res.pool.seqs):
         if q.alive:
             pool.materialize(s)
+            res.pool.materialize(s)     # the oracle's shared rows owe their turn too
             assert not pool.lag(s)[~pool.tokens(s)[2]].any()
     torch.cuda.synchronize()
+    _check_tables(pool, res.pool)
     wk = _check_visible_kv(pool, res.pool, wl.layout)
     _say(f"[gpu] {wl.name} deferred: attention abs err {wa:.2e}, rel L2 {wr:.2e}, keys after materialize {wk:.2e}")
     return pool
@@ -708,7 +728,7 @@ def test_prefill_fused_rotation_full(seed, pairing, mode):
     assert any(isinstance(o, W.Repos) for o in wl.ops)
     pool = D.make_pool(wl)
     pool.fused_rotation(mode)
-    _deferred_parity(wl, pool).close()
+    _deferred_parity(wl, pool, mode).close()
 
 
 @pytest.mark.parametrize("pairing", [0, 1])
@@ -754,3 +774,75 @@ def test_background_compaction_beside_decode_full(seed):
     queues, every visible K/V row and every output row against the oracle."""
     _full_parity(W.decode_with_idle(seed, n_req=12, n_idle=4, idle_ctx=6000, ctx_lo=2000, ctx_hi=6000,
                                     attend_idle=True))
+
+
+# ---------------------------------------------------------------------------
+# shared pages: frozen checkpoints re-used at other positions
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("mode", ["auto", "always", "never"])
+def test_share_scripts_full(seed, mode):
+    """A frozen checkpoint shared by two sequences at other positions (its
+    rows owed the turn), drops and repos across shared and own rows,
+    compaction or copy on write, the source released while shared, a clone
+    of a sharer: one launch over three sequences, every output row against
+    the oracle; then each sequence materialized and its keys against the
+    oracle's."""
+    wl = W.share_fuzz(seed, mla=seed == 3, page_size=[16, 8, 4, 16][seed], d=[64, 128, 128, 64][seed],
+                      materialize=[True, False, None, True][seed])
+    pool = D.make_pool(wl)
+    pool.fused_rotation(mode)
+    _deferred_parity(wl, pool, mode).close()
+
+
+@pytest.mark.parametrize("mla", [False, True])
+def test_share_writes_nothing_and_copy_on_write_keeps_the_source(mla):
+    """share writes no row of the pool; a sharer's repos and materialize
+    leave every row of the frozen source bit for bit as it was, and the
+    sharer's materialized keys equal those of a clone at the same delta
+    (bit for bit: the same table and rounding)."""
+    lay = (W.Layout(4, 4, 32, 32, 32, 8, 64, rope_theta=1e4) if mla else
+           W.Layout(8, 2, 0, 128, 128, 8, 64, rope_theta=1e4))
+    rng = np.random.default_rng(11)
+    wl = W.Workload("share_cow", lay, rng.permutation(lay.num_pages).astype(np.int32), [])
+    pool = D.make_pool(wl)
+    a, b, c = pool.seq_create(), pool.seq_create(), pool.seq_create()
+    n = 90
+    k = D.dev_bf16(W.to_bf16(rng.normal(size=(n, lay.n_rope_heads, lay.d_rope)).astype(np.float32)))
+    kn = D.dev_bf16(W.to_bf16(rng.normal(size=(n, lay.n_kv_heads, lay.d_nope)).astype(np.float32))) if mla else None
+    v = D.dev_bf16(W.to_bf16(rng.normal(size=(n, lay.n_kv_heads, lay.d_v)).astype(np.float32)))
+    if mla:
+        pool.append(a, np.arange(n), kn, k, v)
+    else:
+        pool.append(a, np.arange(n), k, None, v)
+    pool.freeze(a)
+    torch.cuda.synchronize()
+    snap = [t.clone() for t in (pool.k_pages, pool.v_pages) + ((pool.kpe_pages,) if mla else ())]
+    pool.share(a, 10, 70, b, 333)
+    torch.cuda.synchronize()
+    after = (pool.k_pages, pool.v_pages) + ((pool.kpe_pages,) if mla else ())
+    for s0, s1 in zip(snap, after):
+        assert torch.equal(s0.view(torch.int16), s1.view(torch.int16)), "share wrote the pool"
+    pool.repos(b, [[20, 70]], [-7])          # shared rows: owed, not written
+    pool.materialize(b)                      # copy on write
+    pool.clone(a, 10, 70, c, 333)
+    pool.repos(c, [[20, 70]], [-7])
+    torch.cuda.synchronize()
+    sa = pool.tokens(a)[0]
+    pa = torch.as_tensor(np.unique(sa // lay.page_size), dtype=torch.long, device=snap[0].device)
+    for s0, s1 in zip(snap, after):
+        # every row of a's pages as it was (b's copies went to b's own pages)
+        assert torch.equal(s0[pa].view(torch.int16), s1[pa].view(torch.int16))
+    sb, sc = pool.tokens(b)[0], pool.tokens(c)[0]
+    assert not np.isin(sb, pool.tokens(a)[0]).any(), "materialize left shared slots"
+    np.testing.assert_array_equal(pool.lag(b), 0)
+    kr = pool.kpe_pages if mla else pool.k_pages
+    pb, ob = (torch.as_tensor(x, dtype=torch.long, device=kr.device) for x in (sb // lay.page_size, sb % lay.page_size))
+    pc, oc = (torch.as_tensor(x, dtype=torch.long, device=kr.device) for x in (sc // lay.page_size, sc % lay.page_size))
+    # c's keys were turned twice (333, then -7 on part): b's once per distinct owed delta
+    kb, kc = D.to_f64(kr[pb, :, ob]), D.to_f64(kr[pc, :, oc])
+    np.testing.assert_array_equal(kb[:20], kc[:20])      # one turn by 333 on both
+    err = np.linalg.norm(kb - kc, axis=-1) / np.maximum(np.linalg.norm(kc, axis=-1), 1e-30)
+    assert err.max() <= 2 * RTOL_KEY
+    np.testing.assert_array_equal(D.to_f64(pool.v_pages[pb, :, ob]), D.to_f64(pool.v_pages[pc, :, oc]))
+    pool.close()

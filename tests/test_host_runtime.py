@@ -61,15 +61,18 @@ def _compare(hp, op_pool, tag=""):
         np.testing.assert_array_equal(slot, q.slot, err_msg=tag)
         np.testing.assert_array_equal(pos, q.pos, err_msg=tag)
         np.testing.assert_array_equal(dropped, q.dropped, err_msg=tag)
+        np.testing.assert_array_equal(hp.lag(s), q.lag, err_msg=tag)
         np.testing.assert_array_equal(hp.visible(s), op_pool.extents(s).reshape(-1, 3), err_msg=tag)
         n, nv, frag = hp.info(s)
         assert nv == int(np.count_nonzero(~q.dropped))
         assert frag == pytest.approx(op_pool.fragmentation(s), abs=1e-12)
 
 
-def _oracle_repos_pairs(op_pool, s, spans, deltas):
+def _oracle_repos_pairs(op_pool, s, spans, deltas, inplace=None):
     q = op_pool.seqs[s]
     tot = op_pool.repos_deltas(s, spans, deltas)
+    if inplace is not None:
+        tot = np.where(inplace, tot, 0)
     t = np.nonzero(tot)[0]
     return sorted(zip(q.slot[t].tolist(), tot[t].tolist()))
 
@@ -92,17 +95,20 @@ def _replay(wl: W.Workload, check_every_op=True):
             oracle.apply_op(op_pool, op)
         elif isinstance(op, W.Repos):
             slot, delta = hp.repos_plan(op.seq, op.spans, op.deltas)
-            assert sorted(zip(slot.tolist(), delta.tolist())) == _oracle_repos_pairs(op_pool, op.seq, op.spans, op.deltas), tag
+            owed = op_pool.repos_deltas(op.seq, op.spans, op.deltas)
+            # rows in shared pages are not written: those tokens owe the turn
+            inplace = op_pool.rotated_in_place(op.seq, np.arange(len(owed)))
+            assert sorted(zip(slot.tolist(), delta.tolist())) == _oracle_repos_pairs(
+                op_pool, op.seq, op.spans, op.deltas, inplace), tag
             assert len(set(slot.tolist())) == len(slot), "a slot rotated twice"
+            before = hp.lag(op.seq)
             if op.deferred:
-                owed = op_pool.repos_deltas(op.seq, op.spans, op.deltas)
-                before = hp.lag(op.seq)
                 hp.repos_deferred(op.seq, op.spans, op.deltas)
                 np.testing.assert_array_equal(hp.lag(op.seq), before + owed[:len(before)], err_msg=tag)
             else:
-                before = hp.lag(op.seq)
                 hp.repos(op.seq, op.spans, op.deltas)
-                np.testing.assert_array_equal(hp.lag(op.seq), before, err_msg=tag)
+                np.testing.assert_array_equal(hp.lag(op.seq), before + np.where(inplace, 0, owed)[:len(before)],
+                                              err_msg=tag)
             oracle.apply_op(op_pool, op)
         elif isinstance(op, W.ReposBatch):
             hp.repos_batch(list(op.entries()))
@@ -116,6 +122,15 @@ def _replay(wl: W.Workload, check_every_op=True):
             oracle.apply_op(op_pool, op)
         elif isinstance(op, W.Clone):
             hp.clone(op.src, op.first, op.n, op.dst, op.delta)
+            oracle.apply_op(op_pool, op)
+        elif isinstance(op, W.Freeze):
+            hp.freeze(op.seq)
+            oracle.apply_op(op_pool, op)
+        elif isinstance(op, W.Share):
+            hp.share(op.src, op.first, op.n, op.dst, op.delta)
+            oracle.apply_op(op_pool, op)
+        elif isinstance(op, W.Materialize):
+            hp.materialize(op.seq)
             oracle.apply_op(op_pool, op)
         elif isinstance(op, (W.CompactMode, W.Release)):
             if isinstance(op, W.CompactMode):
@@ -678,3 +693,50 @@ def test_decode_with_idle_compaction_bit_exact():
     hp, op = _replay(head)
     assert op.queue and list(op.queue) == hp.compact_queue()      # the idle sequences wait for the pass
     _replay(wl)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_share_scripts_bit_exact(seed):
+    """Frozen checkpoints shared at other positions, drops and repos over
+    shared rows, compaction or copy on write, release of a shared source:
+    tables, owed rotations and queues equal the oracle's after every op."""
+    _replay(W.share_fuzz(seed, mla=seed % 3 == 2, page_size=[16, 8, 4, 1, 64][seed % 5],
+                         materialize=[None, True, False][seed % 3]))
+
+
+def test_share_rules():
+    """What sharing refuses and what release of a shared source keeps."""
+    lay = W.Layout(8, 2, 0, 64, 64, 4, 32)
+    hp = _host_pool(lay, None)
+    a, b, c = hp.seq_create(), hp.seq_create(), hp.seq_create()
+    hp.append(a, np.arange(10))
+    with pytest.raises(akv.AkvError) as ei:         # source not frozen
+        hp.share(a, 0, 10, b, 5)
+    assert ei.value.status == akv.AKV_ESTATE
+    hp.freeze(a)
+    for call in (lambda: hp.append(a, [50]), lambda: hp.drop(a, [[0, 1]]), lambda: hp.repos(a, [[0, 1]], [1]),
+                 lambda: hp.compact(a, True), lambda: hp.clone(b, 0, 0, a, 0)):
+        with pytest.raises(akv.AkvError) as ei:
+            call()
+        assert ei.value.status == akv.AKV_ESTATE
+    with pytest.raises(akv.AkvError) as ei:
+        hp.share(a, 5, 10, b, 0)
+    assert ei.value.status == akv.AKV_ERANGE
+    with pytest.raises(akv.AkvError) as ei:
+        hp.share(a, 0, 10, b, -1)                   # position -1
+    assert ei.value.status == akv.AKV_ERANGE
+    assert hp.info(b)[0] == 0, "a refused share left tokens"
+    hp.share(a, 2, 6, b, 100)
+    slot_a = hp.tokens(a)[0]
+    slot_b, pos_b, _ = hp.tokens(b)
+    np.testing.assert_array_equal(slot_b, slot_a[2:8])
+    np.testing.assert_array_equal(pos_b, np.arange(2, 8) + 100)
+    np.testing.assert_array_equal(hp.lag(b), np.full(6, 100))
+    free0 = len(hp.queues()[0])
+    hp.seq_release(a)                               # b still holds its rows
+    assert len(hp.queues()[0]) == free0
+    with pytest.raises(akv.AkvError):
+        hp.tokens(a)
+    hp.seq_release(b)                               # the last holder: a's pages return
+    assert len(hp.queues()[0]) == free0 + 3
+    hp.append(c, np.arange(3))

@@ -305,6 +305,96 @@ def test_clone_places_like_append_and_refusals_are_atomic():
         assert list(p1.evictable) == snap[2] and np.array_equal(p1.kr, snap[3])
 
 
+# ---------------------------------------------------------------------------
+# shared pages ("Cache Engineering for Agents", section 3: copy-on-write
+# page-table references; "Cache Engineering for Autonomous Agents", section 3,
+# Cache Management: re-use by key rotation)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("pairing", [0, 1])
+def test_share_reads_as_fresh_rope_and_copy_on_write(pairing):
+    """A frozen checkpoint shared at delta, then repositioned in part, reads
+    (gathered keys, attention) as the raw keys RoPE'd at the new positions
+    (explicit 2x2 matrices); nothing is written until materialize, which
+    copies into the sharer's own pages and leaves the source's rows as they
+    were."""
+    rng = np.random.default_rng(21)
+    base, d, n = 10000.0, 32, 120
+    lay = _lay(d_rope=d, d_v=8, n_q_heads=4, n_kv_heads=2, pairing=pairing, rope_theta=base, num_pages=40, page_size=8)
+    raw = rng.standard_normal((n, 2, d))
+    m = np.arange(n, dtype=np.float64) * 3.0 + 50.0
+    v = rng.standard_normal((n, 2, 8))
+    pool = AO.Pool(lay)
+    a, b = pool.seq_create(), pool.seq_create()
+    pool.append(a, m.astype(np.int64), _rope_by_matrix(raw, m[:, None, None], base, pairing), None, v)
+    pool.drop(a, [[40, 50]], auto_compact=False)
+    pool.freeze(a)
+    kr0, v0, free0 = pool.kr.copy(), pool.v.copy(), list(pool.free)
+    pool.share(a, 20, 100, b, 999)
+    assert np.array_equal(pool.kr, kr0) and list(pool.free) == free0, "share wrote or allocated"
+    keep = np.array([t for t in range(20, 120) if not 40 <= t < 50])
+    qb = pool.seqs[b]
+    np.testing.assert_array_equal(qb.slot, pool.seqs[a].slot[keep])
+    pool.repos(b, [[30, 90]], [-12])
+    newpos = m[keep] + 999
+    newpos[30:90] -= 12
+    np.testing.assert_array_equal(qb.pos, newpos.astype(np.int64))
+    assert np.array_equal(pool.kr, kr0), "repos wrote a shared row"
+    want = _rope_by_matrix(raw[keep], newpos[:, None, None], base, pairing)
+    got, gv = pool.gather(pool.extents(b), lag=pool.visible_lag(b))
+    order = pool.visible(b)                          # the list is in position order
+    np.testing.assert_allclose(got, want[order], rtol=0, atol=1e-9)
+    np.testing.assert_array_equal(gv, v[keep][order])
+    # attention over the shared, owed keys equals attention over the fresh keys
+    qry = rng.standard_normal((5, 4, d))
+    out = AO.segment_attention(pool, qry, [(0, 5, 0, len(pool.extents(b)))], pool.extents(b), 1 / np.sqrt(d),
+                               lags=pool.visible_lag(b))
+    fresh = AO.Pool(lay)
+    f = fresh.seq_create()
+    fresh.append(f, newpos.astype(np.int64), want, None, v[keep])
+    out2 = AO.segment_attention(fresh, qry, [(0, 5, 0, len(fresh.extents(f)))], fresh.extents(f), 1 / np.sqrt(d))
+    np.testing.assert_allclose(out, out2, rtol=0, atol=1e-12)
+    pool.materialize(b)
+    assert not np.isin(qb.slot, pool.seqs[a].slot).any() and not qb.lag.any()
+    S = lay.page_size
+    np.testing.assert_allclose(pool.kr[qb.slot // S, :, qb.slot % S, :], want, rtol=0, atol=1e-9)
+    qa = pool.seqs[a]
+    np.testing.assert_array_equal(pool.kr[qa.slot // S, :, qa.slot % S, :], kr0[qa.slot // S, :, qa.slot % S, :])
+    np.testing.assert_array_equal(pool.v[qa.slot // S, :, qa.slot % S, :], v0[qa.slot // S, :, qa.slot % S, :])
+    assert pool.seqs[a].refs == 0 and not qb.owners
+
+
+def test_shared_pages_outlive_their_source():
+    """Pages of a released source stay while a sharer holds slots in them
+    and return, in allocation order, when the last one lets go (by release,
+    by dropping every shared token, or by materialize); frozen sequences
+    refuse every change."""
+    rng = np.random.default_rng(22)
+    lay = _lay(page_size=4, num_pages=30)
+    pool = AO.Pool(lay)
+    a, b, c = (pool.seq_create() for _ in range(3))
+    _fill(pool, a, 16, rng)
+    pages_a = list(pool.seqs[a].pages)
+    with pytest.raises(AO.EState):
+        pool.share(a, 0, 16, b, 0)                   # not frozen
+    pool.freeze(a)
+    z = np.zeros((1, 2, 16))
+    for call in (lambda: pool.drop(a, [[0, 1]]), lambda: pool.repos(a, [[0, 1]], [1]),
+                 lambda: pool.append(a, [99], z, None, z), lambda: pool.compact(a, True),
+                 lambda: pool.clone(b, 0, 0, a, 0)):
+        with pytest.raises(AO.EState):
+            call()
+    pool.share(a, 0, 8, b, 10)                       # pages 0, 1 of a
+    pool.share(a, 8, 8, c, 10)                       # pages 2, 3 of a
+    assert pool.seqs[a].refs == 2
+    pool.seq_release(a)
+    assert pool.seqs[a].zombie and not any(p in pool.free for p in pages_a)
+    pool.drop(b, [[0, 8]], auto_compact=False)       # b lets go of every shared token
+    assert pool.seqs[a].refs == 1 and pool.seqs[a].zombie
+    pool.seq_release(c)                              # the last holder
+    assert not pool.seqs[a].zombie
+    assert list(pool.free)[-4:] == pages_a
+
+
 def test_repos_position_range_is_atomic():
     rng = np.random.default_rng(4)
     pool = AO.Pool(_lay())

@@ -36,9 +36,10 @@ import numpy as np
 
 __all__ = [
     "Layout", "SeqCreate", "Append", "AppendBatch", "Drop", "Repos", "Splice", "Compact", "Clone",
+    "Freeze", "Share", "Materialize",
     "Segment", "Attention", "Workload", "to_bf16", "bf16_to_f64",
     "c1_tiny", "c2_64k", "c3_mla", "c4_batched", "c5_128k", "decode_batch", "decode_with_idle", "retrigger",
-    "with_idle_compaction",
+    "with_idle_compaction", "share_fuzz",
     "fuzz_small",
     "CONFIGS", "make", "query_variant",
 ]
@@ -183,6 +184,25 @@ class Clone:
     n: int
     dst: int             # ... appended to dst at pos + delta (positional version)
     delta: int
+
+
+@dataclass
+class Freeze:
+    seq: int             # the sequence becomes a checkpoint (rows never change)
+
+
+@dataclass
+class Share:
+    src: int             # retained tokens [first, first+n) of frozen src ...
+    first: int
+    n: int
+    dst: int             # ... appended to dst by reference, at pos + delta (they owe the rotation)
+    delta: int
+
+
+@dataclass
+class Materialize:
+    seq: int             # every key turned by what it owes (shared rows: copy on write)
 
 
 @dataclass
@@ -658,6 +678,57 @@ def decode_with_idle(seed: int = 0, n_req: int = 48, n_idle: int = 8, idle_ctx: 
     over n_idle fragmented idle sequences (with_idle_compaction)."""
     return with_idle_compaction(decode_batch(seed, n_req=n_req, **kw), seed, n_idle, idle_ctx,
                                 attend_idle=attend_idle)
+
+
+def share_fuzz(seed: int, mla: bool = False, page_size: int = 16, d: int = 64, pairing: int = 0,
+               n_hist: int = 600, n_q: int = 24, group: int = 4, materialize: Optional[bool] = None) -> Workload:
+    """Checkpoints and sharers: sequence 0 (a history with a drop and a
+    repos) is frozen; sequences 1 and 2 share all or a suffix of it at other
+    positions (one delta each, either sign, or 0); sequence 1 appends, drops
+    shared and own tokens, repositions across both, then compacts or
+    materializes (copy on write); sequence 0 is released while shared;
+    sequence 2 drops shared tokens; sequence 3 clones half of sequence 1.
+    Then sequences 1, 2 and 3 append n_q query tokens each (positions past
+    every earlier one, so they are each list's last entries) and attend in
+    one launch."""
+    rng = _rng(seed)
+    if mla:
+        lay = Layout(4, 4, 32, 32, 32, page_size, 0, pairing=pairing, rope_theta=10000.0)
+    else:
+        lay = Layout(2 * group, 2, 0, d, d, page_size, 0, pairing=pairing, rope_theta=10000.0)
+    n0 = n_hist
+    ops: list = [SeqCreate() for _ in range(4)]
+    ops.append(_append_op(rng, lay, 0, np.arange(n0, dtype=np.int32)))
+    b = int(rng.integers(50, n0 // 2))
+    e = b + int(rng.integers(10, 80))
+    ops.append(Drop(0, _spans([(b, e)])))
+    ops.append(Repos(0, _spans([(e, n0)]), np.array([-(e - b)], np.int32)))
+    ops.append(Freeze(0))
+    vis0 = n0 - (e - b)
+    d1 = int(rng.choice([0, 333, -40, 1000]))
+    d2 = int(rng.choice([77, -30, 0]))
+    first2 = int(rng.integers(0, b))
+    ops.append(Share(0, 0, n0, 1, d1 + 60))
+    ops.append(Share(0, first2, n0 - first2, 2, d2 + 60))
+    ops.append(_append_op(rng, lay, 1, np.arange(500_000, 500_030, dtype=np.int32)))
+    n1 = vis0 + 30
+    s1 = int(rng.integers(20, vis0 - 60))
+    ops.append(Drop(1, _spans([(s1, s1 + 25), (vis0 + 5, vis0 + 9)])))
+    ops.append(Repos(1, _spans([(s1 + 25, n1)]), np.array([-25], np.int32)))
+    mat = bool(rng.random() < 0.5) if materialize is None else materialize
+    ops.append(Materialize(1) if mat else Compact(1, 1))
+    ops.append(Release(0))                     # still shared: its pages stay
+    ops.append(Drop(2, _spans([(3, 11)])))
+    ops.append(Clone(1, 0, n1 // 2, 3, int(rng.choice([0, 55]))))
+    segs = []
+    for i, sq in enumerate((1, 2, 3)):
+        ops.append(_append_op(rng, lay, sq, np.arange(1_000_000, 1_000_000 + n_q, dtype=np.int32)))
+        segs.append(Segment(sq, i * n_q, n_q, np.zeros((0, 2), np.int32)))
+    ops.append(Attention(_normal_bf16(rng, (3 * n_q, lay.n_q_heads, lay.d_qk), scale=0.5), segs))
+    lay.num_pages = 4 * ((n0 + 3 * n_q + 64) // page_size + 8)
+    wl = Workload(f"share_fuzz_{seed}", lay, rng.permutation(lay.num_pages).astype(np.int32), ops)
+    wl.notes.update(materialize=mat)
+    return wl
 
 
 # --------------------------------------------------------------------------
