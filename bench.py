@@ -258,7 +258,7 @@ def run_config(args) -> dict:
     gens = {"c1": lambda s: W.c1_tiny(s, "canonical"), "c3": W.c3_mla, "c4": W.c4_batched, "c5": W.c5_128k,
             "decode": W.decode_batch, "decode_fused": lambda s: W.decode_batch(s, deferred=True),
             "retrigger": W.retrigger, "c2_fused": lambda s: deferred(W.c2_64k(s)),
-            "decode_compact": W.decode_with_idle,
+            "decode_compact": W.decode_with_idle, "decode_mass": W.decode_batch,
             "c2_compact": lambda s: W.with_idle_compaction(W.c2_64k(s), s, n_idle=2, idle_ctx=16384)}
     wl = gens[args.config](args.seed)
     L = wl.layout
@@ -287,16 +287,19 @@ def run_config(args) -> dict:
                       segs)
     flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
     rope_heads = L.n_kv_heads if (not L.mla or L.kpe_per_head) else 1
-    tot = {k: [0.0, 0] for k in ("attention", "rotate", "append", "compact", "expand", "combine", "clone")}
+    tot = {k: [0.0, 0] for k in ("attention", "rotate", "append", "compact", "expand", "combine", "clone", "mass")}
     walls, flops, pairs, kv_bytes, n_rot, n_q, clone_bytes = [], 0.0, 0, 0, 0, 0, 0
     idle_moved = 0
     kern = None
-    n_dec = args.decode_steps if args.config in ("decode", "decode_fused", "decode_compact") else 1
+    n_dec = args.decode_steps if args.config in ("decode", "decode_fused", "decode_compact", "decode_mass") else 1
     first_walls = []
     for rep in range(args.warmup + args.steps):
         pool = D.make_pool(wl)
         if args.config == "c2_fused":
             pool.fused_rotation("always")     # keys turned in the attention kernel, not in place
+        if args.config == "decode_mass":       # per-page attention mass of every decode launch
+            mass_out = torch.zeros(L.num_pages, dtype=torch.float32, device="cuda:0")
+            pool.attention_mass(mass_out)
         keep = []
         for op in ops[:i0]:
             D.apply_op(pool, op, keep)
@@ -436,7 +439,15 @@ def run_config(args) -> dict:
                                    "launches_per_pass": cm_per_step, "avg_launch_ms": round(cm_ms, 5)}
         rec["note"] = ("the workload's step on the pool stream, then the background compaction pass (its copies on "
                        "the pool's second stream, beside the step's kernels)")
-    if args.config in ("decode", "decode_fused", "decode_compact"):
+    if tot["mass"][1]:
+        # the second pass reads every visible K row once more
+        ms_m = tot["mass"][0] / tot["mass"][1]
+        k_bytes = kv_bytes * (L.d_nope + L.d_rope) / (L.d_nope + L.d_rope + L.d_v)
+        gbps_m = k_bytes / (ms_m * 1e-3) / 1e9
+        rec["roofline_mass"] = {"bound": "hbm", "achieved": round(gbps_m, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                "frac": round(gbps_m / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": "k_page_mass",
+                                "k_bytes_per_launch": k_bytes, "avg_launch_ms": round(ms_m, 5)}
+    if args.config in ("decode", "decode_fused", "decode_compact", "decode_mass"):
         # one query row per kv-head group: the launch streams the visible K/V once
         hbm_gbps = kv_bytes / (attn_ms * 1e-3) / 1e9
         rec["roofline"] = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -488,6 +499,8 @@ CONFIG_NAMES = {
                   "8-token blocks, its copies on the pool's second stream beside the step's attention",
     "decode_fused": "the decode step of 48 requests of 2K-16K tokens whose survivors' repos was deferred: the "
                     "keys stay at their old positions and the decode kernel turns them as it reads them",
+    "decode_mass": "the decode step of 48 requests of 2K-16K tokens (32 q / 8 kv heads, head_dim 128, page 16) "
+                   "with the per-page attention mass output set (a second pass over each launch's K rows)",
     "decode": "48 requests of 2K-16K tokens on the 64K layer shape (32 q / 8 kv heads, head_dim 128, page 16), "
               "dropped and repositioned at set-up; the step appends one token per request and runs 48 one-query "
               "segments in one launch",
@@ -497,7 +510,7 @@ CONFIG_NAMES = {
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2_fused", "c3", "c4", "c5", "decode", "decode_fused",
-                                                       "decode_compact", "c2_compact", "retrigger"],
+                                                       "decode_compact", "decode_mass", "c2_compact", "retrigger"],
                     help="c2 (default) is the headline 64K step; the others print one record each")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)

@@ -393,6 +393,24 @@ akv_status akv_segment_attention_static(akv_pool* pool, const void* Q, int32_t n
 akv_status akv_seq_attention(akv_pool* pool, const void* Q, int32_t n_q_tokens, const akv_seq_segment* segs,
                              int32_t n_segs, const akv_span* masks, int32_t n_masks, float scale, void* out);
 
+/* Attention mass per page, the statistic a server-side drop policy watches
+ * ([AKV-blog] section 7, Dilemma 1: blocks whose cumulative attention weight
+ * stays below a threshold over consecutive decode turns are dropped).
+ * mass: device float array of num_pages entries (caller-owned, not cleared
+ * by the library), or NULL to stop.  While set, every decode launch of
+ * akv_segment_attention or akv_seq_attention on the pool (128-dim GQA,
+ * segments of at most 16 packed rows per kv head) also adds, to mass[page],
+ * the softmax weight its rows put on the page's keys: summed over the
+ * segments' query tokens and q heads, so the pages of one launch receive
+ * (query tokens x q heads) in total (divide by that for the mean weight).
+ * Keys owing a rotation count at their position.  It is a second pass over
+ * the launch's K rows (one more read of K) after the attention, which also
+ * writes each row's log-sum-exp to the pool's scratch buffer; other launches
+ * (prefill, other layouts, akv_segment_attention_static) leave mass alone.
+ * Errors: AKV_EINVAL (n_pages differs from the pool's page count),
+ * AKV_ESTATE (page-table-only pool). */
+akv_status akv_attention_mass(akv_pool* pool, float* mass, int32_t n_pages);
+
 /* ---- extended radix tree of cached states ([AKV-blog] section 3; [AKV-notes]
  * section 3, Cache Management and Cache Reuse Matching Rules) -------------------- */
 
@@ -479,7 +497,7 @@ akv_status akv_attention_plan(akv_pool* pool, int32_t n_q_tokens, const akv_segm
  * stream, returns the summed milliseconds and launch count of one kernel kind
  * since the last read of that kind, and clears them. */
 enum { AKV_K_APPEND = 0, AKV_K_ROTATE = 1, AKV_K_COMPACT = 2, AKV_K_EXPAND = 3,
-       AKV_K_ATTN = 4, AKV_K_COMBINE = 5, AKV_K_CLONE = 6, AKV_K_KINDS = 7 };
+       AKV_K_ATTN = 4, AKV_K_COMBINE = 5, AKV_K_CLONE = 6, AKV_K_MASS = 7, AKV_K_KINDS = 8 };
 akv_status akv_timing_enable(akv_pool* pool, int32_t enable);
 akv_status akv_timing_read(akv_pool* pool, int32_t kind, double* total_ms, int32_t* count);
 /* The individual launch durations (ms) behind the next akv_timing_read of

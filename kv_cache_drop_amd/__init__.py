@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "AKV_OK", -1: "AKV_EINVAL", -2: "AKV_ERANGE", -3: "AKV_ENOMEM
                 -4: "AKV_ESTATE", -5: "AKV_EHIP"}
 EV_TOKEN, EV_DROP, EV_REPOS = 0, 1, 2
 KERNEL_KINDS = {"append": 0, "rotate": 1, "compact": 2, "expand": 3, "attention": 4, "combine": 5,
-                "clone": 6}
+                "clone": 6, "mass": 7}
 
 
 class AkvError(RuntimeError):
@@ -76,6 +76,7 @@ SYMBOLS = {
     "akv_seq_visible": [_P, _I, _IP, _I, _IP, _I, _IP],
     "akv_segment_attention": [_P, _P, _I, _IP, _I, _IP, _I, ctypes.c_float, _P],
     "akv_segment_attention_static": [_P, _P, _I, _IP, _I, _IP, _I, ctypes.c_float, _P],
+    "akv_attention_mass": [_P, _P, _I],
     "akv_seq_tokens": [_P, _I, _I, _I, _IP, _IP, ctypes.POINTER(ctypes.c_uint8)],
     "akv_seq_info": [_P, _I, _IP, _IP, ctypes.POINTER(ctypes.c_double)],
     "akv_pool_queues": [_P, _IP, _I, _IP, _IP, _I, _IP],
@@ -322,6 +323,20 @@ class Pool:
 
     def share(self, src: int, first: int, n: int, dst: int, delta: int = 0) -> None:
         _check(lib().akv_seq_share(self._h, src, first, n, dst, delta))
+
+    def attention_mass(self, mass) -> None:
+        """Per-page attention mass of decode launches added to `mass` (a
+        device float32 tensor of num_pages entries), or None to stop
+        (akv_attention_mass).  The tensor must outlive its use."""
+        if mass is None:
+            _check(lib().akv_attention_mass(self._h, None, 0))
+            self._mass = None
+            return
+        import torch
+        if mass.dtype != torch.float32 or mass.numel() != self.layout["num_pages"]:
+            raise ValueError("mass must be float32 with one entry per page")
+        _check(lib().akv_attention_mass(self._h, _dptr(mass), mass.numel()))
+        self._mass = mass
 
     def clone(self, src: int, first: int, n: int, dst: int, delta: int) -> None:
         """Positional version: append src's retained tokens [first, first+n)

@@ -335,6 +335,8 @@ __global__ __launch_bounds__(64 * DEC_WAVES, 2) void k_decode_attn(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) ov[e] = pk_bf2(o[2 * e] * inv, o[2 * e + 1] * inv);
     *(u32x4_t*)(a.out + ((size_t)(sg.q_begin + otok) * a.n_q_heads + ohq) * DEC_D + oc) = ov;
+    if (a.lse && (tid & 15) == 0)
+      a.lse[(size_t)(sg.q_begin + otok) * a.n_q_heads + ohq] = L > 0.f ? Mu + __log2f(L) : INFINITY;
   } else {
     const size_t prow = (size_t)it.part + orow;
     float* po = a.part_o + prow * DEC_D + oc;
@@ -345,6 +347,141 @@ __global__ __launch_bounds__(64 * DEC_WAVES, 2) void k_decode_attn(AttnArgs a) {
       a.part_ml[2 * prow + 1] = L;
     }
   }
+}
+
+// Attention mass per page ("AKV: Cache Engineering for Autonomous Agents",
+// section 7, Dilemma 1: a server-side drop policy watches the cumulative
+// attention weight of each block of the history over decode turns).  Second
+// pass over a decode launch's lists: with each row's log-sum-exp from the
+// attention, key k's weight for row r (token, q head) is 2^(s_rk c - lse_r)
+// for keys within the row's causal limit; the weights of the segment's rows
+// are summed per key and added to mass[page].
+//
+// Block: MASS_CHUNK consecutive list entries of one segment, one kv head
+// (blockIdx.y); 16 groups of 16 lanes, group g takes entries g*16 .. +15 in
+// order, lane j of a group holds d 8j .. 8j+7 of the key (one 16-byte load
+// per lane, so a key row is one load of the group).  The group's lanes (one
+// DPP row) reduce each row's dot product with DPP moves, lane 0 adds the weights and
+// flushes one atomic add per run of entries in one page.  Keys owing a
+// rotation are turned as the attention turned them (same table row, fp32
+// formula and bf16 rounding).
+constexpr int MASS_GROUPS = 16;
+constexpr int MASS_PER_GROUP = MASS_CHUNK / MASS_GROUPS;
+constexpr int MASS_BATCH = 8;
+static_assert(MASS_PER_GROUP % MASS_BATCH == 0, "the group walk takes MASS_BATCH keys at a time");
+
+// Sum over the 16 lanes of a DPP row (every lane gets it): quad xor 1, quad
+// xor 2, half-row mirror, row mirror.
+__device__ __forceinline__ float row_sum16(float s) {
+  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));
+  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));
+  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x141, 0xF, 0xF, false));
+  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x140, 0xF, 0xF, false));
+  return s;
+}
+
+// dot product of 8 bf16 pairs-of-words: key w, query qw (both packed bf16)
+__device__ __forceinline__ float dot8(const u32x4_t& w, const u32x4_t& qw) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s = fmaf(__uint_as_float(w[e] << 16), __uint_as_float(qw[e] << 16), s);
+    s = fmaf(__uint_as_float(w[e] & 0xffff0000u), __uint_as_float(qw[e] & 0xffff0000u), s);
+  }
+  return s;
+}
+
+// R: rows per (segment, kv head) the launch holds at most (4, 8 or 16);
+// ROT: list entries may owe a rotation (a.key_didx set).
+template <int R, bool ROT>
+__global__ __launch_bounds__(256) void k_page_mass(AttnArgs a, const MassItem* __restrict__ items,
+                                                   float* __restrict__ mass) {
+  const MassItem it = items[blockIdx.x];
+  const int kvh = blockIdx.y;
+  const AttnSeg sg = a.segs[it.seg];
+  const int G = a.group, rows = sg.q_len * G;
+  const int tid = threadIdx.x;
+  const int grp = tid >> 4, j = tid & 15;
+  // this lane's eight d of every row's query (packed bf16), the rows'
+  // log-sum-exp and causal limits
+  u32x4_t qw[R];
+  float lse[R];
+  int lim[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rr = r < rows ? r : 0;
+    const int tok = rr / G, hq = kvh * G + (rr - tok * G);
+    const size_t qrow = (size_t)(sg.q_begin + tok) * a.n_q_heads + hq;
+    qw[r] = *(const u32x4_t*)(a.q + qrow * DEC_D + 8 * j);
+    lse[r] = a.lse[qrow];
+    lim[r] = r < rows ? sg.lkv - sg.q_len + tok : -1;
+  }
+  const int Hkv = a.n_kv_heads, S = a.page_size, lg = a.log2_page;
+  const float c2 = a.scale_log2e;
+  const int kb = it.k0 + grp * MASS_PER_GROUP;
+  const int32_t* __restrict__ slots = a.slots + sg.list_off;
+  int cur_page = -1;
+  float acc = 0.f;
+  int slot_n[MASS_BATCH];
+#pragma unroll
+  for (int u = 0; u < MASS_BATCH; ++u) slot_n[u] = slots[min(kb + u, sg.lkv - 1)];
+  for (int k4 = 0; k4 < MASS_PER_GROUP; k4 += MASS_BATCH) {
+    // this batch's rows in flight (entries past the list end re-read its
+    // last), the next batch's slots behind them
+    u32x4_t w[MASS_BATCH];
+    int page[MASS_BATCH], didx[MASS_BATCH];
+#pragma unroll
+    for (int u = 0; u < MASS_BATCH; ++u) {
+      const int e = min(kb + k4 + u, sg.lkv - 1);
+      page[u] = slot_n[u] >> lg;
+      const size_t row = ((size_t)page[u] * Hkv + kvh) * S + (slot_n[u] & (S - 1));
+      w[u] = *(const u32x4_t*)(a.k_a + row * DEC_D + 8 * j);
+      didx[u] = ROT ? a.key_didx[sg.list_off + e] : -1;
+    }
+    if (k4 + MASS_BATCH < MASS_PER_GROUP) {
+#pragma unroll
+      for (int u = 0; u < MASS_BATCH; ++u) slot_n[u] = slots[min(kb + k4 + MASS_BATCH + u, sg.lkv - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < MASS_BATCH; ++u) {
+      const int e = kb + k4 + u;
+      if (e < sg.lkv) {
+        if (ROT && didx[u] >= 0) {   // the same for all 16 lanes of the group
+          const float* row = a.rot_table + (size_t)didx[u] * DEC_D;
+          if (a.rot_pairing == 0) {
+            const f32x4_t cs = *(const f32x4_t*)(row + 4 * j), sn = *(const f32x4_t*)(row + DEC_D / 2 + 4 * j);
+            turn_interleaved(w[u], cs, sn);
+          } else {
+            // lanes j < 8 hold the first elements of pairs 8j .. 8j+7, lane
+            // j + 8 their second elements
+            const int p0 = 8 * (j & 7);
+            u32x4_t o;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) o[e2] = (unsigned)__shfl_xor((int)w[u][e2], 8, 16);
+            u32x4_t xw = j < 8 ? w[u] : o, yw = j < 8 ? o : w[u];
+            const f32x4_t c0 = *(const f32x4_t*)(row + p0), c1 = *(const f32x4_t*)(row + p0 + 4);
+            const f32x4_t s0 = *(const f32x4_t*)(row + DEC_D / 2 + p0);
+            const f32x4_t s1 = *(const f32x4_t*)(row + DEC_D / 2 + p0 + 4);
+            turn_half(xw, yw, c0, c1, s0, s1);
+            w[u] = j < 8 ? xw : yw;
+          }
+        }
+        float km = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float s = row_sum16(dot8(w[u], qw[r]));
+          if (e <= lim[r]) km += __builtin_amdgcn_exp2f(fmaf(s, c2, -lse[r]));
+        }
+        if (page[u] != cur_page) {
+          if (cur_page >= 0 && j == 0) atomicAdd(mass + cur_page, acc);
+          cur_page = page[u];
+          acc = 0.f;
+        }
+        acc += km;
+      }
+    }
+  }
+  if (cur_page >= 0 && j == 0) atomicAdd(mass + cur_page, acc);
 }
 
 }  // namespace
@@ -363,6 +500,25 @@ hipError_t launch_expand_didx(hipStream_t st, const Extent* ex, const int32_t* e
   if (n_ext <= 0) return hipSuccess;
   const int blocks = std::min(4096, (n_ext + 255) / 256);
   hipLaunchKernelGGL(k_expand_didx, dim3(blocks), dim3(256), 0, st, ex, ex_off, ex_didx, n_ext, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_page_mass(hipStream_t st, const AttnArgs& a, const MassItem* items, int n_items, int max_rows,
+                            float* mass) {
+  if (n_items <= 0) return hipSuccess;
+  if (a.n_kv_heads > 65535 || !a.lse || max_rows > DECODE_ROWS) return hipErrorInvalidValue;
+  const dim3 grid(n_items, a.n_kv_heads);
+  const bool rot = a.key_didx != nullptr;
+  if (max_rows <= 4) {
+    if (rot) hipLaunchKernelGGL((k_page_mass<4, true>), grid, dim3(256), 0, st, a, items, mass);
+    else hipLaunchKernelGGL((k_page_mass<4, false>), grid, dim3(256), 0, st, a, items, mass);
+  } else if (max_rows <= 8) {
+    if (rot) hipLaunchKernelGGL((k_page_mass<8, true>), grid, dim3(256), 0, st, a, items, mass);
+    else hipLaunchKernelGGL((k_page_mass<8, false>), grid, dim3(256), 0, st, a, items, mass);
+  } else {
+    if (rot) hipLaunchKernelGGL((k_page_mass<16, true>), grid, dim3(256), 0, st, a, items, mass);
+    else hipLaunchKernelGGL((k_page_mass<16, false>), grid, dim3(256), 0, st, a, items, mass);
+  }
   return hipGetLastError();
 }
 

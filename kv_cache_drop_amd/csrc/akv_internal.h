@@ -105,6 +105,12 @@ struct AttnArgs {
   const int32_t* key_didx;
   const float* rot_table;
   int rot_pairing;
+  // optional: per output row (token, q head) its log-sum-exp in base 2,
+  // lse = m + log2(l) in the units of scale * log2(e) (so a key's weight for
+  // the row is 2^(s * scale_log2e - lse)); +inf for a row with no key.
+  // Written by the decode kernel for rows it finishes and by the combine
+  // kernel; nullptr when not wanted
+  float* lse;
 };
 
 // Returns hipErrorInvalidValue when no kernel is instantiated for the dims.
@@ -117,6 +123,16 @@ hipError_t launch_combine(hipStream_t st, const AttnArgs& a, const CombItem* ite
 // DECODE_ROWS packed rows, the block's waves splitting the key range.
 constexpr int DECODE_ROWS = 16;
 hipError_t launch_decode_attn(hipStream_t st, const AttnArgs& a);
+// Attention mass per page of a decode launch (second pass with a.lse): work
+// item = (segment, first list entry of a chunk of MASS_CHUNK entries), grid
+// rows = kv heads; mass[page] += the weight of the page's keys, summed over
+// the segment's rows and q heads.
+constexpr int MASS_CHUNK = 256;
+struct MassItem {
+  int32_t seg, k0;
+};
+hipError_t launch_page_mass(hipStream_t st, const AttnArgs& a, const MassItem* items, int n_items, int max_rows,
+                            float* mass);
 // Per list entry of each extent e (entries ex_off[e] .. + hi - lo): ex_didx[e].
 hipError_t launch_expand_didx(hipStream_t st, const Extent* ex, const int32_t* ex_off, const int32_t* ex_didx,
                               int n_ext, int32_t* out);

@@ -1086,6 +1086,8 @@ __global__ __launch_bounds__(256) void k_combine(AttnArgs a, const CombItem* __r
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   const int tok = r / G, hq = it.kvh * G + (r - tok * G);
+  if (a.lse && lane == 0)
+    a.lse[(size_t)(sg.q_begin + tok) * a.n_q_heads + hq] = L > 0.f ? Mu + __log2f(L) : INFINITY;
   uint16_t* op = a.out + ((size_t)(sg.q_begin + tok) * a.n_q_heads + hq) * DV;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {

@@ -147,6 +147,7 @@ struct AttnHostBufs {
   std::vector<akv_extent> lists, masked;
   std::vector<int32_t> lags, mlag, ex_off, ex_didx;
   std::vector<akv::Extent> ex_used;
+  std::vector<akv::MassItem> mass_items;
   AttnPlan plan;
 };
 
@@ -197,6 +198,7 @@ struct akv_pool {
   double thr = kDefaultCompactThreshold;
   int compact_mode = AKV_COMPACT_IMMEDIATE;
   int fuse_mode = AKV_FUSE_AUTO;   // where owed rotations are applied (akv_fused_rotation)
+  float* mass = nullptr;           // per-page attention mass of decode launches (akv_attention_mass)
   std::deque<int32_t> compact_q;   // deferred compactions, in the order queued
 
   std::deque<int32_t> free_q;
@@ -2782,11 +2784,20 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
       }
     }
     const size_t keys4 = (size_t)std::max<int64_t>(total, 1) * 4;
+    // attention mass per page (decode launches): chunks of each segment's list
+    const bool want_mass = decode && p->mass && !ws_static;
+    std::vector<akv::MassItem>& mass_items = p->hb.mass_items;
+    mass_items.clear();
+    if (want_mass)
+      for (int32_t i = 0; i < n_segs; ++i)
+        if (segs[i].q_len > 0)
+          for (int64_t k0 = 0; k0 < lkv[i]; k0 += akv::MASS_CHUNK) mass_items.push_back({i, (int32_t)k0});
+    const size_t lse_bytes = want_mass ? (size_t)n_q_tokens * L.n_q_heads * 4 : 0;
     const size_t need = plan.segs.size() * sizeof(akv::AttnSeg) + plan.items.size() * sizeof(akv::AttnItem) +
                         plan.comb.size() * sizeof(akv::CombItem) + ex_off.size() * sizeof(akv::Extent) +
                         (ex_off.size() + ex_didx.size()) * 4 + keys4 * (fused ? 2 : 1) +
                         rot_deltas.size() * (size_t)L.d_rope * 4 + (size_t)plan.part_rows * (L.d_v + 2) * 4 +
-                        12 * 256;
+                        mass_items.size() * sizeof(akv::MassItem) + lse_bytes + 14 * 256;
     static const std::vector<float> no_rows;
     const std::vector<float>& rot_rows = fused ? rot_table_rows(p, rot_deltas.data(), rot_deltas.size()) : no_rows;
     const std::pair<const void*, size_t> up_parts[7] = {
@@ -2802,6 +2813,8 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
     int32_t* dkey_didx = nullptr;
     float* part_o = nullptr;
     float* part_ml = nullptr;
+    float* dlse = nullptr;
+    void* dmass_items = nullptr;
     if (ws_static) {
       // The call's tables, slot list and partials in the library's static
       // device workspace: one copy of the tables on the pool stream (after
@@ -2839,15 +2852,20 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
       }
     } else {
       ScratchCursor sc(p, need);
+      void* dv8[8];
       akv_status st = upload_arrays(p, sc, {up_parts[0], up_parts[1], up_parts[2], up_parts[3], up_parts[4],
-                                            up_parts[5], up_parts[6]}, dv);
+                                            up_parts[5], up_parts[6],
+                                            {mass_items.data(), mass_items.size() * sizeof(akv::MassItem)}}, dv8);
       if (st != AKV_OK) return st;
+      for (int i = 0; i < 7; ++i) dv[i] = dv8[i];
+      dmass_items = dv8[7];
       dslots = (int32_t*)sc.take((size_t)std::max<int64_t>(total, 1) * 4);
       dkey_didx = fused ? (int32_t*)sc.take((size_t)std::max<int64_t>(total, 1) * 4) : nullptr;
       if (plan.part_rows > 0) {
         part_o = (float*)sc.take((size_t)plan.part_rows * L.d_v * 4);
         part_ml = (float*)sc.take((size_t)plan.part_rows * 2 * 4);
       }
+      if (want_mass) dlse = (float*)sc.take(lse_bytes);
       if (!sc.ok()) return fail(AKV_ENOMEM, "scratch too small for this call (%zu bytes per call)",
                                    p->scratch_bytes - p->scratch_base);
     }
@@ -2894,6 +2912,7 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
     a.key_didx = dkey_didx;
     a.rot_table = drot;
     a.rot_pairing = L.pairing;
+    a.lse = dlse;
     {
       KTimer tm(p, AKV_K_ATTN);
       e = decode ? akv::launch_decode_attn(p->stream, a) : akv::launch_seg_attn(p->stream, a, L.d_nope, L.d_rope, L.d_v);
@@ -2906,10 +2925,29 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
       tm.done();
       if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
     }
+    if (want_mass && !mass_items.empty()) {
+      KTimer tm(p, AKV_K_MASS);
+      int64_t max_rows = 0;
+      for (int32_t i = 0; i < n_segs; ++i)
+        max_rows = std::max<int64_t>(max_rows, (int64_t)segs[i].q_len * (L.n_q_heads / L.n_kv_heads));
+      e = akv::launch_page_mass(p->stream, a, (const akv::MassItem*)dmass_items, (int)mass_items.size(),
+                                (int)max_rows, p->mass);
+      tm.done();
+      if (e != hipSuccess) return hip_fail(e, "attention mass kernel launch");
+    }
     return AKV_OK;
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
   }
+}
+
+akv_status akv_attention_mass(akv_pool* p, float* mass, int32_t n_pages) {
+  if (!p) return fail(AKV_EINVAL, "NULL pool");
+  if (!p->device) return fail(AKV_ESTATE, "attention mass needs a device pool");
+  if (mass && n_pages != p->L.num_pages)
+    return fail(AKV_EINVAL, "mass holds %d pages, the pool %d", n_pages, p->L.num_pages);
+  p->mass = mass;
+  return AKV_OK;
 }
 
 akv_status akv_segment_attention(akv_pool* p, const void* Q, int32_t n_q_tokens, const akv_segment* segs,

@@ -7,6 +7,6 @@ the `cpu_baseline` leg of `bench.py`, never by the product package
 """
 from .akv_oracle import (  # noqa: F401
     DEFAULT_COMPACT_THRESHOLD, EInval, ENoMem, ERange, EState, OracleError, Pool,
-    dense_masked_attention, rope_inv_freq, rotate, segment_attention,
+    dense_masked_attention, page_mass, rope_inv_freq, rotate, segment_attention,
 )
 from .script import OracleRun, apply_op, run_workload, segment_lists  # noqa: F401

@@ -870,6 +870,47 @@ def segment_attention(pool: Pool, q: np.ndarray, segments, page_lists, scale: fl
     return out
 
 
+def page_mass(pool: Pool, q: np.ndarray, segments, page_lists, scale: float = 0.0, lags=None) -> np.ndarray:
+    """Attention weight per page: the statistic the server-side drop policy
+    of [AKV-blog] section 7 (Dilemma 1) watches, the cumulative attention
+    weight of each block of the history.  For every segment, query row and
+    q head, the softmax weights over the segment's list (as in
+    segment_attention) are added to the page of each list entry; the result
+    is summed over rows, heads and segments ([num_pages], fp64)."""
+    L = pool.L
+    q = np.asarray(q, np.float64)
+    if scale == 0.0:
+        scale = 1.0 / np.sqrt(L.d_qk)
+    ex_all = check_extents(pool, page_lists)
+    mass = np.zeros(L.num_pages)
+    grp = L.n_q_heads // L.n_kv_heads
+    for qb, ql, eb, el in segments:
+        if ql == 0:
+            continue
+        ex = ex_all[eb:eb + el]
+        seg_lag = None
+        if lags is not None:
+            off = int(sum((ex_all[:eb, 2] - ex_all[:eb, 1]).tolist()))
+            n_e = int((ex[:, 2] - ex[:, 1]).sum())
+            seg_lag = np.asarray(lags)[off:off + n_e]
+        k, _ = pool.gather(ex, seg_lag)
+        lkv = k.shape[0]
+        if lkv < ql:
+            raise EInval("segment has fewer KV entries than queries")
+        page_of = np.repeat(ex[:, 0], ex[:, 2] - ex[:, 1])      # the page of every list entry
+        lim = last_visible(lkv, ql, np.arange(ql))
+        w = np.zeros(lkv)
+        for h in range(L.n_q_heads):
+            s = (q[qb:qb + ql, h, :] @ k[:, h // grp, :].T) * scale
+            s[np.arange(lkv)[None, :] > lim[:, None]] = -np.inf
+            s -= s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            w += p.sum(axis=0)
+        np.add.at(mass, page_of, w)
+    return mass
+
+
 # ---------------------------------------------------------------------------
 # dense brute force: the masked-softmax definition of [AKV-blog] section 2
 # ---------------------------------------------------------------------------

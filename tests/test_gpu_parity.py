@@ -846,3 +846,48 @@ def test_share_writes_nothing_and_copy_on_write_keeps_the_source(mla):
     assert err.max() <= 2 * RTOL_KEY
     np.testing.assert_array_equal(D.to_f64(pool.v_pages[pb, :, ob]), D.to_f64(pool.v_pages[pc, :, oc]))
     pool.close()
+
+
+# ---------------------------------------------------------------------------
+# attention mass per page (the server-side drop policy's statistic)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed,pairing,lq,deferred,heads,mode", [
+    (0, 0, 1, False, 32, "stress"), (1, 1, 1, True, 32, "stress"), (2, 0, 3, True, 32, "focus"),
+    (3, 0, 2, False, 64, "base"), (4, 1, 4, True, 32, "focus")])
+def test_page_mass_decode_full(seed, pairing, lq, deferred, heads, mode):
+    """A decode launch with the mass output set: every page's mass against
+    the oracle's page_mass (the softmax weights of every row and q head
+    summed per page), owed rotations included; the launch's total equals
+    query tokens x q heads; the attention outputs are unchanged."""
+    wl = _variant(W.decode_batch(seed, n_req=8, ctx_lo=1500, ctx_hi=6000, q_len=lq, deferred=deferred,
+                                 pairing=pairing, n_q_heads=heads), mode)
+    L = wl.layout
+    _say(f"[gpu] page mass: {wl.name} lq {lq} heads {heads} deferred {deferred}")
+    pool = D.make_pool(wl)
+    mass = torch.zeros(L.num_pages, dtype=torch.float32, device="cuda:0")
+    pool.attention_mass(mass)
+    pool, outs = D.run(wl, pool=pool)
+    got = mass.cpu().numpy().astype(np.float64)
+    op_pool = AO.Pool(L, wl.page_order, key_store=_key_store(wl))
+    want = np.zeros(L.num_pages)
+    n_rows = 0
+    for op in wl.ops:
+        if isinstance(op, W.Attention):
+            ex, rows, lags = oracle.segment_lists(op_pool, op.segments, with_lags=True)
+            want += AO.page_mass(op_pool, W.bf16_to_f64(op.q), rows, ex, op.scale, lags=lags)
+            n_rows += sum(sg.q_len for sg in op.segments) * L.n_q_heads
+        else:
+            oracle.apply_op(op_pool, op)
+    assert abs(got.sum() - n_rows) <= 1e-3 * n_rows, (got.sum(), n_rows)
+    err = np.abs(got - want)
+    bad = err > 2e-3 * want + 1e-6 * n_rows
+    assert not bad.any(), f"{bad.sum()} pages off; worst {err.max():.3e} at mass {want[err.argmax()]:.3e}"
+    _say(f"[gpu] page mass: {int((want > 0).sum())} pages, worst abs err {err.max():.2e}, total {got.sum():.3f}"
+         f" of {n_rows}")
+    # the side output leaves the attention as it was
+    pool2, outs2 = D.run(wl)
+    for o1, o2 in zip(outs, outs2):
+        assert torch.equal(o1["out"].view(torch.int16), o2["out"].view(torch.int16))
+    pool.attention_mass(None)
+    pool.close()
+    pool2.close()

@@ -740,3 +740,13 @@ def test_share_rules():
     hp.seq_release(b)                               # the last holder: a's pages return
     assert len(hp.queues()[0]) == free0 + 3
     hp.append(c, np.arange(3))
+
+
+def test_attention_mass_is_validated():
+    """akv_attention_mass: a page-table-only pool has no device output
+    (AKV_ESTATE); NULL disables it everywhere."""
+    lay = W.Layout(8, 2, 0, 128, 128, 16, 8)
+    hp = _host_pool(lay, None)
+    with pytest.raises(akv.AkvError) as ei:
+        hp.attention_mass(None)
+    assert ei.value.status == akv.AKV_ESTATE

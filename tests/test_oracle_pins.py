@@ -395,6 +395,67 @@ def test_shared_pages_outlive_their_source():
     assert list(pool.free)[-4:] == pages_a
 
 
+# ---------------------------------------------------------------------------
+# attention mass per page ("AKV: Cache Engineering for Autonomous Agents ...",
+# section 7, Dilemma 1: the cumulative attention weight of each block)
+# ---------------------------------------------------------------------------
+def _mass_pool(rng, page_size=4):
+    lay = _lay(page_size=page_size, num_pages=40, n_q_heads=4, n_kv_heads=2)
+    pool = AO.Pool(lay, rng.permutation(40))
+    a, b = pool.seq_create(), pool.seq_create()
+    _fill(pool, a, 50, rng)
+    _fill(pool, b, 23, rng)
+    pool.drop(a, [[5, 17], [30, 31]], auto_compact=False)
+    ex_a, ex_b = pool.extents(a), pool.extents(b)
+    ex = np.concatenate([ex_a, ex_b])
+    segs = [(0, 3, 0, len(ex_a)), (3, 2, len(ex_a), len(ex_b))]
+    return pool, lay, ex, segs
+
+
+def test_page_mass_uniform_queries_closed_form():
+    """Zero queries make every visible weight 1 / (limit + 1): the mass of a
+    page is heads x sum over rows of (its entries up to the row's causal
+    limit) / (limit + 1), counted here from the extents alone."""
+    rng = np.random.default_rng(31)
+    pool, lay, ex, segs = _mass_pool(rng)
+    q = np.zeros((5, lay.n_q_heads, lay.d_qk))
+    got = AO.page_mass(pool, q, segs, ex)
+    want = np.zeros(lay.num_pages)
+    for qb, ql, eb, el in segs:
+        pages = np.concatenate([[p] * (hi - lo) for p, lo, hi in ex[eb:eb + el]])
+        lkv = len(pages)
+        for i in range(ql):
+            lim = lkv - ql + i
+            for idx in range(lim + 1):
+                want[pages[idx]] += lay.n_q_heads / (lim + 1)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    assert abs(got.sum() - 5 * lay.n_q_heads) < 1e-9
+
+
+def test_page_mass_sums_to_rows_and_follows_a_sharp_key():
+    """Random queries: the mass of a launch sums to (query rows x q heads);
+    a query aimed hard at one key puts almost all of its row's weight on
+    that key's page; pages of dropped tokens get nothing."""
+    rng = np.random.default_rng(32)
+    pool, lay, ex, segs = _mass_pool(rng)
+    q = rng.standard_normal((5, lay.n_q_heads, lay.d_qk))
+    m = AO.page_mass(pool, q, segs, ex)
+    assert abs(m.sum() - 5 * lay.n_q_heads) < 1e-9
+    used = set(ex[:, 0].tolist())
+    assert np.all(m[[p for p in range(lay.num_pages) if p not in used]] == 0)
+    # row 0 of segment 0, every head aimed at list entry 2 of its own list
+    k, _ = pool.gather(ex[:segs[0][3]])
+    q2 = q.copy()
+    grp = lay.n_q_heads // lay.n_kv_heads
+    for h in range(lay.n_q_heads):
+        q2[0, h] = 200.0 * k[2, h // grp] / np.linalg.norm(k[2, h // grp])
+    m2 = AO.page_mass(pool, q2, [segs[0]], ex[:segs[0][3]])
+    page2 = np.repeat(ex[:segs[0][3], 0], ex[:segs[0][3], 2] - ex[:segs[0][3], 1])[2]
+    # the aimed row's heads each give nearly 1 to page2; the two other rows at most 2 x heads in total
+    assert m2[page2] >= lay.n_q_heads * (1 - 1e-6)
+    assert abs(m2.sum() - 3 * lay.n_q_heads) < 1e-9
+
+
 def test_repos_position_range_is_atomic():
     rng = np.random.default_rng(4)
     pool = AO.Pool(_lay())
