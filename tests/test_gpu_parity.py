@@ -891,3 +891,14 @@ def test_page_mass_decode_full(seed, pairing, lq, deferred, heads, mode):
     pool.attention_mass(None)
     pool.close()
     pool2.close()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_share_through_background_compaction_full(seed):
+    """The background pass copies a sharer's rows (shared ones included) out
+    of a released source's pages, which go back to the queue at once; a new
+    sequence appends into them (its writes wait for the copies that read
+    them); both sequences attend.  Tables, every visible row and every
+    output row against the oracle; then each sequence materialized."""
+    wl = W.share_background(seed, page_size=[8, 16][seed])
+    _deferred_parity(wl, D.make_pool(wl), "auto").close()

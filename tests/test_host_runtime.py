@@ -750,3 +750,11 @@ def test_attention_mass_is_validated():
     with pytest.raises(akv.AkvError) as ei:
         hp.attention_mass(None)
     assert ei.value.status == akv.AKV_ESTATE
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_share_through_background_compaction_bit_exact(seed):
+    """A sharer compacted by the deferred pass while its source is a
+    released, still-shared sequence: the pass lets go of the source's pages,
+    which a new sequence then takes; tables and queues equal the oracle's."""
+    _replay(W.share_background(seed, page_size=[8, 16, 8][seed]))

@@ -39,7 +39,7 @@ __all__ = [
     "Freeze", "Share", "Materialize",
     "Segment", "Attention", "Workload", "to_bf16", "bf16_to_f64",
     "c1_tiny", "c2_64k", "c3_mla", "c4_batched", "c5_128k", "decode_batch", "decode_with_idle", "retrigger",
-    "with_idle_compaction", "share_fuzz",
+    "with_idle_compaction", "share_fuzz", "share_background",
     "fuzz_small",
     "CONFIGS", "make", "query_variant",
 ]
@@ -729,6 +729,40 @@ def share_fuzz(seed: int, mla: bool = False, page_size: int = 16, d: int = 64, p
     wl = Workload(f"share_fuzz_{seed}", lay, rng.permutation(lay.num_pages).astype(np.int32), ops)
     wl.notes.update(materialize=mat)
     return wl
+
+
+def share_background(seed: int, page_size: int = 8, n_src: int = 400, n_q: int = 16) -> Workload:
+    """Shared rows through a background compaction pass: sequence 0 is
+    frozen and shared (at +50) by sequence 1, which appends its own tokens;
+    sequence 0 is released while shared; in deferred compaction mode
+    sequence 1 drops every other block of 4 shared tokens (fragmented), and
+    the background pass moves its rows, shared ones included, into its own
+    pages, so the source's last holder lets go and the source's pages return
+    to the queue while the copies that read them may still run; a new
+    sequence then appends into pages the queue hands out, and sequences 1
+    and 2 attend in one launch."""
+    rng = _rng(seed)
+    lay = Layout(8, 2, 0, 64, 64, page_size, 0, rope_theta=10000.0)
+    ops: list = [SeqCreate(), SeqCreate()]
+    ops.append(_append_op(rng, lay, 0, np.arange(n_src, dtype=np.int32)))
+    ops.append(Freeze(0))
+    ops.append(Share(0, 0, n_src, 1, 50))
+    ops.append(_append_op(rng, lay, 1, np.arange(n_src + 50, n_src + 90, dtype=np.int32)))
+    ops.append(Release(0))
+    ops.append(CompactMode(True))
+    ops.append(Drop(1, _spans([(b, b + 4) for b in range(4, n_src - 8, 8)])))
+    ops.append(CompactPending(1 << 30))
+    ops.append(SeqCreate())
+    ops.append(_append_op(rng, lay, 2, np.arange(0, n_src, dtype=np.int32)))
+    segs = []
+    for i, (sq, p0) in enumerate([(1, 1_000_000), (2, 2_000_000)]):
+        ops.append(_append_op(rng, lay, sq, np.arange(p0, p0 + n_q, dtype=np.int32)))
+        segs.append(Segment(sq, i * n_q, n_q, np.zeros((0, 2), np.int32)))
+    ops.append(Attention(_normal_bf16(rng, (2 * n_q, lay.n_q_heads, lay.d_qk), scale=0.5), segs))
+    # tight: the new sequence's pages must include the source's, given back
+    # during the pass
+    lay.num_pages = (n_src + 90 + n_src // 2 + 60) // page_size + 12
+    return Workload(f"share_background_{seed}", lay, rng.permutation(lay.num_pages).astype(np.int32), ops)
 
 
 # --------------------------------------------------------------------------
