@@ -1022,6 +1022,321 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Segment-batch attention for the MLA row, direct-to-LDS (gfx950): K_nope
+// (per head, DNOPE), K_pe (shared by the heads or per head, DPE) and V (per
+// head, DV).  The math, lane layout and row DMA are those of k_seg_attn_dl;
+// the K tile is held in two LDS parts (K_nope, then K_pe) and the S^T k-steps
+// walk K_nope then K_pe, so Q rows are [q_nope | q_pe].  A 64-key stage holds
+// 40 KiB of K and V, so three stages fit in LDS: tile t goes to stage t % 3
+// and its slots to ring entry t % 3.  With three stages the scores are not
+// computed a tile ahead (that would leave one iteration to land each tile):
+// iteration j waits for tile j's rows (issued at iteration j - 2; iteration
+// j - 1's loads stay in flight), barrier, issues tile j + 2's rows into tile
+// j - 1's stage and tile j + 4's slots into tile j + 1's ring entry, then
+// runs S, softmax and PV of tile j; the two waves of a SIMD overlap each
+// other's matrix and vector work.
+// ---------------------------------------------------------------------------
+template <int DNOPE, int DPE, int DV>
+__global__ __launch_bounds__(512, 1) void k_seg_attn_mla(AttnArgs a) {
+  constexpr int NW = 8;
+  constexpr int DQK = DNOPE + DPE;
+  constexpr int RB = 32 * NW;
+  constexpr int KT = ATTN_KTILE;
+  constexpr int NKS = DQK / 16, NKN = DNOPE / 16;
+  constexpr int NCB = DV / 32;
+  constexpr int CHN = DNOPE / 8, CHP = DPE / 8, CHV = DV / 8;
+  using PN = LdsPart<CHN, 16>;
+  using PP = LdsPart<CHP, 16>;
+  using PV = LdsPart<CHV, 64>;
+  constexpr int OP = PN::BYTES, OV = PN::BYTES + PP::BYTES;
+  constexpr int SSTAGE = OV + PV::BYTES;
+  static_assert(KT == 64 && CHN % NW == 0 && CHP % NW == 0 && CHV % NW == 0 && 64 % CHP == 0,
+                "blocks per wave");
+  constexpr int NIW = (CHN + CHP + CHV) / NW;          // row loads per wave per tile
+  static_assert(NIW + 1 <= 15, "vmcnt");
+  __shared__ __attribute__((aligned(16))) unsigned char st0[SSTAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[SSTAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st2[SSTAGE];
+  __shared__ __attribute__((aligned(16))) int32_t sr0[NW * 64];
+  __shared__ __attribute__((aligned(16))) int32_t sr1[NW * 64];
+  __shared__ __attribute__((aligned(16))) int32_t sr2[NW * 64];
+
+  const AttnItem it = a.items[blockIdx.x];
+  if (it.seg < 0) return;
+  const AttnSeg sg = a.segs[it.seg];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 5, l32 = lane & 31;
+  const int G = a.group;
+  const int lq = sg.q_len, lkv = sg.lkv;
+  const int rows_total = lq * G;
+  const int brow_last = min(it.row0 + RB, rows_total) - 1;
+  const int lim_first = lkv - lq + it.row0 / G;
+  const int lim_last = lkv - lq + brow_last / G;
+  const int k_end = it.k_end;
+  const int k_stop = min(k_end, lim_last + 1);
+  const int n_tiles = k_stop > it.k_begin ? (k_stop - it.k_begin + KT - 1) / KT : 0;
+  const int Hkv = a.n_kv_heads, S = a.page_size, lg = a.log2_page;
+  const int kvh = it.kvh;
+  const int32_t* __restrict__ slots = a.slots + sg.list_off;
+  const int HS = Hkv * S, hoff = kvh * S;
+  const int HP = a.kpe_heads * S, hpoff = (a.kpe_heads > 1 ? kvh : 0) * S;
+
+  const int r0 = it.row0 + 32 * w + l32;
+  const bool valid = r0 < rows_total;
+  const int tok = valid ? r0 / G : 0;
+  const int hq = kvh * G + (valid ? r0 - tok * G : 0);
+  const int lim = valid ? min(lkv - lq + tok, k_end - 1) : k_stop - 1;
+  bf16x8 qf[NKS];
+  {
+    const uint16_t* qp = a.q + ((size_t)(sg.q_begin + tok) * a.n_q_heads + hq) * DQK + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (valid) {
+        qf[ks] = *(const bf16x8*)(qp + 16 * ks);
+      } else {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qf[ks] = __builtin_bit_cast(bf16x8, z);
+      }
+    }
+  }
+
+  auto stage_ptr = [&](int s) __attribute__((always_inline)) -> unsigned char AKV_LDS* {
+    return (unsigned char AKV_LDS*)(s == 0 ? st0 : (s == 1 ? st1 : st2));
+  };
+  auto ring_ptr = [&](int e) __attribute__((always_inline)) -> int32_t AKV_LDS* {
+    int32_t* r = e == 0 ? sr0 : (e == 1 ? sr1 : sr2);
+    return (int32_t AKV_LDS*)r + 64 * w;
+  };
+  auto slot_load = [&](int e, int t) __attribute__((always_inline)) {
+    const int idx = min(it.k_begin + t * KT + lane, lkv - 1);
+    __builtin_amdgcn_global_load_lds(slots + idx, (void AKV_LDS*)ring_ptr(e), 4, 0, 0);
+  };
+  // Row loads of one tile: this wave's blocks b = w + NW m of each part;
+  // lane holds key b + CH (lane / CH), chunk lane % CH of the part.
+  auto issue_tile = [&](unsigned char AKV_LDS* stg, int e) __attribute__((always_inline)) {
+    const int32_t AKV_LDS* ring = ring_ptr(e);
+#pragma unroll
+    for (int m = 0; m < CHN / NW; ++m) {
+      const int b = w + NW * m, c = lane % CHN;
+      const int slot = ring[b + CHN * (lane / CHN)];
+      const uint32_t row = __umul24(slot >> lg, HS) + hoff + (slot & (S - 1));
+      __builtin_amdgcn_global_load_lds(a.k_a + (size_t)row * DNOPE + 8 * c, (void AKV_LDS*)(stg + b * PN::BLK),
+                                       16, 0, 0);
+    }
+#pragma unroll
+    for (int m = 0; m < CHP / NW; ++m) {
+      const int b = w + NW * m, c = lane % CHP;
+      const int slot = ring[b + CHP * (lane / CHP)];
+      const uint32_t row = __umul24(slot >> lg, HP) + hpoff + (slot & (S - 1));
+      __builtin_amdgcn_global_load_lds(a.k_b + (size_t)row * DPE + 8 * c, (void AKV_LDS*)(stg + OP + b * PP::BLK),
+                                       16, 0, 0);
+    }
+#pragma unroll
+    for (int m = 0; m < CHV / NW; ++m) {
+      const int b = w + NW * m, c = lane % CHV;
+      const int slot = ring[b + CHV * (lane / CHV)];
+      const uint32_t row = __umul24(slot >> lg, HS) + hoff + (slot & (S - 1));
+      __builtin_amdgcn_global_load_lds(a.v + (size_t)row * DV + 8 * c, (void AKV_LDS*)(stg + OV + b * PV::BLK),
+                                       16, 0, 0);
+    }
+  };
+
+  f32x16 oacc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[cb][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = a.scale_log2e;
+  int koffN[2], koffP[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    koffN[kb] = PN::off(32 * kb + l32, g);
+    koffP[kb] = OP + PP::off(32 * kb + l32, g);
+  }
+  const int qq = lane >> 4, ii = lane & 15;
+  const int voff0 = OV + PV::off(4 * g + (ii >> 2), 0) + 2 * (16 * (qq & 1) + 4 * (ii & 3));
+
+  auto qk = [&](const unsigned char AKV_LDS* stg, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8 af[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        af[kb] = ks < NKN ? *(const bf16x8 AKV_LDS*)(stg + koffN[kb] + 32 * ks)
+                          : *(const bf16x8 AKV_LDS*)(stg + koffP[kb] + 32 * (ks - NKN));
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], qf[ks], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1], qf[ks], sacc[1], 0, 0, 0);
+    }
+  };
+  auto sm_mask = [&](f32x16 (&sacc)[2], int j) __attribute__((always_inline)) {
+    const int k0 = it.k_begin + j * KT;
+    if ((k0 + KT > k_end) || (k0 + KT - 1 > lim_first)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key > lim) sacc[kb][i] = -INFINITY;
+        }
+    }
+  };
+  auto sm_max = [&](const f32x16 (&sacc)[2]) __attribute__((always_inline)) -> float {
+    float m = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, sacc[kb][i]);
+    return fmaxf(m, __shfl_xor(m, 32));
+  };
+  auto sm_rescale = [&](float mx, int j) __attribute__((always_inline)) -> float {
+    const float m_cand = fmaxf(m_run, mx * c2);
+    if (__ballot(m_cand > m_run + RESCALE_LOG2)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
+      l_run *= alpha;
+      if (j > 0) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+      }
+      m_run = m_cand;
+    }
+    return (m_run == -INFINITY) ? 0.f : m_run;
+  };
+  auto sm_exp = [&](const f32x16 (&sacc)[2], float m_use, bf16x8 (&pf)[4]) __attribute__((always_inline)) {
+    float rs = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kb = t >> 1, q0 = 8 * (t & 1);
+      u32x4 pk;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][q0 + 2 * k], c2, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][q0 + 2 * k + 1], c2, -m_use));
+        rs += p0 + p1;
+        pk[k] = pack_bf2(p0, p1);
+      }
+      pf[t] = __builtin_bit_cast(bf16x8, pk);
+    }
+    l_run += rs;
+  };
+  auto pv = [&](const unsigned char AKV_LDS* stg, const bf16x8 (&pf)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const unsigned char AKV_LDS* vp = stg + voff0 + 2 * 32 * cb;
+        const int kA = 16 * t, kB = 16 * t + 8;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 AKV_LDS*)(vp + (kA % CHV) * PV::BLK + (kA / CHV) * (CHV * 16)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 AKV_LDS*)(vp + (kB % CHV) * PV::BLK + (kB / CHV) * (CHV * 16)));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[cb], 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int t = 0; t < 3; ++t) slot_load(t, t);
+  __builtin_amdgcn_s_waitcnt(0);
+  issue_tile(stage_ptr(0), 0);
+  issue_tile(stage_ptr(1), 1);
+  slot_load(0, 3);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const bool idle = it.row0 + 32 * w >= rows_total;
+  // iteration j: tile j landed at iteration j - 2; iteration j - 1's loads
+  // (NIW rows + 1 slot load) may still be in flight
+  constexpr int WAITV = NIW + 1;
+  constexpr int WAIT_SYNC = (WAITV & 0xF) | ((WAITV >> 4) << 14) | (0x7 << 4);
+  auto sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(WAIT_SYNC);
+    __builtin_amdgcn_s_barrier();
+  };
+  const int lmask = min(k_end, lim_first + 1) - it.k_begin;
+  const int jm = lmask > 0 ? lmask / KT : 0;
+  auto iter = [&](int j, auto c, auto masked) __attribute__((always_inline)) {
+    constexpr int C = decltype(c)::value;
+    sync();
+    issue_tile(stage_ptr((C + 2) % 3), (C + 2) % 3);
+    slot_load((C + 1) % 3, j + 4);
+    f32x16 sc[2];
+    qk(stage_ptr(C), sc);
+    if constexpr (decltype(masked)::value) sm_mask(sc, j);
+    const float m_use = sm_rescale(sm_max(sc), j);
+    bf16x8 pf[4];
+    sm_exp(sc, m_use, pf);
+    pv(stage_ptr(C), pf);
+  };
+  auto idle_iter = [&](int j, auto c) __attribute__((always_inline)) {
+    constexpr int C = decltype(c)::value;
+    sync();
+    issue_tile(stage_ptr((C + 2) % 3), (C + 2) % 3);
+    slot_load((C + 1) % 3, j + 4);
+  };
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+  using J2 = std::integral_constant<int, 2>;
+  using TF = std::false_type;
+  using TT = std::true_type;
+  int j = 0;
+  if (idle) {
+    for (; j < n_tiles; j += 3) {
+      idle_iter(j, J0{});
+      idle_iter(j + 1, J1{});
+      idle_iter(j + 2, J2{});
+    }
+  } else {
+    for (; j + 3 <= jm; j += 3) {
+      iter(j, J0{}, TF{});
+      iter(j + 1, J1{}, TF{});
+      iter(j + 2, J2{}, TF{});
+    }
+    for (; j < n_tiles; j += 3) {
+      iter(j, J0{}, TT{});
+      iter(j + 1, J1{}, TT{});
+      iter(j + 2, J2{}, TT{});
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  const float l = l_run + __shfl_xor(l_run, 32);
+  if (!valid) return;
+  if (it.part < 0) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* op = a.out + ((size_t)(sg.q_begin + tok) * a.n_q_heads + hq) * DV;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        u32x2 v2 = {pack_bf2(oacc[cb][4 * m] * inv, oacc[cb][4 * m + 1] * inv),
+                    pack_bf2(oacc[cb][4 * m + 2] * inv, oacc[cb][4 * m + 3] * inv)};
+        *(u32x2*)(op + 32 * cb + 8 * m + 4 * g) = v2;
+      }
+  } else {
+    const int prow = it.part + 32 * w + l32;
+    float* po = a.part_o + (size_t)prow * DV;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f32x4 v4 = {oacc[cb][4 * m], oacc[cb][4 * m + 1], oacc[cb][4 * m + 2], oacc[cb][4 * m + 3]};
+        *(f32x4*)(po + 32 * cb + 8 * m + 4 * g) = v4;
+      }
+    if (g == 0) {
+      a.part_ml[2 * (size_t)prow] = m_run;
+      a.part_ml[2 * (size_t)prow + 1] = l;
+    }
+  }
+}
+
 // Split-KV merge: O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j (m in log2
 // units).  One wave per row, four rows per block, so every row of every item
 // is its own wave: lane j holds split j's (m, l) (the planner splits at most
@@ -1146,6 +1461,9 @@ static hipError_t launch_attn_t(hipStream_t st, const AttnArgs& a) {
       hipLaunchKernelGGL((k_seg_attn_dl<128, 128, 0, 8, 1, 4, true>), dim3(a.n_items), dim3(512), 0, st, a);
     else
       hipLaunchKernelGGL((k_seg_attn_dl<128, 128, 0, 8, 1, 4, false>), dim3(a.n_items), dim3(512), 0, st, a);
+  } else if constexpr (DNOPE == 128 && DQK == 192 && DV == 128) {
+    // the MLA row (K_nope 128, K_pe 64, V 128): direct-to-LDS, three stages
+    hipLaunchKernelGGL((k_seg_attn_mla<128, 64, 128>), dim3(a.n_items), dim3(512), 0, st, a);
   } else {
     hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE, 8>), dim3(a.n_items), dim3(512), 0, st, a);
   }

@@ -1491,10 +1491,12 @@ void plan_attention(const akv_pool* p, const akv_segment* segs, int32_t n_segs,
   for (int32_t i = 0; i < n_segs; ++i)
     if (segs[i].q_len > 0) base += (int64_t)L.n_kv_heads * ((segs[i].q_len * (int64_t)G + RB - 1) / RB);
   int target = 1;
-  // split the key range only when the row tiles alone cannot fill the CUs
-  // (at most 16 here, 64 for decode items: the combine kernel holds one split
-  // per lane of a wave)
-  if (base > 0 && base < n_cu) target = (int)std::min<int64_t>(16, (2LL * n_cu + base - 1) / base);
+  // split the key range only when the row tiles alone cannot fill the CUs,
+  // into about one work item per CU (a prefill block holds its CU's LDS, so
+  // a second round of blocks would pay its pipeline fill again); at most 16
+  // here, 64 for decode items: the combine kernel holds one split per lane of
+  // a wave
+  if (base > 0 && base < n_cu) target = (int)std::min<int64_t>(16, ((int64_t)n_cu + base - 1) / base);
   // ... or when one row tile alone would hold a CU well past the even share
   // of the launch (few query rows over long lists: decode): such a segment's
   // key range is cut into blocks of at most half a CU's share.
