@@ -169,6 +169,37 @@ def cpu_baseline(wl):
                         f"({t_att:.1f} s)"))
 
 
+def hbm_reference() -> dict:
+    """Streaming rates of the chip for the access kinds of the HBM-bound
+    kernels, measured with torch's own elementwise kernels on contiguous
+    4 GiB buffers (well past the 256 MB Infinity Cache): an in-place
+    read-modify-write (x *= 1, what repos does to its keys) and a copy
+    (what compaction and clones do).  A reference for the roofline
+    fractions, not part of the path."""
+    import torch
+    n = 4 << 30
+    x = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda:0")
+    y = torch.empty_like(x)
+    out = {}
+    for name, fn, nbytes in (("rmw_in_place", lambda: x.mul_(1.0), 2 * n),
+                             ("copy", lambda: y.copy_(x), 2 * n)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        t = float(np.median(ms))
+        out[name] = {"bytes": nbytes, "ms": round(t, 4), "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
+                     "frac_of_8TBps": round(nbytes / (t * 1e-3) / 8e12, 4)}
+    return {"hbm_reference": out, "note": "torch elementwise kernels on contiguous 4 GiB bf16 buffers"}
+
+
 def compact_extra(pool, seqs, L) -> dict:
     """Extra line: forced compaction (k_move_tokens) of C2 sequences after their
     step, each the only work on its copy since that step (the earliest timed
@@ -522,7 +553,13 @@ def main():
                     help="layers of the extra batched-repos line (0: skip it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--hbm-reference", action="store_true",
+                    help="only time plain streaming kernels (torch's in-place multiply and copy over 4 GiB, "
+                         "out of every cache): the chip's rates for in-place read-modify-write and copy")
     args = ap.parse_args()
+    if args.hbm_reference:
+        print(json.dumps(hbm_reference()), flush=True)
+        return
     if args.calibrate_copy:
         import torch
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
