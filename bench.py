@@ -325,6 +325,11 @@ def run_config(args) -> dict:
     kern = None
     n_dec = args.decode_steps if args.config in ("decode", "decode_fused", "decode_compact", "decode_mass") else 1
     first_walls = []
+    # no collector pause inside a timed step, and none right before it (the
+    # idle GPU it leaves makes the next launches slower): one collection
+    # before the reps, the collector off until they end
+    gc.collect()
+    gc.disable()
     for rep in range(args.warmup + args.steps):
         pool = D.make_pool(wl)
         if args.config == "c2_fused":
@@ -361,8 +366,6 @@ def run_config(args) -> dict:
                 else:
                     D.apply_op(pool, op, keep)
 
-        gc.collect()
-        gc.disable()        # no collector pause inside the timed step
         t0 = time.perf_counter()
         run_ops(0)
         if n_dec > 1:
@@ -377,7 +380,6 @@ def run_config(args) -> dict:
         if n_dec > 1:
             first = t1 - t0
             wall = (time.perf_counter() - t1) / (n_dec - 1)
-        gc.enable()
         if timed:
             walls.append(wall)
             if n_dec > 1:
@@ -429,6 +431,7 @@ def run_config(args) -> dict:
                     "k_seg_attn_dl<128,128,0,8,1,4,rotating>" if kern.startswith("k_seg_attn_dl") else kern)
         pool.close()
         del pool, keep
+    gc.enable()
     ms_step = float(np.median(walls)) * 1e3
     attn_ms = tot["attention"][0] / max(tot["attention"][1], 1)
     n_launch_steps = max(args.steps, 1) * n_dec     # steps whose kernels the timers saw
