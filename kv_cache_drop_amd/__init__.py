@@ -18,7 +18,9 @@ import numpy as np
 __all__ = ["AkvError", "Pool", "Tree", "lib", "LIB_PATH", "SYMBOLS", "KERNEL_KINDS", "attention_supported",
            "repos_layers", "EV_TOKEN", "EV_DROP", "EV_REPOS"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libakv.so")
+# The built library; AKV_LIB_PATH may name another build of the same sources
+# (the host-sanitized one of `python -m kv_cache_drop_amd.build --sanitize`).
+LIB_PATH = os.environ.get("AKV_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libakv.so")
 
 AKV_OK, AKV_EINVAL, AKV_ERANGE, AKV_ENOMEM, AKV_ESTATE, AKV_EHIP = 0, -1, -2, -3, -4, -5
 STATUS_NAMES = {0: "AKV_OK", -1: "AKV_EINVAL", -2: "AKV_ERANGE", -3: "AKV_ENOMEM",

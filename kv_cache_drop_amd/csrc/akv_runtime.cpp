@@ -2996,8 +2996,10 @@ akv_status akv_attention_plan(akv_pool* p, int32_t n_q_tokens, const akv_segment
     static_assert(sizeof(akv_attn_combine) == sizeof(akv::CombItem), "combine layouts");
     if ((items && items_cap < *n_items) || (comb && comb_cap < *n_comb))
       return fail(AKV_ERANGE, "plan needs %d items and %d combine entries", *n_items, *n_comb);
-    if (items) std::memcpy(items, plan.items.data(), plan.items.size() * sizeof(akv::AttnItem));
-    if (comb) std::memcpy(comb, plan.comb.data(), plan.comb.size() * sizeof(akv::CombItem));
+    if (items && !plan.items.empty())
+      std::memcpy(items, plan.items.data(), plan.items.size() * sizeof(akv::AttnItem));
+    if (comb && !plan.comb.empty())
+      std::memcpy(comb, plan.comb.data(), plan.comb.size() * sizeof(akv::CombItem));
     return AKV_OK;
   } catch (const std::bad_alloc&) {
     return fail(AKV_ENOMEM, "host allocation failed");
