@@ -145,10 +145,19 @@ def cpu_baseline(wl):
         oracle.apply_op(pool, op)
     att = ops[-1]
     t0 = time.perf_counter()
+    t_repos, n_repos = 0.0, 0
     for op in ops[i_drop:-1]:
-        oracle.apply_op(pool, op)
+        if isinstance(op, W.Repos):
+            n_repos += int(np.count_nonzero(pool.repos_deltas(op.seq, op.spans, op.deltas)))
+            t1 = time.perf_counter()
+            oracle.apply_op(pool, op)
+            t_repos += time.perf_counter() - t1
+        else:
+            oracle.apply_op(pool, op)
     ex, rows = oracle.segment_lists(pool, att.segments)
     t_ops = time.perf_counter() - t0
+    L = wl.layout
+    repos_bytes = 2.0 * L.n_rope_heads * L.d_rope * 2 * n_repos      # the bf16 bytes the device rotation moves
     q = W.bf16_to_f64(att.q)
     _CPU_JOB.update(pool=pool, q=q, rows=rows, ex=ex)
     tasks = [(si, g) for si in range(len(rows)) for g in range(wl.layout.n_kv_heads)]
@@ -164,6 +173,7 @@ def cpu_baseline(wl):
     return dict(value=round(flops / t_step / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
                 cpu=model, ms_per_step=round(t_step * 1e3, 1),
                 query_tokens_per_s=round(n_q / t_step, 1),
+                repos_ms=round(t_repos * 1e3, 1), repos_gbps_equiv=round(repos_bytes / max(t_repos, 1e-9) / 1e9, 3),
                 sample=(f"the whole 64K step once: drop / repos / append / page lists in one process "
                         f"({t_ops:.1f} s), attention for all {n_q} query rows as {len(tasks)} "
                         f"(segment, kv head) items over {cores} worker processes with one BLAS thread each "
