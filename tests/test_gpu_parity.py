@@ -853,7 +853,7 @@ def test_share_writes_nothing_and_copy_on_write_keeps_the_source(mla):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("seed,pairing,lq,deferred,heads,mode", [
     (0, 0, 1, False, 32, "stress"), (1, 1, 1, True, 32, "stress"), (2, 0, 3, True, 32, "focus"),
-    (3, 0, 2, False, 64, "base"), (4, 1, 4, True, 32, "focus")])
+    (3, 0, 2, False, 64, "base"), (4, 1, 4, True, 32, "focus"), (5, 0, 2, True, 32, "stress")])
 def test_page_mass_decode_full(seed, pairing, lq, deferred, heads, mode):
     """A decode launch with the mass output set: every page's mass against
     the oracle's page_mass (the softmax weights of every row and q head
