@@ -1146,11 +1146,12 @@ akv_status compact_plan(akv_pool* p, int32_t s, std::vector<akv::MovePair>& mv) 
   }
   mv.reserve(mv.size() + nv);
   std::vector<int32_t> shared_src;   // slots given up in other sequences' pages
+  const bool shares = !q.owners.empty();
   for (int64_t i = 0; i < nv; ++i) {
     const int32_t t = order[i];
     const int32_t dst = dest[i / S] * S + (int32_t)(i % S);
     mv.push_back({q.slot[t], dst});
-    if (foreign_slot(p, s, q.slot[t])) shared_src.push_back(q.slot[t]);
+    if (shares && foreign_slot(p, s, q.slot[t])) shared_src.push_back(q.slot[t]);
     q.slot[t] = dst;
     p->pages[dest[i / S]].toks.push_back(t);
   }
@@ -1322,11 +1323,12 @@ void repos_items_append(const akv_pool* p, const SeqRec& q, const std::vector<Ru
   size_t span_tokens = 0;
   for (const Run& r : runs) span_tokens += (size_t)(r.e - r.b);
   items.reserve(items.size() + span_tokens / (size_t)std::min(max_rows, S) + 2 * runs.size() + 16);
+  const bool shares = !q.owners.empty();   // the sequence holds slots in other sequences' pages
   for (const Run& r : runs) {
     int32_t di = -1;   // looked up at the run's first moved token
     for (int32_t t = r.b; t < r.e; ++t) {
       if (q.dropped[t]) continue;
-      if (foreign_slot(p, q.id, q.slot[t])) continue;   // a shared row is not written: the token owes it
+      if (shares && foreign_slot(p, q.id, q.slot[t])) continue;   // a shared row is not written: the token owes it
       if (di < 0) {
         auto f = didx.find(r.d);
         if (f == didx.end()) {
@@ -1363,6 +1365,7 @@ void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<Run>& run
 // Positions after a repos; tokens whose rows are shared pages (not rotated in
 // place) owe the rotation instead, as after a deferred repos.
 void repos_commit(const akv_pool* p, SeqRec& q, const std::vector<Run>& runs, bool owe_shared = true) {
+  owe_shared = owe_shared && !q.owners.empty();
   for (const Run& r : runs)
     for (int32_t t = r.b; t < r.e; ++t)
       if (!q.dropped[t]) {
