@@ -687,7 +687,8 @@ def share_fuzz(seed: int, mla: bool = False, page_size: int = 16, d: int = 64, p
     positions (one delta each, either sign, or 0); sequence 1 appends, drops
     shared and own tokens, repositions across both, then compacts or
     materializes (copy on write); sequence 0 is released while shared;
-    sequence 2 drops shared tokens; sequence 3 clones half of sequence 1.
+    sequence 2 drops shared tokens and splices over shared rows; sequence 3
+    clones half of sequence 1.
     Then sequences 1, 2 and 3 append n_q query tokens each (positions past
     every earlier one, so they are each list's last entries) and attend in
     one launch."""
@@ -719,6 +720,11 @@ def share_fuzz(seed: int, mla: bool = False, page_size: int = 16, d: int = 64, p
     ops.append(Materialize(1) if mat else Compact(1, 1))
     ops.append(Release(0))                     # still shared: its pages stay
     ops.append(Drop(2, _spans([(3, 11)])))
+    # a splice over shared rows: the span's shared tokens give their slots
+    # up, the stub goes to sequence 2's own pages, the shared tokens
+    # downstream owe the shift
+    stub = _append_op(rng, lay, 2, np.zeros(5, np.int32))
+    ops.append(Splice(2, _spans([(20, 60)]), np.array([5], np.int32), stub.k, stub.kpe, stub.v))
     ops.append(Clone(1, 0, n1 // 2, 3, int(rng.choice([0, 55]))))
     segs = []
     for i, sq in enumerate((1, 2, 3)):
