@@ -32,7 +32,20 @@
  *   themselves after akv_sync or after such a launch).
  * - Calls on one pool are not re-entrant; separate pools are independent.
  * - Every call validates all arguments before changing any state: a call that
- *   fails leaves the pool as it was.  akv_last_error() gives the reason.
+ *   fails leaves the pool as it was.  akv_last_error() gives the reason.  The
+ *   exception is AKV_EHIP: a HIP call that fails is seen after the host
+ *   metadata has changed, and the rows the call was to write are then
+ *   undefined (release the pool).
+ * - Debug switches, read from the environment once per process:
+ *   AKV_CHECKS=1 checks every device work list on the host before its launch
+ *   (slots and pages inside the pool and in use, rows inside their page,
+ *   rotate items disjoint, copy destinations distinct and apart from the
+ *   sources, attention items covering each row tile's keys once); a failed
+ *   check is a library bug, returned as AKV_ESTATE with "AKV_CHECKS" in the
+ *   error text.  AKV_TRACE=1 prints one line per planning decision to stderr.
+ *   AKV_COMPACT_THRESHOLD=x (0 < x <= 1) replaces the 0.40 default
+ *   threshold.  AKV_FAULT_INJECT=launch makes every kernel launch report
+ *   failure once enqueued (AKV_EHIP), for tests of error handling.
  * - Spans are half-open [begin, end) over a sequence's logical token indices,
  *   which never change: the n-th token appended to a sequence has index n.
  * - Page slots are numbered page * page_size + offset.
@@ -93,7 +106,8 @@ typedef struct {
   double rope_theta;     /* theta_i = rope_theta^(-2i/d_rope) unless inv_freq is given */
   const double* inv_freq;/* optional d_rope/2 angular frequencies (copied)          */
   double compact_threshold; /* automatic compaction above this fragmentation;
-                               <= 0 selects 0.40, >= 1 disables it               */
+                               <= 0 selects 0.40 (or AKV_COMPACT_THRESHOLD),
+                               >= 1 disables it                                  */
 } akv_layout;
 
 /* ---- pool ---------------------------------------------------------------- */

@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <deque>
 #include <new>
@@ -54,6 +55,72 @@ akv_status hip_fail(hipError_t e, const char* what) {
 
 constexpr double kDefaultCompactThreshold = 0.40;
 constexpr int64_t kInt32Max = 2147483647LL;
+
+// Debug switches, read from the environment once per process:
+//   AKV_TRACE=1             one line on stderr per planning decision
+//                           (attention plans, rotations, copies, compaction)
+//   AKV_CHECKS=1            every device work list is checked on the host
+//                           before its launch (also in page-table-only pools,
+//                           which build the lists without launching them):
+//                           slots inside the pool and in pages in use, rows
+//                           inside their page, rotate items disjoint, copy
+//                           destinations distinct and apart from the sources,
+//                           attention items inside their segment and list and
+//                           covering each row tile's keys exactly once.  A
+//                           failed check is a library bug: the call returns
+//                           AKV_ESTATE and the pool's state is undefined.
+//   AKV_FAULT_INJECT=launch every kernel launch reports failure once it is
+//                           enqueued (the kernel itself runs normally), so each
+//                           call takes its AKV_EHIP error path: for tests of
+//                           error handling.
+//   AKV_COMPACT_THRESHOLD=x fragmentation threshold (0 < x <= 1) of pools
+//                           whose layout leaves compact_threshold at 0.
+struct DebugFlags {
+  bool trace = false, checks = false, inject_launch = false;
+  double thr = kDefaultCompactThreshold;
+};
+
+bool env_on(const char* name) {
+  const char* v = std::getenv(name);
+  return v && *v && std::strcmp(v, "0") != 0;
+}
+
+const DebugFlags& dbg() {
+  static const DebugFlags flags = [] {
+    DebugFlags f;
+    f.trace = env_on("AKV_TRACE");
+    f.checks = env_on("AKV_CHECKS");
+    const char* fi = std::getenv("AKV_FAULT_INJECT");
+    f.inject_launch = fi && std::strcmp(fi, "launch") == 0;
+    if (const char* t = std::getenv("AKV_COMPACT_THRESHOLD")) {
+      char* end = nullptr;
+      const double x = std::strtod(t, &end);
+      if (end != t && x > 0.0 && x <= 1.0) f.thr = x;
+    }
+    return f;
+  }();
+  return flags;
+}
+
+void trace(const char* fmt, ...) {
+  if (!dbg().trace) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "akv: %s\n", buf);
+}
+
+akv_status check_fail(const char* fmt, ...) {
+  char buf[448];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  trace("AKV_CHECKS failed: %s", buf);
+  return fail(AKV_ESTATE, "AKV_CHECKS: %s", buf);
+}
 
 struct PageRec {
   int32_t owner = -1;   // sequence id, -1 when free
@@ -929,6 +996,68 @@ akv_status scratch_fits(const akv_pool* p, size_t bytes) {
 
 akv_status check_launch(hipError_t e, const char* what) {
   if (e != hipSuccess) return hip_fail(e, what);
+  if (dbg().inject_launch) return fail(AKV_EHIP, "%s: injected failure (AKV_FAULT_INJECT=launch)", what);
+  return AKV_OK;
+}
+
+// ---- AKV_CHECKS: host checks of device work lists ---------------------------
+bool slot_in_pool(const akv_pool* p, int32_t slot) {
+  return slot >= 0 && (int64_t)slot < (int64_t)p->L.num_pages * p->L.page_size;
+}
+
+// Slots written by one launch: inside the pool, in pages in use, distinct.
+akv_status check_slots(const akv_pool* p, const int32_t* slots, size_t n, const char* what) {
+  std::vector<int32_t> s(slots, slots + n);
+  for (int32_t x : s) {
+    if (!slot_in_pool(p, x)) return check_fail("%s: slot %d outside the pool", what, x);
+    if (p->pages[x >> p->log2S].owner < 0) return check_fail("%s: slot %d lies in a free page", what, x);
+  }
+  std::sort(s.begin(), s.end());
+  for (size_t i = 1; i < s.size(); ++i)
+    if (s[i] == s[i - 1]) return check_fail("%s: slot %d written twice", what, s[i]);
+  return AKV_OK;
+}
+
+// Rotate items: rows inside pages in use, a valid table row, and no row
+// turned by two items (the kernel works in place).
+akv_status check_rot_items(const akv_pool* p, const std::vector<akv::RotItem>& items, size_t n_deltas) {
+  const akv_layout& L = p->L;
+  for (const akv::RotItem& it : items) {
+    if (it.page < 0 || it.page >= L.num_pages || it.lo < 0 || it.lo >= it.hi || it.hi > L.page_size)
+      return check_fail("rotate item (%d, %d, %d) outside the pool", it.page, it.lo, it.hi);
+    if (p->pages[it.page].owner < 0) return check_fail("rotate item in free page %d", it.page);
+    if (it.didx < 0 || (size_t)it.didx >= n_deltas)
+      return check_fail("rotate item of page %d: table row %d of %zu", it.page, it.didx, n_deltas);
+  }
+  std::vector<akv::RotItem> s(items);
+  std::sort(s.begin(), s.end(), [](const akv::RotItem& a, const akv::RotItem& b) {
+    return a.page != b.page ? a.page < b.page : a.lo < b.lo;
+  });
+  for (size_t i = 1; i < s.size(); ++i)
+    if (s[i].page == s[i - 1].page && s[i].lo < s[i - 1].hi)
+      return check_fail("rows %d..%d of page %d rotated twice", s[i].lo, s[i - 1].hi, s[i].page);
+  return AKV_OK;
+}
+
+// Row copies: slots inside the pool, destinations in pages in use, distinct,
+// and none of them a source (copies of one launch run in any order).
+akv_status check_moves(const akv_pool* p, const akv::MovePair* mv, size_t n, const char* what) {
+  std::vector<int32_t> src(n), dst(n);
+  for (size_t i = 0; i < n; ++i) {
+    if (!slot_in_pool(p, mv[i].src) || !slot_in_pool(p, mv[i].dst))
+      return check_fail("%s: copy %d -> %d outside the pool", what, mv[i].src, mv[i].dst);
+    src[i] = mv[i].src;
+    dst[i] = mv[i].dst;
+  }
+  akv_status st = check_slots(p, dst.data(), n, what);
+  if (st != AKV_OK) return st;
+  std::sort(src.begin(), src.end());
+  std::sort(dst.begin(), dst.end());
+  for (size_t i = 0, j = 0; i < n && j < n;) {
+    if (src[i] == dst[j]) return check_fail("%s: slot %d is both a source and a destination", what, src[i]);
+    if (src[i] < dst[j]) ++i;
+    else ++j;
+  }
   return AKV_OK;
 }
 
@@ -965,6 +1094,10 @@ akv_status bg_wait_slots(akv_pool* p, const int32_t* slots, size_t n) {
 // scatter appended rows of one token batch into the pool arrays
 akv_status device_append(akv_pool* p, const std::vector<int32_t>& slots, const void* K,
                          const void* Kpe, const void* V) {
+  if (dbg().checks) {
+    akv_status cst = check_slots(p, slots.data(), slots.size(), "append");
+    if (cst != AKV_OK) return cst;
+  }
   if (!p->device || !K) return AKV_OK;
   akv_status bst = bg_wait_slots(p, slots.data(), slots.size());
   if (bst != AKV_OK) return bst;
@@ -1001,6 +1134,13 @@ akv_status device_append(akv_pool* p, const std::vector<int32_t>& slots, const v
 akv_status device_rotate(akv_pool* p, const std::vector<akv::RotItem>& items,
                          const std::vector<int32_t>& deltas,
                          const std::vector<akv_pool*>& layers = {}) {
+  if (dbg().checks) {
+    akv_status cst = check_rot_items(p, items, deltas.size());
+    if (cst != AKV_OK) return cst;
+  }
+  if (!items.empty())
+    trace("rotate: %zu items, %zu distinct deltas, %zu layer(s)", items.size(), deltas.size(),
+          std::max<size_t>(layers.size(), 1));
   if (!p->device || items.empty()) return AKV_OK;
   akv_status bst = bg_wait(p);
   for (akv_pool* l : layers)
@@ -1047,6 +1187,10 @@ hipError_t move_tokens(akv_pool* p, const akv::MovePair* pairs, int n, const flo
 }
 
 akv_status device_move(akv_pool* p, const std::vector<akv::MovePair>& mv) {
+  if (dbg().checks) {
+    akv_status cst = check_moves(p, mv.data(), mv.size(), "compaction");
+    if (cst != AKV_OK) return cst;
+  }
   if (!p->device || mv.empty()) return AKV_OK;
   akv_status bst = bg_wait(p);
   if (bst != AKV_OK) return bst;
@@ -1068,6 +1212,11 @@ akv_status device_move(akv_pool* p, const std::vector<akv::MovePair>& mv) {
 // written), beside the pool stream's later work; every page the copies read
 // or write is flagged until the pool stream waits for them.
 akv_status device_move_bg(akv_pool* p, const std::vector<akv::MovePair>& mv, bool after_all) {
+  if (dbg().checks) {
+    akv_status cst = check_moves(p, mv.data(), mv.size(), "background compaction");
+    if (cst != AKV_OK) return cst;
+  }
+  if (!mv.empty()) trace("background compaction: %zu row copies on the second stream", mv.size());
   if (!p->device || mv.empty()) return AKV_OK;
   // ordered after the last write of pool rows and after the work that may
   // still read pages given back to the queues, not after later work; when
@@ -1110,7 +1259,7 @@ akv_status device_move_bg(akv_pool* p, const std::vector<akv::MovePair>& mv, boo
   e = akv::launch_move_tokens(p->kstream, p->rope_array(), p->rope_heads(), L.d_rope, L.pairing, plain, np,
                               (const akv::MovePair*)dmv, (int)mv.size(), L.page_size, p->log2S, nullptr);
   tm.done();
-  if (e != hipSuccess) return check_launch(e, "background compaction kernel launch");
+  if (e != hipSuccess) return hip_fail(e, "background compaction kernel launch");
   e = hipEventRecord(p->bg_done, p->kstream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord(background compaction)");
   p->bg_pending = true;
@@ -1122,7 +1271,7 @@ akv_status device_move_bg(akv_pool* p, const std::vector<akv::MovePair>& mv, boo
         p->bg_pages.push_back(pg);
       }
     }
-  return AKV_OK;
+  return check_launch(e, "background compaction kernel launch");
 }
 
 // ---------------------------------------------------------------------------
@@ -1144,6 +1293,7 @@ akv_status compact_plan(akv_pool* p, int32_t s, std::vector<akv::MovePair>& mv) 
     dest.push_back(take_page(p, s));
     p->pages[dest.back()].toks.reserve(S);
   }
+  trace("compact seq %d: %lld visible tokens into %lld fresh pages", s, (long long)nv, (long long)need);
   mv.reserve(mv.size() + nv);
   std::vector<int32_t> shared_src;   // slots given up in other sequences' pages
   const bool shares = !q.owners.empty();
@@ -1218,16 +1368,23 @@ void drop_tokens(akv_pool* p, SeqRec& q, int32_t b, int32_t e, bool keep_cache =
 // akv_compact_pending.
 akv_status auto_compact(akv_pool* p, int32_t s) {
   SeqRec& q = p->seqs[s];
-  if (fragmentation(p, q) > p->thr) {
+  const double frag = fragmentation(p, q);
+  if (frag > p->thr) {
     if (p->compact_mode == AKV_COMPACT_DEFERRED) {
       if (!q.queued) {
         q.queued = true;
         p->compact_q.push_back(s);
+        trace("seq %d: fragmentation %.3f above %.2f, queued for compaction", s, frag, p->thr);
       }
       return AKV_OK;
     }
     const int64_t need = (q.n_vis + p->L.page_size - 1) / p->L.page_size;
-    if (need <= available(p)) return compact_seq(p, s);
+    if (need <= available(p)) {
+      trace("seq %d: fragmentation %.3f above %.2f, compacting", s, frag, p->thr);
+      return compact_seq(p, s);
+    }
+    trace("seq %d: fragmentation %.3f above %.2f, compaction skipped (%lld pages needed, %lld available)", s,
+          frag, p->thr, (long long)need, (long long)available(p));
   }
   return AKV_OK;
 }
@@ -1404,6 +1561,11 @@ void place_existing(akv_pool* p, int32_t s, const std::vector<int32_t>& toks, st
 // rotated-key part turned by R(delta) (the table row and fp32 formula of an
 // in-place repos; delta 0 copies).
 akv_status device_copy_rows(akv_pool* p, const std::vector<akv::MovePair>& mv, int32_t delta) {
+  if (dbg().checks) {
+    akv_status cst = check_moves(p, mv.data(), mv.size(), "row copy");
+    if (cst != AKV_OK) return cst;
+  }
+  if (!mv.empty()) trace("copy on write: %zu rows turned by %d", mv.size(), delta);
   if (!p->device || mv.empty()) return AKV_OK;
   ScratchCursor sc(p, mv.size() * sizeof(akv::MovePair) + (size_t)p->L.d_rope * 4 + 3 * 256);
   const std::vector<float>& tab = rot_table_rows(p, &delta, 1);
@@ -1441,6 +1603,7 @@ akv_status materialize_seq(akv_pool* p, SeqRec& q) {
   }
   if (!cow.empty() && pages_needed(p, q, (int64_t)cow.size()) > available(p))
     return fail(AKV_ENOMEM, "copy on write of %zu shared rows: pool exhausted", cow.size());
+  trace("materialize seq %d: %zu runs in place, %zu shared rows copied", q.id, runs.size(), cow.size());
   std::vector<akv::RotItem> items;
   std::vector<int32_t> deltas;
   repos_items(p, q, runs, items, deltas);
@@ -1729,7 +1892,7 @@ akv_status akv_pool_create(const akv_layout* layout, const int32_t* page_order, 
       p->inv_freq[i] = L.inv_freq ? L.inv_freq[i] : std::pow(L.rope_theta, -2.0 * i / L.d_rope);
     p->log2S = 0;
     while ((1 << p->log2S) < L.page_size) ++p->log2S;
-    p->thr = L.compact_threshold > 0 ? L.compact_threshold : kDefaultCompactThreshold;
+    p->thr = L.compact_threshold > 0 ? L.compact_threshold : dbg().thr;
     p->free_q.assign(order.begin(), order.end());
     p->pages.resize(L.num_pages);
     p->device = any_dev;
@@ -1924,6 +2087,11 @@ akv_status akv_seq_clone(akv_pool* p, int32_t src, int32_t first, int32_t n, int
         qd2.lg_ok = false;
       }
     }
+    if (dbg().checks) {
+      akv_status cst = check_moves(p, mv.data(), mv.size(), "clone");
+      if (cst != AKV_OK) return cst;
+    }
+    trace("clone: %d rows of seq %d into seq %d turned by %d", m, src, dst, delta);
     if (!p->device) return AKV_OK;
     ScratchCursor sc(p, mv.size() * sizeof(akv::MovePair) + (size_t)p->L.d_rope * 4 + 3 * 256);
     const std::vector<float>& tab = rot_table_rows(p, &delta, 1);
@@ -2642,6 +2810,10 @@ akv_status akv_seq_attention(akv_pool* p, const void* Q, int32_t n_q_tokens, con
       rows[i] = {sg.q_begin, sg.q_len, (int32_t)lists.size(), (int32_t)ex->size()};
       lists.insert(lists.end(), ex->begin(), ex->end());
     }
+    if (dbg().checks)
+      for (const akv_extent& x : lists)
+        if (x.page < 0 || x.page >= p->L.num_pages || p->pages[x.page].owner < 0)
+          return check_fail("a visible list reads page %d, which is not in use", x.page);
     return attention_impl(p, Q, n_q_tokens, rows.data(), n_segs, lists.data(), (int32_t)lists.size(),
                           fused ? lags.data() : nullptr, scale, out);
   } catch (const std::bad_alloc&) {
@@ -2660,9 +2832,6 @@ static bool decode_launch(const akv_pool* p, const int64_t* q_len, int32_t n, in
          max_rows <= akv::DECODE_ROWS;
 }
 
-// Segment-batch attention over caller lists; ext_lag (optional, one per
-// extent) is the rotation each extent's keys still owe, applied inside the
-// decode kernel (only decode launches take it).
 // Checks the segments and page lists of an attention launch; fills each
 // segment's list length and offset in the expanded slot list.  *any_rows is
 // false when no segment has a query row.
@@ -2712,6 +2881,73 @@ static akv_status attn_validate(akv_pool* p, int32_t n_q_tokens, const akv_segme
   return AKV_OK;
 }
 
+// AKV_CHECKS: the plan's items lie inside their segment's rows and list, and
+// the key splits of every row tile cover its list exactly once; combine items
+// and partial rows stay inside the partial buffer.
+static akv_status check_plan(const akv_pool* p, const AttnPlan& plan, const akv_segment* segs, int32_t n_segs,
+                             const std::vector<int64_t>& lkv, int RB) {
+  const akv_layout& L = p->L;
+  const int64_t G = L.n_q_heads / L.n_kv_heads;
+  struct Key {
+    int32_t seg, kvh, row0, kb, ke;
+  };
+  std::vector<Key> keys;
+  keys.reserve(plan.items.size());
+  for (const akv::AttnItem& it : plan.items) {
+    if (it.seg < 0) continue;
+    if (it.seg >= n_segs || segs[it.seg].q_len <= 0) return check_fail("attention item of segment %d", it.seg);
+    const int64_t rows = segs[it.seg].q_len * G;
+    if (it.kvh < 0 || it.kvh >= L.n_kv_heads) return check_fail("attention item of kv head %d", it.kvh);
+    if (it.row0 < 0 || it.row0 >= rows || it.row0 % RB)
+      return check_fail("attention item rows from %d in a segment of %lld rows", it.row0, (long long)rows);
+    if (it.k_begin < 0 || it.k_begin >= it.k_end || it.k_end > lkv[it.seg])
+      return check_fail("attention item keys %d..%d of a list of %lld", it.k_begin, it.k_end,
+                        (long long)lkv[it.seg]);
+    const int64_t nr = std::min<int64_t>(RB, rows - it.row0);
+    if (it.part >= 0 && it.part + nr > plan.part_rows)
+      return check_fail("attention item partial rows %d..%lld of %lld", it.part, (long long)(it.part + nr),
+                        (long long)plan.part_rows);
+    keys.push_back({it.seg, it.kvh, it.row0, it.k_begin, it.k_end});
+  }
+  std::sort(keys.begin(), keys.end(), [](const Key& a, const Key& b) {
+    if (a.seg != b.seg) return a.seg < b.seg;
+    if (a.kvh != b.kvh) return a.kvh < b.kvh;
+    if (a.row0 != b.row0) return a.row0 < b.row0;
+    return a.kb < b.kb;
+  });
+  int64_t tiles = 0, want = 0;
+  for (int32_t i = 0; i < n_segs; ++i)
+    if (segs[i].q_len > 0) want += (int64_t)L.n_kv_heads * ((segs[i].q_len * G + RB - 1) / RB);
+  for (size_t i = 0; i < keys.size();) {
+    size_t j = i;
+    int32_t at = 0;
+    for (; j < keys.size() && keys[j].seg == keys[i].seg && keys[j].kvh == keys[i].kvh &&
+           keys[j].row0 == keys[i].row0;
+         ++j) {
+      if (keys[j].kb != at) break;
+      at = keys[j].ke;
+    }
+    const bool same = j < keys.size() && keys[j].seg == keys[i].seg && keys[j].kvh == keys[i].kvh &&
+                      keys[j].row0 == keys[i].row0;
+    if (same || at != lkv[keys[i].seg])
+      return check_fail("row tile (segment %d, kv head %d, row %d): key splits do not cover its list once",
+                        keys[i].seg, keys[i].kvh, keys[i].row0);
+    ++tiles;
+    i = j;
+  }
+  if (tiles != want) return check_fail("%lld row tiles planned, %lld expected", (long long)tiles, (long long)want);
+  for (const akv::CombItem& c : plan.comb)
+    if (c.seg < 0 || c.seg >= n_segs || c.nsplit < 2 || c.nsplit > 64 || c.rows < 1 || c.rows > RB ||
+        c.part0 < 0 || c.part0 + (int64_t)c.nsplit * c.rows > plan.part_rows)
+      return check_fail("combine item (segment %d, %d splits of %d rows from %d) outside %lld partial rows", c.seg,
+                        c.nsplit, c.rows, c.part0, (long long)plan.part_rows);
+  return AKV_OK;
+}
+
+// Segment-batch attention over caller lists; ext_lag (optional, one per
+// extent) is the rotation each extent's keys still owe, applied inside the
+// kernel that reads them (the decode kernel and the 128-dim GQA prefill
+// kernel take it).  ws_static: tables and partials in the static workspace.
 static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens, const akv_segment* segs,
                                  int32_t n_segs, const akv_extent* page_lists, int32_t n_ext,
                                  const int32_t* ext_lag, float scale, void* out, bool ws_static) {
@@ -2759,6 +2995,10 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
     AttnPlan& plan = p->hb.plan;
     plan_attention(p, segs, n_segs, lkv, list_off, rb, p->n_cu, plan);
     if (plan.part_rows > kInt32Max) return fail(AKV_ERANGE, "too many split-KV partial rows");
+    if (dbg().checks) {
+      akv_status cst = check_plan(p, plan, segs, n_segs, lkv, rb);
+      if (cst != AKV_OK) return cst;
+    }
     // extent offsets for the slot expansion (over all segments' ranges, in order)
     const bool fused = !rot_deltas.empty();
     // The segments' ranges usually tile the page lists in order: then the
@@ -2798,6 +3038,17 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
         if (segs[i].q_len > 0)
           for (int64_t k0 = 0; k0 < lkv[i]; k0 += akv::MASS_CHUNK) mass_items.push_back({i, (int32_t)k0});
     const size_t lse_bytes = want_mass ? (size_t)n_q_tokens * L.n_q_heads * 4 : 0;
+    if (dbg().trace) {
+      int64_t pad = 0;
+      for (const akv::AttnItem& it : plan.items) pad += it.seg < 0;
+      int max_split = 1;
+      for (int32_t ns : plan.nsplit) max_split = std::max(max_split, (int)ns);
+      trace("attention: %d segments, %lld keys, %s kernel, %zu items (%lld padding), up to %d key splits, "
+            "%zu combine items, %lld partial rows, %zu owed rotations applied in the kernel, %zu mass items",
+            n_segs, (long long)total, decode ? "decode" : (L.d_nope > 0 ? "MLA prefill" : "prefill"),
+            plan.items.size(), (long long)pad, max_split, plan.comb.size(), (long long)plan.part_rows,
+            rot_deltas.size(), mass_items.size());
+    }
     const size_t need = plan.segs.size() * sizeof(akv::AttnSeg) + plan.items.size() * sizeof(akv::AttnItem) +
                         plan.comb.size() * sizeof(akv::CombItem) + ex_off.size() * sizeof(akv::Extent) +
                         (ex_off.size() + ex_didx.size()) * 4 + keys4 * (fused ? 2 : 1) +
@@ -2885,13 +3136,13 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
                              (int)ex_off.size(), L.page_size, dslots);
       tm.done();
     }
-    if (e != hipSuccess) return hip_fail(e, "expand kernel launch");
+    if (akv_status lst = check_launch(e, "expand kernel launch")) return lst;
     if (fused) {
       KTimer tm(p, AKV_K_EXPAND);
       e = akv::launch_expand_didx(p->stream, (const akv::Extent*)dex, (const int32_t*)doff,
                                     (const int32_t*)dv[5], (int)ex_off.size(), dkey_didx);
       tm.done();
-      if (e != hipSuccess) return hip_fail(e, "owed-rotation table launch");
+      if (akv_status lst = check_launch(e, "owed-rotation table launch")) return lst;
     }
     akv::AttnArgs a{};
     a.q = (const uint16_t*)Q;
@@ -2923,12 +3174,12 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
       e = decode ? akv::launch_decode_attn(p->stream, a) : akv::launch_seg_attn(p->stream, a, L.d_nope, L.d_rope, L.d_v);
       tm.done();
     }
-    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    if (akv_status lst = check_launch(e, "attention kernel launch")) return lst;
     if (!plan.comb.empty()) {
       KTimer tm(p, AKV_K_COMBINE);
       e = akv::launch_combine(p->stream, a, (const akv::CombItem*)dcomb, (int)plan.comb.size(), L.d_v);
       tm.done();
-      if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+      if (akv_status lst = check_launch(e, "combine kernel launch")) return lst;
     }
     if (want_mass && !mass_items.empty()) {
       KTimer tm(p, AKV_K_MASS);
@@ -2938,7 +3189,7 @@ static akv_status attention_impl(akv_pool* p, const void* Q, int32_t n_q_tokens,
       e = akv::launch_page_mass(p->stream, a, (const akv::MassItem*)dmass_items, (int)mass_items.size(),
                                 (int)max_rows, p->mass);
       tm.done();
-      if (e != hipSuccess) return hip_fail(e, "attention mass kernel launch");
+      if (akv_status lst = check_launch(e, "attention mass kernel launch")) return lst;
     }
     return AKV_OK;
   } catch (const std::bad_alloc&) {
@@ -2992,6 +3243,10 @@ akv_status akv_attention_plan(akv_pool* p, int32_t n_q_tokens, const akv_segment
     if (!any_rows) return AKV_OK;
     AttnPlan plan;
     plan_attention(p, segs, n_segs, lkv, list_off, rb, n_cu > 0 ? n_cu : p->n_cu, plan);
+    if (dbg().checks) {
+      akv_status cst = check_plan(p, plan, segs, n_segs, lkv, rb);
+      if (cst != AKV_OK) return cst;
+    }
     *n_items = (int32_t)plan.items.size();
     *n_comb = (int32_t)plan.comb.size();
     *part_rows = plan.part_rows;
