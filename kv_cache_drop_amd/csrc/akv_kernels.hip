@@ -934,6 +934,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
     sm_exp(s_cur, m_use, pf);
     pv(stage_ptr(C), pf);
     sm_max(s_nxt, mx);
+    // the compiler's small-GEMM interleave (two LDS reads per MFMA, the
+    // vector work left free): fragment reads run ahead of the MFMAs that
+    // take them (measured: 2% faster at the 64K step)
+    __builtin_amdgcn_iglp_opt(0);
   };
   auto tail_iter = [&](int j, auto c, f32x16 (&s_cur)[QB][2], f32x16 (&s_nxt)[QB][2])
       __attribute__((always_inline)) {
