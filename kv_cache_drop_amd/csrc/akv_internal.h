@@ -115,6 +115,8 @@ struct AttnArgs {
 
 // Returns hipErrorInvalidValue when no kernel is instantiated for the dims.
 hipError_t launch_seg_attn(hipStream_t st, const AttnArgs& a, int d_nope, int d_rope, int d_v);
+// The 128-dim GQA prefill kernel (akv_attn_dl.hip), called by launch_seg_attn.
+hipError_t launch_seg_attn_dl(hipStream_t st, const AttnArgs& a);
 
 hipError_t launch_combine(hipStream_t st, const AttnArgs& a, const CombItem* items, int n_items,
                           int d_v);
