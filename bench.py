@@ -37,15 +37,16 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # the 64K step.  A plain 1 GiB device copy reads FETCH_SIZE = 524,302 KiB and
 # WRITE_SIZE = 1,048,576 KiB, so fetched KiB are scaled by 2.0 and written KiB
 # by 1.0.  When the kernel's source differs, its traffic is reported as null.
-_KERNELS_SHA1 = "36ced118bf5c453daf2dcc2ab22371c10d118293"    # akv_kernels.hip
+_ATTN_SHA1 = "3025c1acd8308d687a4c6bd44e7bea4778792dfa"       # akv_attn_dl.hip
+_KERNELS_SHA1 = "cd8221e20cdc0714f5e0fdcf2babbd00d47fc5d2"    # akv_kernels.hip
 _COPY_SHA1 = "2a16fbd3bdf4c924c007ee7a8f5e9337713b3565"       # akv_copy.hip
 _DECODE_SHA1 = "0082925b3cccf80941e542f22120c7047941fd13"     # akv_decode.hip
 COUNTERS = {
     "fetch_scale": 1048576 / 524302, "write_scale": 1.0,
-    "attention": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 111977, "write_kib": 16384},
-    "rotate": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 39272, "write_kib": 77627},
-    "rotate_32_layers": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 1248264,
-                         "write_kib": 2484299},
+    "attention": {"source": "akv_attn_dl.hip", "sha1": _ATTN_SHA1, "fetch_kib": 113262, "write_kib": 18433},
+    "rotate": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 39274, "write_kib": 77627},
+    "rotate_32_layers": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 1248953,
+                         "write_kib": 2484447},
     "compact": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 85348, "write_kib": 165578},
     # the decode steps of 48 requests (seed 0, mean over 8 steps), k_decode_attn<false>
     "decode": {"source": "akv_decode.hip", "sha1": _DECODE_SHA1, "fetch_kib": 611720, "write_kib": 3625},
