@@ -128,6 +128,7 @@ struct PageRec {
   int32_t filled = 0;   // slots written
   bool in_evict = false;
   uint32_t evict_gen = 0;
+  uint32_t take_gen = 0;   // bumped each time the page is taken by a sequence
   std::vector<int32_t> toks;   // tokens of the owner whose slot is in this page
 };
 
@@ -138,7 +139,11 @@ struct SeqRec {
   // encodes): nonzero only after a deferred repos, until it is materialized
   std::vector<int32_t> lag;
   bool lagging = false;        // some token may have lag != 0
-  std::vector<int32_t> pages;  // owned pages in allocation order
+  // owned pages in allocation order; an entry (page, take_gen) is live while
+  // the page still carries that generation (evicted pages leave stale
+  // entries behind, dropped in bulk once they are half of the list)
+  std::vector<std::pair<int32_t, uint32_t>> pages;
+  size_t stale_pages = 0;
   int32_t tail = -1;           // open page, or -1
   bool alive = true;
   int64_t n_vis = 0;
@@ -549,9 +554,19 @@ int32_t evict_pop(akv_pool* p) {
   return -1;
 }
 
-void remove_page_from_seq(SeqRec& q, int32_t pg) {
-  auto it = std::find(q.pages.begin(), q.pages.end(), pg);
-  if (it != q.pages.end()) q.pages.erase(it);
+// A live entry of q's page list: the page was taken by q and not since.
+inline bool page_live(const akv_pool* p, const std::pair<int32_t, uint32_t>& e);
+
+// The page leaves q's list (its entry goes stale; the list drops stale
+// entries, keeping the live ones in order, once they are half of it).
+void remove_page_from_seq(akv_pool* p, SeqRec& q) {
+  q.stale_pages += 1;
+  if (2 * q.stale_pages < q.pages.size()) return;
+  size_t w = 0;
+  for (const auto& e : q.pages)
+    if (page_live(p, e)) q.pages[w++] = e;
+  q.pages.resize(w);
+  q.stale_pages = 0;
 }
 
 // Reclaim an evictable page: its tokens (all dropped) lose their slot.
@@ -560,7 +575,8 @@ void evict_page(akv_pool* p, int32_t pg) {
   SeqRec& o = p->seqs[r.owner];
   for (int32_t t : r.toks) o.slot[t] = -1;
   r.toks.clear();
-  remove_page_from_seq(o, pg);
+  r.take_gen += 1;   // o's entry for the page goes stale
+  remove_page_from_seq(p, o);
 }
 
 int32_t take_page(akv_pool* p, int32_t s) {
@@ -577,8 +593,14 @@ int32_t take_page(akv_pool* p, int32_t s) {
   r.nvis = 0;
   r.filled = 0;
   r.toks.clear();
-  p->seqs[s].pages.push_back(pg);
+  r.toks.reserve(p->L.page_size);   // one allocation per page record, kept across reuse
+  r.take_gen += 1;
+  p->seqs[s].pages.emplace_back(pg, r.take_gen);
   return pg;
+}
+
+inline bool page_live(const akv_pool* p, const std::pair<int32_t, uint32_t>& e) {
+  return p->pages[e.first].take_gen == e.second;
 }
 
 int64_t pages_needed(const akv_pool* p, const SeqRec& q, int64_t n) {
@@ -662,7 +684,9 @@ void note_free(akv_pool* p);
 // order (pages waiting in the evictable queue are taken out of it).
 void finish_release(akv_pool* p, int32_t s) {
   SeqRec& q = p->seqs[s];
-  for (int32_t pg : q.pages) {
+  for (const auto& e : q.pages) {
+    if (!page_live(p, e)) continue;
+    const int32_t pg = e.first;
     PageRec& r = p->pages[pg];
     if (r.in_evict) evict_unlink(p, pg);
     r.owner = -1;
@@ -672,6 +696,7 @@ void finish_release(akv_pool* p, int32_t s) {
     p->free_q.push_back(pg);
   }
   q.pages.clear();
+  q.stale_pages = 0;
   q.tail = -1;
   q.zombie = false;
   note_free(p);
@@ -859,9 +884,9 @@ double fragmentation(const akv_pool* p, const SeqRec& q) {
   const size_t np = q.pages.size();
   int64_t cap = 0;
   for (size_t i = 0; i < np; ++i) {
-    if (i + kAhead < np) __builtin_prefetch(p->pages.data() + q.pages[i + kAhead]);
-    const PageRec& r = p->pages[q.pages[i]];
-    if (r.nvis > 0) cap += r.filled;
+    if (i + kAhead < np) __builtin_prefetch(p->pages.data() + q.pages[i + kAhead].first);
+    const PageRec& r = p->pages[q.pages[i].first];
+    if (r.take_gen == q.pages[i].second && r.nvis > 0) cap += r.filled;
   }
   for (const auto& f : q.fvis) cap += p->pages[f.first].filled;   // shared pages holding a visible token
   if (cap == 0) return 0.0;
@@ -1286,13 +1311,13 @@ akv_status compact_plan(akv_pool* p, int32_t s, std::vector<akv::MovePair>& mv) 
   const int64_t nv = (int64_t)order.size();
   const int64_t need = (nv + S - 1) / S;
   if (need > available(p)) return fail(AKV_ENOMEM, "compaction needs %lld free pages", (long long)need);
-  const std::vector<int32_t> old_pages = q.pages;
+  std::vector<int32_t> old_pages;
+  old_pages.reserve(q.pages.size());
+  for (const auto& e : q.pages)
+    if (page_live(p, e)) old_pages.push_back(e.first);
   std::vector<int32_t> dest;
   dest.reserve(need);
-  for (int64_t i = 0; i < need; ++i) {
-    dest.push_back(take_page(p, s));
-    p->pages[dest.back()].toks.reserve(S);
-  }
+  for (int64_t i = 0; i < need; ++i) dest.push_back(take_page(p, s));
   trace("compact seq %d: %lld visible tokens into %lld fresh pages", s, (long long)nv, (long long)need);
   mv.reserve(mv.size() + nv);
   std::vector<int32_t> shared_src;   // slots given up in other sequences' pages
@@ -1341,25 +1366,47 @@ akv_status compact_seq(akv_pool* p, int32_t s) {
 
 void drop_tokens(akv_pool* p, SeqRec& q, int32_t b, int32_t e, bool keep_cache = false) {
   // page records lie in allocation order, not in the sequence's: fetch the
-  // record a few pages ahead (tokens of evicted pages have no slot)
+  // record a few pages ahead (tokens of evicted pages have no slot).  Tokens
+  // dropped from one of q's own pages in a row are counted together: the
+  // page's record is updated once per run (a page empties at the last token
+  // of its run, so the evictable queue gets pages in the same order).
   constexpr int32_t kAhead = 64;
+  const int32_t lg = p->log2S;
+  uint8_t* const dropped = q.dropped.data();
+  int32_t* const slot = q.slot.data();
+  const PageRec* const recs = p->pages.data();
+  int64_t n_drop = 0;
+  int32_t run_pg = -1, run_n = 0;
+  auto flush = [&]() {
+    if (run_n == 0) return;
+    PageRec& r = p->pages[run_pg];
+    r.nvis -= run_n;
+    if (r.nvis == 0 && run_pg != q.tail && !r.in_evict) evict_push(p, run_pg);
+    run_n = 0;
+  };
   for (int32_t t = b; t < e; ++t) {
-    if (t + kAhead < e && q.slot[t + kAhead] >= 0)
-      __builtin_prefetch(p->pages.data() + (q.slot[t + kAhead] >> p->log2S));
-    if (q.dropped[t]) continue;
-    q.dropped[t] = 1;
-    q.n_vis -= 1;
-    const int32_t pg = q.slot[t] >> p->log2S;
-    if (foreign_slot(p, q.id, q.slot[t])) {   // a shared token gives its slot up at once
-      fvis_dec(q, pg);
-      unref(p, q, q.slot[t]);
-      q.slot[t] = -1;
+    if (t + kAhead < e && slot[t + kAhead] >= 0) __builtin_prefetch(recs + (slot[t + kAhead] >> lg));
+    if (dropped[t]) continue;
+    dropped[t] = 1;
+    n_drop += 1;
+    const int32_t pg = slot[t] >> lg;
+    if (pg == run_pg) {   // the run's page is one of q's own
+      run_n += 1;
       continue;
     }
-    PageRec& r = p->pages[pg];
-    r.nvis -= 1;
-    if (r.nvis == 0 && pg != q.tail && !r.in_evict) evict_push(p, pg);
+    flush();
+    run_pg = -1;
+    if (foreign_slot(p, q.id, slot[t])) {   // a shared token gives its slot up at once
+      fvis_dec(q, pg);
+      unref(p, q, slot[t]);
+      slot[t] = -1;
+      continue;
+    }
+    run_pg = pg;
+    run_n = 1;
   }
+  flush();
+  q.n_vis -= n_drop;
   if (!keep_cache) q.stale();
 }
 
@@ -1479,8 +1526,17 @@ void repos_items_append(const akv_pool* p, const SeqRec& q, const std::vector<Ru
   const int32_t max_rows = std::max<int32_t>(1, 16384 / row_bytes);
   size_t span_tokens = 0;
   for (const Run& r : runs) span_tokens += (size_t)(r.e - r.b);
-  items.reserve(items.size() + span_tokens / (size_t)std::min(max_rows, S) + 2 * runs.size() + 16);
+  // grow geometrically: a batched repos calls this once per sequence
+  const size_t want = items.size() + span_tokens / (size_t)std::min(max_rows, S) + 2 * runs.size() + 16;
+  if (want > items.capacity()) items.reserve(std::max(want, 2 * items.capacity()));
   const bool shares = !q.owners.empty();   // the sequence holds slots in other sequences' pages
+  // the open item is kept in registers and stored when the next one starts
+  // (it may continue the last item of the list)
+  akv::RotItem cur{-1, 0, 0, -1};
+  if (!items.empty()) {
+    cur = items.back();
+    items.pop_back();
+  }
   for (const Run& r : runs) {
     int32_t di = -1;   // looked up at the run's first moved token
     for (int32_t t = r.b; t < r.e; ++t) {
@@ -1498,13 +1554,15 @@ void repos_items_append(const akv_pool* p, const SeqRec& q, const std::vector<Ru
       }
       const int32_t slot = q.slot[t];
       const int32_t pg = slot >> lg, off = slot & (S - 1);
-      if (!items.empty() && items.back().page == pg && items.back().hi == off &&
-          items.back().didx == di && items.back().hi - items.back().lo < max_rows)
-        items.back().hi += 1;
-      else
-        items.push_back({pg, off, off + 1, di});
+      if (cur.page == pg && cur.hi == off && cur.didx == di && cur.hi - cur.lo < max_rows) {
+        cur.hi += 1;
+      } else {
+        if (cur.page >= 0) items.push_back(cur);
+        cur = {pg, off, off + 1, di};
+      }
     }
   }
+  if (cur.page >= 0) items.push_back(cur);
 }
 
 void repos_items(const akv_pool* p, const SeqRec& q, const std::vector<Run>& runs,
