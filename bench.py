@@ -37,7 +37,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # the 64K step.  A plain 1 GiB device copy reads FETCH_SIZE = 524,302 KiB and
 # WRITE_SIZE = 1,048,576 KiB, so fetched KiB are scaled by 2.0 and written KiB
 # by 1.0.  When the kernel's source differs, its traffic is reported as null.
-_ATTN_SHA1 = "3025c1acd8308d687a4c6bd44e7bea4778792dfa"       # akv_attn_dl.hip
+_ATTN_SHA1 = "5f038eabb1099ac21aacb7c994d84a2d4d3b7bc3"       # akv_attn_dl.hip
 _KERNELS_SHA1 = "cd8221e20cdc0714f5e0fdcf2babbd00d47fc5d2"    # akv_kernels.hip
 _COPY_SHA1 = "2a16fbd3bdf4c924c007ee7a8f5e9337713b3565"       # akv_copy.hip
 _DECODE_SHA1 = "0082925b3cccf80941e542f22120c7047941fd13"     # akv_decode.hip

@@ -138,11 +138,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
       __builtin_amdgcn_global_load_lds(a.key_didx + sg.list_off + idx, (void AKV_LDS*)dring_ptr(e), 4, 0, 0);
   };
   // Turn the owed keys of the K tile in stage stg (di: this lane's key's
-  // table row, read from the ring before the ring entry was reloaded), then
-  // a barrier so every wave reads turned keys.  Skipped, barrier included,
-  // when no key of the tile owes a rotation (the same decision in every
-  // wave: each holds the tile's 64 rows).
-  auto rotate_tile = [&](unsigned char AKV_LDS* stg, int di) __attribute__((always_inline)) {
+  // table row, read from the ring before the ring entry is reloaded).  With
+  // with_barrier, a barrier follows so every wave reads turned keys; in the
+  // loop the next iteration's barrier publishes them instead.  Skipped when
+  // no key of the tile owes a rotation (the same decision in every wave:
+  // each holds the tile's 64 rows).
+  auto rotate_tile = [&](unsigned char AKV_LDS* stg, int di, auto with_barrier) __attribute__((always_inline)) {
     if constexpr (ROT) {
       uint64_t todo = __ballot(di >= 0);
       if (todo == 0) return;
@@ -179,8 +180,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
       }
       *p0 = o0;
       *p1 = o1;
-      __builtin_amdgcn_s_waitcnt(WAIT_LDS);
-      __builtin_amdgcn_s_barrier();
+      if constexpr (decltype(with_barrier)::value) {
+        __builtin_amdgcn_s_waitcnt(WAIT_LDS);
+        __builtin_amdgcn_s_barrier();
+      }
     }
   };
   auto ring_didx = [&](int e) __attribute__((always_inline)) -> int {
@@ -359,6 +362,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
   // tile j + 5 into tile j + 1's ring entry (read at iteration j - 2), then
   // S(j + 1) and softmax / PV of tile j.  Loads past the list end are
   // clamped (in bounds); extra tiles past the range are fully masked.
+  // ROT: iteration j also turns tile j + 2 (issued at iteration j - 1, so the
+  // wait covers every row load but the last iteration's slot loads); the
+  // barrier of iteration j + 1 publishes the turned keys before S(j + 2).
   auto stage_ptr = [&](int s) __attribute__((always_inline)) -> unsigned char AKV_LDS* {
     return (unsigned char AKV_LDS*)(s == 0 ? st0 : (s == 1 ? st1 : (s == 2 ? st2 : st3)));
   };
@@ -371,7 +377,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
   slot_load(0, 4);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  rotate_tile(stage_ptr(0), di0);
+  const int di1 = ring_didx(1);
+  rotate_tile(stage_ptr(0), di0, std::false_type{});
+  rotate_tile(stage_ptr(1), di1, std::true_type{});
   // A wave whose rows all lie past the segment's last row (a short segment's
   // padding) computes nothing: it keeps its share of the tile loads and every
   // barrier, and leaves its SIMD's matrix core to the other wave there.
@@ -380,11 +388,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
   if (!idle) qk(stage_ptr(0), sa);
 
   // All of iteration j - 2's loads have landed once at most one iteration's
-  // worth (NIW rows + 1 slot load) is outstanding.  The barrier carries no
+  // worth (NIW rows + 1 slot load) is outstanding (ROT: iteration j - 1's
+  // rows too, once only its two slot loads are).  The barrier carries no
   // memory fence: a workgroup fence would wait for every LDS load in flight,
   // tiles j + 2 and j + 3 included.  lgkmcnt(0) makes this wave's reads of
   // tile j - 1's stage complete before any wave reloads it.
-  constexpr int WAITV = NIW + (ROT ? 2 : 1);
+  constexpr int WAITV = ROT ? 2 : NIW + 1;
   // s_waitcnt operands (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
   // 6:4, lgkmcnt 11:8), given through the builtin so the compiler's own wait
   // tracking knows them and adds no stricter wait of its own
@@ -412,10 +421,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
     sync();
     float m_use[QB];
     sm_rescale(mx, j, m_use);
-    const int di = ring_didx((C + 1) & 3);
+    const int di = ring_didx((C + 2) & 3);
     issue_tile(stage_ptr((C + 3) & 3), (C + 3) & 3);
     slot_load((C + 1) & 3, j + 5);
-    rotate_tile(stage_ptr((C + 1) & 3), di);
+    rotate_tile(stage_ptr((C + 2) & 3), di, std::false_type{});
     qk(stage_ptr((C + 1) & 3), s_nxt);
     bf16x8 pf[QB][4];
     sm_exp(s_cur, m_use, pf);
@@ -430,10 +439,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
       __attribute__((always_inline)) {
     constexpr int C = decltype(c)::value;
     sync();
-    const int di = ring_didx((C + 1) & 3);
+    const int di = ring_didx((C + 2) & 3);
     issue_tile(stage_ptr((C + 3) & 3), (C + 3) & 3);
     slot_load((C + 1) & 3, j + 5);
-    rotate_tile(stage_ptr((C + 1) & 3), di);
+    rotate_tile(stage_ptr((C + 2) & 3), di, std::false_type{});
     float m_use[QB];
     bf16x8 pf[QB][4];
     sm_mask(s_cur, j);
@@ -446,10 +455,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
   auto idle_iter = [&](int j, auto c) __attribute__((always_inline)) {
     constexpr int C = decltype(c)::value;
     sync();
-    const int di = ring_didx((C + 1) & 3);
+    const int di = ring_didx((C + 2) & 3);
     issue_tile(stage_ptr((C + 3) & 3), (C + 3) & 3);
     slot_load((C + 1) & 3, j + 5);
-    rotate_tile(stage_ptr((C + 1) & 3), di);
+    rotate_tile(stage_ptr((C + 2) & 3), di, std::false_type{});
   };
   int j = 0;
   if (idle) {
