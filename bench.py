@@ -336,6 +336,14 @@ def run_config(args) -> dict:
     kern = None
     n_dec = args.decode_steps if args.config in ("decode", "decode_fused", "decode_compact", "decode_mass") else 1
     first_walls = []
+    # each decode step's positions and the batch's index arrays, made once
+    # (int32, contiguous: the binding passes them on as they are)
+    step_args = {}
+    for i, op in enumerate(ops[i0:], start=i0):
+        if isinstance(op, W.AppendBatch):
+            rep_counts = np.repeat(op.counts, op.counts).astype(np.int32)
+            step_args[i] = (np.ascontiguousarray(op.seqs, np.int32), np.ascontiguousarray(op.counts, np.int32),
+                            [np.ascontiguousarray(op.pos + t * rep_counts, np.int32) for t in range(n_dec)])
     # no collector pause inside a timed step, and none right before it (the
     # idle GPU it leaves makes the next launches slower): one collection
     # before the reps, the collector off until they end
@@ -365,8 +373,8 @@ def run_config(args) -> dict:
                 if isinstance(op, W.Append):
                     pool.append(op.seq, op.pos, dev[i][0], dev[i][1], dev[i][2])
                 elif isinstance(op, W.AppendBatch):
-                    pos = op.pos + shift * np.repeat(op.counts, op.counts).astype(np.int32)
-                    pool.append_batch(op.seqs, op.counts, pos, dev[i][0], dev[i][1], dev[i][2])
+                    seqs, counts, pos = step_args[i]
+                    pool.append_batch(seqs, counts, pos[shift], dev[i][0], dev[i][1], dev[i][2])
                 elif isinstance(op, W.Splice):
                     pool.splice(op.seq, op.spans, op.stub_lens, dev[i][0], dev[i][1], dev[i][2])
                 elif isinstance(op, W.Attention):
