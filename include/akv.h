@@ -506,10 +506,11 @@ akv_status akv_attention_plan(akv_pool* pool, int32_t n_q_tokens, const akv_segm
                               int32_t items_cap, int32_t* n_items, akv_attn_combine* comb, int32_t comb_cap,
                               int32_t* n_comb, int32_t* rows_per_block, int64_t* part_rows);
 
-/* Kernel timing: when enabled, the library brackets each of its kernel
- * launches with HIP events on the pool's stream.  akv_timing_read waits for the
- * stream, returns the summed milliseconds and launch count of one kernel kind
- * since the last read of that kind, and clears them. */
+/* Kernel timing: when enabled, each kernel launch of the library carries a
+ * start and a stop HIP event, stamped by the dispatch at the kernel's start and
+ * end (the launch's duration, without the gap before it).  akv_timing_read
+ * waits for the events, returns the summed milliseconds and launch count of one
+ * kernel kind since the last read of that kind, and clears them. */
 enum { AKV_K_APPEND = 0, AKV_K_ROTATE = 1, AKV_K_COMPACT = 2, AKV_K_EXPAND = 3,
        AKV_K_ATTN = 4, AKV_K_COMBINE = 5, AKV_K_CLONE = 6, AKV_K_MASS = 7, AKV_K_KINDS = 8 };
 akv_status akv_timing_enable(akv_pool* pool, int32_t enable);

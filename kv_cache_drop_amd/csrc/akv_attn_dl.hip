@@ -14,6 +14,7 @@
 
 #include "akv_device.h"
 #include "akv_internal.h"
+#include "akv_launch.h"
 
 namespace akv {
 
@@ -526,9 +527,9 @@ hipError_t launch_seg_attn_dl(hipStream_t st, const AttnArgs& a) {
   // keys owing a rotation are turned in LDS when the launch carries a
   // rotation table
   if (a.key_didx)
-    hipLaunchKernelGGL((k_seg_attn_dl<128, 128, 0, 8, 1, 4, true>), dim3(a.n_items), dim3(512), 0, st, a);
+    launch_k(k_seg_attn_dl<128, 128, 0, 8, 1, 4, true>, dim3(a.n_items), dim3(512), st, a);
   else
-    hipLaunchKernelGGL((k_seg_attn_dl<128, 128, 0, 8, 1, 4, false>), dim3(a.n_items), dim3(512), 0, st, a);
+    launch_k(k_seg_attn_dl<128, 128, 0, 8, 1, 4, false>, dim3(a.n_items), dim3(512), st, a);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@
 #include <cstdint>
 
 #include "akv_internal.h"
+#include "akv_launch.h"
 
 namespace akv {
 namespace {
@@ -233,7 +234,7 @@ hipError_t launch_scatter_tokens(hipStream_t st, const TokenRows* rows, int n_ro
   a.n = n;
   a.S = page_size;
   a.log2S = log2_page;
-  hipLaunchKernelGGL(k_scatter_tokens, dim3(blocks_for(most)), dim3(kThreads), 0, st, a);
+  launch_k(k_scatter_tokens, dim3(blocks_for(most)), dim3(kThreads), st, a);
   return hipGetLastError();
 }
 
@@ -258,7 +259,7 @@ hipError_t launch_move_tokens(hipStream_t st, uint16_t* kr, int rope_heads, int 
   a.log2S = log2_page;
   a.d_rope = d_rope;
   a.pairing = pairing;
-  hipLaunchKernelGGL(k_move_tokens, dim3(blocks_for(most)), dim3(kThreads), 0, st, a);
+  launch_k(k_move_tokens, dim3(blocks_for(most)), dim3(kThreads), st, a);
   return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@
 #include <cstdint>
 
 #include "akv_internal.h"
+#include "akv_launch.h"
 
 namespace akv {
 namespace {
@@ -499,7 +500,7 @@ hipError_t launch_expand_didx(hipStream_t st, const Extent* ex, const int32_t* e
                               int n_ext, int32_t* out) {
   if (n_ext <= 0) return hipSuccess;
   const int blocks = std::min(4096, (n_ext + 255) / 256);
-  hipLaunchKernelGGL(k_expand_didx, dim3(blocks), dim3(256), 0, st, ex, ex_off, ex_didx, n_ext, out);
+  launch_k(k_expand_didx, dim3(blocks), dim3(256), st, ex, ex_off, ex_didx, n_ext, out);
   return hipGetLastError();
 }
 
@@ -510,14 +511,14 @@ hipError_t launch_page_mass(hipStream_t st, const AttnArgs& a, const MassItem* i
   const dim3 grid(n_items, a.n_kv_heads);
   const bool rot = a.key_didx != nullptr;
   if (max_rows <= 4) {
-    if (rot) hipLaunchKernelGGL((k_page_mass<4, true>), grid, dim3(256), 0, st, a, items, mass);
-    else hipLaunchKernelGGL((k_page_mass<4, false>), grid, dim3(256), 0, st, a, items, mass);
+    if (rot) launch_k(k_page_mass<4, true>, grid, dim3(256), st, a, items, mass);
+    else launch_k(k_page_mass<4, false>, grid, dim3(256), st, a, items, mass);
   } else if (max_rows <= 8) {
-    if (rot) hipLaunchKernelGGL((k_page_mass<8, true>), grid, dim3(256), 0, st, a, items, mass);
-    else hipLaunchKernelGGL((k_page_mass<8, false>), grid, dim3(256), 0, st, a, items, mass);
+    if (rot) launch_k(k_page_mass<8, true>, grid, dim3(256), st, a, items, mass);
+    else launch_k(k_page_mass<8, false>, grid, dim3(256), st, a, items, mass);
   } else {
-    if (rot) hipLaunchKernelGGL((k_page_mass<16, true>), grid, dim3(256), 0, st, a, items, mass);
-    else hipLaunchKernelGGL((k_page_mass<16, false>), grid, dim3(256), 0, st, a, items, mass);
+    if (rot) launch_k(k_page_mass<16, true>, grid, dim3(256), st, a, items, mass);
+    else launch_k(k_page_mass<16, false>, grid, dim3(256), st, a, items, mass);
   }
   return hipGetLastError();
 }
@@ -525,9 +526,9 @@ hipError_t launch_page_mass(hipStream_t st, const AttnArgs& a, const MassItem* i
 hipError_t launch_decode_attn(hipStream_t st, const AttnArgs& a) {
   if (a.n_items <= 0) return hipSuccess;
   if (a.key_didx)
-    hipLaunchKernelGGL(k_decode_attn<true>, dim3(a.n_items), dim3(64 * DEC_WAVES), 0, st, a);
+    launch_k(k_decode_attn<true>, dim3(a.n_items), dim3(64 * DEC_WAVES), st, a);
   else
-    hipLaunchKernelGGL(k_decode_attn<false>, dim3(a.n_items), dim3(64 * DEC_WAVES), 0, st, a);
+    launch_k(k_decode_attn<false>, dim3(a.n_items), dim3(64 * DEC_WAVES), st, a);
   return hipGetLastError();
 }
 

@@ -150,4 +150,12 @@ hipError_t static_workspace(void** ptr);
 // Text returned by akv_last_error (thread-local; host code of the library).
 void set_error(const char* msg);
 
+// Timer events armed for the next kernel launch of this thread (both null:
+// none); a launch that carries them sets used (akv_launch.h).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;
+};
+LaunchEvents& launch_events();
+
 }  // namespace akv

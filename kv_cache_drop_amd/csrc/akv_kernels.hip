@@ -21,6 +21,7 @@
 
 #include "akv_device.h"
 #include "akv_internal.h"
+#include "akv_launch.h"
 
 namespace akv {
 
@@ -129,8 +130,8 @@ __global__ __launch_bounds__(ROT_THREADS, 8) void k_rotate(uint16_t* const* __re
 hipError_t launch_rotate(hipStream_t st, uint16_t* const* krs, int n_layers, int n_heads, int page_size,
                          int d_rope, int pairing, const RotItem* items, int n_items, const float* table) {
   if (n_items <= 0 || n_layers <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rotate, dim3(n_items, n_layers), dim3(ROT_THREADS), 0, st, krs, n_heads, page_size,
-                     d_rope, pairing, items, table);
+  launch_k(k_rotate, dim3(n_items, n_layers), dim3(ROT_THREADS), st, krs, n_heads, page_size, d_rope, pairing,
+           items, table);
   return hipGetLastError();
 }
 
@@ -151,8 +152,7 @@ __global__ __launch_bounds__(256) void k_expand(const Extent* __restrict__ ex,
 hipError_t launch_expand(hipStream_t st, const Extent* ex, const int32_t* ex_off, int n_ext,
                          int page_size, int32_t* slots) {
   if (n_ext <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_expand, dim3((n_ext + 255) / 256), dim3(256), 0, st, ex, ex_off, n_ext,
-                     page_size, slots);
+  launch_k(k_expand, dim3((n_ext + 255) / 256), dim3(256), st, ex, ex_off, n_ext, page_size, slots);
   return hipGetLastError();
 }
 
@@ -925,9 +925,9 @@ static hipError_t launch_attn_t(hipStream_t st, const AttnArgs& a) {
     return launch_seg_attn_dl(st, a);
   } else if constexpr (DNOPE == 128 && DQK == 192 && DV == 128) {
     // the MLA row (K_nope 128, K_pe 64, V 128): direct-to-LDS, three stages
-    hipLaunchKernelGGL((k_seg_attn_mla<128, 64, 128>), dim3(a.n_items), dim3(512), 0, st, a);
+    launch_k(k_seg_attn_mla<128, 64, 128>, dim3(a.n_items), dim3(512), st, a);
   } else {
-    hipLaunchKernelGGL((k_seg_attn<DQK, DV, DNOPE, 8>), dim3(a.n_items), dim3(512), 0, st, a);
+    launch_k(k_seg_attn<DQK, DV, DNOPE, 8>, dim3(a.n_items), dim3(512), st, a);
   }
   return hipGetLastError();
 }
@@ -951,9 +951,9 @@ hipError_t launch_combine(hipStream_t st, const AttnArgs& a, const CombItem* ite
   const int bpi = (a.rows_per_block + 3) / 4;
   const dim3 grid((unsigned)(n_items * bpi));
   switch (d_v) {
-    case 128: hipLaunchKernelGGL((k_combine<128>), grid, dim3(256), 0, st, a, items, bpi); break;
-    case 64: hipLaunchKernelGGL((k_combine<64>), grid, dim3(256), 0, st, a, items, bpi); break;
-    case 32: hipLaunchKernelGGL((k_combine<32>), grid, dim3(256), 0, st, a, items, bpi); break;
+    case 128: launch_k(k_combine<128>, grid, dim3(256), st, a, items, bpi); break;
+    case 64: launch_k(k_combine<64>, grid, dim3(256), st, a, items, bpi); break;
+    case 32: launch_k(k_combine<32>, grid, dim3(256), st, a, items, bpi); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -47,6 +47,11 @@ akv_status fail(akv_status s, const char* fmt, ...) {
 
 void akv::set_error(const char* msg) { g_err = msg; }
 
+akv::LaunchEvents& akv::launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+
 namespace {
 
 akv_status hip_fail(hipError_t e, const char* what) {
@@ -483,23 +488,34 @@ hipError_t tev_get(akv_pool* p, hipEvent_t* ev) {
   return hipEventCreate(ev);
 }
 
+// Times the one launch made between construction and done(): the two events
+// are armed for that launch, which carries them (stamped by the dispatch at
+// the kernel's start and end; no packets of their own on the stream).
 struct KTimer {
   akv_pool* p;
   int kind;
-  hipStream_t st;
   hipEvent_t a = nullptr, b = nullptr;
-  KTimer(akv_pool* pp, int k, hipStream_t s = nullptr) : p(pp), kind(k), st(s ? s : pp->stream) {
-    if (p->timing && tev_get(p, &a) == hipSuccess && tev_get(p, &b) == hipSuccess)
-      (void)hipEventRecord(a, st);
-    else
-      a = b = nullptr;
-  }
-  void done() {
-    if (a && b) {
-      (void)hipEventRecord(b, st);
-      p->tev.push_back({kind, a, b});
+  KTimer(akv_pool* pp, int k, hipStream_t = nullptr) : p(pp), kind(k) {
+    if (p->timing && tev_get(p, &a) == hipSuccess && tev_get(p, &b) == hipSuccess) {
+      akv::LaunchEvents& ev = akv::launch_events();
+      ev.start = a;
+      ev.stop = b;
+      ev.used = false;
+    } else {
       a = b = nullptr;
     }
+  }
+  void done() {
+    if (!a || !b) return;
+    akv::LaunchEvents& ev = akv::launch_events();
+    if (ev.used) {
+      p->tev.push_back({kind, a, b});
+    } else {   // no launch took them (nothing to do)
+      p->ev_spare.push_back(a);
+      p->ev_spare.push_back(b);
+    }
+    ev = akv::LaunchEvents{};
+    a = b = nullptr;
   }
 };
 
