@@ -37,21 +37,21 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # the 64K step.  A plain 1 GiB device copy reads FETCH_SIZE = 524,302 KiB and
 # WRITE_SIZE = 1,048,576 KiB, so fetched KiB are scaled by 2.0 and written KiB
 # by 1.0.  When the kernel's source differs, its traffic is reported as null.
-_ATTN_SHA1 = "5f038eabb1099ac21aacb7c994d84a2d4d3b7bc3"       # akv_attn_dl.hip
-_KERNELS_SHA1 = "cd8221e20cdc0714f5e0fdcf2babbd00d47fc5d2"    # akv_kernels.hip
-_COPY_SHA1 = "2a16fbd3bdf4c924c007ee7a8f5e9337713b3565"       # akv_copy.hip
-_DECODE_SHA1 = "0082925b3cccf80941e542f22120c7047941fd13"     # akv_decode.hip
+_ATTN_SHA1 = "adaa2bddcc5a394cec08357144e884b7cc558c04"       # akv_attn_dl.hip
+_KERNELS_SHA1 = "6a0e8f28a1396015ae04e86664c2a80bcd9ac662"    # akv_kernels.hip
+_COPY_SHA1 = "e0150158ee0d1c27d58bdf5f6e0337b98da28d4d"       # akv_copy.hip
+_DECODE_SHA1 = "060e1f71384fd8b27f435f682fbb320b988863d4"     # akv_decode.hip
 COUNTERS = {
     "fetch_scale": 1048576 / 524302, "write_scale": 1.0,
-    "attention": {"source": "akv_attn_dl.hip", "sha1": _ATTN_SHA1, "fetch_kib": 113262, "write_kib": 18433},
-    "rotate": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 39274, "write_kib": 77627},
-    "rotate_32_layers": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 1248953,
-                         "write_kib": 2484447},
-    "compact": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 85348, "write_kib": 165578},
+    "attention": {"source": "akv_attn_dl.hip", "sha1": _ATTN_SHA1, "fetch_kib": 113172, "write_kib": 18432},
+    "rotate": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 39278, "write_kib": 77640},
+    "rotate_32_layers": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 1248996,
+                         "write_kib": 2484301},
+    "compact": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 85344, "write_kib": 165581},
     # the decode steps of 48 requests (seed 0, mean over 8 steps), k_decode_attn<false>
-    "decode": {"source": "akv_decode.hip", "sha1": _DECODE_SHA1, "fetch_kib": 611720, "write_kib": 3625},
+    "decode": {"source": "akv_decode.hip", "sha1": _DECODE_SHA1, "fetch_kib": 611717, "write_kib": 3625},
     # the retrigger clone (seed 0), k_move_tokens with the rotation
-    "clone": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 80734, "write_kib": 157391},
+    "clone": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 80741, "write_kib": 157387},
 }
 
 
