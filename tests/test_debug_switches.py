@@ -1,4 +1,5 @@
-"""Debug switches of libakv.so, read from the environment once per process:
+"""Debug switches and kernel timers of libakv.so.  The switches are read from the
+environment once per process:
 AKV_CHECKS (host checks of every device work list before its launch),
 AKV_TRACE (planning decisions on stderr), AKV_COMPACT_THRESHOLD (default
 fragmentation threshold) and AKV_FAULT_INJECT=launch (every launch reports
@@ -184,3 +185,45 @@ def test_checks_on_device_scripts():
     out, err = _child(code, timeout=600, AKV_CHECKS="1", AKV_TRACE="1")
     assert "CHECKED" in out and "AKV_CHECKS failed" not in err, err[-2000:]
     assert "akv: attention:" in err
+
+
+@pytest.mark.gpu
+def test_kernel_timers_count_each_launch():
+    """With the pool's timers on, every kernel launch carries its own start and
+    stop events: one duration per launch and kind (append, rotate, expand,
+    attention, compaction), each positive and below the wall time of the
+    synchronised call sequence; with the timers off nothing is recorded."""
+    _need_lib()
+    import time
+
+    import numpy as np
+    import torch
+
+    p = akv.Pool(8, 2, 0, 128, 128, 16, 256)
+    s = p.seq_create()
+    n = 1024
+    k = torch.randn(n, 2, 128, dtype=torch.bfloat16, device="cuda:0")
+    v = torch.randn(n, 2, 128, dtype=torch.bfloat16, device="cuda:0")
+    q = torch.randn(64, 8, 128, dtype=torch.bfloat16, device="cuda:0")
+    p.append(s, np.arange(n), k, None, v)        # untimed
+    torch.cuda.synchronize()
+    p.timing_enable(True)
+    for kind in akv.KERNEL_KINDS:
+        p.timing_read(kind)
+    t0 = time.perf_counter()
+    p.drop(s, [[100, 500]])
+    p.repos(s, [[500, n]], [-400])
+    p.seq_attention(q, [(s, 0, 64, None)])
+    p.compact(s, True)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    got = {kind: p.timing_read(kind) for kind in ("append", "rotate", "expand", "attention", "compact")}
+    assert got["append"] == (0.0, 0), got
+    for kind in ("rotate", "expand", "attention", "compact"):
+        ms, cnt = got[kind]
+        assert cnt == 1 and 0.0 < ms < wall_ms, (kind, got)
+    p.timing_enable(False)
+    p.seq_attention(q, [(s, 0, 64, None)])
+    torch.cuda.synchronize()
+    assert p.timing_read("attention") == (0.0, 0)
+    p.close()
