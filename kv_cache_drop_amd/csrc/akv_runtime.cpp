@@ -517,6 +517,7 @@ struct KTimer {
     ev = akv::LaunchEvents{};
     a = b = nullptr;
   }
+  ~KTimer() { done(); }   // a path that returns early leaves no events armed
 };
 
 akv_status timing_collect(akv_pool* p) {
