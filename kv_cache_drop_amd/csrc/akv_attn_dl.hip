@@ -284,7 +284,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) m = fmaxf(m, sacc[qb][kb][i]);
-      mx[qb] = fmaxf(m, __shfl_xor(m, 32));
+      mx[qb] = max_xor32(m);
     }
   };
   // Lazy rescale: move the running offset only when the max grew by more
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_seg_attn_dl(AttnArgs a) {
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l = l_run[qb] + __shfl_xor(l_run[qb], 32);
+    const float l = sum_xor32(l_run[qb]);
     if (!valid[qb]) continue;
     if (it.part < 0) {
       const float inv = l > 0.f ? 1.f / l : 0.f;

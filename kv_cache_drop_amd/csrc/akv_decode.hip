@@ -29,6 +29,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "akv_device.h"
 #include "akv_internal.h"
 #include "akv_launch.h"
 
@@ -231,8 +232,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES, 2) void k_decode_attn(AttnArgs a) {
     }
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float m_cand = fmaxf(m_run, mx * c2);
     if (__ballot(m_cand > m_run + DEC_RESCALE_LOG2)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
@@ -298,8 +298,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES, 2) void k_decode_attn(AttnArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // merge the waves: (m, l) per row, O^T rows through LDS
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_xor32(sum_xor16(l_run));
   __syncthreads();
   float* s_o = (float*)s_v;   // [wave][row 16][d 128] (32 KiB of the staging space)
   if (g == 0) {

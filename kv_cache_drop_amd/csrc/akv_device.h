@@ -56,6 +56,28 @@ struct LdsPart {
   }
 };
 
+// Reductions over lane pairs of a wave without LDS traffic.  On gfx950,
+// v_permlane32_swap (v_permlane16_swap) with one register as both operands
+// leaves each lane the two values of its pair, lane l and lane l ^ 32 (within
+// each half of 32 lanes, l ^ 16), in two registers, in the same order for both
+// lanes of the pair, which therefore agree bit for bit.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Eight floats from a wave-uniform address through the scalar data cache
 // (a load: counted by lgkmcnt, so waiting for it never drains the tile DMAs
 // that vmcnt counts).

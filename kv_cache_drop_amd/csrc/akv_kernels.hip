@@ -405,7 +405,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_seg_attn(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(mx);
     const float m_cand = fmaxf(m_run, mx * c2);
     if (__ballot(m_cand > m_run + RESCALE_LOG2)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_seg_attn(AttnArgs a) {
   }
 
   // the two lanes of a row hold disjoint key halves of l
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_xor32(l_run);
   // epilogue: lane holds O^T columns c = 32cb + 8m + 4g + 0..3 of its row
   if (!valid) return;
   if (it.part < 0) {
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(512, 1) void k_seg_attn_mla(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) m = fmaxf(m, sacc[kb][i]);
-    return fmaxf(m, __shfl_xor(m, 32));
+    return max_xor32(m);
   };
   auto sm_rescale = [&](float mx, int j) __attribute__((always_inline)) -> float {
     const float m_cand = fmaxf(m_run, mx * c2);
@@ -773,7 +773,7 @@ __global__ __launch_bounds__(512, 1) void k_seg_attn_mla(AttnArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
 
-  const float l = l_run + __shfl_xor(l_run, 32);
+  const float l = sum_xor32(l_run);
   if (!valid) return;
   if (it.part < 0) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
