@@ -37,21 +37,21 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # the 64K step.  A plain 1 GiB device copy reads FETCH_SIZE = 524,302 KiB and
 # WRITE_SIZE = 1,048,576 KiB, so fetched KiB are scaled by 2.0 and written KiB
 # by 1.0.  When the kernel's source differs, its traffic is reported as null.
-_ATTN_SHA1 = "adaa2bddcc5a394cec08357144e884b7cc558c04"       # akv_attn_dl.hip
-_KERNELS_SHA1 = "6a0e8f28a1396015ae04e86664c2a80bcd9ac662"    # akv_kernels.hip
+_ATTN_SHA1 = "4883d2cf4f9938a8863e15488837c3e251c40763"       # akv_attn_dl.hip
+_KERNELS_SHA1 = "28cf8d7a53eb19500e6149ba20c49866ca3a66b4"    # akv_kernels.hip
 _COPY_SHA1 = "e0150158ee0d1c27d58bdf5f6e0337b98da28d4d"       # akv_copy.hip
-_DECODE_SHA1 = "060e1f71384fd8b27f435f682fbb320b988863d4"     # akv_decode.hip
+_DECODE_SHA1 = "f1365b8a3e8adaa58c6f7eaa0af19166e1d18e45"     # akv_decode.hip
 COUNTERS = {
     "fetch_scale": 1048576 / 524302, "write_scale": 1.0,
-    "attention": {"source": "akv_attn_dl.hip", "sha1": _ATTN_SHA1, "fetch_kib": 113172, "write_kib": 18432},
-    "rotate": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 39278, "write_kib": 77640},
-    "rotate_32_layers": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 1248996,
-                         "write_kib": 2484301},
-    "compact": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 85344, "write_kib": 165581},
+    "attention": {"source": "akv_attn_dl.hip", "sha1": _ATTN_SHA1, "fetch_kib": 112697, "write_kib": 17408},
+    "rotate": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 39275, "write_kib": 77627},
+    "rotate_32_layers": {"source": "akv_kernels.hip", "sha1": _KERNELS_SHA1, "fetch_kib": 1248979,
+                         "write_kib": 2484443},
+    "compact": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 85360, "write_kib": 165591},
     # the decode steps of 48 requests (seed 0, mean over 8 steps), k_decode_attn<false>
-    "decode": {"source": "akv_decode.hip", "sha1": _DECODE_SHA1, "fetch_kib": 611717, "write_kib": 3625},
+    "decode": {"source": "akv_decode.hip", "sha1": _DECODE_SHA1, "fetch_kib": 611701, "write_kib": 3625},
     # the retrigger clone (seed 0), k_move_tokens with the rotation
-    "clone": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 80741, "write_kib": 157387},
+    "clone": {"source": "akv_copy.hip", "sha1": _COPY_SHA1, "fetch_kib": 80743, "write_kib": 157375},
 }
 
 
