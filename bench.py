@@ -212,6 +212,36 @@ def hbm_reference() -> dict:
     return {"hbm_reference": out, "note": "torch elementwise kernels on contiguous 4 GiB bf16 buffers"}
 
 
+def mfma_reference() -> dict:
+    """The chip's dense bf16 rate through the vendor GEMM library (torch.matmul
+    of contiguous square bf16 matrices, fp32 accumulation, on hipBLASLt or
+    rocBLAS): a reference for the attention kernel's roofline fraction, not
+    part of the path.  Median of 5 timed products after 3 warm-ups."""
+    import torch
+    out = {}
+    for n in (4096, 8192, 16384):
+        g = torch.Generator(device="cuda:0").manual_seed(n)
+        a = torch.randn(n, n, device="cuda:0", generator=g).to(torch.bfloat16)
+        b = torch.randn(n, n, device="cuda:0", generator=g).to(torch.bfloat16)
+        for _ in range(3):
+            c = torch.matmul(a, b)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            c = torch.matmul(a, b)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        t = float(np.median(ms))
+        flop = 2.0 * n ** 3
+        out[f"gemm_{n}"] = {"flop": flop, "ms": round(t, 4), "TFLOP/s": round(flop / (t * 1e-3) / 1e12, 1),
+                            "frac_of_2.5PFLOPs": round(flop / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del a, b, c
+    return {"mfma_reference": out, "note": "torch.matmul, contiguous square bf16 operands, fp32 accumulation"}
+
+
 def compact_extra(pool, seqs, L) -> dict:
     """Extra line: forced compaction (k_move_tokens) of C2 sequences after their
     step, each the only work on its copy since that step (the earliest timed
@@ -587,7 +617,13 @@ def main():
     ap.add_argument("--hbm-reference", action="store_true",
                     help="only time plain streaming kernels (torch's in-place multiply and copy over 4 GiB, "
                          "out of every cache): the chip's rates for in-place read-modify-write and copy")
+    ap.add_argument("--mfma-reference", action="store_true",
+                    help="only time plain bf16 GEMMs of the vendor library (torch.matmul, 4K-16K squares): "
+                         "the chip's dense bf16 rate as a library reaches it")
     args = ap.parse_args()
+    if args.mfma_reference:
+        print(json.dumps(mfma_reference()), flush=True)
+        return
     if args.hbm_reference:
         print(json.dumps(hbm_reference()), flush=True)
         return
