@@ -113,8 +113,8 @@ def _cpu_item(task):
 
 
 def host_cpu():
-    """CPU model and the cores this process may use (at most 16: the GPU machine's
-    share for one GPU)."""
+    """CPU model and the cores this process may use (at most 16: the host
+    share that goes with one GPU)."""
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:

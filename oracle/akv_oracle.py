@@ -165,8 +165,8 @@ class Pool:
 
     key_store: "fp64" keeps a rotated key exactly (the method's own values);
     "bf16" stores each key a repos, splice or clone rotates as its bfloat16
-    rounding, once per call, as a pool held in bf16 does (the benchmark spec: the
-    paged pool is bf16; [Leyline] Limitations: the rotation is done in
+    rounding, once per call, as a pool held in bf16 does (the device pool
+    holds bf16 pages; [Leyline] Limitations: the rotation is done in
     higher precision and stored)."""
 
     def __init__(self, layout, page_order: Optional[Sequence[int]] = None,
