@@ -665,7 +665,7 @@ def main():
     hist, drop, repos, new, att = ops[1], ops[2], ops[3], ops[4], ops[5]
     assert isinstance(drop, W.Drop) and isinstance(repos, W.Repos) and isinstance(att, W.Attention)
     # After the GPU has idled (set-up, a Python collection), the first ~10
-    # steps run 10-25% slower than the later ones (on the box: attention
+    # steps run 10-25% slower than the later ones (measured: attention
     # launches of 1.3-1.48 ms against 1.12-1.15 ms, settling over ~30 ms of
     # load); untimed prelude steps on their own copies keep that transient
     # out of the timed steps.
